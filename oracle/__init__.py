@@ -1,0 +1,193 @@
+"""CPU oracle for SPICY-KV coarsen + decode — TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product path (``coarse_grained_decode_amd``)
+never imports it and shares no code with it.
+
+The arithmetic lives in ``spicy_oracle.c`` (plain C, double precision, one
+step at a time as the pages define it).  This module only marshals numpy
+arrays into that library and splits the batch over host threads.
+
+Parity: coarsening and decoding are pinned by the tests in ``tests/`` against
+closed forms, library routines and invariants (see the test docstrings).  The
+agreement with the pages' own quality results (RULER recall, the demo page's
+simulator table) is *parity unpinned*: the pages print no values to compare.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB = os.path.join(HERE, "liboracle.so")
+SRC = os.path.join(HERE, "spicy_oracle.c")
+
+DT = {"f32": 0, "bf16": 1, "f64": 2}
+NP = {"f32": np.float32, "bf16": np.uint16, "f64": np.float64}
+META_DTYPE = np.dtype([("kind", "<i4"), ("mass", "<i4"), ("pos_sum", "<i8")])
+PAGE = 16
+
+_lib = None
+_lock = threading.Lock()
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (plain -O2, no fast-math, no contraction)."""
+    if force or not os.path.exists(LIB):
+        cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-ffp-contract=off",
+               "-fno-fast-math", "-shared", "-fPIC", "-o", LIB, SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+    return LIB
+
+
+def lib():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+                build()
+            L = ctypes.CDLL(LIB)
+            P = ctypes.c_void_p
+            i32 = ctypes.c_int32
+            L.oracle_coarsen.restype = ctypes.c_int
+            L.oracle_coarsen.argtypes = [ctypes.c_int, ctypes.c_int, i32, i32, P, P, P, P, P, P, P,
+                                         i32, ctypes.c_double, P, P, P, P, i32, P, i32, P, P, i32, i32]
+            L.oracle_decode.restype = ctypes.c_int
+            L.oracle_decode.argtypes = [ctypes.c_int, ctypes.c_int, i32, i32, i32, P, P, P, P, i32,
+                                        P, i32, P, i32, P, P, i32, i32]
+            L.oracle_bf16_round.restype = ctypes.c_uint16
+            L.oracle_bf16_round.argtypes = [ctypes.c_double]
+            L.oracle_bf16_value.restype = ctypes.c_double
+            L.oracle_bf16_value.argtypes = [ctypes.c_uint16]
+            L.oracle_rope.restype = None
+            L.oracle_rope.argtypes = [P, P, i32, ctypes.c_double, ctypes.c_double]
+            _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _chunks(B, threads):
+    threads = max(1, min(threads, B))
+    step = -(-B // threads) if B else 1
+    return [(s, min(B, s + step)) for s in range(0, B, step)] or [(0, 0)]
+
+
+def default_threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+class Cache:
+    """Host copy of a paged compressed cache in the library's layout."""
+
+    def __init__(self, store: str, num_pages: int, H_kv: int, d: int, fill: bool = True):
+        self.store, self.num_pages, self.H_kv, self.d = store, num_pages, H_kv, d
+        dt = NP[store]
+        self.k = np.empty((num_pages, H_kv, PAGE, d), dtype=dt)
+        self.v = np.empty((num_pages, H_kv, d, PAGE), dtype=dt)
+        self.ab = np.empty((num_pages, H_kv, PAGE, 2), dtype=dt)
+        self.meta = np.zeros((num_pages, H_kv, PAGE), dtype=META_DTYPE)
+        if fill:  # recognisable garbage so that unwritten slots never look valid
+            for a in (self.k, self.v, self.ab):
+                if store == "bf16":
+                    a.fill(0x7FC1)
+                else:
+                    a.fill(np.nan)
+            self.meta["kind"] = -1
+
+
+def coarsen(call, cache: Cache, in_dtype: str | None = None, threads: int | None = None) -> np.ndarray:
+    """Run oracle_coarsen for one CoarsenCall into `cache`; returns lengths_out."""
+    L = lib()
+    in_dtype = in_dtype or call.dtype
+    k = np.ascontiguousarray(call.k)
+    v = np.ascontiguousarray(call.v)
+    lengths = np.zeros(call.B, dtype=np.int32)
+    args_fixed = dict()
+    rcs = []
+
+    def run(rng):
+        b0, b1 = rng
+        rc = L.oracle_coarsen(DT[in_dtype], DT[cache.store], call.H_kv, call.d, _p(k), _p(v),
+                              _p(call.seq_offsets), _p(call.pos_base), _p(call.seg_offsets),
+                              _p(call.seq_seg_ptr), _p(call.mask), call.B, call.rope_base,
+                              _p(cache.k), _p(cache.v), _p(cache.ab), _p(cache.meta), cache.num_pages,
+                              _p(call.page_table), call.max_pages, _p(call.entry_start), _p(lengths),
+                              b0, b1)
+        rcs.append(rc)
+
+    del args_fixed
+    chunks = _chunks(call.B, threads or default_threads())
+    if len(chunks) == 1:
+        run(chunks[0])
+    else:
+        with ThreadPoolExecutor(len(chunks)) as ex:
+            list(ex.map(run, chunks))
+    if any(rc != 0 for rc in rcs):
+        raise ValueError(f"oracle_coarsen failed: codes {sorted(set(rcs))}")
+    return lengths
+
+
+def decode(q: np.ndarray, q_dtype: str, cache: Cache, H_q: int, page_table: np.ndarray,
+           lengths: np.ndarray, threads: int | None = None):
+    """Run oracle_decode; returns (o [B, H_q, d] float64, lse [B, H_q] float64)."""
+    L = lib()
+    q = np.ascontiguousarray(q)
+    B = int(q.shape[0])
+    d = cache.d
+    o = np.zeros((B, H_q, d), dtype=np.float64)
+    lse = np.zeros((B, H_q), dtype=np.float64)
+    table = np.ascontiguousarray(page_table, dtype=np.int32)
+    lens = np.ascontiguousarray(lengths, dtype=np.int32)
+    rcs = []
+
+    def run(rng):
+        b0, b1 = rng
+        rcs.append(L.oracle_decode(DT[q_dtype], DT[cache.store], H_q, cache.H_kv, d, _p(q),
+                                   _p(cache.k), _p(cache.v), _p(cache.ab), cache.num_pages,
+                                   _p(table), int(table.shape[1]), _p(lens), B,
+                                   _p(o), _p(lse), b0, b1))
+
+    chunks = _chunks(B, threads or default_threads())
+    if len(chunks) == 1:
+        run(chunks[0])
+    else:
+        with ThreadPoolExecutor(len(chunks)) as ex:
+            list(ex.map(run, chunks))
+    if any(rc != 0 for rc in rcs):
+        raise ValueError(f"oracle_decode failed: codes {sorted(set(rcs))}")
+    return o, lse
+
+
+def run_workload(wl, store: str | None = None, threads: int | None = None):
+    """Coarsen every call of a workload (setup calls, then the step call once)
+    into a fresh cache and decode its queries.  Returns (cache, lengths, o, lse)."""
+    store = store or wl.dtype
+    cache = Cache(store, wl.num_pages, wl.H_kv, wl.d)
+    lengths = None
+    for call in wl.calls:
+        lengths = coarsen(call, cache, threads=threads)
+    o, lse = decode(wl.q, wl.dtype, cache, wl.H_q, wl.page_table, lengths, threads=threads)
+    return cache, lengths, o, lse
+
+
+def bf16_round(x: float) -> int:
+    return int(lib().oracle_bf16_round(float(x)))
+
+
+def bf16_value(bits: int) -> float:
+    return float(lib().oracle_bf16_value(int(bits)))
+
+
+def rope(x: np.ndarray, pos: float, base: float) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    y = np.empty_like(x)
+    lib().oracle_rope(_p(y), _p(x), int(x.shape[0]), float(pos), float(base))
+    return y

@@ -1,0 +1,362 @@
+/*
+ * CPU oracle for SPICY-KV coarse-grained decode — TEST INFRASTRUCTURE ONLY.
+ * (See spicy_oracle.h for who may use it and for the cache layout.)
+ *
+ * Everything here is the definition written out in double precision, one
+ * step at a time, in the order the pages give it.  No blocking, no fusion,
+ * no reordering beyond the definition.  Rounding to the storage type happens
+ * exactly once, when a value is stored.
+ */
+#include "spicy_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define PAGE 16
+
+/* ------------------------------------------------------------------------ */
+/* Storage rounding                                                          */
+/* ------------------------------------------------------------------------ */
+
+/* bfloat16 value of a bit pattern: the bits are the top half of a binary32. */
+double oracle_bf16_value(uint16_t bits) {
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* Round a double to the nearest bfloat16, ties to even, in one step (no
+ * intermediate binary32 rounding).  bfloat16 has 8 significant bits and the
+ * binary32 exponent range, so the spacing of representable values around x is
+ * 2^(E-7) with E = max(floor(log2|x|), -126).  Scaling by a power of two is
+ * exact, rint() rounds to nearest-even, scaling back is exact. */
+uint16_t oracle_bf16_round(double x) {
+    if (isnan(x)) return (uint16_t)0x7FC0;
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs(x);
+    if (isinf(a)) return (uint16_t)(sign | 0x7F80);
+    if (a == 0.0) return sign;
+    int e2;
+    (void)frexp(a, &e2);          /* a = f * 2^e2, f in [0.5, 1) */
+    int E = e2 - 1;               /* leading bit weight 2^E      */
+    if (E < -126) E = -126;       /* subnormal spacing           */
+    int lsb = E - 7;
+    double q = rint(ldexp(a, -lsb));
+    double r = ldexp(q, lsb);
+    if (r >= ldexp(1.0, 128)) return (uint16_t)(sign | 0x7F80);
+    float f = (float)r;           /* exact: r has <= 8 significant bits */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(sign | (uint16_t)(u >> 16));
+}
+
+static double load_elem(int dtype, const void* base, size_t i) {
+    switch (dtype) {
+    case ORACLE_F32: return (double)((const float*)base)[i];
+    case ORACLE_BF16: return oracle_bf16_value(((const uint16_t*)base)[i]);
+    default: return ((const double*)base)[i];
+    }
+}
+
+static void store_elem(int dtype, void* base, size_t i, double x) {
+    switch (dtype) {
+    case ORACLE_F32: ((float*)base)[i] = (float)x; break;     /* RNE */
+    case ORACLE_BF16: ((uint16_t*)base)[i] = oracle_bf16_round(x); break;
+    default: ((double*)base)[i] = x; break;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Rotary position embedding                                                 */
+/* ------------------------------------------------------------------------ */
+
+/* y = R(pos) x with the half-split pairing (i, i + d/2) and frequencies
+ * theta_i = base^(-2i/d).  The position is a real number: macro-nodes are
+ * rotated to their mass-weighted anchor (SPICY-KV demo page, Claim 2:
+ * "spectral center-of-mass position").  base <= 0 means no rotation. */
+void oracle_rope(double* y, const double* x, int32_t d, double pos, double base) {
+    int32_t half = d / 2;
+    if (!(base > 0.0)) {
+        for (int32_t i = 0; i < d; ++i) y[i] = x[i];
+        return;
+    }
+    for (int32_t i = 0; i < half; ++i) {
+        double theta = pow(base, -2.0 * (double)i / (double)d);
+        double phi = pos * theta;
+        double c = cos(phi), s = sin(phi);
+        double lo = x[i], hi = x[i + half];
+        y[i] = lo * c - hi * s;
+        y[i + half] = hi * c + lo * s;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Coarsening                                                                */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    int32_t kind;
+    int32_t mass;
+    int64_t pos_sum;
+} oracle_meta;
+
+typedef struct {
+    int dtype;
+    int32_t H, d, num_pages, max_pages;
+    void *k, *v, *ab;
+    oracle_meta* meta;
+    const int32_t* table_row;
+} cache_view;
+
+/* Store one entry at logical index e of a sequence.  key and val are
+ * d-vectors already in their final (rotated) form. */
+static int put_entry(const cache_view* c, int32_t h, int64_t e,
+                     const double* key, const double* val,
+                     double alpha, double beta,
+                     int32_t kind, int32_t mass, int64_t pos_sum) {
+    int64_t lp = e / PAGE;
+    if (lp >= c->max_pages) return 3;
+    int32_t P = c->table_row[lp];
+    if (P < 0 || P >= c->num_pages) return 2;
+    int32_t slot = (int32_t)(e % PAGE);
+    size_t ph = (size_t)P * (size_t)c->H + (size_t)h;
+    for (int32_t i = 0; i < c->d; ++i) {
+        store_elem(c->dtype, c->k, (ph * PAGE + (size_t)slot) * (size_t)c->d + (size_t)i, key[i]);
+        store_elem(c->dtype, c->v, (ph * (size_t)c->d + (size_t)i) * PAGE + (size_t)slot, val[i]);
+    }
+    store_elem(c->dtype, c->ab, (ph * PAGE + (size_t)slot) * 2 + 0, alpha);
+    store_elem(c->dtype, c->ab, (ph * PAGE + (size_t)slot) * 2 + 1, beta);
+    if (c->meta) {
+        oracle_meta* m = &c->meta[ph * PAGE + (size_t)slot];
+        m->kind = kind;
+        m->mass = mass;
+        m->pos_sum = pos_sum;
+    }
+    return 0;
+}
+
+/* spicy_coarsen, defined step by step.
+ *
+ * Per sequence b and KV head h, the caller's segments split the sequence's
+ * tokens into contiguous runs.  Inside a segment the protected tokens are
+ * C-points (exact, mass 1, own position) and the rest are F-points merged into
+ * one macro-node (SPICY-KV demo page, Claim 2; SPICY-KV abstract, item (3)):
+ *   m      = |F|                                  conserved mass
+ *   kbar   = (1/m) sum_F k_t     (pre-RoPE keys)  mass-weighted mean key
+ *   vbar   = (1/m) sum_F v_t                      mean value
+ *   sigma2 = (1/(m d)) sum_F ||k_t - kbar||^2     scalar sub-grid variance
+ *   tbar   = (1/m) sum_F p_t                      centre-of-mass position
+ * stored as key R(tbar) kbar, value vbar, alpha = ln m and
+ * beta = sigma2 / (2 d) (demo page, section 2, and Claim 3).
+ * A C-point stores R(p_t) k_t, v_t, alpha = 0, beta = 0 (m_c = 1, exact t_c).
+ * Order inside a segment: macro-node first, then C-points by position.
+ * Heads with fewer entries than the most populous head are padded with null
+ * entries (alpha = -inf, zero key and value) up to that count, and the tail
+ * of the last page touched is padded with nulls as well.
+ * lengths_out[b] = entry_start[b] + max over heads of the entry count. */
+int oracle_coarsen(int in_dtype, int dtype, int32_t H_kv, int32_t d,
+                   const void* k_pre, const void* v,
+                   const int32_t* seq_offsets, const int32_t* pos_base,
+                   const int32_t* seg_offsets, const int32_t* seq_seg_ptr,
+                   const uint8_t* protected_mask,
+                   int32_t B, double rope_base,
+                   void* k_pool, void* v_pool, void* ab_pool, void* meta,
+                   int32_t num_pages,
+                   const int32_t* page_table, int32_t max_pages_per_seq,
+                   const int32_t* entry_start, int32_t* lengths_out,
+                   int32_t b_begin, int32_t b_end) {
+    if (dtype < 0 || dtype > 2 || in_dtype < 0 || in_dtype > 2) return 1;
+    if (H_kv <= 0 || d <= 0 || (d % 2) != 0 || B < 0) return 1;
+    if (!k_pre || !v || !seq_offsets || !seg_offsets || !seq_seg_ptr || !protected_mask) return 1;
+    if (!k_pool || !v_pool || !ab_pool || !page_table || !lengths_out) return 1;
+    if (b_begin < 0 || b_end > B || b_begin > b_end) return 1;
+
+    double* key = malloc(sizeof(double) * (size_t)d);
+    double* rot = malloc(sizeof(double) * (size_t)d);
+    double* val = malloc(sizeof(double) * (size_t)d);
+    double* zero = calloc((size_t)d, sizeof(double));
+    int64_t* total = malloc(sizeof(int64_t) * (size_t)H_kv);
+    if (!key || !rot || !val || !zero || !total) {
+        free(key); free(rot); free(val); free(zero); free(total);
+        return 1;
+    }
+    int rc = 0;
+
+    for (int32_t b = b_begin; b < b_end && rc == 0; ++b) {
+        cache_view c = {dtype, H_kv, d, num_pages, max_pages_per_seq,
+                        k_pool, v_pool, ab_pool, (oracle_meta*)meta,
+                        page_table + (size_t)b * (size_t)max_pages_per_seq};
+        int32_t t0 = seq_offsets[b], t1 = seq_offsets[b + 1];
+        int32_t s0 = seq_seg_ptr[b], s1 = seq_seg_ptr[b + 1];
+        int64_t e0 = entry_start ? entry_start[b] : 0;
+        int64_t p0 = pos_base ? pos_base[b] : 0;
+        if (t0 > t1 || s0 > s1 || e0 < 0) { rc = 1; break; }
+        if (seg_offsets[s0] != t0 || seg_offsets[s1] != t1) { rc = 1; break; }
+        for (int32_t s = s0; s < s1; ++s)
+            if (seg_offsets[s] > seg_offsets[s + 1]) { rc = 1; break; }
+        if (rc) break;
+
+        for (int32_t h = 0; h < H_kv && rc == 0; ++h) {
+            int64_t e = e0;
+            for (int32_t s = s0; s < s1 && rc == 0; ++s) {
+                int32_t a = seg_offsets[s], z = seg_offsets[s + 1];
+
+                /* F-points: the unprotected tokens of the segment. */
+                int32_t m = 0;
+                int64_t pos_sum = 0;
+                for (int32_t i = 0; i < d; ++i) { key[i] = 0.0; val[i] = 0.0; }
+                for (int32_t t = a; t < z; ++t) {
+                    if (protected_mask[(size_t)t * (size_t)H_kv + (size_t)h]) continue;
+                    ++m;
+                    pos_sum += p0 + (t - t0);
+                    for (int32_t i = 0; i < d; ++i) {
+                        size_t ix = ((size_t)t * (size_t)H_kv + (size_t)h) * (size_t)d + (size_t)i;
+                        key[i] += load_elem(in_dtype, k_pre, ix);
+                        val[i] += load_elem(in_dtype, v, ix);
+                    }
+                }
+                if (m > 0) {
+                    for (int32_t i = 0; i < d; ++i) { key[i] /= (double)m; val[i] /= (double)m; }
+                    /* second pass: population variance around the mean */
+                    double ss = 0.0;
+                    for (int32_t t = a; t < z; ++t) {
+                        if (protected_mask[(size_t)t * (size_t)H_kv + (size_t)h]) continue;
+                        for (int32_t i = 0; i < d; ++i) {
+                            size_t ix = ((size_t)t * (size_t)H_kv + (size_t)h) * (size_t)d + (size_t)i;
+                            double dv = load_elem(in_dtype, k_pre, ix) - key[i];
+                            ss += dv * dv;
+                        }
+                    }
+                    double sigma2 = ss / ((double)m * (double)d);
+                    double tbar = (double)pos_sum / (double)m;
+                    oracle_rope(rot, key, d, tbar, rope_base);
+                    rc = put_entry(&c, h, e, rot, val, log((double)m),
+                                   sigma2 / (2.0 * (double)d), 2, m, pos_sum);
+                    ++e;
+                }
+
+                /* C-points, ascending position. */
+                for (int32_t t = a; t < z && rc == 0; ++t) {
+                    if (!protected_mask[(size_t)t * (size_t)H_kv + (size_t)h]) continue;
+                    int64_t p = p0 + (t - t0);
+                    for (int32_t i = 0; i < d; ++i) {
+                        size_t ix = ((size_t)t * (size_t)H_kv + (size_t)h) * (size_t)d + (size_t)i;
+                        key[i] = load_elem(in_dtype, k_pre, ix);
+                        val[i] = load_elem(in_dtype, v, ix);
+                    }
+                    oracle_rope(rot, key, d, (double)p, rope_base);
+                    rc = put_entry(&c, h, e, rot, val, 0.0, 0.0, 1, 1, p);
+                    ++e;
+                }
+            }
+            total[h] = e - e0;
+        }
+        if (rc) break;
+
+        int64_t most = 0;
+        for (int32_t h = 0; h < H_kv; ++h) if (total[h] > most) most = total[h];
+        int64_t len = e0 + most;
+        int64_t padded = (len + PAGE - 1) / PAGE * PAGE;
+        for (int32_t h = 0; h < H_kv && rc == 0; ++h)
+            for (int64_t e = e0 + total[h]; e < padded && rc == 0; ++e)
+                rc = put_entry(&c, h, e, zero, zero, -INFINITY, 0.0, 0, 0, 0);
+        if (rc) break;
+        lengths_out[b] = (int32_t)len;
+    }
+    free(key); free(rot); free(val); free(zero); free(total);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Decode                                                                    */
+/* ------------------------------------------------------------------------ */
+
+/* spicy_decode_attn, defined directly.  For query head g (KV head
+ * h = g / (H_q / H_kv)) and every logical entry e < lengths[b]:
+ *   s_e = (q . k_e) / sqrt(d) + alpha_e + ||q||^2 beta_e
+ * (SPICY-KV demo page, section 2: the logit with log_mass and
+ * half_inv_dk_sigma_sq; Claim 3: the closure term ||q||^2 sigma^2 / (2 d_k)).
+ *   LSE = ln sum_e exp(s_e),   O = sum_e exp(s_e - LSE) v_e.
+ * A null entry (alpha = -inf) has weight zero.  With no entry of non-zero
+ * weight: LSE = -inf and O = 0.  o is [B][H_q][d], lse is [B][H_q]. */
+int oracle_decode(int q_dtype, int dtype, int32_t H_q, int32_t H_kv, int32_t d,
+                  const void* q,
+                  const void* k_pool, const void* v_pool, const void* ab_pool,
+                  int32_t num_pages,
+                  const int32_t* page_table, int32_t max_pages_per_seq,
+                  const int32_t* lengths, int32_t B,
+                  double* o, double* lse,
+                  int32_t b_begin, int32_t b_end) {
+    if (dtype < 0 || dtype > 2 || q_dtype < 0 || q_dtype > 2) return 1;
+    if (H_q <= 0 || H_kv <= 0 || d <= 0 || (H_q % H_kv) != 0) return 1;
+    if (!q || !k_pool || !v_pool || !ab_pool || !page_table || !lengths || !o || !lse) return 1;
+    if (b_begin < 0 || b_end > B || b_begin > b_end) return 1;
+    int32_t G = H_q / H_kv;
+    for (int32_t b = b_begin; b < b_end; ++b) {
+        int32_t L = lengths[b];
+        if (L < 0) return 1;
+        if ((int64_t)(L + PAGE - 1) / PAGE > max_pages_per_seq) return 3;
+        for (int32_t lp = 0; lp < (L + PAGE - 1) / PAGE; ++lp) {
+            int32_t P = page_table[(size_t)b * (size_t)max_pages_per_seq + (size_t)lp];
+            if (P < 0 || P >= num_pages) return 2;
+        }
+    }
+
+    double* s = malloc(sizeof(double) * 1);
+    int32_t cap = 1;
+    for (int32_t b = b_begin; b < b_end; ++b) {
+        int32_t L = lengths[b];
+        if (L > cap) {
+            free(s);
+            s = malloc(sizeof(double) * (size_t)L);
+            cap = L;
+        }
+        if (!s) return 1;
+        const int32_t* row = page_table + (size_t)b * (size_t)max_pages_per_seq;
+        for (int32_t g = 0; g < H_q; ++g) {
+            int32_t h = g / G;
+            size_t qo = ((size_t)b * (size_t)H_q + (size_t)g) * (size_t)d;
+            double qn2 = 0.0;
+            for (int32_t i = 0; i < d; ++i) {
+                double qi = load_elem(q_dtype, q, qo + (size_t)i);
+                qn2 += qi * qi;
+            }
+            double smax = -INFINITY;
+            for (int32_t e = 0; e < L; ++e) {
+                size_t ph = (size_t)row[e / PAGE] * (size_t)H_kv + (size_t)h;
+                int32_t slot = e % PAGE;
+                double alpha = load_elem(dtype, ab_pool, (ph * PAGE + (size_t)slot) * 2 + 0);
+                double beta = load_elem(dtype, ab_pool, (ph * PAGE + (size_t)slot) * 2 + 1);
+                if (alpha == -INFINITY) { s[e] = -INFINITY; continue; }
+                double dot = 0.0;
+                for (int32_t i = 0; i < d; ++i)
+                    dot += load_elem(q_dtype, q, qo + (size_t)i) *
+                           load_elem(dtype, k_pool, (ph * PAGE + (size_t)slot) * (size_t)d + (size_t)i);
+                s[e] = dot / sqrt((double)d) + alpha + qn2 * beta;
+                if (s[e] > smax) smax = s[e];
+            }
+            double* out = o + qo;
+            for (int32_t i = 0; i < d; ++i) out[i] = 0.0;
+            if (smax == -INFINITY) {
+                lse[(size_t)b * (size_t)H_q + (size_t)g] = -INFINITY;
+                continue;
+            }
+            double z = 0.0;
+            for (int32_t e = 0; e < L; ++e) z += exp(s[e] - smax);
+            double lz = smax + log(z);
+            lse[(size_t)b * (size_t)H_q + (size_t)g] = lz;
+            for (int32_t e = 0; e < L; ++e) {
+                double w = exp(s[e] - lz);
+                if (w == 0.0) continue;
+                size_t ph = (size_t)row[e / PAGE] * (size_t)H_kv + (size_t)h;
+                int32_t slot = e % PAGE;
+                for (int32_t i = 0; i < d; ++i)
+                    out[i] += w * load_elem(dtype, v_pool, (ph * (size_t)d + (size_t)i) * PAGE + (size_t)slot);
+            }
+        }
+    }
+    free(s);
+    return 0;
+}

@@ -1,0 +1,73 @@
+/*
+ * CPU oracle for SPICY-KV coarse-grained decode — TEST INFRASTRUCTURE ONLY.
+ *
+ * Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may
+ * load or call this library.  The GPU library never links it and shares no
+ * code, header, table or helper with it.
+ *
+ * Plain, slow, definitional C in double precision.  Every function states
+ * the passage of the pages it follows:
+ *   - "SPICY-KV demo page" = the SPICY-KV demo page ("SPectral Invariant
+ *     Coarse-graining with dYadic KV Renormalization"), with its sections
+ *     "2. FlashAttention-2/3 & PagedAttention Online-Softmax Kernel Fusion"
+ *     and "Patent Pending Notice & Claims 1-20" (Claims 1, 2, 3).
+ *   - "SPICY-KV abstract" = the abstract page of the same method, items (1)-(4).
+ *
+ * in_dtype / q_dtype is the type of the caller's inputs (keys, values,
+ * queries); dtype is the storage type of the cache.
+ *
+ * Storage dtypes: ORACLE_F32 (IEEE binary32), ORACLE_BF16 (bfloat16 bits in a
+ * uint16), ORACLE_F64 (no rounding at all: the "exact layer" used by the
+ * invariant tests).
+ *
+ * Cache layout (the same contract the GPU library documents, implemented
+ * here independently):
+ *   k_pool : [num_pages][H_kv][16][d]      entry-major key rows
+ *   v_pool : [num_pages][H_kv][d][16]      dim-major value tile
+ *   ab_pool: [num_pages][H_kv][16][2]      (alpha, beta) per entry
+ *   meta   : [num_pages][H_kv][16] x {int32 kind, int32 mass, int64 pos_sum}
+ *            kind 0 = null, 1 = exact C-point, 2 = macro-node
+ * Logical entry e of sequence b lives in physical page page_table[b][e/16],
+ * slot e%16.
+ */
+#ifndef SPICY_ORACLE_H
+#define SPICY_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_F64 = 2 };
+
+/* Return codes: 0 ok, 1 bad argument, 2 index out of range, 3 capacity. */
+
+int oracle_coarsen(int in_dtype, int dtype, int32_t H_kv, int32_t d,
+                   const void* k_pre, const void* v,
+                   const int32_t* seq_offsets, const int32_t* pos_base,
+                   const int32_t* seg_offsets, const int32_t* seq_seg_ptr,
+                   const uint8_t* protected_mask,
+                   int32_t B, double rope_base,
+                   void* k_pool, void* v_pool, void* ab_pool, void* meta,
+                   int32_t num_pages,
+                   const int32_t* page_table, int32_t max_pages_per_seq,
+                   const int32_t* entry_start, int32_t* lengths_out,
+                   int32_t b_begin, int32_t b_end);
+
+int oracle_decode(int q_dtype, int dtype, int32_t H_q, int32_t H_kv, int32_t d,
+                  const void* q,
+                  const void* k_pool, const void* v_pool, const void* ab_pool,
+                  int32_t num_pages,
+                  const int32_t* page_table, int32_t max_pages_per_seq,
+                  const int32_t* lengths, int32_t B,
+                  double* o, double* lse,
+                  int32_t b_begin, int32_t b_end);
+
+uint16_t oracle_bf16_round(double x);
+double oracle_bf16_value(uint16_t bits);
+void oracle_rope(double* y, const double* x, int32_t d, double pos, double base);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
