@@ -1,1 +1,213 @@
-"""SPICY-KV coarse-grained decode for MI355X (placeholder; binding added with the library)."""
+"""SPICY-KV coarse-grained decode for MI355X (gfx950).
+
+Thin Python binding over the C ABI in ``include/spicy.h``: argument
+marshalling only (torch tensors -> device pointers, the current HIP stream).
+Every step of coarsening and decoding runs in the library's HIP kernels
+(``coarse_grained_decode_amd/libspicy.so``, built by
+``python -m coarse_grained_decode_amd.build``).  There is no CPU fallback: if
+the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+__all__ = [
+    "SpicyError", "PagedCache", "spicy_coarsen", "spicy_decode_attn",
+    "spicy_coarsen_workspace_bytes", "spicy_decode_workspace_bytes", "spicy_decode_num_splits",
+    "spicy_status_string", "library_path", "load_library",
+    "SPICY_F32", "SPICY_BF16", "PAGE_SIZE", "WORKSPACE_HEADER",
+    "DEVERR_PAGE_ID", "DEVERR_CAPACITY", "DEVERR_SEGMENTS", "DEVERR_LENGTH",
+]
+
+SPICY_F32 = 0
+SPICY_BF16 = 1
+PAGE_SIZE = 16
+WORKSPACE_HEADER = 256
+DEVERR_PAGE_ID = 0x1
+DEVERR_CAPACITY = 0x2
+DEVERR_SEGMENTS = 0x4
+DEVERR_LENGTH = 0x8
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libspicy.so")
+_lib = None
+
+
+class SpicyError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {spicy_status_string(status)} ({status})")
+
+
+class _Cache(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("ab", ctypes.c_void_p), ("meta", ctypes.c_void_p)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libspicy.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                           "`python -m coarse_grained_decode_amd.build` (hipcc, gfx950)")
+    L = ctypes.CDLL(_LIB_PATH)
+    P, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    CP = ctypes.POINTER(_Cache)
+    L.spicy_status_string.restype = ctypes.c_char_p
+    L.spicy_status_string.argtypes = [ctypes.c_int]
+    L.spicy_coarsen_workspace_bytes.restype = sz
+    L.spicy_coarsen_workspace_bytes.argtypes = [i32, i32, i32]
+    L.spicy_coarsen.restype = ctypes.c_int
+    L.spicy_coarsen.argtypes = [CP, P, P, i32, P, P, P, P, i32, P, i32, ctypes.c_double, P, i32,
+                                P, P, P, sz, P]
+    L.spicy_decode_num_splits.restype = i32
+    L.spicy_decode_num_splits.argtypes = [i32, i32, i32, i32]
+    L.spicy_decode_workspace_bytes.restype = sz
+    L.spicy_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    L.spicy_decode_attn.restype = ctypes.c_int
+    L.spicy_decode_attn.argtypes = [CP, P, i32, P, i32, P, i32, P, P, P, sz, i32, P]
+    _lib = L
+    return L
+
+
+def spicy_status_string(status: int) -> str:
+    return load_library().spicy_status_string(int(status)).decode()
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, torch.Tensor):
+        return t.data_ptr() if t.numel() > 0 else None
+    return int(t)
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        if torch.cuda.is_available():
+            return torch.cuda.current_stream().cuda_stream or None
+        return None
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream or None
+    return int(stream) or None
+
+
+@dataclass
+class PagedCache:
+    """Caller-owned paged compressed cache (device tensors in the library's layout).
+
+    k    [num_pages, H_kv, 16, d]       rotated key rows
+    v    [num_pages, H_kv, d, 16]       dim-major value tiles
+    ab   [num_pages, H_kv, 16, 2]       (alpha, beta)
+    meta [num_pages, H_kv, 16, 4] int32 {kind, mass, pos_sum lo, pos_sum hi} or None
+    """
+    k: torch.Tensor
+    v: torch.Tensor
+    ab: torch.Tensor
+    meta: torch.Tensor | None
+
+    @staticmethod
+    def empty(num_pages: int, H_kv: int, d: int, dtype: torch.dtype, device, meta: bool = True,
+              fill: float | None = None) -> "PagedCache":
+        mk = torch.empty if fill is None else (lambda *s, **kw: torch.full(s, fill, **kw))
+        k = mk(num_pages, H_kv, PAGE_SIZE, d, dtype=dtype, device=device)
+        v = mk(num_pages, H_kv, d, PAGE_SIZE, dtype=dtype, device=device)
+        ab = mk(num_pages, H_kv, PAGE_SIZE, 2, dtype=dtype, device=device)
+        mt = torch.zeros(num_pages, H_kv, PAGE_SIZE, 4, dtype=torch.int32, device=device) if meta else None
+        return PagedCache(k, v, ab, mt)
+
+    @property
+    def num_pages(self) -> int:
+        return int(self.k.shape[0])
+
+    @property
+    def num_kv_heads(self) -> int:
+        return int(self.k.shape[1])
+
+    @property
+    def head_dim(self) -> int:
+        return int(self.k.shape[3])
+
+    @property
+    def dtype_code(self) -> int:
+        if self.k.dtype == torch.bfloat16:
+            return SPICY_BF16
+        if self.k.dtype == torch.float32:
+            return SPICY_F32
+        raise ValueError(f"unsupported cache dtype {self.k.dtype}")
+
+    def struct(self) -> _Cache:
+        return _Cache(self.dtype_code, self.num_kv_heads, self.head_dim, self.num_pages,
+                      _ptr(self.k), _ptr(self.v), _ptr(self.ab), _ptr(self.meta))
+
+
+def spicy_coarsen_workspace_bytes(B: int, n_seg: int, num_kv_heads: int) -> int:
+    return int(load_library().spicy_coarsen_workspace_bytes(B, n_seg, num_kv_heads))
+
+
+def spicy_decode_num_splits(B: int, num_kv_heads: int, max_pages_per_seq: int, num_splits: int = 0) -> int:
+    return int(load_library().spicy_decode_num_splits(B, num_kv_heads, max_pages_per_seq, num_splits))
+
+
+def spicy_decode_workspace_bytes(B: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                                 max_pages_per_seq: int, num_splits: int = 0) -> int:
+    return int(load_library().spicy_decode_workspace_bytes(B, num_q_heads, num_kv_heads, head_dim,
+                                                           max_pages_per_seq, num_splits))
+
+
+def spicy_coarsen(cache: PagedCache, k_pre, v, seq_offsets, pos_base, seg_offsets, seq_seg_ptr,
+                  protected_mask, rope_base: float, page_table, entry_start, lengths_out,
+                  workspace, stream=None, *, total_tokens: int | None = None, n_seg: int | None = None,
+                  B: int | None = None, max_pages_per_seq: int | None = None) -> None:
+    """spicy_coarsen through the C ABI (see include/spicy.h)."""
+    L = load_library()
+    B = int(seq_offsets.shape[0] - 1) if B is None else B
+    n_seg = int(seg_offsets.shape[0] - 1) if n_seg is None else n_seg
+    total_tokens = int(k_pre.shape[0]) if total_tokens is None else total_tokens
+    max_pages = int(page_table.shape[-1]) if max_pages_per_seq is None else max_pages_per_seq
+    st = cache.struct()
+    ws_bytes = workspace.numel() * workspace.element_size() if isinstance(workspace, torch.Tensor) else 0
+    rc = L.spicy_coarsen(ctypes.byref(st), _ptr(k_pre), _ptr(v), total_tokens, _ptr(seq_offsets),
+                         _ptr(pos_base), _ptr(seg_offsets), _ptr(seq_seg_ptr), n_seg, _ptr(protected_mask),
+                         B, float(rope_base), _ptr(page_table), max_pages, _ptr(entry_start),
+                         _ptr(lengths_out), _ptr(workspace), ws_bytes, _stream(stream))
+    if rc != 0:
+        raise SpicyError(rc, "spicy_coarsen")
+
+
+def spicy_decode_attn(cache: PagedCache, q, page_table, lengths, o, lse, workspace,
+                      num_splits: int = 0, stream=None, *, B: int | None = None,
+                      num_q_heads: int | None = None, max_pages_per_seq: int | None = None) -> None:
+    """spicy_decode_attn through the C ABI (see include/spicy.h)."""
+    L = load_library()
+    B = int(q.shape[0]) if B is None else B
+    H_q = int(q.shape[1]) if num_q_heads is None else num_q_heads
+    max_pages = int(page_table.shape[-1]) if max_pages_per_seq is None else max_pages_per_seq
+    st = cache.struct()
+    ws_bytes = workspace.numel() * workspace.element_size() if isinstance(workspace, torch.Tensor) else 0
+    rc = L.spicy_decode_attn(ctypes.byref(st), _ptr(q), H_q, _ptr(page_table), max_pages, _ptr(lengths), B,
+                             _ptr(o), _ptr(lse), _ptr(workspace), ws_bytes, int(num_splits), _stream(stream))
+    if rc != 0:
+        raise SpicyError(rc, "spicy_decode_attn")
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    """A zeroed workspace buffer (the sticky error word starts at zero)."""
+    return torch.zeros((nbytes + 3) // 4, dtype=torch.int32, device=device)
+
+
+def device_error(ws: torch.Tensor) -> int:
+    """Read (synchronously) the sticky device error word of a workspace."""
+    return int(ws[0].item())

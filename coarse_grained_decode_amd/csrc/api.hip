@@ -1,0 +1,175 @@
+// C ABI of the gfx950 SPICY-KV library: host-side validation, workspace
+// carving and launches on the caller's stream.  No allocation, no
+// synchronisation, no global state.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "launch.h"
+#include "spicy.h"
+#include "spicy_device.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int32_t kMaxKvHeads = 64;
+constexpr int32_t kMaxGroup = 16;       // query heads per KV head (MFMA columns)
+constexpr int32_t kTargetWaves = 2048;  // split-K aims for ~2 waves per SIMD
+constexpr int32_t kMinPagesPerSplit = 4;
+constexpr int32_t kMaxSplits = 256;
+constexpr int32_t kMaxGridY = 65535;      // grid y/z extent limit (sequences, heads)
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool head_dim_ok(int32_t d) { return d == 64 || d == 128; }
+
+spicy_status check_cache(const spicy_cache* c) {
+    if (!c) return SPICY_ERR_ARG;
+    if (c->dtype != SPICY_F32 && c->dtype != SPICY_BF16) return SPICY_ERR_ARG;
+    if (c->num_kv_heads < 1 || c->num_pages < 0) return SPICY_ERR_ARG;
+    if (!head_dim_ok(c->head_dim) || c->num_kv_heads > kMaxKvHeads) return SPICY_ERR_UNSUPPORTED;
+    if (c->num_pages > 0 && (!c->k || !c->v || !c->ab)) return SPICY_ERR_ARG;
+    return SPICY_OK;
+}
+
+int32_t ceil_div(int64_t a, int64_t b) { return static_cast<int32_t>((a + b - 1) / b); }
+
+int32_t pages_per_split(int32_t max_pages, int32_t splits) {
+    return std::max<int32_t>(1, ceil_div(max_pages, splits));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* spicy_status_string(spicy_status s) {
+    switch (s) {
+    case SPICY_OK: return "SPICY_OK";
+    case SPICY_ERR_ARG: return "SPICY_ERR_ARG: invalid argument";
+    case SPICY_ERR_RANGE: return "SPICY_ERR_RANGE: size out of range";
+    case SPICY_ERR_CAPACITY: return "SPICY_ERR_CAPACITY: workspace too small";
+    case SPICY_ERR_UNSUPPORTED: return "SPICY_ERR_UNSUPPORTED: unsupported shape";
+    case SPICY_ERR_HIP: return "SPICY_ERR_HIP: kernel launch failed";
+    }
+    return "unknown spicy_status";
+}
+
+size_t spicy_coarsen_workspace_bytes(int32_t B, int32_t n_seg, int32_t num_kv_heads) {
+    if (B < 0 || n_seg < 0 || num_kv_heads < 1) return 0;
+    const size_t ns = static_cast<size_t>(n_seg);
+    const size_t nh = ns * static_cast<size_t>(num_kv_heads);
+    return SPICY_WORKSPACE_HEADER + align_up(4 * ns) + 2 * align_up(4 * nh);
+}
+
+spicy_status spicy_coarsen(const spicy_cache* cache, const void* k_pre, const void* v,
+                           int32_t total_tokens, const int32_t* seq_offsets, const int32_t* pos_base,
+                           const int32_t* seg_offsets, const int32_t* seq_seg_ptr, int32_t n_seg,
+                           const uint8_t* protected_mask, int32_t B, double rope_base,
+                           const int32_t* page_table, int32_t max_pages_per_seq,
+                           const int32_t* entry_start, int32_t* lengths_out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    spicy_status st = check_cache(cache);
+    if (st != SPICY_OK) return st;
+    if (B < 0 || n_seg < 0 || total_tokens < 0) return SPICY_ERR_ARG;
+    if (B > kMaxGridY) return SPICY_ERR_UNSUPPORTED;
+    if (B == 0) return SPICY_OK;
+    if (!seq_offsets || !seg_offsets || !seq_seg_ptr || !page_table || !lengths_out || !workspace)
+        return SPICY_ERR_ARG;
+    if (total_tokens > 0 && (!k_pre || !v || !protected_mask)) return SPICY_ERR_ARG;
+    if (max_pages_per_seq < 1) return SPICY_ERR_ARG;
+    if (cache->num_pages < 1) return SPICY_ERR_RANGE;
+    if (workspace_bytes < spicy_coarsen_workspace_bytes(B, n_seg, cache->num_kv_heads))
+        return SPICY_ERR_CAPACITY;
+
+    spicy::CoarsenArgs a{};
+    a.cache = spicy::CacheArgs{cache->k, cache->v, cache->ab, cache->meta, cache->num_pages, cache->num_kv_heads};
+    a.k_pre = k_pre;
+    a.v = v;
+    a.seq_offsets = seq_offsets;
+    a.pos_base = pos_base;
+    a.seg_offsets = seg_offsets;
+    a.seq_seg_ptr = seq_seg_ptr;
+    a.mask = protected_mask;
+    a.page_table = page_table;
+    a.entry_start = entry_start;
+    a.lengths_out = lengths_out;
+    char* ws = static_cast<char*>(workspace);
+    a.err = reinterpret_cast<int32_t*>(ws);
+    const size_t ns = static_cast<size_t>(n_seg);
+    const size_t nh = ns * static_cast<size_t>(cache->num_kv_heads);
+    a.seg_seq = reinterpret_cast<int32_t*>(ws + SPICY_WORKSPACE_HEADER);
+    a.seg_start = reinterpret_cast<int32_t*>(ws + SPICY_WORKSPACE_HEADER + align_up(4 * ns));
+    a.seg_ncnt = reinterpret_cast<int32_t*>(ws + SPICY_WORKSPACE_HEADER + align_up(4 * ns) + align_up(4 * nh));
+    a.total_tokens = total_tokens;
+    a.n_seg = n_seg;
+    a.B = B;
+    a.max_pages = max_pages_per_seq;
+    a.rope_base = rope_base;
+    return spicy::launch_coarsen(a, cache->dtype, cache->head_dim, static_cast<hipStream_t>(stream));
+}
+
+int32_t spicy_decode_num_splits(int32_t B, int32_t num_kv_heads, int32_t max_pages_per_seq,
+                                int32_t num_splits) {
+    if (max_pages_per_seq < 1) return 1;
+    int32_t s;
+    if (num_splits > 0) {
+        s = std::min(num_splits, max_pages_per_seq);
+    } else {
+        const int64_t units = std::max<int64_t>(1, static_cast<int64_t>(B) * std::max(1, num_kv_heads));
+        s = ceil_div(kTargetWaves, units);
+        s = std::min(s, ceil_div(max_pages_per_seq, kMinPagesPerSplit));
+    }
+    s = std::max(1, std::min(s, kMaxSplits));
+    return ceil_div(max_pages_per_seq, pages_per_split(max_pages_per_seq, s));
+}
+
+size_t spicy_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t max_pages_per_seq, int32_t num_splits) {
+    if (B < 0 || num_q_heads < 1 || head_dim < 1) return 0;
+    const int32_t s = spicy_decode_num_splits(B, num_kv_heads, max_pages_per_seq, num_splits);
+    const size_t rows = static_cast<size_t>(B) * static_cast<size_t>(num_q_heads) * static_cast<size_t>(s);
+    return SPICY_WORKSPACE_HEADER + align_up(rows * 2 * sizeof(float)) +
+           align_up(rows * static_cast<size_t>(head_dim) * sizeof(float));
+}
+
+spicy_status spicy_decode_attn(const spicy_cache* cache, const void* q, int32_t num_q_heads,
+                               const int32_t* page_table, int32_t max_pages_per_seq,
+                               const int32_t* lengths, int32_t B, float* o, float* lse,
+                               void* workspace, size_t workspace_bytes, int32_t num_splits,
+                               void* stream) {
+    spicy_status st = check_cache(cache);
+    if (st != SPICY_OK) return st;
+    if (B < 0 || num_q_heads < 1 || num_splits < 0) return SPICY_ERR_ARG;
+    if (B > kMaxGridY || num_q_heads > kMaxGridY) return SPICY_ERR_UNSUPPORTED;
+    if (num_q_heads % cache->num_kv_heads != 0) return SPICY_ERR_UNSUPPORTED;
+    if (num_q_heads / cache->num_kv_heads > kMaxGroup) return SPICY_ERR_UNSUPPORTED;
+    if (B == 0) return SPICY_OK;
+    if (!q || !page_table || !lengths || !o || !lse || !workspace) return SPICY_ERR_ARG;
+    if (max_pages_per_seq < 1) return SPICY_ERR_ARG;
+    const int32_t splits = spicy_decode_num_splits(B, cache->num_kv_heads, max_pages_per_seq, num_splits);
+    if (workspace_bytes < spicy_decode_workspace_bytes(B, num_q_heads, cache->num_kv_heads, cache->head_dim,
+                                                       max_pages_per_seq, num_splits))
+        return SPICY_ERR_CAPACITY;
+
+    spicy::DecodeArgs a{};
+    a.cache = spicy::CacheArgs{cache->k, cache->v, cache->ab, cache->meta, cache->num_pages, cache->num_kv_heads};
+    a.q = q;
+    a.page_table = page_table;
+    a.lengths = lengths;
+    a.o = o;
+    a.lse = lse;
+    char* ws = static_cast<char*>(workspace);
+    const size_t rows = static_cast<size_t>(B) * static_cast<size_t>(num_q_heads) * static_cast<size_t>(splits);
+    a.err = reinterpret_cast<int32_t*>(ws);
+    a.part_ml = reinterpret_cast<float*>(ws + SPICY_WORKSPACE_HEADER);
+    a.part_o = reinterpret_cast<float*>(ws + SPICY_WORKSPACE_HEADER + align_up(rows * 2 * sizeof(float)));
+    a.B = B;
+    a.H_q = num_q_heads;
+    a.max_pages = max_pages_per_seq;
+    a.splits = splits;
+    a.pages_per_split = pages_per_split(max_pages_per_seq, splits);
+    return spicy::launch_decode(a, cache->dtype, cache->head_dim, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,120 @@
+"""Put a synthetic workload on the GPU and drive it through the C ABI.
+
+Plumbing only: copies the host arrays of a workload to device memory once,
+allocates the paged cache pool and the workspaces, and issues
+spicy_coarsen / spicy_decode_attn calls on the current stream.  Used by the
+tests, the smoke check and the benchmark.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+from . import (PagedCache, spicy_coarsen, spicy_coarsen_workspace_bytes, spicy_decode_attn,
+               spicy_decode_num_splits, spicy_decode_workspace_bytes, workspace)
+from .workloads import CoarsenCall, Workload
+
+
+def _tensor(a: np.ndarray, dtype: str | None, device) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if dtype == "bf16":
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(a).to(device)
+
+
+@dataclass
+class DeviceCall:
+    call: CoarsenCall
+    k: torch.Tensor
+    v: torch.Tensor
+    seq_offsets: torch.Tensor
+    pos_base: torch.Tensor
+    seg_offsets: torch.Tensor
+    seq_seg_ptr: torch.Tensor
+    mask: torch.Tensor
+    page_table: torch.Tensor
+    entry_start: torch.Tensor
+    lengths: torch.Tensor
+    ws: torch.Tensor
+
+    @staticmethod
+    def of(call: CoarsenCall, device) -> "DeviceCall":
+        return DeviceCall(
+            call=call,
+            k=_tensor(call.k, call.dtype, device), v=_tensor(call.v, call.dtype, device),
+            seq_offsets=_tensor(call.seq_offsets, None, device), pos_base=_tensor(call.pos_base, None, device),
+            seg_offsets=_tensor(call.seg_offsets, None, device), seq_seg_ptr=_tensor(call.seq_seg_ptr, None, device),
+            mask=_tensor(call.mask, None, device), page_table=_tensor(call.page_table, None, device),
+            entry_start=_tensor(call.entry_start, None, device),
+            lengths=torch.zeros(call.B, dtype=torch.int32, device=device),
+            ws=workspace(spicy_coarsen_workspace_bytes(call.B, call.n_seg, call.H_kv), device),
+        )
+
+    def run(self, cache: PagedCache, stream=None) -> None:
+        c = self.call
+        spicy_coarsen(cache, self.k, self.v, self.seq_offsets, self.pos_base, self.seg_offsets,
+                      self.seq_seg_ptr, self.mask, c.rope_base, self.page_table, self.entry_start,
+                      self.lengths, self.ws, stream, total_tokens=c.total_tokens, n_seg=c.n_seg, B=c.B,
+                      max_pages_per_seq=c.max_pages)
+
+    @property
+    def input_bytes(self) -> int:
+        return self.k.numel() * self.k.element_size() * 2
+
+
+@dataclass
+class DeviceWorkload:
+    wl: Workload
+    device: torch.device
+    cache: PagedCache
+    setup: List[DeviceCall]
+    step: Optional[DeviceCall]
+    q: torch.Tensor
+    page_table: torch.Tensor
+    o: torch.Tensor
+    lse: torch.Tensor
+    num_splits: int
+    dws: torch.Tensor
+    lengths: torch.Tensor = field(default=None)
+
+    @staticmethod
+    def of(wl: Workload, device="cuda", meta: bool = True, num_splits: int = 0,
+           fill: float | None = float("nan")) -> "DeviceWorkload":
+        device = torch.device(device)
+        tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+        cache = PagedCache.empty(wl.num_pages, wl.H_kv, wl.d, tdt, device, meta=meta, fill=fill)
+        setup = [DeviceCall.of(c, device) for c in wl.setup]
+        step = DeviceCall.of(wl.step, device) if wl.step is not None else None
+        q = _tensor(wl.q, wl.dtype, device)
+        table = _tensor(wl.page_table, None, device)
+        o = torch.empty(wl.B, wl.H_q, wl.d, dtype=torch.float32, device=device)
+        lse = torch.empty(wl.B, wl.H_q, dtype=torch.float32, device=device)
+        dws = workspace(spicy_decode_workspace_bytes(wl.B, wl.H_q, wl.H_kv, wl.d, wl.max_pages, num_splits),
+                        device)
+        return DeviceWorkload(wl, device, cache, setup, step, q, table, o, lse, num_splits, dws)
+
+    def run_setup(self) -> None:
+        for c in self.setup:
+            c.run(self.cache)
+        self.lengths = self.setup[-1].lengths if self.step is None else None
+
+    def run_step_coarsen(self) -> None:
+        if self.step is not None:
+            self.step.run(self.cache)
+            self.lengths = self.step.lengths
+
+    def decode(self) -> None:
+        spicy_decode_attn(self.cache, self.q, self.page_table, self.lengths, self.o, self.lse, self.dws,
+                          self.num_splits)
+
+    def step_once(self) -> None:
+        """One pass of the hot path: coarsen the per-step chunk (if any), then decode."""
+        self.run_step_coarsen()
+        self.decode()
+
+    @property
+    def splits(self) -> int:
+        return spicy_decode_num_splits(self.wl.B, self.wl.H_kv, self.wl.max_pages, self.num_splits)

@@ -1,0 +1,199 @@
+/*
+ * spicy.h — C ABI of the MI355X (gfx950) SPICY-KV coarse-grained decode library.
+ *
+ * Two operations, following the pages' statement of the problem:
+ *
+ *   spicy_coarsen      pre-RoPE keys + values + segment partition + protected
+ *                      mask  ->  paged compressed cache
+ *                      (SPICY-KV demo page, "Patent Pending Notice & Claims",
+ *                      Claim 2: C-points kept exact, F-points merged into
+ *                      macro-nodes with mass-weighted mean key, mean value,
+ *                      conserved mass and centre-of-mass position; Claim 3:
+ *                      scalar sub-grid variance; SPICY-KV abstract, items (1)
+ *                      and (3): pre-RoPE tap, C/F splitting)
+ *
+ *   spicy_decode_attn  query + paged compressed cache -> attention output and
+ *                      log-sum-exp (SPICY-KV demo page, section "2.
+ *                      FlashAttention-2/3 & PagedAttention Online-Softmax
+ *                      Kernel Fusion": logit q.k/sqrt(d_k) + log_mass +
+ *                      |q|^2 * half_inv_dk_sigma_sq inside a standard online
+ *                      softmax; Claim 3 and abstract item (4): first-order
+ *                      log-mass offset and second-order variance closure)
+ *
+ * Conventions for every entry point
+ *   - All buffers are owned and allocated by the caller.  Pointers are DEVICE
+ *     pointers unless the comment says host.  The library allocates nothing,
+ *     keeps no state between calls and never synchronises; work is enqueued on
+ *     the caller's stream (`stream` is a hipStream_t; NULL = default stream).
+ *   - Arguments the host can see (sizes, dtypes, null pointers, workspace
+ *     size) are validated before anything is launched; on error nothing is
+ *     launched and nothing is written.
+ *   - Data that live in device memory (offsets, page ids, lengths, masks) are
+ *     bounds-checked by the kernels themselves: an index outside its buffer is
+ *     never dereferenced; the offending read is skipped (treated as a null
+ *     entry / empty segment) and a bit is OR-ed into the sticky device error
+ *     word at the start of the workspace (see SPICY_DEVERR_*).  The library
+ *     never clears that word: the caller zeroes it (for example with a fill
+ *     kernel) when it allocates the workspace and after reading it.
+ *   - Kernel faults surface at the caller's next synchronisation; a launch
+ *     that fails to enqueue returns SPICY_ERR_HIP.
+ *   - Calls on different streams with disjoint outputs may run concurrently;
+ *     calls that share a workspace must be ordered by the caller.
+ *
+ * Paged compressed cache (caller-allocated pool of `num_pages` pages; one page
+ * holds PAGE_SIZE = 16 consecutive logical entries of one sequence for all KV
+ * heads):
+ *   k    : [num_pages][H_kv][16][d]   entry-major key rows, already rotated
+ *                                     (RoPE) to the entry's position
+ *   v    : [num_pages][H_kv][d][16]   dim-major value tile
+ *   ab   : [num_pages][H_kv][16][2]   per entry (alpha, beta):
+ *                                     alpha = ln(mass), beta = sigma^2/(2d);
+ *                                     a null entry has alpha = -inf
+ *   meta : optional (may be NULL), [num_pages][H_kv][16] x 16 bytes
+ *          { int32 kind; int32 mass; int64 pos_sum; }
+ *          kind 0 = null, 1 = exact C-point, 2 = macro-node; pos_sum is the sum
+ *          of the member positions (anchor = pos_sum / mass).
+ *   Element type of k, v, ab: dtype (SPICY_BF16 or SPICY_F32).
+ *   Logical entry e of sequence b lives in page page_table[b*max_pages + e/16],
+ *   slot e%16.
+ */
+#ifndef SPICY_H
+#define SPICY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SPICY_OK = 0,
+    SPICY_ERR_ARG = 1,          /* null pointer, negative size, bad enum      */
+    SPICY_ERR_RANGE = 2,        /* a host-visible size outside what it indexes */
+    SPICY_ERR_CAPACITY = 3,     /* workspace too small                         */
+    SPICY_ERR_UNSUPPORTED = 4,  /* head_dim not 64/128, GQA group > 16, ...    */
+    SPICY_ERR_HIP = 5           /* a HIP launch failed to enqueue              */
+} spicy_status;
+
+typedef enum { SPICY_F32 = 0, SPICY_BF16 = 1 } spicy_dtype;
+
+/* Sticky device error bits (first int32 of every workspace). */
+#define SPICY_DEVERR_PAGE_ID     0x1  /* page id outside [0, num_pages)          */
+#define SPICY_DEVERR_CAPACITY    0x2  /* entries beyond max_pages_per_seq * 16   */
+#define SPICY_DEVERR_SEGMENTS    0x4  /* segment/sequence offsets inconsistent   */
+#define SPICY_DEVERR_LENGTH      0x8  /* a length < 0                            */
+
+#define SPICY_PAGE_SIZE 16
+#define SPICY_WORKSPACE_HEADER 256   /* bytes before any per-call scratch     */
+
+typedef struct {
+    int32_t dtype;          /* spicy_dtype                                   */
+    int32_t num_kv_heads;   /* H_kv >= 1                                     */
+    int32_t head_dim;       /* d: 64 or 128                                  */
+    int32_t num_pages;      /* pages in the pool                             */
+    void* k;                /* device, see layout above                      */
+    void* v;                /* device                                        */
+    void* ab;               /* device                                        */
+    void* meta;             /* device or NULL                                */
+} spicy_cache;
+
+/* Workspace bytes spicy_coarsen needs for `n_seg` segments over `B`
+ * sequences and `num_kv_heads` heads (header + per segment/head offsets). */
+size_t spicy_coarsen_workspace_bytes(int32_t B, int32_t n_seg, int32_t num_kv_heads);
+
+/* spicy_coarsen — build compressed entries for B sequences.
+ *
+ * Inputs (device):
+ *   k_pre, v        [total_tokens][H_kv][d] in cache->dtype; keys are taken
+ *                   before RoPE (demo page Claim 1 (b), pre-RoPE tap).
+ *   seq_offsets     int32 [B+1]: tokens of sequence b are
+ *                   [seq_offsets[b], seq_offsets[b+1]) of the packed input.
+ *   pos_base        int32 [B] or NULL: absolute position of sequence b's first
+ *                   token (NULL = 0).  Token t of sequence b sits at position
+ *                   pos_base[b] + t - seq_offsets[b].
+ *   seg_offsets     int32 [n_seg+1]: segment s covers packed tokens
+ *                   [seg_offsets[s], seg_offsets[s+1]).
+ *   seq_seg_ptr     int32 [B+1]: segments of sequence b are
+ *                   [seq_seg_ptr[b], seq_seg_ptr[b+1]); they must tile that
+ *                   sequence's tokens in order (an empty segment emits nothing).
+ *   protected_mask  uint8 [total_tokens][H_kv]: non-zero = C-point (kept exact).
+ *   page_table      int32 [B][max_pages_per_seq]: physical page of each
+ *                   logical page; only the pages this call writes are read.
+ *   entry_start     int32 [B] or NULL: first logical entry written for
+ *                   sequence b (NULL = 0).  Entries before it are untouched.
+ * Output:
+ *   Per sequence b and KV head h, segment by segment: if the segment has
+ *   unprotected tokens, one macro-node (key R(tbar)·mean, value mean,
+ *   alpha = ln m, beta = sigma^2/(2d), sigma^2 = per-dimension population
+ *   variance of the member keys, tbar = mean member position); then every
+ *   protected token in position order as an exact entry (key R(p)·k, value v,
+ *   alpha = beta = 0).  Heads with fewer entries are padded with null entries
+ *   to the longest head, and the last page written is padded with nulls to its
+ *   end.  lengths_out[b] (int32, device) = entry_start[b] + the longest head's
+ *   entry count.  RoPE uses the half-split pairing (i, i+d/2) with
+ *   theta_i = rope_base^(-2i/d); rope_base <= 0 means no rotation.  Values are
+ *   accumulated in double precision and rounded once, to nearest-even, on store.
+ * Workspace: device, >= spicy_coarsen_workspace_bytes(B, n_seg, H_kv) bytes,
+ *   first int32 = sticky device error word (not cleared by the library).
+ * Errors: SPICY_ERR_ARG (null required pointer, B < 0, n_seg < 0, bad dtype),
+ *   SPICY_ERR_UNSUPPORTED (head_dim not 64/128, H_kv > 64),
+ *   SPICY_ERR_CAPACITY (workspace too small), SPICY_ERR_HIP. */
+spicy_status spicy_coarsen(const spicy_cache* cache,              /* host struct */
+                           const void* k_pre, const void* v, int32_t total_tokens,
+                           const int32_t* seq_offsets, const int32_t* pos_base,
+                           const int32_t* seg_offsets, const int32_t* seq_seg_ptr,
+                           int32_t n_seg, const uint8_t* protected_mask,
+                           int32_t B, double rope_base,
+                           const int32_t* page_table, int32_t max_pages_per_seq,
+                           const int32_t* entry_start, int32_t* lengths_out,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Split-K plan: how many splits per (sequence, KV head) the decode uses when
+ * asked for `num_splits` (0 = automatic) for a batch of B sequences of at most
+ * max_pages_per_seq pages.  Pure host function. */
+int32_t spicy_decode_num_splits(int32_t B, int32_t num_kv_heads, int32_t max_pages_per_seq,
+                                int32_t num_splits);
+
+/* Workspace bytes spicy_decode_attn needs (header + fp32 partial (m, l, o[d])
+ * per (sequence, query head, split)). */
+size_t spicy_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t max_pages_per_seq,
+                                    int32_t num_splits);
+
+/* spicy_decode_attn — one decode query per sequence over the compressed cache.
+ *
+ * Inputs (device):
+ *   q        [B][num_q_heads][d] in cache->dtype, already RoPE-rotated to the
+ *            query position.  Query head g reads KV head g / (H_q / H_kv).
+ *   lengths  int32 [B]: logical entries of sequence b (null entries inside
+ *            count; they get weight zero).  0 = empty sequence.
+ *   page_table int32 [B][max_pages_per_seq].
+ * Output (device):
+ *   o        float32 [B][num_q_heads][d]: sum_e softmax(s)_e v_e with
+ *            s_e = q.k_e / sqrt(d) + alpha_e + |q|^2 beta_e (|q|^2 of the
+ *            unscaled query).
+ *   lse      float32 [B][num_q_heads]: natural-log log-sum-exp of s; -inf (and
+ *            o = 0) when a sequence has no entry of non-zero weight.
+ * The entries of each (sequence, KV head) are split over up to
+ * spicy_decode_num_splits(...) workgroups of equal page count (split-K); a
+ * second kernel merges the partials by log-sum-exp.
+ * Workspace: device, >= spicy_decode_workspace_bytes(...) with the same
+ *   num_splits; first int32 = sticky device error word.
+ * Errors: SPICY_ERR_ARG, SPICY_ERR_UNSUPPORTED (head_dim not 64/128,
+ *   H_q % H_kv != 0, H_q / H_kv > 16), SPICY_ERR_CAPACITY, SPICY_ERR_HIP. */
+spicy_status spicy_decode_attn(const spicy_cache* cache,          /* host struct */
+                               const void* q, int32_t num_q_heads,
+                               const int32_t* page_table, int32_t max_pages_per_seq,
+                               const int32_t* lengths, int32_t B,
+                               float* o, float* lse,
+                               void* workspace, size_t workspace_bytes,
+                               int32_t num_splits, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* spicy_status_string(spicy_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPICY_H */

@@ -1,0 +1,121 @@
+"""The C ABI on the host: the library loads, exports every function declared in
+include/spicy.h, and rejects bad arguments before launching anything (these
+calls never reach the GPU, so they run anywhere)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import coarse_grained_decode_amd as cgd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spicy.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spicy_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(cgd.library_path()):
+        from coarse_grained_decode_amd import build
+        build.build(verbose=False)
+    return cgd.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert {"spicy_coarsen", "spicy_decode_attn", "spicy_coarsen_workspace_bytes",
+            "spicy_decode_workspace_bytes", "spicy_decode_num_splits", "spicy_status_string"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in range(6):
+        assert cgd.spicy_status_string(code).startswith("SPICY_")
+    assert "unknown" in cgd.spicy_status_string(99)
+
+
+def test_workspace_and_split_plan(lib):
+    # split plan: explicit counts are honoured up to the page count; the
+    # effective count never leaves an empty split
+    assert cgd.spicy_decode_num_splits(1, 1, 10, 4) == 4
+    assert cgd.spicy_decode_num_splits(1, 1, 10, 6) == 5          # 2 pages each
+    assert cgd.spicy_decode_num_splits(1, 1, 3, 100) == 3
+    assert cgd.spicy_decode_num_splits(4, 4, 0, 0) == 1
+    for B, H, P in ((16, 4, 72), (8, 4, 164), (32, 4, 290), (8, 2, 24), (1, 1, 8)):
+        s = cgd.spicy_decode_num_splits(B, H, P, 0)
+        pps = -(-P // s)
+        assert 1 <= s <= P and -(-P // pps) == s
+        assert s * B * H >= min(2048, B * H * -(-P // 4)) // 2
+    n = cgd.spicy_decode_workspace_bytes(16, 28, 4, 128, 72, 8)
+    assert n == 256 + (16 * 28 * 8 * 2 * 4 + 255) // 256 * 256 + (16 * 28 * 8 * 128 * 4 + 255) // 256 * 256
+    assert cgd.spicy_coarsen_workspace_bytes(2, 10, 4) == 256 + 256 + 2 * 256
+    assert cgd.spicy_coarsen_workspace_bytes(-1, 10, 4) == 0
+
+
+def _cache(dtype=1, H=4, d=128, pages=8, k=1, v=1, ab=1):
+    return cgd._Cache(dtype, H, d, pages, k, v, ab, None)
+
+
+def test_decode_rejects_bad_arguments(lib):
+    P = 0x1000  # never dereferenced: validation fails before any launch
+    c = _cache()
+
+    def call(cache=c, q=P, hq=28, table=P, maxp=8, lengths=P, B=2, o=P, lse=P, ws=P, wsb=1 << 30, ns=0):
+        return lib.spicy_decode_attn(ctypes.byref(cache) if cache is not None else None, q, hq, table, maxp,
+                                     lengths, B, o, lse, ws, wsb, ns, None)
+
+    assert call(cache=None) == 1
+    assert call(cache=_cache(dtype=7)) == 1
+    assert call(cache=_cache(d=96)) == 4
+    assert call(cache=_cache(H=65)) == 4
+    assert call(cache=_cache(k=0)) == 1
+    assert call(hq=30) == 4                 # not a multiple of H_kv
+    assert call(hq=4 * 17) == 4             # group of 17 > 16
+    assert call(q=0) == 1
+    assert call(lengths=0) == 1
+    assert call(o=0) == 1
+    assert call(ws=0) == 1
+    assert call(maxp=0) == 1
+    assert call(B=-1) == 1
+    assert call(ns=-2) == 1
+    assert call(wsb=16) == 3
+    assert call(B=0, q=0, table=0) == 0     # nothing to do
+
+
+def test_coarsen_rejects_bad_arguments(lib):
+    P = 0x1000
+    c = _cache()
+
+    def call(cache=c, k=P, v=P, total=100, so=P, pb=P, seg=P, ssp=P, nseg=10, mask=P, B=2, table=P, maxp=8,
+             es=P, lo=P, ws=P, wsb=1 << 30):
+        return lib.spicy_coarsen(ctypes.byref(cache) if cache is not None else None, k, v, total, so, pb, seg,
+                                 ssp, nseg, mask, B, 1e4, table, maxp, es, lo, ws, wsb, None)
+
+    assert call(cache=None) == 1
+    assert call(cache=_cache(d=32)) == 4
+    assert call(k=0) == 1
+    assert call(mask=0) == 1
+    assert call(so=0) == 1
+    assert call(lo=0) == 1
+    assert call(ws=0) == 1
+    assert call(B=-3) == 1
+    assert call(nseg=-1) == 1
+    assert call(total=-1) == 1
+    assert call(maxp=0) == 1
+    assert call(cache=_cache(pages=0)) == 2
+    assert call(wsb=100) == 3
+    assert call(B=0) == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(cgd, "_LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(cgd, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        cgd.load_library()
