@@ -1,0 +1,214 @@
+"""Benchmark: SPICY-KV compressed-KV decode on one MI355X.
+
+One step = one pass of the whole hot path over one batch: spicy_coarsen of the
+batch's fresh chunk into the paged cache (plan + segmented moments + RoPE +
+pack), then spicy_decode_attn of one query token per sequence over the whole
+compressed cache (split-K decode + log-sum-exp combine).
+
+Default workload: the shared-prefix batch (32 sequences sharing one
+65536-token prefix compressed 28.6x, a private exact suffix of U[512, 2048]
+tokens each, and a fresh 8192-token chunk per sequence coarsened every step
+with equal-variation segments), Qwen2-7B head shape (28 query / 4 KV heads,
+d = 128), bf16.  Other workloads: --workload qwen2_7b_layer | long_ragged |
+qwen2_1.5b_layer | tiny_fp32 (those have no per-step coarsen; a step is their
+whole coarsen + decode).
+
+Prints ONE JSON line.  `value` = query tokens per second of whole steps.
+`roofline` describes the step's dominant launch (largest share of the step
+time), `roofline_decode` the decode call; `achieved` = algorithmic bytes per
+call / mean call duration from HIP events recorded on the stream the
+kernels run on.  Inputs are resident in HBM before the timed region.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+ENTRY_EXTRA_META = 16          # bytes of optional metadata per entry-head (not used here)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="shared_prefix")
+    ap.add_argument("--splits", type=int, default=0, help="decode split count (0 = automatic)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-reps", type=int, default=3)
+    return ap.parse_args()
+
+
+def elem_bytes(dtype: str) -> int:
+    return 2 if dtype == "bf16" else 4
+
+
+def coarsen_alg_bytes(call, lengths: np.ndarray) -> int:
+    """Bytes the coarsening must move: read K and V of every token and the
+    mask; write every entry it produces (key row, value column, alpha, beta),
+    null padding included."""
+    eb = elem_bytes(call.dtype)
+    T, H, d = call.total_tokens, call.H_kv, call.d
+    read = T * H * d * 2 * eb + T * H
+    written_entries = 0
+    for b in range(call.B):
+        end = -(-int(lengths[b]) // 16) * 16
+        written_entries += H * (end - int(call.entry_start[b]))
+    write = written_entries * (2 * d + 2) * eb + call.B * 4
+    return read + write
+
+
+def decode_alg_bytes(wl, lengths: np.ndarray) -> int:
+    """Bytes the decode must move: every cache entry it attends to, once per
+    physical slot (the shared prefix is read from HBM once), plus Q, O, LSE."""
+    eb = elem_bytes(wl.dtype)
+    used = {}
+    for b in range(wl.B):
+        L = int(lengths[b])
+        for lp in range(-(-L // 16)):
+            p = int(wl.page_table[b, lp])
+            used[p] = max(used.get(p, 0), min(16, L - 16 * lp))
+    entries = sum(used.values()) * wl.H_kv
+    per_entry = (2 * wl.d + 2) * eb
+    qol = wl.B * wl.H_q * (wl.d * eb + wl.d * 4 + 4)
+    return entries * per_entry + qol
+
+
+def cpu_baseline(wl, reps: int):
+    """The oracle (plain C, double precision) on the host cores: one whole
+    step for every sequence of the batch (the workload's per-step coarsen, then
+    decode), setup calls untimed.  Returns query tokens/s and details."""
+    import oracle
+    threads = oracle.default_threads()
+    cache = oracle.Cache(wl.dtype, wl.num_pages, wl.H_kv, wl.d, fill=False)
+    lengths = None
+    for call in wl.setup:
+        lengths = oracle.coarsen(call, cache, threads=threads)
+    times = []
+    for r in range(reps + 1):
+        t0 = time.perf_counter()
+        if wl.step is not None:
+            lengths = oracle.coarsen(wl.step, cache, threads=threads)
+        oracle.decode(wl.q, wl.dtype, cache, wl.H_q, wl.page_table, lengths, threads=threads)
+        dt = time.perf_counter() - t0
+        if r > 0:
+            times.append(dt)
+        print(f"[bench] cpu oracle step {r}: {dt:.3f} s", file=sys.stderr, flush=True)
+    med = statistics.median(times)
+    return dict(value=wl.B / med, unit="query-tokens/s", cores=threads, kind="oracle",
+                sample=f"one whole step of the same workload ({wl.B} sequences: "
+                       f"{'per-step coarsen + ' if wl.step is not None else ''}decode), "
+                       f"median of {reps} after 1 warm-up, {med:.3f} s per step")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path has no "
+              "multi-GPU leg in this build", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from coarse_grained_decode_amd import workloads as W
+    from coarse_grained_decode_amd.runner import DeviceWorkload
+
+    if args.workload not in W.WORKLOADS:
+        sys.exit(f"unknown workload {args.workload}; choose from {sorted(W.WORKLOADS)}")
+    t_gen = time.perf_counter()
+    wl = W.WORKLOADS[args.workload]()
+    print(f"[bench] generated {wl.name} in {time.perf_counter() - t_gen:.1f} s: {wl.description}",
+          file=sys.stderr, flush=True)
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dw = DeviceWorkload.of(wl, dev, meta=False, num_splits=args.splits, fill=None)
+    dw.run_setup()
+    torch.cuda.synchronize()
+    # a step: the per-step coarsen call if the workload has one, else its whole
+    # coarsen (setup) again, then the decode
+    step_calls = [dw.step] if dw.step is not None else dw.setup
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        for c in step_calls:
+            c.run(dw.cache)
+        if ev is not None:
+            ev[1].record()
+        dw.lengths = step_calls[-1].lengths
+        dw.decode()
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    for c in dw.setup + step_calls:
+        assert int(c.ws[0].item()) == 0, "device error word set"
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    assert int(dw.dws[0].item()) == 0, "device error word set (decode)"
+
+    coarsen_ms = statistics.mean(e[0].elapsed_time(e[1]) for e in evs)
+    decode_ms = statistics.mean(e[1].elapsed_time(e[2]) for e in evs)
+    lengths = dw.lengths.cpu().numpy()
+    cb = sum(coarsen_alg_bytes(c.call, c.lengths.cpu().numpy()) for c in step_calls)
+    db = decode_alg_bytes(wl, lengths)
+
+    def roof(nbytes, ms):
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "alg_bytes_per_call": int(nbytes), "mean_call_us": round(ms * 1e3, 2)}
+
+    r_coarsen = roof(cb, coarsen_ms)
+    r_decode = roof(db, decode_ms)
+    r_coarsen["kernel"] = "spicy_coarsen (coarsen_plan + coarsen_main)"
+    r_decode["kernel"] = "spicy_decode_attn (decode_mfma + combine)"
+    dominant, other = (r_coarsen, r_decode) if coarsen_ms >= decode_ms else (r_decode, r_coarsen)
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    out = {
+        "metric": "compressed-KV decode query-tokens/s and achieved HBM GB/s (% of peak), 1 GPU",
+        "value": round(wl.B * args.steps / elapsed, 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded clustered-Gaussian keys, Gaussian values/queries)",
+        "config": {"workload": wl.name, "description": wl.description, "batch": wl.B,
+                   "num_q_heads": wl.H_q, "num_kv_heads": wl.H_kv, "head_dim": wl.d,
+                   "decode_splits": dw.splits, "cache_entries_per_seq_mean": float(lengths.mean())},
+        "roofline": dominant,
+        "roofline_decode": r_decode,
+        "roofline_other": other,
+        "decode_query_tokens_per_s": round(wl.B / (decode_ms * 1e-3), 1),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_reps)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

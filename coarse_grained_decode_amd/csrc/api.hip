@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdint>
 
 #include "launch.h"
@@ -13,7 +14,7 @@
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr int32_t kMaxKvHeads = 64;
+constexpr int32_t kMaxKvHeads = 16;
 constexpr int32_t kMaxGroup = 16;       // query heads per KV head (MFMA columns)
 constexpr int32_t kTargetWaves = 2048;  // split-K aims for ~2 waves per SIMD
 constexpr int32_t kMinPagesPerSplit = 4;
@@ -59,7 +60,7 @@ size_t spicy_coarsen_workspace_bytes(int32_t B, int32_t n_seg, int32_t num_kv_he
     if (B < 0 || n_seg < 0 || num_kv_heads < 1) return 0;
     const size_t ns = static_cast<size_t>(n_seg);
     const size_t nh = ns * static_cast<size_t>(num_kv_heads);
-    return SPICY_WORKSPACE_HEADER + align_up(4 * ns) + 2 * align_up(4 * nh);
+    return SPICY_WORKSPACE_HEADER + align_up(16 * ns) + align_up(8 * nh);
 }
 
 spicy_status spicy_coarsen(const spicy_cache* cache, const void* k_pre, const void* v,
@@ -97,15 +98,15 @@ spicy_status spicy_coarsen(const spicy_cache* cache, const void* k_pre, const vo
     char* ws = static_cast<char*>(workspace);
     a.err = reinterpret_cast<int32_t*>(ws);
     const size_t ns = static_cast<size_t>(n_seg);
-    const size_t nh = ns * static_cast<size_t>(cache->num_kv_heads);
-    a.seg_seq = reinterpret_cast<int32_t*>(ws + SPICY_WORKSPACE_HEADER);
-    a.seg_start = reinterpret_cast<int32_t*>(ws + SPICY_WORKSPACE_HEADER + align_up(4 * ns));
-    a.seg_ncnt = reinterpret_cast<int32_t*>(ws + SPICY_WORKSPACE_HEADER + align_up(4 * ns) + align_up(4 * nh));
+    a.seg_desc = reinterpret_cast<int4*>(ws + SPICY_WORKSPACE_HEADER);
+    a.seg_head = reinterpret_cast<int2*>(ws + SPICY_WORKSPACE_HEADER + align_up(16 * ns));
     a.total_tokens = total_tokens;
     a.n_seg = n_seg;
     a.B = B;
     a.max_pages = max_pages_per_seq;
     a.rope_base = rope_base;
+    for (int i = 0; i < cache->head_dim / 2; ++i)
+        a.theta[i] = rope_base > 0.0 ? std::pow(rope_base, -2.0 * static_cast<double>(i) / cache->head_dim) : 0.0;
     return spicy::launch_coarsen(a, cache->dtype, cache->head_dim, static_cast<hipStream_t>(stream));
 }
 

@@ -7,21 +7,30 @@
 // beta = sigma^2 / (2d) (sigma^2 = per-dimension population variance of the
 // member keys); protected ("C") tokens stay exact (mass 1, own position).
 //
-// Two kernels:
-//   coarsen_plan  one workgroup per sequence: counts the protected tokens of
-//                 every (segment, head), scans the per-head entry counts into
-//                 entry offsets, writes lengths_out and the null padding.
-//   coarsen_main  one wavefront per segment and pair of KV heads: streams
-//                 the segment's keys and values once (32 lanes per head, each
-//                 lane owning d/64 rotary pairs), accumulates in double
-//                 precision, writes C-points as they pass and the macro-node
-//                 at the end.  The work is bound by reading K and V from HBM.
+// Three kernels:
+//   coarsen_plan  one 1024-thread workgroup per sequence, one thread per
+//                 segment: counts the protected tokens of each (segment,
+//                 head), block-scans the per-head entry counts into entry
+//                 offsets, writes a compact descriptor per segment, the
+//                 sequence's length and its null padding.
+//   coarsen_main  one wavefront per segment and group of KV heads (4 heads at
+//                 d = 128).  A lane owns 8 consecutive dimensions of one head,
+//                 so one 16-byte load per lane reads a whole token row of the
+//                 wave's heads; tokens stream through a register ring.
+//                 F-tokens are accumulated branch-free in double precision
+//                 (mask as a 0/1 weight) and the macro-node is written at the
+//                 segment end.  Bound by reading K and V from HBM.
+//   coarsen_cpoint one workgroup per segment: the segment's protected tokens,
+//                 in position order per head, stored exact; every 16-lane
+//                 group takes its own (token, head) item, so a fully
+//                 protected segment (a recent window, a cluster of landmarks)
+//                 is spread over all the workgroup's lanes.
 //
-// Variance without a second pass: with c the first merged key of the
-// segment, sum (k - mean)^2 = sum (k - c)^2 - (sum k - m c)^2 / m per
-// dimension.  Inputs are bf16 (8 significant bits), so sum k, m c and
-// sum (k - c)^2 are exact in double precision for any realistic segment and a
-// segment of identical keys gives exactly zero.
+// Exactness: inputs are bf16 (8 significant bits).  Sums of bf16 values and
+// of their squares are exact in double precision for any realistic segment,
+// so the mean is one correctly rounded division, as in a sequential sum, and
+// the variance sum (k^2) - (sum k)^2 / m is zero for a segment of identical
+// keys.  Every stored value is rounded once, to nearest-even.
 #include "launch.h"
 #include "spicy_device.h"
 
@@ -29,10 +38,12 @@ namespace spicy {
 
 namespace {
 
-constexpr int kPlanThreads = 256;
-constexpr int kHeadsPerWave = 2;
-constexpr int kLanesPerHead = 32;
-constexpr int kUnroll = 8;
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanWaves = kPlanThreads / kWave;
+constexpr int kMaxH = 16;
+constexpr int kRing = 4;
+constexpr int kResidentBlocks = 1024;   // 4 workgroups of 4 waves per CU
+constexpr int32_t kWindow = 65536;      // tokens per buffer resource (< 4 GiB)
 
 struct Meta {
     int32_t kind;
@@ -40,13 +51,7 @@ struct Meta {
     int64_t pos_sum;
 };
 
-__device__ __forceinline__ int wave_sum(int x) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-    return x;
-}
-
-// Resolve logical entry e of sequence b to (physical page, slot); -1 on error.
+// Resolve logical entry e of sequence b to its physical page; -1 on error.
 __device__ __forceinline__ int32_t entry_page(const CoarsenArgs& a, int b, int64_t e) {
     const int64_t lp = e / kPage;
     if (e < 0 || lp >= a.max_pages) {
@@ -63,8 +68,8 @@ __device__ __forceinline__ int32_t entry_page(const CoarsenArgs& a, int b, int64
 
 template <typename T, int D>
 __device__ void write_null(const CoarsenArgs& a, int b, int h, int64_t e, int elem) {
-    // one thread writes element `elem` of the key row and value column;
-    // element 0 also writes the sidecars and the metadata.
+    // one thread writes element `elem` of the key row and the value column;
+    // element 0 also writes the sidecars and the metadata
     const int32_t P = entry_page(a, b, e);
     if (P < 0) return;
     const int slot = static_cast<int>(e % kPage);
@@ -77,12 +82,73 @@ __device__ void write_null(const CoarsenArgs& a, int b, int h, int64_t e, int el
         T* ab = static_cast<T*>(a.cache.ab);
         ab[(ph * kPage + slot) * 2 + 0] = Elem<T>::from_f32(-__builtin_huge_valf());
         ab[(ph * kPage + slot) * 2 + 1] = Elem<T>::from_f32(0.f);
-        if (a.cache.meta) {
-            Meta* m = static_cast<Meta*>(a.cache.meta);
-            m[ph * kPage + slot] = Meta{0, 0, 0};
-        }
+        if (a.cache.meta) static_cast<Meta*>(a.cache.meta)[ph * kPage + slot] = Meta{0, 0, 0};
     }
 }
+
+// 8 consecutive elements of one row: a 16-byte (bf16) or 32-byte (fp32) load
+template <typename T> struct Row8;
+template <> struct Row8<uint16_t> {
+    uint4 x;
+    __device__ __forceinline__ void load(const uint16_t* p) { x = *reinterpret_cast<const uint4*>(p); }
+    static __device__ __forceinline__ void load_buf(Row8& r, __amdgpu_buffer_rsrc_t rs, uint32_t voff, int soff) {
+        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, static_cast<int>(voff), soff, 0);
+        r.x = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+    __device__ __forceinline__ uint32_t word(int i) const {
+        return (i < 2) ? x.x : (i < 4) ? x.y : (i < 6) ? x.z : x.w;
+    }
+    __device__ __forceinline__ uint16_t raw(int i) const {
+        const uint32_t w = word(i);
+        return static_cast<uint16_t>((i & 1) ? (w >> 16) : (w & 0xFFFFu));
+    }
+    __device__ __forceinline__ double f64(int i) const {
+        const uint32_t w = word(i);
+        const uint32_t bits = (i & 1) ? (w & 0xFFFF0000u) : (w << 16);
+        return static_cast<double>(__uint_as_float(bits));
+    }
+};
+template <> struct Row8<float> {
+    float4 x, y;
+    __device__ __forceinline__ void load(const float* p) {
+        x = *reinterpret_cast<const float4*>(p);
+        y = *reinterpret_cast<const float4*>(p + 4);
+    }
+    static __device__ __forceinline__ void load_buf(Row8& r, __amdgpu_buffer_rsrc_t rs, uint32_t voff, int soff) {
+        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, static_cast<int>(voff), soff, 0);
+        const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(rs, static_cast<int>(voff + 16), soff, 0);
+        r.x = make_float4(__uint_as_float(a[0]), __uint_as_float(a[1]), __uint_as_float(a[2]), __uint_as_float(a[3]));
+        r.y = make_float4(__uint_as_float(b[0]), __uint_as_float(b[1]), __uint_as_float(b[2]), __uint_as_float(b[3]));
+    }
+    __device__ __forceinline__ float raw(int i) const {
+        const float4& q = i < 4 ? x : y;
+        const int j = i & 3;
+        return j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w;
+    }
+    __device__ __forceinline__ double f64(int i) const { return static_cast<double>(raw(i)); }
+};
+
+template <typename T> struct Pack8;
+template <> struct Pack8<uint16_t> {
+    __device__ __forceinline__ static void store(uint16_t* p, const double (&y)[8]) {
+        uint4 o;
+        o.x = f64_to_bf16(y[0]) | (static_cast<uint32_t>(f64_to_bf16(y[1])) << 16);
+        o.y = f64_to_bf16(y[2]) | (static_cast<uint32_t>(f64_to_bf16(y[3])) << 16);
+        o.z = f64_to_bf16(y[4]) | (static_cast<uint32_t>(f64_to_bf16(y[5])) << 16);
+        o.w = f64_to_bf16(y[6]) | (static_cast<uint32_t>(f64_to_bf16(y[7])) << 16);
+        *reinterpret_cast<uint4*>(p) = o;
+    }
+};
+template <> struct Pack8<float> {
+    __device__ __forceinline__ static void store(float* p, const double (&y)[8]) {
+        *reinterpret_cast<float4*>(p) = make_float4(static_cast<float>(y[0]), static_cast<float>(y[1]),
+                                                    static_cast<float>(y[2]), static_cast<float>(y[3]));
+        *reinterpret_cast<float4*>(p + 4) = make_float4(static_cast<float>(y[4]), static_cast<float>(y[5]),
+                                                        static_cast<float>(y[6]), static_cast<float>(y[7]));
+    }
+};
 
 }  // namespace
 
@@ -90,76 +156,148 @@ __device__ void write_null(const CoarsenArgs& a, int b, int h, int64_t e, int el
 
 template <typename T, int D>
 __global__ __launch_bounds__(kPlanThreads) void coarsen_plan_kernel(CoarsenArgs a) {
-    __shared__ int32_t s_total[64];
+    __shared__ int32_t s_wave[kPlanWaves][kMaxH];
+    __shared__ int32_t s_carry[kMaxH];
     __shared__ int32_t s_ok;
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
     const int wave = tid / kWave;
-    const int nwaves = blockDim.x / kWave;
     const int H = a.cache.H;
 
     const int32_t t0 = a.seq_offsets[b], t1 = a.seq_offsets[b + 1];
     const int32_t s0 = a.seq_seg_ptr[b], s1 = a.seq_seg_ptr[b + 1];
     const int32_t e0 = a.entry_start ? a.entry_start[b] : 0;
+    const bool ranges_sane = 0 <= s0 && s0 <= s1 && s1 <= a.n_seg;
     if (tid == 0) {
-        bool ok = 0 <= t0 && t0 <= t1 && t1 <= a.total_tokens && 0 <= s0 && s0 <= s1 &&
-                  s1 <= a.n_seg && e0 >= 0;
+        bool ok = ranges_sane && 0 <= t0 && t0 <= t1 && t1 <= a.total_tokens && e0 >= 0;
         if (ok) ok = a.seg_offsets[s0] == t0 && a.seg_offsets[s1] == t1;
         s_ok = ok;
         if (!ok) {
             raise_err(a.err, SPICY_DEVERR_SEGMENTS);
             a.lengths_out[b] = e0 < 0 ? 0 : e0;
         }
+        if (b == a.B - 1 && a.seq_seg_ptr[a.B] != a.n_seg) raise_err(a.err, SPICY_DEVERR_SEGMENTS);
+        if (b == 0 && a.seq_seg_ptr[0] != 0) raise_err(a.err, SPICY_DEVERR_SEGMENTS);
     }
+    if (tid < kMaxH) s_carry[tid] = 0;
     __syncthreads();
-    if (!s_ok) return;
-
-    // 1. protected-token count and entry count per (segment, head)
-    for (int32_t s = s0 + wave; s < s1; s += nwaves) {
-        int32_t sa = a.seg_offsets[s], sz = a.seg_offsets[s + 1];
-        if (!(t0 <= sa && sa <= sz && sz <= t1)) {
-            if (lane == 0) raise_err(a.err, SPICY_DEVERR_SEGMENTS);
-            sa = sz = t0;                 // treated as empty by both kernels
-        }
-        for (int h = 0; h < H; ++h) {
-            int c = 0;
-            for (int32_t t = sa + lane; t < sz; t += kWave)
-                c += a.mask[static_cast<int64_t>(t) * H + h] != 0;
-            c = wave_sum(c);
-            if (lane == 0) {
-                a.seg_ncnt[static_cast<int64_t>(s) * H + h] = c;
-                a.seg_start[static_cast<int64_t>(s) * H + h] = c + ((sz - sa - c) > 0 ? 1 : 0);
-            }
-        }
-        if (lane == 0) a.seg_seq[s] = b;
+    // segments no valid sequence owns are marked so that coarsen_main skips them
+    if (b == a.B - 1) {
+        const int32_t first = max(a.seq_seg_ptr[a.B], 0);
+        for (int32_t s = first + tid; s < a.n_seg; s += kPlanThreads) a.seg_desc[s] = make_int4(-1, 0, 0, 0);
     }
-    __threadfence_block();
-    __syncthreads();
+    if (b == 0) {
+        const int32_t last = min(a.seq_seg_ptr[0], a.n_seg);
+        for (int32_t s = tid; s < last; s += kPlanThreads) a.seg_desc[s] = make_int4(-1, 0, 0, 0);
+    }
+    if (!s_ok) {
+        if (ranges_sane)
+            for (int32_t s = s0 + tid; s < s1; s += kPlanThreads) a.seg_desc[s] = make_int4(-1, 0, 0, 0);
+        return;
+    }
 
-    // 2. exclusive scan of the counts per head (one wave per head)
-    for (int h = wave; h < H; h += nwaves) {
-        int32_t running = e0;
-        for (int32_t base = s0; base < s1; base += kWave) {
-            const int32_t s = base + lane;
-            const int c = s < s1 ? a.seg_start[static_cast<int64_t>(s) * H + h] : 0;
-            int incl = c;
+    const int32_t pos_off = (a.pos_base ? a.pos_base[b] : 0) - t0;
+    const bool dword_rows = (H % 4) == 0;
+
+    for (int32_t base = s0; base < s1; base += kPlanThreads) {
+        const int32_t s = base + tid;
+        int cnt[kMaxH];
 #pragma unroll
-            for (int o = 1; o < kWave; o <<= 1) {
-                const int y = __shfl_up(incl, o);
-                if (lane >= o) incl += y;
+        for (int h = 0; h < kMaxH; ++h) cnt[h] = 0;
+        int32_t sa = 0, sz = 0;
+        if (s < s1) {
+            sa = a.seg_offsets[s];
+            sz = a.seg_offsets[s + 1];
+            if (!(t0 <= sa && sa <= sz && sz <= t1)) {
+                raise_err(a.err, SPICY_DEVERR_SEGMENTS);
+                sa = sz = t0;
             }
-            if (s < s1) a.seg_start[static_cast<int64_t>(s) * H + h] = running + incl - c;
-            running += __shfl(incl, kWave - 1);
+            // protected tokens per head (mask rows read as dwords when aligned)
+            if (dword_rows && H == 4) {
+                // one dword per token; 16 tokens per round, loads clamped to
+                // the segment so they can all be in flight together
+                for (int32_t tb = sa; tb < sz; tb += 16) {
+                    uint32_t w[16];
+#pragma unroll
+                    for (int u = 0; u < 16; ++u)
+                        w[u] = reinterpret_cast<const uint32_t*>(a.mask)[min(tb + u, sz - 1)];
+#pragma unroll
+                    for (int u = 0; u < 16; ++u) {
+                        const uint32_t x = tb + u < sz ? w[u] : 0u;
+                        cnt[0] += (x & 0xFFu) != 0;
+                        cnt[1] += (x & 0xFF00u) != 0;
+                        cnt[2] += (x & 0xFF0000u) != 0;
+                        cnt[3] += (x & 0xFF000000u) != 0;
+                    }
+                }
+            } else if (dword_rows) {
+                for (int32_t t = sa; t < sz; ++t) {
+                    const uint32_t* row = reinterpret_cast<const uint32_t*>(a.mask + static_cast<int64_t>(t) * H);
+#pragma unroll
+                    for (int q = 0; q < kMaxH / 4; ++q) {
+                        if (4 * q < H) {
+                            const uint32_t w = row[q];
+                            cnt[4 * q + 0] += (w & 0xFFu) != 0;
+                            cnt[4 * q + 1] += (w & 0xFF00u) != 0;
+                            cnt[4 * q + 2] += (w & 0xFF0000u) != 0;
+                            cnt[4 * q + 3] += (w & 0xFF000000u) != 0;
+                        }
+                    }
+                }
+            } else {
+                for (int32_t t = sa; t < sz; ++t) {
+#pragma unroll
+                    for (int h = 0; h < kMaxH; ++h)
+                        if (h < H) cnt[h] += a.mask[static_cast<int64_t>(t) * H + h] != 0;
+                }
+            }
+            a.seg_desc[s] = make_int4(b, sa, sz, pos_off);
         }
-        if (lane == 0) s_total[h] = running - e0;
+        // entries per head: protected tokens + one macro-node if any F-token
+        int c[kMaxH], incl[kMaxH];
+#pragma unroll
+        for (int h = 0; h < kMaxH; ++h) {
+            c[h] = (s < s1 && h < H) ? cnt[h] + ((sz - sa - cnt[h]) > 0 ? 1 : 0) : 0;
+            incl[h] = c[h];
+        }
+        // block-wide inclusive scan per head: within waves, then across waves
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+#pragma unroll
+            for (int h = 0; h < kMaxH; ++h) {
+                if (h < H) {
+                    const int y = __shfl_up(incl[h], o);
+                    if (lane >= o) incl[h] += y;
+                }
+            }
+        }
+        if (lane == kWave - 1)
+            for (int h = 0; h < H; ++h) s_wave[wave][h] = incl[h];
+        __syncthreads();
+        if (s < s1) {
+#pragma unroll
+            for (int h = 0; h < kMaxH; ++h) {
+                if (h < H) {
+                    int before = s_carry[h];
+                    for (int w = 0; w < wave; ++w) before += s_wave[w][h];
+                    a.seg_head[static_cast<int64_t>(s) * H + h] =
+                        make_int2(e0 + before + incl[h] - c[h], (sz - sa - cnt[h]) > 0 ? 1 : 0);
+                }
+            }
+        }
+        __syncthreads();
+        if (tid < H) {
+            int tot = 0;
+            for (int w = 0; w < kPlanWaves; ++w) tot += s_wave[w][tid];
+            s_carry[tid] += tot;
+        }
+        __syncthreads();
     }
-    __threadfence_block();
-    __syncthreads();
 
-    // 3. length and null padding
+    // length and null padding
     int32_t most = 0;
-    for (int h = 0; h < H; ++h) most = max(most, s_total[h]);
+    for (int h = 0; h < H; ++h) most = max(most, s_carry[h]);
     const int64_t len = static_cast<int64_t>(e0) + most;
     const int64_t padded = (len + kPage - 1) / kPage * kPage;
     if (tid == 0) {
@@ -167,213 +305,397 @@ __global__ __launch_bounds__(kPlanThreads) void coarsen_plan_kernel(CoarsenArgs 
         if (padded / kPage > a.max_pages) raise_err(a.err, SPICY_DEVERR_CAPACITY);
     }
     for (int h = 0; h < H; ++h) {
-        const int64_t first = static_cast<int64_t>(e0) + s_total[h];
+        const int64_t first = static_cast<int64_t>(e0) + s_carry[h];
         const int64_t n = (padded - first) * D;
-        for (int64_t i = tid; i < n; i += blockDim.x)
+        for (int64_t i = tid; i < n; i += kPlanThreads)
             write_null<T, D>(a, b, h, first + i / D, static_cast<int>(i % D));
     }
 }
 
-// ------------------------------------------------------------------- main
+// ---------------------------------------------------------- main + C-points
+
+// Lane layout shared by coarsen_main and coarsen_cpoint: one wavefront covers
+// HW heads of one token; lane (hl, j) owns dims 8j .. 8j+7 of head hl.  RoPE
+// pairs dims (i, i + D/2), held by lanes j and j + PARTNER.
+template <typename T, int D>
+struct Lanes {
+    static constexpr int LPH = D / 8;         // lanes per head
+    static constexpr int HW = kWave / LPH;    // heads per wavefront
+    static constexpr int PARTNER = LPH / 2;   // lane distance to the rotary partner
+    int lane, hl, j, h, hh, hbase, d0;
+    bool active, hi_half, rotate;
+    double theta[4];                          // the 4 frequencies this lane evaluates
+
+    __device__ __forceinline__ Lanes(const CoarsenArgs& a) {
+        lane = threadIdx.x % kWave;
+        hl = lane / LPH;
+        j = lane % LPH;
+        hbase = blockIdx.y * HW;
+        h = hbase + hl;
+        active = h < a.cache.H;
+        hh = active ? h : 0;
+        hi_half = j >= PARTNER;
+        d0 = 8 * j;
+        rotate = a.rope_base > 0.0;
+        const int pair0 = 8 * (hi_half ? j - PARTNER : j) + (hi_half ? 4 : 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            theta[r] = a.theta[pair0 + r];
+    }
+
+    // Rotate this lane's 8 key values to position pos (all lanes of the wave
+    // must call it together: it exchanges sin/cos and partner values).  One
+    // rotary pair index q at a time, to keep few double-precision values live.
+    template <typename GetX>
+    __device__ __forceinline__ void rope(const GetX& x, double pos, double (&y)[8]) const {
+        if (!rotate) {
+#pragma unroll
+            for (int r = 0; r < 8; ++r) y[r] = x(r);
+            return;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            double sq, cq;
+            sincos_f64(pos * theta[q], &sq, &cq);          // angle of index (hi ? 4 : 0) + q
+            const double oc = __shfl_xor(cq, PARTNER);      // angle of index (hi ? 0 : 4) + q
+            const double os = __shfl_xor(sq, PARTNER);
+            const double xa = x(q), xb = x(4 + q);
+            const double pa = __shfl_xor(xa, PARTNER), pb = __shfl_xor(xb, PARTNER);
+            const double ca = hi_half ? oc : cq, sa_ = hi_half ? os : sq;   // index q
+            const double cb = hi_half ? cq : oc, sb = hi_half ? sq : os;    // index 4 + q
+            y[q] = hi_half ? xa * ca + pa * sa_ : xa * ca - pa * sa_;
+            y[4 + q] = hi_half ? xb * cb + pb * sb : xb * cb - pb * sb;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+};
+
+// Write entry e of sequence b for this lane's head: key row slice (already
+// rotated), value column slice (rounded from vals, or copied bit for bit from
+// vraw), and, from the head's first lane, alpha/beta and the metadata.
+template <typename T, int D, typename VSrc>
+__device__ __forceinline__ void store_entry(const CoarsenArgs& a, const Lanes<T, D>& L, int b, int64_t e,
+                                            const double (&y)[8], const VSrc& vsrc, double alpha,
+                                            double beta, int32_t kind, int32_t mass, int64_t ps) {
+    const int32_t Pg = entry_page(a, b, e);
+    if (Pg < 0) return;
+    const int slot = static_cast<int>(e % kPage);
+    const int64_t ph = static_cast<int64_t>(Pg) * a.cache.H + L.h;
+    Pack8<T>::store(static_cast<T*>(a.cache.k) + (ph * kPage + slot) * D + L.d0, y);
+    T* vcol = static_cast<T*>(a.cache.v) + (ph * D + L.d0) * kPage + slot;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) vcol[r * kPage] = vsrc(r);
+    if (L.j == 0) {
+        T* abc = static_cast<T*>(a.cache.ab);
+        abc[(ph * kPage + slot) * 2 + 0] = Elem<T>::from_f64(alpha);
+        abc[(ph * kPage + slot) * 2 + 1] = Elem<T>::from_f64(beta);
+        if (a.cache.meta) static_cast<Meta*>(a.cache.meta)[ph * kPage + slot] = Meta{kind, mass, ps};
+    }
+}
+
+// coarsen_main: stream one segment's tokens and write its macro-node.
+template <typename T, int D>
+__device__ __forceinline__ void coarsen_segment(const CoarsenArgs& a, const Lanes<T, D>& L, int32_t s) {
+    const int H = a.cache.H;
+    const int4 desc = a.seg_desc[s];
+    const int2 head = a.seg_head[static_cast<int64_t>(s) * H + L.hh];
+    // the descriptor is the same for the whole wave: keep it in scalar registers
+    const int32_t b = __builtin_amdgcn_readfirstlane(desc.x);
+    const int32_t sa = __builtin_amdgcn_readfirstlane(desc.y);
+    const int32_t sz = __builtin_amdgcn_readfirstlane(desc.z);
+    const int64_t pos_off = __builtin_amdgcn_readfirstlane(desc.w);
+    if (b < 0 || b >= a.B || !(0 <= sa && sa < sz && sz <= a.total_tokens)) return;
+    const T* kin = static_cast<const T*>(a.k_pre);
+    const T* vin = static_cast<const T*>(a.v);
+
+    // masked sums of the F-tokens, double-buffered: block B (kRing tokens)
+    // is in flight while block A is accumulated and vice versa.  Rows are read
+    // through buffer resources spanning the segment (rebased every kWindow
+    // tokens): the per-token offset is a scalar, and reads past the segment's
+    // end return zeros, which add nothing to the sums.
+    double sk[8], sq[8], sv[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) sk[r] = sq[r] = sv[r] = 0.0;
+    int32_t m = 0;
+    int64_t psum = 0;
+    struct Block {
+        Row8<T> k[kRing], v[kRing];
+        uint8_t mk[kRing];
+    };
+    Block A, Bk;
+    constexpr uint32_t kRow = static_cast<uint32_t>(D * sizeof(T));      // one head's row
+    const uint32_t tok_bytes = static_cast<uint32_t>(H) * kRow;
+    const uint32_t lane_off = static_cast<uint32_t>(L.hh) * kRow + static_cast<uint32_t>(L.d0 * sizeof(T));
+    for (int32_t w0 = sa; w0 < sz; w0 += kWindow) {
+        const int32_t wn = min(sz - w0, kWindow);
+        const int64_t row0 = static_cast<int64_t>(w0) * H;
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kin + row0 * D, static_cast<uint32_t>(wn) * tok_bytes);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vin + row0 * D, static_cast<uint32_t>(wn) * tok_bytes);
+        const __amdgpu_buffer_rsrc_t rm = make_rsrc(a.mask + row0, static_cast<uint32_t>(wn * H));
+        auto fetch = [&](Block& X, int32_t u0) {
+#pragma unroll
+            for (int u = 0; u < kRing; ++u) {
+                const int so = (u0 + u) * static_cast<int>(tok_bytes);
+                Row8<T>::load_buf(X.k[u], rk, lane_off, so);
+                Row8<T>::load_buf(X.v[u], rv, lane_off, so);
+                X.mk[u] = __builtin_amdgcn_raw_buffer_load_b8(rm, L.hh, (u0 + u) * H, 0);
+            }
+        };
+        auto accumulate = [&](const Block& X, int32_t u0) {
+            const int nvalid = min(kRing, wn - u0);
+#pragma unroll
+            for (int u = 0; u < kRing; ++u) {
+                const bool take = (u < nvalid) && !X.mk[u];
+                const double w = take ? 1.0 : 0.0;
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const double x = X.k[u].f64(r);
+                    const double xw = x * w;
+                    sk[r] += xw;
+                    sq[r] = fma(xw, x, sq[r]);
+                    sv[r] = fma(X.v[u].f64(r), w, sv[r]);
+                }
+                m += take ? 1 : 0;
+                psum += take ? static_cast<int64_t>(w0) + u0 + u + pos_off : 0;
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        fetch(A, 0);
+        fetch(Bk, kRing);
+        for (int32_t u0 = 0; u0 < wn; u0 += 2 * kRing) {
+            accumulate(A, u0);
+            fetch(A, u0 + 2 * kRing);
+            accumulate(Bk, u0 + kRing);
+            fetch(Bk, u0 + 3 * kRing);
+        }
+    }
+
+    // the macro-node (all lanes take part in the shuffles)
+    const double md = m > 0 ? static_cast<double>(m) : 1.0;
+    double part = 0.0;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) part += sq[r] - sk[r] * sk[r] / md;
+#pragma unroll
+    for (int o = 1; o < Lanes<T, D>::LPH; o <<= 1) part += __shfl_xor(part, o);
+    const bool mine = L.active && head.y && m > 0;
+    if (!__any(mine)) return;
+    double y[8];
+    L.rope([&](int r) { return sk[r] / md; }, static_cast<double>(psum) / md, y);
+    if (!mine) return;
+    const double sigma2 = (part > 0.0 ? part : 0.0) / (md * D);
+    store_entry(a, L, b, head.x, y, [&](int r) { return Elem<T>::from_f64(sv[r] / md); }, log(md),
+                sigma2 / (2.0 * D), 2, m, psum);
+}
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void coarsen_main_kernel(CoarsenArgs a) {
-    constexpr int P = D / (2 * kLanesPerHead);   // rotary pairs per lane
-    constexpr int HALF = D / 2;
-    typedef T vecP __attribute__((ext_vector_type(P)));
+    const int wave = threadIdx.x / kWave;
+    const Lanes<T, D> L(a);
+    // persistent: wave w of the grid takes segments w, w + W, w + 2W, ...
+    const int32_t stride = gridDim.x * (blockDim.x / kWave);
+    for (int32_t s = blockIdx.x * (blockDim.x / kWave) + wave; s < a.n_seg; s += stride)
+        coarsen_segment<T, D>(a, L, s);
+}
 
+// coarsen_cpoint: the protected tokens of one segment, stored exact after the
+// segment's macro-node in position order per head, by one whole workgroup.
+// For each 64-token block the protected (token, head) items are
+// enumerated head by head in position order, so an item's index within its
+// head is its rank; each group of LPH lanes stores one item (4 items per
+// wavefront step at d = 128) and the next step's rows are prefetched.
+template <typename T, int D>
+__device__ __forceinline__ void cpoint_segment(const CoarsenArgs& a, int32_t s) {
+    constexpr int LPH = D / 8;
+    constexpr int HW = kWave / LPH;           // heads per wavefront (and items per step)
+    constexpr int PARTNER = LPH / 2;
+    const int H = a.cache.H;
+    const int4 desc = a.seg_desc[s];
+    const int32_t b = desc.x, sa = desc.y, sz = desc.z;
+    if (b < 0 || b >= a.B || !(0 <= sa && sa < sz && sz <= a.total_tokens)) return;
     const int lane = threadIdx.x % kWave;
     const int wave = threadIdx.x / kWave;
-    const int32_t s = blockIdx.x * (blockDim.x / kWave) + wave;
-    if (s >= a.n_seg) return;
-    const int H = a.cache.H;
-    const int hs = lane / kLanesPerHead;
-    const int ql = lane % kLanesPerHead;
-    const int h = blockIdx.y * kHeadsPerWave + hs;
-    const bool active = h < H;
-
-    // which sequence owns this segment; give up on anything inconsistent
-    // (the same checks the plan kernel made, so that a segment is only
-    // processed when its plan entries were written by this call)
-    const int32_t b = a.seg_seq[s];
-    if (b < 0 || b >= a.B) return;
-    const int32_t s0 = a.seq_seg_ptr[b], s1 = a.seq_seg_ptr[b + 1];
-    if (!(0 <= s0 && s0 <= s && s < s1 && s1 <= a.n_seg)) return;
-    const int32_t t0 = a.seq_offsets[b], t1 = a.seq_offsets[b + 1];
-    if (!(0 <= t0 && t0 <= t1 && t1 <= a.total_tokens)) return;
-    if (a.seg_offsets[s0] != t0 || a.seg_offsets[s1] != t1) return;
-    if (a.entry_start && a.entry_start[b] < 0) return;
-    const int32_t sa = a.seg_offsets[s], sz = a.seg_offsets[s + 1];
-    if (!(t0 <= sa && sa <= sz && sz <= t1)) return;
-    const int64_t pos0 = a.pos_base ? a.pos_base[b] : 0;
-
-    const int hh = active ? h : 0;
-    const int32_t start = a.seg_start[static_cast<int64_t>(s) * H + hh];
-    const int32_t ncnt = a.seg_ncnt[static_cast<int64_t>(s) * H + hh];
-    const int hasF = (sz - sa - ncnt) > 0 ? 1 : 0;
-
-    // frequencies of this lane's rotary pairs
-    double theta[P];
-    const bool rotate = a.rope_base > 0.0;
-#pragma unroll
-    for (int i = 0; i < P; ++i) {
-        const int pair = P * ql + i;
-        theta[i] = rotate ? pow(a.rope_base, -2.0 * static_cast<double>(pair) / static_cast<double>(D)) : 0.0;
-    }
-
+    const int nwaves = blockDim.x / kWave;
+    const int hbase = blockIdx.y * HW;
+    const int grp = lane / LPH;
+    const int j = lane % LPH;
+    const bool hi_half = j >= PARTNER;
+    const int d0 = 8 * j;
+    const int64_t pos_off = desc.w;
     const T* kin = static_cast<const T*>(a.k_pre);
     const T* vin = static_cast<const T*>(a.v);
-    T* kc = static_cast<T*>(a.cache.k);
-    T* vc = static_cast<T*>(a.cache.v);
-    T* abc = static_cast<T*>(a.cache.ab);
-    Meta* meta = static_cast<Meta*>(a.cache.meta);
+    const bool rotate = a.rope_base > 0.0;
+    bool have_theta = false;
+    double theta[4];
 
-    double sk[2 * P], sv[2 * P], qk[2 * P];
+    int32_t running[HW];                      // C-points of each head in earlier blocks
 #pragma unroll
-    for (int i = 0; i < 2 * P; ++i) sk[i] = sv[i] = qk[i] = 0.0;
-    vecP shift_lo = {}, shift_hi = {};
-    int32_t m = 0;
-    int64_t pos_sum = 0;
-    int32_t rank = 0;
+    for (int q = 0; q < HW; ++q) running[q] = 0;
 
-    auto rotate_store = [&](const double (&x)[2 * P], double pos, int64_t e, int32_t kind,
-                            int32_t mass, int64_t psum, double alpha, double beta,
-                            const T (&vraw)[2 * P], const double (&vmean)[2 * P], bool raw_v) {
-        const int32_t Pg = entry_page(a, b, e);
-        if (Pg < 0) return;
-        const int slot = static_cast<int>(e % kPage);
-        const int64_t ph = static_cast<int64_t>(Pg) * H + h;
-        vecP lo, hi;
+    for (int32_t blk = sa; blk < sz; blk += kWave) {
+        // which of the group's heads protect token blk + lane
+        const int32_t t = blk + lane;
+        uint32_t bits = 0;
+        if (t < sz) {
+            const uint8_t* row = a.mask + static_cast<int64_t>(t) * H + hbase;
+            if (H % 4 == 0 && hbase + HW <= H) {
 #pragma unroll
-        for (int i = 0; i < P; ++i) {
-            double yl = x[i], yh = x[P + i];
+                for (int q = 0; q < HW / 4; ++q) {
+                    const uint32_t w = reinterpret_cast<const uint32_t*>(row)[q];
+#pragma unroll
+                    for (int y = 0; y < 4; ++y)
+                        if ((w >> (8 * y)) & 0xFFu) bits |= 1u << (4 * q + y);
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < HW; ++q)
+                    if (hbase + q < H && row[q]) bits |= 1u << q;
+            }
+        }
+        uint64_t hb[HW];
+        int pre[HW + 1];
+        pre[0] = 0;
+#pragma unroll
+        for (int q = 0; q < HW; ++q) {
+            hb[q] = __ballot((bits >> q) & 1u);
+            pre[q + 1] = pre[q] + __popcll(hb[q]);
+        }
+        const int n = pre[HW];
+        if (n > 0 && !have_theta) {
+            const int pair0 = 8 * (hi_half ? j - PARTNER : j) + (hi_half ? 4 : 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                theta[r] = a.theta[pair0 + r];
+            have_theta = true;
+        }
+
+        // item p -> (head q, token tc, entry e); invalid items read a valid row
+        auto locate = [&](int p, int& q, int32_t& tc, int64_t& e, bool& valid) {
+            valid = p < n;
+            const int pp = valid ? p : 0;
+            q = 0;
+#pragma unroll
+            for (int y = 1; y < HW; ++y) q += (pp >= pre[y]) ? 1 : 0;
+            uint64_t m = 0;
+            int before = 0, rk = 0;
+#pragma unroll
+            for (int y = 0; y < HW; ++y)
+                if (y == q) { m = hb[y]; before = pre[y]; rk = running[y]; }
+            for (int k = pp - before; k > 0; --k) m &= m - 1;
+            tc = valid ? blk + __ffsll(static_cast<unsigned long long>(m)) - 1 : sa;
+            const int h = min(hbase + q, H - 1);
+            const int2 hd = a.seg_head[static_cast<int64_t>(s) * H + h];
+            e = static_cast<int64_t>(hd.x) + hd.y + rk + (pp - before);
+        };
+        auto load_rows = [&](int q, int32_t tc, Row8<T>& kx, Row8<T>& vx) {
+            const int h = min(hbase + q, H - 1);
+            const int64_t base = (static_cast<int64_t>(tc) * H + h) * D + d0;
+            kx.load(kin + base);
+            vx.load(vin + base);
+        };
+
+        const int steps = (n + HW - 1) / HW;
+        int q0;
+        int32_t tc0;
+        int64_t e0;
+        bool v0;
+        Row8<T> k0, vv0;
+        int st = wave;
+        if (st < steps) {
+            locate(st * HW + grp, q0, tc0, e0, v0);
+            load_rows(q0, tc0, k0, vv0);
+        }
+        for (; st < steps; st += nwaves) {
+            // prefetch this wave's next step
+            int q1 = 0;
+            int32_t tc1 = sa;
+            int64_t e1 = 0;
+            bool v1 = false;
+            Row8<T> k1, vv1;
+            if (st + nwaves < steps) {
+                locate((st + nwaves) * HW + grp, q1, tc1, e1, v1);
+                load_rows(q1, tc1, k1, vv1);
+            }
+            double x[8], y[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) x[r] = k0.f64(r);
+            const double pos = static_cast<double>(tc0 + pos_off);
             if (rotate) {
-                double sn, cs;
-                sincos(pos * theta[i], &sn, &cs);
-                yl = x[i] * cs - x[P + i] * sn;
-                yh = x[P + i] * cs + x[i] * sn;
-            }
-            lo[i] = Elem<T>::from_f64(yl);
-            hi[i] = Elem<T>::from_f64(yh);
-        }
-        T* krow = kc + (ph * kPage + slot) * D;
-        *reinterpret_cast<vecP*>(krow + P * ql) = lo;
-        *reinterpret_cast<vecP*>(krow + HALF + P * ql) = hi;
-        T* vcol = vc + ph * D * kPage + slot;
+                double c4[4], s4[4], cs[8], sn[8];
 #pragma unroll
-        for (int i = 0; i < P; ++i) {
-            vcol[(P * ql + i) * kPage] = raw_v ? vraw[i] : Elem<T>::from_f64(vmean[i]);
-            vcol[(HALF + P * ql + i) * kPage] = raw_v ? vraw[P + i] : Elem<T>::from_f64(vmean[P + i]);
-        }
-        if (ql == 0) {
-            abc[(ph * kPage + slot) * 2 + 0] = Elem<T>::from_f64(alpha);
-            abc[(ph * kPage + slot) * 2 + 1] = Elem<T>::from_f64(beta);
-            if (meta) meta[ph * kPage + slot] = Meta{kind, mass, psum};
-        }
-    };
-
-    for (int32_t tb = sa; tb < sz; tb += kUnroll) {
-        vecP klo[kUnroll], khi[kUnroll], vlo[kUnroll], vhi[kUnroll];
-        uint8_t msk[kUnroll];
+                for (int r = 0; r < 4; ++r) sincos_f64(pos * theta[r], &s4[r], &c4[r]);
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int32_t t = tb + u;
-            if (active && t < sz) {
-                const int64_t base = (static_cast<int64_t>(t) * H + h) * D;
-                klo[u] = *reinterpret_cast<const vecP*>(kin + base + P * ql);
-                khi[u] = *reinterpret_cast<const vecP*>(kin + base + HALF + P * ql);
-                vlo[u] = *reinterpret_cast<const vecP*>(vin + base + P * ql);
-                vhi[u] = *reinterpret_cast<const vecP*>(vin + base + HALF + P * ql);
-                msk[u] = a.mask[static_cast<int64_t>(t) * H + h];
-            } else {
-                msk[u] = 0;
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int32_t t = tb + u;
-            if (!(active && t < sz)) continue;
-            const int64_t pos = pos0 + (t - t0);
-            double x[2 * P];
-            T vr[2 * P];
-#pragma unroll
-            for (int i = 0; i < P; ++i) {
-                x[i] = Elem<T>::to_f64(klo[u][i]);
-                x[P + i] = Elem<T>::to_f64(khi[u][i]);
-                vr[i] = vlo[u][i];
-                vr[P + i] = vhi[u][i];
-            }
-            if (msk[u]) {
-                // C-point: exact entry after the macro-node of this segment
-                const int64_t e = static_cast<int64_t>(start) + hasF + rank;
-                ++rank;
-                rotate_store(x, static_cast<double>(pos), e, 1, 1, pos, 0.0, 0.0, vr, sv, true);
-            } else {
-                ++m;
-                pos_sum += pos;
-                if (m == 1) {
-                    shift_lo = klo[u];
-                    shift_hi = khi[u];
+                for (int r = 0; r < 4; ++r) {
+                    const double oc = __shfl_xor(c4[r], PARTNER);
+                    const double os = __shfl_xor(s4[r], PARTNER);
+                    cs[r] = hi_half ? oc : c4[r];
+                    sn[r] = hi_half ? os : s4[r];
+                    cs[4 + r] = hi_half ? c4[r] : oc;
+                    sn[4 + r] = hi_half ? s4[r] : os;
                 }
 #pragma unroll
-                for (int i = 0; i < 2 * P; ++i) {
-                    sk[i] += x[i];
-                    const double c = Elem<T>::to_f64(i < P ? shift_lo[i] : shift_hi[i - P]);
-                    const double dd = x[i] - c;
-                    qk[i] += dd * dd;
-                    sv[i] += Elem<T>::to_f64(vr[i]);
+                for (int r = 0; r < 8; ++r) {
+                    const double other = __shfl_xor(x[r], PARTNER);
+                    y[r] = hi_half ? x[r] * cs[r] + other * sn[r] : x[r] * cs[r] - other * sn[r];
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 8; ++r) y[r] = x[r];
+            }
+            if (v0) {
+                const int h = hbase + q0;
+                const int32_t Pg = entry_page(a, b, e0);
+                if (Pg >= 0) {
+                    const int slot = static_cast<int>(e0 % kPage);
+                    const int64_t ph = static_cast<int64_t>(Pg) * H + h;
+                    Pack8<T>::store(static_cast<T*>(a.cache.k) + (ph * kPage + slot) * D + d0, y);
+                    T* vcol = static_cast<T*>(a.cache.v) + (ph * D + d0) * kPage + slot;
+#pragma unroll
+                    for (int r = 0; r < 8; ++r) vcol[r * kPage] = vv0.raw(r);
+                    if (j == 0) {
+                        T* abc = static_cast<T*>(a.cache.ab);
+                        abc[(ph * kPage + slot) * 2 + 0] = Elem<T>::from_f32(0.f);
+                        abc[(ph * kPage + slot) * 2 + 1] = Elem<T>::from_f32(0.f);
+                        const int64_t p = tc0 + pos_off;
+                        if (a.cache.meta) static_cast<Meta*>(a.cache.meta)[ph * kPage + slot] = Meta{1, 1, p};
+                    }
                 }
             }
+            q0 = q1; tc0 = tc1; e0 = e1; v0 = v1; k0 = k1; vv0 = vv1;
         }
+#pragma unroll
+        for (int q = 0; q < HW; ++q) running[q] += pre[q + 1] - pre[q];
     }
+}
 
-    // variance of the merged keys: per lane sum_i (Q_i - D_i^2/m) with
-    // D_i = sum k_i - m c_i, then over the lanes of the head
-    double part = 0.0;
-    if (active && m > 0) {
-#pragma unroll
-        for (int i = 0; i < 2 * P; ++i) {
-            const double c = Elem<T>::to_f64(i < P ? shift_lo[i] : shift_hi[i - P]);
-            const double dsum = sk[i] - static_cast<double>(m) * c;
-            part += qk[i] - dsum * dsum / static_cast<double>(m);
-        }
-    }
-#pragma unroll
-    for (int o = 1; o < kLanesPerHead; o <<= 1) part += __shfl_xor(part, o);
-
-    if (active && m > 0) {
-        double mean_k[2 * P], mean_v[2 * P];
-#pragma unroll
-        for (int i = 0; i < 2 * P; ++i) {
-            mean_k[i] = sk[i] / static_cast<double>(m);
-            mean_v[i] = sv[i] / static_cast<double>(m);
-        }
-        const double sigma2 = (part > 0.0 ? part : 0.0) / (static_cast<double>(m) * D);
-        const double tbar = static_cast<double>(pos_sum) / static_cast<double>(m);
-        T unused[2 * P];
-        rotate_store(mean_k, tbar, start, 2, m, pos_sum, log(static_cast<double>(m)),
-                     sigma2 / (2.0 * D), unused, mean_v, false);
-    }
+template <typename T, int D>
+__global__ __launch_bounds__(256) void coarsen_cpoint_kernel(CoarsenArgs a) {
+    // persistent: workgroup g takes segments g, g + G, g + 2G, ...
+    for (int32_t s = blockIdx.x; s < a.n_seg; s += gridDim.x) cpoint_segment<T, D>(a, s);
 }
 
 // ------------------------------------------------------------------ launch
 
 template <typename T, int D>
 static spicy_status launch_coarsen_t(const CoarsenArgs& a, hipStream_t stream) {
-    if (a.B > 0) {
-        hipLaunchKernelGGL((coarsen_plan_kernel<T, D>), dim3(a.B), dim3(kPlanThreads), 0, stream, a);
-        if (hipGetLastError() != hipSuccess) return SPICY_ERR_HIP;
-    }
+    constexpr int HW = kWave / (D / 8);
+    hipLaunchKernelGGL((coarsen_plan_kernel<T, D>), dim3(a.B), dim3(kPlanThreads), 0, stream, a);
+    if (hipGetLastError() != hipSuccess) return SPICY_ERR_HIP;
     if (a.n_seg > 0) {
+        // persistent grids: at most kResidentBlocks workgroups per head group
         const int wpb = 4;
-        dim3 grid((a.n_seg + wpb - 1) / wpb, (a.cache.H + kHeadsPerWave - 1) / kHeadsPerWave);
+        const int nblk = min((a.n_seg + wpb - 1) / wpb, kResidentBlocks);
+        dim3 grid(nblk, (a.cache.H + HW - 1) / HW);
         hipLaunchKernelGGL((coarsen_main_kernel<T, D>), grid, dim3(wpb * kWave), 0, stream, a);
+        if (hipGetLastError() != hipSuccess) return SPICY_ERR_HIP;
+        dim3 cgrid(min(a.n_seg, kResidentBlocks), (a.cache.H + HW - 1) / HW);
+        hipLaunchKernelGGL((coarsen_cpoint_kernel<T, D>), cgrid, dim3(256), 0, stream, a);
         if (hipGetLastError() != hipSuccess) return SPICY_ERR_HIP;
     }
     return SPICY_OK;
 }
 
 spicy_status launch_coarsen(const CoarsenArgs& a, int dtype, int D, hipStream_t stream) {
+    if (a.B == 0) return SPICY_OK;
     if (dtype == SPICY_BF16) {
         return D == 128 ? launch_coarsen_t<uint16_t, 128>(a, stream) : launch_coarsen_t<uint16_t, 64>(a, stream);
     }

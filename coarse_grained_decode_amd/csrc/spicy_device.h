@@ -25,37 +25,63 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
     return static_cast<uint16_t>(u >> 16);
 }
 
-// binary64 -> bfloat16 in a single nearest-even rounding, on the bit pattern:
-// bfloat16 keeps 8 significant bits and the binary32 exponent range, so the
-// result is the 64-bit significand shifted to the bf16 spacing with a sticky
-// round-half-even on the bits shifted out.
+// binary64 -> bfloat16 in a single nearest-even rounding.  The double is
+// first rounded to binary32 "to odd" (truncate, then set the last bit if
+// anything was lost), then binary32 -> bfloat16 rounds to nearest-even.
+// Because binary32 keeps at least two more bits than bfloat16, the two steps
+// give exactly the nearest-even bfloat16 of the double (Boldo & Melquiond,
+// rounding to odd).  The truncation is recovered from the hardware's
+// nearest-even conversion: if it rounded away from zero, step one unit back.
 __device__ __forceinline__ uint16_t f64_to_bf16(double x) {
-    const uint64_t u = static_cast<uint64_t>(__double_as_longlong(x));
-    const uint16_t sign = static_cast<uint16_t>((u >> 48) & 0x8000u);
-    const uint64_t a = u & 0x7FFFFFFFFFFFFFFFull;
-    if (a > 0x7FF0000000000000ull) return 0x7FC0;                      // NaN
-    if (a == 0x7FF0000000000000ull) return sign | 0x7F80;              // inf
-    if (a == 0) return sign;
-    int be = static_cast<int>(a >> 52);
-    uint64_t mant = a & 0x000FFFFFFFFFFFFFull;
-    if (be != 0) mant |= 0x0010000000000000ull; else be = 1;           // subnormal double
-    const int E = be - 1023;                                           // exponent of bit 52
-    const int lsb = (E < -126 ? -126 : E) - 7;                         // bf16 spacing
-    const int sh = lsb - (be - 1075);                                  // >= 45
-    uint64_t q;
-    if (sh >= 54) {
-        q = 0;                                                         // below half the spacing
-    } else {
-        q = mant >> sh;
-        const uint64_t rem = mant & ((1ull << sh) - 1);
-        const uint64_t half = 1ull << (sh - 1);
-        if (rem > half || (rem == half && (q & 1))) ++q;
+    if (x != x) return 0x7FC0;                                         // NaN
+    const float f = static_cast<float>(x);
+    uint32_t u = __float_as_uint(f);
+    const double d = static_cast<double>(f);
+    if (d != x) {
+        if (fabs(d) > fabs(x)) u -= 1u;                                // toward zero
+        u |= 1u;                                                       // sticky
     }
-    if (E < -126) return sign | static_cast<uint16_t>(q);            // subnormal (q==128: min normal)
-    int Eo = E;
-    if (q == 256) { q = 128; ++Eo; }
-    if (Eo > 127) return sign | 0x7F80;
-    return sign | static_cast<uint16_t>(((Eo + 127) << 7) | (q & 0x7F));
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+// sin and cos of a double-precision angle, accurate to a few units in the
+// last place for |x| up to ~1e9.  Cody-Waite reduction by pi/2 with pi/2 split
+// into two 32-bit pieces and a double tail (each product with the quadrant
+// number is exact for |k| < 2^21), then Taylor series of sin and cos on
+// |r| <= pi/4 up to r^17 / r^16 (the first omitted terms are below 1e-17).
+__device__ __forceinline__ void sincos_f64(double x, double* s, double* c) {
+    constexpr double kTwoOverPi = 0.6366197723675814;
+    constexpr double kPio2Hi = 1.5707963267341256;      // first 32 bits of pi/2
+    constexpr double kPio2Mid = 6.077100506303966e-11;  // next 32 bits
+    constexpr double kPio2Lo = 2.0222662487959506e-21;  // the rest
+    const double k = rint(x * kTwoOverPi);
+    const double r = ((x - k * kPio2Hi) - k * kPio2Mid) - k * kPio2Lo;
+    const double z = r * r;
+    // 1/n! for n = 3, 5, ..., 17 and n = 2, 4, ..., 16
+    double ps = 1.0 / 355687428096000.0;                 // 1/17!
+    ps = fma(ps, z, -1.0 / 1307674368000.0);             // 1/15!
+    ps = fma(ps, z, 1.0 / 6227020800.0);                 // 1/13!
+    ps = fma(ps, z, -1.0 / 39916800.0);                  // 1/11!
+    ps = fma(ps, z, 1.0 / 362880.0);                     // 1/9!
+    ps = fma(ps, z, -1.0 / 5040.0);                      // 1/7!
+    ps = fma(ps, z, 1.0 / 120.0);                        // 1/5!
+    ps = fma(ps, z, -1.0 / 6.0);                         // 1/3!
+    const double sr = fma(r * z, ps, r);
+    double pc = 1.0 / 20922789888000.0;                  // 1/16!
+    pc = fma(pc, z, -1.0 / 87178291200.0);               // 1/14!
+    pc = fma(pc, z, 1.0 / 479001600.0);                  // 1/12!
+    pc = fma(pc, z, -1.0 / 3628800.0);                   // 1/10!
+    pc = fma(pc, z, 1.0 / 40320.0);                      // 1/8!
+    pc = fma(pc, z, -1.0 / 720.0);                       // 1/6!
+    pc = fma(pc, z, 1.0 / 24.0);                         // 1/4!
+    pc = fma(pc, z, -0.5);                               // 1/2!
+    const double cr = fma(z, pc, 1.0);
+    const int q = static_cast<int>(static_cast<long long>(k) & 3);
+    const double ss = (q & 1) ? cr : sr;
+    const double cc = (q & 1) ? sr : cr;
+    *s = (q & 2) ? -ss : ss;
+    *c = ((q + 1) & 2) ? -cc : cc;
 }
 
 template <typename T> struct Elem;
@@ -71,6 +97,15 @@ template <> struct Elem<float> {
     static __device__ __forceinline__ float from_f64(double x) { return static_cast<float>(x); }
     static __device__ __forceinline__ float from_f32(float x) { return x; }
 };
+
+// ------------------------------------------------------------ buffer loads
+
+// Raw buffer resource over `bytes` bytes at p: loads at offsets >= bytes
+// return zero instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), static_cast<short>(0),
+                                             static_cast<int>(bytes), 0x00020000);
+}
 
 // --------------------------------------------------------- error reporting
 
@@ -102,14 +137,14 @@ struct CoarsenArgs {
     const int32_t* entry_start;
     int32_t* lengths_out;
     int32_t* err;          // workspace header word
-    int32_t* seg_seq;      // [n_seg]           owning sequence of each segment
-    int32_t* seg_start;    // [n_seg][H]        first entry of the segment per head
-    int32_t* seg_ncnt;     // [n_seg][H]        protected tokens of the segment per head
+    int4* seg_desc;        // [n_seg]     {sequence (-1 = skip), first token, end token, position offset}
+    int2* seg_head;        // [n_seg][H]  {first entry of the segment, has a macro-node}
     int32_t total_tokens;
     int32_t n_seg;
     int32_t B;
     int32_t max_pages;
     double rope_base;
+    double theta[64];      // rotary frequencies rope_base^(-2i/d), i < d/2 (host libm pow)
 };
 
 struct DecodeArgs {
