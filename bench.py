@@ -46,6 +46,10 @@ def parse():
     ap.add_argument("--splits", type=int, default=0, help="decode split count (0 = automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--decode-only", action="store_true",
+                    help="diagnostic: time spicy_decode_attn alone over rotated copies of the cache")
+    ap.add_argument("--rotate-bytes", type=float, default=1.5e9,
+                    help="decode-only: total bytes of distinct cache copies rotated through")
     return ap.parse_args()
 
 
@@ -111,6 +115,41 @@ def cpu_baseline(wl, reps: int):
                        f"median of {reps} after 1 warm-up, {med:.3f} s per step")
 
 
+def decode_only(args, wl, dw):
+    """Diagnostic mode: the decode call alone.  The compressed cache is
+    copied into L distinct buffers (L x cache bytes >= --rotate-bytes, well
+    above the 256 MB Infinity Cache) and the calls rotate through them, so
+    every call streams its cache from HBM."""
+    import torch
+    from coarse_grained_decode_amd import PagedCache, spicy_decode_attn
+    if dw.step is not None:
+        for c in [dw.step]:
+            c.run(dw.cache)
+        dw.lengths = dw.step.lengths
+    torch.cuda.synchronize()
+    lengths = dw.lengths.cpu().numpy()
+    cache_bytes = sum(t.numel() * t.element_size() for t in (dw.cache.k, dw.cache.v, dw.cache.ab))
+    L = max(1, int(np.ceil(args.rotate_bytes / cache_bytes)))
+    copies = [PagedCache(dw.cache.k.clone(), dw.cache.v.clone(), dw.cache.ab.clone(), None) for _ in range(L)]
+    for i in range(args.warmup * L):
+        spicy_decode_attn(copies[i % L], dw.q, dw.page_table, dw.lengths, dw.o, dw.lse, dw.dws, dw.num_splits)
+    torch.cuda.synchronize()
+    n = args.steps * L
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(n):
+        spicy_decode_attn(copies[i % L], dw.q, dw.page_table, dw.lengths, dw.o, dw.lse, dw.dws, dw.num_splits)
+    ev1.record()
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / n
+    db = decode_alg_bytes(wl, lengths)
+    gbs = db / (us * 1e-6) / 1e9
+    print(json.dumps({"mode": "decode-only", "workload": wl.name, "calls": n, "layers_rotated": L,
+                      "cache_bytes": int(cache_bytes), "alg_bytes_per_call": int(db), "mean_call_us": round(us, 2),
+                      "achieved_GBps": round(gbs, 1), "frac_of_8TBps": round(gbs / HBM_PEAK_GBS, 4),
+                      "query_tokens_per_s": round(wl.B / (us * 1e-6), 1), "decode_splits": dw.splits}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -149,6 +188,9 @@ def main():
         dw.decode()
         if ev is not None:
             ev[2].record()
+
+    if args.decode_only:
+        return decode_only(args, wl, dw)
 
     for _ in range(args.warmup):
         step()

@@ -18,6 +18,8 @@ constexpr int32_t kMaxKvHeads = 16;
 constexpr int32_t kMaxGroup = 16;       // query heads per KV head (MFMA columns)
 constexpr int32_t kTargetWaves = 2048;  // split-K aims for ~2 waves per SIMD
 constexpr int32_t kMinPagesPerSplit = 4;
+constexpr int32_t kPagesInFlight = 4;     // decode pipeline depth (pages per wavefront)
+constexpr int32_t kMaxResidentWaves = 4096;
 constexpr int32_t kMaxSplits = 256;
 constexpr int32_t kMaxGridY = 65535;      // grid y/z extent limit (sequences, heads)
 
@@ -117,9 +119,16 @@ int32_t spicy_decode_num_splits(int32_t B, int32_t num_kv_heads, int32_t max_pag
     if (num_splits > 0) {
         s = std::min(num_splits, max_pages_per_seq);
     } else {
+        // Prefer splits short enough that a wavefront issues all its pages'
+        // loads at once (kPagesInFlight); otherwise aim for ~2 waves per SIMD.
         const int64_t units = std::max<int64_t>(1, static_cast<int64_t>(B) * std::max(1, num_kv_heads));
-        s = ceil_div(kTargetWaves, units);
-        s = std::min(s, ceil_div(max_pages_per_seq, kMinPagesPerSplit));
+        const int32_t full = ceil_div(max_pages_per_seq, kPagesInFlight);
+        if (units * full <= kMaxResidentWaves) {
+            s = full;
+        } else {
+            s = ceil_div(kTargetWaves, units);
+            s = std::min(s, ceil_div(max_pages_per_seq, kMinPagesPerSplit));
+        }
     }
     s = std::max(1, std::min(s, kMaxSplits));
     return ceil_div(max_pages_per_seq, pages_per_split(max_pages_per_seq, s));
@@ -163,8 +172,10 @@ spicy_status spicy_decode_attn(const spicy_cache* cache, const void* q, int32_t 
     char* ws = static_cast<char*>(workspace);
     const size_t rows = static_cast<size_t>(B) * static_cast<size_t>(num_q_heads) * static_cast<size_t>(splits);
     a.err = reinterpret_cast<int32_t*>(ws);
-    a.part_ml = reinterpret_cast<float*>(ws + SPICY_WORKSPACE_HEADER);
-    a.part_o = reinterpret_cast<float*>(ws + SPICY_WORKSPACE_HEADER + align_up(rows * 2 * sizeof(float)));
+    size_t off = SPICY_WORKSPACE_HEADER;
+    a.part_ml = reinterpret_cast<float*>(ws + off);
+    off += align_up(rows * 2 * sizeof(float));
+    a.part_o = reinterpret_cast<float*>(ws + off);
     a.B = B;
     a.H_q = num_q_heads;
     a.max_pages = max_pages_per_seq;

@@ -120,14 +120,25 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     const uint16_t* abpool = static_cast<const uint16_t*>(a.cache.ab);
     const int32_t* table = a.page_table + static_cast<int64_t>(b) * a.max_pages;
 
-    auto load = [&](PageRegs<D>& r, int32_t lp) {
-        const int32_t pid = table[lp];
-        r.ok = pid >= 0 && pid < a.cache.num_pages;
-        if (!r.ok) {
-            raise_err(a.err, SPICY_DEVERR_PAGE_ID);
-            return;
+    // Page ids of the split, 64 at a time: one vector load, then each page's
+    // id is read out of its lane (uniform).  Pages past the split's end and
+    // invalid ids load a valid page (so that every load is unconditional and
+    // each wait covers exactly one page); they are skipped when processed.
+    int32_t ids = 0;
+    int32_t ids_base = -kWave;
+    auto page_id = [&](int32_t lp) {
+        const int32_t q = min(lp, p1 - 1);
+        if (q - ids_base >= kWave) {            // uniform
+            ids_base = q;
+            ids = (q + lane < p1) ? table[q + lane] : 0;
         }
-        const int64_t ph = static_cast<int64_t>(pid) * H + h;
+        return __builtin_amdgcn_readlane(ids, q - ids_base);
+    };
+    auto load = [&](PageRegs<D>& r, int32_t lp) {
+        const int32_t pid = page_id(lp);
+        r.ok = pid >= 0 && pid < a.cache.num_pages;
+        if (!r.ok) raise_err(a.err, SPICY_DEVERR_PAGE_ID);
+        const int64_t ph = static_cast<int64_t>(r.ok ? pid : 0) * H + h;
         const uint16_t* kp = kpool + ph * kPage * D + row * D + 8 * grp;
 #pragma unroll
         for (int i = 0; i < KC; ++i) r.k[i] = *reinterpret_cast<const bf16x8*>(kp + 32 * i);
@@ -194,15 +205,12 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
 
     PageRegs<D> buf[NBUF];
 #pragma unroll
-    for (int i = 0; i < NBUF; ++i)
-        if (p0 + i < p1) load(buf[i], p0 + i);
+    for (int i = 0; i < NBUF; ++i) load(buf[i], p0 + i);
     for (int32_t lp = p0; lp < p1; lp += NBUF) {
 #pragma unroll
         for (int i = 0; i < NBUF; ++i) {
-            if (lp + i < p1) {
-                process(buf[i], lp + i);
-                if (lp + i + NBUF < p1) load(buf[i], lp + i + NBUF);
-            }
+            if (lp + i < p1) process(buf[i], lp + i);
+            load(buf[i], lp + i + NBUF);
         }
     }
 
@@ -319,9 +327,12 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
 
 // ----------------------------------------------------------------- combine
 
+// One wavefront per (sequence, query head): merge the splits by log-sum-exp.
+// Loads of kChunk splits are issued together; lanes own D/64 dimensions.
 template <int D>
 __global__ __launch_bounds__(64) void combine_kernel(DecodeArgs a) {
     constexpr int DL = D / kWave;
+    constexpr int kChunk = 16;
     const int lane = threadIdx.x;
     const int hq = blockIdx.x;
     const int b = blockIdx.y;
@@ -340,28 +351,36 @@ __global__ __launch_bounds__(64) void combine_kernel(DecodeArgs a) {
     float acc[DL];
 #pragma unroll
     for (int j = 0; j < DL; ++j) acc[j] = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-        const float w = fast_exp2(a.part_ml[2 * (base + s)] - msub);
-        L += w * a.part_ml[2 * (base + s) + 1];
+    for (int s0 = 0; s0 < nsplit; s0 += kChunk) {
+        float w[kChunk], l[kChunk], ov[kChunk][DL];
 #pragma unroll
-        for (int j = 0; j < DL; ++j) acc[j] += w * a.part_o[(base + s) * D + lane + kWave * j];
+        for (int u = 0; u < kChunk; ++u) {
+            const int s = min(s0 + u, nsplit - 1);
+            w[u] = a.part_ml[2 * (base + s)];
+            l[u] = a.part_ml[2 * (base + s) + 1];
+#pragma unroll
+            for (int j = 0; j < DL; ++j) ov[u][j] = a.part_o[(base + s) * D + lane + kWave * j];
+        }
+#pragma unroll
+        for (int u = 0; u < kChunk; ++u) {
+            const float wu = (s0 + u < nsplit) ? fast_exp2(w[u] - msub) : 0.f;
+            L += wu * l[u];
+#pragma unroll
+            for (int j = 0; j < DL; ++j) acc[j] += wu * ov[u][j];
+        }
     }
     float* orow = a.o + (static_cast<int64_t>(b) * a.H_q + hq) * D;
-    if (L > 0.f) {
-        const float inv = 1.f / L;
+    const bool live = L > 0.f;
+    const float inv = live ? 1.f / L : 0.f;
 #pragma unroll
-        for (int j = 0; j < DL; ++j) orow[lane + kWave * j] = acc[j] * inv;
-        if (lane == 0) a.lse[static_cast<int64_t>(b) * a.H_q + hq] = (msub + __log2f(L)) * kLn2;
-    } else {
-#pragma unroll
-        for (int j = 0; j < DL; ++j) orow[lane + kWave * j] = 0.f;
-        if (lane == 0) a.lse[static_cast<int64_t>(b) * a.H_q + hq] = -__builtin_huge_valf();
-    }
+    for (int j = 0; j < DL; ++j) orow[lane + kWave * j] = live ? acc[j] * inv : 0.f;
+    if (lane == 0)
+        a.lse[static_cast<int64_t>(b) * a.H_q + hq] = live ? (msub + __log2f(L)) * kLn2 : -__builtin_huge_valf();
 }
 
 // ------------------------------------------------------------------ launch
 
-constexpr int kNbuf = 2;
+constexpr int kNbuf = 4;
 
 template <int D>
 static spicy_status launch_decode_t(const DecodeArgs& a, int dtype, hipStream_t stream) {

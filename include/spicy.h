@@ -176,7 +176,7 @@ size_t spicy_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t num_
  *   lse      float32 [B][num_q_heads]: natural-log log-sum-exp of s; -inf (and
  *            o = 0) when a sequence has no entry of non-zero weight.
  * The entries of each (sequence, KV head) are split over up to
- * spicy_decode_num_splits(...) workgroups of equal page count (split-K); a
+ * spicy_decode_num_splits(...) wavefronts of equal page count (split-K); a
  * second kernel merges the partials by log-sum-exp.
  * Workspace: device, >= spicy_decode_workspace_bytes(...) with the same
  *   num_splits; first int32 = sticky device error word.
