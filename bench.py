@@ -50,6 +50,8 @@ def parse():
                     help="diagnostic: time spicy_decode_attn alone over rotated copies of the cache")
     ap.add_argument("--rotate-bytes", type=float, default=1.5e9,
                     help="decode-only: total bytes of distinct cache copies rotated through")
+    ap.add_argument("--no-shared-prefix", action="store_true",
+                    help="decode a shared-prefix batch with spicy_decode_attn (every page per sequence)")
     return ap.parse_args()
 
 
@@ -121,7 +123,7 @@ def decode_only(args, wl, dw):
     above the 256 MB Infinity Cache) and the calls rotate through them, so
     every call streams its cache from HBM."""
     import torch
-    from coarse_grained_decode_amd import PagedCache, spicy_decode_attn
+    from coarse_grained_decode_amd import PagedCache
     if dw.step is not None:
         for c in [dw.step]:
             c.run(dw.cache)
@@ -132,13 +134,13 @@ def decode_only(args, wl, dw):
     L = max(1, int(np.ceil(args.rotate_bytes / cache_bytes)))
     copies = [PagedCache(dw.cache.k.clone(), dw.cache.v.clone(), dw.cache.ab.clone(), None) for _ in range(L)]
     for i in range(args.warmup * L):
-        spicy_decode_attn(copies[i % L], dw.q, dw.page_table, dw.lengths, dw.o, dw.lse, dw.dws, dw.num_splits)
+        dw.decode(copies[i % L])
     torch.cuda.synchronize()
     n = args.steps * L
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record()
     for i in range(n):
-        spicy_decode_attn(copies[i % L], dw.q, dw.page_table, dw.lengths, dw.o, dw.lse, dw.dws, dw.num_splits)
+        dw.decode(copies[i % L])
     ev1.record()
     torch.cuda.synchronize()
     us = ev0.elapsed_time(ev1) * 1e3 / n
@@ -147,7 +149,8 @@ def decode_only(args, wl, dw):
     print(json.dumps({"mode": "decode-only", "workload": wl.name, "calls": n, "layers_rotated": L,
                       "cache_bytes": int(cache_bytes), "alg_bytes_per_call": int(db), "mean_call_us": round(us, 2),
                       "achieved_GBps": round(gbs, 1), "frac_of_8TBps": round(gbs / HBM_PEAK_GBS, 4),
-                      "query_tokens_per_s": round(wl.B / (us * 1e-6), 1), "decode_splits": dw.splits}), flush=True)
+                      "query_tokens_per_s": round(wl.B / (us * 1e-6), 1), "decode_splits": dw.splits,
+                      "shared_prefix_pages": dw.shared_prefix_pages}), flush=True)
 
 
 def main():
@@ -170,7 +173,8 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    dw = DeviceWorkload.of(wl, dev, meta=False, num_splits=args.splits, fill=None)
+    dw = DeviceWorkload.of(wl, dev, meta=False, num_splits=args.splits, fill=None,
+                           use_shared_prefix=not args.no_shared_prefix)
     dw.run_setup()
     torch.cuda.synchronize()
     # a step: the per-step coarsen call if the workload has one, else its whole
@@ -222,7 +226,8 @@ def main():
     r_coarsen = roof(cb, coarsen_ms)
     r_decode = roof(db, decode_ms)
     r_coarsen["kernel"] = "spicy_coarsen (coarsen_plan + coarsen_main)"
-    r_decode["kernel"] = "spicy_decode_attn (decode_mfma + combine)"
+    r_decode["kernel"] = ("spicy_decode_attn_shared" if dw.shared_prefix_pages else "spicy_decode_attn") + \
+        " (decode_mfma + combine)"
     dominant, other = (r_coarsen, r_decode) if coarsen_ms >= decode_ms else (r_decode, r_coarsen)
 
     ms_per_step = elapsed * 1e3 / args.steps
@@ -241,7 +246,8 @@ def main():
         "data": "synthetic (seeded clustered-Gaussian keys, Gaussian values/queries)",
         "config": {"workload": wl.name, "description": wl.description, "batch": wl.B,
                    "num_q_heads": wl.H_q, "num_kv_heads": wl.H_kv, "head_dim": wl.d,
-                   "decode_splits": dw.splits, "cache_entries_per_seq_mean": float(lengths.mean())},
+                   "decode_splits": dw.splits, "shared_prefix_pages": dw.shared_prefix_pages,
+                   "cache_entries_per_seq_mean": float(lengths.mean())},
         "roofline": dominant,
         "roofline_decode": r_decode,
         "roofline_other": other,

@@ -18,6 +18,7 @@ import torch
 __all__ = [
     "SpicyError", "PagedCache", "spicy_coarsen", "spicy_decode_attn",
     "spicy_coarsen_workspace_bytes", "spicy_decode_workspace_bytes", "spicy_decode_num_splits",
+    "spicy_decode_attn_shared", "spicy_decode_shared_workspace_bytes",
     "spicy_status_string", "library_path", "load_library",
     "SPICY_F32", "SPICY_BF16", "PAGE_SIZE", "WORKSPACE_HEADER",
     "DEVERR_PAGE_ID", "DEVERR_CAPACITY", "DEVERR_SEGMENTS", "DEVERR_LENGTH",
@@ -78,6 +79,10 @@ def load_library():
     L.spicy_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     L.spicy_decode_attn.restype = ctypes.c_int
     L.spicy_decode_attn.argtypes = [CP, P, i32, P, i32, P, i32, P, P, P, sz, i32, P]
+    L.spicy_decode_shared_workspace_bytes.restype = sz
+    L.spicy_decode_shared_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    L.spicy_decode_attn_shared.restype = ctypes.c_int
+    L.spicy_decode_attn_shared.argtypes = [CP, P, i32, P, i32, P, i32, i32, P, P, P, sz, i32, P]
     _lib = L
     return L
 
@@ -201,6 +206,31 @@ def spicy_decode_attn(cache: PagedCache, q, page_table, lengths, o, lse, workspa
                              _ptr(o), _ptr(lse), _ptr(workspace), ws_bytes, int(num_splits), _stream(stream))
     if rc != 0:
         raise SpicyError(rc, "spicy_decode_attn")
+
+
+def spicy_decode_shared_workspace_bytes(B: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                                        max_pages_per_seq: int, shared_prefix_pages: int,
+                                        num_splits: int = 0) -> int:
+    return int(load_library().spicy_decode_shared_workspace_bytes(B, num_q_heads, num_kv_heads, head_dim,
+                                                                  max_pages_per_seq, shared_prefix_pages,
+                                                                  num_splits))
+
+
+def spicy_decode_attn_shared(cache: PagedCache, q, page_table, lengths, shared_prefix_pages: int, o, lse,
+                             workspace, num_splits: int = 0, stream=None, *, B: int | None = None,
+                             num_q_heads: int | None = None, max_pages_per_seq: int | None = None) -> None:
+    """spicy_decode_attn_shared through the C ABI (see include/spicy.h)."""
+    L = load_library()
+    B = int(q.shape[0]) if B is None else B
+    H_q = int(q.shape[1]) if num_q_heads is None else num_q_heads
+    max_pages = int(page_table.shape[-1]) if max_pages_per_seq is None else max_pages_per_seq
+    st = cache.struct()
+    ws_bytes = workspace.numel() * workspace.element_size() if isinstance(workspace, torch.Tensor) else 0
+    rc = L.spicy_decode_attn_shared(ctypes.byref(st), _ptr(q), H_q, _ptr(page_table), max_pages,
+                                    _ptr(lengths), B, int(shared_prefix_pages), _ptr(o), _ptr(lse),
+                                    _ptr(workspace), ws_bytes, int(num_splits), _stream(stream))
+    if rc != 0:
+        raise SpicyError(rc, "spicy_decode_attn_shared")
 
 
 def workspace(nbytes: int, device) -> torch.Tensor:

@@ -42,6 +42,47 @@ int32_t pages_per_split(int32_t max_pages, int32_t splits) {
     return std::max<int32_t>(1, ceil_div(max_pages, splits));
 }
 
+// Partial-slot plan of one decode call: prefix_splits chunks of the shared
+// prefix, then priv_splits splits of the private pages [P, max_pages).
+struct DecodePlan {
+    int32_t prefix_chunk = 1;
+    int32_t prefix_splits = 0;
+    int32_t priv_splits = 1;
+    int32_t pages_per_split = 1;
+    int32_t slots() const { return prefix_splits + priv_splits; }
+};
+
+constexpr int32_t kPrefixWaveTarget = 256;  // shared-prefix wavefronts per call
+constexpr int32_t kMinPrefixChunk = 8;
+constexpr int32_t kMaxPrefixChunk = 64;     // one page id per lane
+
+DecodePlan plan_decode(int32_t B, int32_t H_q, int32_t H_kv, int32_t max_pages, int32_t P, int32_t num_splits) {
+    DecodePlan p;
+    if (P > 0) {
+        // chunks long enough that the partials they write (one per query row
+        // and chunk) stay small next to the pages, yet enough wavefronts
+        const int64_t rows = static_cast<int64_t>(B) * (H_q / std::max(1, H_kv));
+        const int64_t tiles = (rows + 15) / 16;
+        const int64_t work = static_cast<int64_t>(P) * std::max(1, H_kv) * tiles;
+        int32_t c = ceil_div(work, kPrefixWaveTarget);
+        c = std::min(std::max(c, kMinPrefixChunk), kMaxPrefixChunk);
+        c = std::min(c, P);
+        p.prefix_splits = ceil_div(P, c);
+        p.prefix_chunk = ceil_div(P, p.prefix_splits);
+    }
+    const int32_t priv = max_pages - P;
+    if (priv > 0) {
+        p.priv_splits = spicy_decode_num_splits(B, H_kv, priv, num_splits);
+        p.pages_per_split = pages_per_split(priv, p.priv_splits);
+    }
+    return p;
+}
+
+size_t decode_workspace(int32_t B, int32_t H_q, int32_t d, int32_t slots) {
+    const size_t rows = static_cast<size_t>(B) * static_cast<size_t>(H_q) * static_cast<size_t>(slots);
+    return SPICY_WORKSPACE_HEADER + align_up(rows * 2 * sizeof(float)) + align_up(rows * static_cast<size_t>(d) * sizeof(float));
+}
+
 }  // namespace
 
 extern "C" {
@@ -136,11 +177,20 @@ int32_t spicy_decode_num_splits(int32_t B, int32_t num_kv_heads, int32_t max_pag
 
 size_t spicy_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
                                     int32_t head_dim, int32_t max_pages_per_seq, int32_t num_splits) {
-    if (B < 0 || num_q_heads < 1 || head_dim < 1) return 0;
-    const int32_t s = spicy_decode_num_splits(B, num_kv_heads, max_pages_per_seq, num_splits);
-    const size_t rows = static_cast<size_t>(B) * static_cast<size_t>(num_q_heads) * static_cast<size_t>(s);
-    return SPICY_WORKSPACE_HEADER + align_up(rows * 2 * sizeof(float)) +
-           align_up(rows * static_cast<size_t>(head_dim) * sizeof(float));
+    return spicy_decode_shared_workspace_bytes(B, num_q_heads, num_kv_heads, head_dim, max_pages_per_seq, 0,
+                                               num_splits);
+}
+
+size_t spicy_decode_shared_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t max_pages_per_seq,
+                                           int32_t shared_prefix_pages, int32_t num_splits) {
+    if (B < 0 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 || shared_prefix_pages < 0)
+        return 0;
+    // the fp32 path ignores the prefix; reserve for whichever plan is larger
+    const DecodePlan p0 = plan_decode(B, num_q_heads, num_kv_heads, max_pages_per_seq, 0, num_splits);
+    const DecodePlan p1 = plan_decode(B, num_q_heads, num_kv_heads, max_pages_per_seq, shared_prefix_pages,
+                                      num_splits);
+    return decode_workspace(B, num_q_heads, head_dim, std::max(p0.slots(), p1.slots()));
 }
 
 spicy_status spicy_decode_attn(const spicy_cache* cache, const void* q, int32_t num_q_heads,
@@ -148,19 +198,32 @@ spicy_status spicy_decode_attn(const spicy_cache* cache, const void* q, int32_t 
                                const int32_t* lengths, int32_t B, float* o, float* lse,
                                void* workspace, size_t workspace_bytes, int32_t num_splits,
                                void* stream) {
+    return spicy_decode_attn_shared(cache, q, num_q_heads, page_table, max_pages_per_seq, lengths, B, 0, o, lse,
+                                    workspace, workspace_bytes, num_splits, stream);
+}
+
+spicy_status spicy_decode_attn_shared(const spicy_cache* cache, const void* q, int32_t num_q_heads,
+                                      const int32_t* page_table, int32_t max_pages_per_seq,
+                                      const int32_t* lengths, int32_t B, int32_t shared_prefix_pages,
+                                      float* o, float* lse, void* workspace, size_t workspace_bytes,
+                                      int32_t num_splits, void* stream) {
     spicy_status st = check_cache(cache);
     if (st != SPICY_OK) return st;
-    if (B < 0 || num_q_heads < 1 || num_splits < 0) return SPICY_ERR_ARG;
+    if (B < 0 || num_q_heads < 1 || num_splits < 0 || shared_prefix_pages < 0) return SPICY_ERR_ARG;
     if (B > kMaxGridY || num_q_heads > kMaxGridY) return SPICY_ERR_UNSUPPORTED;
     if (num_q_heads % cache->num_kv_heads != 0) return SPICY_ERR_UNSUPPORTED;
     if (num_q_heads / cache->num_kv_heads > kMaxGroup) return SPICY_ERR_UNSUPPORTED;
     if (B == 0) return SPICY_OK;
     if (!q || !page_table || !lengths || !o || !lse || !workspace) return SPICY_ERR_ARG;
     if (max_pages_per_seq < 1) return SPICY_ERR_ARG;
-    const int32_t splits = spicy_decode_num_splits(B, cache->num_kv_heads, max_pages_per_seq, num_splits);
-    if (workspace_bytes < spicy_decode_workspace_bytes(B, num_q_heads, cache->num_kv_heads, cache->head_dim,
-                                                       max_pages_per_seq, num_splits))
+    if (shared_prefix_pages > max_pages_per_seq) return SPICY_ERR_RANGE;
+    if (workspace_bytes < spicy_decode_shared_workspace_bytes(B, num_q_heads, cache->num_kv_heads,
+                                                              cache->head_dim, max_pages_per_seq,
+                                                              shared_prefix_pages, num_splits))
         return SPICY_ERR_CAPACITY;
+    // the fp32 kernel has no shared-prefix role: every page is private there
+    const int32_t P = cache->dtype == SPICY_BF16 ? shared_prefix_pages : 0;
+    const DecodePlan plan = plan_decode(B, num_q_heads, cache->num_kv_heads, max_pages_per_seq, P, num_splits);
 
     spicy::DecodeArgs a{};
     a.cache = spicy::CacheArgs{cache->k, cache->v, cache->ab, cache->meta, cache->num_pages, cache->num_kv_heads};
@@ -170,7 +233,8 @@ spicy_status spicy_decode_attn(const spicy_cache* cache, const void* q, int32_t 
     a.o = o;
     a.lse = lse;
     char* ws = static_cast<char*>(workspace);
-    const size_t rows = static_cast<size_t>(B) * static_cast<size_t>(num_q_heads) * static_cast<size_t>(splits);
+    const size_t rows = static_cast<size_t>(B) * static_cast<size_t>(num_q_heads) *
+                        static_cast<size_t>(plan.slots());
     a.err = reinterpret_cast<int32_t*>(ws);
     size_t off = SPICY_WORKSPACE_HEADER;
     a.part_ml = reinterpret_cast<float*>(ws + off);
@@ -179,8 +243,13 @@ spicy_status spicy_decode_attn(const spicy_cache* cache, const void* q, int32_t 
     a.B = B;
     a.H_q = num_q_heads;
     a.max_pages = max_pages_per_seq;
-    a.splits = splits;
-    a.pages_per_split = pages_per_split(max_pages_per_seq, splits);
+    a.splits = plan.slots();
+    a.pages_per_split = plan.pages_per_split;
+    a.page_begin = P;
+    a.priv_splits = plan.priv_splits;
+    a.prefix_pages = P;
+    a.prefix_chunk = plan.prefix_chunk;
+    a.prefix_splits = plan.prefix_splits;
     return spicy::launch_decode(a, cache->dtype, cache->head_dim, static_cast<hipStream_t>(stream));
 }
 

@@ -7,26 +7,35 @@
 // followed by an ordinary online softmax.  Everything runs in base 2:
 // s2 = s * log2(e), so p = exp2(s2 - m2) and LSE = ln2 * (m2 + log2 l).
 //
-// bf16 caches (decode_mfma_kernel): one wavefront owns one (sequence, KV head,
-// split).  The G = H_q / H_kv query heads sharing the KV head are packed into
-// the 16 columns of MFMA tiles, so every key and value byte is read from HBM
-// once per KV head:
-//   S^T[16 entries x 16 heads] = K_page[16 x d] . Q^T[d x 16]
+// bf16 caches (decode_mfma_kernel).  A query "tile" is up to 16 query rows
+// that attend to the same KV head.  The rows fill the 16 columns of the MFMA
+// tiles, so each key and value byte loaded serves all of them:
+//   S^T[16 entries x 16 rows] = K_page[16 x d] . Q^T[d x 16]
 //       d/32 x v_mfma_f32_16x16x32_bf16, K rows straight from the page
 //       (lane l holds entry l%16, 8 dims of each 32-dim chunk)
-//   the accumulator layout of S^T (lane l: entries 4(l/16)+j, head l%16) is
+//   the accumulator layout of S^T (lane l: entries 4(l/16)+j, row l%16) is
 //   exactly the B operand of the next product, so the probabilities go from
 //   exp2 to bf16 to MFMA without any lane exchange:
-//   O^T[d x 16 heads] += V^T_page[d x 16 entries] . P^T[16 entries x 16 heads]
-//       d/16 x v_mfma_f32_16x16x16_bf16, value tiles stored dim-major in the
-//       page so each lane's 4 entries of one dimension are 8 contiguous bytes.
-// Pages are prefetched NBUF deep in registers; page ids are scalar loads.
+//   O^T[d x 16 rows] += V^T_page[d x 16 entries] . P^T[16 entries x 16 rows]
+//       d/16 x v_mfma_f32_16x16x16_bf16.  Value tiles are stored dim-major in
+//       the page, so each lane's 4 entries of one dimension are 8 contiguous
+//       bytes.
+// One launch holds two kinds of workgroups:
+//   split-K: one wavefront per (sequence, KV head, split).  Its tile is the
+//       G = H_q / H_kv query heads of that KV head, and it prefetches its pages
+//       NBUF deep in registers.
+//   shared prefix (only when the caller declares one): the first P logical
+//       pages map to the same physical pages in every sequence.  One wavefront
+//       applies a chunk of them to a tile of 16 rows drawn from all sequences
+//       (B x G rows per KV head).  The wavefronts of one (chunk, KV head) run
+//       on one XCD, so HBM delivers each shared page once to its L2.
+// Both kinds write partials (running max, sum, unnormalised output) to the
+// workspace.  combine_kernel merges the partials of each (sequence, query
+// head) by log-sum-exp and writes O (fp32) and LSE (natural log).
 //
 // fp32 caches (decode_f32_kernel): a plain VALU kernel, one wavefront per
-// (sequence, query head, split), lanes = 16 entries x 4 quarter-rows.
-//
-// combine_kernel merges the splits of each (sequence, query head) by
-// log-sum-exp and writes O (fp32) and LSE (natural log).
+// (sequence, query head, split), lanes = 16 entries x 4 quarter-rows.  It has
+// no shared-prefix role: the host gives it every page as private.
 #include "launch.h"
 #include "spicy_device.h"
 
@@ -41,6 +50,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kWavesPerBlock = 4;
+constexpr int kXcds = 8;                  // MI355X: workgroups go round-robin over 8 XCDs
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -64,103 +75,83 @@ struct PageRegs {
     bf16x8 k[D / 32];      // K rows: entry lane%16, dims 32i + 8(lane/16) .. +8
     s16x4 v[D / 16];       // V^T tile t: dim 16t + lane%16, entries 4(lane/16) .. +4
     bf16x8 ab;             // (alpha, beta) of entries 4(lane/16) .. +4
-    bool ok;
+    bool ok;               // page id was valid (uniform)
 };
 
-}  // namespace
-
-// ---------------------------------------------------------------- bf16 MFMA
-
-template <int D, int NBUF>
-__global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
+// Load KV head h of physical page pid, or of page 0 when pid is invalid
+// (then r.ok is false and the page is skipped when processed).
+template <int D>
+__device__ __forceinline__ void load_page(const DecodeArgs& a, PageRegs<D>& r, int32_t pid, int h) {
     constexpr int KC = D / 32;
     constexpr int NT = D / 16;
     const int lane = threadIdx.x % kWave;
-    const int wave = threadIdx.x / kWave;
-    const int row = lane % 16;     // entry (A rows) / query head (B, C columns)
-    const int grp = lane / 16;
-    const int split = blockIdx.x * (blockDim.x / kWave) + wave;
-    const int h = blockIdx.y;
-    const int b = blockIdx.z;
-    const int H = a.cache.H;
-    const int G = a.H_q / H;
-    if (split >= a.splits) return;
-
-    const int32_t len = checked_length(a, b);
-    const int32_t npages = (len + kPage - 1) / kPage;
-    const int32_t p0 = split * a.pages_per_split;
-    const int32_t p1 = min(p0 + a.pages_per_split, npages);
-    if (p0 >= p1) return;
-
-    // query operand (B of S^T = K Q^T): lane holds head `row`, 8 dims per chunk
-    const uint16_t* qbase = static_cast<const uint16_t*>(a.q) +
-                            (static_cast<int64_t>(b) * a.H_q + static_cast<int64_t>(h) * G + row) * D;
-    bf16x8 qv[KC];
-    float n2 = 0.f;
+    const int row = lane % 16, grp = lane / 16;
+    r.ok = pid >= 0 && pid < a.cache.num_pages;
+    if (!r.ok) raise_err(a.err, SPICY_DEVERR_PAGE_ID);
+    const int64_t ph = static_cast<int64_t>(r.ok ? pid : 0) * a.cache.H + h;
+    const uint16_t* kp = static_cast<const uint16_t*>(a.cache.k) + ph * kPage * D + row * D + 8 * grp;
 #pragma unroll
-    for (int i = 0; i < KC; ++i) {
-        if (row < G) {
-            qv[i] = *reinterpret_cast<const bf16x8*>(qbase + 32 * i + 8 * grp);
-        } else {
-            qv[i] = bf16x8{};
-        }
+    for (int i = 0; i < KC; ++i) r.k[i] = *reinterpret_cast<const bf16x8*>(kp + 32 * i);
+    const uint16_t* vp = static_cast<const uint16_t*>(a.cache.v) + ph * D * kPage + row * kPage + 4 * grp;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float x = static_cast<float>(qv[i][j]);
-            n2 += x * x;
-        }
-    }
-    n2 += __shfl_xor(n2, 16);
-    n2 += __shfl_xor(n2, 32);
-    const float c_dot = kLog2e / sqrtf(static_cast<float>(D));
-    const float c_beta = n2 * kLog2e;
+    for (int t = 0; t < NT; ++t) r.v[t] = *reinterpret_cast<const s16x4*>(vp + 16 * kPage * t);
+    r.ab = *reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(a.cache.ab) + ph * kPage * 2 + 8 * grp);
+}
 
-    const uint16_t* kpool = static_cast<const uint16_t*>(a.cache.k);
-    const uint16_t* vpool = static_cast<const uint16_t*>(a.cache.v);
-    const uint16_t* abpool = static_cast<const uint16_t*>(a.cache.ab);
-    const int32_t* table = a.page_table + static_cast<int64_t>(b) * a.max_pages;
-
-    // Page ids of the split, 64 at a time: one vector load, then each page's
-    // id is read out of its lane (uniform).  Pages past the split's end and
-    // invalid ids load a valid page (so that every load is unconditional and
-    // each wait covers exactly one page); they are skipped when processed.
-    int32_t ids = 0;
-    int32_t ids_base = -kWave;
-    auto page_id = [&](int32_t lp) {
-        const int32_t q = min(lp, p1 - 1);
-        if (q - ids_base >= kWave) {            // uniform
-            ids_base = q;
-            ids = (q + lane < p1) ? table[q + lane] : 0;
-        }
-        return __builtin_amdgcn_readlane(ids, q - ids_base);
-    };
-    auto load = [&](PageRegs<D>& r, int32_t lp) {
-        const int32_t pid = page_id(lp);
-        r.ok = pid >= 0 && pid < a.cache.num_pages;
-        if (!r.ok) raise_err(a.err, SPICY_DEVERR_PAGE_ID);
-        const int64_t ph = static_cast<int64_t>(r.ok ? pid : 0) * H + h;
-        const uint16_t* kp = kpool + ph * kPage * D + row * D + 8 * grp;
-#pragma unroll
-        for (int i = 0; i < KC; ++i) r.k[i] = *reinterpret_cast<const bf16x8*>(kp + 32 * i);
-        const uint16_t* vp = vpool + ph * D * kPage + row * kPage + 4 * grp;
-#pragma unroll
-        for (int t = 0; t < NT; ++t) r.v[t] = *reinterpret_cast<const s16x4*>(vp + 16 * kPage * t);
-        r.ab = *reinterpret_cast<const bf16x8*>(abpool + ph * kPage * 2 + 8 * grp);
-    };
-
-    float m_run = -__builtin_huge_valf();
-    float l_run = 0.f;
+// Online-softmax state of one query tile; lane l serves query row l%16.
+template <int D>
+struct Tile {
+    static constexpr int KC = D / 32;
+    static constexpr int NT = D / 16;
+    bf16x8 q[KC];          // B operand of S^T = K Q^T: 8 dims of each 32-dim chunk
+    float c_beta;          // |q|^2 log2(e) of this lane's row
+    int32_t len;           // entries of this row's sequence (0 for a padding row)
+    int32_t vlen;          // uniform: largest len of the tile
+    float m_run, l_run;
     f32x4 acc[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto process = [&](const PageRegs<D>& r, int32_t lp) {
+    // rowq: this lane's query row, or nullptr for a padding row
+    __device__ __forceinline__ void init(const uint16_t* rowq, int32_t length) {
+        const int grp = (threadIdx.x % kWave) / 16;
+        float n2 = 0.f;
+#pragma unroll
+        for (int i = 0; i < KC; ++i) {
+            if (rowq) {
+                q[i] = *reinterpret_cast<const bf16x8*>(rowq + 32 * i + 8 * grp);
+            } else {
+                q[i] = bf16x8{};
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float x = static_cast<float>(q[i][j]);
+                n2 += x * x;
+            }
+        }
+        n2 += __shfl_xor(n2, 16);
+        n2 += __shfl_xor(n2, 32);
+        c_beta = n2 * kLog2e;
+        len = rowq ? length : 0;
+        int32_t mx = len;
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) mx = max(mx, __shfl_xor(mx, o));
+        vlen = __builtin_amdgcn_readfirstlane(mx);
+        m_run = -__builtin_huge_valf();
+        l_run = 0.f;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // Fold logical page lp into the state.  A row's entries at or past its
+    // length get weight zero; a page whose id was invalid is skipped.
+    __device__ __forceinline__ void process(const PageRegs<D>& r, int32_t lp) {
         if (!r.ok) return;
+        const int grp = (threadIdx.x % kWave) / 16;
+        const float c_dot = kLog2e / sqrtf(static_cast<float>(D));
         f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < KC; ++i) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.k[i], qv[i], s, 0, 0, 0);
-        float s2[4];
+        for (int i = 0; i < KC; ++i) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.k[i], q[i], s, 0, 0, 0);
         const int32_t ebase = lp * kPage + 4 * grp;
+        float s2[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const float alpha = static_cast<float>(r.ab[2 * j]);
@@ -182,25 +173,148 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
         const bf16x4 pb = {static_cast<__bf16>(p[0]), static_cast<__bf16>(p[1]),
                            static_cast<__bf16>(p[2]), static_cast<__bf16>(p[3])};
         const s16x4 pk = __builtin_bit_cast(s16x4, pb);
-        if (lp * kPage + kPage <= len) {
+        if (lp * kPage + kPage <= vlen) {
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 acc[t] *= scale;
                 acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(r.v[t], pk, acc[t], 0, 0, 0);
             }
         } else {
-            // last, partly used page: slots past the length may hold anything,
-            // so their values are zeroed (0 * NaN would poison the product)
+            // a page past the end of some row: slots no row uses may hold
+            // anything, so their values are zeroed (0 * NaN would poison the
+            // product)
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 s16x4 vt = r.v[t];
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    if (ebase + j >= len) vt[j] = 0;
+                    if (ebase + j >= vlen) vt[j] = 0;
                 acc[t] *= scale;
                 acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pk, acc[t], 0, 0, 0);
             }
         }
+    }
+
+    // Finish the row sums (held per lane group) and store this lane's row as
+    // partial `slot` of partial row `prow` (= sequence * H_q + query head).
+    __device__ __forceinline__ void store(const DecodeArgs& a, bool row_valid, int64_t prow, int slot) {
+        const int grp = (threadIdx.x % kWave) / 16;
+        float l = l_run;
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
+        if (!row_valid) return;
+        const int64_t idx = prow * a.splits + slot;
+        if (grp == 0) {
+            a.part_ml[2 * idx + 0] = m_run;
+            a.part_ml[2 * idx + 1] = l;
+        }
+        float* po = a.part_o + idx * D + 4 * grp;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) *reinterpret_cast<f32x4*>(po + 16 * t) = acc[t];
+    }
+};
+
+}  // namespace
+
+// ---------------------------------------------------------------- bf16 MFMA
+
+// Workgroup w (linear over a 2-D grid) of 4 wavefronts.  Both roles run the
+// same page pipeline; they differ in the rows of their tile, the page range
+// and where its page ids come from.
+//   w < prefix_blocks: shared-prefix role, work item (chunk c, KV head h, tile
+//       t).  Tile t holds rows r = 16t .. 16t+15 of the B x G (sequence,
+//       query head of h) rows; its pages are [c * prefix_chunk, ...) of the
+//       shared prefix, with ids from sequence 0's table row.  w is first
+//       remapped so that the prefix_blocks / 8 consecutive work items of each
+//       XCD are contiguous: the tiles of one (chunk, KV head) share an L2.
+//   otherwise: split-K role, work item (split, KV head h, sequence b).  The
+//       tile is the G query heads of h; the pages are private pages
+//       [page_begin + split * pages_per_split, ...) of sequence b.
+// Pages are prefetched NBUF deep in registers.  Page ids are read 64 at a
+// time with one vector load, then each page's id is read out of its lane
+// (uniform).  Pages past the range's end load its last page again (every
+// load is unconditional, so each wait covers exactly one page); they are
+// never processed.
+template <int D, int NBUF>
+__global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
+    const int lane = threadIdx.x % kWave;
+    const int wave = threadIdx.x / kWave;
+    const int row = lane % 16;
+    const int H = a.cache.H;
+    const int G = a.H_q / H;
+    int64_t blk = static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x;
+
+    int h, slot;
+    int32_t p0, p1;
+    const int32_t* table;
+    int64_t prow;          // this lane's partial row (sequence * H_q + query head)
+    int32_t rlen;          // this lane's sequence length
+    bool row_valid;
+    if (blk < a.prefix_blocks) {
+        const int per_xcd = a.prefix_blocks / kXcds;      // prefix_blocks is a multiple of 8
+        int w = static_cast<int>(blk % kXcds) * per_xcd + static_cast<int>(blk / kXcds);
+        const int tgb = a.prefix_tile_blocks;
+        const int t = (w % tgb) * kWavesPerBlock + wave;
+        w /= tgb;
+        h = w % H;
+        const int c = w / H;
+        const int rows = a.B * G;
+        if (c >= a.prefix_splits || t * 16 >= rows) return;
+        slot = c;
+        p0 = c * a.prefix_chunk;
+        p1 = min(p0 + a.prefix_chunk, a.prefix_pages);
+        table = a.page_table;
+        const int r = t * 16 + row;
+        row_valid = r < rows;
+        const int bq = row_valid ? r / G : 0;
+        prow = static_cast<int64_t>(bq) * a.H_q + static_cast<int64_t>(h) * G + (row_valid ? r % G : 0);
+        rlen = row_valid ? checked_length(a, bq) : 0;
+        // the KV head 0 wavefronts check that the sequences of their tile map
+        // the chunk's pages like sequence 0: independent loads, one flag
+        if (h == 0) {
+            const int b_first = (t * 16) / G;
+            const int b_last = min(rows - 1, t * 16 + 15) / G;
+            const int npg = p1 - p0;
+            const int n = (b_last - b_first + 1) * npg;
+            bool bad = false;
+            for (int i = lane; i < n; i += kWave) {
+                const int32_t pg = p0 + i % npg;
+                const int64_t bb = b_first + i / npg;
+                bad |= a.page_table[bb * a.max_pages + pg] != a.page_table[pg];
+            }
+            if (bad) raise_err(a.err, SPICY_DEVERR_SHARED);
+        }
+    } else {
+        blk -= a.prefix_blocks;
+        const int sgb = (a.priv_splits + kWavesPerBlock - 1) / kWavesPerBlock;
+        const int split = static_cast<int>(blk % sgb) * kWavesPerBlock + wave;
+        blk /= sgb;
+        h = static_cast<int>(blk % H);
+        const int64_t b = blk / H;
+        if (split >= a.priv_splits || b >= a.B) return;
+        slot = a.prefix_splits + split;
+        const int32_t len = checked_length(a, static_cast<int>(b));
+        p0 = a.page_begin + split * a.pages_per_split;
+        p1 = min(p0 + a.pages_per_split, (len + kPage - 1) / kPage);
+        table = a.page_table + b * a.max_pages;
+        row_valid = row < G;
+        prow = b * a.H_q + static_cast<int64_t>(h) * G + row;
+        rlen = len;
+    }
+    if (p0 >= p1) return;
+
+    Tile<D> T;
+    T.init(row_valid ? static_cast<const uint16_t*>(a.q) + prow * D : nullptr, rlen);
+
+    int32_t ids = 0;
+    int32_t ids_base = -kWave;
+    auto load = [&](PageRegs<D>& r, int32_t lp) {
+        const int32_t q = min(lp, p1 - 1);
+        if (q - ids_base >= kWave) {            // uniform
+            ids_base = q;
+            ids = (q + lane < p1) ? table[q + lane] : 0;
+        }
+        load_page<D>(a, r, __builtin_amdgcn_readlane(ids, q - ids_base), h);
     };
 
     PageRegs<D> buf[NBUF];
@@ -209,23 +323,11 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     for (int32_t lp = p0; lp < p1; lp += NBUF) {
 #pragma unroll
         for (int i = 0; i < NBUF; ++i) {
-            if (lp + i < p1) process(buf[i], lp + i);
+            if (lp + i < p1) T.process(buf[i], lp + i);
             load(buf[i], lp + i + NBUF);
         }
     }
-
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
-    if (row < G) {
-        const int64_t idx = (static_cast<int64_t>(b) * a.H_q + static_cast<int64_t>(h) * G + row) * a.splits + split;
-        if (grp == 0) {
-            a.part_ml[2 * idx + 0] = m_run;
-            a.part_ml[2 * idx + 1] = l_run;
-        }
-        float* po = a.part_o + idx * D + 4 * grp;
-#pragma unroll
-        for (int t = 0; t < NT; ++t) *reinterpret_cast<f32x4*>(po + 16 * t) = acc[t];
-    }
+    T.store(a, row_valid, prow, slot);
 }
 
 // -------------------------------------------------------------- fp32 VALU
@@ -244,11 +346,11 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
     const int H = a.cache.H;
     const int G = a.H_q / H;
     const int h = hq / G;
-    if (split >= a.splits) return;
+    if (split >= a.priv_splits) return;
 
     const int32_t len = checked_length(a, b);
     const int32_t npages = (len + kPage - 1) / kPage;
-    const int32_t p0 = split * a.pages_per_split;
+    const int32_t p0 = a.page_begin + split * a.pages_per_split;
     const int32_t p1 = min(p0 + a.pages_per_split, npages);
     if (p0 >= p1) return;
 
@@ -316,7 +418,7 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
     }
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) l_run += __shfl_xor(l_run, o);
-    const int64_t idx = (static_cast<int64_t>(b) * a.H_q + hq) * a.splits + split;
+    const int64_t idx = (static_cast<int64_t>(b) * a.H_q + hq) * a.splits + a.prefix_splits + split;
     if (lane == 0) {
         a.part_ml[2 * idx + 0] = m_run;
         a.part_ml[2 * idx + 1] = l_run;
@@ -327,8 +429,9 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
 
 // ----------------------------------------------------------------- combine
 
-// One wavefront per (sequence, query head): merge the splits by log-sum-exp.
-// Loads of kChunk splits are issued together; lanes own D/64 dimensions.
+// One wavefront per (sequence, query head): merge its partials (prefix chunks
+// first, then the private splits that hold pages) by log-sum-exp.  Loads of
+// kChunk partials are issued together; lanes own D/64 dimensions.
 template <int D>
 __global__ __launch_bounds__(64) void combine_kernel(DecodeArgs a) {
     constexpr int DL = D / kWave;
@@ -338,7 +441,8 @@ __global__ __launch_bounds__(64) void combine_kernel(DecodeArgs a) {
     const int b = blockIdx.y;
     const int32_t len = checked_length(a, b);
     const int32_t npages = (len + kPage - 1) / kPage;
-    const int nsplit = min(a.splits, (npages + a.pages_per_split - 1) / a.pages_per_split);
+    const int32_t priv = max(0, npages - a.page_begin);
+    const int nsplit = a.prefix_splits + min(a.priv_splits, (priv + a.pages_per_split - 1) / a.pages_per_split);
     const int64_t base = (static_cast<int64_t>(b) * a.H_q + hq) * a.splits;
 
     float M = -__builtin_huge_valf();
@@ -381,15 +485,26 @@ __global__ __launch_bounds__(64) void combine_kernel(DecodeArgs a) {
 // ------------------------------------------------------------------ launch
 
 constexpr int kNbuf = 4;
+constexpr int64_t kMaxGridX = 65536;
 
 template <int D>
-static spicy_status launch_decode_t(const DecodeArgs& a, int dtype, hipStream_t stream) {
-    const int wpb = a.splits < 4 ? a.splits : 4;
+static spicy_status launch_decode_t(const DecodeArgs& a0, int dtype, hipStream_t stream) {
+    DecodeArgs a = a0;
     if (dtype == SPICY_BF16) {
-        dim3 grid((a.splits + wpb - 1) / wpb, a.cache.H, a.B);
-        hipLaunchKernelGGL((decode_mfma_kernel<D, kNbuf>), grid, dim3(wpb * kWave), 0, stream, a);
+        const int G = a.H_q / a.cache.H;
+        const int tiles = (a.B * G + 15) / 16;
+        a.prefix_tile_blocks = (tiles + kWavesPerBlock - 1) / kWavesPerBlock;
+        const int64_t pb = static_cast<int64_t>(a.prefix_splits) * a.cache.H * a.prefix_tile_blocks;
+        a.prefix_blocks = static_cast<int32_t>((pb + kXcds - 1) / kXcds * kXcds);
+        const int64_t sgb = (a.priv_splits + kWavesPerBlock - 1) / kWavesPerBlock;
+        const int64_t nblk = a.prefix_blocks + sgb * a.cache.H * a.B;
+        const int64_t gx = nblk < kMaxGridX ? nblk : kMaxGridX;
+        const int64_t gy = (nblk + gx - 1) / gx;
+        hipLaunchKernelGGL((decode_mfma_kernel<D, kNbuf>), dim3(static_cast<unsigned>(gx), static_cast<unsigned>(gy)),
+                           dim3(kWavesPerBlock * kWave), 0, stream, a);
     } else {
-        dim3 grid((a.splits + wpb - 1) / wpb, a.H_q, a.B);
+        const int wpb = a.priv_splits < 4 ? a.priv_splits : 4;
+        dim3 grid((a.priv_splits + wpb - 1) / wpb, a.H_q, a.B);
         hipLaunchKernelGGL((decode_f32_kernel<D>), grid, dim3(wpb * kWave), 0, stream, a);
     }
     if (hipGetLastError() != hipSuccess) return SPICY_ERR_HIP;

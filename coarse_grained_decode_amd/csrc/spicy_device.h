@@ -160,8 +160,15 @@ struct DecodeArgs {
     int32_t B;
     int32_t H_q;
     int32_t max_pages;
-    int32_t splits;        // S
-    int32_t pages_per_split;
+    int32_t splits;        // S = prefix_splits + priv_splits partial slots per row
+    int32_t pages_per_split;   // private pages per split
+    int32_t page_begin;        // first private logical page (= prefix_pages on the MFMA path)
+    int32_t priv_splits;       // split-K wavefronts per (sequence, KV head)
+    int32_t prefix_pages;      // P shared logical pages (0 = none)
+    int32_t prefix_chunk;      // pages per shared-prefix wavefront (<= 64)
+    int32_t prefix_splits;     // ceil(P / prefix_chunk) chunks (slots 0 .. prefix_splits-1)
+    int32_t prefix_blocks;     // set by the launcher: workgroups of the prefix role
+    int32_t prefix_tile_blocks;  // set by the launcher: workgroups per (chunk, KV head)
 };
 
 }  // namespace spicy

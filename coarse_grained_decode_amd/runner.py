@@ -14,7 +14,8 @@ import numpy as np
 import torch
 
 from . import (PagedCache, spicy_coarsen, spicy_coarsen_workspace_bytes, spicy_decode_attn,
-               spicy_decode_num_splits, spicy_decode_workspace_bytes, workspace)
+               spicy_decode_attn_shared, spicy_decode_num_splits, spicy_decode_shared_workspace_bytes,
+               workspace)
 from .workloads import CoarsenCall, Workload
 
 
@@ -78,11 +79,12 @@ class DeviceWorkload:
     lse: torch.Tensor
     num_splits: int
     dws: torch.Tensor
+    shared_prefix_pages: int = 0
     lengths: torch.Tensor = field(default=None)
 
     @staticmethod
     def of(wl: Workload, device="cuda", meta: bool = True, num_splits: int = 0,
-           fill: float | None = float("nan")) -> "DeviceWorkload":
+           fill: float | None = float("nan"), use_shared_prefix: bool = True) -> "DeviceWorkload":
         device = torch.device(device)
         tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
         cache = PagedCache.empty(wl.num_pages, wl.H_kv, wl.d, tdt, device, meta=meta, fill=fill)
@@ -92,9 +94,10 @@ class DeviceWorkload:
         table = _tensor(wl.page_table, None, device)
         o = torch.empty(wl.B, wl.H_q, wl.d, dtype=torch.float32, device=device)
         lse = torch.empty(wl.B, wl.H_q, dtype=torch.float32, device=device)
-        dws = workspace(spicy_decode_workspace_bytes(wl.B, wl.H_q, wl.H_kv, wl.d, wl.max_pages, num_splits),
-                        device)
-        return DeviceWorkload(wl, device, cache, setup, step, q, table, o, lse, num_splits, dws)
+        P = wl.shared_prefix_pages if use_shared_prefix else 0
+        dws = workspace(spicy_decode_shared_workspace_bytes(wl.B, wl.H_q, wl.H_kv, wl.d, wl.max_pages, P,
+                                                            num_splits), device)
+        return DeviceWorkload(wl, device, cache, setup, step, q, table, o, lse, num_splits, dws, P)
 
     def run_setup(self) -> None:
         for c in self.setup:
@@ -106,9 +109,16 @@ class DeviceWorkload:
             self.step.run(self.cache)
             self.lengths = self.step.lengths
 
-    def decode(self) -> None:
-        spicy_decode_attn(self.cache, self.q, self.page_table, self.lengths, self.o, self.lse, self.dws,
-                          self.num_splits)
+    def decode(self, cache: PagedCache | None = None) -> None:
+        """spicy_decode_attn, or spicy_decode_attn_shared when the batch
+        declares a shared prefix."""
+        cache = self.cache if cache is None else cache
+        if self.shared_prefix_pages > 0:
+            spicy_decode_attn_shared(cache, self.q, self.page_table, self.lengths, self.shared_prefix_pages,
+                                     self.o, self.lse, self.dws, self.num_splits)
+        else:
+            spicy_decode_attn(cache, self.q, self.page_table, self.lengths, self.o, self.lse, self.dws,
+                              self.num_splits)
 
     def step_once(self) -> None:
         """One pass of the hot path: coarsen the per-step chunk (if any), then decode."""

@@ -27,7 +27,7 @@ of both paths.  bf16 arrays are carried as uint16 bit patterns.
 from __future__ import annotations
 
 import dataclasses
-from typing import List, Optional
+from typing import List, Optional, Tuple
 
 import numpy as np
 
@@ -116,6 +116,7 @@ class Workload:
     page_table: np.ndarray            # int32 [B, max_pages] used by decode
     q: np.ndarray                     # [B, H_q, d]
     description: str = ""
+    shared_prefix_pages: int = 0      # leading logical pages identical in every table row
 
     @property
     def calls(self) -> List[CoarsenCall]:
@@ -424,9 +425,68 @@ def make_shared_prefix(config_id: int = 4, *, B: int = 32, H_q: int = 28, H_kv: 
     return Workload(name=name, dtype=dtype, B=B, H_q=H_q, H_kv=H_kv, d=d, rope_base=rope_base,
                     num_pages=num_pages, setup=[prefix_call, suffix_call], step=chunk_call,
                     page_table=np.ascontiguousarray(table, dtype=np.int32), q=q,
+                    shared_prefix_pages=prefix_pages,
                     description=f"{B} seqs share a {prefix_T}-token prefix at {ratio}x; "
                                 f"suffix U[{suffix_range[0]},{suffix_range[1]}] exact; "
                                 f"{chunk_T}-token chunk per step, equal-variation N={N}")
+
+
+@dataclasses.dataclass
+class DecodeCase:
+    """Cache contents and a batch for decode-only cases (no coarsening):
+    k [P, H, 16, d], v [P, H, d, 16], ab [P, H, 16, 2] in storage format
+    (bf16 bits or float32), page_table int32 [B, max_pages], lengths int32 [B],
+    q [B, H_q, d]."""
+    dtype: str
+    H_q: int
+    H_kv: int
+    d: int
+    k: np.ndarray
+    v: np.ndarray
+    ab: np.ndarray
+    page_table: np.ndarray
+    lengths: np.ndarray
+    q: np.ndarray
+    shared_prefix_pages: int
+
+
+def random_decode_case(seed: int, *, B: int, H_q: int, H_kv: int, d: int, dtype: str = "bf16",
+                       prefix_pages: int = 0, private_pages: Tuple[int, int] = (1, 6),
+                       null_frac: float = 0.05) -> DecodeCase:
+    """A synthetic paged cache for decode tests: keys, values and queries
+    N(0, 1); alpha ~ U(0, 4) (a null_frac share of entries null: alpha = -inf);
+    beta ~ U(0, 0.01).  Every sequence maps the same `prefix_pages` physical
+    pages first, then U[private_pages] private pages in a shuffled pool; its
+    length ends at a random slot of its last page.  Slots past a sequence's
+    length in its own last page hold NaN, so reading them would show."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(5000 + seed)))
+    npriv = rng.integers(private_pages[0], private_pages[1] + 1, size=B)
+    num_pages = prefix_pages + int(npriv.sum())
+    max_pages = prefix_pages + int(npriv.max())
+    k = rng.standard_normal((num_pages, H_kv, PAGE, d), dtype=np.float32)
+    v = rng.standard_normal((num_pages, H_kv, d, PAGE), dtype=np.float32)
+    ab = np.empty((num_pages, H_kv, PAGE, 2), dtype=np.float32)
+    ab[..., 0] = rng.uniform(0.0, 4.0, size=ab.shape[:-1])
+    ab[..., 0][rng.random(ab.shape[:-1]) < null_frac] = -np.inf
+    ab[..., 1] = rng.uniform(0.0, 0.01, size=ab.shape[:-1])
+    pool = prefix_pages + rng.permutation(int(npriv.sum()))
+    table = np.full((B, max_pages), -1, dtype=np.int32)
+    lengths = np.empty(B, dtype=np.int32)
+    nxt = 0
+    for b in range(B):
+        n = int(npriv[b])
+        table[b, :prefix_pages] = np.arange(prefix_pages)
+        table[b, prefix_pages:prefix_pages + n] = pool[nxt:nxt + n]
+        nxt += n
+        used = int(rng.integers(1, PAGE + 1))
+        lengths[b] = (prefix_pages + n - 1) * PAGE + used
+        last = table[b, prefix_pages + n - 1]
+        k[last, :, used:, :] = np.nan
+        v[last, :, :, used:] = np.nan
+        ab[last, :, used:, :] = np.nan
+    q = rng.standard_normal((B, H_q, d), dtype=np.float32)
+    return DecodeCase(dtype, H_q, H_kv, d, _store(k, dtype), _store(v, dtype), _store(ab, dtype),
+                      table, lengths, _store(q, dtype), prefix_pages)
 
 
 def tiny_fp32(**over) -> Workload:

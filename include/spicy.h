@@ -83,6 +83,7 @@ typedef enum { SPICY_F32 = 0, SPICY_BF16 = 1 } spicy_dtype;
 #define SPICY_DEVERR_CAPACITY    0x2  /* entries beyond max_pages_per_seq * 16   */
 #define SPICY_DEVERR_SEGMENTS    0x4  /* segment/sequence offsets inconsistent   */
 #define SPICY_DEVERR_LENGTH      0x8  /* a length < 0                            */
+#define SPICY_DEVERR_SHARED      0x10 /* declared shared prefix pages differ      */
 
 #define SPICY_PAGE_SIZE 16
 #define SPICY_WORKSPACE_HEADER 256   /* bytes before any per-call scratch     */
@@ -189,6 +190,45 @@ spicy_status spicy_decode_attn(const spicy_cache* cache,          /* host struct
                                float* o, float* lse,
                                void* workspace, size_t workspace_bytes,
                                int32_t num_splits, void* stream);
+
+/* Workspace bytes spicy_decode_attn_shared needs for the same shapes and a
+ * shared prefix of `shared_prefix_pages` pages (either cache dtype). */
+size_t spicy_decode_shared_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t max_pages_per_seq,
+                                           int32_t shared_prefix_pages, int32_t num_splits);
+
+/* spicy_decode_attn_shared — spicy_decode_attn for a batch whose sequences
+ * share a compressed prefix: logical pages [0, shared_prefix_pages) map to the
+ * same physical pages in every row of page_table (SPICY-KV demo page, "Patent
+ * Pending Notice & Claims", Claim 13: multi-turn shared-prefix reuse; and the
+ * page's evaluation list, "4-Turn Shared-Prefix RadixAttention Reuse").  The
+ * prefix is compressed once and its pages are referenced by every sequence.
+ *
+ * Same inputs, outputs, errors and results (up to the order of
+ * floating-point additions) as spicy_decode_attn, plus:
+ *   shared_prefix_pages  P, host int, 0 <= P <= max_pages_per_seq.  Every row
+ *            of page_table must hold the same valid page ids in its first P
+ *            entries.  A sequence may be shorter than P pages: entries past its
+ *            length get weight zero as usual.
+ * On bf16 caches each shared page is read once per KV head and applied to the
+ * queries of all B sequences together (rows of 16 query heads x sequences fill
+ * the MFMA tiles); the private pages [P, ...) are split as in
+ * spicy_decode_attn with `num_splits` (0 = automatic) splits over the longest
+ * private part.  Rows whose first P ids differ from row 0's set
+ * SPICY_DEVERR_SHARED (the results then follow row 0's ids for the prefix).  On
+ * fp32 caches P is only range-checked and every page is read per sequence.
+ * Workspace: >= spicy_decode_shared_workspace_bytes(...) with the same P and
+ *   num_splits.
+ * Errors: those of spicy_decode_attn; SPICY_ERR_ARG if P < 0, SPICY_ERR_RANGE
+ *   if P > max_pages_per_seq. */
+spicy_status spicy_decode_attn_shared(const spicy_cache* cache,   /* host struct */
+                                      const void* q, int32_t num_q_heads,
+                                      const int32_t* page_table, int32_t max_pages_per_seq,
+                                      const int32_t* lengths, int32_t B,
+                                      int32_t shared_prefix_pages,
+                                      float* o, float* lse,
+                                      void* workspace, size_t workspace_bytes,
+                                      int32_t num_splits, void* stream);
 
 /* Human-readable name of a status code (static string). */
 const char* spicy_status_string(spicy_status s);

@@ -30,7 +30,8 @@ def lib():
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert {"spicy_coarsen", "spicy_decode_attn", "spicy_coarsen_workspace_bytes",
-            "spicy_decode_workspace_bytes", "spicy_decode_num_splits", "spicy_status_string"} <= set(names)
+            "spicy_decode_workspace_bytes", "spicy_decode_num_splits", "spicy_status_string",
+            "spicy_decode_attn_shared", "spicy_decode_shared_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -56,6 +57,20 @@ def test_workspace_and_split_plan(lib):
     n = cgd.spicy_decode_workspace_bytes(16, 28, 4, 128, 72, 8)
     up = lambda x: (x + 255) // 256 * 256
     assert n == 256 + up(16 * 28 * 8 * 2 * 4) + up(16 * 28 * 8 * 128 * 4)
+    # shared prefix: slots = prefix chunks + private splits; 32 sequences x 7
+    # query heads per KV head = 14 tiles, 144 shared pages -> chunks of
+    # max(8, ceil(144 * 4 * 14 / 256)) = 32 pages -> 5 chunks of 29;
+    # 97 private pages, 8 splits
+    assert cgd.spicy_decode_shared_workspace_bytes(32, 28, 4, 128, 241, 144, 8) == \
+        256 + up(32 * 28 * 13 * 2 * 4) + up(32 * 28 * 13 * 128 * 4)
+    # fp32 caches ignore the prefix, so the size covers the plain plan too
+    assert cgd.spicy_decode_shared_workspace_bytes(2, 4, 2, 64, 40, 39, 5) >= \
+        cgd.spicy_decode_workspace_bytes(2, 4, 2, 64, 40, 5)
+    assert cgd.spicy_decode_shared_workspace_bytes(2, 4, 2, 64, 40, 1, 40) >= \
+        cgd.spicy_decode_workspace_bytes(2, 4, 2, 64, 40, 40)
+    assert cgd.spicy_decode_shared_workspace_bytes(2, 4, 2, 64, 40, 0, 0) == \
+        cgd.spicy_decode_workspace_bytes(2, 4, 2, 64, 40, 0)
+    assert cgd.spicy_decode_shared_workspace_bytes(2, 4, 2, 64, 40, -1, 0) == 0
     assert cgd.spicy_coarsen_workspace_bytes(2, 10, 4) == 256 + 256 + 512
     assert cgd.spicy_coarsen_workspace_bytes(-1, 10, 4) == 0
 
@@ -88,6 +103,20 @@ def test_decode_rejects_bad_arguments(lib):
     assert call(ns=-2) == 1
     assert call(wsb=16) == 3
     assert call(B=0, q=0, table=0) == 0     # nothing to do
+
+
+def test_shared_decode_rejects_bad_arguments(lib):
+    P = 0x1000
+    c = _cache()
+
+    def call(shared, maxp=8, wsb=1 << 30, cache=c):
+        return lib.spicy_decode_attn_shared(ctypes.byref(cache), P, 28, P, maxp, P, 2, shared, P, P, P, wsb, 0,
+                                            None)
+
+    assert call(-1) == 1
+    assert call(9) == 2                     # more shared pages than the table has
+    assert call(4, wsb=16) == 3
+    assert call(4, cache=_cache(d=96)) == 4
 
 
 def test_coarsen_rejects_bad_arguments(lib):

@@ -292,3 +292,118 @@ def test_full_size_against_oracle(name):
     e_o, e_l = compare_decode(dw.o, dw.lse, ro, rlse, wl.dtype)
     print(f"[{name}] exact keys {stats['k_exact']:.6f}; O max-abs {e_o:.3e}  LSE rel {e_l:.3e}")
     _cache.pop(name, None)
+
+
+# --------------------------------------------------------------------------
+# shared-prefix decode (spicy_decode_attn_shared)
+# --------------------------------------------------------------------------
+
+SPICY_DEVERR_SHARED = 0x10
+
+
+def upload_case(c):
+    import coarse_grained_decode_amd as cgd
+    from coarse_grained_decode_amd.runner import _tensor
+    return (cgd.PagedCache(_tensor(c.k, c.dtype, DEV), _tensor(c.v, c.dtype, DEV), _tensor(c.ab, c.dtype, DEV),
+                           None), _tensor(c.q, c.dtype, DEV))
+
+
+def oracle_case(c, table=None, lengths=None):
+    cache = oracle.Cache(c.dtype, c.k.shape[0], c.H_kv, c.d, fill=False)
+    cache.k[:] = c.k; cache.v[:] = c.v; cache.ab[:] = c.ab
+    return oracle.decode(c.q, c.dtype, cache, c.H_q, c.page_table if table is None else table,
+                         c.lengths if lengths is None else lengths)
+
+
+def gpu_decode_shared(cache, q, table, lengths, P, H_kv, num_splits=0, expect_err=0):
+    import coarse_grained_decode_amd as cgd
+    B, H_q, d = q.shape
+    tb = torch.from_numpy(np.ascontiguousarray(table, dtype=np.int32)).to(DEV)
+    ln = torch.from_numpy(np.ascontiguousarray(lengths, dtype=np.int32)).to(DEV)
+    o = torch.empty(B, H_q, d, dtype=torch.float32, device=DEV)
+    lse = torch.empty(B, H_q, dtype=torch.float32, device=DEV)
+    ws = cgd.workspace(cgd.spicy_decode_shared_workspace_bytes(B, H_q, H_kv, d, tb.shape[1], P, num_splits), DEV)
+    cgd.spicy_decode_attn_shared(cache, q, tb, ln, P, o, lse, ws, num_splits)
+    torch.cuda.synchronize()
+    assert cgd.device_error(ws) == expect_err
+    return o, lse
+
+
+SHARED_CASES = [
+    # (seed, B, H_q, H_kv, d, dtype, prefix pages, private pages)
+    (1, 7, 28, 4, 128, "bf16", 9, (1, 6)),       # 49 rows per KV head: 4 tiles, ragged last
+    (2, 1, 2, 1, 64, "bf16", 5, (0, 0)),         # one sequence, prefix only
+    (3, 40, 16, 1, 64, "bf16", 70, (2, 30)),     # 2 chunks of <= 64 pages, 40 tiles
+    (4, 3, 6, 3, 128, "bf16", 1, (1, 3)),        # one shared page
+    (5, 5, 4, 2, 64, "f32", 4, (1, 4)),          # fp32: prefix read per sequence
+]
+
+
+@pytest.mark.parametrize("case", SHARED_CASES)
+def test_shared_prefix_decode_matches_oracle(case):
+    _need_gpu()
+    seed, B, H_q, H_kv, d, dtype, P, priv = case
+    c = W.random_decode_case(seed, B=B, H_q=H_q, H_kv=H_kv, d=d, dtype=dtype, prefix_pages=P,
+                             private_pages=priv)
+    ro, rlse = oracle_case(c)
+    cache, q = upload_case(c)
+    for ns in (0, 1, 3):
+        o, lse = gpu_decode_shared(cache, q, c.page_table, c.lengths, P, H_kv, num_splits=ns)
+        compare_decode(o, lse, ro, rlse, dtype)
+    # any declared prefix length up to the real one is valid
+    for p in (0, P // 2, P):
+        o, lse = gpu_decode_shared(cache, q, c.page_table, c.lengths, p, H_kv)
+        compare_decode(o, lse, ro, rlse, dtype)
+
+
+def test_shared_prefix_short_and_empty_sequences():
+    """Sequences shorter than the shared prefix (and empty ones) mask the
+    prefix entries past their length; the shared pages stay as they are."""
+    _need_gpu()
+    c = W.random_decode_case(11, B=9, H_q=14, H_kv=2, d=128, prefix_pages=12, private_pages=(1, 3))
+    lengths = c.lengths.copy()
+    lengths[0] = 0
+    lengths[2] = 1
+    lengths[3] = 5 * 16 + 7
+    lengths[5] = 12 * 16
+    ro, rlse = oracle_case(c, lengths=lengths)
+    cache, q = upload_case(c)
+    o, lse = gpu_decode_shared(cache, q, c.page_table, lengths, 12, 2)
+    compare_decode(o, lse, ro, rlse, "bf16")
+    assert np.all(lse.cpu().numpy()[0] == -np.inf)
+
+
+def test_shared_prefix_mismatch_sets_error_bit():
+    """A row whose declared prefix differs from row 0 sets the sticky
+    SPICY_DEVERR_SHARED bit; the prefix is then read from row 0's ids."""
+    _need_gpu()
+    c = W.random_decode_case(12, B=4, H_q=8, H_kv=2, d=64, prefix_pages=6, private_pages=(2, 2))
+    bad = c.page_table.copy()
+    bad[2, 3] = c.page_table[1, 7]                 # another sequence's private page
+    ro, rlse = oracle_case(c)                      # row 0's ids everywhere
+    cache, q = upload_case(c)
+    o, lse = gpu_decode_shared(cache, q, bad, c.lengths, 6, 2, expect_err=SPICY_DEVERR_SHARED)
+    compare_decode(o, lse, ro, rlse, "bf16")
+
+
+def test_shared_prefix_large_batch_two_dimensional_grid():
+    """9000 sequences x 4 KV heads x 6 splits: more than 65536 workgroups,
+    so the launch folds them into a 2-D grid; 1125 prefix tiles."""
+    _need_gpu()
+    c = W.random_decode_case(13, B=9000, H_q=8, H_kv=4, d=64, prefix_pages=3, private_pages=(1, 6))
+    ro, rlse = oracle_case(c)
+    cache, q = upload_case(c)
+    o, lse = gpu_decode_shared(cache, q, c.page_table, c.lengths, 3, 4, num_splits=16)
+    compare_decode(o, lse, ro, rlse, "bf16")
+
+
+def test_shared_and_plain_decode_agree_on_full_workload():
+    """The benchmark's shared-prefix batch decoded both ways: every page per
+    sequence (spicy_decode_attn) and the prefix once (spicy_decode_attn_shared)."""
+    _need_gpu()
+    wl, dw, ref_cache, ref_len, ro, rlse = run_case("shared_prefix_small")
+    assert dw.shared_prefix_pages > 0
+    o1, l1 = gpu_decode(dw.cache, wl, ref_len)
+    compare_decode(o1, l1, ro, rlse, wl.dtype)
+    e = float((o1 - dw.o).abs().max())
+    assert e <= 1e-2, e
