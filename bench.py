@@ -50,6 +50,9 @@ def parse():
                     help="diagnostic: time spicy_decode_attn alone over rotated copies of the cache")
     ap.add_argument("--rotate-bytes", type=float, default=1.5e9,
                     help="decode-only: total bytes of distinct cache copies rotated through")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 512 MiB device copy (torch.neg, fp32) 5 times: the known-size "
+                         "reference that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes")
     ap.add_argument("--no-shared-prefix", action="store_true",
                     help="decode a shared-prefix batch with spicy_decode_attn (every page per sequence)")
     return ap.parse_args()
@@ -88,6 +91,56 @@ def decode_alg_bytes(wl, lengths: np.ndarray) -> int:
     per_entry = (2 * wl.d + 2) * eb
     qol = wl.B * wl.H_q * (wl.d * eb + wl.d * 4 + 4)
     return entries * per_entry + qol
+
+
+COPY_BYTES = 512 << 20
+
+
+def copy_calibration():
+    import torch
+    x = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(5):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    print(json.dumps({"mode": "copy-calibration", "bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES,
+                      "kernel": "torch.neg fp32", "launches": 5}), flush=True)
+
+
+def sources_digest() -> str:
+    """sha256 over the library's kernel sources and headers: a traffic figure
+    measured on other sources is not reported."""
+    import hashlib
+    from coarse_grained_decode_amd import build as B
+    h = hashlib.sha256()
+    for f in sorted(B.SOURCES + B.HEADERS):
+        h.update(f.encode())
+        with open(os.path.join(B.CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    with open(os.path.join(ROOT, "include", "spicy.h"), "rb") as fh:
+        h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from profiles/traffic_<workload>.txt (rocprofv3
+    FETCH_SIZE and WRITE_SIZE passes, scaled by the copy calibration), keyed
+    by kernel name; None when the file is missing or was measured on other
+    kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    digest, table = None, {}
+    with open(path) as fh:
+        for line in fh:
+            parts = line.split()
+            if len(parts) >= 2 and parts[0] == "sources_sha256":
+                digest = parts[1]
+            elif len(parts) >= 3 and parts[0] == "traffic_bytes":
+                table[parts[1]] = float(parts[2])
+    if digest != sources_digest():
+        return None
+    return table
 
 
 def cpu_baseline(wl, reps: int):
@@ -155,6 +208,8 @@ def decode_only(args, wl, dw):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        return copy_calibration()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path has no "
               "multi-GPU leg in this build", file=sys.stderr)
@@ -217,15 +272,20 @@ def main():
     cb = sum(coarsen_alg_bytes(c.call, c.lengths.cpu().numpy()) for c in step_calls)
     db = decode_alg_bytes(wl, lengths)
 
-    def roof(nbytes, ms):
+    traffic = measured_traffic(wl.name)
+
+    def roof(nbytes, ms, kernels):
         gbs = nbytes / (ms * 1e-3) / 1e9
+        t = None
+        if traffic is not None and all(k in traffic for k in kernels):
+            t = int(sum(traffic[k] for k in kernels))
         return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": t,
                 "alg_bytes_per_call": int(nbytes), "mean_call_us": round(ms * 1e3, 2)}
 
-    r_coarsen = roof(cb, coarsen_ms)
-    r_decode = roof(db, decode_ms)
-    r_coarsen["kernel"] = "spicy_coarsen (coarsen_plan + coarsen_main)"
+    r_coarsen = roof(cb, coarsen_ms, ["coarsen_plan_kernel", "coarsen_main_kernel", "coarsen_cpoint_kernel"])
+    r_decode = roof(db, decode_ms, ["decode_mfma_kernel", "combine_kernel"])
+    r_coarsen["kernel"] = "spicy_coarsen (coarsen_plan + coarsen_main + coarsen_cpoint)"
     r_decode["kernel"] = ("spicy_decode_attn_shared" if dw.shared_prefix_pages else "spicy_decode_attn") + \
         " (decode_mfma + combine)"
     dominant, other = (r_coarsen, r_decode) if coarsen_ms >= decode_ms else (r_decode, r_coarsen)

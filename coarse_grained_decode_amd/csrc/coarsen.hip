@@ -460,13 +460,19 @@ __device__ __forceinline__ void coarsen_segment(const CoarsenArgs& a, const Lane
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
+        // the barriers keep every load of one block ahead of the next block's,
+        // so each wait covers only the token about to be accumulated
         fetch(A, 0);
+        __builtin_amdgcn_sched_barrier(0);
         fetch(Bk, kRing);
+        __builtin_amdgcn_sched_barrier(0);
         for (int32_t u0 = 0; u0 < wn; u0 += 2 * kRing) {
             accumulate(A, u0);
             fetch(A, u0 + 2 * kRing);
+            __builtin_amdgcn_sched_barrier(0);
             accumulate(Bk, u0 + kRing);
             fetch(Bk, u0 + 3 * kRing);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 

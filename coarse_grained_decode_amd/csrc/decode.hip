@@ -232,7 +232,7 @@ struct Tile {
 //       [page_begin + split * pages_per_split, ...) of sequence b.
 // Pages are prefetched NBUF deep in registers.  Page ids are read 64 at a
 // time with one vector load, then each page's id is read out of its lane
-// (uniform).  Pages past the range's end load its last page again (every
+// (uniform).  Pages past the window's end load its last page again (every
 // load is unconditional, so each wait covers exactly one page); they are
 // never processed.
 template <int D, int NBUF>
@@ -306,25 +306,24 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
     Tile<D> T;
     T.init(row_valid ? static_cast<const uint16_t*>(a.q) + prow * D : nullptr, rlen);
 
-    int32_t ids = 0;
-    int32_t ids_base = -kWave;
-    auto load = [&](PageRegs<D>& r, int32_t lp) {
-        const int32_t q = min(lp, p1 - 1);
-        if (q - ids_base >= kWave) {            // uniform
-            ids_base = q;
-            ids = (q + lane < p1) ? table[q + lane] : 0;
-        }
-        load_page<D>(a, r, __builtin_amdgcn_readlane(ids, q - ids_base), h);
-    };
-
+    // Pages go in windows of 64: one vector load brings the window's page ids
+    // (lane i: page w0 + i) before its pipeline starts, so no wait inside the
+    // pipeline depends on it.
     PageRegs<D> buf[NBUF];
+    for (int32_t w0 = p0; w0 < p1; w0 += kWave) {
+        const int32_t w1 = min(w0 + kWave, p1);
+        const int32_t ids = (w0 + lane < w1) ? table[w0 + lane] : 0;
+        auto load = [&](PageRegs<D>& r, int32_t lp) {
+            load_page<D>(a, r, __builtin_amdgcn_readlane(ids, min(lp, w1 - 1) - w0), h);
+        };
 #pragma unroll
-    for (int i = 0; i < NBUF; ++i) load(buf[i], p0 + i);
-    for (int32_t lp = p0; lp < p1; lp += NBUF) {
+        for (int i = 0; i < NBUF; ++i) load(buf[i], w0 + i);
+        for (int32_t lp = w0; lp < w1; lp += NBUF) {
 #pragma unroll
-        for (int i = 0; i < NBUF; ++i) {
-            if (lp + i < p1) T.process(buf[i], lp + i);
-            load(buf[i], lp + i + NBUF);
+            for (int i = 0; i < NBUF; ++i) {
+                if (lp + i < w1) T.process(buf[i], lp + i);
+                load(buf[i], lp + i + NBUF);
+            }
         }
     }
     T.store(a, row_valid, prow, slot);
