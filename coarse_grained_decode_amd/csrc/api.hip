@@ -22,6 +22,7 @@ constexpr int32_t kPagesInFlight = 4;     // decode pipeline depth (pages per wa
 constexpr int32_t kMaxResidentWaves = 4096;
 constexpr int32_t kMaxSplits = 256;
 constexpr int32_t kMaxGridY = 65535;      // grid y/z extent limit (sequences, heads)
+constexpr int32_t kMaxPagesPerSeq = 1 << 23;  // entry ids fit the 27 bits a C-point item keeps
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -99,11 +100,14 @@ const char* spicy_status_string(spicy_status s) {
     return "unknown spicy_status";
 }
 
-size_t spicy_coarsen_workspace_bytes(int32_t B, int32_t n_seg, int32_t num_kv_heads) {
-    if (B < 0 || n_seg < 0 || num_kv_heads < 1) return 0;
+size_t spicy_coarsen_workspace_bytes(int32_t B, int32_t n_seg, int32_t total_tokens, int32_t num_kv_heads) {
+    if (B < 0 || n_seg < 0 || total_tokens < 0 || num_kv_heads < 1) return 0;
     const size_t ns = static_cast<size_t>(n_seg);
     const size_t nh = ns * static_cast<size_t>(num_kv_heads);
-    return SPICY_WORKSPACE_HEADER + align_up(16 * ns) + align_up(8 * nh);
+    const size_t items = static_cast<size_t>(total_tokens) * static_cast<size_t>(num_kv_heads);
+    const size_t nb = static_cast<size_t>(B);
+    return SPICY_WORKSPACE_HEADER + align_up(16 * ns) + align_up(8 * nh) + align_up(8 * items) + align_up(4 * nb) +
+           align_up(4 * nb * static_cast<size_t>(num_kv_heads));
 }
 
 spicy_status spicy_coarsen(const spicy_cache* cache, const void* k_pre, const void* v,
@@ -123,7 +127,8 @@ spicy_status spicy_coarsen(const spicy_cache* cache, const void* k_pre, const vo
     if (total_tokens > 0 && (!k_pre || !v || !protected_mask)) return SPICY_ERR_ARG;
     if (max_pages_per_seq < 1) return SPICY_ERR_ARG;
     if (cache->num_pages < 1) return SPICY_ERR_RANGE;
-    if (workspace_bytes < spicy_coarsen_workspace_bytes(B, n_seg, cache->num_kv_heads))
+    if (max_pages_per_seq > kMaxPagesPerSeq) return SPICY_ERR_UNSUPPORTED;
+    if (workspace_bytes < spicy_coarsen_workspace_bytes(B, n_seg, total_tokens, cache->num_kv_heads))
         return SPICY_ERR_CAPACITY;
 
     spicy::CoarsenArgs a{};
@@ -142,7 +147,14 @@ spicy_status spicy_coarsen(const spicy_cache* cache, const void* k_pre, const vo
     a.err = reinterpret_cast<int32_t*>(ws);
     const size_t ns = static_cast<size_t>(n_seg);
     a.seg_desc = reinterpret_cast<int4*>(ws + SPICY_WORKSPACE_HEADER);
-    a.seg_head = reinterpret_cast<int2*>(ws + SPICY_WORKSPACE_HEADER + align_up(16 * ns));
+    size_t off = SPICY_WORKSPACE_HEADER + align_up(16 * ns);
+    a.seg_head = reinterpret_cast<int2*>(ws + off);
+    off += align_up(8 * ns * static_cast<size_t>(cache->num_kv_heads));
+    a.cp_items = reinterpret_cast<int2*>(ws + off);
+    off += align_up(8 * static_cast<size_t>(total_tokens) * static_cast<size_t>(cache->num_kv_heads));
+    a.cp_count = reinterpret_cast<int32_t*>(ws + off);
+    off += align_up(4 * static_cast<size_t>(B));
+    a.null_from = reinterpret_cast<int32_t*>(ws + off);
     a.total_tokens = total_tokens;
     a.n_seg = n_seg;
     a.B = B;

@@ -8,11 +8,14 @@
 // member keys); protected ("C") tokens stay exact (mass 1, own position).
 //
 // Three kernels:
-//   coarsen_plan  one 1024-thread workgroup per sequence, one thread per
+//   coarsen_plan  one 256-thread workgroup per sequence, one thread per
 //                 segment: counts the protected tokens of each (segment,
-//                 head), block-scans the per-head entry counts into entry
-//                 offsets, writes a compact descriptor per segment, the
-//                 sequence's length and its null padding.
+//                 head) with 32 mask rows in flight, block-scans the per-head
+//                 entry counts into entry offsets (and the C-point counts into
+//                 item offsets), writes a compact descriptor per segment, then
+//                 lists the segment's C-points as items {token, entry, head}
+//                 in position order per head; records the sequence's length
+//                 and where each head's null padding starts.
 //   coarsen_main  one wavefront per segment and group of KV heads (4 heads at
 //                 d = 128).  A lane owns 8 consecutive dimensions of one head,
 //                 so one 16-byte load per lane reads a whole token row of the
@@ -20,11 +23,10 @@
 //                 F-tokens are accumulated branch-free in double precision
 //                 (mask as a 0/1 weight) and the macro-node is written at the
 //                 segment end.  Bound by reading K and V from HBM.
-//   coarsen_cpoint one workgroup per segment: the segment's protected tokens,
-//                 in position order per head, stored exact; every 16-lane
-//                 group takes its own (token, head) item, so a fully
-//                 protected segment (a recent window, a cluster of landmarks)
-//                 is spread over all the workgroup's lanes.
+//   coarsen_cpoint the listed C-point items, spread over ~1024 workgroups:
+//                 every 16-lane group stores one item at a time (value bits
+//                 copied, key rotated to the token's position), prefetching
+//                 the next; then the null entries the same way.
 //
 // Exactness: inputs are bf16 (8 significant bits).  Sums of bf16 values and
 // of their squares are exact in double precision for any realistic segment,
@@ -38,8 +40,9 @@ namespace spicy {
 
 namespace {
 
-constexpr int kPlanThreads = 1024;
+constexpr int kPlanThreads = 256;
 constexpr int kPlanWaves = kPlanThreads / kWave;
+constexpr int kCpointBlocksPerSeq = 64;
 constexpr int kMaxH = 16;
 constexpr int kRing = 4;
 constexpr int kResidentBlocks = 1024;   // 4 workgroups of 4 waves per CU
@@ -64,26 +67,6 @@ __device__ __forceinline__ int32_t entry_page(const CoarsenArgs& a, int b, int64
         return -1;
     }
     return P;
-}
-
-template <typename T, int D>
-__device__ void write_null(const CoarsenArgs& a, int b, int h, int64_t e, int elem) {
-    // one thread writes element `elem` of the key row and the value column;
-    // element 0 also writes the sidecars and the metadata
-    const int32_t P = entry_page(a, b, e);
-    if (P < 0) return;
-    const int slot = static_cast<int>(e % kPage);
-    const int64_t ph = static_cast<int64_t>(P) * a.cache.H + h;
-    T* k = static_cast<T*>(a.cache.k);
-    T* v = static_cast<T*>(a.cache.v);
-    k[(ph * kPage + slot) * D + elem] = Elem<T>::from_f32(0.f);
-    v[(ph * D + elem) * kPage + slot] = Elem<T>::from_f32(0.f);
-    if (elem == 0) {
-        T* ab = static_cast<T*>(a.cache.ab);
-        ab[(ph * kPage + slot) * 2 + 0] = Elem<T>::from_f32(-__builtin_huge_valf());
-        ab[(ph * kPage + slot) * 2 + 1] = Elem<T>::from_f32(0.f);
-        if (a.cache.meta) static_cast<Meta*>(a.cache.meta)[ph * kPage + slot] = Meta{0, 0, 0};
-    }
 }
 
 // 8 consecutive elements of one row: a 16-byte (bf16) or 32-byte (fp32) load
@@ -154,15 +137,63 @@ template <> struct Pack8<float> {
 
 // ------------------------------------------------------------------- plan
 
-template <typename T, int D>
-__global__ __launch_bounds__(kPlanThreads) void coarsen_plan_kernel(CoarsenArgs a) {
-    __shared__ int32_t s_wave[kPlanWaves][kMaxH];
-    __shared__ int32_t s_carry[kMaxH];
-    __shared__ int32_t s_ok;
+// Protection bits of token t (bit h = head h) from its mask row.  NQ > 0:
+// the row is NQ dwords (H = 4 NQ); NQ = 0: H bytes, read one by one (the
+// clamped index keeps every load unconditional).
+template <int NQ>
+__device__ __forceinline__ uint32_t row_bits(const CoarsenArgs& a, int32_t t) {
+    const int H = a.cache.H;
+    const uint8_t* row = a.mask + static_cast<int64_t>(t) * H;
+    uint32_t bits = 0;
+    if constexpr (NQ > 0) {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const uint32_t w = reinterpret_cast<const uint32_t*>(row)[q];
+#pragma unroll
+            for (int y = 0; y < 4; ++y)
+                if ((w >> (8 * y)) & 0xFFu) bits |= 1u << (4 * q + y);
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < kMaxH; ++q) {
+            const uint8_t x = row[min(q, H - 1)];
+            if (q < H && x) bits |= 1u << q;
+        }
+    }
+    return bits;
+}
+
+// Inclusive sum over the workgroup's threads (in thread order) of x, given
+// the wave-level scratch; returns this thread's inclusive prefix and leaves
+// the workgroup total in *total.  All threads must call it.
+__device__ __forceinline__ int block_inclusive_scan(int x, int32_t* s_wave, int* total) {
+    const int lane = threadIdx.x % kWave;
+    const int wave = threadIdx.x / kWave;
+    int incl = x;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+    }
+    if (lane == kWave - 1) s_wave[wave] = incl;
+    __syncthreads();
+    int before = 0, tot = 0;
+    for (int w = 0; w < kPlanWaves; ++w) {
+        before += w < wave ? s_wave[w] : 0;
+        tot += s_wave[w];
+    }
+    __syncthreads();
+    *total = tot;
+    return before + incl;
+}
+
+template <typename T, int D, int NQ>
+__device__ __forceinline__ void plan_sequence(const CoarsenArgs& a, int32_t (*s_wave)[kPlanWaves],
+                                              int32_t (*s_next)[kPlanThreads], int32_t& s_ok) {
+    constexpr int NH = NQ > 0 ? 4 * NQ : kMaxH;      // heads a mask row can hold
+    constexpr int kRound = NQ > 0 ? 32 : 4;          // mask rows in flight per thread
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
-    const int lane = tid % kWave;
-    const int wave = tid / kWave;
     const int H = a.cache.H;
 
     const int32_t t0 = a.seq_offsets[b], t1 = a.seq_offsets[b + 1];
@@ -176,11 +207,11 @@ __global__ __launch_bounds__(kPlanThreads) void coarsen_plan_kernel(CoarsenArgs 
         if (!ok) {
             raise_err(a.err, SPICY_DEVERR_SEGMENTS);
             a.lengths_out[b] = e0 < 0 ? 0 : e0;
+            a.cp_count[b] = 0;
         }
         if (b == a.B - 1 && a.seq_seg_ptr[a.B] != a.n_seg) raise_err(a.err, SPICY_DEVERR_SEGMENTS);
         if (b == 0 && a.seq_seg_ptr[0] != 0) raise_err(a.err, SPICY_DEVERR_SEGMENTS);
     }
-    if (tid < kMaxH) s_carry[tid] = 0;
     __syncthreads();
     // segments no valid sequence owns are marked so that coarsen_main skips them
     if (b == a.B - 1) {
@@ -194,11 +225,15 @@ __global__ __launch_bounds__(kPlanThreads) void coarsen_plan_kernel(CoarsenArgs 
     if (!s_ok) {
         if (ranges_sane)
             for (int32_t s = s0 + tid; s < s1; s += kPlanThreads) a.seg_desc[s] = make_int4(-1, 0, 0, 0);
+        if (tid < H) a.null_from[static_cast<int64_t>(b) * H + tid] = INT32_MAX;
         return;
     }
 
     const int32_t pos_off = (a.pos_base ? a.pos_base[b] : 0) - t0;
-    const bool dword_rows = (H % 4) == 0;
+    int2* items = a.cp_items + static_cast<int64_t>(t0) * H;
+    int carry[kMaxH + 1];                      // entries per head, then C-point items, so far
+#pragma unroll
+    for (int h = 0; h <= kMaxH; ++h) carry[h] = 0;
 
     for (int32_t base = s0; base < s1; base += kPlanThreads) {
         const int32_t s = base + tid;
@@ -213,102 +248,105 @@ __global__ __launch_bounds__(kPlanThreads) void coarsen_plan_kernel(CoarsenArgs 
                 raise_err(a.err, SPICY_DEVERR_SEGMENTS);
                 sa = sz = t0;
             }
-            // protected tokens per head (mask rows read as dwords when aligned)
-            if (dword_rows && H == 4) {
-                // one dword per token; 16 tokens per round, loads clamped to
-                // the segment so they can all be in flight together
-                for (int32_t tb = sa; tb < sz; tb += 16) {
-                    uint32_t w[16];
+            // protected tokens per head, kRound mask rows in flight
+            for (int32_t tb = sa; tb < sz; tb += kRound) {
+                uint32_t w[kRound];
 #pragma unroll
-                    for (int u = 0; u < 16; ++u)
-                        w[u] = reinterpret_cast<const uint32_t*>(a.mask)[min(tb + u, sz - 1)];
+                for (int u = 0; u < kRound; ++u) w[u] = row_bits<NQ>(a, min(tb + u, sz - 1));
 #pragma unroll
-                    for (int u = 0; u < 16; ++u) {
-                        const uint32_t x = tb + u < sz ? w[u] : 0u;
-                        cnt[0] += (x & 0xFFu) != 0;
-                        cnt[1] += (x & 0xFF00u) != 0;
-                        cnt[2] += (x & 0xFF0000u) != 0;
-                        cnt[3] += (x & 0xFF000000u) != 0;
-                    }
-                }
-            } else if (dword_rows) {
-                for (int32_t t = sa; t < sz; ++t) {
-                    const uint32_t* row = reinterpret_cast<const uint32_t*>(a.mask + static_cast<int64_t>(t) * H);
+                for (int u = 0; u < kRound; ++u) {
+                    const uint32_t bits = tb + u < sz ? w[u] : 0u;
 #pragma unroll
-                    for (int q = 0; q < kMaxH / 4; ++q) {
-                        if (4 * q < H) {
-                            const uint32_t w = row[q];
-                            cnt[4 * q + 0] += (w & 0xFFu) != 0;
-                            cnt[4 * q + 1] += (w & 0xFF00u) != 0;
-                            cnt[4 * q + 2] += (w & 0xFF0000u) != 0;
-                            cnt[4 * q + 3] += (w & 0xFF000000u) != 0;
-                        }
-                    }
-                }
-            } else {
-                for (int32_t t = sa; t < sz; ++t) {
-#pragma unroll
-                    for (int h = 0; h < kMaxH; ++h)
-                        if (h < H) cnt[h] += a.mask[static_cast<int64_t>(t) * H + h] != 0;
+                    for (int h = 0; h < NH; ++h) cnt[h] += (bits >> h) & 1u;
                 }
             }
             a.seg_desc[s] = make_int4(b, sa, sz, pos_off);
         }
-        // entries per head: protected tokens + one macro-node if any F-token
-        int c[kMaxH], incl[kMaxH];
+        // entries per head: protected tokens + one macro-node if any F-token;
+        // C-point items: protected (token, head) pairs of the segment
+        int first[kMaxH], has_f[kMaxH];
+        int ncount = 0, item0 = 0;
 #pragma unroll
         for (int h = 0; h < kMaxH; ++h) {
-            c[h] = (s < s1 && h < H) ? cnt[h] + ((sz - sa - cnt[h]) > 0 ? 1 : 0) : 0;
-            incl[h] = c[h];
+            const bool live = s < s1 && h < H;
+            has_f[h] = live && (sz - sa - cnt[h]) > 0 ? 1 : 0;
+            ncount += live ? cnt[h] : 0;
         }
-        // block-wide inclusive scan per head: within waves, then across waves
 #pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-#pragma unroll
-            for (int h = 0; h < kMaxH; ++h) {
-                if (h < H) {
-                    const int y = __shfl_up(incl[h], o);
-                    if (lane >= o) incl[h] += y;
+        for (int h = 0; h <= kMaxH; ++h) {
+            if (h < H || h == kMaxH) {         // uniform: every thread scans alike
+                const int x = h == kMaxH ? ncount : (s < s1 ? cnt[h] + has_f[h] : 0);
+                int tot;
+                const int incl = block_inclusive_scan(x, s_wave[h], &tot);
+                if (h < kMaxH) {
+                    first[h] = e0 + carry[h] + incl - x;
+                } else {
+                    item0 = carry[kMaxH] + incl - x;
                 }
+                carry[h] += tot;
             }
         }
-        if (lane == kWave - 1)
-            for (int h = 0; h < H; ++h) s_wave[wave][h] = incl[h];
-        __syncthreads();
         if (s < s1) {
 #pragma unroll
-            for (int h = 0; h < kMaxH; ++h) {
-                if (h < H) {
-                    int before = s_carry[h];
-                    for (int w = 0; w < wave; ++w) before += s_wave[w][h];
-                    a.seg_head[static_cast<int64_t>(s) * H + h] =
-                        make_int2(e0 + before + incl[h] - c[h], (sz - sa - cnt[h]) > 0 ? 1 : 0);
+            for (int h = 0; h < kMaxH; ++h)
+                if (h < H) a.seg_head[static_cast<int64_t>(s) * H + h] = make_int2(first[h], has_f[h]);
+            // the segment's C-point items, in position order within each head
+            // (s_next: this thread's next entry per head)
+#pragma unroll
+            for (int h = 0; h < kMaxH; ++h)
+                if (h < H) s_next[h][tid] = first[h] + has_f[h];
+            int64_t k = item0;
+            const int32_t cap = a.max_pages * kPage;
+            for (int32_t tb = sa; tb < sz && ncount > 0; tb += kRound) {
+                uint32_t w[kRound];
+#pragma unroll
+                for (int u = 0; u < kRound; ++u) w[u] = row_bits<NQ>(a, min(tb + u, sz - 1));
+#pragma unroll
+                for (int u = 0; u < kRound; ++u) {
+                    uint32_t bits = tb + u < sz ? w[u] : 0u;
+                    while (bits) {
+                        const int h = __builtin_ctz(bits);
+                        bits &= bits - 1;
+                        // an entry past the table's capacity is clamped to its
+                        // end, which the storing kernel reports
+                        const int32_t e = min(s_next[h][tid], cap);
+                        s_next[h][tid] += 1;
+                        items[k] = make_int2(tb + u, (e << 4) | h);
+                        k += 1;
+                    }
                 }
             }
         }
-        __syncthreads();
-        if (tid < H) {
-            int tot = 0;
-            for (int w = 0; w < kPlanWaves; ++w) tot += s_wave[w][tid];
-            s_carry[tid] += tot;
-        }
-        __syncthreads();
     }
 
-    // length and null padding
+    // length, C-point count and where each head's null padding starts
+    // (coarsen_cpoint writes the nulls)
     int32_t most = 0;
-    for (int h = 0; h < H; ++h) most = max(most, s_carry[h]);
+    for (int h = 0; h < H; ++h) most = max(most, carry[h]);
     const int64_t len = static_cast<int64_t>(e0) + most;
     const int64_t padded = (len + kPage - 1) / kPage * kPage;
     if (tid == 0) {
         a.lengths_out[b] = static_cast<int32_t>(len);
+        a.cp_count[b] = carry[kMaxH];
         if (padded / kPage > a.max_pages) raise_err(a.err, SPICY_DEVERR_CAPACITY);
     }
-    for (int h = 0; h < H; ++h) {
-        const int64_t first = static_cast<int64_t>(e0) + s_carry[h];
-        const int64_t n = (padded - first) * D;
-        for (int64_t i = tid; i < n; i += kPlanThreads)
-            write_null<T, D>(a, b, h, first + i / D, static_cast<int>(i % D));
+#pragma unroll
+    for (int h = 0; h < kMaxH; ++h)
+        if (h < H && tid == h) a.null_from[static_cast<int64_t>(b) * H + h] = e0 + carry[h];
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kPlanThreads) void coarsen_plan_kernel(CoarsenArgs a) {
+    __shared__ int32_t s_wave[kMaxH + 1][kPlanWaves];
+    __shared__ int32_t s_next[kMaxH][kPlanThreads];
+    __shared__ int32_t s_ok;
+    // mask rows read as H / 4 dwords when H is a multiple of 4, else as bytes
+    switch (a.cache.H % 4 == 0 ? a.cache.H / 4 : 0) {
+    case 1: plan_sequence<T, D, 1>(a, s_wave, s_next, s_ok); break;
+    case 2: plan_sequence<T, D, 2>(a, s_wave, s_next, s_ok); break;
+    case 3: plan_sequence<T, D, 3>(a, s_wave, s_next, s_ok); break;
+    case 4: plan_sequence<T, D, 4>(a, s_wave, s_next, s_ok); break;
+    default: plan_sequence<T, D, 0>(a, s_wave, s_next, s_ok); break;
     }
 }
 
@@ -503,128 +541,64 @@ __global__ __launch_bounds__(256) void coarsen_main_kernel(CoarsenArgs a) {
         coarsen_segment<T, D>(a, L, s);
 }
 
-// coarsen_cpoint: the protected tokens of one segment, stored exact after the
-// segment's macro-node in position order per head, by one whole workgroup.
-// For each 64-token block the protected (token, head) items are
-// enumerated head by head in position order, so an item's index within its
-// head is its rank; each group of LPH lanes stores one item (4 items per
-// wavefront step at d = 128) and the next step's rows are prefetched.
+// coarsen_cpoint: every C-point item {token, entry, head} that coarsen_plan
+// listed, stored exact (value bits copied, key rotated to the token's own
+// position, alpha = beta = 0).  Workgroups (x, b) share the items of
+// sequence b; each 16-lane group (8 at d = 64) takes every G-th item and
+// prefetches the next one's rows while it rotates and stores the current one.
 template <typename T, int D>
-__device__ __forceinline__ void cpoint_segment(const CoarsenArgs& a, int32_t s) {
-    constexpr int LPH = D / 8;
-    constexpr int HW = kWave / LPH;           // heads per wavefront (and items per step)
+__global__ __launch_bounds__(256) void coarsen_cpoint_kernel(CoarsenArgs a) {
+    constexpr int LPH = D / 8;                // lanes per item
+    constexpr int IPW = kWave / LPH;          // items per wavefront step
     constexpr int PARTNER = LPH / 2;
+    const int b = blockIdx.y;
     const int H = a.cache.H;
-    const int4 desc = a.seg_desc[s];
-    const int32_t b = desc.x, sa = desc.y, sz = desc.z;
-    if (b < 0 || b >= a.B || !(0 <= sa && sa < sz && sz <= a.total_tokens)) return;
+    const int32_t t0 = a.seq_offsets[b], t1 = a.seq_offsets[b + 1];
+    int32_t n = a.cp_count[b];
+    if (n < 0 || t0 < 0 || t0 > t1 || t1 > a.total_tokens || n > static_cast<int64_t>(t1 - t0) * H) n = 0;
     const int lane = threadIdx.x % kWave;
-    const int wave = threadIdx.x / kWave;
-    const int nwaves = blockDim.x / kWave;
-    const int hbase = blockIdx.y * HW;
-    const int grp = lane / LPH;
+    const int grp = (threadIdx.x / kWave) * IPW + lane / LPH;
+    const int ngrp = (blockDim.x / kWave) * IPW;
     const int j = lane % LPH;
     const bool hi_half = j >= PARTNER;
     const int d0 = 8 * j;
-    const int64_t pos_off = desc.w;
+    const int64_t pos_off = static_cast<int64_t>(a.pos_base ? a.pos_base[b] : 0) - t0;
+    const bool rotate = a.rope_base > 0.0;
+    double theta[4];
+    {
+        const int pair0 = 8 * (hi_half ? j - PARTNER : j) + (hi_half ? 4 : 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) theta[r] = a.theta[pair0 + r];
+    }
+    const int2* items = a.cp_items + static_cast<int64_t>(t0) * H;
     const T* kin = static_cast<const T*>(a.k_pre);
     const T* vin = static_cast<const T*>(a.v);
-    const bool rotate = a.rope_base > 0.0;
-    bool have_theta = false;
-    double theta[4];
 
-    int32_t running[HW];                      // C-points of each head in earlier blocks
-#pragma unroll
-    for (int q = 0; q < HW; ++q) running[q] = 0;
-
-    for (int32_t blk = sa; blk < sz; blk += kWave) {
-        // which of the group's heads protect token blk + lane
-        const int32_t t = blk + lane;
-        uint32_t bits = 0;
-        if (t < sz) {
-            const uint8_t* row = a.mask + static_cast<int64_t>(t) * H + hbase;
-            if (H % 4 == 0 && hbase + HW <= H) {
-#pragma unroll
-                for (int q = 0; q < HW / 4; ++q) {
-                    const uint32_t w = reinterpret_cast<const uint32_t*>(row)[q];
-#pragma unroll
-                    for (int y = 0; y < 4; ++y)
-                        if ((w >> (8 * y)) & 0xFFu) bits |= 1u << (4 * q + y);
-                }
-            } else {
-#pragma unroll
-                for (int q = 0; q < HW; ++q)
-                    if (hbase + q < H && row[q]) bits |= 1u << q;
-            }
-        }
-        uint64_t hb[HW];
-        int pre[HW + 1];
-        pre[0] = 0;
-#pragma unroll
-        for (int q = 0; q < HW; ++q) {
-            hb[q] = __ballot((bits >> q) & 1u);
-            pre[q + 1] = pre[q] + __popcll(hb[q]);
-        }
-        const int n = pre[HW];
-        if (n > 0 && !have_theta) {
-            const int pair0 = 8 * (hi_half ? j - PARTNER : j) + (hi_half ? 4 : 0);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                theta[r] = a.theta[pair0 + r];
-            have_theta = true;
-        }
-
-        // item p -> (head q, token tc, entry e); invalid items read a valid row
-        auto locate = [&](int p, int& q, int32_t& tc, int64_t& e, bool& valid) {
-            valid = p < n;
-            const int pp = valid ? p : 0;
-            q = 0;
-#pragma unroll
-            for (int y = 1; y < HW; ++y) q += (pp >= pre[y]) ? 1 : 0;
-            uint64_t m = 0;
-            int before = 0, rk = 0;
-#pragma unroll
-            for (int y = 0; y < HW; ++y)
-                if (y == q) { m = hb[y]; before = pre[y]; rk = running[y]; }
-            for (int k = pp - before; k > 0; --k) m &= m - 1;
-            tc = valid ? blk + __ffsll(static_cast<unsigned long long>(m)) - 1 : sa;
-            const int h = min(hbase + q, H - 1);
-            const int2 hd = a.seg_head[static_cast<int64_t>(s) * H + h];
-            e = static_cast<int64_t>(hd.x) + hd.y + rk + (pp - before);
-        };
-        auto load_rows = [&](int q, int32_t tc, Row8<T>& kx, Row8<T>& vx) {
-            const int h = min(hbase + q, H - 1);
-            const int64_t base = (static_cast<int64_t>(tc) * H + h) * D + d0;
-            kx.load(kin + base);
-            vx.load(vin + base);
-        };
-
-        const int steps = (n + HW - 1) / HW;
-        int q0;
-        int32_t tc0;
-        int64_t e0;
-        bool v0;
-        Row8<T> k0, vv0;
-        int st = wave;
-        if (st < steps) {
-            locate(st * HW + grp, q0, tc0, e0, v0);
-            load_rows(q0, tc0, k0, vv0);
-        }
-        for (; st < steps; st += nwaves) {
-            // prefetch this wave's next step
-            int q1 = 0;
-            int32_t tc1 = sa;
-            int64_t e1 = 0;
-            bool v1 = false;
-            Row8<T> k1, vv1;
-            if (st + nwaves < steps) {
-                locate((st + nwaves) * HW + grp, q1, tc1, e1, v1);
-                load_rows(q1, tc1, k1, vv1);
-            }
-            double x[8], y[8];
-#pragma unroll
-            for (int r = 0; r < 8; ++r) x[r] = k0.f64(r);
-            const double pos = static_cast<double>(tc0 + pos_off);
+    // item i -> its rows; indexes are checked so a bad list never reads out of bounds
+    auto fetch = [&](int32_t i, int2& it, Row8<T>& kx, Row8<T>& vx) {
+        it = items[min(i, n - 1)];
+        const int32_t t = min(max(it.x, t0), t1 - 1);
+        const int h = min(it.y & 15, H - 1);
+        const int64_t base = (static_cast<int64_t>(t) * H + h) * D + d0;
+        kx.load(kin + base);
+        vx.load(vin + base);
+    };
+    const int32_t stride = gridDim.x * ngrp;
+    int32_t i = blockIdx.x * ngrp + grp;
+    if (i < n) {
+        int2 it0;
+        Row8<T> k0, v0;
+        fetch(i, it0, k0, v0);
+        for (; i < n; i += stride) {
+            int2 it1;
+            Row8<T> k1, v1;
+            const bool more = i + stride < n;
+            fetch(more ? i + stride : i, it1, k1, v1);
+            const int32_t t = it0.x;
+            const int h = it0.y & 15;
+            const int64_t e = static_cast<uint32_t>(it0.y) >> 4;
+            const double pos = static_cast<double>(t + pos_off);
+            double y[8];
             if (rotate) {
                 double c4[4], s4[4], cs[8], sn[8];
 #pragma unroll
@@ -640,43 +614,75 @@ __device__ __forceinline__ void cpoint_segment(const CoarsenArgs& a, int32_t s) 
                 }
 #pragma unroll
                 for (int r = 0; r < 8; ++r) {
-                    const double other = __shfl_xor(x[r], PARTNER);
-                    y[r] = hi_half ? x[r] * cs[r] + other * sn[r] : x[r] * cs[r] - other * sn[r];
+                    const double x = k0.f64(r);
+                    const double other = __shfl_xor(x, PARTNER);
+                    y[r] = hi_half ? x * cs[r] + other * sn[r] : x * cs[r] - other * sn[r];
                 }
             } else {
 #pragma unroll
-                for (int r = 0; r < 8; ++r) y[r] = x[r];
+                for (int r = 0; r < 8; ++r) y[r] = k0.f64(r);
             }
-            if (v0) {
-                const int h = hbase + q0;
-                const int32_t Pg = entry_page(a, b, e0);
-                if (Pg >= 0) {
-                    const int slot = static_cast<int>(e0 % kPage);
-                    const int64_t ph = static_cast<int64_t>(Pg) * H + h;
-                    Pack8<T>::store(static_cast<T*>(a.cache.k) + (ph * kPage + slot) * D + d0, y);
-                    T* vcol = static_cast<T*>(a.cache.v) + (ph * D + d0) * kPage + slot;
+            const bool sane = t >= t0 && t < t1 && h < H;
+            if (!sane) raise_err(a.err, SPICY_DEVERR_SEGMENTS);
+            const int32_t Pg = sane ? entry_page(a, b, e) : -1;
+            if (Pg >= 0) {
+                const int slot = static_cast<int>(e % kPage);
+                const int64_t ph = static_cast<int64_t>(Pg) * H + h;
+                Pack8<T>::store(static_cast<T*>(a.cache.k) + (ph * kPage + slot) * D + d0, y);
+                T* vcol = static_cast<T*>(a.cache.v) + (ph * D + d0) * kPage + slot;
 #pragma unroll
-                    for (int r = 0; r < 8; ++r) vcol[r * kPage] = vv0.raw(r);
-                    if (j == 0) {
-                        T* abc = static_cast<T*>(a.cache.ab);
-                        abc[(ph * kPage + slot) * 2 + 0] = Elem<T>::from_f32(0.f);
-                        abc[(ph * kPage + slot) * 2 + 1] = Elem<T>::from_f32(0.f);
-                        const int64_t p = tc0 + pos_off;
-                        if (a.cache.meta) static_cast<Meta*>(a.cache.meta)[ph * kPage + slot] = Meta{1, 1, p};
-                    }
+                for (int r = 0; r < 8; ++r) vcol[r * kPage] = v0.raw(r);
+                if (j == 0) {
+                    T* abc = static_cast<T*>(a.cache.ab);
+                    abc[(ph * kPage + slot) * 2 + 0] = Elem<T>::from_f32(0.f);
+                    abc[(ph * kPage + slot) * 2 + 1] = Elem<T>::from_f32(0.f);
+                    if (a.cache.meta) static_cast<Meta*>(a.cache.meta)[ph * kPage + slot] = Meta{1, 1, t + pos_off};
                 }
             }
-            q0 = q1; tc0 = tc1; e0 = e1; v0 = v1; k0 = k1; vv0 = vv1;
+            it0 = it1;
+            k0 = k1;
+            v0 = v1;
         }
-#pragma unroll
-        for (int q = 0; q < HW; ++q) running[q] += pre[q + 1] - pre[q];
     }
-}
 
-template <typename T, int D>
-__global__ __launch_bounds__(256) void coarsen_cpoint_kernel(CoarsenArgs a) {
-    // persistent: workgroup g takes segments g, g + G, g + 2G, ...
-    for (int32_t s = blockIdx.x; s < a.n_seg; s += gridDim.x) cpoint_segment<T, D>(a, s);
+    // null entries: each head from its own end up to the end of the
+    // sequence's last page (k = v = 0, alpha = -inf, beta = 0)
+    const int64_t len = a.lengths_out[b];
+    const int64_t padded = (len + kPage - 1) / kPage * kPage;
+    int64_t units = 0;
+    for (int h = 0; h < H; ++h) {
+        const int64_t c = padded - a.null_from[static_cast<int64_t>(b) * H + h];
+        units += c > 0 ? c : 0;
+    }
+    for (int64_t u = static_cast<int64_t>(blockIdx.x) * ngrp + grp; u < units; u += stride) {
+        int64_t rem = u, e = 0;
+        int h = 0;
+        for (int q = 0; q < H; ++q) {
+            const int64_t nf = a.null_from[static_cast<int64_t>(b) * H + q];
+            const int64_t cnt = padded - nf > 0 ? padded - nf : 0;
+            if (rem < cnt) {
+                h = q;
+                e = nf + rem;
+                break;
+            }
+            rem -= cnt;
+        }
+        const int32_t Pg = entry_page(a, b, e);
+        if (Pg < 0) continue;
+        const int slot = static_cast<int>(e % kPage);
+        const int64_t ph = static_cast<int64_t>(Pg) * H + h;
+        const double zero[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        Pack8<T>::store(static_cast<T*>(a.cache.k) + (ph * kPage + slot) * D + d0, zero);
+        T* vcol = static_cast<T*>(a.cache.v) + (ph * D + d0) * kPage + slot;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) vcol[r * kPage] = Elem<T>::from_f32(0.f);
+        if (j == 0) {
+            T* abc = static_cast<T*>(a.cache.ab);
+            abc[(ph * kPage + slot) * 2 + 0] = Elem<T>::from_f32(-__builtin_huge_valf());
+            abc[(ph * kPage + slot) * 2 + 1] = Elem<T>::from_f32(0.f);
+            if (a.cache.meta) static_cast<Meta*>(a.cache.meta)[ph * kPage + slot] = Meta{0, 0, 0};
+        }
+    }
 }
 
 // ------------------------------------------------------------------ launch
@@ -693,8 +699,12 @@ static spicy_status launch_coarsen_t(const CoarsenArgs& a, hipStream_t stream) {
         dim3 grid(nblk, (a.cache.H + HW - 1) / HW);
         hipLaunchKernelGGL((coarsen_main_kernel<T, D>), grid, dim3(wpb * kWave), 0, stream, a);
         if (hipGetLastError() != hipSuccess) return SPICY_ERR_HIP;
-        dim3 cgrid(min(a.n_seg, kResidentBlocks), (a.cache.H + HW - 1) / HW);
-        hipLaunchKernelGGL((coarsen_cpoint_kernel<T, D>), cgrid, dim3(256), 0, stream, a);
+    }
+    {
+        // C-point items and null entries: about kResidentBlocks workgroups
+        // shared by the sequences
+        const int cx = max(1, min(kCpointBlocksPerSeq, kResidentBlocks / max(a.B, 1)));
+        hipLaunchKernelGGL((coarsen_cpoint_kernel<T, D>), dim3(cx, a.B), dim3(256), 0, stream, a);
         if (hipGetLastError() != hipSuccess) return SPICY_ERR_HIP;
     }
     return SPICY_OK;

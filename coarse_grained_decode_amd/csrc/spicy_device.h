@@ -139,6 +139,10 @@ struct CoarsenArgs {
     int32_t* err;          // workspace header word
     int4* seg_desc;        // [n_seg]     {sequence (-1 = skip), first token, end token, position offset}
     int2* seg_head;        // [n_seg][H]  {first entry of the segment, has a macro-node}
+    int2* cp_items;        // C-points of sequence b at [seq_offsets[b] * H, + cp_count[b]):
+                           //   {token, entry << 4 | head}
+    int32_t* cp_count;     // [B]
+    int32_t* null_from;    // [B][H]      first null-padding entry of each head (INT32_MAX: none)
     int32_t total_tokens;
     int32_t n_seg;
     int32_t B;

@@ -99,9 +99,11 @@ typedef struct {
     void* meta;             /* device or NULL                                */
 } spicy_cache;
 
-/* Workspace bytes spicy_coarsen needs for `n_seg` segments over `B`
- * sequences and `num_kv_heads` heads (header + per segment/head offsets). */
-size_t spicy_coarsen_workspace_bytes(int32_t B, int32_t n_seg, int32_t num_kv_heads);
+/* Workspace bytes spicy_coarsen needs for `n_seg` segments and
+ * `total_tokens` tokens over `B` sequences and `num_kv_heads` heads (header,
+ * per segment and per (segment, head) plan, a list of C-point items of up
+ * to total_tokens x num_kv_heads entries, per (sequence, head) counts). */
+size_t spicy_coarsen_workspace_bytes(int32_t B, int32_t n_seg, int32_t total_tokens, int32_t num_kv_heads);
 
 /* spicy_coarsen — build compressed entries for B sequences.
  *
@@ -135,10 +137,10 @@ size_t spicy_coarsen_workspace_bytes(int32_t B, int32_t n_seg, int32_t num_kv_he
  *   entry count.  RoPE uses the half-split pairing (i, i+d/2) with
  *   theta_i = rope_base^(-2i/d); rope_base <= 0 means no rotation.  Values are
  *   accumulated in double precision and rounded once, to nearest-even, on store.
- * Workspace: device, >= spicy_coarsen_workspace_bytes(B, n_seg, H_kv) bytes,
+ * Workspace: device, >= spicy_coarsen_workspace_bytes(B, n_seg, total_tokens, H_kv) bytes,
  *   first int32 = sticky device error word (not cleared by the library).
  * Errors: SPICY_ERR_ARG (null required pointer, B < 0, n_seg < 0, bad dtype),
- *   SPICY_ERR_UNSUPPORTED (head_dim not 64/128, H_kv > 64),
+ *   SPICY_ERR_UNSUPPORTED (head_dim not 64/128, H_kv > 16, max_pages_per_seq > 2^23),
  *   SPICY_ERR_CAPACITY (workspace too small), SPICY_ERR_HIP. */
 spicy_status spicy_coarsen(const spicy_cache* cache,              /* host struct */
                            const void* k_pre, const void* v, int32_t total_tokens,

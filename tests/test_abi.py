@@ -71,8 +71,11 @@ def test_workspace_and_split_plan(lib):
     assert cgd.spicy_decode_shared_workspace_bytes(2, 4, 2, 64, 40, 0, 0) == \
         cgd.spicy_decode_workspace_bytes(2, 4, 2, 64, 40, 0)
     assert cgd.spicy_decode_shared_workspace_bytes(2, 4, 2, 64, 40, -1, 0) == 0
-    assert cgd.spicy_coarsen_workspace_bytes(2, 10, 4) == 256 + 256 + 512
-    assert cgd.spicy_coarsen_workspace_bytes(-1, 10, 4) == 0
+    # header, 16 B per segment, 8 B per (segment, head), 8 B per C-point
+    # item (at most tokens x heads), 4 B per sequence and per (sequence, head)
+    assert cgd.spicy_coarsen_workspace_bytes(2, 10, 100, 4) == 256 + 256 + 512 + 3328 + 256 + 256
+    assert cgd.spicy_coarsen_workspace_bytes(-1, 10, 100, 4) == 0
+    assert cgd.spicy_coarsen_workspace_bytes(2, 10, -1, 4) == 0
 
 
 def _cache(dtype=1, H=4, d=128, pages=8, k=1, v=1, ab=1):
@@ -139,6 +142,7 @@ def test_coarsen_rejects_bad_arguments(lib):
     assert call(nseg=-1) == 1
     assert call(total=-1) == 1
     assert call(maxp=0) == 1
+    assert call(maxp=(1 << 23) + 1) == 4   # entry ids would not fit a C-point item
     assert call(cache=_cache(pages=0)) == 2
     assert call(wsb=100) == 3
     assert call(B=0) == 0
