@@ -187,11 +187,23 @@ __device__ __forceinline__ int block_inclusive_scan(int x, int32_t* s_wave, int*
     return before + incl;
 }
 
+// kRound mask rows of tokens tb .. tb+kRound-1 of a segment ending at sz,
+// all loads in flight together (indexes clamped into the segment and the
+// input, so every load is unconditional and in bounds).
+template <int NQ, int kRound>
+__device__ __forceinline__ void load_round(const CoarsenArgs& a, int32_t tb, int32_t sz, uint32_t (&w)[kRound]) {
+    const int32_t last = min(sz, a.total_tokens) - 1;
+#pragma unroll
+    for (int u = 0; u < kRound; ++u) w[u] = row_bits<NQ>(a, max(min(tb + u, last), 0));
+}
+
+// One workgroup plans sequence b: per segment (one thread each) the
+// protected tokens of every head, block scans into entry and item offsets,
+// descriptors, and the C-point items in position order per head.
 template <typename T, int D, int NQ>
-__device__ __forceinline__ void plan_sequence(const CoarsenArgs& a, int32_t (*s_wave)[kPlanWaves],
-                                              int32_t (*s_next)[kPlanThreads], int32_t& s_ok) {
+__device__ __forceinline__ void plan_sequence(const CoarsenArgs& a, int32_t (*s_wave)[kPlanWaves], int32_t& s_ok) {
     constexpr int NH = NQ > 0 ? 4 * NQ : kMaxH;      // heads a mask row can hold
-    constexpr int kRound = NQ > 0 ? 32 : 4;          // mask rows in flight per thread
+    constexpr int kRound = NQ > 0 ? 64 / NQ : 8;     // mask rows in flight per thread
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
     const int H = a.cache.H;
@@ -200,6 +212,15 @@ __device__ __forceinline__ void plan_sequence(const CoarsenArgs& a, int32_t (*s_
     const int32_t s0 = a.seq_seg_ptr[b], s1 = a.seq_seg_ptr[b + 1];
     const int32_t e0 = a.entry_start ? a.entry_start[b] : 0;
     const bool ranges_sane = 0 <= s0 && s0 <= s1 && s1 <= a.n_seg;
+    // this thread's first segment and its first mask rows are read before the
+    // sequence is validated (every index is bounded by the array it reads)
+    int32_t sa = 0, sz = 0;
+    uint32_t w[kRound];
+    if (ranges_sane && s0 + tid < s1) {
+        sa = a.seg_offsets[s0 + tid];
+        sz = a.seg_offsets[s0 + tid + 1];
+    }
+    load_round<NQ, kRound>(a, sa, sz, w);
     if (tid == 0) {
         bool ok = ranges_sane && 0 <= t0 && t0 <= t1 && t1 <= a.total_tokens && e0 >= 0;
         if (ok) ok = a.seg_offsets[s0] == t0 && a.seg_offsets[s1] == t1;
@@ -231,28 +252,32 @@ __device__ __forceinline__ void plan_sequence(const CoarsenArgs& a, int32_t (*s_
 
     const int32_t pos_off = (a.pos_base ? a.pos_base[b] : 0) - t0;
     int2* items = a.cp_items + static_cast<int64_t>(t0) * H;
+    const int32_t cap = a.max_pages * kPage;
     int carry[kMaxH + 1];                      // entries per head, then C-point items, so far
 #pragma unroll
     for (int h = 0; h <= kMaxH; ++h) carry[h] = 0;
 
     for (int32_t base = s0; base < s1; base += kPlanThreads) {
         const int32_t s = base + tid;
-        int cnt[kMaxH];
+        if (base != s0) {                      // later rounds of segments: read now
+            sa = sz = 0;
+            if (s < s1) {
+                sa = a.seg_offsets[s];
+                sz = a.seg_offsets[s + 1];
+            }
+            load_round<NQ, kRound>(a, sa, sz, w);
+        }
+        int cnt[NH];
 #pragma unroll
-        for (int h = 0; h < kMaxH; ++h) cnt[h] = 0;
-        int32_t sa = 0, sz = 0;
+        for (int h = 0; h < NH; ++h) cnt[h] = 0;
         if (s < s1) {
-            sa = a.seg_offsets[s];
-            sz = a.seg_offsets[s + 1];
             if (!(t0 <= sa && sa <= sz && sz <= t1)) {
                 raise_err(a.err, SPICY_DEVERR_SEGMENTS);
                 sa = sz = t0;
             }
-            // protected tokens per head, kRound mask rows in flight
+            // protected tokens per head; w holds the segment's first round
             for (int32_t tb = sa; tb < sz; tb += kRound) {
-                uint32_t w[kRound];
-#pragma unroll
-                for (int u = 0; u < kRound; ++u) w[u] = row_bits<NQ>(a, min(tb + u, sz - 1));
+                if (tb != sa) load_round<NQ, kRound>(a, tb, sz, w);
 #pragma unroll
                 for (int u = 0; u < kRound; ++u) {
                     const uint32_t bits = tb + u < sz ? w[u] : 0u;
@@ -264,54 +289,58 @@ __device__ __forceinline__ void plan_sequence(const CoarsenArgs& a, int32_t (*s_
         }
         // entries per head: protected tokens + one macro-node if any F-token;
         // C-point items: protected (token, head) pairs of the segment
-        int first[kMaxH], has_f[kMaxH];
+        int first[NH], has_f[NH];
         int ncount = 0, item0 = 0;
 #pragma unroll
-        for (int h = 0; h < kMaxH; ++h) {
+        for (int h = 0; h < NH; ++h) {
             const bool live = s < s1 && h < H;
             has_f[h] = live && (sz - sa - cnt[h]) > 0 ? 1 : 0;
             ncount += live ? cnt[h] : 0;
+            first[h] = 0;
         }
 #pragma unroll
-        for (int h = 0; h <= kMaxH; ++h) {
-            if (h < H || h == kMaxH) {         // uniform: every thread scans alike
-                const int x = h == kMaxH ? ncount : (s < s1 ? cnt[h] + has_f[h] : 0);
+        for (int h = 0; h <= NH; ++h) {
+            if (h < H || h == NH) {            // uniform: every thread scans alike
+                const int x = h == NH ? ncount : (s < s1 ? cnt[h] + has_f[h] : 0);
                 int tot;
                 const int incl = block_inclusive_scan(x, s_wave[h], &tot);
-                if (h < kMaxH) {
+                if (h < NH) {
                     first[h] = e0 + carry[h] + incl - x;
+                    carry[h] += tot;
                 } else {
                     item0 = carry[kMaxH] + incl - x;
+                    carry[kMaxH] += tot;
                 }
-                carry[h] += tot;
             }
         }
         if (s < s1) {
 #pragma unroll
-            for (int h = 0; h < kMaxH; ++h)
+            for (int h = 0; h < NH; ++h)
                 if (h < H) a.seg_head[static_cast<int64_t>(s) * H + h] = make_int2(first[h], has_f[h]);
             // the segment's C-point items, in position order within each head
-            // (s_next: this thread's next entry per head)
+            int nxt[NH];
 #pragma unroll
-            for (int h = 0; h < kMaxH; ++h)
-                if (h < H) s_next[h][tid] = first[h] + has_f[h];
+            for (int h = 0; h < NH; ++h) nxt[h] = first[h] + has_f[h];
             int64_t k = item0;
-            const int32_t cap = a.max_pages * kPage;
             for (int32_t tb = sa; tb < sz && ncount > 0; tb += kRound) {
-                uint32_t w[kRound];
-#pragma unroll
-                for (int u = 0; u < kRound; ++u) w[u] = row_bits<NQ>(a, min(tb + u, sz - 1));
+                if (sz - sa > kRound) load_round<NQ, kRound>(a, tb, sz, w);   // else still in w
 #pragma unroll
                 for (int u = 0; u < kRound; ++u) {
                     uint32_t bits = tb + u < sz ? w[u] : 0u;
                     while (bits) {
                         const int h = __builtin_ctz(bits);
                         bits &= bits - 1;
+                        int32_t e = 0;
+#pragma unroll
+                        for (int q = 0; q < NH; ++q) {
+                            if (q == h) {
+                                e = nxt[q];
+                                nxt[q] = e + 1;
+                            }
+                        }
                         // an entry past the table's capacity is clamped to its
                         // end, which the storing kernel reports
-                        const int32_t e = min(s_next[h][tid], cap);
-                        s_next[h][tid] += 1;
-                        items[k] = make_int2(tb + u, (e << 4) | h);
+                        items[k] = make_int2(tb + u, (min(e, cap) << 4) | h);
                         k += 1;
                     }
                 }
@@ -322,7 +351,9 @@ __device__ __forceinline__ void plan_sequence(const CoarsenArgs& a, int32_t (*s_
     // length, C-point count and where each head's null padding starts
     // (coarsen_cpoint writes the nulls)
     int32_t most = 0;
-    for (int h = 0; h < H; ++h) most = max(most, carry[h]);
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+        if (h < H) most = max(most, carry[h]);
     const int64_t len = static_cast<int64_t>(e0) + most;
     const int64_t padded = (len + kPage - 1) / kPage * kPage;
     if (tid == 0) {
@@ -331,22 +362,21 @@ __device__ __forceinline__ void plan_sequence(const CoarsenArgs& a, int32_t (*s_
         if (padded / kPage > a.max_pages) raise_err(a.err, SPICY_DEVERR_CAPACITY);
     }
 #pragma unroll
-    for (int h = 0; h < kMaxH; ++h)
+    for (int h = 0; h < NH; ++h)
         if (h < H && tid == h) a.null_from[static_cast<int64_t>(b) * H + h] = e0 + carry[h];
 }
 
 template <typename T, int D>
 __global__ __launch_bounds__(kPlanThreads) void coarsen_plan_kernel(CoarsenArgs a) {
     __shared__ int32_t s_wave[kMaxH + 1][kPlanWaves];
-    __shared__ int32_t s_next[kMaxH][kPlanThreads];
     __shared__ int32_t s_ok;
     // mask rows read as H / 4 dwords when H is a multiple of 4, else as bytes
     switch (a.cache.H % 4 == 0 ? a.cache.H / 4 : 0) {
-    case 1: plan_sequence<T, D, 1>(a, s_wave, s_next, s_ok); break;
-    case 2: plan_sequence<T, D, 2>(a, s_wave, s_next, s_ok); break;
-    case 3: plan_sequence<T, D, 3>(a, s_wave, s_next, s_ok); break;
-    case 4: plan_sequence<T, D, 4>(a, s_wave, s_next, s_ok); break;
-    default: plan_sequence<T, D, 0>(a, s_wave, s_next, s_ok); break;
+    case 1: plan_sequence<T, D, 1>(a, s_wave, s_ok); break;
+    case 2: plan_sequence<T, D, 2>(a, s_wave, s_ok); break;
+    case 3: plan_sequence<T, D, 3>(a, s_wave, s_ok); break;
+    case 4: plan_sequence<T, D, 4>(a, s_wave, s_ok); break;
+    default: plan_sequence<T, D, 0>(a, s_wave, s_ok); break;
     }
 }
 
