@@ -113,8 +113,8 @@ def _stream(stream) -> int | None:
 class PagedCache:
     """Caller-owned paged compressed cache (device tensors in the library's layout).
 
-    k    [num_pages, H_kv, 16, d]       rotated key rows
-    v    [num_pages, H_kv, d, 16]       dim-major value tiles
+    k    [num_pages, H_kv, d/32, 16, 32] rotated key rows, cut in 32-dim chunks
+    v    [num_pages, H_kv, d/32, 16, 32] value rows, the same way
     ab   [num_pages, H_kv, 16, 2]       (alpha, beta)
     meta [num_pages, H_kv, 16, 4] int32 {kind, mass, pos_sum lo, pos_sum hi} or None
     """
@@ -127,8 +127,8 @@ class PagedCache:
     def empty(num_pages: int, H_kv: int, d: int, dtype: torch.dtype, device, meta: bool = True,
               fill: float | None = None) -> "PagedCache":
         mk = torch.empty if fill is None else (lambda *s, **kw: torch.full(s, fill, **kw))
-        k = mk(num_pages, H_kv, PAGE_SIZE, d, dtype=dtype, device=device)
-        v = mk(num_pages, H_kv, d, PAGE_SIZE, dtype=dtype, device=device)
+        k = mk(num_pages, H_kv, d // 32, PAGE_SIZE, 32, dtype=dtype, device=device)
+        v = mk(num_pages, H_kv, d // 32, PAGE_SIZE, 32, dtype=dtype, device=device)
         ab = mk(num_pages, H_kv, PAGE_SIZE, 2, dtype=dtype, device=device)
         mt = torch.zeros(num_pages, H_kv, PAGE_SIZE, 4, dtype=torch.int32, device=device) if meta else None
         return PagedCache(k, v, ab, mt)
@@ -143,7 +143,7 @@ class PagedCache:
 
     @property
     def head_dim(self) -> int:
-        return int(self.k.shape[3])
+        return int(self.k.shape[2] * self.k.shape[4])
 
     @property
     def dtype_code(self) -> int:

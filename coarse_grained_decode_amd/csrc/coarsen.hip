@@ -133,6 +133,28 @@ template <> struct Pack8<float> {
     }
 };
 
+// 8 consecutive elements given one by one, stored with one (bf16) or two
+// (fp32) 16-byte writes.
+template <typename T> struct Store8;
+template <> struct Store8<uint16_t> {
+    template <typename F>
+    __device__ __forceinline__ static void store(uint16_t* p, const F& f) {
+        uint4 o;
+        o.x = f(0) | (static_cast<uint32_t>(f(1)) << 16);
+        o.y = f(2) | (static_cast<uint32_t>(f(3)) << 16);
+        o.z = f(4) | (static_cast<uint32_t>(f(5)) << 16);
+        o.w = f(6) | (static_cast<uint32_t>(f(7)) << 16);
+        *reinterpret_cast<uint4*>(p) = o;
+    }
+};
+template <> struct Store8<float> {
+    template <typename F>
+    __device__ __forceinline__ static void store(float* p, const F& f) {
+        *reinterpret_cast<float4*>(p) = make_float4(f(0), f(1), f(2), f(3));
+        *reinterpret_cast<float4*>(p + 4) = make_float4(f(4), f(5), f(6), f(7));
+    }
+};
+
 }  // namespace
 
 // ------------------------------------------------------------------- plan
@@ -449,10 +471,8 @@ __device__ __forceinline__ void store_entry(const CoarsenArgs& a, const Lanes<T,
     if (Pg < 0) return;
     const int slot = static_cast<int>(e % kPage);
     const int64_t ph = static_cast<int64_t>(Pg) * a.cache.H + L.h;
-    Pack8<T>::store(static_cast<T*>(a.cache.k) + (ph * kPage + slot) * D + L.d0, y);
-    T* vcol = static_cast<T*>(a.cache.v) + (ph * D + L.d0) * kPage + slot;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) vcol[r * kPage] = vsrc(r);
+    Pack8<T>::store(static_cast<T*>(a.cache.k) + ph * kPage * D + slot_elem(slot, L.d0), y);
+    Store8<T>::store(static_cast<T*>(a.cache.v) + ph * kPage * D + slot_elem(slot, L.d0), vsrc);
     if (L.j == 0) {
         T* abc = static_cast<T*>(a.cache.ab);
         abc[(ph * kPage + slot) * 2 + 0] = Elem<T>::from_f64(alpha);
@@ -658,10 +678,9 @@ __global__ __launch_bounds__(256) void coarsen_cpoint_kernel(CoarsenArgs a) {
             if (Pg >= 0) {
                 const int slot = static_cast<int>(e % kPage);
                 const int64_t ph = static_cast<int64_t>(Pg) * H + h;
-                Pack8<T>::store(static_cast<T*>(a.cache.k) + (ph * kPage + slot) * D + d0, y);
-                T* vcol = static_cast<T*>(a.cache.v) + (ph * D + d0) * kPage + slot;
-#pragma unroll
-                for (int r = 0; r < 8; ++r) vcol[r * kPage] = v0.raw(r);
+                Pack8<T>::store(static_cast<T*>(a.cache.k) + ph * kPage * D + slot_elem(slot, d0), y);
+                Store8<T>::store(static_cast<T*>(a.cache.v) + ph * kPage * D + slot_elem(slot, d0),
+                                 [&](int r) { return v0.raw(r); });
                 if (j == 0) {
                     T* abc = static_cast<T*>(a.cache.ab);
                     abc[(ph * kPage + slot) * 2 + 0] = Elem<T>::from_f32(0.f);
@@ -702,10 +721,8 @@ __global__ __launch_bounds__(256) void coarsen_cpoint_kernel(CoarsenArgs a) {
         const int slot = static_cast<int>(e % kPage);
         const int64_t ph = static_cast<int64_t>(Pg) * H + h;
         const double zero[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        Pack8<T>::store(static_cast<T*>(a.cache.k) + (ph * kPage + slot) * D + d0, zero);
-        T* vcol = static_cast<T*>(a.cache.v) + (ph * D + d0) * kPage + slot;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) vcol[r * kPage] = Elem<T>::from_f32(0.f);
+        Pack8<T>::store(static_cast<T*>(a.cache.k) + ph * kPage * D + slot_elem(slot, d0), zero);
+        Pack8<T>::store(static_cast<T*>(a.cache.v) + ph * kPage * D + slot_elem(slot, d0), zero);
         if (j == 0) {
             T* abc = static_cast<T*>(a.cache.ab);
             abc[(ph * kPage + slot) * 2 + 0] = Elem<T>::from_f32(-__builtin_huge_valf());

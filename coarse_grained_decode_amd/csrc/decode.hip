@@ -17,9 +17,12 @@
 //   exactly the B operand of the next product, so the probabilities go from
 //   exp2 to bf16 to MFMA without any lane exchange:
 //   O^T[d x 16 rows] += V^T_page[d x 16 entries] . P^T[16 entries x 16 rows]
-//       d/16 x v_mfma_f32_16x16x16_bf16.  Value tiles are stored dim-major in
-//       the page, so each lane's 4 entries of one dimension are 8 contiguous
-//       bytes.
+//       d/16 x v_mfma_f32_16x16x16_bf16.  Values are stored like keys (rows
+//       cut in 32-dim chunks, so the coarsening writes 64-byte pieces and a
+//       chunk of all 16 slots is one contiguous 1 KB load); each
+//       32-dim chunk becomes two V^T operand tiles through two MFMAs with
+//       0/1 selector matrices (exact), whose accumulator layout is the A
+//       operand layout the product needs.
 // One launch holds two kinds of workgroups:
 //   split-K: one wavefront per (sequence, KV head, split).  Its tile is the
 //       G = H_q / H_kv query heads of that KV head, and it prefetches its pages
@@ -73,7 +76,7 @@ __device__ __forceinline__ int32_t checked_length(const DecodeArgs& a, int b) {
 template <int D>
 struct PageRegs {
     bf16x8 k[D / 32];      // K rows: entry lane%16, dims 32i + 8(lane/16) .. +8
-    s16x4 v[D / 16];       // V^T tile t: dim 16t + lane%16, entries 4(lane/16) .. +4
+    bf16x8 v[D / 32];      // V rows, the same way
     bf16x8 ab;             // (alpha, beta) of entries 4(lane/16) .. +4
     bool ok;               // page id was valid (uniform)
 };
@@ -83,18 +86,18 @@ struct PageRegs {
 template <int D>
 __device__ __forceinline__ void load_page(const DecodeArgs& a, PageRegs<D>& r, int32_t pid, int h) {
     constexpr int KC = D / 32;
-    constexpr int NT = D / 16;
     const int lane = threadIdx.x % kWave;
     const int row = lane % 16, grp = lane / 16;
     r.ok = pid >= 0 && pid < a.cache.num_pages;
     if (!r.ok) raise_err(a.err, SPICY_DEVERR_PAGE_ID);
     const int64_t ph = static_cast<int64_t>(r.ok ? pid : 0) * a.cache.H + h;
-    const uint16_t* kp = static_cast<const uint16_t*>(a.cache.k) + ph * kPage * D + row * D + 8 * grp;
+    // chunk i of all 16 slots is 1 KB: one load per lane covers it
+    const uint16_t* kp = static_cast<const uint16_t*>(a.cache.k) + ph * kPage * D + slot_elem(row, 8 * grp);
 #pragma unroll
-    for (int i = 0; i < KC; ++i) r.k[i] = *reinterpret_cast<const bf16x8*>(kp + 32 * i);
-    const uint16_t* vp = static_cast<const uint16_t*>(a.cache.v) + ph * D * kPage + row * kPage + 4 * grp;
+    for (int i = 0; i < KC; ++i) r.k[i] = *reinterpret_cast<const bf16x8*>(kp + kPage * kChunk * i);
+    const uint16_t* vp = static_cast<const uint16_t*>(a.cache.v) + ph * kPage * D + slot_elem(row, 8 * grp);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) r.v[t] = *reinterpret_cast<const s16x4*>(vp + 16 * kPage * t);
+    for (int i = 0; i < KC; ++i) r.v[i] = *reinterpret_cast<const bf16x8*>(vp + kPage * kChunk * i);
     r.ab = *reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(a.cache.ab) + ph * kPage * 2 + 8 * grp);
 }
 
@@ -104,6 +107,7 @@ struct Tile {
     static constexpr int KC = D / 32;
     static constexpr int NT = D / 16;
     bf16x8 q[KC];          // B operand of S^T = K Q^T: 8 dims of each 32-dim chunk
+    bf16x8 sel[2];         // B operands [I; 0] and [0; I] (32 x 16) that transpose V
     float c_beta;          // |q|^2 log2(e) of this lane's row
     int32_t len;           // entries of this row's sequence (0 for a padding row)
     int32_t vlen;          // uniform: largest len of the tile
@@ -130,6 +134,14 @@ struct Tile {
         n2 += __shfl_xor(n2, 16);
         n2 += __shfl_xor(n2, 32);
         c_beta = n2 * kLog2e;
+        // lane (column c = lane%16, k-group g) holds rows 8g .. 8g+7 of a
+        // selector: [I; 0] has a one at row c, [0; I] at row 16 + c
+        const int c = threadIdx.x % 16;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            sel[0][j] = static_cast<__bf16>(8 * grp + j == c ? 1.f : 0.f);
+            sel[1][j] = static_cast<__bf16>(8 * grp + j == 16 + c ? 1.f : 0.f);
+        }
         len = rowq ? length : 0;
         int32_t mx = len;
 #pragma unroll
@@ -173,22 +185,30 @@ struct Tile {
         const bf16x4 pb = {static_cast<__bf16>(p[0]), static_cast<__bf16>(p[1]),
                            static_cast<__bf16>(p[2]), static_cast<__bf16>(p[3])};
         const s16x4 pk = __builtin_bit_cast(s16x4, pb);
-        if (lp * kPage + kPage <= vlen) {
+        // V^T tiles for the product: V_chunk (16 entries x 32 dims, loaded as
+        // an A operand like K) times a selector gives V^T of 16 of its dims in
+        // the accumulator layout (lane: entries 4g .. 4g+3 of dim lane%16),
+        // exactly the A operand layout of O^T += V^T P^T.  The products are
+        // exact: one bf16 term per output, the rest zeros.
+        const bool partial = lp * kPage + kPage > vlen;
 #pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                acc[t] *= scale;
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(r.v[t], pk, acc[t], 0, 0, 0);
-            }
-        } else {
-            // a page past the end of some row: slots no row uses may hold
-            // anything, so their values are zeroed (0 * NaN would poison the
-            // product)
+        for (int i = 0; i < KC; ++i) {
 #pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                s16x4 vt = r.v[t];
+            for (int hsel = 0; hsel < 2; ++hsel) {
+                const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                const f32x4 vtf = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.v[i], sel[hsel], z, 0, 0, 0);
+                uint32_t u[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (ebase + j >= vlen) vt[j] = 0;
+                for (int j = 0; j < 4; ++j) {
+                    u[j] = __float_as_uint(vtf[j]);
+                    // slots no row uses may hold anything: zero their values so
+                    // that 0 * NaN cannot poison the product
+                    if (partial && ebase + j >= vlen) u[j] = 0;
+                }
+                const uint32_t w0 = __builtin_amdgcn_perm(u[1], u[0], 0x07060302u);
+                const uint32_t w1 = __builtin_amdgcn_perm(u[3], u[2], 0x07060302u);
+                const s16x4 vt = __builtin_bit_cast(s16x4, make_uint2(w0, w1));
+                const int t = 2 * i + hsel;
                 acc[t] *= scale;
                 acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pk, acc[t], 0, 0, 0);
             }
@@ -384,7 +404,7 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
             continue;
         }
         const int64_t ph = static_cast<int64_t>(pid) * H + h;
-        const float* krow = kpool + (ph * kPage + ent) * D + qtr * QD;
+        const float* krow = kpool + ph * kPage * D + slot_elem(ent, qtr * QD);   // QD <= 32: one chunk
         float dot = 0.f;
 #pragma unroll
         for (int i = 0; i < QD; ++i) dot += qv[i] * krow[i];
@@ -403,14 +423,14 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
         const float p = fast_exp2(s2 - msub);
         l_run = l_run * scale + (qtr == 0 ? p : 0.f);
         m_run = m_new;
+        const float* vpage = vpool + ph * kPage * D;
 #pragma unroll
         for (int j = 0; j < DL; ++j) {
-            const float* vrow = vpool + (ph * D + lane + kWave * j) * kPage;
             float o = acc[j] * scale;
 #pragma unroll
             for (int e = 0; e < kPage; ++e) {
                 const float pe = __shfl(p, 4 * e);
-                if (lp * kPage + e < len) o += pe * vrow[e];
+                if (lp * kPage + e < len) o += pe * vpage[slot_elem(e, lane + kWave * j)];
             }
             acc[j] = o;
         }

@@ -11,6 +11,14 @@ namespace spicy {
 
 constexpr int kPage = 16;      // entries per page
 constexpr int kWave = 64;      // gfx950 wavefront
+constexpr int kChunk = 32;     // dims per chunk of a key/value page row
+
+// Offset of element (slot s, dim i) inside a page-head's 16 x d key or value
+// block: 32-dim chunks outermost, then the 16 slots, then the chunk's dims.
+// One chunk of all 16 slots is 1 KB of bf16, read by one wavefront-wide load.
+__device__ __forceinline__ int slot_elem(int s, int i) {
+    return ((i / kChunk) * kPage + s) * kChunk + i % kChunk;
+}
 
 // ---------------------------------------------------------------- numerics
 

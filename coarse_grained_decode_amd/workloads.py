@@ -431,10 +431,18 @@ def make_shared_prefix(config_id: int = 4, *, B: int = 32, H_q: int = 28, H_kv: 
                                 f"{chunk_T}-token chunk per step, equal-variation N={N}")
 
 
+def chunked(x: np.ndarray) -> np.ndarray:
+    """[P, H, 16, d] entry rows in the cache's page layout [P, H, d/W, 16, W],
+    W = min(32, d)."""
+    P, H, S, d = x.shape
+    W = d if d < 32 else 32
+    return np.ascontiguousarray(x.reshape(P, H, S, d // W, W).transpose(0, 1, 3, 2, 4))
+
+
 @dataclasses.dataclass
 class DecodeCase:
     """Cache contents and a batch for decode-only cases (no coarsening):
-    k [P, H, 16, d], v [P, H, d, 16], ab [P, H, 16, 2] in storage format
+    k, v [P, H, d/W, 16, W] (the cache's page layout), ab [P, H, 16, 2] in storage format
     (bf16 bits or float32), page_table int32 [B, max_pages], lengths int32 [B],
     q [B, H_q, d]."""
     dtype: str
@@ -464,7 +472,7 @@ def random_decode_case(seed: int, *, B: int, H_q: int, H_kv: int, d: int, dtype:
     num_pages = prefix_pages + int(npriv.sum())
     max_pages = prefix_pages + int(npriv.max())
     k = rng.standard_normal((num_pages, H_kv, PAGE, d), dtype=np.float32)
-    v = rng.standard_normal((num_pages, H_kv, d, PAGE), dtype=np.float32)
+    v = rng.standard_normal((num_pages, H_kv, PAGE, d), dtype=np.float32)
     ab = np.empty((num_pages, H_kv, PAGE, 2), dtype=np.float32)
     ab[..., 0] = rng.uniform(0.0, 4.0, size=ab.shape[:-1])
     ab[..., 0][rng.random(ab.shape[:-1]) < null_frac] = -np.inf
@@ -482,11 +490,11 @@ def random_decode_case(seed: int, *, B: int, H_q: int, H_kv: int, d: int, dtype:
         lengths[b] = (prefix_pages + n - 1) * PAGE + used
         last = table[b, prefix_pages + n - 1]
         k[last, :, used:, :] = np.nan
-        v[last, :, :, used:] = np.nan
+        v[last, :, used:, :] = np.nan
         ab[last, :, used:, :] = np.nan
     q = rng.standard_normal((B, H_q, d), dtype=np.float32)
-    return DecodeCase(dtype, H_q, H_kv, d, _store(k, dtype), _store(v, dtype), _store(ab, dtype),
-                      table, lengths, _store(q, dtype), prefix_pages)
+    return DecodeCase(dtype, H_q, H_kv, d, _store(chunked(k), dtype), _store(chunked(v), dtype),
+                      _store(ab, dtype), table, lengths, _store(q, dtype), prefix_pages)
 
 
 def tiny_fp32(**over) -> Workload:

@@ -43,9 +43,11 @@
  * Paged compressed cache (caller-allocated pool of `num_pages` pages; one page
  * holds PAGE_SIZE = 16 consecutive logical entries of one sequence for all KV
  * heads):
- *   k    : [num_pages][H_kv][16][d]   entry-major key rows, already rotated
- *                                     (RoPE) to the entry's position
- *   v    : [num_pages][H_kv][d][16]   dim-major value tile
+ *   k    : [num_pages][H_kv][d/32][16][32]  key rows, already rotated (RoPE)
+ *                                     to the entry's position, cut in 32-dim
+ *                                     chunks: element (slot s, dim i) of a
+ *                                     page-head is at ((i/32)*16 + s)*32 + i%32
+ *   v    : [num_pages][H_kv][d/32][16][32]  value rows, the same way
  *   ab   : [num_pages][H_kv][16][2]   per entry (alpha, beta):
  *                                     alpha = ln(mass), beta = sigma^2/(2d);
  *                                     a null entry has alpha = -inf

@@ -84,14 +84,28 @@ def default_threads() -> int:
     return max(1, min(16, os.cpu_count() or 1))
 
 
+def chunk_width(d: int) -> int:
+    """Dims per chunk of the key/value page layout: min(32, d)."""
+    return d if d < 32 else 32
+
+
+def rows(x: np.ndarray) -> np.ndarray:
+    """[P, H, d/W, 16, W] key or value pages as [P, H, 16, d] entry rows (copy)."""
+    P, H, C, S, W = x.shape
+    return np.ascontiguousarray(x.transpose(0, 1, 3, 2, 4)).reshape(P, H, S, C * W)
+
+
 class Cache:
-    """Host copy of a paged compressed cache in the library's layout."""
+    """Host copy of a paged compressed cache in the library's layout:
+    k, v [P, H, d/W, 16, W] (entry rows cut in chunks of W = min(32, d) dims),
+    ab [P, H, 16, 2], meta [P, H, 16]."""
 
     def __init__(self, store: str, num_pages: int, H_kv: int, d: int, fill: bool = True):
         self.store, self.num_pages, self.H_kv, self.d = store, num_pages, H_kv, d
         dt = NP[store]
-        self.k = np.empty((num_pages, H_kv, PAGE, d), dtype=dt)
-        self.v = np.empty((num_pages, H_kv, d, PAGE), dtype=dt)
+        W = chunk_width(d)
+        self.k = np.empty((num_pages, H_kv, d // W, PAGE, W), dtype=dt)
+        self.v = np.empty((num_pages, H_kv, d // W, PAGE, W), dtype=dt)
         self.ab = np.empty((num_pages, H_kv, PAGE, 2), dtype=dt)
         self.meta = np.zeros((num_pages, H_kv, PAGE), dtype=META_DTYPE)
         if fill:  # recognisable garbage so that unwritten slots never look valid

@@ -110,6 +110,18 @@ typedef struct {
     const int32_t* table_row;
 } cache_view;
 
+/* Offset of element (slot, i) inside a page-head block of 16 x d values:
+ * chunks of W = min(32, d) dimensions outermost, then the 16 slots, then the
+ * W dims of the chunk (the cache layout the header documents; for d < 32 it
+ * is plain entry-major rows). */
+static size_t slot_elem(int32_t d, int32_t slot, int32_t i) {
+    const int32_t W = d < 32 ? d : 32;
+    return ((size_t)(i / W) * PAGE + (size_t)slot) * (size_t)W + (size_t)(i % W);
+}
+
+/* Head sizes the chunked layout can hold: below 32, or a multiple of 32. */
+static int head_dim_ok(int32_t d) { return d > 0 && (d < 32 || d % 32 == 0); }
+
 /* Store one entry at logical index e of a sequence.  key and val are
  * d-vectors already in their final (rotated) form. */
 static int put_entry(const cache_view* c, int32_t h, int64_t e,
@@ -123,8 +135,8 @@ static int put_entry(const cache_view* c, int32_t h, int64_t e,
     int32_t slot = (int32_t)(e % PAGE);
     size_t ph = (size_t)P * (size_t)c->H + (size_t)h;
     for (int32_t i = 0; i < c->d; ++i) {
-        store_elem(c->dtype, c->k, (ph * PAGE + (size_t)slot) * (size_t)c->d + (size_t)i, key[i]);
-        store_elem(c->dtype, c->v, (ph * (size_t)c->d + (size_t)i) * PAGE + (size_t)slot, val[i]);
+        store_elem(c->dtype, c->k, ph * PAGE * (size_t)c->d + slot_elem(c->d, slot, i), key[i]);
+        store_elem(c->dtype, c->v, ph * PAGE * (size_t)c->d + slot_elem(c->d, slot, i), val[i]);
     }
     store_elem(c->dtype, c->ab, (ph * PAGE + (size_t)slot) * 2 + 0, alpha);
     store_elem(c->dtype, c->ab, (ph * PAGE + (size_t)slot) * 2 + 1, beta);
@@ -168,7 +180,7 @@ int oracle_coarsen(int in_dtype, int dtype, int32_t H_kv, int32_t d,
                    const int32_t* entry_start, int32_t* lengths_out,
                    int32_t b_begin, int32_t b_end) {
     if (dtype < 0 || dtype > 2 || in_dtype < 0 || in_dtype > 2) return 1;
-    if (H_kv <= 0 || d <= 0 || (d % 2) != 0 || B < 0) return 1;
+    if (H_kv <= 0 || !head_dim_ok(d) || (d % 2) != 0 || B < 0) return 1;
     if (!k_pre || !v || !seq_offsets || !seg_offsets || !seq_seg_ptr || !protected_mask) return 1;
     if (!k_pool || !v_pool || !ab_pool || !page_table || !lengths_out) return 1;
     if (b_begin < 0 || b_end > B || b_begin > b_end) return 1;
@@ -290,7 +302,7 @@ int oracle_decode(int q_dtype, int dtype, int32_t H_q, int32_t H_kv, int32_t d,
                   double* o, double* lse,
                   int32_t b_begin, int32_t b_end) {
     if (dtype < 0 || dtype > 2 || q_dtype < 0 || q_dtype > 2) return 1;
-    if (H_q <= 0 || H_kv <= 0 || d <= 0 || (H_q % H_kv) != 0) return 1;
+    if (H_q <= 0 || H_kv <= 0 || !head_dim_ok(d) || (H_q % H_kv) != 0) return 1;
     if (!q || !k_pool || !v_pool || !ab_pool || !page_table || !lengths || !o || !lse) return 1;
     if (b_begin < 0 || b_end > B || b_begin > b_end) return 1;
     int32_t G = H_q / H_kv;
@@ -333,7 +345,7 @@ int oracle_decode(int q_dtype, int dtype, int32_t H_q, int32_t H_kv, int32_t d,
                 double dot = 0.0;
                 for (int32_t i = 0; i < d; ++i)
                     dot += load_elem(q_dtype, q, qo + (size_t)i) *
-                           load_elem(dtype, k_pool, (ph * PAGE + (size_t)slot) * (size_t)d + (size_t)i);
+                           load_elem(dtype, k_pool, ph * PAGE * (size_t)d + slot_elem(d, slot, i));
                 s[e] = dot / sqrt((double)d) + alpha + qn2 * beta;
                 if (s[e] > smax) smax = s[e];
             }
@@ -353,7 +365,7 @@ int oracle_decode(int q_dtype, int dtype, int32_t H_q, int32_t H_kv, int32_t d,
                 size_t ph = (size_t)row[e / PAGE] * (size_t)H_kv + (size_t)h;
                 int32_t slot = e % PAGE;
                 for (int32_t i = 0; i < d; ++i)
-                    out[i] += w * load_elem(dtype, v_pool, (ph * (size_t)d + (size_t)i) * PAGE + (size_t)slot);
+                    out[i] += w * load_elem(dtype, v_pool, ph * PAGE * (size_t)d + slot_elem(d, slot, i));
             }
         }
     }

@@ -84,8 +84,7 @@ def compare_cache(dw, ref: oracle.Cache, lengths: np.ndarray):
     # values: C-points are bit copies; macro-node means within 1 ulp
     kind = rm["kind"]
     cpt = (kind == 1)
-    vt = np.swapaxes(gv, -1, -2)       # [P, H, 16, d]
-    rvt = np.swapaxes(rv, -1, -2)
+    vt, rvt = oracle.rows(gv), oracle.rows(rv)      # [P, H, 16, d]
     assert np.array_equal(vt[cpt], rvt[cpt]), "C-point values are not exact copies"
     assert ulp_dist(vt, rvt, store).max() <= 1, "values differ by > 1 ulp"
     dk = ulp_dist(gk, rk, store)

@@ -41,7 +41,7 @@ def run(call, store="f64", q=None, H_q=None):
 def entry(cache, call, b, h, e):
     P = call.page_table[b, e // 16]
     s = e % 16
-    return dict(k=cache.k[P, h, s].astype(np.float64), v=cache.v[P, h, :, s].astype(np.float64),
+    return dict(k=oracle.rows(cache.k)[P, h, s].astype(np.float64), v=oracle.rows(cache.v)[P, h, s].astype(np.float64),
                 alpha=float(cache.ab[P, h, s, 0]), beta=float(cache.ab[P, h, s, 1]),
                 kind=int(cache.meta[P, h, s]["kind"]), mass=int(cache.meta[P, h, s]["mass"]),
                 pos_sum=int(cache.meta[P, h, s]["pos_sum"]))
