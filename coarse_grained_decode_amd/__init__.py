@@ -69,7 +69,7 @@ def load_library():
     L.spicy_status_string.restype = ctypes.c_char_p
     L.spicy_status_string.argtypes = [ctypes.c_int]
     L.spicy_coarsen_workspace_bytes.restype = sz
-    L.spicy_coarsen_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    L.spicy_coarsen_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     L.spicy_coarsen.restype = ctypes.c_int
     L.spicy_coarsen.argtypes = [CP, P, P, i32, P, P, P, P, i32, P, i32, ctypes.c_double, P, i32,
                                 P, P, P, sz, P]
@@ -158,8 +158,10 @@ class PagedCache:
                       _ptr(self.k), _ptr(self.v), _ptr(self.ab), _ptr(self.meta))
 
 
-def spicy_coarsen_workspace_bytes(B: int, n_seg: int, total_tokens: int, num_kv_heads: int) -> int:
-    return int(load_library().spicy_coarsen_workspace_bytes(B, n_seg, total_tokens, num_kv_heads))
+def spicy_coarsen_workspace_bytes(B: int, n_seg: int, total_tokens: int, num_kv_heads: int, head_dim: int,
+                                  dtype: int) -> int:
+    return int(load_library().spicy_coarsen_workspace_bytes(B, n_seg, total_tokens, num_kv_heads, head_dim,
+                                                            dtype))
 
 
 def spicy_decode_num_splits(B: int, num_kv_heads: int, max_pages_per_seq: int, num_splits: int = 0) -> int:

@@ -100,14 +100,19 @@ const char* spicy_status_string(spicy_status s) {
     return "unknown spicy_status";
 }
 
-size_t spicy_coarsen_workspace_bytes(int32_t B, int32_t n_seg, int32_t total_tokens, int32_t num_kv_heads) {
-    if (B < 0 || n_seg < 0 || total_tokens < 0 || num_kv_heads < 1) return 0;
+size_t spicy_coarsen_workspace_bytes(int32_t B, int32_t n_seg, int32_t total_tokens, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t dtype) {
+    if (B < 0 || n_seg < 0 || total_tokens < 0 || num_kv_heads < 1 || head_dim < 1) return 0;
+    if (dtype != SPICY_F32 && dtype != SPICY_BF16) return 0;
+    const size_t elem = dtype == SPICY_BF16 ? 2 : 4;
     const size_t ns = static_cast<size_t>(n_seg);
     const size_t nh = ns * static_cast<size_t>(num_kv_heads);
     const size_t items = static_cast<size_t>(total_tokens) * static_cast<size_t>(num_kv_heads);
     const size_t nb = static_cast<size_t>(B);
+    const size_t d = static_cast<size_t>(head_dim);
     return SPICY_WORKSPACE_HEADER + align_up(16 * ns) + align_up(8 * nh) + align_up(8 * items) + align_up(4 * nb) +
-           align_up(4 * nb * static_cast<size_t>(num_kv_heads));
+           align_up(4 * nb * static_cast<size_t>(num_kv_heads)) + 2 * align_up(nh * d * elem) +
+           align_up(nh * 2 * elem) + align_up(16 * nh);
 }
 
 spicy_status spicy_coarsen(const spicy_cache* cache, const void* k_pre, const void* v,
@@ -128,7 +133,8 @@ spicy_status spicy_coarsen(const spicy_cache* cache, const void* k_pre, const vo
     if (max_pages_per_seq < 1) return SPICY_ERR_ARG;
     if (cache->num_pages < 1) return SPICY_ERR_RANGE;
     if (max_pages_per_seq > kMaxPagesPerSeq) return SPICY_ERR_UNSUPPORTED;
-    if (workspace_bytes < spicy_coarsen_workspace_bytes(B, n_seg, total_tokens, cache->num_kv_heads))
+    if (workspace_bytes < spicy_coarsen_workspace_bytes(B, n_seg, total_tokens, cache->num_kv_heads,
+                                                        cache->head_dim, cache->dtype))
         return SPICY_ERR_CAPACITY;
 
     spicy::CoarsenArgs a{};
@@ -155,6 +161,16 @@ spicy_status spicy_coarsen(const spicy_cache* cache, const void* k_pre, const vo
     a.cp_count = reinterpret_cast<int32_t*>(ws + off);
     off += align_up(4 * static_cast<size_t>(B));
     a.null_from = reinterpret_cast<int32_t*>(ws + off);
+    off += align_up(4 * static_cast<size_t>(B) * static_cast<size_t>(cache->num_kv_heads));
+    const size_t nh = ns * static_cast<size_t>(cache->num_kv_heads);
+    const size_t elem = cache->dtype == SPICY_BF16 ? 2 : 4;
+    a.stage_k = ws + off;
+    off += align_up(nh * static_cast<size_t>(cache->head_dim) * elem);
+    a.stage_v = ws + off;
+    off += align_up(nh * static_cast<size_t>(cache->head_dim) * elem);
+    a.stage_ab = ws + off;
+    off += align_up(nh * 2 * elem);
+    a.stage_meta = reinterpret_cast<int4*>(ws + off);
     a.total_tokens = total_tokens;
     a.n_seg = n_seg;
     a.B = B;

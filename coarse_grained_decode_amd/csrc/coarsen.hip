@@ -389,7 +389,7 @@ __device__ __forceinline__ void plan_sequence(const CoarsenArgs& a, int32_t (*s_
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(kPlanThreads) void coarsen_plan_kernel(CoarsenArgs a) {
+__device__ __forceinline__ void plan_role(const CoarsenArgs& a) {
     __shared__ int32_t s_wave[kMaxH + 1][kPlanWaves];
     __shared__ int32_t s_ok;
     // mask rows read as H / 4 dwords when H is a multiple of 4, else as bytes
@@ -460,39 +460,31 @@ struct Lanes {
     }
 };
 
-// Write entry e of sequence b for this lane's head: key row slice (already
-// rotated), value column slice (rounded from vals, or copied bit for bit from
-// vraw), and, from the head's first lane, alpha/beta and the metadata.
-template <typename T, int D, typename VSrc>
-__device__ __forceinline__ void store_entry(const CoarsenArgs& a, const Lanes<T, D>& L, int b, int64_t e,
-                                            const double (&y)[8], const VSrc& vsrc, double alpha,
-                                            double beta, int32_t kind, int32_t mass, int64_t ps) {
-    const int32_t Pg = entry_page(a, b, e);
-    if (Pg < 0) return;
-    const int slot = static_cast<int>(e % kPage);
-    const int64_t ph = static_cast<int64_t>(Pg) * a.cache.H + L.h;
-    Pack8<T>::store(static_cast<T*>(a.cache.k) + ph * kPage * D + slot_elem(slot, L.d0), y);
-    Store8<T>::store(static_cast<T*>(a.cache.v) + ph * kPage * D + slot_elem(slot, L.d0), vsrc);
-    if (L.j == 0) {
-        T* abc = static_cast<T*>(a.cache.ab);
-        abc[(ph * kPage + slot) * 2 + 0] = Elem<T>::from_f64(alpha);
-        abc[(ph * kPage + slot) * 2 + 1] = Elem<T>::from_f64(beta);
-        if (a.cache.meta) static_cast<Meta*>(a.cache.meta)[ph * kPage + slot] = Meta{kind, mass, ps};
+// Sequence that owns segment s: the last b with seq_seg_ptr[b] <= s, found
+// with one ballot per 64 entries of seq_seg_ptr; -1 if none (or s lies past
+// every sequence).
+__device__ __forceinline__ int32_t find_sequence(const CoarsenArgs& a, int32_t s) {
+    const int lane = threadIdx.x % kWave;
+    int32_t cnt = 0;
+    for (int32_t base = 0; base <= a.B; base += kWave) {
+        const int32_t i = base + lane;
+        const bool le = i <= a.B && a.seq_seg_ptr[min(i, a.B)] <= s;
+        cnt += __popcll(__ballot(le));
     }
+    return cnt - 1 < a.B ? cnt - 1 : -1;
 }
 
-// coarsen_main: stream one segment's tokens and write its macro-node.
+// Streaming role: one segment's F-tokens summed in double precision, then the
+// macro-node (mean key rotated to the mean position, mean value, alpha,
+// beta) written to the staging area at (segment, head).  Needs nothing from
+// the plan role, which runs at the same time.
 template <typename T, int D>
-__device__ __forceinline__ void coarsen_segment(const CoarsenArgs& a, const Lanes<T, D>& L, int32_t s) {
+__device__ __forceinline__ void stream_segment(const CoarsenArgs& a, const Lanes<T, D>& L, int32_t s) {
     const int H = a.cache.H;
-    const int4 desc = a.seg_desc[s];
-    const int2 head = a.seg_head[static_cast<int64_t>(s) * H + L.hh];
-    // the descriptor is the same for the whole wave: keep it in scalar registers
-    const int32_t b = __builtin_amdgcn_readfirstlane(desc.x);
-    const int32_t sa = __builtin_amdgcn_readfirstlane(desc.y);
-    const int32_t sz = __builtin_amdgcn_readfirstlane(desc.z);
-    const int64_t pos_off = __builtin_amdgcn_readfirstlane(desc.w);
-    if (b < 0 || b >= a.B || !(0 <= sa && sa < sz && sz <= a.total_tokens)) return;
+    // the segment bounds are the same for the whole wave: keep them in scalar registers
+    const int32_t sa = __builtin_amdgcn_readfirstlane(a.seg_offsets[s]);
+    const int32_t sz = __builtin_amdgcn_readfirstlane(a.seg_offsets[s + 1]);
+    if (!(0 <= sa && sa < sz && sz <= a.total_tokens)) return;     // reported by the plan role
     const T* kin = static_cast<const T*>(a.k_pre);
     const T* vin = static_cast<const T*>(a.v);
 
@@ -500,12 +492,13 @@ __device__ __forceinline__ void coarsen_segment(const CoarsenArgs& a, const Lane
     // is in flight while block A is accumulated and vice versa.  Rows are read
     // through buffer resources spanning the segment (rebased every kWindow
     // tokens): the per-token offset is a scalar, and reads past the segment's
-    // end return zeros, which add nothing to the sums.
+    // end return zeros, which add nothing to the sums.  Positions are summed
+    // relative to the segment's first token.
     double sk[8], sq[8], sv[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) sk[r] = sq[r] = sv[r] = 0.0;
     int32_t m = 0;
-    int64_t psum = 0;
+    int64_t prel = 0;
     struct Block {
         Row8<T> k[kRing], v[kRing];
         uint8_t mk[kRing];
@@ -544,7 +537,7 @@ __device__ __forceinline__ void coarsen_segment(const CoarsenArgs& a, const Lane
                     sv[r] = fma(X.v[u].f64(r), w, sv[r]);
                 }
                 m += take ? 1 : 0;
-                psum += take ? static_cast<int64_t>(w0) + u0 + u + pos_off : 0;
+                prel += take ? static_cast<int64_t>(w0 - sa) + u0 + u : 0;
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
@@ -565,37 +558,60 @@ __device__ __forceinline__ void coarsen_segment(const CoarsenArgs& a, const Lane
     }
 
     // the macro-node (all lanes take part in the shuffles)
+    const int32_t b = find_sequence(a, s);
+    if (b < 0) return;
+    const int64_t pos_off = static_cast<int64_t>(a.pos_base ? a.pos_base[b] : 0) - a.seq_offsets[b];
+    const int64_t psum = prel + static_cast<int64_t>(m) * (sa + pos_off);
     const double md = m > 0 ? static_cast<double>(m) : 1.0;
     double part = 0.0;
 #pragma unroll
     for (int r = 0; r < 8; ++r) part += sq[r] - sk[r] * sk[r] / md;
 #pragma unroll
     for (int o = 1; o < Lanes<T, D>::LPH; o <<= 1) part += __shfl_xor(part, o);
-    const bool mine = L.active && head.y && m > 0;
+    const bool mine = L.active && m > 0;
     if (!__any(mine)) return;
     double y[8];
     L.rope([&](int r) { return sk[r] / md; }, static_cast<double>(psum) / md, y);
     if (!mine) return;
     const double sigma2 = (part > 0.0 ? part : 0.0) / (md * D);
-    store_entry(a, L, b, head.x, y, [&](int r) { return Elem<T>::from_f64(sv[r] / md); }, log(md),
-                sigma2 / (2.0 * D), 2, m, psum);
+    const int64_t idx = static_cast<int64_t>(s) * H + L.h;
+    Pack8<T>::store(static_cast<T*>(a.stage_k) + idx * D + L.d0, y);
+    Store8<T>::store(static_cast<T*>(a.stage_v) + idx * D + L.d0,
+                     [&](int r) { return Elem<T>::from_f64(sv[r] / md); });
+    if (L.j == 0) {
+        T* ab = static_cast<T*>(a.stage_ab);
+        ab[idx * 2 + 0] = Elem<T>::from_f64(log(md));
+        ab[idx * 2 + 1] = Elem<T>::from_f64(sigma2 / (2.0 * D));
+        a.stage_meta[idx] = make_int4(m, b, static_cast<int32_t>(psum & 0xFFFFFFFF), static_cast<int32_t>(psum >> 32));
+    }
 }
 
+// coarsen_main: workgroups x < B plan sequence x (with head group 0); the
+// others are persistent streaming workgroups: wave w takes segments w,
+// w + W, w + 2W, ...  The two roles share nothing, so they run side by side.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void coarsen_main_kernel(CoarsenArgs a) {
+__global__ __launch_bounds__(256, 2) void coarsen_main_kernel(CoarsenArgs a) {
+    if (static_cast<int>(blockIdx.x) < a.B) {
+        if (blockIdx.y == 0) plan_role<T, D>(a);
+        return;
+    }
     const int wave = threadIdx.x / kWave;
     const Lanes<T, D> L(a);
-    // persistent: wave w of the grid takes segments w, w + W, w + 2W, ...
-    const int32_t stride = gridDim.x * (blockDim.x / kWave);
-    for (int32_t s = blockIdx.x * (blockDim.x / kWave) + wave; s < a.n_seg; s += stride)
-        coarsen_segment<T, D>(a, L, s);
+    const int32_t nstream = gridDim.x - a.B;
+    const int32_t stride = nstream * (blockDim.x / kWave);
+    for (int32_t s = (blockIdx.x - a.B) * (blockDim.x / kWave) + wave; s < a.n_seg; s += stride)
+        stream_segment<T, D>(a, L, s);
 }
 
-// coarsen_cpoint: every C-point item {token, entry, head} that coarsen_plan
-// listed, stored exact (value bits copied, key rotated to the token's own
-// position, alpha = beta = 0).  Workgroups (x, b) share the items of
-// sequence b; each 16-lane group (8 at d = 64) takes every G-th item and
-// prefetches the next one's rows while it rotates and stores the current one.
+// coarsen_cpoint: places every entry of sequence b, spread over workgroups
+// (x, b) and their 16-lane groups (8 at d = 64), each group one entry at a
+// time:
+//   1. the staged macro-nodes, at the entry the plan gave their (segment,
+//      head);
+//   2. every C-point item {token, entry, head} the plan listed, stored exact
+//      (value bits copied, key rotated to the token's own position,
+//      alpha = beta = 0), prefetching the next item's rows;
+//   3. the null entries.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void coarsen_cpoint_kernel(CoarsenArgs a) {
     constexpr int LPH = D / 8;                // lanes per item
@@ -623,6 +639,50 @@ __global__ __launch_bounds__(256) void coarsen_cpoint_kernel(CoarsenArgs a) {
     const int2* items = a.cp_items + static_cast<int64_t>(t0) * H;
     const T* kin = static_cast<const T*>(a.k_pre);
     const T* vin = static_cast<const T*>(a.v);
+    const int32_t stride = gridDim.x * ngrp;
+
+    // 1. macro-nodes of the sequence's segments
+    {
+        const int32_t s0 = a.seq_seg_ptr[b], s1 = a.seq_seg_ptr[b + 1];
+        const int64_t units = (0 <= s0 && s0 <= s1 && s1 <= a.n_seg) ? static_cast<int64_t>(s1 - s0) * H : 0;
+        for (int64_t u = static_cast<int64_t>(blockIdx.x) * ngrp + grp; u < units; u += stride) {
+            const int32_t sg = s0 + static_cast<int32_t>(u / H);
+            const int h = static_cast<int>(u % H);
+            if (a.seg_desc[sg].x != b) continue;               // sequence failed its checks
+            const int64_t idx = static_cast<int64_t>(sg) * H + h;
+            const int2 hd = a.seg_head[idx];
+            if (!(hd.y & 1)) continue;                          // no F-token in this head
+            const int4 mt = a.stage_meta[idx];
+            if (mt.y != b || mt.x <= 0) {
+                raise_err(a.err, SPICY_DEVERR_SEGMENTS);
+                continue;
+            }
+            const int32_t Pg = entry_page(a, b, hd.x);
+            if (Pg < 0) continue;
+            const int slot = hd.x % kPage;
+            const int64_t ph = static_cast<int64_t>(Pg) * H + h;
+            Row8<T> kx, vx;
+            kx.load(static_cast<const T*>(a.stage_k) + idx * D + d0);
+            vx.load(static_cast<const T*>(a.stage_v) + idx * D + d0);
+            Store8<T>::store(static_cast<T*>(a.cache.k) + ph * kPage * D + slot_elem(slot, d0),
+                             [&](int r) { return kx.raw(r); });
+            Store8<T>::store(static_cast<T*>(a.cache.v) + ph * kPage * D + slot_elem(slot, d0),
+                             [&](int r) { return vx.raw(r); });
+            if (j == 0) {
+                const T* sab = static_cast<const T*>(a.stage_ab);
+                T* abc = static_cast<T*>(a.cache.ab);
+                abc[(ph * kPage + slot) * 2 + 0] = sab[idx * 2 + 0];
+                abc[(ph * kPage + slot) * 2 + 1] = sab[idx * 2 + 1];
+                if (a.cache.meta) {
+                    const int64_t ps = static_cast<int64_t>(static_cast<uint32_t>(mt.z)) |
+                                       (static_cast<int64_t>(mt.w) << 32);
+                    static_cast<Meta*>(a.cache.meta)[ph * kPage + slot] = Meta{2, mt.x, ps};
+                }
+            }
+        }
+    }
+
+    // 2. C-point items
 
     // item i -> its rows; indexes are checked so a bad list never reads out of bounds
     auto fetch = [&](int32_t i, int2& it, Row8<T>& kx, Row8<T>& vx) {
@@ -633,7 +693,6 @@ __global__ __launch_bounds__(256) void coarsen_cpoint_kernel(CoarsenArgs a) {
         kx.load(kin + base);
         vx.load(vin + base);
     };
-    const int32_t stride = gridDim.x * ngrp;
     int32_t i = blockIdx.x * ngrp + grp;
     if (i < n) {
         int2 it0;
@@ -694,7 +753,7 @@ __global__ __launch_bounds__(256) void coarsen_cpoint_kernel(CoarsenArgs a) {
         }
     }
 
-    // null entries: each head from its own end up to the end of the
+    // 3. null entries: each head from its own end up to the end of the
     // sequence's last page (k = v = 0, alpha = -inf, beta = 0)
     const int64_t len = a.lengths_out[b];
     const int64_t padded = (len + kPage - 1) / kPage * kPage;
@@ -737,23 +796,16 @@ __global__ __launch_bounds__(256) void coarsen_cpoint_kernel(CoarsenArgs a) {
 template <typename T, int D>
 static spicy_status launch_coarsen_t(const CoarsenArgs& a, hipStream_t stream) {
     constexpr int HW = kWave / (D / 8);
-    hipLaunchKernelGGL((coarsen_plan_kernel<T, D>), dim3(a.B), dim3(kPlanThreads), 0, stream, a);
+    // plan workgroups (one per sequence) + persistent streaming workgroups
+    const int wpb = 4;
+    const int nstream = max(1, min((a.n_seg + wpb - 1) / wpb, kResidentBlocks));
+    dim3 grid(a.B + nstream, (a.cache.H + HW - 1) / HW);
+    hipLaunchKernelGGL((coarsen_main_kernel<T, D>), grid, dim3(wpb * kWave), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return SPICY_ERR_HIP;
-    if (a.n_seg > 0) {
-        // persistent grids: at most kResidentBlocks workgroups per head group
-        const int wpb = 4;
-        const int nblk = min((a.n_seg + wpb - 1) / wpb, kResidentBlocks);
-        dim3 grid(nblk, (a.cache.H + HW - 1) / HW);
-        hipLaunchKernelGGL((coarsen_main_kernel<T, D>), grid, dim3(wpb * kWave), 0, stream, a);
-        if (hipGetLastError() != hipSuccess) return SPICY_ERR_HIP;
-    }
-    {
-        // C-point items and null entries: about kResidentBlocks workgroups
-        // shared by the sequences
-        const int cx = max(1, min(kCpointBlocksPerSeq, kResidentBlocks / max(a.B, 1)));
-        hipLaunchKernelGGL((coarsen_cpoint_kernel<T, D>), dim3(cx, a.B), dim3(256), 0, stream, a);
-        if (hipGetLastError() != hipSuccess) return SPICY_ERR_HIP;
-    }
+    // entries: about kResidentBlocks workgroups shared by the sequences
+    const int cx = max(1, min(kCpointBlocksPerSeq, kResidentBlocks / max(a.B, 1)));
+    hipLaunchKernelGGL((coarsen_cpoint_kernel<T, D>), dim3(cx, a.B), dim3(256), 0, stream, a);
+    if (hipGetLastError() != hipSuccess) return SPICY_ERR_HIP;
     return SPICY_OK;
 }
 

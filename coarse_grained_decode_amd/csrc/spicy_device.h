@@ -151,6 +151,10 @@ struct CoarsenArgs {
                            //   {token, entry << 4 | head}
     int32_t* cp_count;     // [B]
     int32_t* null_from;    // [B][H]      first null-padding entry of each head (INT32_MAX: none)
+    void* stage_k;         // [n_seg][H][d]  macro-node keys (rotated, rounded), as streamed
+    void* stage_v;         // [n_seg][H][d]  macro-node values
+    void* stage_ab;        // [n_seg][H][2]  alpha, beta
+    int4* stage_meta;      // [n_seg][H]     {mass, sequence, pos_sum lo, pos_sum hi}
     int32_t total_tokens;
     int32_t n_seg;
     int32_t B;

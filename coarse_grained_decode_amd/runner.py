@@ -51,7 +51,8 @@ class DeviceCall:
             mask=_tensor(call.mask, None, device), page_table=_tensor(call.page_table, None, device),
             entry_start=_tensor(call.entry_start, None, device),
             lengths=torch.zeros(call.B, dtype=torch.int32, device=device),
-            ws=workspace(spicy_coarsen_workspace_bytes(call.B, call.n_seg, call.total_tokens, call.H_kv), device),
+            ws=workspace(spicy_coarsen_workspace_bytes(call.B, call.n_seg, call.total_tokens, call.H_kv, call.d,
+                                                       1 if call.dtype == "bf16" else 0), device),
         )
 
     def run(self, cache: PagedCache, stream=None) -> None:

@@ -102,10 +102,14 @@ typedef struct {
 } spicy_cache;
 
 /* Workspace bytes spicy_coarsen needs for `n_seg` segments and
- * `total_tokens` tokens over `B` sequences and `num_kv_heads` heads (header,
- * per segment and per (segment, head) plan, a list of C-point items of up
- * to total_tokens x num_kv_heads entries, per (sequence, head) counts). */
-size_t spicy_coarsen_workspace_bytes(int32_t B, int32_t n_seg, int32_t total_tokens, int32_t num_kv_heads);
+ * `total_tokens` tokens over `B` sequences, `num_kv_heads` heads of
+ * `head_dim` dims in cache dtype `dtype` (header, per segment and per
+ * (segment, head) plan, a list of C-point items of up to
+ * total_tokens x num_kv_heads entries, per (sequence, head) counts, and one
+ * macro-node per (segment, head) staged before it is placed).  0 for
+ * invalid sizes. */
+size_t spicy_coarsen_workspace_bytes(int32_t B, int32_t n_seg, int32_t total_tokens, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t dtype);
 
 /* spicy_coarsen — build compressed entries for B sequences.
  *
@@ -139,7 +143,7 @@ size_t spicy_coarsen_workspace_bytes(int32_t B, int32_t n_seg, int32_t total_tok
  *   entry count.  RoPE uses the half-split pairing (i, i+d/2) with
  *   theta_i = rope_base^(-2i/d); rope_base <= 0 means no rotation.  Values are
  *   accumulated in double precision and rounded once, to nearest-even, on store.
- * Workspace: device, >= spicy_coarsen_workspace_bytes(B, n_seg, total_tokens, H_kv) bytes,
+ * Workspace: device, >= spicy_coarsen_workspace_bytes(B, n_seg, total_tokens, H_kv, d, dtype) bytes,
  *   first int32 = sticky device error word (not cleared by the library).
  * Errors: SPICY_ERR_ARG (null required pointer, B < 0, n_seg < 0, bad dtype),
  *   SPICY_ERR_UNSUPPORTED (head_dim not 64/128, H_kv > 16, max_pages_per_seq > 2^23),

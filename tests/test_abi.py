@@ -72,10 +72,13 @@ def test_workspace_and_split_plan(lib):
         cgd.spicy_decode_workspace_bytes(2, 4, 2, 64, 40, 0)
     assert cgd.spicy_decode_shared_workspace_bytes(2, 4, 2, 64, 40, -1, 0) == 0
     # header, 16 B per segment, 8 B per (segment, head), 8 B per C-point
-    # item (at most tokens x heads), 4 B per sequence and per (sequence, head)
-    assert cgd.spicy_coarsen_workspace_bytes(2, 10, 100, 4) == 256 + 256 + 512 + 3328 + 256 + 256
-    assert cgd.spicy_coarsen_workspace_bytes(-1, 10, 100, 4) == 0
-    assert cgd.spicy_coarsen_workspace_bytes(2, 10, -1, 4) == 0
+    # item (at most tokens x heads), 4 B per sequence and per (sequence,
+    # head), then staged macro-nodes: key and value rows, alpha/beta, 16 B
+    stage = 2 * up(40 * 128 * 2) + up(40 * 2 * 2) + up(40 * 16)
+    assert cgd.spicy_coarsen_workspace_bytes(2, 10, 100, 4, 128, 1) == 256 + 256 + 512 + 3328 + 256 + 256 + stage
+    assert cgd.spicy_coarsen_workspace_bytes(-1, 10, 100, 4, 128, 1) == 0
+    assert cgd.spicy_coarsen_workspace_bytes(2, 10, -1, 4, 128, 1) == 0
+    assert cgd.spicy_coarsen_workspace_bytes(2, 10, 100, 4, 128, 7) == 0
 
 
 def _cache(dtype=1, H=4, d=128, pages=8, k=1, v=1, ab=1):
