@@ -648,11 +648,16 @@ __global__ __launch_bounds__(256) void coarsen_cpoint_kernel(CoarsenArgs a) {
         for (int64_t u = static_cast<int64_t>(blockIdx.x) * ngrp + grp; u < units; u += stride) {
             const int32_t sg = s0 + static_cast<int32_t>(u / H);
             const int h = static_cast<int>(u % H);
-            if (a.seg_desc[sg].x != b) continue;               // sequence failed its checks
             const int64_t idx = static_cast<int64_t>(sg) * H + h;
+            // every read of the unit is independent: issue them together
+            const int32_t owner = a.seg_desc[sg].x;
             const int2 hd = a.seg_head[idx];
-            if (!(hd.y & 1)) continue;                          // no F-token in this head
             const int4 mt = a.stage_meta[idx];
+            Row8<T> kx, vx;
+            kx.load(static_cast<const T*>(a.stage_k) + idx * D + d0);
+            vx.load(static_cast<const T*>(a.stage_v) + idx * D + d0);
+            if (owner != b) continue;                           // sequence failed its checks
+            if (!(hd.y & 1)) continue;                          // no F-token in this head
             if (mt.y != b || mt.x <= 0) {
                 raise_err(a.err, SPICY_DEVERR_SEGMENTS);
                 continue;
@@ -661,9 +666,6 @@ __global__ __launch_bounds__(256) void coarsen_cpoint_kernel(CoarsenArgs a) {
             if (Pg < 0) continue;
             const int slot = hd.x % kPage;
             const int64_t ph = static_cast<int64_t>(Pg) * H + h;
-            Row8<T> kx, vx;
-            kx.load(static_cast<const T*>(a.stage_k) + idx * D + d0);
-            vx.load(static_cast<const T*>(a.stage_v) + idx * D + d0);
             Store8<T>::store(static_cast<T*>(a.cache.k) + ph * kPage * D + slot_elem(slot, d0),
                              [&](int r) { return kx.raw(r); });
             Store8<T>::store(static_cast<T*>(a.cache.v) + ph * kPage * D + slot_elem(slot, d0),
