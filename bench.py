@@ -283,9 +283,9 @@ def main():
                 "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": t,
                 "alg_bytes_per_call": int(nbytes), "mean_call_us": round(ms * 1e3, 2)}
 
-    r_coarsen = roof(cb, coarsen_ms, ["coarsen_plan_kernel", "coarsen_main_kernel", "coarsen_cpoint_kernel"])
+    r_coarsen = roof(cb, coarsen_ms, ["coarsen_main_kernel", "coarsen_cpoint_kernel"])
     r_decode = roof(db, decode_ms, ["decode_mfma_kernel", "combine_kernel"])
-    r_coarsen["kernel"] = "spicy_coarsen (coarsen_plan + coarsen_main + coarsen_cpoint)"
+    r_coarsen["kernel"] = "spicy_coarsen (coarsen_main: plan + streaming, then coarsen_cpoint: entries)"
     r_decode["kernel"] = ("spicy_decode_attn_shared" if dw.shared_prefix_pages else "spicy_decode_attn") + \
         " (decode_mfma + combine)"
     dominant, other = (r_coarsen, r_decode) if coarsen_ms >= decode_ms else (r_decode, r_coarsen)
