@@ -44,7 +44,7 @@ constexpr int kPlanThreads = 256;
 constexpr int kPlanWaves = kPlanThreads / kWave;
 constexpr int kCpointBlocksPerSeq = 64;
 constexpr int kMaxH = 16;
-constexpr int kRing = 4;
+constexpr int kRing = 3;
 constexpr int kResidentBlocks = 1024;   // 4 workgroups of 4 waves per CU
 constexpr int32_t kWindow = 65536;      // tokens per buffer resource (< 4 GiB)
 
@@ -547,7 +547,10 @@ __device__ __forceinline__ void stream_segment(const CoarsenArgs& a, const Lanes
         __builtin_amdgcn_sched_barrier(0);
         fetch(Bk, kRing);
         __builtin_amdgcn_sched_barrier(0);
-        for (int32_t u0 = 0; u0 < wn; u0 += 2 * kRing) {
+        // steady state refills a block only while it starts inside the
+        // window; the last two blocks are drained without refills
+        int32_t u0 = 0;
+        for (; u0 + 2 * kRing < wn; u0 += 2 * kRing) {
             accumulate(A, u0);
             fetch(A, u0 + 2 * kRing);
             __builtin_amdgcn_sched_barrier(0);
@@ -555,6 +558,8 @@ __device__ __forceinline__ void stream_segment(const CoarsenArgs& a, const Lanes
             fetch(Bk, u0 + 3 * kRing);
             __builtin_amdgcn_sched_barrier(0);
         }
+        accumulate(A, u0);
+        if (u0 + kRing < wn) accumulate(Bk, u0 + kRing);
     }
 
     // the macro-node (all lanes take part in the shuffles)
