@@ -16,10 +16,11 @@ namespace {
 constexpr size_t kAlign = 256;
 constexpr int32_t kMaxKvHeads = 16;
 constexpr int32_t kMaxGroup = 16;       // query heads per KV head (MFMA columns)
-constexpr int32_t kTargetWaves = 2048;  // split-K aims for ~2 waves per SIMD
-constexpr int32_t kMinPagesPerSplit = 4;
-constexpr int32_t kPagesInFlight = 4;     // decode pipeline depth (pages per wavefront)
-constexpr int32_t kMaxResidentWaves = 4096;
+// The decode wavefronts all fit the chip at once: 256 CUs x 4 SIMDs x 2
+// wavefronts (its register use allows two per SIMD).  Spreading the pages
+// evenly over that many wavefronts, in one round, is what bounds its time.
+constexpr int32_t kResidentWaves = 2048;
+constexpr int32_t kPagesInFlight = 4;     // decode pipeline depth: fewer pages per wave gain nothing
 constexpr int32_t kMaxSplits = 256;
 constexpr int32_t kMaxGridY = 65535;      // grid y/z extent limit (sequences, heads)
 constexpr int32_t kMaxPagesPerSeq = 1 << 23;  // entry ids fit the 27 bits a C-point item keeps
@@ -53,27 +54,33 @@ struct DecodePlan {
     int32_t slots() const { return prefix_splits + priv_splits; }
 };
 
-constexpr int32_t kPrefixWaveTarget = 256;  // shared-prefix wavefronts per call
-constexpr int32_t kMinPrefixChunk = 8;
 constexpr int32_t kMaxPrefixChunk = 64;     // one page id per lane
+
+// Pages per wavefront that spread `visits` page visits (one wavefront visit
+// = one page of one KV head for one tile of query rows) over the resident
+// wavefronts, at least the pipeline depth.
+int32_t pages_per_wave(int64_t visits) {
+    return std::max<int32_t>(kPagesInFlight, ceil_div(visits, kResidentWaves));
+}
 
 DecodePlan plan_decode(int32_t B, int32_t H_q, int32_t H_kv, int32_t max_pages, int32_t P, int32_t num_splits) {
     DecodePlan p;
+    const int64_t units = static_cast<int64_t>(B) * std::max(1, H_kv);
+    const int32_t priv = max_pages - P;
+    const int64_t rows = static_cast<int64_t>(B) * (H_q / std::max(1, H_kv));
+    const int64_t tiles = (rows + 15) / 16;
+    // the work of the whole call: private pages per (sequence, KV head) and
+    // shared pages per (KV head, query tile)
+    const int64_t visits = units * std::max(priv, 0) + static_cast<int64_t>(P) * std::max(1, H_kv) * tiles;
+    const int32_t ppw = pages_per_wave(visits);
     if (P > 0) {
-        // chunks long enough that the partials they write (one per query row
-        // and chunk) stay small next to the pages, yet enough wavefronts
-        const int64_t rows = static_cast<int64_t>(B) * (H_q / std::max(1, H_kv));
-        const int64_t tiles = (rows + 15) / 16;
-        const int64_t work = static_cast<int64_t>(P) * std::max(1, H_kv) * tiles;
-        int32_t c = ceil_div(work, kPrefixWaveTarget);
-        c = std::min(std::max(c, kMinPrefixChunk), kMaxPrefixChunk);
-        c = std::min(c, P);
+        const int32_t c = std::min(std::min(ppw, kMaxPrefixChunk), P);
         p.prefix_splits = ceil_div(P, c);
         p.prefix_chunk = ceil_div(P, p.prefix_splits);
     }
-    const int32_t priv = max_pages - P;
     if (priv > 0) {
-        p.priv_splits = spicy_decode_num_splits(B, H_kv, priv, num_splits);
+        p.priv_splits = num_splits > 0 ? spicy_decode_num_splits(B, H_kv, priv, num_splits)
+                                       : ceil_div(priv, pages_per_split(priv, ceil_div(priv, ppw)));
         p.pages_per_split = pages_per_split(priv, p.priv_splits);
     }
     return p;
@@ -188,16 +195,10 @@ int32_t spicy_decode_num_splits(int32_t B, int32_t num_kv_heads, int32_t max_pag
     if (num_splits > 0) {
         s = std::min(num_splits, max_pages_per_seq);
     } else {
-        // Prefer splits short enough that a wavefront issues all its pages'
-        // loads at once (kPagesInFlight); otherwise aim for ~2 waves per SIMD.
+        // the pages of every (sequence, KV head) spread evenly over the
+        // resident wavefronts, at least kPagesInFlight pages each
         const int64_t units = std::max<int64_t>(1, static_cast<int64_t>(B) * std::max(1, num_kv_heads));
-        const int32_t full = ceil_div(max_pages_per_seq, kPagesInFlight);
-        if (units * full <= kMaxResidentWaves) {
-            s = full;
-        } else {
-            s = ceil_div(kTargetWaves, units);
-            s = std::min(s, ceil_div(max_pages_per_seq, kMinPagesPerSplit));
-        }
+        s = ceil_div(max_pages_per_seq, pages_per_wave(units * max_pages_per_seq));
     }
     s = std::max(1, std::min(s, kMaxSplits));
     return ceil_div(max_pages_per_seq, pages_per_split(max_pages_per_seq, s));
