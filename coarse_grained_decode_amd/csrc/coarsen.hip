@@ -609,14 +609,132 @@ __global__ __launch_bounds__(256, 2) void coarsen_main_kernel(CoarsenArgs a) {
 }
 
 // coarsen_cpoint: places every entry of sequence b, spread over workgroups
-// (x, b) and their 16-lane groups (8 at d = 64), each group one entry at a
-// time:
-//   1. the staged macro-nodes, at the entry the plan gave their (segment,
-//      head);
-//   2. every C-point item {token, entry, head} the plan listed, stored exact
-//      (value bits copied, key rotated to the token's own position,
-//      alpha = beta = 0), prefetching the next item's rows;
-//   3. the null entries.
+// (x, b) and their 16-lane groups (8 at d = 64).  The sequence's entries form
+// one index space walked with a grid stride, so each group pays one chain of
+// dependent reads per entry whatever its kind:
+//   [0, n_mac)              the staged macro-nodes, unit (segment, head), at
+//                           the entry the plan gave them;
+//   [n_mac, n_mac + n_cp)   the C-point items {token, entry, head} the plan
+//                           listed, stored exact (value bits copied, key
+//                           rotated to the token's own position,
+//                           alpha = beta = 0);
+//   [.., + n_null)          the null entries: each head from its own end up
+//                           to the end of the sequence's last page
+//                           (k = v = 0, alpha = -inf, beta = 0).
+template <typename T, int D>
+__device__ __forceinline__ void place_macro(const CoarsenArgs& a, int b, int32_t s0, int64_t u, int d0, int j) {
+    const int H = a.cache.H;
+    const int32_t sg = s0 + static_cast<int32_t>(u / H);
+    const int h = static_cast<int>(u % H);
+    const int64_t idx = static_cast<int64_t>(sg) * H + h;
+    // every read of the unit is independent: issue them together
+    const int32_t owner = a.seg_desc[sg].x;
+    const int2 hd = a.seg_head[idx];
+    const int4 mt = a.stage_meta[idx];
+    Row8<T> kx, vx;
+    kx.load(static_cast<const T*>(a.stage_k) + idx * D + d0);
+    vx.load(static_cast<const T*>(a.stage_v) + idx * D + d0);
+    if (owner != b) return;                             // sequence failed its checks
+    if (!(hd.y & 1)) return;                            // no F-token in this head
+    if (mt.y != b || mt.x <= 0) {
+        raise_err(a.err, SPICY_DEVERR_SEGMENTS);
+        return;
+    }
+    const int32_t Pg = entry_page(a, b, hd.x);
+    if (Pg < 0) return;
+    const int slot = hd.x % kPage;
+    const int64_t ph = static_cast<int64_t>(Pg) * H + h;
+    Store8<T>::store(static_cast<T*>(a.cache.k) + ph * kPage * D + slot_elem(slot, d0),
+                     [&](int r) { return kx.raw(r); });
+    Store8<T>::store(static_cast<T*>(a.cache.v) + ph * kPage * D + slot_elem(slot, d0),
+                     [&](int r) { return vx.raw(r); });
+    if (j == 0) {
+        const T* sab = static_cast<const T*>(a.stage_ab);
+        T* abc = static_cast<T*>(a.cache.ab);
+        abc[(ph * kPage + slot) * 2 + 0] = sab[idx * 2 + 0];
+        abc[(ph * kPage + slot) * 2 + 1] = sab[idx * 2 + 1];
+        if (a.cache.meta) {
+            const int64_t ps = static_cast<int64_t>(static_cast<uint32_t>(mt.z)) |
+                               (static_cast<int64_t>(mt.w) << 32);
+            static_cast<Meta*>(a.cache.meta)[ph * kPage + slot] = Meta{2, mt.x, ps};
+        }
+    }
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void place_cpoint(const CoarsenArgs& a, int b, int2 it, int32_t t0, int32_t t1,
+                                             int64_t pos_off, const double (&theta)[4], int d0, int j) {
+    constexpr int PARTNER = D / 16;
+    const int H = a.cache.H;
+    const bool hi_half = j >= PARTNER;
+    // indexes are clamped so a bad list never reads out of bounds
+    const int32_t t = it.x;
+    const int h = it.y & 15;
+    const int64_t e = static_cast<uint32_t>(it.y) >> 4;
+    const bool sane = t >= t0 && t < t1 && h < H;
+    const int64_t base = (static_cast<int64_t>(min(max(t, t0), t1 - 1)) * H + min(h, H - 1)) * D + d0;
+    Row8<T> kx, vx;
+    kx.load(static_cast<const T*>(a.k_pre) + base);
+    vx.load(static_cast<const T*>(a.v) + base);
+    if (!sane) raise_err(a.err, SPICY_DEVERR_SEGMENTS);
+    const int32_t Pg = sane ? entry_page(a, b, e) : -1;
+    double y[8];
+    if (a.rope_base > 0.0) {
+        const double pos = static_cast<double>(t + pos_off);
+        double c4[4], s4[4], cs[8], sn[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sincos_f64(pos * theta[r], &s4[r], &c4[r]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const double oc = __shfl_xor(c4[r], PARTNER);
+            const double os = __shfl_xor(s4[r], PARTNER);
+            cs[r] = hi_half ? oc : c4[r];
+            sn[r] = hi_half ? os : s4[r];
+            cs[4 + r] = hi_half ? c4[r] : oc;
+            sn[4 + r] = hi_half ? s4[r] : os;
+        }
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const double x = kx.f64(r);
+            const double other = __shfl_xor(x, PARTNER);
+            y[r] = hi_half ? x * cs[r] + other * sn[r] : x * cs[r] - other * sn[r];
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) y[r] = kx.f64(r);
+    }
+    if (Pg < 0) return;
+    const int slot = static_cast<int>(e % kPage);
+    const int64_t ph = static_cast<int64_t>(Pg) * H + h;
+    Pack8<T>::store(static_cast<T*>(a.cache.k) + ph * kPage * D + slot_elem(slot, d0), y);
+    Store8<T>::store(static_cast<T*>(a.cache.v) + ph * kPage * D + slot_elem(slot, d0),
+                     [&](int r) { return vx.raw(r); });
+    if (j == 0) {
+        T* abc = static_cast<T*>(a.cache.ab);
+        abc[(ph * kPage + slot) * 2 + 0] = Elem<T>::from_f32(0.f);
+        abc[(ph * kPage + slot) * 2 + 1] = Elem<T>::from_f32(0.f);
+        if (a.cache.meta) static_cast<Meta*>(a.cache.meta)[ph * kPage + slot] = Meta{1, 1, t + pos_off};
+    }
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void place_null(const CoarsenArgs& a, int b, int h, int64_t e, int d0, int j) {
+    const int H = a.cache.H;
+    const int32_t Pg = entry_page(a, b, e);
+    if (Pg < 0) return;
+    const int slot = static_cast<int>(e % kPage);
+    const int64_t ph = static_cast<int64_t>(Pg) * H + h;
+    const double zero[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    Pack8<T>::store(static_cast<T*>(a.cache.k) + ph * kPage * D + slot_elem(slot, d0), zero);
+    Pack8<T>::store(static_cast<T*>(a.cache.v) + ph * kPage * D + slot_elem(slot, d0), zero);
+    if (j == 0) {
+        T* abc = static_cast<T*>(a.cache.ab);
+        abc[(ph * kPage + slot) * 2 + 0] = Elem<T>::from_f32(-__builtin_huge_valf());
+        abc[(ph * kPage + slot) * 2 + 1] = Elem<T>::from_f32(0.f);
+        if (a.cache.meta) static_cast<Meta*>(a.cache.meta)[ph * kPage + slot] = Meta{0, 0, 0};
+    }
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void coarsen_cpoint_kernel(CoarsenArgs a) {
     constexpr int LPH = D / 8;                // lanes per item
@@ -624,176 +742,55 @@ __global__ __launch_bounds__(256) void coarsen_cpoint_kernel(CoarsenArgs a) {
     constexpr int PARTNER = LPH / 2;
     const int b = blockIdx.y;
     const int H = a.cache.H;
+    // the sequence's bounds: independent reads, issued together
     const int32_t t0 = a.seq_offsets[b], t1 = a.seq_offsets[b + 1];
-    int32_t n = a.cp_count[b];
-    if (n < 0 || t0 < 0 || t0 > t1 || t1 > a.total_tokens || n > static_cast<int64_t>(t1 - t0) * H) n = 0;
+    const int32_t s0 = a.seq_seg_ptr[b], s1 = a.seq_seg_ptr[b + 1];
+    int32_t n_cp = a.cp_count[b];
+    const int64_t len = a.lengths_out[b];
+    const int64_t pos_off = static_cast<int64_t>(a.pos_base ? a.pos_base[b] : 0) - t0;
+    const int64_t padded = (len + kPage - 1) / kPage * kPage;
+    int64_t n_null = 0;
+    for (int h = 0; h < H; ++h) {
+        const int64_t c = padded - a.null_from[static_cast<int64_t>(b) * H + h];
+        n_null += c > 0 ? c : 0;
+    }
+    if (n_cp < 0 || t0 < 0 || t0 > t1 || t1 > a.total_tokens || n_cp > static_cast<int64_t>(t1 - t0) * H) n_cp = 0;
+    const int64_t n_mac = (0 <= s0 && s0 <= s1 && s1 <= a.n_seg) ? static_cast<int64_t>(s1 - s0) * H : 0;
+    const int64_t n_all = n_mac + n_cp + n_null;
+
     const int lane = threadIdx.x % kWave;
     const int grp = (threadIdx.x / kWave) * IPW + lane / LPH;
     const int ngrp = (blockDim.x / kWave) * IPW;
     const int j = lane % LPH;
-    const bool hi_half = j >= PARTNER;
     const int d0 = 8 * j;
-    const int64_t pos_off = static_cast<int64_t>(a.pos_base ? a.pos_base[b] : 0) - t0;
-    const bool rotate = a.rope_base > 0.0;
     double theta[4];
     {
+        const bool hi_half = j >= PARTNER;
         const int pair0 = 8 * (hi_half ? j - PARTNER : j) + (hi_half ? 4 : 0);
 #pragma unroll
         for (int r = 0; r < 4; ++r) theta[r] = a.theta[pair0 + r];
     }
     const int2* items = a.cp_items + static_cast<int64_t>(t0) * H;
-    const T* kin = static_cast<const T*>(a.k_pre);
-    const T* vin = static_cast<const T*>(a.v);
-    const int32_t stride = gridDim.x * ngrp;
-
-    // 1. macro-nodes of the sequence's segments
-    {
-        const int32_t s0 = a.seq_seg_ptr[b], s1 = a.seq_seg_ptr[b + 1];
-        const int64_t units = (0 <= s0 && s0 <= s1 && s1 <= a.n_seg) ? static_cast<int64_t>(s1 - s0) * H : 0;
-        for (int64_t u = static_cast<int64_t>(blockIdx.x) * ngrp + grp; u < units; u += stride) {
-            const int32_t sg = s0 + static_cast<int32_t>(u / H);
-            const int h = static_cast<int>(u % H);
-            const int64_t idx = static_cast<int64_t>(sg) * H + h;
-            // every read of the unit is independent: issue them together
-            const int32_t owner = a.seg_desc[sg].x;
-            const int2 hd = a.seg_head[idx];
-            const int4 mt = a.stage_meta[idx];
-            Row8<T> kx, vx;
-            kx.load(static_cast<const T*>(a.stage_k) + idx * D + d0);
-            vx.load(static_cast<const T*>(a.stage_v) + idx * D + d0);
-            if (owner != b) continue;                           // sequence failed its checks
-            if (!(hd.y & 1)) continue;                          // no F-token in this head
-            if (mt.y != b || mt.x <= 0) {
-                raise_err(a.err, SPICY_DEVERR_SEGMENTS);
-                continue;
-            }
-            const int32_t Pg = entry_page(a, b, hd.x);
-            if (Pg < 0) continue;
-            const int slot = hd.x % kPage;
-            const int64_t ph = static_cast<int64_t>(Pg) * H + h;
-            Store8<T>::store(static_cast<T*>(a.cache.k) + ph * kPage * D + slot_elem(slot, d0),
-                             [&](int r) { return kx.raw(r); });
-            Store8<T>::store(static_cast<T*>(a.cache.v) + ph * kPage * D + slot_elem(slot, d0),
-                             [&](int r) { return vx.raw(r); });
-            if (j == 0) {
-                const T* sab = static_cast<const T*>(a.stage_ab);
-                T* abc = static_cast<T*>(a.cache.ab);
-                abc[(ph * kPage + slot) * 2 + 0] = sab[idx * 2 + 0];
-                abc[(ph * kPage + slot) * 2 + 1] = sab[idx * 2 + 1];
-                if (a.cache.meta) {
-                    const int64_t ps = static_cast<int64_t>(static_cast<uint32_t>(mt.z)) |
-                                       (static_cast<int64_t>(mt.w) << 32);
-                    static_cast<Meta*>(a.cache.meta)[ph * kPage + slot] = Meta{2, mt.x, ps};
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * ngrp;
+    for (int64_t u = static_cast<int64_t>(blockIdx.x) * ngrp + grp; u < n_all; u += stride) {
+        if (u < n_mac) {
+            place_macro<T, D>(a, b, s0, u, d0, j);
+        } else if (u < n_mac + n_cp) {
+            place_cpoint<T, D>(a, b, items[u - n_mac], t0, t1, pos_off, theta, d0, j);
+        } else {
+            int64_t rem = u - n_mac - n_cp, e = 0;
+            int h = 0;
+            for (int q = 0; q < H; ++q) {
+                const int64_t nf = a.null_from[static_cast<int64_t>(b) * H + q];
+                const int64_t cnt = padded - nf > 0 ? padded - nf : 0;
+                if (rem < cnt) {
+                    h = q;
+                    e = nf + rem;
+                    break;
                 }
+                rem -= cnt;
             }
-        }
-    }
-
-    // 2. C-point items
-
-    // item i -> its rows; indexes are checked so a bad list never reads out of bounds
-    auto fetch = [&](int32_t i, int2& it, Row8<T>& kx, Row8<T>& vx) {
-        it = items[min(i, n - 1)];
-        const int32_t t = min(max(it.x, t0), t1 - 1);
-        const int h = min(it.y & 15, H - 1);
-        const int64_t base = (static_cast<int64_t>(t) * H + h) * D + d0;
-        kx.load(kin + base);
-        vx.load(vin + base);
-    };
-    int32_t i = blockIdx.x * ngrp + grp;
-    if (i < n) {
-        int2 it0;
-        Row8<T> k0, v0;
-        fetch(i, it0, k0, v0);
-        for (; i < n; i += stride) {
-            int2 it1;
-            Row8<T> k1, v1;
-            const bool more = i + stride < n;
-            fetch(more ? i + stride : i, it1, k1, v1);
-            const int32_t t = it0.x;
-            const int h = it0.y & 15;
-            const int64_t e = static_cast<uint32_t>(it0.y) >> 4;
-            const double pos = static_cast<double>(t + pos_off);
-            double y[8];
-            if (rotate) {
-                double c4[4], s4[4], cs[8], sn[8];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) sincos_f64(pos * theta[r], &s4[r], &c4[r]);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const double oc = __shfl_xor(c4[r], PARTNER);
-                    const double os = __shfl_xor(s4[r], PARTNER);
-                    cs[r] = hi_half ? oc : c4[r];
-                    sn[r] = hi_half ? os : s4[r];
-                    cs[4 + r] = hi_half ? c4[r] : oc;
-                    sn[4 + r] = hi_half ? s4[r] : os;
-                }
-#pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    const double x = k0.f64(r);
-                    const double other = __shfl_xor(x, PARTNER);
-                    y[r] = hi_half ? x * cs[r] + other * sn[r] : x * cs[r] - other * sn[r];
-                }
-            } else {
-#pragma unroll
-                for (int r = 0; r < 8; ++r) y[r] = k0.f64(r);
-            }
-            const bool sane = t >= t0 && t < t1 && h < H;
-            if (!sane) raise_err(a.err, SPICY_DEVERR_SEGMENTS);
-            const int32_t Pg = sane ? entry_page(a, b, e) : -1;
-            if (Pg >= 0) {
-                const int slot = static_cast<int>(e % kPage);
-                const int64_t ph = static_cast<int64_t>(Pg) * H + h;
-                Pack8<T>::store(static_cast<T*>(a.cache.k) + ph * kPage * D + slot_elem(slot, d0), y);
-                Store8<T>::store(static_cast<T*>(a.cache.v) + ph * kPage * D + slot_elem(slot, d0),
-                                 [&](int r) { return v0.raw(r); });
-                if (j == 0) {
-                    T* abc = static_cast<T*>(a.cache.ab);
-                    abc[(ph * kPage + slot) * 2 + 0] = Elem<T>::from_f32(0.f);
-                    abc[(ph * kPage + slot) * 2 + 1] = Elem<T>::from_f32(0.f);
-                    if (a.cache.meta) static_cast<Meta*>(a.cache.meta)[ph * kPage + slot] = Meta{1, 1, t + pos_off};
-                }
-            }
-            it0 = it1;
-            k0 = k1;
-            v0 = v1;
-        }
-    }
-
-    // 3. null entries: each head from its own end up to the end of the
-    // sequence's last page (k = v = 0, alpha = -inf, beta = 0)
-    const int64_t len = a.lengths_out[b];
-    const int64_t padded = (len + kPage - 1) / kPage * kPage;
-    int64_t units = 0;
-    for (int h = 0; h < H; ++h) {
-        const int64_t c = padded - a.null_from[static_cast<int64_t>(b) * H + h];
-        units += c > 0 ? c : 0;
-    }
-    for (int64_t u = static_cast<int64_t>(blockIdx.x) * ngrp + grp; u < units; u += stride) {
-        int64_t rem = u, e = 0;
-        int h = 0;
-        for (int q = 0; q < H; ++q) {
-            const int64_t nf = a.null_from[static_cast<int64_t>(b) * H + q];
-            const int64_t cnt = padded - nf > 0 ? padded - nf : 0;
-            if (rem < cnt) {
-                h = q;
-                e = nf + rem;
-                break;
-            }
-            rem -= cnt;
-        }
-        const int32_t Pg = entry_page(a, b, e);
-        if (Pg < 0) continue;
-        const int slot = static_cast<int>(e % kPage);
-        const int64_t ph = static_cast<int64_t>(Pg) * H + h;
-        const double zero[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        Pack8<T>::store(static_cast<T*>(a.cache.k) + ph * kPage * D + slot_elem(slot, d0), zero);
-        Pack8<T>::store(static_cast<T*>(a.cache.v) + ph * kPage * D + slot_elem(slot, d0), zero);
-        if (j == 0) {
-            T* abc = static_cast<T*>(a.cache.ab);
-            abc[(ph * kPage + slot) * 2 + 0] = Elem<T>::from_f32(-__builtin_huge_valf());
-            abc[(ph * kPage + slot) * 2 + 1] = Elem<T>::from_f32(0.f);
-            if (a.cache.meta) static_cast<Meta*>(a.cache.meta)[ph * kPage + slot] = Meta{0, 0, 0};
+            place_null<T, D>(a, b, h, e, d0, j);
         }
     }
 }
