@@ -58,9 +58,9 @@ constexpr int kXcds = 8;                  // MI355X: workgroups go round-robin o
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Clamp a sequence's length to what its page table row can address.
-__device__ __forceinline__ int32_t checked_length(const DecodeArgs& a, int b) {
-    int32_t len = a.lengths[b];
+// Clamp a sequence's length (as read from lengths[]) to what its page table
+// row can address.
+__device__ __forceinline__ int32_t check_length(const DecodeArgs& a, int32_t len) {
     if (len < 0) {
         raise_err(a.err, SPICY_DEVERR_LENGTH);
         len = 0;
@@ -72,6 +72,8 @@ __device__ __forceinline__ int32_t checked_length(const DecodeArgs& a, int b) {
     }
     return len;
 }
+
+__device__ __forceinline__ int32_t checked_length(const DecodeArgs& a, int b) { return check_length(a, a.lengths[b]); }
 
 template <int D>
 struct PageRegs {
@@ -114,17 +116,23 @@ struct Tile {
     float m_run, l_run;
     f32x4 acc[NT];
 
-    // rowq: this lane's query row, or nullptr for a padding row
-    __device__ __forceinline__ void init(const uint16_t* rowq, int32_t length) {
+    // rowq: this lane's query row (a padding row passes any valid row).  Only
+    // issues the loads, unconditionally, so that nothing waits on them here;
+    // init() uses them.
+    __device__ __forceinline__ void load_q(const uint16_t* rowq) {
+        const int grp = (threadIdx.x % kWave) / 16;
+#pragma unroll
+        for (int i = 0; i < KC; ++i) q[i] = *reinterpret_cast<const bf16x8*>(rowq + 32 * i + 8 * grp);
+    }
+
+    // valid: this lane's row is a real query row (else its query is zeroed);
+    // length: entries of that row's sequence, 0 for a padding row
+    __device__ __forceinline__ void init(bool valid, int32_t length) {
         const int grp = (threadIdx.x % kWave) / 16;
         float n2 = 0.f;
 #pragma unroll
         for (int i = 0; i < KC; ++i) {
-            if (rowq) {
-                q[i] = *reinterpret_cast<const bf16x8*>(rowq + 32 * i + 8 * grp);
-            } else {
-                q[i] = bf16x8{};
-            }
+            if (!valid) q[i] = bf16x8{};
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const float x = static_cast<float>(q[i][j]);
@@ -142,7 +150,7 @@ struct Tile {
             sel[0][j] = static_cast<__bf16>(8 * grp + j == c ? 1.f : 0.f);
             sel[1][j] = static_cast<__bf16>(8 * grp + j == 16 + c ? 1.f : 0.f);
         }
-        len = rowq ? length : 0;
+        len = length;
         int32_t mx = len;
 #pragma unroll
         for (int o = 1; o < 16; o <<= 1) mx = max(mx, __shfl_xor(mx, o));
@@ -264,17 +272,31 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
     const int G = a.H_q / H;
     int64_t blk = static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x;
 
-    int h, slot;
+    int h, slot, t = 0;
     int32_t p0, p1;
+    int32_t id_end;        // page-id entries this wavefront's table row holds
     const int32_t* table;
     int64_t prow;          // this lane's partial row (sequence * H_q + query head)
-    int32_t rlen;          // this lane's sequence length
+    int32_t raw_len;       // this lane's sequence length as read, checked below
     bool row_valid;
-    if (blk < a.prefix_blocks) {
+    const bool prefix_role = blk < a.prefix_blocks;
+    // The query rows and the first window of page ids do not depend on the
+    // length: each role issues their loads together with it, so the wavefront
+    // waits one memory round trip before its first pages are requested.
+    Tile<D> T;
+    int32_t ids;
+    int64_t prow0;         // a valid query row of the wavefront's KV head
+    auto issue_loads = [&]() {
+        T.load_q(static_cast<const uint16_t*>(a.q) + (row_valid ? prow : prow0) * D);
+        ids = (p0 + lane < min(p0 + kWave, id_end)) ? table[p0 + lane] : 0;
+        // keep the compiler from sinking those loads below the exit test
+        asm volatile("" ::: "memory");
+    };
+    if (prefix_role) {
         const int per_xcd = a.prefix_blocks / kXcds;      // prefix_blocks is a multiple of 8
         int w = static_cast<int>(blk % kXcds) * per_xcd + static_cast<int>(blk / kXcds);
         const int tgb = a.prefix_tile_blocks;
-        const int t = (w % tgb) * kWavesPerBlock + wave;
+        t = (w % tgb) * kWavesPerBlock + wave;
         w /= tgb;
         h = w % H;
         const int c = w / H;
@@ -283,27 +305,15 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
         slot = c;
         p0 = c * a.prefix_chunk;
         p1 = min(p0 + a.prefix_chunk, a.prefix_pages);
+        id_end = a.prefix_pages;
         table = a.page_table;
         const int r = t * 16 + row;
         row_valid = r < rows;
         const int bq = row_valid ? r / G : 0;
         prow = static_cast<int64_t>(bq) * a.H_q + static_cast<int64_t>(h) * G + (row_valid ? r % G : 0);
-        rlen = row_valid ? checked_length(a, bq) : 0;
-        // the KV head 0 wavefronts check that the sequences of their tile map
-        // the chunk's pages like sequence 0: independent loads, one flag
-        if (h == 0) {
-            const int b_first = (t * 16) / G;
-            const int b_last = min(rows - 1, t * 16 + 15) / G;
-            const int npg = p1 - p0;
-            const int n = (b_last - b_first + 1) * npg;
-            bool bad = false;
-            for (int i = lane; i < n; i += kWave) {
-                const int32_t pg = p0 + i % npg;
-                const int64_t bb = b_first + i / npg;
-                bad |= a.page_table[bb * a.max_pages + pg] != a.page_table[pg];
-            }
-            if (bad) raise_err(a.err, SPICY_DEVERR_SHARED);
-        }
+        raw_len = row_valid ? a.lengths[bq] : 0;
+        prow0 = static_cast<int64_t>(h) * G;
+        issue_loads();
     } else {
         blk -= a.prefix_blocks;
         const int sgb = (a.priv_splits + kWavesPerBlock - 1) / kWavesPerBlock;
@@ -313,18 +323,20 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
         const int64_t b = blk / H;
         if (split >= a.priv_splits || b >= a.B) return;
         slot = a.prefix_splits + split;
-        const int32_t len = checked_length(a, static_cast<int>(b));
+        raw_len = a.lengths[b];
         p0 = a.page_begin + split * a.pages_per_split;
-        p1 = min(p0 + a.pages_per_split, (len + kPage - 1) / kPage);
+        p1 = p0 + a.pages_per_split;                      // clamped to the length below
+        id_end = a.max_pages;
         table = a.page_table + b * a.max_pages;
         row_valid = row < G;
         prow = b * a.H_q + static_cast<int64_t>(h) * G + row;
-        rlen = len;
+        prow0 = b * a.H_q + static_cast<int64_t>(h) * G;
+        issue_loads();
     }
+    const int32_t len = (prefix_role && !row_valid) ? 0 : check_length(a, raw_len);
+    if (!prefix_role) p1 = min(p1, (len + kPage - 1) / kPage);
     if (p0 >= p1) return;
-
-    Tile<D> T;
-    T.init(row_valid ? static_cast<const uint16_t*>(a.q) + prow * D : nullptr, rlen);
+    T.init(row_valid, row_valid ? len : 0);
 
     // Pages go in windows of 64: one vector load brings the window's page ids
     // (lane i: page w0 + i) before its pipeline starts, so no wait inside the
@@ -332,7 +344,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
     PageRegs<D> buf[NBUF];
     for (int32_t w0 = p0; w0 < p1; w0 += kWave) {
         const int32_t w1 = min(w0 + kWave, p1);
-        const int32_t ids = (w0 + lane < w1) ? table[w0 + lane] : 0;
+        if (w0 != p0) ids = (w0 + lane < w1) ? table[w0 + lane] : 0;
         auto load = [&](PageRegs<D>& r, int32_t lp) {
             load_page<D>(a, r, __builtin_amdgcn_readlane(ids, min(lp, w1 - 1) - w0), h);
         };
@@ -347,6 +359,24 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
         }
     }
     T.store(a, row_valid, prow, slot);
+
+    // The KV head 0 wavefronts of the shared prefix check that the sequences
+    // of their tile map the chunk's pages like sequence 0 (independent loads,
+    // one flag).  It is done last, off the path to the first pages.
+    if (prefix_role && h == 0) {
+        const int rows = a.B * G;
+        const int b_first = (t * 16) / G;
+        const int b_last = min(rows - 1, t * 16 + 15) / G;
+        const int npg = p1 - p0;
+        const int n = (b_last - b_first + 1) * npg;
+        bool bad = false;
+        for (int i = lane; i < n; i += kWave) {
+            const int32_t pg = p0 + i % npg;
+            const int64_t bb = b_first + i / npg;
+            bad |= a.page_table[bb * a.max_pages + pg] != a.page_table[pg];
+        }
+        if (bad) raise_err(a.err, SPICY_DEVERR_SHARED);
+    }
 }
 
 // -------------------------------------------------------------- fp32 VALU
