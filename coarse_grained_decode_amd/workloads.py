@@ -102,6 +102,20 @@ class CoarsenCall:
 
 
 @dataclasses.dataclass
+class PolicySpec:
+    """Inputs of spicy_policy for a per-step chunk: the projection P of the
+    equal-variation feature as signed column lists (row r: proj_idx[proj_ptr[r]
+    : proj_ptr[r+1]], entry c + 1 for +1 at column c, -(c + 1) for -1), the
+    segment slots N per sequence and the landmark rule."""
+    proj_ptr: np.ndarray       # int32 [R+1]
+    proj_idx: np.ndarray       # int32 [nnz]
+    n_segments: int
+    n_landmarks: int
+    sink: int
+    recent: int
+
+
+@dataclasses.dataclass
 class Workload:
     name: str
     dtype: str
@@ -117,6 +131,7 @@ class Workload:
     q: np.ndarray                     # [B, H_q, d]
     description: str = ""
     shared_prefix_pages: int = 0      # leading logical pages identical in every table row
+    policy: Optional[PolicySpec] = None   # device-side policy for the per-step chunk, if offered
 
     @property
     def calls(self) -> List[CoarsenCall]:
@@ -261,6 +276,33 @@ def equal_variation_segments(quanta: np.ndarray, N: int) -> np.ndarray:
         bounds.append(min(b, T))
     bounds.append(T)
     return np.unique(np.asarray(bounds, dtype=np.int64))
+
+
+def sparse_sign_projection(rng: np.random.Generator, rows: int, cols: int,
+                           density: float) -> Tuple[np.ndarray, np.ndarray]:
+    """A very sparse random projection (Li, Hastie and Church, 2006): each
+    entry is +1 or -1 with probability density/2 and 0 otherwise, drawn row
+    by row.  Returned as (proj_ptr [rows+1], proj_idx [nnz]) with signed
+    1-based column ids; a row that draws no entry gets one random +-1 so that
+    every feature sees the input."""
+    ptr, idx = [0], []
+    for _ in range(rows):
+        u = rng.random(cols)
+        cols_r = np.nonzero(u < density)[0]
+        if cols_r.size == 0:
+            cols_r = rng.integers(0, cols, size=1)
+        sign = np.where(rng.random(cols_r.size) < 0.5, 1, -1)
+        idx.extend((sign * (cols_r + 1)).tolist())
+        ptr.append(len(idx))
+    return np.asarray(ptr, dtype=np.int32), np.asarray(idx, dtype=np.int32)
+
+
+def policy_spec(rng: np.random.Generator, H: int, d: int, n_segments: int, n_landmarks: int,
+                sink: int = 0, recent: int = 0, rows: int = 16) -> PolicySpec:
+    """Policy inputs with a 16-row projection of [k; v] at density 1/sqrt(2 H d)."""
+    D = 2 * H * d
+    ptr, idx = sparse_sign_projection(rng, rows, D, 1.0 / np.sqrt(D))
+    return PolicySpec(ptr, idx, n_segments, n_landmarks, sink, recent)
 
 
 # ---------------------------------------------------------------------------
@@ -422,10 +464,12 @@ def make_shared_prefix(config_id: int = 4, *, B: int = 32, H_q: int = 28, H_kv: 
     chunk_call = _concat_call(dtype, H_kv, d, rope_base, ks, vs, ms, ss,
                               prefix_T + S, table, entry_start)
     q = _query(rngs, B, H_q, d, dtype)
+    pol = policy_spec(np.random.Generator(np.random.PCG64(np.random.SeedSequence([1000 + config_id, 7]))),
+                      H_kv, d, N, n_land)
     return Workload(name=name, dtype=dtype, B=B, H_q=H_q, H_kv=H_kv, d=d, rope_base=rope_base,
                     num_pages=num_pages, setup=[prefix_call, suffix_call], step=chunk_call,
                     page_table=np.ascontiguousarray(table, dtype=np.int32), q=q,
-                    shared_prefix_pages=prefix_pages,
+                    shared_prefix_pages=prefix_pages, policy=pol,
                     description=f"{B} seqs share a {prefix_T}-token prefix at {ratio}x; "
                                 f"suffix U[{suffix_range[0]},{suffix_range[1]}] exact; "
                                 f"{chunk_T}-token chunk per step, equal-variation N={N}")
@@ -495,6 +539,39 @@ def random_decode_case(seed: int, *, B: int, H_q: int, H_kv: int, d: int, dtype:
     q = rng.standard_normal((B, H_q, d), dtype=np.float32)
     return DecodeCase(dtype, H_q, H_kv, d, _store(chunked(k), dtype), _store(chunked(v), dtype),
                       _store(ab, dtype), table, lengths, _store(q, dtype), prefix_pages)
+
+
+@dataclasses.dataclass
+class PolicyCase:
+    """Inputs of one spicy_policy call (host copies, bf16 bits)."""
+    k: np.ndarray              # uint16 [sum_T, H, d]
+    v: np.ndarray              # uint16 [sum_T, H, d]
+    seq_offsets: np.ndarray    # int32 [B+1]
+    spec: PolicySpec
+
+
+def random_policy_case(seed: int, *, B: int, T_range: Tuple[int, int], H: int, d: int, n_segments: int,
+                       n_landmarks: int, sink: int = 0, recent: int = 0, mean_run: float = 48.0,
+                       proj_rows: int = 16) -> PolicyCase:
+    """Clustered keys (geometric runs, as the benchmark workloads) and N(0, 1)
+    values for B sequences of U[T_range] tokens, with a seeded very sparse
+    projection of [k; v]."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(7000 + seed)))
+    rngs = {r: np.random.Generator(np.random.PCG64(ss))
+            for r, ss in zip(("runs", "centres", "noise", "values"), rng.bit_generator.seed_seq.spawn(4))}
+    Ts = rng.integers(T_range[0], T_range[1] + 1, size=B)
+    ks, vs = [], []
+    for T in Ts:
+        ks.append(_store(clustered_keys(rngs, int(T), H, d, None, mean_run), "bf16"))
+        vs.append(_store(rngs["values"].standard_normal((int(T), H, d), dtype=np.float32), "bf16"))
+    so = np.zeros(B + 1, dtype=np.int32)
+    so[1:] = np.cumsum(Ts)
+    D = 2 * H * d
+    ptr, idx = sparse_sign_projection(rng, proj_rows, D, 1.0 / np.sqrt(D))
+    spec = PolicySpec(ptr, idx, n_segments, n_landmarks, sink, recent)
+    k = np.concatenate(ks) if B else np.zeros((0, H, d), np.uint16)
+    v = np.concatenate(vs) if B else np.zeros((0, H, d), np.uint16)
+    return PolicyCase(k, v, so, spec)
 
 
 def tiny_fp32(**over) -> Workload:

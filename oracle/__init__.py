@@ -66,6 +66,13 @@ def lib():
             L.oracle_bf16_value.argtypes = [ctypes.c_uint16]
             L.oracle_rope.restype = None
             L.oracle_rope.argtypes = [P, P, i32, ctypes.c_double, ctypes.c_double]
+            L.oracle_fix16.restype = ctypes.c_int64
+            L.oracle_fix16.argtypes = [ctypes.c_uint16]
+            L.oracle_isqrt_u128.restype = ctypes.c_uint64
+            L.oracle_isqrt_u128.argtypes = [ctypes.c_uint64, ctypes.c_uint64]
+            L.oracle_policy.restype = ctypes.c_int
+            L.oracle_policy.argtypes = [i32, i32, P, P, P, i32, P, P, i32, i32, i32, i32, i32,
+                                        P, P, P, P, P]
             _lib = L
     return _lib
 
@@ -205,3 +212,49 @@ def rope(x: np.ndarray, pos: float, base: float) -> np.ndarray:
     y = np.empty_like(x)
     lib().oracle_rope(_p(y), _p(x), int(x.shape[0]), float(pos), float(base))
     return y
+
+
+# ---------------------------------------------------------------------------
+# per-step policy (equal-variation segments, key-norm landmarks)
+# ---------------------------------------------------------------------------
+
+def fix16(bits: int) -> int:
+    """bf16 value x -> x * 2^16 rounded half to even, clamped to +-2^28."""
+    return int(lib().oracle_fix16(int(bits) & 0xFFFF))
+
+
+def isqrt_u128(x: int) -> int:
+    """floor(sqrt(x)) for 0 <= x < 2^128, as the policy computes it."""
+    return int(lib().oracle_isqrt_u128((x >> 64) & 0xFFFFFFFFFFFFFFFF, x & 0xFFFFFFFFFFFFFFFF))
+
+
+class PolicyResult:
+    def __init__(self, seg_offsets, seq_seg_ptr, mask, variation, norm2):
+        self.seg_offsets, self.seq_seg_ptr, self.mask = seg_offsets, seq_seg_ptr, mask
+        self.variation, self.norm2 = variation, norm2
+
+
+def policy(k: np.ndarray, v: np.ndarray, seq_offsets: np.ndarray, proj_ptr: np.ndarray,
+           proj_idx: np.ndarray, n_segments: int, n_landmarks: int, sink: int, recent: int) -> PolicyResult:
+    """oracle_policy: k, v [total_tokens, H, d] bf16 bits (uint16).  Returns the
+    N-slot segment offsets [B*N + 1], seq_seg_ptr [B + 1], the protection mask
+    [total_tokens, H] and the per-token variation d_t and key norms^2."""
+    k = np.ascontiguousarray(k, dtype=np.uint16)
+    v = np.ascontiguousarray(v, dtype=np.uint16)
+    T, H, d = k.shape
+    so = np.ascontiguousarray(seq_offsets, dtype=np.int32)
+    B = so.shape[0] - 1
+    pp = np.ascontiguousarray(proj_ptr, dtype=np.int32)
+    pi = np.ascontiguousarray(proj_idx, dtype=np.int32)
+    seg = np.zeros(B * n_segments + 1, dtype=np.int32)
+    ssp = np.zeros(B + 1, dtype=np.int32)
+    mask = np.zeros((T, H), dtype=np.uint8)
+    var = np.zeros(T, dtype=np.int64)
+    n2 = np.zeros((T, H), dtype=np.uint64)
+    rc = lib().oracle_policy(H, d, _p(k), _p(v), _p(so), B, _p(pp), _p(pi) if pi.size else _p(np.zeros(1, np.int32)),
+                             pp.shape[0] - 1, n_segments, n_landmarks, sink, recent,
+                             _p(seg), _p(ssp), _p(mask), _p(var), _p(n2))
+    if rc != 0:
+        raise RuntimeError(f"oracle_policy failed ({rc})")
+    return PolicyResult(seg, ssp, mask, var, n2)
+

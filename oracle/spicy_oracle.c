@@ -372,3 +372,196 @@ int oracle_decode(int q_dtype, int dtype, int32_t H_q, int32_t H_kv, int32_t d,
     free(s);
     return 0;
 }
+
+/* ------------------------------------------------------------------------
+ * Per-step coarsening policy (the step upstream of oracle_coarsen).
+ *
+ * Equal-variation segments: Equal-Variation KV Cache page, "Mathematical
+ * statement" (breakpoints at equal increments of cumulative variation, first
+ * hitting time on flat stretches) and "Implementation notes" (feature
+ * z_t = P [k_t; v_t] with P a fixed random projection, local variation
+ * d_t = ||z_t - z_{t-1}||_2, cumulative c_t, thresholds q_j = j c_T / N,
+ * boundary = the first token whose cumulative variation reaches q_j).
+ * Landmarks: SPICY-KV demo page, Claim 2 (exact C-points) and section 1
+ * (sink and recent tokens kept exact); the landmark rule is the largest key
+ * norms per (sequence, KV head).
+ *
+ * Everything is integer, so the result does not depend on any summation
+ * order:
+ *   fix(x)   = x * 2^16 rounded to nearest, ties to even, clamped to
+ *              [-2^28, 2^28] (bf16 input; NaN -> 0, +-inf -> +-2^28);
+ *   z_t[r]   = sum over the entries of row r of P of sign * fix(x_t[c]),
+ *              x_t = [k_t (head-major); v_t (head-major)], P ternary and
+ *              given as signed column lists;
+ *   d_t      = floor(sqrt(sum_r (z_t[r] - z_{t-1}[r])^2)), d = 0 at a
+ *              sequence's first token;
+ *   C_t      = d_0 + ... + d_t,  Q_j = floor(j * C_T / N), j = 1..N-1;
+ *   b_j      = min { t : C_t >= Q_j };   segment j = [b_j, b_{j+1}),
+ *              b_0 = 0, b_N = T, so N slots per sequence, empty ones allowed;
+ *   norm2    = sum_i fix(k_t,h[i])^2 (uint64), landmarks = the n_landmarks
+ *              largest norm2 among positions [sink, T - recent) of the
+ *              sequence, ties to the lower position; the mask also holds
+ *              the first `sink` and the last `recent` positions.
+ * ------------------------------------------------------------------------ */
+
+int64_t oracle_fix16(uint16_t bits) {
+    const int64_t lim = (int64_t)1 << 28;
+    int neg = (bits >> 15) & 1;
+    int e = (bits >> 7) & 0xFF;
+    int64_t m = bits & 0x7F;
+    int64_t r;
+    if (e == 0xFF) {
+        if (m) return 0;                                  /* NaN */
+        r = lim;                                          /* infinity */
+    } else if (e == 0) {
+        r = 0;                                            /* |x| < 2^-126: rounds to 0 */
+    } else {
+        /* x = (128 + m) * 2^(e - 134);  x * 2^16 = (128 + m) * 2^(e - 118) */
+        int64_t M = 128 + m;
+        int sh = e - 118;
+        if (sh >= 0) {
+            r = sh > 21 ? lim : (M << sh);                /* M < 2^8: sh > 21 exceeds 2^28 */
+            if (r > lim) r = lim;
+        } else if (sh < -9) {
+            r = 0;                                        /* M / 2^10 < 1/2 */
+        } else {
+            int64_t q = M >> (-sh);
+            int64_t rem = M - (q << (-sh));
+            int64_t half = (int64_t)1 << (-sh - 1);
+            if (rem > half || (rem == half && (q & 1))) ++q;
+            r = q;
+        }
+    }
+    return neg ? -r : r;
+}
+
+/* floor(sqrt(x)) for a 128-bit x, by bisection on the answer: the largest
+ * r < 2^64 with r * r <= x. */
+static uint64_t isqrt_u128(unsigned __int128 x) {
+    uint64_t lo = 0, hi = UINT64_MAX;
+    while (lo < hi) {
+        uint64_t mid = lo + ((hi - lo) >> 1) + ((hi - lo) & 1);     /* upper middle, no overflow */
+        unsigned __int128 sq = (unsigned __int128)mid * mid;
+        if (sq <= x) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+uint64_t oracle_isqrt_u128(uint64_t hi, uint64_t lo) {
+    return isqrt_u128(((unsigned __int128)hi << 64) | lo);
+}
+
+typedef struct { uint64_t norm2; int32_t pos; } oracle_rank;
+
+static int rank_cmp(const void* a, const void* b) {
+    const oracle_rank* x = (const oracle_rank*)a;
+    const oracle_rank* y = (const oracle_rank*)b;
+    if (x->norm2 != y->norm2) return x->norm2 > y->norm2 ? -1 : 1;   /* larger norm first */
+    return (x->pos > y->pos) - (x->pos < y->pos);                     /* then lower position */
+}
+
+int oracle_policy(int32_t H_kv, int32_t d, const uint16_t* k_pre, const uint16_t* v,
+                  const int32_t* seq_offsets, int32_t B,
+                  const int32_t* proj_ptr, const int32_t* proj_idx, int32_t proj_rows,
+                  int32_t n_segments, int32_t n_landmarks, int32_t sink, int32_t recent,
+                  int32_t* seg_offsets, int32_t* seq_seg_ptr, uint8_t* protected_mask,
+                  int64_t* variation_out, uint64_t* norm2_out) {
+    if (H_kv <= 0 || d <= 0 || B < 0 || proj_rows <= 0 || proj_rows > 16) return 1;
+    if (n_segments <= 0 || n_landmarks < 0 || sink < 0 || recent < 0) return 1;
+    if (!k_pre || !v || !seq_offsets || !proj_ptr || !proj_idx || !seg_offsets || !seq_seg_ptr ||
+        !protected_mask)
+        return 1;
+    const int64_t width = (int64_t)H_kv * d;              /* one of k_t, v_t */
+    if (proj_ptr[0] != 0) return 2;
+    for (int32_t r = 0; r < proj_rows; ++r) {
+        if (proj_ptr[r + 1] < proj_ptr[r]) return 2;
+        for (int32_t i = proj_ptr[r]; i < proj_ptr[r + 1]; ++i) {
+            int64_t c = proj_idx[i] > 0 ? proj_idx[i] - 1 : -(int64_t)proj_idx[i] - 1;
+            if (proj_idx[i] == 0 || c >= 2 * width) return 2;
+        }
+    }
+    for (int32_t b = 0; b <= B; ++b) seq_seg_ptr[b] = b * n_segments;
+
+    int64_t z_prev[16], z[16];
+    for (int32_t b = 0; b < B; ++b) {
+        const int32_t t0 = seq_offsets[b], t1 = seq_offsets[b + 1];
+        if (t0 < 0 || t1 < t0) return 2;
+        const int32_t T = t1 - t0;
+        if (T > (1 << 20)) return 4;
+        int64_t* C = (int64_t*)malloc(sizeof(int64_t) * (size_t)(T > 0 ? T : 1));
+        if (!C) return 1;
+        /* variation and cumulative variation */
+        int64_t acc = 0;
+        for (int32_t t = 0; t < T; ++t) {
+            const size_t row = (size_t)(t0 + t) * (size_t)width;
+            for (int32_t r = 0; r < proj_rows; ++r) {
+                int64_t s = 0;
+                for (int32_t i = proj_ptr[r]; i < proj_ptr[r + 1]; ++i) {
+                    int64_t c = proj_idx[i] > 0 ? proj_idx[i] - 1 : -(int64_t)proj_idx[i] - 1;
+                    uint16_t bits = c < width ? k_pre[row + (size_t)c] : v[row + (size_t)(c - width)];
+                    int64_t x = oracle_fix16(bits);
+                    s += proj_idx[i] > 0 ? x : -x;
+                }
+                z[r] = s;
+            }
+            uint64_t dt = 0;
+            if (t > 0) {
+                unsigned __int128 ss = 0;
+                for (int32_t r = 0; r < proj_rows; ++r) {
+                    int64_t dz = z[r] - z_prev[r];
+                    unsigned __int128 a = (unsigned __int128)(dz < 0 ? -dz : dz);
+                    ss += a * a;
+                }
+                dt = isqrt_u128(ss);
+            }
+            for (int32_t r = 0; r < proj_rows; ++r) z_prev[r] = z[r];
+            acc += (int64_t)dt;
+            C[t] = acc;
+            if (variation_out) variation_out[t0 + t] = (int64_t)dt;
+        }
+        const int64_t CT = T > 0 ? C[T - 1] : 0;
+        if (CT > 0 && (unsigned __int128)CT * (unsigned __int128)n_segments >= ((unsigned __int128)1 << 62)) {
+            free(C);
+            return 4;
+        }
+        /* boundaries: b_j = min { t : C_t >= Q_j } (T if none) */
+        int32_t* so = seg_offsets + (size_t)b * (size_t)n_segments;
+        so[0] = t0;
+        int32_t t = 0;
+        for (int32_t j = 1; j < n_segments; ++j) {
+            int64_t Q = (int64_t)(((unsigned __int128)j * (unsigned __int128)CT) / (unsigned __int128)n_segments);
+            while (t < T && C[t] < Q) ++t;
+            so[j] = t0 + t;
+        }
+        free(C);
+
+        /* protection mask: sink, recent, landmarks per head */
+        oracle_rank* cand = (oracle_rank*)malloc(sizeof(oracle_rank) * (size_t)(T > 0 ? T : 1));
+        if (!cand) return 1;
+        for (int32_t h = 0; h < H_kv; ++h) {
+            int32_t n = 0;
+            for (int32_t u = 0; u < T; ++u) {
+                const size_t row = ((size_t)(t0 + u) * (size_t)H_kv + (size_t)h) * (size_t)d;
+                uint64_t n2 = 0;
+                for (int32_t i = 0; i < d; ++i) {
+                    int64_t x = oracle_fix16(k_pre[row + (size_t)i]);
+                    n2 += (uint64_t)(x * x);
+                }
+                if (norm2_out) norm2_out[(size_t)(t0 + u) * (size_t)H_kv + (size_t)h] = n2;
+                int prot = u < sink || u >= T - recent;
+                protected_mask[(size_t)(t0 + u) * (size_t)H_kv + (size_t)h] = (uint8_t)prot;
+                if (!prot) {
+                    cand[n].norm2 = n2;
+                    cand[n].pos = u;
+                    ++n;
+                }
+            }
+            qsort(cand, (size_t)n, sizeof(oracle_rank), rank_cmp);
+            for (int32_t i = 0; i < n && i < n_landmarks; ++i)
+                protected_mask[(size_t)(t0 + cand[i].pos) * (size_t)H_kv + (size_t)h] = 1;
+        }
+        free(cand);
+    }
+    seg_offsets[(size_t)B * (size_t)n_segments] = seq_offsets[B];
+    return 0;
+}

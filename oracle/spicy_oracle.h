@@ -68,6 +68,18 @@ uint16_t oracle_bf16_round(double x);
 double oracle_bf16_value(uint16_t bits);
 void oracle_rope(double* y, const double* x, int32_t d, double pos, double base);
 
+/* Per-step coarsening policy: equal-variation segments and key-norm
+ * landmarks, in integer arithmetic (see spicy_oracle.c).  Return codes as
+ * above, plus 4 = a sequence outside the policy's integer range. */
+int64_t oracle_fix16(uint16_t bf16_bits);
+uint64_t oracle_isqrt_u128(uint64_t hi, uint64_t lo);
+int oracle_policy(int32_t H_kv, int32_t d, const uint16_t* k_pre, const uint16_t* v,
+                  const int32_t* seq_offsets, int32_t B,
+                  const int32_t* proj_ptr, const int32_t* proj_idx, int32_t proj_rows,
+                  int32_t n_segments, int32_t n_landmarks, int32_t sink, int32_t recent,
+                  int32_t* seg_offsets, int32_t* seq_seg_ptr, uint8_t* protected_mask,
+                  int64_t* variation_out, uint64_t* norm2_out);
+
 #ifdef __cplusplus
 }
 #endif
