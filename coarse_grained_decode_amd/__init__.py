@@ -19,9 +19,10 @@ __all__ = [
     "SpicyError", "PagedCache", "spicy_coarsen", "spicy_decode_attn",
     "spicy_coarsen_workspace_bytes", "spicy_decode_workspace_bytes", "spicy_decode_num_splits",
     "spicy_decode_attn_shared", "spicy_decode_shared_workspace_bytes",
+    "spicy_policy", "spicy_policy_workspace_bytes",
     "spicy_status_string", "library_path", "load_library",
     "SPICY_F32", "SPICY_BF16", "PAGE_SIZE", "WORKSPACE_HEADER",
-    "DEVERR_PAGE_ID", "DEVERR_CAPACITY", "DEVERR_SEGMENTS", "DEVERR_LENGTH",
+    "DEVERR_PAGE_ID", "DEVERR_CAPACITY", "DEVERR_SEGMENTS", "DEVERR_LENGTH", "DEVERR_POLICY",
 ]
 
 SPICY_F32 = 0
@@ -32,6 +33,8 @@ DEVERR_PAGE_ID = 0x1
 DEVERR_CAPACITY = 0x2
 DEVERR_SEGMENTS = 0x4
 DEVERR_LENGTH = 0x8
+DEVERR_SHARED = 0x10
+DEVERR_POLICY = 0x20
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libspicy.so")
@@ -83,6 +86,11 @@ def load_library():
     L.spicy_decode_shared_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     L.spicy_decode_attn_shared.restype = ctypes.c_int
     L.spicy_decode_attn_shared.argtypes = [CP, P, i32, P, i32, P, i32, i32, P, P, P, sz, i32, P]
+    L.spicy_policy_workspace_bytes.restype = sz
+    L.spicy_policy_workspace_bytes.argtypes = [i32, i32]
+    L.spicy_policy.restype = ctypes.c_int
+    L.spicy_policy.argtypes = [P, P, i32, i32, i32, i32, P, i32, P, P, i32, i32, i32, i32, i32, i32,
+                               P, P, P, P, sz, P]
     _lib = L
     return L
 
@@ -233,6 +241,29 @@ def spicy_decode_attn_shared(cache: PagedCache, q, page_table, lengths, shared_p
                                     _ptr(workspace), ws_bytes, int(num_splits), _stream(stream))
     if rc != 0:
         raise SpicyError(rc, "spicy_decode_attn_shared")
+
+
+def spicy_policy_workspace_bytes(total_tokens: int, num_kv_heads: int) -> int:
+    return int(load_library().spicy_policy_workspace_bytes(total_tokens, num_kv_heads))
+
+
+def spicy_policy(k_pre, v, seq_offsets, proj_ptr, proj_idx, n_segments: int, n_landmarks: int, sink: int,
+                 recent: int, seg_offsets, seq_seg_ptr, protected_mask, workspace, stream=None, *,
+                 B: int | None = None, total_tokens: int | None = None) -> None:
+    """spicy_policy through the C ABI (see include/spicy.h): segment slots and
+    protection mask of a chunk (k_pre, v: [total_tokens, H, d] bf16)."""
+    L = load_library()
+    B = int(seq_offsets.shape[0] - 1) if B is None else B
+    total_tokens = int(k_pre.shape[0]) if total_tokens is None else total_tokens
+    H, d = int(k_pre.shape[1]), int(k_pre.shape[2])
+    dtype = SPICY_BF16 if k_pre.dtype == torch.bfloat16 else SPICY_F32
+    ws_bytes = workspace.numel() * workspace.element_size() if isinstance(workspace, torch.Tensor) else 0
+    rc = L.spicy_policy(_ptr(k_pre), _ptr(v), total_tokens, H, d, dtype, _ptr(seq_offsets), B,
+                        _ptr(proj_ptr), _ptr(proj_idx), int(proj_ptr.shape[0] - 1), int(proj_idx.numel()),
+                        int(n_segments), int(n_landmarks), int(sink), int(recent), _ptr(seg_offsets),
+                        _ptr(seq_seg_ptr), _ptr(protected_mask), _ptr(workspace), ws_bytes, _stream(stream))
+    if rc != 0:
+        raise SpicyError(rc, "spicy_policy")
 
 
 def workspace(nbytes: int, device) -> torch.Tensor:

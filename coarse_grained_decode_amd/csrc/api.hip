@@ -282,4 +282,59 @@ spicy_status spicy_decode_attn_shared(const spicy_cache* cache, const void* q, i
     return spicy::launch_decode(a, cache->dtype, cache->head_dim, static_cast<hipStream_t>(stream));
 }
 
+size_t spicy_policy_workspace_bytes(int32_t total_tokens, int32_t num_kv_heads) {
+    if (total_tokens < 0 || num_kv_heads < 1) return 0;
+    const size_t T = static_cast<size_t>(total_tokens);
+    return SPICY_WORKSPACE_HEADER + align_up(8 * T) + align_up(8 * T * static_cast<size_t>(num_kv_heads));
+}
+
+spicy_status spicy_policy(const void* k_pre, const void* v, int32_t total_tokens, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t dtype, const int32_t* seq_offsets, int32_t B,
+                          const int32_t* proj_ptr, const int32_t* proj_idx, int32_t proj_rows, int32_t proj_nnz,
+                          int32_t n_segments, int32_t n_landmarks, int32_t sink, int32_t recent,
+                          int32_t* seg_offsets, int32_t* seq_seg_ptr, uint8_t* protected_mask, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+    if (dtype != SPICY_BF16 && dtype != SPICY_F32) return SPICY_ERR_ARG;
+    if (dtype != SPICY_BF16) return SPICY_ERR_UNSUPPORTED;
+    if (!head_dim_ok(head_dim)) return SPICY_ERR_UNSUPPORTED;
+    if (num_kv_heads < 1 || num_kv_heads > kMaxKvHeads) return SPICY_ERR_UNSUPPORTED;
+    if (total_tokens < 0 || B < 0 || proj_nnz < 0 || n_segments < 1 || n_landmarks < 0 || sink < 0 ||
+        recent < 0 || proj_rows < 1 || proj_rows > 16)
+        return SPICY_ERR_ARG;
+    if (static_cast<int64_t>(B) * n_segments + 1 > INT32_MAX) return SPICY_ERR_ARG;
+    if (B > kMaxGridY) return SPICY_ERR_UNSUPPORTED;
+    if (B == 0) return SPICY_OK;
+    if (!k_pre || !v || !seq_offsets || !proj_ptr || (proj_nnz > 0 && !proj_idx) || !seg_offsets ||
+        !seq_seg_ptr || !protected_mask || !workspace)
+        return SPICY_ERR_ARG;
+    if (workspace_bytes < spicy_policy_workspace_bytes(total_tokens, num_kv_heads)) return SPICY_ERR_CAPACITY;
+
+    spicy::PolicyArgs a{};
+    a.k = static_cast<const uint16_t*>(k_pre);
+    a.v = static_cast<const uint16_t*>(v);
+    a.seq_offsets = seq_offsets;
+    a.proj_ptr = proj_ptr;
+    a.proj_idx = proj_idx;
+    a.seg_offsets = seg_offsets;
+    a.seq_seg_ptr = seq_seg_ptr;
+    a.mask = protected_mask;
+    char* ws = static_cast<char*>(workspace);
+    a.err = reinterpret_cast<int32_t*>(ws);
+    size_t off = SPICY_WORKSPACE_HEADER;
+    a.var = reinterpret_cast<int64_t*>(ws + off);
+    off += align_up(8 * static_cast<size_t>(total_tokens));
+    a.norm2 = reinterpret_cast<uint64_t*>(ws + off);
+    a.total_tokens = total_tokens;
+    a.B = B;
+    a.H = num_kv_heads;
+    a.d = head_dim;
+    a.R = proj_rows;
+    a.nnz = proj_nnz;
+    a.N = n_segments;
+    a.L = n_landmarks;
+    a.sink = sink;
+    a.recent = recent;
+    return spicy::launch_policy(a, static_cast<hipStream_t>(stream));
+}
+
 }  // extern "C"

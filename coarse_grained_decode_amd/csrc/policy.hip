@@ -1,0 +1,413 @@
+// SPICY-KV per-step policy on gfx950: the segment partition and the
+// protection mask of a freshly appended chunk, computed from the chunk itself
+// (the inputs spicy_coarsen then consumes).
+//
+// Equal-Variation KV Cache page, "Mathematical statement" and "Implementation
+// notes": a feature z_t = P [k_t; v_t] with P a fixed random projection, the
+// local variation d_t = ||z_t - z_{t-1}||_2, the cumulative variation, the
+// thresholds q_j = j c_T / N and each boundary at the first token whose
+// cumulative variation reaches the next threshold (first hitting time).
+// SPICY-KV demo page, Claim 2 and section 1: exact C-points (the landmarks:
+// here the largest key norms per KV head) and protected sink / recent tokens.
+//
+// The arithmetic is integer end to end, so every order of summation gives
+// the same bits:
+//   fix(x)  = x * 2^16 rounded half to even, clamped to +-2^28, NaN -> 0.
+//             Done in fp32, which is exact here: bf16 -> fp32 is exact, the
+//             scaling by 2^16 is exact and v_rndne_f32 rounds that exact
+//             value half to even.
+//   z_t[r]  = sum of sign * fix(x_t[c]) over the entries of row r (int64);
+//   d_t     = floor(sqrt(sum_r (z_t[r] - z_{t-1}[r])^2)), the square sum in
+//             128 bits, the root from an fp64 estimate corrected with exact
+//             integer comparisons; d = 0 at a sequence's first token;
+//   C_t     = prefix sums of d, and with
+//             cnt(C) = #{j in [1, N-1] : floor(j C_T / N) <= C}
+//                    = clamp(floor(((C + 1) N - 1) / C_T), 0, N - 1)
+//             token t is boundary b_j = min{t : C_t >= floor(j C_T / N)} of
+//             every j in (cnt(C_{t-1}), cnt(C_t)] (cnt(C_{-1}) = 0);
+//   norm2   = sum_i fix(k_t,h[i])^2 (uint64); the landmarks of (sequence,
+//             head) are its L largest among the positions [sink, T - recent),
+//             ties to the lower position: an 8-bit radix select finds the
+//             L-th largest value, a position-ordered scan takes its ties.
+//
+// policy_token_kernel: one wavefront per run of kRun consecutive tokens (it
+//   recomputes z of the token before its run); token rows stream through a
+//   ring of kRing prefetched tokens, and each row is staged as fixed-point
+//   int32 in the wavefront's LDS slice for the projection's gathers: lanes
+//   4r .. 4r+3 own row r of P, each every fourth entry.  Writes d_t and
+//   norm2[t][h].
+// policy_seq_kernel: workgroup (b, y).  y < H: landmarks of head y of
+//   sequence b, written into that head's mask column.  y == H: the scan of
+//   d over the sequence and its N segment offsets.
+#include "launch.h"
+#include "spicy_device.h"
+
+namespace spicy {
+
+namespace {
+
+constexpr int kRun = 32;             // tokens per wavefront
+constexpr int kRing = 4;             // token rows in flight per wavefront
+constexpr int kMaxEnt = 16;          // projection entries a lane keeps in registers
+constexpr int kTokWaves = 4;         // wavefronts per token workgroup
+constexpr int kSeqThreads = 256;
+constexpr int64_t kRangeLimit = int64_t(1) << 62;
+
+__device__ __forceinline__ int32_t fix16(uint32_t bf16_bits) {
+    const float x = __uint_as_float(bf16_bits << 16);
+    if (x != x) return 0;
+    const float y = __builtin_amdgcn_fmed3f(__builtin_rintf(x * 65536.0f), -268435456.0f, 268435456.0f);
+    return static_cast<int32_t>(y);
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {
+    const uint32_t lo = static_cast<uint32_t>(__shfl_xor(static_cast<int>(x & 0xFFFFFFFFu), m));
+    const uint32_t hi = static_cast<uint32_t>(__shfl_xor(static_cast<int>(x >> 32), m));
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t shfl_up_u64(uint64_t x, int d) {
+    const uint32_t lo = static_cast<uint32_t>(__shfl_up(static_cast<int>(x & 0xFFFFFFFFu), d));
+    const uint32_t hi = static_cast<uint32_t>(__shfl_up(static_cast<int>(x >> 32), d));
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t isqrt_u128(unsigned __int128 s) {
+    const double est = static_cast<double>(static_cast<uint64_t>(s >> 64)) * 18446744073709551616.0 +
+                       static_cast<double>(static_cast<uint64_t>(s));
+    uint64_t r = static_cast<uint64_t>(sqrt(est));
+    while (static_cast<unsigned __int128>(r) * r > s) --r;
+    while (static_cast<unsigned __int128>(r + 1) * (r + 1) <= s) ++r;
+    return r;
+}
+
+// A projection entry, checked: returned as is when its column lies inside
+// [k_t; v_t], else 0 (skipped) with the error bit raised.
+__device__ __forceinline__ int32_t checked_entry(const PolicyArgs& a, int32_t e, int32_t width2) {
+    const int32_t c = e > 0 ? e - 1 : -e - 1;
+    if (e == 0 || c >= width2) {
+        raise_err(a.err, SPICY_DEVERR_POLICY);
+        return 0;
+    }
+    return e;
+}
+
+template <int CPL>
+struct TokRow {
+    uint4 k[CPL], v[CPL];
+};
+
+template <int D, int CPL>
+__global__ __launch_bounds__(kTokWaves * kWave) void policy_token_kernel(PolicyArgs a) {
+    extern __shared__ int32_t lds[];
+    const int lane = threadIdx.x % kWave;
+    const int wave = threadIdx.x / kWave;
+    const int H = a.H;
+    const int W = H * D;                 // elements of k_t (and of v_t)
+    const int nch = W / 8;               // 16-byte chunks of one row
+    int32_t* xs = lds + static_cast<int64_t>(wave) * 2 * W;
+    const int64_t run = static_cast<int64_t>(blockIdx.x) * kTokWaves + wave;
+    const int64_t t_begin = run * kRun;
+    if (t_begin >= a.total_tokens) return;
+    const int64_t t_end = min(t_begin + kRun, static_cast<int64_t>(a.total_tokens));
+
+    // this lane's projection entries: row r = lane / 4, entries q, q + 4, ...
+    const int r = lane / 4, q = lane % 4;
+    int32_t e0 = 0, n_own = 0;
+    if (r < a.R) {
+        e0 = a.proj_ptr[r];
+        const int32_t e1 = a.proj_ptr[r + 1];
+        if (e0 < 0 || e1 < e0 || e1 > a.nnz) {
+            raise_err(a.err, SPICY_DEVERR_POLICY);
+            e0 = 0;
+        } else {
+            n_own = max(0, (e1 - e0 - q + 3) / 4);
+        }
+    }
+    int32_t ent[kMaxEnt];
+#pragma unroll
+    for (int i = 0; i < kMaxEnt; ++i) ent[i] = i < n_own ? checked_entry(a, a.proj_idx[e0 + q + 4 * i], 2 * W) : 0;
+
+    // the sequence holding t_begin: the largest b with seq_offsets[b] <= t_begin
+    int32_t lo = 0, hi = a.B;
+    while (lo < hi) {
+        const int32_t mid = (lo + hi + 1) / 2;
+        if (a.seq_offsets[mid] <= t_begin) lo = mid; else hi = mid - 1;
+    }
+    int32_t b = lo;
+    int64_t cur_start = a.seq_offsets[b];
+    int64_t next_start = b < a.B ? a.seq_offsets[b + 1] : INT64_MAX;
+    // z of the token before the run, unless the run starts a sequence
+    const int64_t t_first = (t_begin == cur_start || t_begin == 0) ? t_begin : t_begin - 1;
+
+    const uint16_t* kin = a.k;
+    const uint16_t* vin = a.v;
+    auto load = [&](TokRow<CPL>& x, int64_t t) {
+        const int64_t tc = min(t, t_end - 1);
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const int c = min(lane + kWave * j, nch - 1);
+            x.k[j] = *reinterpret_cast<const uint4*>(kin + tc * W + 8 * c);
+            x.v[j] = *reinterpret_cast<const uint4*>(vin + tc * W + 8 * c);
+        }
+    };
+
+    int64_t zprev = 0;
+    auto process = [&](const TokRow<CPL>& x, int64_t t) {
+        while (b < a.B && t >= next_start) {          // sequences are contiguous: step to t's
+            ++b;
+            cur_start = next_start;
+            next_start = b < a.B ? a.seq_offsets[b + 1] : INT64_MAX;
+        }
+        const bool first = (b >= a.B) || t == cur_start;
+        const bool out = t >= t_begin;
+        // fixed point, staged in LDS; squared norms per head
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const int c = lane + kWave * j;
+            uint64_t n2 = 0;
+            if (c < nch) {
+                const uint32_t kw[4] = {x.k[j].x, x.k[j].y, x.k[j].z, x.k[j].w};
+                const uint32_t vw[4] = {x.v[j].x, x.v[j].y, x.v[j].z, x.v[j].w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t kb = (e & 1) ? (kw[e / 2] >> 16) : (kw[e / 2] & 0xFFFFu);
+                    const uint32_t vb = (e & 1) ? (vw[e / 2] >> 16) : (vw[e / 2] & 0xFFFFu);
+                    const int32_t xk = fix16(kb);
+                    xs[8 * c + e] = xk;
+                    xs[W + 8 * c + e] = fix16(vb);
+                    n2 += static_cast<uint64_t>(static_cast<int64_t>(xk) * xk);
+                }
+            }
+            // lanes of one head are D/8 consecutive chunks
+#pragma unroll
+            for (int o = 1; o < D / 8; o <<= 1) n2 += shfl_xor_u64(n2, o);
+            if (out && c < nch && (c % (D / 8)) == 0) a.norm2[t * H + (8 * c) / D] = n2;
+        }
+        __builtin_amdgcn_wave_barrier();
+        // projection row r: this lane's entries, then the other three lanes'
+        int64_t acc = 0;
+#pragma unroll
+        for (int i = 0; i < kMaxEnt; ++i) {
+            const int32_t e = ent[i];
+            if (e != 0) {
+                const int32_t v = xs[e > 0 ? e - 1 : -e - 1];
+                acc += e > 0 ? v : -v;
+            }
+        }
+        for (int32_t i = kMaxEnt; i < n_own; ++i) {
+            const int32_t e = checked_entry(a, a.proj_idx[e0 + q + 4 * i], 2 * W);
+            if (e != 0) {
+                const int32_t v = xs[e > 0 ? e - 1 : -e - 1];
+                acc += e > 0 ? v : -v;
+            }
+        }
+        acc += static_cast<int64_t>(shfl_xor_u64(static_cast<uint64_t>(acc), 1));
+        acc += static_cast<int64_t>(shfl_xor_u64(static_cast<uint64_t>(acc), 2));
+        const int64_t z = r < a.R ? acc : 0;
+        const int64_t dz = z - zprev;
+        zprev = z;
+        const uint64_t adz = static_cast<uint64_t>(dz < 0 ? -dz : dz);
+        unsigned __int128 sq = (q == 0) ? static_cast<unsigned __int128>(adz) * adz : 0;
+        uint64_t sl = static_cast<uint64_t>(sq), sh = static_cast<uint64_t>(sq >> 64);
+#pragma unroll
+        for (int o = 4; o < kWave; o <<= 1) {
+            const uint64_t ol = shfl_xor_u64(sl, o), oh = shfl_xor_u64(sh, o);
+            const uint64_t nl = sl + ol;
+            sh = sh + oh + (nl < sl ? 1 : 0);
+            sl = nl;
+        }
+        const uint64_t d = first ? 0 : isqrt_u128((static_cast<unsigned __int128>(sh) << 64) | sl);
+        if (out && lane == 0) a.var[t] = static_cast<int64_t>(d);
+        __builtin_amdgcn_wave_barrier();
+    };
+
+    TokRow<CPL> ring[kRing];
+#pragma unroll
+    for (int u = 0; u < kRing; ++u) load(ring[u], t_first + u);
+    for (int64_t tt = t_first; tt < t_end; tt += kRing) {
+#pragma unroll
+        for (int u = 0; u < kRing; ++u) {
+            if (tt + u < t_end) process(ring[u], tt + u);
+            load(ring[u], tt + u + kRing);
+        }
+    }
+}
+
+// Exclusive prefix sum over the workgroup (kSeqThreads threads) and the total.
+__device__ __forceinline__ int64_t block_exclusive_scan(int64_t x, int64_t* total, int64_t* scratch) {
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    int64_t incl = x;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int64_t y = static_cast<int64_t>(shfl_up_u64(static_cast<uint64_t>(incl), o));
+        if (lane >= o) incl += y;
+    }
+    if (lane == kWave - 1) scratch[wave] = incl;
+    __syncthreads();
+    int64_t before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < kSeqThreads / kWave; ++w) {
+        const int64_t s = scratch[w];
+        if (w < wave) before += s;
+        all += s;
+    }
+    __syncthreads();
+    *total = all;
+    return before + incl - x;
+}
+
+__device__ __forceinline__ int32_t cnt_below(int64_t C, int64_t CT, int32_t N) {
+    if (C < 0) return 0;
+    if (CT == 0) return N - 1;
+    const int64_t j = ((C + 1) * N - 1) / CT;
+    return static_cast<int32_t>(min(j, static_cast<int64_t>(N - 1)));
+}
+
+__global__ __launch_bounds__(kSeqThreads) void policy_seq_kernel(PolicyArgs a) {
+    __shared__ int64_t scratch[kSeqThreads / kWave];
+    __shared__ uint32_t hist[256];
+    __shared__ uint32_t s_digit;
+    __shared__ int64_t s_above;
+    const int tid = threadIdx.x;
+    const int b = blockIdx.x;
+    const int y = blockIdx.y;
+    const int H = a.H;
+    const int64_t t0 = a.seq_offsets[b], t1 = a.seq_offsets[b + 1];
+    const bool bad = t0 < 0 || t1 < t0 || t1 > a.total_tokens || t1 - t0 > (int64_t(1) << 20);
+    const int64_t T = bad ? 0 : t1 - t0;
+    const int64_t chunk = (T + kSeqThreads - 1) / kSeqThreads;
+    const int64_t u_lo = min(T, tid * chunk), u_hi = min(T, u_lo + chunk);
+
+    if (y == H) {
+        // ---- segment boundaries
+        const int32_t N = a.N;
+        int32_t* so = a.seg_offsets + static_cast<int64_t>(b) * N;
+        if (bad && tid == 0) raise_err(a.err, SPICY_DEVERR_POLICY);
+        const int32_t base = bad ? 0 : static_cast<int32_t>(t0);
+        int64_t local = 0;
+        for (int64_t u = u_lo; u < u_hi; ++u) local += a.var[t0 + u];
+        int64_t CT;
+        int64_t C = block_exclusive_scan(local, &CT, scratch);
+        if (CT >= kRangeLimit / N) {
+            if (tid == 0) raise_err(a.err, SPICY_DEVERR_POLICY);
+            CT = 0;
+            C = 0;
+        }
+        if (tid == 0) {
+            so[0] = base;
+            a.seq_seg_ptr[b] = b * N;
+            if (b == a.B - 1) {
+                a.seq_seg_ptr[a.B] = a.B * N;
+                a.seg_offsets[static_cast<int64_t>(a.B) * N] = a.seq_offsets[a.B];
+            }
+        }
+        if (T == 0) {
+            for (int32_t j = 1 + tid; j < N; j += kSeqThreads) so[j] = base;
+            return;
+        }
+        for (int64_t u = u_lo; u < u_hi; ++u) {
+            const int32_t cp = u == 0 ? 0 : cnt_below(C, CT, N);
+            C += a.var[t0 + u];
+            const int32_t cc = cnt_below(C, CT, N);
+            for (int32_t j = cp + 1; j <= cc; ++j) so[j] = static_cast<int32_t>(t0 + u);
+        }
+        return;
+    }
+
+    // ---- landmarks of head y
+    const int h = y;
+    if (bad) return;                                   // reported by the boundary workgroup
+    const int64_t c_lo = min(static_cast<int64_t>(a.sink), T);
+    const int64_t c_hi = max(c_lo, T - a.recent);
+    const int64_t n_cand = c_hi - c_lo;
+    const int64_t Lsel = min(static_cast<int64_t>(a.L), n_cand);
+    uint64_t tau;
+    int64_t take_eq;                                   // ties of tau to take, lowest positions first
+    if (Lsel == n_cand) {
+        tau = 0;
+        take_eq = INT64_MAX;                           // every candidate
+    } else if (Lsel == 0) {
+        tau = UINT64_MAX;
+        take_eq = 0;                                   // none
+    } else {
+        uint64_t prefix = 0, pmask = 0;
+        int64_t k = Lsel;                              // rank of the wanted value from the top
+        for (int shift = 56; shift >= 0; shift -= 8) {
+            hist[tid] = 0;
+            __syncthreads();
+            for (int64_t u = c_lo + tid; u < c_hi; u += kSeqThreads) {
+                const uint64_t v = a.norm2[(t0 + u) * H + h];
+                if ((v & pmask) == prefix) atomicAdd(&hist[(v >> shift) & 255u], 1u);
+            }
+            __syncthreads();
+            // suffix sums over the bins, high digit first: thread i holds bin 255 - i
+            const int bin = 255 - tid;
+            const int64_t cntb = hist[bin];
+            int64_t dummy;
+            const int64_t above = block_exclusive_scan(cntb, &dummy, scratch);   // count in higher bins
+            if (above < k && above + cntb >= k) {
+                s_digit = static_cast<uint32_t>(bin);
+                s_above = above;
+            }
+            __syncthreads();
+            prefix |= static_cast<uint64_t>(s_digit) << shift;
+            pmask |= uint64_t(255) << shift;
+            k -= s_above;
+            __syncthreads();
+        }
+        tau = prefix;
+        take_eq = k;
+    }
+    // ties in position order: this thread's chunk of [0, T)
+    int64_t eq_local = 0;
+    for (int64_t u = u_lo; u < u_hi; ++u)
+        if (u >= c_lo && u < c_hi && a.norm2[(t0 + u) * H + h] == tau) ++eq_local;
+    int64_t dummy;
+    int64_t eq_rank = block_exclusive_scan(eq_local, &dummy, scratch);
+    for (int64_t u = u_lo; u < u_hi; ++u) {
+        uint8_t m = 1;
+        if (u >= c_lo && u < c_hi) {
+            const uint64_t v = a.norm2[(t0 + u) * H + h];
+            m = v > tau ? 1 : 0;
+            if (v == tau) {
+                m = eq_rank < take_eq ? 1 : 0;
+                ++eq_rank;
+            }
+        }
+        a.mask[(t0 + u) * H + h] = m;
+    }
+}
+
+template <int D, int CPL>
+spicy_status launch_token(const PolicyArgs& a, hipStream_t stream) {
+    const int64_t runs = (static_cast<int64_t>(a.total_tokens) + kRun - 1) / kRun;
+    const int64_t blocks = (runs + kTokWaves - 1) / kTokWaves;
+    const size_t lds = static_cast<size_t>(kTokWaves) * 2 * a.H * D * sizeof(int32_t);
+    hipLaunchKernelGGL((policy_token_kernel<D, CPL>), dim3(static_cast<unsigned>(blocks)), dim3(kTokWaves * kWave),
+                       lds, stream, a);
+    return hipGetLastError() == hipSuccess ? SPICY_OK : SPICY_ERR_HIP;
+}
+
+}  // namespace
+
+spicy_status launch_policy(const PolicyArgs& a, hipStream_t stream) {
+    if (a.B == 0) return SPICY_OK;
+    if (a.total_tokens > 0) {
+        const int chunks = a.H * a.d / 8;
+        const int cpl = (chunks + kWave - 1) / kWave;
+        spicy_status st;
+        if (a.d == 128) {
+            st = cpl == 1 ? launch_token<128, 1>(a, stream) : cpl == 2 ? launch_token<128, 2>(a, stream)
+                                                                      : launch_token<128, 4>(a, stream);
+        } else {
+            st = cpl == 1 ? launch_token<64, 1>(a, stream) : launch_token<64, 2>(a, stream);
+        }
+        if (st != SPICY_OK) return st;
+    }
+    hipLaunchKernelGGL(policy_seq_kernel, dim3(static_cast<unsigned>(a.B), static_cast<unsigned>(a.H + 1)),
+                       dim3(kSeqThreads), 0, stream, a);
+    return hipGetLastError() == hipSuccess ? SPICY_OK : SPICY_ERR_HIP;
+}
+
+}  // namespace spicy

@@ -132,6 +132,22 @@ struct CacheArgs {
     int32_t H;      // KV heads
 };
 
+// spicy_policy: per-step segments and protection mask from the chunk itself.
+struct PolicyArgs {
+    const uint16_t* k;           // [total_tokens][H][d] bf16 keys (pre-RoPE)
+    const uint16_t* v;           // [total_tokens][H][d] bf16 values
+    const int32_t* seq_offsets;  // [B+1]
+    const int32_t* proj_ptr;     // [R+1]  row r of P: proj_idx[proj_ptr[r] .. proj_ptr[r+1])
+    const int32_t* proj_idx;     // [nnz]  +(c+1) / -(c+1): +-1 at column c of [k_t; v_t]
+    int32_t* seg_offsets;        // [B*N + 1] out
+    int32_t* seq_seg_ptr;        // [B+1]     out
+    uint8_t* mask;               // [total_tokens][H] out
+    int64_t* var;                // [total_tokens]    workspace: d_t
+    uint64_t* norm2;             // [total_tokens][H] workspace: squared fixed-point key norms
+    int32_t* err;
+    int32_t total_tokens, B, H, d, R, nnz, N, L, sink, recent;
+};
+
 struct CoarsenArgs {
     CacheArgs cache;
     const void* k_pre;

@@ -86,6 +86,10 @@ typedef enum { SPICY_F32 = 0, SPICY_BF16 = 1 } spicy_dtype;
 #define SPICY_DEVERR_SEGMENTS    0x4  /* segment/sequence offsets inconsistent   */
 #define SPICY_DEVERR_LENGTH      0x8  /* a length < 0                            */
 #define SPICY_DEVERR_SHARED      0x10 /* declared shared prefix pages differ      */
+#define SPICY_DEVERR_POLICY      0x20 /* spicy_policy: projection entry outside
+                                          [k_t; v_t], bad row pointers, a sequence
+                                          longer than 2^20 tokens or one whose
+                                          total variation times N reaches 2^62   */
 
 #define SPICY_PAGE_SIZE 16
 #define SPICY_WORKSPACE_HEADER 256   /* bytes before any per-call scratch     */
@@ -240,6 +244,64 @@ spicy_status spicy_decode_attn_shared(const spicy_cache* cache,   /* host struct
 
 /* Human-readable name of a status code (static string). */
 const char* spicy_status_string(spicy_status s);
+
+/* ------------------------------------------------------------------------
+ * Per-step policy: the segment partition and the protection mask of a chunk,
+ * from the chunk itself, for a following spicy_coarsen call.
+ *
+ * Equal-Variation KV Cache page, "Mathematical statement" (breakpoints at
+ * equal increments of cumulative variation, first hitting time) and
+ * "Implementation notes" (feature z_t = P [k_t; v_t] with a fixed random
+ * projection P, local variation d_t = ||z_t - z_{t-1}||_2, thresholds
+ * q_j = j c_T / N, a boundary at the first token whose cumulative variation
+ * reaches the next threshold).  SPICY-KV demo page, Claim 2 (exact
+ * C-points) and section 1 (sink and recent tokens kept exact); the landmark
+ * rule is the largest key norms per (sequence, KV head).
+ *
+ * Arithmetic (integer, so the result is exact whatever the order):
+ *   fix(x) = x * 2^16 rounded half to even, clamped to [-2^28, 2^28],
+ *            NaN -> 0, for each bf16 element x of k_t and v_t;
+ *   z_t[r] = sum over row r of P of (+-1) * fix(x_t[c]), with
+ *            x_t = [k_t; v_t], each in [H_kv][head_dim] order, so columns
+ *            [0, H d) are keys and [H d, 2 H d) values;
+ *   d_t    = floor(sqrt(sum_r (z_t[r] - z_{t-1}[r])^2)), 0 at a sequence's
+ *            first token;  C_t = d_0 + ... + d_t;
+ *   b_j    = min{t : C_t >= floor(j C_T / N)}, j = 1 .. N-1, b_0 = 0,
+ *            b_N = T: sequence b gets exactly N segment slots
+ *            [b_j, b_{j+1}), empty ones included (spicy_coarsen gives an empty
+ *            segment no entry);
+ *   mask   = 1 for the first `sink` and the last `recent` tokens of each
+ *            sequence, and for the n_landmarks largest
+ *            sum_i fix(k_t,h[i])^2 among the others, per KV head h, ties to
+ *            the lower position.
+ *
+ * P is given as signed column lists: row r (r < proj_rows <= 16) has the
+ * entries proj_idx[proj_ptr[r] .. proj_ptr[r+1]), value c + 1 for +1 at
+ * column c and -(c + 1) for -1; proj_idx has proj_nnz entries.  All device.
+ *
+ * Inputs (device): k_pre, v [total_tokens][H_kv][head_dim] bf16;
+ *   seq_offsets [B+1] (sequence b = tokens [seq_offsets[b], seq_offsets[b+1])).
+ * Outputs (device, caller-allocated): seg_offsets [B * n_segments + 1] (global
+ *   token indices), seq_seg_ptr [B+1] = b * n_segments, protected_mask
+ *   [total_tokens][H_kv] (1 = keep exact), ready to be passed to spicy_coarsen
+ *   with n_seg = B * n_segments.  B = 0 writes nothing.
+ * Workspace: device, >= spicy_policy_workspace_bytes(total_tokens, H_kv),
+ *   first int32 = sticky device error word (SPICY_DEVERR_POLICY).
+ * Errors: SPICY_ERR_ARG (null pointer, negative count, n_segments < 1,
+ *   proj_rows outside [1, 16], B * n_segments + 1 > INT32_MAX),
+ *   SPICY_ERR_UNSUPPORTED (dtype not bf16, head_dim not 64/128, H_kv outside
+ *   [1, 16]), SPICY_ERR_CAPACITY (workspace too small), SPICY_ERR_HIP.
+ * ------------------------------------------------------------------------ */
+size_t spicy_policy_workspace_bytes(int32_t total_tokens, int32_t num_kv_heads);
+
+spicy_status spicy_policy(const void* k_pre, const void* v, int32_t total_tokens,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                          const int32_t* seq_offsets, int32_t B,
+                          const int32_t* proj_ptr, const int32_t* proj_idx, int32_t proj_rows,
+                          int32_t proj_nnz, int32_t n_segments, int32_t n_landmarks,
+                          int32_t sink, int32_t recent,
+                          int32_t* seg_offsets, int32_t* seq_seg_ptr, uint8_t* protected_mask,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -31,7 +31,8 @@ def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert {"spicy_coarsen", "spicy_decode_attn", "spicy_coarsen_workspace_bytes",
             "spicy_decode_workspace_bytes", "spicy_decode_num_splits", "spicy_status_string",
-            "spicy_decode_attn_shared", "spicy_decode_shared_workspace_bytes"} <= set(names)
+            "spicy_decode_attn_shared", "spicy_decode_shared_workspace_bytes",
+            "spicy_policy", "spicy_policy_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -149,6 +150,36 @@ def test_coarsen_rejects_bad_arguments(lib):
     assert call(maxp=0) == 1
     assert call(maxp=(1 << 23) + 1) == 4   # entry ids would not fit a C-point item
     assert call(cache=_cache(pages=0)) == 2
+    assert call(wsb=100) == 3
+    assert call(B=0) == 0
+
+
+def test_policy_workspace_and_bad_arguments(lib):
+    # header, then int64 d_t per token and uint64 key norms per (token, head)
+    assert lib.spicy_policy_workspace_bytes(1000, 4) == 256 + 8192 + 32000
+    assert lib.spicy_policy_workspace_bytes(-1, 4) == 0
+    P = 0x1000
+
+    def call(k=P, v=P, total=100, H=4, d=128, dtype=1, so=P, B=2, pp=P, pi=P, R=16, nnz=40, N=5, L=3, sink=0,
+             recent=0, seg=P, ssp=P, mask=P, ws=P, wsb=1 << 30):
+        return lib.spicy_policy(k, v, total, H, d, dtype, so, B, pp, pi, R, nnz, N, L, sink, recent, seg, ssp,
+                                mask, ws, wsb, None)
+
+    assert call(k=0) == 1
+    assert call(mask=0) == 1
+    assert call(pi=0) == 1
+    assert call(N=0) == 1
+    assert call(R=0) == 1
+    assert call(R=17) == 1
+    assert call(L=-1) == 1
+    assert call(sink=-1) == 1
+    assert call(B=-1) == 1
+    assert call(total=-5) == 1
+    assert call(B=1 << 20, N=1 << 12) == 1  # B * N + 1 overflows int32
+    assert call(dtype=0) == 4               # fp32 inputs: not supported by the policy
+    assert call(dtype=7) == 1
+    assert call(d=96) == 4
+    assert call(H=17) == 4
     assert call(wsb=100) == 3
     assert call(B=0) == 0
 
