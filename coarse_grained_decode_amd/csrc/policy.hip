@@ -51,6 +51,7 @@ constexpr int kRing = 4;             // token rows in flight per wavefront
 constexpr int kMaxEnt = 16;          // projection entries a lane keeps in registers
 constexpr int kTokWaves = 4;         // wavefronts per token workgroup
 constexpr int kSeqThreads = 256;
+constexpr int kPerThread = 32;       // candidates a select thread keeps in registers
 constexpr int64_t kRangeLimit = int64_t(1) << 62;
 
 __device__ __forceinline__ int32_t fix16(uint32_t bf16_bits) {
@@ -97,6 +98,51 @@ struct TokRow {
     uint4 k[CPL], v[CPL];
 };
 
+// DPP moves (within rows of 16 lanes); 64-bit values move as two halves.
+constexpr int kQuadXor1 = 0xB1;       // quad_perm(1, 0, 3, 2)
+constexpr int kQuadXor2 = 0x4E;       // quad_perm(2, 3, 0, 1)
+constexpr int kRowRor4 = 0x124;
+constexpr int kRowRor8 = 0x128;
+constexpr int kHalfMirror = 0x141;    // lane i <-> 7 - i within each half row
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t x) {
+    const uint32_t lo = static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(x & 0xFFFFFFFFu), CTRL, 0xF, 0xF, false));
+    const uint32_t hi = static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(x >> 32), CTRL, 0xF, 0xF, false));
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+    return __builtin_bit_cast(double, dpp_u64<CTRL>(__builtin_bit_cast(uint64_t, x)));
+}
+
+// Sum over aligned groups of 16 lanes (D = 128: one head) or 8 lanes (D = 64).
+template <int G>
+__device__ __forceinline__ uint64_t group_sum_u64(uint64_t v) {
+    if constexpr (G == 16) {
+        v += dpp_u64<kRowRor8>(v);
+        v += dpp_u64<kRowRor4>(v);
+    } else {
+        v += dpp_u64<kHalfMirror>(v);
+    }
+    v += dpp_u64<kQuadXor2>(v);
+    v += dpp_u64<kQuadXor1>(v);
+    return v;
+}
+
+// floor(sqrt(s)) for s < 2^62, from the reciprocal square root estimate.
+__device__ __forceinline__ uint64_t isqrt_u64(uint64_t s) {
+    if (s == 0) return 0;
+    const double e = static_cast<double>(s);
+    uint64_t r = static_cast<uint64_t>(e * __builtin_amdgcn_rsq(e));
+    while (r * r > s) --r;
+    while ((r + 1) * (r + 1) <= s) ++r;
+    return r;
+}
+
 template <int D, int CPL>
 __global__ __launch_bounds__(kTokWaves * kWave) void policy_token_kernel(PolicyArgs a) {
     extern __shared__ int32_t lds[];
@@ -105,13 +151,15 @@ __global__ __launch_bounds__(kTokWaves * kWave) void policy_token_kernel(PolicyA
     const int H = a.H;
     const int W = H * D;                 // elements of k_t (and of v_t)
     const int nch = W / 8;               // 16-byte chunks of one row
-    int32_t* xs = lds + static_cast<int64_t>(wave) * 2 * W;
+    int32_t* xs = lds + static_cast<int64_t>(wave) * (2 * W + 4);   // + a zero slot at 2W
     const int64_t run = static_cast<int64_t>(blockIdx.x) * kTokWaves + wave;
     const int64_t t_begin = run * kRun;
     if (t_begin >= a.total_tokens) return;
     const int64_t t_end = min(t_begin + kRun, static_cast<int64_t>(a.total_tokens));
+    if (lane == 0) xs[2 * W] = 0;
 
     // this lane's projection entries: row r = lane / 4, entries q, q + 4, ...
+    // kept as (LDS index, sign); missing or invalid entries read the zero slot
     const int r = lane / 4, q = lane % 4;
     int32_t e0 = 0, n_own = 0;
     if (r < a.R) {
@@ -124,9 +172,18 @@ __global__ __launch_bounds__(kTokWaves * kWave) void policy_token_kernel(PolicyA
             n_own = max(0, (e1 - e0 - q + 3) / 4);
         }
     }
-    int32_t ent[kMaxEnt];
+    int32_t goff[kMaxEnt];
+    double gsgn[kMaxEnt];
 #pragma unroll
-    for (int i = 0; i < kMaxEnt; ++i) ent[i] = i < n_own ? checked_entry(a, a.proj_idx[e0 + q + 4 * i], 2 * W) : 0;
+    for (int i = 0; i < kMaxEnt; ++i) {
+        const int32_t e = i < n_own ? checked_entry(a, a.proj_idx[e0 + q + 4 * i], 2 * W) : 0;
+        goff[i] = e == 0 ? 2 * W : (e > 0 ? e - 1 : -e - 1);
+        gsgn[i] = e < 0 ? -1.0 : 1.0;
+    }
+    int32_t nmax = n_own;                // entries the wavefront loops over (uniform)
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) nmax = max(nmax, __shfl_xor(nmax, o));
+    nmax = __builtin_amdgcn_readfirstlane(nmax);
 
     // the sequence holding t_begin: the largest b with seq_offsets[b] <= t_begin
     int32_t lo = 0, hi = a.B;
@@ -152,7 +209,7 @@ __global__ __launch_bounds__(kTokWaves * kWave) void policy_token_kernel(PolicyA
         }
     };
 
-    int64_t zprev = 0;
+    double zprev = 0.0;
     auto process = [&](const TokRow<CPL>& x, int64_t t) {
         while (b < a.B && t >= next_start) {          // sequences are contiguous: step to t's
             ++b;
@@ -169,55 +226,69 @@ __global__ __launch_bounds__(kTokWaves * kWave) void policy_token_kernel(PolicyA
             if (c < nch) {
                 const uint32_t kw[4] = {x.k[j].x, x.k[j].y, x.k[j].z, x.k[j].w};
                 const uint32_t vw[4] = {x.v[j].x, x.v[j].y, x.v[j].z, x.v[j].w};
+                int32_t xk[8], xv[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const uint32_t kb = (e & 1) ? (kw[e / 2] >> 16) : (kw[e / 2] & 0xFFFFu);
-                    const uint32_t vb = (e & 1) ? (vw[e / 2] >> 16) : (vw[e / 2] & 0xFFFFu);
-                    const int32_t xk = fix16(kb);
-                    xs[8 * c + e] = xk;
-                    xs[W + 8 * c + e] = fix16(vb);
-                    n2 += static_cast<uint64_t>(static_cast<int64_t>(xk) * xk);
+                    xk[e] = fix16((e & 1) ? (kw[e / 2] >> 16) : (kw[e / 2] & 0xFFFFu));
+                    xv[e] = fix16((e & 1) ? (vw[e / 2] >> 16) : (vw[e / 2] & 0xFFFFu));
+                    n2 += static_cast<uint64_t>(static_cast<int64_t>(xk[e]) * xk[e]);
                 }
+                *reinterpret_cast<int4*>(xs + 8 * c) = make_int4(xk[0], xk[1], xk[2], xk[3]);
+                *reinterpret_cast<int4*>(xs + 8 * c + 4) = make_int4(xk[4], xk[5], xk[6], xk[7]);
+                *reinterpret_cast<int4*>(xs + W + 8 * c) = make_int4(xv[0], xv[1], xv[2], xv[3]);
+                *reinterpret_cast<int4*>(xs + W + 8 * c + 4) = make_int4(xv[4], xv[5], xv[6], xv[7]);
             }
-            // lanes of one head are D/8 consecutive chunks
-#pragma unroll
-            for (int o = 1; o < D / 8; o <<= 1) n2 += shfl_xor_u64(n2, o);
+            n2 = group_sum_u64<D / 8>(n2);              // lanes of one head: D/8 consecutive chunks
             if (out && c < nch && (c % (D / 8)) == 0) a.norm2[t * H + (8 * c) / D] = n2;
         }
         __builtin_amdgcn_wave_barrier();
-        // projection row r: this lane's entries, then the other three lanes'
-        int64_t acc = 0;
+        // projection row r: this lane's entries (exact in double: every
+        // partial sum is an integer below 2^53), then the quad's sum
+        double acc = 0.0;
 #pragma unroll
-        for (int i = 0; i < kMaxEnt; ++i) {
-            const int32_t e = ent[i];
-            if (e != 0) {
-                const int32_t v = xs[e > 0 ? e - 1 : -e - 1];
-                acc += e > 0 ? v : -v;
+        for (int i = 0; i < kMaxEnt; ++i)
+            if (i < nmax) acc = fma(gsgn[i], static_cast<double>(xs[goff[i]]), acc);
+        for (int32_t i = kMaxEnt; i < nmax; ++i) {
+            if (i < n_own) {
+                const int32_t e = checked_entry(a, a.proj_idx[e0 + q + 4 * i], 2 * W);
+                const double v = static_cast<double>(xs[e == 0 ? 2 * W : (e > 0 ? e - 1 : -e - 1)]);
+                acc += e < 0 ? -v : v;
             }
         }
-        for (int32_t i = kMaxEnt; i < n_own; ++i) {
-            const int32_t e = checked_entry(a, a.proj_idx[e0 + q + 4 * i], 2 * W);
-            if (e != 0) {
-                const int32_t v = xs[e > 0 ? e - 1 : -e - 1];
-                acc += e > 0 ? v : -v;
-            }
-        }
-        acc += static_cast<int64_t>(shfl_xor_u64(static_cast<uint64_t>(acc), 1));
-        acc += static_cast<int64_t>(shfl_xor_u64(static_cast<uint64_t>(acc), 2));
-        const int64_t z = r < a.R ? acc : 0;
-        const int64_t dz = z - zprev;
+        acc += dpp_f64<kQuadXor1>(acc);
+        acc += dpp_f64<kQuadXor2>(acc);
+        const double z = r < a.R ? acc : 0.0;
+        const double dzd = z - zprev;
         zprev = z;
-        const uint64_t adz = static_cast<uint64_t>(dz < 0 ? -dz : dz);
-        unsigned __int128 sq = (q == 0) ? static_cast<unsigned __int128>(adz) * adz : 0;
-        uint64_t sl = static_cast<uint64_t>(sq), sh = static_cast<uint64_t>(sq >> 64);
+        const uint64_t adz = static_cast<uint64_t>(dzd < 0.0 ? -dzd : dzd);
+        uint64_t d;
+        if (!__any(adz >= (uint64_t(1) << 29))) {
+            // every |dz| < 2^29: the 16 squares sum below 2^62 in 64 bits
+            const uint32_t a32 = static_cast<uint32_t>(adz);
+            uint64_t sq = q == 0 ? static_cast<uint64_t>(a32) * a32 : 0;
+            sq = group_sum_u64<16>(sq);
+            // row totals sit in lanes 0, 16, 32, 48 (words read as uint32: no sign extension)
+            uint64_t tot = 0;
 #pragma unroll
-        for (int o = 4; o < kWave; o <<= 1) {
-            const uint64_t ol = shfl_xor_u64(sl, o), oh = shfl_xor_u64(sh, o);
-            const uint64_t nl = sl + ol;
-            sh = sh + oh + (nl < sl ? 1 : 0);
-            sl = nl;
+            for (int rr = 0; rr < kWave / 16; ++rr) {
+                const uint32_t lo32 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(sq), 16 * rr));
+                const uint32_t hi32 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(sq >> 32), 16 * rr));
+                tot += (static_cast<uint64_t>(hi32) << 32) | lo32;
+            }
+            d = isqrt_u64(tot);
+        } else {
+            unsigned __int128 sq = (q == 0) ? static_cast<unsigned __int128>(adz) * adz : 0;
+            uint64_t sl = static_cast<uint64_t>(sq), sh = static_cast<uint64_t>(sq >> 64);
+#pragma unroll
+            for (int o = 4; o < kWave; o <<= 1) {
+                const uint64_t ol = shfl_xor_u64(sl, o), oh = shfl_xor_u64(sh, o);
+                const uint64_t nl = sl + ol;
+                sh = sh + oh + (nl < sl ? 1 : 0);
+                sl = nl;
+            }
+            d = isqrt_u128((static_cast<unsigned __int128>(sh) << 64) | sl);
         }
-        const uint64_t d = first ? 0 : isqrt_u128((static_cast<unsigned __int128>(sh) << 64) | sl);
+        if (first) d = 0;
         if (out && lane == 0) a.var[t] = static_cast<int64_t>(d);
         __builtin_amdgcn_wave_barrier();
     };
@@ -333,12 +404,39 @@ __global__ __launch_bounds__(kSeqThreads) void policy_seq_kernel(PolicyArgs a) {
     } else {
         uint64_t prefix = 0, pmask = 0;
         int64_t k = Lsel;                              // rank of the wanted value from the top
+        // candidates c_lo + tid + 256 m stay in registers when they fit
+        const bool in_regs = n_cand <= static_cast<int64_t>(kSeqThreads) * kPerThread;
+        uint64_t vals[kPerThread];
+#pragma unroll
+        for (int m = 0; m < kPerThread; ++m) {
+            const int64_t u = c_lo + tid + static_cast<int64_t>(kSeqThreads) * m;
+            vals[m] = (in_regs && u < c_hi) ? a.norm2[(t0 + u) * H + h] : 0;
+        }
         for (int shift = 56; shift >= 0; shift -= 8) {
             hist[tid] = 0;
             __syncthreads();
-            for (int64_t u = c_lo + tid; u < c_hi; u += kSeqThreads) {
-                const uint64_t v = a.norm2[(t0 + u) * H + h];
-                if ((v & pmask) == prefix) atomicAdd(&hist[(v >> shift) & 255u], 1u);
+            if (in_regs) {
+#pragma unroll
+                for (int m = 0; m < kPerThread; ++m) {
+                    const int64_t u = c_lo + tid + static_cast<int64_t>(kSeqThreads) * m;
+                    const uint64_t v = vals[m];
+                    const bool hit = u < c_hi && (v & pmask) == prefix;
+                    const uint32_t dg = static_cast<uint32_t>(v >> shift) & 255u;
+                    // one atomic per wavefront when all its hits share the digit
+                    const uint32_t d0 = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(dg)));
+                    if (__all(!hit || dg == d0)) {
+                        const uint64_t hits = __ballot(hit);
+                        if ((threadIdx.x % kWave) == 0 && hits)
+                            atomicAdd(&hist[d0], static_cast<uint32_t>(__popcll(hits)));
+                    } else if (hit) {
+                        atomicAdd(&hist[dg], 1u);
+                    }
+                }
+            } else {
+                for (int64_t u = c_lo + tid; u < c_hi; u += kSeqThreads) {
+                    const uint64_t v = a.norm2[(t0 + u) * H + h];
+                    if ((v & pmask) == prefix) atomicAdd(&hist[(v >> shift) & 255u], 1u);
+                }
             }
             __syncthreads();
             // suffix sums over the bins, high digit first: thread i holds bin 255 - i
@@ -383,7 +481,7 @@ template <int D, int CPL>
 spicy_status launch_token(const PolicyArgs& a, hipStream_t stream) {
     const int64_t runs = (static_cast<int64_t>(a.total_tokens) + kRun - 1) / kRun;
     const int64_t blocks = (runs + kTokWaves - 1) / kTokWaves;
-    const size_t lds = static_cast<size_t>(kTokWaves) * 2 * a.H * D * sizeof(int32_t);
+    const size_t lds = static_cast<size_t>(kTokWaves) * (2 * a.H * D + 4) * sizeof(int32_t);
     hipLaunchKernelGGL((policy_token_kernel<D, CPL>), dim3(static_cast<unsigned>(blocks)), dim3(kTokWaves * kWave),
                        lds, stream, a);
     return hipGetLastError() == hipSuccess ? SPICY_OK : SPICY_ERR_HIP;
