@@ -50,8 +50,8 @@ constexpr int kRun = 32;             // tokens per wavefront
 constexpr int kRing = 4;             // token rows in flight per wavefront
 constexpr int kMaxEnt = 16;          // projection entries a lane keeps in registers
 constexpr int kTokWaves = 4;         // wavefronts per token workgroup
-constexpr int kSeqThreads = 256;
-constexpr int kPerThread = 32;       // candidates a select thread keeps in registers
+constexpr int kSeqThreads = 512;
+constexpr int kPer = 16;             // tokens (or candidates) a sequence-kernel thread holds
 constexpr int64_t kRangeLimit = int64_t(1) << 62;
 
 __device__ __forceinline__ int32_t fix16(uint32_t bf16_bits) {
@@ -328,11 +328,19 @@ __device__ __forceinline__ int64_t block_exclusive_scan(int64_t x, int64_t* tota
     return before + incl - x;
 }
 
-__device__ __forceinline__ int32_t cnt_below(int64_t C, int64_t CT, int32_t N) {
+// cnt(C) = #{j in [1, N-1] : floor(j CT / N) <= C} = clamp(floor(((C+1) N - 1) / CT), 0, N - 1).
+// The quotient comes from an fp64 estimate (off by at most one: the operands
+// are below 2^63 and the quotient below 2N) corrected with exact products.
+__device__ __forceinline__ int32_t cnt_below(int64_t C, int64_t CT, int32_t N, double inv_ct) {
     if (C < 0) return 0;
     if (CT == 0) return N - 1;
-    const int64_t j = ((C + 1) * N - 1) / CT;
-    return static_cast<int32_t>(min(j, static_cast<int64_t>(N - 1)));
+    const uint64_t num = static_cast<uint64_t>(C + 1) * static_cast<uint64_t>(N) - 1;
+    const uint64_t ct = static_cast<uint64_t>(CT);
+    uint64_t j = static_cast<uint64_t>(static_cast<double>(num) * inv_ct);
+    j = min(j, static_cast<uint64_t>(2) * static_cast<uint64_t>(N));
+    while (j > 0 && j * ct > num) --j;
+    while ((j + 1) * ct <= num) ++j;
+    return static_cast<int32_t>(min(j, static_cast<uint64_t>(N - 1)));
 }
 
 __global__ __launch_bounds__(kSeqThreads) void policy_seq_kernel(PolicyArgs a) {
@@ -340,6 +348,7 @@ __global__ __launch_bounds__(kSeqThreads) void policy_seq_kernel(PolicyArgs a) {
     __shared__ uint32_t hist[256];
     __shared__ uint32_t s_digit;
     __shared__ int64_t s_above;
+    constexpr int64_t kRound = static_cast<int64_t>(kSeqThreads) * kPer;   // tokens per round
     const int tid = threadIdx.x;
     const int b = blockIdx.x;
     const int y = blockIdx.y;
@@ -347,24 +356,14 @@ __global__ __launch_bounds__(kSeqThreads) void policy_seq_kernel(PolicyArgs a) {
     const int64_t t0 = a.seq_offsets[b], t1 = a.seq_offsets[b + 1];
     const bool bad = t0 < 0 || t1 < t0 || t1 > a.total_tokens || t1 - t0 > (int64_t(1) << 20);
     const int64_t T = bad ? 0 : t1 - t0;
-    const int64_t chunk = (T + kSeqThreads - 1) / kSeqThreads;
-    const int64_t u_lo = min(T, tid * chunk), u_hi = min(T, u_lo + chunk);
 
     if (y == H) {
-        // ---- segment boundaries
+        // ---- segment boundaries.  Round r covers tokens [r kRound, (r+1) kRound);
+        // thread tid owns the kPer consecutive tokens starting at tid * kPer.
         const int32_t N = a.N;
         int32_t* so = a.seg_offsets + static_cast<int64_t>(b) * N;
         if (bad && tid == 0) raise_err(a.err, SPICY_DEVERR_POLICY);
         const int32_t base = bad ? 0 : static_cast<int32_t>(t0);
-        int64_t local = 0;
-        for (int64_t u = u_lo; u < u_hi; ++u) local += a.var[t0 + u];
-        int64_t CT;
-        int64_t C = block_exclusive_scan(local, &CT, scratch);
-        if (CT >= kRangeLimit / N) {
-            if (tid == 0) raise_err(a.err, SPICY_DEVERR_POLICY);
-            CT = 0;
-            C = 0;
-        }
         if (tid == 0) {
             so[0] = base;
             a.seq_seg_ptr[b] = b * N;
@@ -377,11 +376,50 @@ __global__ __launch_bounds__(kSeqThreads) void policy_seq_kernel(PolicyArgs a) {
             for (int32_t j = 1 + tid; j < N; j += kSeqThreads) so[j] = base;
             return;
         }
-        for (int64_t u = u_lo; u < u_hi; ++u) {
-            const int32_t cp = u == 0 ? 0 : cnt_below(C, CT, N);
-            C += a.var[t0 + u];
-            const int32_t cc = cnt_below(C, CT, N);
-            for (int32_t j = cp + 1; j <= cc; ++j) so[j] = static_cast<int32_t>(t0 + u);
+        int64_t dv[kPer];
+        auto load_round = [&](int64_t r0) {
+#pragma unroll
+            for (int m = 0; m < kPer; ++m) {
+                const int64_t u = r0 + static_cast<int64_t>(tid) * kPer + m;
+                dv[m] = u < T ? a.var[t0 + u] : 0;
+            }
+        };
+        // total variation
+        int64_t CT = 0;
+        for (int64_t r0 = 0; r0 < T; r0 += kRound) {
+            load_round(r0);
+            int64_t local = 0;
+#pragma unroll
+            for (int m = 0; m < kPer; ++m) local += dv[m];
+            int64_t tot;
+            block_exclusive_scan(local, &tot, scratch);
+            CT += tot;
+        }
+        if (CT >= kRangeLimit / N) {
+            if (tid == 0) raise_err(a.err, SPICY_DEVERR_POLICY);
+            CT = 0;
+        }
+        const double inv_ct = CT > 0 ? 1.0 / static_cast<double>(CT) : 0.0;
+        // boundaries: token t is b_j for every j in (cnt(C_{t-1}), cnt(C_t)]
+        int64_t carry = 0;
+        for (int64_t r0 = 0; r0 < T; r0 += kRound) {
+            if (r0 != 0 || T > kRound) load_round(r0);
+            int64_t local = 0;
+#pragma unroll
+            for (int m = 0; m < kPer; ++m) local += dv[m];
+            int64_t tot;
+            int64_t C = carry + block_exclusive_scan(local, &tot, scratch);
+            carry += tot;
+#pragma unroll
+            for (int m = 0; m < kPer; ++m) {
+                const int64_t u = r0 + static_cast<int64_t>(tid) * kPer + m;
+                if (u < T) {
+                    const int32_t cp = u == 0 ? 0 : cnt_below(C, CT, N, inv_ct);
+                    C += dv[m];
+                    const int32_t cc = cnt_below(C, CT, N, inv_ct);
+                    for (int32_t j = cp + 1; j <= cc; ++j) so[j] = static_cast<int32_t>(t0 + u);
+                }
+            }
         }
         return;
     }
@@ -404,20 +442,20 @@ __global__ __launch_bounds__(kSeqThreads) void policy_seq_kernel(PolicyArgs a) {
     } else {
         uint64_t prefix = 0, pmask = 0;
         int64_t k = Lsel;                              // rank of the wanted value from the top
-        // candidates c_lo + tid + 256 m stay in registers when they fit
-        const bool in_regs = n_cand <= static_cast<int64_t>(kSeqThreads) * kPerThread;
-        uint64_t vals[kPerThread];
+        // candidates c_lo + tid + kSeqThreads m stay in registers when they fit
+        const bool in_regs = n_cand <= kRound;
+        uint64_t vals[kPer];
 #pragma unroll
-        for (int m = 0; m < kPerThread; ++m) {
+        for (int m = 0; m < kPer; ++m) {
             const int64_t u = c_lo + tid + static_cast<int64_t>(kSeqThreads) * m;
             vals[m] = (in_regs && u < c_hi) ? a.norm2[(t0 + u) * H + h] : 0;
         }
         for (int shift = 56; shift >= 0; shift -= 8) {
-            hist[tid] = 0;
+            if (tid < 256) hist[tid] = 0;
             __syncthreads();
             if (in_regs) {
 #pragma unroll
-                for (int m = 0; m < kPerThread; ++m) {
+                for (int m = 0; m < kPer; ++m) {
                     const int64_t u = c_lo + tid + static_cast<int64_t>(kSeqThreads) * m;
                     const uint64_t v = vals[m];
                     const bool hit = u < c_hi && (v & pmask) == prefix;
@@ -439,12 +477,12 @@ __global__ __launch_bounds__(kSeqThreads) void policy_seq_kernel(PolicyArgs a) {
                 }
             }
             __syncthreads();
-            // suffix sums over the bins, high digit first: thread i holds bin 255 - i
+            // counts above each bin, high digit first: thread i < 256 holds bin 255 - i
             const int bin = 255 - tid;
-            const int64_t cntb = hist[bin];
+            const int64_t cntb = tid < 256 ? hist[bin] : 0;
             int64_t dummy;
-            const int64_t above = block_exclusive_scan(cntb, &dummy, scratch);   // count in higher bins
-            if (above < k && above + cntb >= k) {
+            const int64_t above = block_exclusive_scan(cntb, &dummy, scratch);
+            if (tid < 256 && above < k && above + cntb >= k) {
                 s_digit = static_cast<uint32_t>(bin);
                 s_above = above;
             }
@@ -457,23 +495,40 @@ __global__ __launch_bounds__(kSeqThreads) void policy_seq_kernel(PolicyArgs a) {
         tau = prefix;
         take_eq = k;
     }
-    // ties in position order: this thread's chunk of [0, T)
-    int64_t eq_local = 0;
-    for (int64_t u = u_lo; u < u_hi; ++u)
-        if (u >= c_lo && u < c_hi && a.norm2[(t0 + u) * H + h] == tau) ++eq_local;
-    int64_t dummy;
-    int64_t eq_rank = block_exclusive_scan(eq_local, &dummy, scratch);
-    for (int64_t u = u_lo; u < u_hi; ++u) {
-        uint8_t m = 1;
-        if (u >= c_lo && u < c_hi) {
-            const uint64_t v = a.norm2[(t0 + u) * H + h];
-            m = v > tau ? 1 : 0;
-            if (v == tau) {
-                m = eq_rank < take_eq ? 1 : 0;
-                ++eq_rank;
+    // the mask, in rounds: thread tid owns kPer consecutive positions; ties of
+    // tau are ranked in position order by a block scan with a running carry
+    int64_t eq_carry = 0;
+    for (int64_t r0 = 0; r0 < T; r0 += kRound) {
+        uint64_t nv[kPer];
+#pragma unroll
+        for (int m = 0; m < kPer; ++m) {
+            const int64_t u = r0 + static_cast<int64_t>(tid) * kPer + m;
+            nv[m] = (u >= c_lo && u < c_hi) ? a.norm2[(t0 + u) * H + h] : 0;
+        }
+        int64_t eq_local = 0;
+#pragma unroll
+        for (int m = 0; m < kPer; ++m) {
+            const int64_t u = r0 + static_cast<int64_t>(tid) * kPer + m;
+            eq_local += (u >= c_lo && u < c_hi && nv[m] == tau) ? 1 : 0;
+        }
+        int64_t eq_tot;
+        int64_t eq_rank = eq_carry + block_exclusive_scan(eq_local, &eq_tot, scratch);
+        eq_carry += eq_tot;
+#pragma unroll
+        for (int m = 0; m < kPer; ++m) {
+            const int64_t u = r0 + static_cast<int64_t>(tid) * kPer + m;
+            if (u < T) {
+                uint8_t mk = 1;
+                if (u >= c_lo && u < c_hi) {
+                    mk = nv[m] > tau ? 1 : 0;
+                    if (nv[m] == tau) {
+                        mk = eq_rank < take_eq ? 1 : 0;
+                        ++eq_rank;
+                    }
+                }
+                a.mask[(t0 + u) * H + h] = mk;
             }
         }
-        a.mask[(t0 + u) * H + h] = m;
     }
 }
 
