@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 512 MiB device copy (torch.neg, fp32) 5 times: the known-size "
                          "reference that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes")
+    ap.add_argument("--device-policy", action="store_true",
+                    help="every step also runs spicy_policy on the chunk (equal-variation segments and "
+                         "key-norm landmarks on the GPU) and coarsens with its output")
     ap.add_argument("--no-shared-prefix", action="store_true",
                     help="decode a shared-prefix batch with spicy_decode_attn (every page per sequence)")
     return ap.parse_args()
@@ -60,6 +63,13 @@ def parse():
 
 def elem_bytes(dtype: str) -> int:
     return 2 if dtype == "bf16" else 4
+
+
+def policy_alg_bytes(call, spec) -> int:
+    """Bytes the policy must move: read K and V of every token of the chunk;
+    write the protection mask and the segment offsets."""
+    T, H, d = call.total_tokens, call.H_kv, call.d
+    return 2 * T * H * d * elem_bytes(call.dtype) + T * H + 4 * (call.B * spec.n_segments + 1) + 4 * (call.B + 1)
 
 
 def coarsen_alg_bytes(call, lengths: np.ndarray) -> int:
@@ -107,13 +117,22 @@ def copy_calibration():
                       "kernel": "torch.neg fp32", "launches": 5}), flush=True)
 
 
-def sources_digest() -> str:
-    """sha256 over the library's kernel sources and headers: a traffic figure
-    measured on other sources is not reported."""
+# the source file that defines each kernel; its digest also covers the
+# headers every kernel includes
+KERNEL_SOURCE = {
+    "coarsen_main_kernel": "coarsen.hip", "coarsen_cpoint_kernel": "coarsen.hip",
+    "decode_mfma_kernel": "decode.hip", "combine_kernel": "decode.hip", "decode_f32_kernel": "decode.hip",
+    "policy_token_kernel": "policy.hip", "policy_seq_kernel": "policy.hip",
+}
+
+
+def kernel_digest(kernel: str) -> str:
+    """sha256 over the file defining `kernel` and the shared headers: a
+    traffic figure measured on other sources is not reported."""
     import hashlib
     from coarse_grained_decode_amd import build as B
     h = hashlib.sha256()
-    for f in sorted(B.SOURCES + B.HEADERS):
+    for f in [KERNEL_SOURCE[kernel]] + sorted(B.HEADERS):
         h.update(f.encode())
         with open(os.path.join(B.CSRC, f), "rb") as fh:
             h.update(fh.read())
@@ -125,28 +144,27 @@ def sources_digest() -> str:
 def measured_traffic(workload: str):
     """HBM bytes per launch from profiles/traffic_<workload>.txt (rocprofv3
     FETCH_SIZE and WRITE_SIZE passes, scaled by the copy calibration), keyed
-    by kernel name; None when the file is missing or was measured on other
-    kernel sources."""
+    by kernel name; a kernel whose sources changed since its counters were
+    taken is left out.  None when the file is missing."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
     if not os.path.exists(path):
         return None
-    digest, table = None, {}
+    table = {}
     with open(path) as fh:
         for line in fh:
             parts = line.split()
-            if len(parts) >= 2 and parts[0] == "sources_sha256":
-                digest = parts[1]
-            elif len(parts) >= 3 and parts[0] == "traffic_bytes":
-                table[parts[1]] = float(parts[2])
-    if digest != sources_digest():
-        return None
+            if len(parts) >= 4 and parts[0] == "traffic_bytes" and parts[1] in KERNEL_SOURCE:
+                if parts[3] == kernel_digest(parts[1]):
+                    table[parts[1]] = float(parts[2])
     return table
 
 
-def cpu_baseline(wl, reps: int):
+def cpu_baseline(wl, reps: int, policy: bool = False):
     """The oracle (plain C, double precision) on the host cores: one whole
-    step for every sequence of the batch (the workload's per-step coarsen, then
-    decode), setup calls untimed.  Returns query tokens/s and details."""
+    step for every sequence of the batch (with `policy`, the oracle's policy
+    on the chunk first; then the per-step coarsen and the decode), setup calls
+    untimed.  Returns query tokens/s and details."""
+    import dataclasses
     import oracle
     threads = oracle.default_threads()
     cache = oracle.Cache(wl.dtype, wl.num_pages, wl.H_kv, wl.d, fill=False)
@@ -156,8 +174,14 @@ def cpu_baseline(wl, reps: int):
     times = []
     for r in range(reps + 1):
         t0 = time.perf_counter()
-        if wl.step is not None:
-            lengths = oracle.coarsen(wl.step, cache, threads=threads)
+        step = wl.step
+        if policy:
+            sp, c = wl.policy, wl.step
+            pr = oracle.policy(c.k, c.v, c.seq_offsets, sp.proj_ptr, sp.proj_idx, sp.n_segments, sp.n_landmarks,
+                               sp.sink, sp.recent)
+            step = dataclasses.replace(c, seg_offsets=pr.seg_offsets, seq_seg_ptr=pr.seq_seg_ptr, mask=pr.mask)
+        if step is not None:
+            lengths = oracle.coarsen(step, cache, threads=threads)
         oracle.decode(wl.q, wl.dtype, cache, wl.H_q, wl.page_table, lengths, threads=threads)
         dt = time.perf_counter() - t0
         if r > 0:
@@ -166,6 +190,7 @@ def cpu_baseline(wl, reps: int):
     med = statistics.median(times)
     return dict(value=wl.B / med, unit="query-tokens/s", cores=threads, kind="oracle",
                 sample=f"one whole step of the same workload ({wl.B} sequences: "
+                       f"{'policy (single thread) + ' if policy else ''}"
                        f"{'per-step coarsen + ' if wl.step is not None else ''}decode), "
                        f"median of {reps} after 1 warm-up, {med:.3f} s per step")
 
@@ -235,8 +260,17 @@ def main():
     # a step: the per-step coarsen call if the workload has one, else its whole
     # coarsen (setup) again, then the decode
     step_calls = [dw.step] if dw.step is not None else dw.setup
+    policy = None
+    if args.device_policy:
+        from coarse_grained_decode_amd.runner import DevicePolicy
+        if wl.policy is None or dw.step is None:
+            sys.exit(f"--device-policy: workload {wl.name} has no per-step chunk with a policy")
+        policy = DevicePolicy.of(wl.policy, dw.step.call, dev)
+        step_calls = [policy.feed(dw.step, dev)]
 
     def step():
+        if policy is not None:
+            policy.run(dw.step)
         for c in step_calls:
             c.run(dw.cache)
         dw.lengths = step_calls[-1].lengths
@@ -250,6 +284,8 @@ def main():
     torch.cuda.synchronize()
     for c in dw.setup + step_calls:
         assert int(c.ws[0].item()) == 0, "device error word set"
+    if policy is not None:
+        assert int(policy.ws[0].item()) == 0, "device error word set (policy)"
 
     # throughput: exactly K whole steps with nothing else on the stream
     torch.cuda.synchronize()
@@ -265,9 +301,12 @@ def main():
     # throughput loop because an event recorded between two calls leaves the
     # GPU idle for a few microseconds; part of that idle time lands inside the
     # bracketed durations, so these err on the slow side.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for e in evs:
+        e[3].record()
+        if policy is not None:
+            policy.run(dw.step)
         e[0].record()
         for c in step_calls:
             c.run(dw.cache)
@@ -277,11 +316,12 @@ def main():
     torch.cuda.synchronize()
     coarsen_ms = statistics.mean(e[0].elapsed_time(e[1]) for e in evs)
     decode_ms = statistics.mean(e[1].elapsed_time(e[2]) for e in evs)
+    policy_ms = statistics.mean(e[3].elapsed_time(e[0]) for e in evs) if policy is not None else None
     lengths = dw.lengths.cpu().numpy()
     cb = sum(coarsen_alg_bytes(c.call, c.lengths.cpu().numpy()) for c in step_calls)
     db = decode_alg_bytes(wl, lengths)
 
-    traffic = measured_traffic(wl.name)
+    traffic = measured_traffic(wl.name + ("_policy" if policy is not None else ""))
 
     def roof(nbytes, ms, kernels):
         gbs = nbytes / (ms * 1e-3) / 1e9
@@ -297,7 +337,16 @@ def main():
     r_coarsen["kernel"] = "spicy_coarsen (coarsen_main: plan + streaming, then coarsen_cpoint: entries)"
     r_decode["kernel"] = ("spicy_decode_attn_shared" if dw.shared_prefix_pages else "spicy_decode_attn") + \
         " (decode_mfma + combine)"
-    dominant, other = (r_coarsen, r_decode) if coarsen_ms >= decode_ms else (r_decode, r_coarsen)
+    calls = [(coarsen_ms, r_coarsen), (decode_ms, r_decode)]
+    if policy is not None:
+        c = dw.step.call
+        pb = policy_alg_bytes(c, wl.policy)
+        r_policy = roof(pb, policy_ms, ["policy_token_kernel", "policy_seq_kernel"])
+        r_policy["kernel"] = "spicy_policy (policy_token: fixed point, projection, variation, key norms; " \
+                             "then policy_seq: scan, boundaries, landmark radix select)"
+        calls.append((policy_ms, r_policy))
+    calls.sort(key=lambda x: -x[0])
+    dominant, other = calls[0][1], calls[1][1]
 
     ms_per_step = elapsed * 1e3 / args.steps
     out = {
@@ -316,13 +365,16 @@ def main():
         "config": {"workload": wl.name, "description": wl.description, "batch": wl.B,
                    "num_q_heads": wl.H_q, "num_kv_heads": wl.H_kv, "head_dim": wl.d,
                    "decode_splits": dw.splits, "shared_prefix_pages": dw.shared_prefix_pages,
-                   "cache_entries_per_seq_mean": float(lengths.mean())},
+                   "cache_entries_per_seq_mean": float(lengths.mean()),
+                   "device_policy": policy is not None},
         "roofline": dominant,
         "roofline_other": other,
         "decode_query_tokens_per_s": round(wl.B / (decode_ms * 1e-3), 1),
     }
+    if policy is not None:
+        out["roofline_policy"] = r_policy
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_reps)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_reps, policy=policy is not None)
     print(json.dumps(out), flush=True)
 
 

@@ -2,11 +2,12 @@
 
 Plumbing only: copies the host arrays of a workload to device memory once,
 allocates the paged cache pool and the workspaces, and issues
-spicy_coarsen / spicy_decode_attn calls on the current stream.  Used by the
+spicy_policy / spicy_coarsen / spicy_decode_attn calls on the current stream.  Used by the
 tests, the smoke check and the benchmark.
 """
 from __future__ import annotations
 
+import dataclasses
 from dataclasses import dataclass, field
 from typing import List, Optional
 
@@ -15,8 +16,8 @@ import torch
 
 from . import (PagedCache, spicy_coarsen, spicy_coarsen_workspace_bytes, spicy_decode_attn,
                spicy_decode_attn_shared, spicy_decode_num_splits, spicy_decode_shared_workspace_bytes,
-               workspace)
-from .workloads import CoarsenCall, Workload
+               spicy_policy, spicy_policy_workspace_bytes, workspace)
+from .workloads import CoarsenCall, PolicySpec, Workload
 
 
 def _tensor(a: np.ndarray, dtype: str | None, device) -> torch.Tensor:
@@ -65,6 +66,51 @@ class DeviceCall:
     @property
     def input_bytes(self) -> int:
         return self.k.numel() * self.k.element_size() * 2
+
+
+@dataclass
+class DevicePolicy:
+    """spicy_policy for a workload's per-step chunk: its inputs (the chunk's
+    k, v and sequence offsets come from the step call) and its outputs, which
+    the step's coarsening then reads instead of the generator's segments and
+    mask."""
+    spec: PolicySpec
+    proj_ptr: torch.Tensor
+    proj_idx: torch.Tensor
+    seg_offsets: torch.Tensor      # [B*N + 1]
+    seq_seg_ptr: torch.Tensor      # [B+1]
+    mask: torch.Tensor             # [total_tokens, H] uint8
+    ws: torch.Tensor
+
+    @staticmethod
+    def of(spec: PolicySpec, call: CoarsenCall, device) -> "DevicePolicy":
+        B, N = call.B, spec.n_segments
+        return DevicePolicy(
+            spec=spec,
+            proj_ptr=_tensor(spec.proj_ptr, None, device), proj_idx=_tensor(spec.proj_idx, None, device),
+            seg_offsets=torch.zeros(B * N + 1, dtype=torch.int32, device=device),
+            seq_seg_ptr=torch.zeros(B + 1, dtype=torch.int32, device=device),
+            mask=torch.zeros((call.total_tokens, call.H_kv), dtype=torch.uint8, device=device),
+            ws=workspace(spicy_policy_workspace_bytes(call.total_tokens, call.H_kv), device),
+        )
+
+    def run(self, step: "DeviceCall", stream=None) -> None:
+        sp = self.spec
+        spicy_policy(step.k, step.v, step.seq_offsets, self.proj_ptr, self.proj_idx, sp.n_segments,
+                     sp.n_landmarks, sp.sink, sp.recent, self.seg_offsets, self.seq_seg_ptr, self.mask, self.ws,
+                     stream, B=step.call.B, total_tokens=step.call.total_tokens)
+
+    def feed(self, step: "DeviceCall", device) -> "DeviceCall":
+        """The step call reading this policy's outputs (N slots per sequence)."""
+        c = step.call
+        B, N = c.B, self.spec.n_segments
+        shaped = dataclasses.replace(c, seg_offsets=np.zeros(B * N + 1, dtype=np.int32),
+                                     seq_seg_ptr=np.zeros(B + 1, dtype=np.int32))
+        return dataclasses.replace(
+            step, call=shaped, seg_offsets=self.seg_offsets, seq_seg_ptr=self.seq_seg_ptr, mask=self.mask,
+            lengths=torch.zeros(B, dtype=torch.int32, device=device),
+            ws=workspace(spicy_coarsen_workspace_bytes(B, B * N, c.total_tokens, c.H_kv, c.d,
+                                                       1 if c.dtype == "bf16" else 0), device))
 
 
 @dataclass
