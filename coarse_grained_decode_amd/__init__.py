@@ -20,6 +20,7 @@ __all__ = [
     "spicy_coarsen_workspace_bytes", "spicy_decode_workspace_bytes", "spicy_decode_num_splits",
     "spicy_decode_attn_shared", "spicy_decode_shared_workspace_bytes",
     "spicy_policy", "spicy_policy_workspace_bytes",
+    "spicy_decode_attn_multi", "spicy_decode_multi_workspace_bytes",
     "spicy_status_string", "library_path", "load_library",
     "SPICY_F32", "SPICY_BF16", "PAGE_SIZE", "WORKSPACE_HEADER",
     "DEVERR_PAGE_ID", "DEVERR_CAPACITY", "DEVERR_SEGMENTS", "DEVERR_LENGTH", "DEVERR_POLICY",
@@ -86,6 +87,10 @@ def load_library():
     L.spicy_decode_shared_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     L.spicy_decode_attn_shared.restype = ctypes.c_int
     L.spicy_decode_attn_shared.argtypes = [CP, P, i32, P, i32, P, i32, i32, P, P, P, sz, i32, P]
+    L.spicy_decode_multi_workspace_bytes.restype = sz
+    L.spicy_decode_multi_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32]
+    L.spicy_decode_attn_multi.restype = ctypes.c_int
+    L.spicy_decode_attn_multi.argtypes = [CP, P, i32, i32, P, i32, P, i32, i32, P, P, P, sz, i32, P]
     L.spicy_policy_workspace_bytes.restype = sz
     L.spicy_policy_workspace_bytes.argtypes = [i32, i32]
     L.spicy_policy.restype = ctypes.c_int
@@ -241,6 +246,32 @@ def spicy_decode_attn_shared(cache: PagedCache, q, page_table, lengths, shared_p
                                     _ptr(workspace), ws_bytes, int(num_splits), _stream(stream))
     if rc != 0:
         raise SpicyError(rc, "spicy_decode_attn_shared")
+
+
+def spicy_decode_multi_workspace_bytes(B: int, num_q_tokens: int, num_q_heads: int, num_kv_heads: int,
+                                       head_dim: int, max_pages_per_seq: int, shared_prefix_pages: int = 0,
+                                       num_splits: int = 0) -> int:
+    return int(load_library().spicy_decode_multi_workspace_bytes(B, num_q_tokens, num_q_heads, num_kv_heads,
+                                                                 head_dim, max_pages_per_seq,
+                                                                 shared_prefix_pages, num_splits))
+
+
+def spicy_decode_attn_multi(cache: PagedCache, q, page_table, lengths, shared_prefix_pages: int, o, lse,
+                            workspace, num_splits: int = 0, stream=None, *, B: int | None = None,
+                            max_pages_per_seq: int | None = None) -> None:
+    """spicy_decode_attn_multi through the C ABI (see include/spicy.h):
+    q [B, n_q, H_q, d] -> o [B, n_q, H_q, d], lse [B, n_q, H_q]."""
+    L = load_library()
+    B = int(q.shape[0]) if B is None else B
+    n_q, H_q = int(q.shape[1]), int(q.shape[2])
+    max_pages = int(page_table.shape[-1]) if max_pages_per_seq is None else max_pages_per_seq
+    st = cache.struct()
+    ws_bytes = workspace.numel() * workspace.element_size() if isinstance(workspace, torch.Tensor) else 0
+    rc = L.spicy_decode_attn_multi(ctypes.byref(st), _ptr(q), n_q, H_q, _ptr(page_table), max_pages,
+                                   _ptr(lengths), B, int(shared_prefix_pages), _ptr(o), _ptr(lse),
+                                   _ptr(workspace), ws_bytes, int(num_splits), _stream(stream))
+    if rc != 0:
+        raise SpicyError(rc, "spicy_decode_attn_multi")
 
 
 def spicy_policy_workspace_bytes(total_tokens: int, num_kv_heads: int) -> int:

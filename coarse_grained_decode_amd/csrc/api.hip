@@ -63,14 +63,20 @@ int32_t pages_per_wave(int64_t visits) {
     return std::max<int32_t>(kPagesInFlight, ceil_div(visits, kResidentWaves));
 }
 
-DecodePlan plan_decode(int32_t B, int32_t H_q, int32_t H_kv, int32_t max_pages, int32_t P, int32_t num_splits) {
+// 16-row query tiles of one (sequence, KV head): its n_q * G (token, head) rows
+int32_t priv_tiles(int32_t n_q, int32_t H_q, int32_t H_kv) {
+    return ceil_div(static_cast<int64_t>(n_q) * (H_q / std::max(1, H_kv)), 16);
+}
+
+DecodePlan plan_decode(int32_t B, int32_t H_q, int32_t H_kv, int32_t max_pages, int32_t P, int32_t num_splits,
+                       int32_t n_q = 1) {
     DecodePlan p;
-    const int64_t units = static_cast<int64_t>(B) * std::max(1, H_kv);
+    const int64_t units = static_cast<int64_t>(B) * std::max(1, H_kv) * priv_tiles(n_q, H_q, H_kv);
     const int32_t priv = max_pages - P;
-    const int64_t rows = static_cast<int64_t>(B) * (H_q / std::max(1, H_kv));
+    const int64_t rows = static_cast<int64_t>(B) * n_q * (H_q / std::max(1, H_kv));
     const int64_t tiles = (rows + 15) / 16;
-    // the work of the whole call: private pages per (sequence, KV head) and
-    // shared pages per (KV head, query tile)
+    // the work of the whole call: private pages per (sequence, KV head, query
+    // tile) and shared pages per (KV head, query tile)
     const int64_t visits = units * std::max(priv, 0) + static_cast<int64_t>(P) * std::max(1, H_kv) * tiles;
     const int32_t ppw = pages_per_wave(visits);
     if (P > 0) {
@@ -213,13 +219,21 @@ size_t spicy_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t num_
 size_t spicy_decode_shared_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
                                            int32_t head_dim, int32_t max_pages_per_seq,
                                            int32_t shared_prefix_pages, int32_t num_splits) {
-    if (B < 0 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 || shared_prefix_pages < 0)
+    return spicy_decode_multi_workspace_bytes(B, 1, num_q_heads, num_kv_heads, head_dim, max_pages_per_seq,
+                                              shared_prefix_pages, num_splits);
+}
+
+size_t spicy_decode_multi_workspace_bytes(int32_t B, int32_t num_q_tokens, int32_t num_q_heads,
+                                          int32_t num_kv_heads, int32_t head_dim, int32_t max_pages_per_seq,
+                                          int32_t shared_prefix_pages, int32_t num_splits) {
+    if (B < 0 || num_q_tokens < 1 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 ||
+        shared_prefix_pages < 0)
         return 0;
     // the fp32 path ignores the prefix; reserve for whichever plan is larger
-    const DecodePlan p0 = plan_decode(B, num_q_heads, num_kv_heads, max_pages_per_seq, 0, num_splits);
+    const DecodePlan p0 = plan_decode(B, num_q_heads, num_kv_heads, max_pages_per_seq, 0, num_splits, num_q_tokens);
     const DecodePlan p1 = plan_decode(B, num_q_heads, num_kv_heads, max_pages_per_seq, shared_prefix_pages,
-                                      num_splits);
-    return decode_workspace(B, num_q_heads, head_dim, std::max(p0.slots(), p1.slots()));
+                                      num_splits, num_q_tokens);
+    return decode_workspace(B * num_q_tokens, num_q_heads, head_dim, std::max(p0.slots(), p1.slots()));
 }
 
 spicy_status spicy_decode_attn(const spicy_cache* cache, const void* q, int32_t num_q_heads,
@@ -227,8 +241,8 @@ spicy_status spicy_decode_attn(const spicy_cache* cache, const void* q, int32_t 
                                const int32_t* lengths, int32_t B, float* o, float* lse,
                                void* workspace, size_t workspace_bytes, int32_t num_splits,
                                void* stream) {
-    return spicy_decode_attn_shared(cache, q, num_q_heads, page_table, max_pages_per_seq, lengths, B, 0, o, lse,
-                                    workspace, workspace_bytes, num_splits, stream);
+    return spicy_decode_attn_multi(cache, q, 1, num_q_heads, page_table, max_pages_per_seq, lengths, B, 0, o, lse,
+                                   workspace, workspace_bytes, num_splits, stream);
 }
 
 spicy_status spicy_decode_attn_shared(const spicy_cache* cache, const void* q, int32_t num_q_heads,
@@ -236,23 +250,36 @@ spicy_status spicy_decode_attn_shared(const spicy_cache* cache, const void* q, i
                                       const int32_t* lengths, int32_t B, int32_t shared_prefix_pages,
                                       float* o, float* lse, void* workspace, size_t workspace_bytes,
                                       int32_t num_splits, void* stream) {
+    return spicy_decode_attn_multi(cache, q, 1, num_q_heads, page_table, max_pages_per_seq, lengths, B,
+                                   shared_prefix_pages, o, lse, workspace, workspace_bytes, num_splits, stream);
+}
+
+spicy_status spicy_decode_attn_multi(const spicy_cache* cache, const void* q, int32_t num_q_tokens,
+                                     int32_t num_q_heads, const int32_t* page_table, int32_t max_pages_per_seq,
+                                     const int32_t* lengths, int32_t B, int32_t shared_prefix_pages, float* o,
+                                     float* lse, void* workspace, size_t workspace_bytes, int32_t num_splits,
+                                     void* stream) {
     spicy_status st = check_cache(cache);
     if (st != SPICY_OK) return st;
-    if (B < 0 || num_q_heads < 1 || num_splits < 0 || shared_prefix_pages < 0) return SPICY_ERR_ARG;
-    if (B > kMaxGridY || num_q_heads > kMaxGridY) return SPICY_ERR_UNSUPPORTED;
+    if (B < 0 || num_q_heads < 1 || num_q_tokens < 1 || num_splits < 0 || shared_prefix_pages < 0)
+        return SPICY_ERR_ARG;
+    if (static_cast<int64_t>(B) * num_q_tokens > kMaxGridY || num_q_heads > kMaxGridY) return SPICY_ERR_UNSUPPORTED;
     if (num_q_heads % cache->num_kv_heads != 0) return SPICY_ERR_UNSUPPORTED;
     if (num_q_heads / cache->num_kv_heads > kMaxGroup) return SPICY_ERR_UNSUPPORTED;
+    if (static_cast<int64_t>(B) * num_q_tokens * num_q_heads >= (int64_t(1) << 31) / kMaxGroup)
+        return SPICY_ERR_UNSUPPORTED;
     if (B == 0) return SPICY_OK;
     if (!q || !page_table || !lengths || !o || !lse || !workspace) return SPICY_ERR_ARG;
     if (max_pages_per_seq < 1) return SPICY_ERR_ARG;
     if (shared_prefix_pages > max_pages_per_seq) return SPICY_ERR_RANGE;
-    if (workspace_bytes < spicy_decode_shared_workspace_bytes(B, num_q_heads, cache->num_kv_heads,
-                                                              cache->head_dim, max_pages_per_seq,
-                                                              shared_prefix_pages, num_splits))
+    if (workspace_bytes < spicy_decode_multi_workspace_bytes(B, num_q_tokens, num_q_heads, cache->num_kv_heads,
+                                                             cache->head_dim, max_pages_per_seq,
+                                                             shared_prefix_pages, num_splits))
         return SPICY_ERR_CAPACITY;
     // the fp32 kernel has no shared-prefix role: every page is private there
     const int32_t P = cache->dtype == SPICY_BF16 ? shared_prefix_pages : 0;
-    const DecodePlan plan = plan_decode(B, num_q_heads, cache->num_kv_heads, max_pages_per_seq, P, num_splits);
+    const DecodePlan plan = plan_decode(B, num_q_heads, cache->num_kv_heads, max_pages_per_seq, P, num_splits,
+                                        num_q_tokens);
 
     spicy::DecodeArgs a{};
     a.cache = spicy::CacheArgs{cache->k, cache->v, cache->ab, cache->meta, cache->num_pages, cache->num_kv_heads};
@@ -262,8 +289,8 @@ spicy_status spicy_decode_attn_shared(const spicy_cache* cache, const void* q, i
     a.o = o;
     a.lse = lse;
     char* ws = static_cast<char*>(workspace);
-    const size_t rows = static_cast<size_t>(B) * static_cast<size_t>(num_q_heads) *
-                        static_cast<size_t>(plan.slots());
+    const size_t rows = static_cast<size_t>(B) * static_cast<size_t>(num_q_tokens) *
+                        static_cast<size_t>(num_q_heads) * static_cast<size_t>(plan.slots());
     a.err = reinterpret_cast<int32_t*>(ws);
     size_t off = SPICY_WORKSPACE_HEADER;
     a.part_ml = reinterpret_cast<float*>(ws + off);
@@ -279,6 +306,8 @@ spicy_status spicy_decode_attn_shared(const spicy_cache* cache, const void* q, i
     a.prefix_pages = P;
     a.prefix_chunk = plan.prefix_chunk;
     a.prefix_splits = plan.prefix_splits;
+    a.n_q = num_q_tokens;
+    a.priv_tiles = priv_tiles(num_q_tokens, num_q_heads, cache->num_kv_heads);
     return spicy::launch_decode(a, cache->dtype, cache->head_dim, static_cast<hipStream_t>(stream));
 }
 

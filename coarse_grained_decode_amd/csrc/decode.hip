@@ -300,7 +300,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
         w /= tgb;
         h = w % H;
         const int c = w / H;
-        const int rows = a.B * G;
+        const int rows = a.B * a.n_q * G;                  // rows (sequence, token, query head)
         if (c >= a.prefix_splits || t * 16 >= rows) return;
         slot = c;
         p0 = c * a.prefix_chunk;
@@ -309,8 +309,10 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
         table = a.page_table;
         const int r = t * 16 + row;
         row_valid = r < rows;
-        const int bq = row_valid ? r / G : 0;
-        prow = static_cast<int64_t>(bq) * a.H_q + static_cast<int64_t>(h) * G + (row_valid ? r % G : 0);
+        const int rq = row_valid ? r : 0;
+        const int bq = rq / (a.n_q * G);                    // sequence
+        const int vq = rq / G;                              // sequence * n_q + token
+        prow = static_cast<int64_t>(vq) * a.H_q + static_cast<int64_t>(h) * G + rq % G;
         raw_len = row_valid ? a.lengths[bq] : 0;
         prow0 = static_cast<int64_t>(h) * G;
         issue_loads();
@@ -319,6 +321,8 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
         const int sgb = (a.priv_splits + kWavesPerBlock - 1) / kWavesPerBlock;
         const int split = static_cast<int>(blk % sgb) * kWavesPerBlock + wave;
         blk /= sgb;
+        const int tile = static_cast<int>(blk % a.priv_tiles);
+        blk /= a.priv_tiles;
         h = static_cast<int>(blk % H);
         const int64_t b = blk / H;
         if (split >= a.priv_splits || b >= a.B) return;
@@ -328,9 +332,12 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
         p1 = p0 + a.pages_per_split;                      // clamped to the length below
         id_end = a.max_pages;
         table = a.page_table + b * a.max_pages;
-        row_valid = row < G;
-        prow = b * a.H_q + static_cast<int64_t>(h) * G + row;
-        prow0 = b * a.H_q + static_cast<int64_t>(h) * G;
+        // the tile's rows: (token, query head) pairs r = token * G + g of this KV head
+        const int r = tile * 16 + row;
+        row_valid = r < a.n_q * G;
+        const int rq = row_valid ? r : 0;
+        prow = (b * a.n_q + rq / G) * a.H_q + static_cast<int64_t>(h) * G + rq % G;
+        prow0 = b * a.n_q * a.H_q + static_cast<int64_t>(h) * G;
         issue_loads();
     }
     const int32_t len = (prefix_role && !row_valid) ? 0 : check_length(a, raw_len);
@@ -364,9 +371,9 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
     // of their tile map the chunk's pages like sequence 0 (independent loads,
     // one flag).  It is done last, off the path to the first pages.
     if (prefix_role && h == 0) {
-        const int rows = a.B * G;
-        const int b_first = (t * 16) / G;
-        const int b_last = min(rows - 1, t * 16 + 15) / G;
+        const int rows = a.B * a.n_q * G;
+        const int b_first = (t * 16) / (a.n_q * G);
+        const int b_last = min(rows - 1, t * 16 + 15) / (a.n_q * G);
         const int npg = p1 - p0;
         const int n = (b_last - b_first + 1) * npg;
         bool bad = false;
@@ -391,7 +398,8 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
     const int qtr = lane % 4;
     const int split = blockIdx.x * (blockDim.x / kWave) + wave;
     const int hq = blockIdx.y;
-    const int b = blockIdx.z;
+    const int bv = blockIdx.z;                 // sequence * n_q + token
+    const int b = bv / a.n_q;
     const int H = a.cache.H;
     const int G = a.H_q / H;
     const int h = hq / G;
@@ -403,7 +411,7 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
     const int32_t p1 = min(p0 + a.pages_per_split, npages);
     if (p0 >= p1) return;
 
-    const float* qrow = static_cast<const float*>(a.q) + (static_cast<int64_t>(b) * a.H_q + hq) * D;
+    const float* qrow = static_cast<const float*>(a.q) + (static_cast<int64_t>(bv) * a.H_q + hq) * D;
     float qv[QD];
     float n2 = 0.f;
 #pragma unroll
@@ -467,7 +475,7 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
     }
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) l_run += __shfl_xor(l_run, o);
-    const int64_t idx = (static_cast<int64_t>(b) * a.H_q + hq) * a.splits + a.prefix_splits + split;
+    const int64_t idx = (static_cast<int64_t>(bv) * a.H_q + hq) * a.splits + a.prefix_splits + split;
     if (lane == 0) {
         a.part_ml[2 * idx + 0] = m_run;
         a.part_ml[2 * idx + 1] = l_run;
@@ -487,12 +495,12 @@ __global__ __launch_bounds__(64) void combine_kernel(DecodeArgs a) {
     constexpr int kChunk = 16;
     const int lane = threadIdx.x;
     const int hq = blockIdx.x;
-    const int b = blockIdx.y;
-    const int32_t len = checked_length(a, b);
+    const int bv = blockIdx.y;                 // sequence * n_q + token
+    const int32_t len = checked_length(a, bv / a.n_q);
     const int32_t npages = (len + kPage - 1) / kPage;
     const int32_t priv = max(0, npages - a.page_begin);
     const int nsplit = a.prefix_splits + min(a.priv_splits, (priv + a.pages_per_split - 1) / a.pages_per_split);
-    const int64_t base = (static_cast<int64_t>(b) * a.H_q + hq) * a.splits;
+    const int64_t base = (static_cast<int64_t>(bv) * a.H_q + hq) * a.splits;
 
     float M = -__builtin_huge_valf();
     for (int s = lane; s < nsplit; s += kWave) M = fmaxf(M, a.part_ml[2 * (base + s)]);
@@ -522,13 +530,13 @@ __global__ __launch_bounds__(64) void combine_kernel(DecodeArgs a) {
             for (int j = 0; j < DL; ++j) acc[j] += wu * ov[u][j];
         }
     }
-    float* orow = a.o + (static_cast<int64_t>(b) * a.H_q + hq) * D;
+    float* orow = a.o + (static_cast<int64_t>(bv) * a.H_q + hq) * D;
     const bool live = L > 0.f;
     const float inv = live ? 1.f / L : 0.f;
 #pragma unroll
     for (int j = 0; j < DL; ++j) orow[lane + kWave * j] = live ? acc[j] * inv : 0.f;
     if (lane == 0)
-        a.lse[static_cast<int64_t>(b) * a.H_q + hq] = live ? (msub + __log2f(L)) * kLn2 : -__builtin_huge_valf();
+        a.lse[static_cast<int64_t>(bv) * a.H_q + hq] = live ? (msub + __log2f(L)) * kLn2 : -__builtin_huge_valf();
 }
 
 // ------------------------------------------------------------------ launch
@@ -541,23 +549,23 @@ static spicy_status launch_decode_t(const DecodeArgs& a0, int dtype, hipStream_t
     DecodeArgs a = a0;
     if (dtype == SPICY_BF16) {
         const int G = a.H_q / a.cache.H;
-        const int tiles = (a.B * G + 15) / 16;
+        const int tiles = (a.B * a.n_q * G + 15) / 16;
         a.prefix_tile_blocks = (tiles + kWavesPerBlock - 1) / kWavesPerBlock;
         const int64_t pb = static_cast<int64_t>(a.prefix_splits) * a.cache.H * a.prefix_tile_blocks;
         a.prefix_blocks = static_cast<int32_t>((pb + kXcds - 1) / kXcds * kXcds);
         const int64_t sgb = (a.priv_splits + kWavesPerBlock - 1) / kWavesPerBlock;
-        const int64_t nblk = a.prefix_blocks + sgb * a.cache.H * a.B;
+        const int64_t nblk = a.prefix_blocks + sgb * a.priv_tiles * a.cache.H * a.B;
         const int64_t gx = nblk < kMaxGridX ? nblk : kMaxGridX;
         const int64_t gy = (nblk + gx - 1) / gx;
         hipLaunchKernelGGL((decode_mfma_kernel<D, kNbuf>), dim3(static_cast<unsigned>(gx), static_cast<unsigned>(gy)),
                            dim3(kWavesPerBlock * kWave), 0, stream, a);
     } else {
         const int wpb = a.priv_splits < 4 ? a.priv_splits : 4;
-        dim3 grid((a.priv_splits + wpb - 1) / wpb, a.H_q, a.B);
+        dim3 grid((a.priv_splits + wpb - 1) / wpb, a.H_q, a.B * a.n_q);
         hipLaunchKernelGGL((decode_f32_kernel<D>), grid, dim3(wpb * kWave), 0, stream, a);
     }
     if (hipGetLastError() != hipSuccess) return SPICY_ERR_HIP;
-    hipLaunchKernelGGL((combine_kernel<D>), dim3(a.H_q, a.B), dim3(kWave), 0, stream, a);
+    hipLaunchKernelGGL((combine_kernel<D>), dim3(a.H_q, a.B * a.n_q), dim3(kWave), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return SPICY_ERR_HIP;
     return SPICY_OK;
 }

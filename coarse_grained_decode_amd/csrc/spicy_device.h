@@ -187,8 +187,8 @@ struct DecodeArgs {
     float* o;
     float* lse;
     int32_t* err;
-    float* part_ml;        // [B][H_q][S][2]    running max (log2 units) and sum
-    float* part_o;         // [B][H_q][S][d]    unnormalised output
+    float* part_ml;        // [B][n_q][H_q][S][2]  running max (log2 units) and sum
+    float* part_o;         // [B][n_q][H_q][S][d]  unnormalised output
     int32_t B;
     int32_t H_q;
     int32_t max_pages;
@@ -201,6 +201,8 @@ struct DecodeArgs {
     int32_t prefix_splits;     // ceil(P / prefix_chunk) chunks (slots 0 .. prefix_splits-1)
     int32_t prefix_blocks;     // set by the launcher: workgroups of the prefix role
     int32_t prefix_tile_blocks;  // set by the launcher: workgroups per (chunk, KV head)
+    int32_t n_q;               // query tokens per sequence (rows: (b * n_q + token) * H_q + head)
+    int32_t priv_tiles;        // 16-row tiles of one (sequence, KV head): ceil(n_q * G / 16)
 };
 
 }  // namespace spicy

@@ -504,13 +504,14 @@ class DecodeCase:
 
 def random_decode_case(seed: int, *, B: int, H_q: int, H_kv: int, d: int, dtype: str = "bf16",
                        prefix_pages: int = 0, private_pages: Tuple[int, int] = (1, 6),
-                       null_frac: float = 0.05) -> DecodeCase:
+                       null_frac: float = 0.05, q_tokens: int = 1) -> DecodeCase:
     """A synthetic paged cache for decode tests: keys, values and queries
     N(0, 1); alpha ~ U(0, 4) (a null_frac share of entries null: alpha = -inf);
     beta ~ U(0, 0.01).  Every sequence maps the same `prefix_pages` physical
     pages first, then U[private_pages] private pages in a shuffled pool; its
     length ends at a random slot of its last page.  Slots past a sequence's
-    length in its own last page hold NaN, so reading them would show."""
+    length in its own last private page hold NaN, so reading them would show.  With
+    q_tokens > 1 the queries are [B, q_tokens, H_q, d]."""
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(5000 + seed)))
     npriv = rng.integers(private_pages[0], private_pages[1] + 1, size=B)
     num_pages = prefix_pages + int(npriv.sum())
@@ -532,11 +533,12 @@ def random_decode_case(seed: int, *, B: int, H_q: int, H_kv: int, d: int, dtype:
         nxt += n
         used = int(rng.integers(1, PAGE + 1))
         lengths[b] = (prefix_pages + n - 1) * PAGE + used
-        last = table[b, prefix_pages + n - 1]
-        k[last, :, used:, :] = np.nan
-        v[last, :, used:, :] = np.nan
-        ab[last, :, used:, :] = np.nan
-    q = rng.standard_normal((B, H_q, d), dtype=np.float32)
+        if n > 0:           # a shared page holds other sequences' entries: leave it whole
+            last = table[b, prefix_pages + n - 1]
+            k[last, :, used:, :] = np.nan
+            v[last, :, used:, :] = np.nan
+            ab[last, :, used:, :] = np.nan
+    q = rng.standard_normal((B, H_q, d) if q_tokens == 1 else (B, q_tokens, H_q, d), dtype=np.float32)
     return DecodeCase(dtype, H_q, H_kv, d, _store(chunked(k), dtype), _store(chunked(v), dtype),
                       _store(ab, dtype), table, lengths, _store(q, dtype), prefix_pages)
 
@@ -572,6 +574,13 @@ def random_policy_case(seed: int, *, B: int, T_range: Tuple[int, int], H: int, d
     k = np.concatenate(ks) if B else np.zeros((0, H, d), np.uint16)
     v = np.concatenate(vs) if B else np.zeros((0, H, d), np.uint16)
     return PolicyCase(k, v, so, spec)
+
+
+def query_tokens(wl: Workload, n_q: int) -> np.ndarray:
+    """n_q query tokens per sequence for wl ([B, n_q, H_q, d], N(0, 1) in the
+    workload's dtype), from a stream of their own: SeedSequence([2000, n_q])."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([2000, n_q])))
+    return _store(rng.standard_normal((wl.B, n_q, wl.H_q, wl.d), dtype=np.float32), wl.dtype)
 
 
 def tiny_fp32(**over) -> Workload:

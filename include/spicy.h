@@ -242,6 +242,39 @@ spicy_status spicy_decode_attn_shared(const spicy_cache* cache,   /* host struct
                                       void* workspace, size_t workspace_bytes,
                                       int32_t num_splits, void* stream);
 
+/* Workspace bytes spicy_decode_attn_multi needs for the same shapes. */
+size_t spicy_decode_multi_workspace_bytes(int32_t B, int32_t num_q_tokens, int32_t num_q_heads,
+                                          int32_t num_kv_heads, int32_t head_dim, int32_t max_pages_per_seq,
+                                          int32_t shared_prefix_pages, int32_t num_splits);
+
+/* spicy_decode_attn_multi — several query tokens per sequence against the
+ * compressed cache: every one of the num_q_tokens query tokens of sequence b
+ * attends to the same entries [0, lengths[b]) with the logit of
+ * spicy_decode_attn (SPICY-KV demo page, section "2. FlashAttention-2/3 &
+ * PagedAttention Online-Softmax Kernel Fusion": the tile loop, here with a
+ * tile of several query tokens), as in speculative verification or chunked
+ * prefill against the compressed history.  The new tokens' own keys and
+ * values are not part of this call: merge their attention with the returned
+ * LSE.
+ *   q    [B][num_q_tokens][num_q_heads][head_dim] (cache dtype), post-RoPE;
+ *   o    [B][num_q_tokens][num_q_heads][head_dim] fp32;
+ *   lse  [B][num_q_tokens][num_q_heads] fp32 (natural log).
+ * Everything else as spicy_decode_attn_shared (shared_prefix_pages = 0 for
+ * none).  On bf16 caches the (token, query head) rows of one KV head fill the
+ * 16 MFMA columns, so each key and value byte loaded serves up to 16 rows of
+ * any tokens; a KV head with more than 16 rows per sequence is processed in
+ * several row tiles.  num_q_tokens = 1 is spicy_decode_attn_shared.
+ * Workspace: >= spicy_decode_multi_workspace_bytes(...) with the same
+ *   arguments.
+ * Errors: those of spicy_decode_attn_shared; SPICY_ERR_ARG if num_q_tokens < 1,
+ *   SPICY_ERR_UNSUPPORTED if B * num_q_tokens > 65535. */
+spicy_status spicy_decode_attn_multi(const spicy_cache* cache,   /* host struct */
+                                     const void* q, int32_t num_q_tokens, int32_t num_q_heads,
+                                     const int32_t* page_table, int32_t max_pages_per_seq,
+                                     const int32_t* lengths, int32_t B, int32_t shared_prefix_pages,
+                                     float* o, float* lse, void* workspace, size_t workspace_bytes,
+                                     int32_t num_splits, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* spicy_status_string(spicy_status s);
 

@@ -187,6 +187,21 @@ def decode(q: np.ndarray, q_dtype: str, cache: Cache, H_q: int, page_table: np.n
     return o, lse
 
 
+def decode_multi(q: np.ndarray, q_dtype: str, cache: Cache, page_table: np.ndarray, lengths: np.ndarray,
+                 threads: int | None = None):
+    """Several query tokens per sequence: q [B, n_q, H_q, d].  Every token's
+    rows attend to its sequence's entries exactly as a single query does
+    (the decode definition applied per query row), so this is oracle_decode
+    over the B * n_q (sequence, token) rows, each with its sequence's page
+    table row and length.  Returns (o [B, n_q, H_q, d], lse [B, n_q, H_q])."""
+    B, n_q, H_q, d = q.shape
+    qq = np.ascontiguousarray(q).reshape(B * n_q, H_q, d)
+    table = np.repeat(np.asarray(page_table), n_q, axis=0)
+    lens = np.repeat(np.asarray(lengths), n_q)
+    o, lse = decode(qq, q_dtype, cache, H_q, table, lens, threads)
+    return o.reshape(B, n_q, H_q, d), lse.reshape(B, n_q, H_q)
+
+
 def run_workload(wl, store: str | None = None, threads: int | None = None):
     """Coarsen every call of a workload (setup calls, then the step call once)
     into a fresh cache and decode its queries.  Returns (cache, lengths, o, lse)."""

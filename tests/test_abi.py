@@ -32,7 +32,8 @@ def test_every_declared_symbol_is_exported(lib):
     assert {"spicy_coarsen", "spicy_decode_attn", "spicy_coarsen_workspace_bytes",
             "spicy_decode_workspace_bytes", "spicy_decode_num_splits", "spicy_status_string",
             "spicy_decode_attn_shared", "spicy_decode_shared_workspace_bytes",
-            "spicy_policy", "spicy_policy_workspace_bytes"} <= set(names)
+            "spicy_policy", "spicy_policy_workspace_bytes",
+            "spicy_decode_attn_multi", "spicy_decode_multi_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -152,6 +153,25 @@ def test_coarsen_rejects_bad_arguments(lib):
     assert call(cache=_cache(pages=0)) == 2
     assert call(wsb=100) == 3
     assert call(B=0) == 0
+
+
+def test_multi_decode_rejects_bad_arguments(lib):
+    P = 0x1000
+    c = _cache()
+
+    def call(nq, B=2, shared=0, wsb=1 << 30):
+        return lib.spicy_decode_attn_multi(ctypes.byref(c), P, nq, 28, P, 8, P, B, shared, P, P, P, wsb, 0, None)
+
+    assert call(0) == 1
+    assert call(-2) == 1
+    assert call(3, B=40000) == 4            # B * tokens above the 65535 rows of the combine grid
+    assert call(3, wsb=16) == 3
+    assert call(3, shared=9) == 2
+    # a single token needs exactly the shared decode's workspace; more tokens more
+    one = lib.spicy_decode_multi_workspace_bytes(2, 1, 28, 4, 128, 8, 3, 0)
+    assert one == lib.spicy_decode_shared_workspace_bytes(2, 28, 4, 128, 8, 3, 0)
+    assert lib.spicy_decode_multi_workspace_bytes(2, 4, 28, 4, 128, 8, 3, 0) > one
+    assert lib.spicy_decode_multi_workspace_bytes(2, 0, 28, 4, 128, 8, 3, 0) == 0
 
 
 def test_policy_workspace_and_bad_arguments(lib):

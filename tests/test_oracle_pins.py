@@ -430,3 +430,16 @@ def test_errors_are_reported():
         oracle.decode(q, "f64", cache, q.shape[1], bad, lengths)
     with pytest.raises(ValueError):
         oracle.decode(q, "f64", cache, q.shape[1], call.page_table[:, :1], lengths)
+
+
+def test_decode_multi_is_per_token_decode():
+    """Several query tokens per sequence: every token's rows attend to the
+    sequence's entries as a single query does."""
+    c = W.random_decode_case(40, B=3, H_q=8, H_kv=2, d=64, q_tokens=3, dtype="f32")
+    cache = oracle.Cache(c.dtype, c.k.shape[0], c.H_kv, c.d, fill=False)
+    cache.k[:] = c.k; cache.v[:] = c.v; cache.ab[:] = c.ab
+    o, lse = oracle.decode_multi(c.q, c.dtype, cache, c.page_table, c.lengths)
+    assert o.shape == (3, 3, 8, 64) and lse.shape == (3, 3, 8)
+    for t in range(3):
+        o1, l1 = oracle.decode(np.ascontiguousarray(c.q[:, t]), c.dtype, cache, 8, c.page_table, c.lengths)
+        assert np.array_equal(o[:, t], o1) and np.array_equal(lse[:, t], l1)
