@@ -56,6 +56,9 @@ def parse():
     ap.add_argument("--device-policy", action="store_true",
                     help="every step also runs spicy_policy on the chunk (equal-variation segments and "
                          "key-norm landmarks on the GPU) and coarsens with its output")
+    ap.add_argument("--query-tokens", type=int, default=1,
+                    help="query tokens per sequence in every decode call (spicy_decode_attn_multi when > 1, "
+                         "as for speculative verification against the compressed cache)")
     ap.add_argument("--no-shared-prefix", action="store_true",
                     help="decode a shared-prefix batch with spicy_decode_attn (every page per sequence)")
     return ap.parse_args()
@@ -87,9 +90,10 @@ def coarsen_alg_bytes(call, lengths: np.ndarray) -> int:
     return read + write
 
 
-def decode_alg_bytes(wl, lengths: np.ndarray) -> int:
+def decode_alg_bytes(wl, lengths: np.ndarray, q_tokens: int = 1) -> int:
     """Bytes the decode must move: every cache entry it attends to, once per
-    physical slot (the shared prefix is read from HBM once), plus Q, O, LSE."""
+    physical slot (the shared prefix is read from HBM once), plus Q, O, LSE of
+    every query token."""
     eb = elem_bytes(wl.dtype)
     used = {}
     for b in range(wl.B):
@@ -99,7 +103,7 @@ def decode_alg_bytes(wl, lengths: np.ndarray) -> int:
             used[p] = max(used.get(p, 0), min(16, L - 16 * lp))
     entries = sum(used.values()) * wl.H_kv
     per_entry = (2 * wl.d + 2) * eb
-    qol = wl.B * wl.H_q * (wl.d * eb + wl.d * 4 + 4)
+    qol = wl.B * q_tokens * wl.H_q * (wl.d * eb + wl.d * 4 + 4)
     return entries * per_entry + qol
 
 
@@ -159,7 +163,7 @@ def measured_traffic(workload: str):
     return table
 
 
-def cpu_baseline(wl, reps: int, policy: bool = False):
+def cpu_baseline(wl, reps: int, policy: bool = False, q_tokens: int = 1):
     """The oracle (plain C, double precision) on the host cores: one whole
     step for every sequence of the batch (with `policy`, the oracle's policy
     on the chunk first; then the per-step coarsen and the decode), setup calls
@@ -171,6 +175,10 @@ def cpu_baseline(wl, reps: int, policy: bool = False):
     lengths = None
     for call in wl.setup:
         lengths = oracle.coarsen(call, cache, threads=threads)
+    qm = None
+    if q_tokens > 1:
+        from coarse_grained_decode_amd import workloads as W
+        qm = W.query_tokens(wl, q_tokens)
     times = []
     for r in range(reps + 1):
         t0 = time.perf_counter()
@@ -182,16 +190,20 @@ def cpu_baseline(wl, reps: int, policy: bool = False):
             step = dataclasses.replace(c, seg_offsets=pr.seg_offsets, seq_seg_ptr=pr.seq_seg_ptr, mask=pr.mask)
         if step is not None:
             lengths = oracle.coarsen(step, cache, threads=threads)
-        oracle.decode(wl.q, wl.dtype, cache, wl.H_q, wl.page_table, lengths, threads=threads)
+        if q_tokens > 1:
+            oracle.decode_multi(qm, wl.dtype, cache, wl.page_table, lengths, threads=threads)
+        else:
+            oracle.decode(wl.q, wl.dtype, cache, wl.H_q, wl.page_table, lengths, threads=threads)
         dt = time.perf_counter() - t0
         if r > 0:
             times.append(dt)
         print(f"[bench] cpu oracle step {r}: {dt:.3f} s", file=sys.stderr, flush=True)
     med = statistics.median(times)
-    return dict(value=wl.B / med, unit="query-tokens/s", cores=threads, kind="oracle",
+    return dict(value=wl.B * q_tokens / med, unit="query-tokens/s", cores=threads, kind="oracle",
                 sample=f"one whole step of the same workload ({wl.B} sequences: "
                        f"{'policy (single thread) + ' if policy else ''}"
-                       f"{'per-step coarsen + ' if wl.step is not None else ''}decode), "
+                       f"{'per-step coarsen + ' if wl.step is not None else ''}decode"
+                       f"{f' of {q_tokens} query tokens per sequence' if q_tokens > 1 else ''}), "
                        f"median of {reps} after 1 warm-up, {med:.3f} s per step")
 
 
@@ -222,12 +234,13 @@ def decode_only(args, wl, dw):
     ev1.record()
     torch.cuda.synchronize()
     us = ev0.elapsed_time(ev1) * 1e3 / n
-    db = decode_alg_bytes(wl, lengths)
+    db = decode_alg_bytes(wl, lengths, dw.q_tokens)
     gbs = db / (us * 1e-6) / 1e9
     print(json.dumps({"mode": "decode-only", "workload": wl.name, "calls": n, "layers_rotated": L,
                       "cache_bytes": int(cache_bytes), "alg_bytes_per_call": int(db), "mean_call_us": round(us, 2),
                       "achieved_GBps": round(gbs, 1), "frac_of_8TBps": round(gbs / HBM_PEAK_GBS, 4),
-                      "query_tokens_per_s": round(wl.B / (us * 1e-6), 1), "decode_splits": dw.splits,
+                      "query_tokens_per_s": round(wl.B * dw.q_tokens / (us * 1e-6), 1),
+                      "query_tokens_per_seq": dw.q_tokens, "decode_splits": dw.splits,
                       "shared_prefix_pages": dw.shared_prefix_pages}), flush=True)
 
 
@@ -254,7 +267,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     dw = DeviceWorkload.of(wl, dev, meta=False, num_splits=args.splits, fill=None,
-                           use_shared_prefix=not args.no_shared_prefix)
+                           use_shared_prefix=not args.no_shared_prefix, q_tokens=args.query_tokens)
     dw.run_setup()
     torch.cuda.synchronize()
     # a step: the per-step coarsen call if the workload has one, else its whole
@@ -319,9 +332,10 @@ def main():
     policy_ms = statistics.mean(e[3].elapsed_time(e[0]) for e in evs) if policy is not None else None
     lengths = dw.lengths.cpu().numpy()
     cb = sum(coarsen_alg_bytes(c.call, c.lengths.cpu().numpy()) for c in step_calls)
-    db = decode_alg_bytes(wl, lengths)
+    db = decode_alg_bytes(wl, lengths, args.query_tokens)
 
-    traffic = measured_traffic(wl.name + ("_policy" if policy is not None else ""))
+    traffic = measured_traffic(wl.name + ("_policy" if policy is not None else "") +
+                               (f"_q{args.query_tokens}" if args.query_tokens > 1 else ""))
 
     def roof(nbytes, ms, kernels):
         gbs = nbytes / (ms * 1e-3) / 1e9
@@ -351,7 +365,7 @@ def main():
     ms_per_step = elapsed * 1e3 / args.steps
     out = {
         "metric": "compressed-KV decode query-tokens/s and achieved HBM GB/s (% of peak), 1 GPU",
-        "value": round(wl.B * args.steps / elapsed, 1),
+        "value": round(wl.B * args.query_tokens * args.steps / elapsed, 1),
         "unit": "query-tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -366,15 +380,16 @@ def main():
                    "num_q_heads": wl.H_q, "num_kv_heads": wl.H_kv, "head_dim": wl.d,
                    "decode_splits": dw.splits, "shared_prefix_pages": dw.shared_prefix_pages,
                    "cache_entries_per_seq_mean": float(lengths.mean()),
-                   "device_policy": policy is not None},
+                   "device_policy": policy is not None, "query_tokens_per_seq": args.query_tokens},
         "roofline": dominant,
         "roofline_other": other,
-        "decode_query_tokens_per_s": round(wl.B / (decode_ms * 1e-3), 1),
+        "decode_query_tokens_per_s": round(wl.B * args.query_tokens / (decode_ms * 1e-3), 1),
     }
     if policy is not None:
         out["roofline_policy"] = r_policy
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_reps, policy=policy is not None)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_reps, policy=policy is not None,
+                                           q_tokens=args.query_tokens)
     print(json.dumps(out), flush=True)
 
 

@@ -318,14 +318,19 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
         issue_loads();
     } else {
         blk -= a.prefix_blocks;
-        const int sgb = (a.priv_splits + kWavesPerBlock - 1) / kWavesPerBlock;
-        const int split = static_cast<int>(blk % sgb) * kWavesPerBlock + wave;
+        // a workgroup's wavefronts: kWavesPerBlock / wpt splits x wpt tiles of
+        // each, so the tiles of one split read its pages together (one L2)
+        const int wpt = a.priv_wpt;
+        const int spb = kWavesPerBlock / wpt;
+        const int sgb = (a.priv_splits + spb - 1) / spb;
+        const int ntg = (a.priv_tiles + wpt - 1) / wpt;
+        const int split = static_cast<int>(blk % sgb) * spb + wave / wpt;
         blk /= sgb;
-        const int tile = static_cast<int>(blk % a.priv_tiles);
-        blk /= a.priv_tiles;
+        const int tile = static_cast<int>(blk % ntg) * wpt + wave % wpt;
+        blk /= ntg;
         h = static_cast<int>(blk % H);
         const int64_t b = blk / H;
-        if (split >= a.priv_splits || b >= a.B) return;
+        if (split >= a.priv_splits || tile >= a.priv_tiles || b >= a.B) return;
         slot = a.prefix_splits + split;
         raw_len = a.lengths[b];
         p0 = a.page_begin + split * a.pages_per_split;
@@ -553,8 +558,11 @@ static spicy_status launch_decode_t(const DecodeArgs& a0, int dtype, hipStream_t
         a.prefix_tile_blocks = (tiles + kWavesPerBlock - 1) / kWavesPerBlock;
         const int64_t pb = static_cast<int64_t>(a.prefix_splits) * a.cache.H * a.prefix_tile_blocks;
         a.prefix_blocks = static_cast<int32_t>((pb + kXcds - 1) / kXcds * kXcds);
-        const int64_t sgb = (a.priv_splits + kWavesPerBlock - 1) / kWavesPerBlock;
-        const int64_t nblk = a.prefix_blocks + sgb * a.priv_tiles * a.cache.H * a.B;
+        a.priv_wpt = a.priv_tiles >= 3 ? 4 : a.priv_tiles;
+        const int64_t spb = kWavesPerBlock / a.priv_wpt;
+        const int64_t sgb = (a.priv_splits + spb - 1) / spb;
+        const int64_t ntg = (a.priv_tiles + a.priv_wpt - 1) / a.priv_wpt;
+        const int64_t nblk = a.prefix_blocks + sgb * ntg * a.cache.H * a.B;
         const int64_t gx = nblk < kMaxGridX ? nblk : kMaxGridX;
         const int64_t gy = (nblk + gx - 1) / gx;
         hipLaunchKernelGGL((decode_mfma_kernel<D, kNbuf>), dim3(static_cast<unsigned>(gx), static_cast<unsigned>(gy)),

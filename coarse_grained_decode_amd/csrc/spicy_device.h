@@ -203,6 +203,7 @@ struct DecodeArgs {
     int32_t prefix_tile_blocks;  // set by the launcher: workgroups per (chunk, KV head)
     int32_t n_q;               // query tokens per sequence (rows: (b * n_q + token) * H_q + head)
     int32_t priv_tiles;        // 16-row tiles of one (sequence, KV head): ceil(n_q * G / 16)
+    int32_t priv_wpt;          // set by the launcher: wavefronts of a workgroup on one split's tiles (1, 2, 4)
 };
 
 }  // namespace spicy

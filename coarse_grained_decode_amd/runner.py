@@ -16,8 +16,9 @@ import torch
 
 from . import (PagedCache, spicy_coarsen, spicy_coarsen_workspace_bytes, spicy_decode_attn,
                spicy_decode_attn_shared, spicy_decode_num_splits, spicy_decode_shared_workspace_bytes,
-               spicy_policy, spicy_policy_workspace_bytes, workspace)
-from .workloads import CoarsenCall, PolicySpec, Workload
+               spicy_decode_attn_multi, spicy_decode_multi_workspace_bytes, spicy_policy,
+               spicy_policy_workspace_bytes, workspace)
+from .workloads import CoarsenCall, PolicySpec, Workload, query_tokens
 
 
 def _tensor(a: np.ndarray, dtype: str | None, device) -> torch.Tensor:
@@ -128,23 +129,33 @@ class DeviceWorkload:
     dws: torch.Tensor
     shared_prefix_pages: int = 0
     lengths: torch.Tensor = field(default=None)
+    q_tokens: int = 1
 
     @staticmethod
     def of(wl: Workload, device="cuda", meta: bool = True, num_splits: int = 0,
-           fill: float | None = float("nan"), use_shared_prefix: bool = True) -> "DeviceWorkload":
+           fill: float | None = float("nan"), use_shared_prefix: bool = True,
+           q_tokens: int = 1) -> "DeviceWorkload":
+        """q_tokens > 1: every decode call is spicy_decode_attn_multi with that
+        many query tokens per sequence (workloads.query_tokens)."""
         device = torch.device(device)
         tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
         cache = PagedCache.empty(wl.num_pages, wl.H_kv, wl.d, tdt, device, meta=meta, fill=fill)
         setup = [DeviceCall.of(c, device) for c in wl.setup]
         step = DeviceCall.of(wl.step, device) if wl.step is not None else None
-        q = _tensor(wl.q, wl.dtype, device)
         table = _tensor(wl.page_table, None, device)
-        o = torch.empty(wl.B, wl.H_q, wl.d, dtype=torch.float32, device=device)
-        lse = torch.empty(wl.B, wl.H_q, dtype=torch.float32, device=device)
         P = wl.shared_prefix_pages if use_shared_prefix else 0
-        dws = workspace(spicy_decode_shared_workspace_bytes(wl.B, wl.H_q, wl.H_kv, wl.d, wl.max_pages, P,
-                                                            num_splits), device)
-        return DeviceWorkload(wl, device, cache, setup, step, q, table, o, lse, num_splits, dws, P)
+        if q_tokens == 1:
+            q = _tensor(wl.q, wl.dtype, device)
+            o = torch.empty(wl.B, wl.H_q, wl.d, dtype=torch.float32, device=device)
+            lse = torch.empty(wl.B, wl.H_q, dtype=torch.float32, device=device)
+        else:
+            q = _tensor(query_tokens(wl, q_tokens), wl.dtype, device)
+            o = torch.empty(wl.B, q_tokens, wl.H_q, wl.d, dtype=torch.float32, device=device)
+            lse = torch.empty(wl.B, q_tokens, wl.H_q, dtype=torch.float32, device=device)
+        dws = workspace(spicy_decode_multi_workspace_bytes(wl.B, q_tokens, wl.H_q, wl.H_kv, wl.d, wl.max_pages, P,
+                                                           num_splits), device)
+        return DeviceWorkload(wl, device, cache, setup, step, q, table, o, lse, num_splits, dws, P,
+                              q_tokens=q_tokens)
 
     def run_setup(self) -> None:
         for c in self.setup:
@@ -158,9 +169,13 @@ class DeviceWorkload:
 
     def decode(self, cache: PagedCache | None = None) -> None:
         """spicy_decode_attn, or spicy_decode_attn_shared when the batch
-        declares a shared prefix."""
+        declares a shared prefix, or spicy_decode_attn_multi with several
+        query tokens."""
         cache = self.cache if cache is None else cache
-        if self.shared_prefix_pages > 0:
+        if self.q_tokens > 1:
+            spicy_decode_attn_multi(cache, self.q, self.page_table, self.lengths, self.shared_prefix_pages,
+                                    self.o, self.lse, self.dws, self.num_splits)
+        elif self.shared_prefix_pages > 0:
             spicy_decode_attn_shared(cache, self.q, self.page_table, self.lengths, self.shared_prefix_pages,
                                      self.o, self.lse, self.dws, self.num_splits)
         else:
