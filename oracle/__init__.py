@@ -60,6 +60,12 @@ def lib():
             L.oracle_decode.restype = ctypes.c_int
             L.oracle_decode.argtypes = [ctypes.c_int, ctypes.c_int, i32, i32, i32, P, P, P, P, i32,
                                         P, i32, P, i32, P, P, i32, i32]
+            L.oracle_coarsen_diag.restype = ctypes.c_int
+            L.oracle_coarsen_diag.argtypes = [ctypes.c_int, ctypes.c_int, i32, i32, P, P, P, P, P, P, P,
+                                              i32, ctypes.c_double, P, P, P, P, P, i32, P, i32, P, P, i32, i32]
+            L.oracle_decode_diag.restype = ctypes.c_int
+            L.oracle_decode_diag.argtypes = [ctypes.c_int, ctypes.c_int, i32, i32, i32, P, P, P, P, P, i32,
+                                             P, i32, P, i32, P, P, i32, i32]
             L.oracle_bf16_round.restype = ctypes.c_uint16
             L.oracle_bf16_round.argtypes = [ctypes.c_double]
             L.oracle_bf16_value.restype = ctypes.c_double
@@ -107,7 +113,7 @@ class Cache:
     k, v [P, H, d/W, 16, W] (entry rows cut in chunks of W = min(32, d) dims),
     ab [P, H, 16, 2], meta [P, H, 16]."""
 
-    def __init__(self, store: str, num_pages: int, H_kv: int, d: int, fill: bool = True):
+    def __init__(self, store: str, num_pages: int, H_kv: int, d: int, fill: bool = True, diag: bool = False):
         self.store, self.num_pages, self.H_kv, self.d = store, num_pages, H_kv, d
         dt = NP[store]
         W = chunk_width(d)
@@ -115,8 +121,10 @@ class Cache:
         self.v = np.empty((num_pages, H_kv, d // W, PAGE, W), dtype=dt)
         self.ab = np.empty((num_pages, H_kv, PAGE, 2), dtype=dt)
         self.meta = np.zeros((num_pages, H_kv, PAGE), dtype=META_DTYPE)
+        # the diagonal closure's per-dimension variance sidecar, laid out like k
+        self.s2 = np.empty((num_pages, H_kv, d // W, PAGE, W), dtype=dt) if diag else None
         if fill:  # recognisable garbage so that unwritten slots never look valid
-            for a in (self.k, self.v, self.ab):
+            for a in (self.k, self.v, self.ab) + ((self.s2,) if diag else ()):
                 if store == "bf16":
                     a.fill(0x7FC1)
                 else:
@@ -125,7 +133,8 @@ class Cache:
 
 
 def coarsen(call, cache: Cache, in_dtype: str | None = None, threads: int | None = None) -> np.ndarray:
-    """Run oracle_coarsen for one CoarsenCall into `cache`; returns lengths_out."""
+    """Run oracle_coarsen for one CoarsenCall into `cache` (oracle_coarsen_diag
+    when the cache carries the diagonal-variance sidecar); returns lengths_out."""
     L = lib()
     in_dtype = in_dtype or call.dtype
     k = np.ascontiguousarray(call.k)
@@ -136,12 +145,15 @@ def coarsen(call, cache: Cache, in_dtype: str | None = None, threads: int | None
 
     def run(rng):
         b0, b1 = rng
-        rc = L.oracle_coarsen(DT[in_dtype], DT[cache.store], call.H_kv, call.d, _p(k), _p(v),
-                              _p(call.seq_offsets), _p(call.pos_base), _p(call.seg_offsets),
-                              _p(call.seq_seg_ptr), _p(call.mask), call.B, call.rope_base,
-                              _p(cache.k), _p(cache.v), _p(cache.ab), _p(cache.meta), cache.num_pages,
-                              _p(call.page_table), call.max_pages, _p(call.entry_start), _p(lengths),
-                              b0, b1)
+        head = (DT[in_dtype], DT[cache.store], call.H_kv, call.d, _p(k), _p(v),
+                _p(call.seq_offsets), _p(call.pos_base), _p(call.seg_offsets),
+                _p(call.seq_seg_ptr), _p(call.mask), call.B, call.rope_base,
+                _p(cache.k), _p(cache.v), _p(cache.ab), _p(cache.meta))
+        tail = (cache.num_pages, _p(call.page_table), call.max_pages, _p(call.entry_start), _p(lengths), b0, b1)
+        if cache.s2 is None:
+            rc = L.oracle_coarsen(*head, *tail)
+        else:
+            rc = L.oracle_coarsen_diag(*head, _p(cache.s2), *tail)
         rcs.append(rc)
 
     del args_fixed
@@ -158,7 +170,8 @@ def coarsen(call, cache: Cache, in_dtype: str | None = None, threads: int | None
 
 def decode(q: np.ndarray, q_dtype: str, cache: Cache, H_q: int, page_table: np.ndarray,
            lengths: np.ndarray, threads: int | None = None):
-    """Run oracle_decode; returns (o [B, H_q, d] float64, lse [B, H_q] float64)."""
+    """Run oracle_decode (oracle_decode_diag on a cache with the diagonal
+    sidecar); returns (o [B, H_q, d] float64, lse [B, H_q] float64)."""
     L = lib()
     q = np.ascontiguousarray(q)
     B = int(q.shape[0])
@@ -171,10 +184,12 @@ def decode(q: np.ndarray, q_dtype: str, cache: Cache, H_q: int, page_table: np.n
 
     def run(rng):
         b0, b1 = rng
-        rcs.append(L.oracle_decode(DT[q_dtype], DT[cache.store], H_q, cache.H_kv, d, _p(q),
-                                   _p(cache.k), _p(cache.v), _p(cache.ab), cache.num_pages,
-                                   _p(table), int(table.shape[1]), _p(lens), B,
-                                   _p(o), _p(lse), b0, b1))
+        head = (DT[q_dtype], DT[cache.store], H_q, cache.H_kv, d, _p(q), _p(cache.k), _p(cache.v), _p(cache.ab))
+        tail = (cache.num_pages, _p(table), int(table.shape[1]), _p(lens), B, _p(o), _p(lse), b0, b1)
+        if cache.s2 is None:
+            rcs.append(L.oracle_decode(*head, *tail))
+        else:
+            rcs.append(L.oracle_decode_diag(*head, _p(cache.s2), *tail))
 
     chunks = _chunks(B, threads or default_threads())
     if len(chunks) == 1:

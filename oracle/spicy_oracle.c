@@ -108,6 +108,7 @@ typedef struct {
     void *k, *v, *ab;
     oracle_meta* meta;
     const int32_t* table_row;
+    void* s2;               /* optional: per-dimension variance sidecar, layout of k */
 } cache_view;
 
 /* Offset of element (slot, i) inside a page-head block of 16 x d values:
@@ -127,7 +128,7 @@ static int head_dim_ok(int32_t d) { return d > 0 && (d < 32 || d % 32 == 0); }
 static int put_entry(const cache_view* c, int32_t h, int64_t e,
                      const double* key, const double* val,
                      double alpha, double beta,
-                     int32_t kind, int32_t mass, int64_t pos_sum) {
+                     int32_t kind, int32_t mass, int64_t pos_sum, const double* s2) {
     int64_t lp = e / PAGE;
     if (lp >= c->max_pages) return 3;
     int32_t P = c->table_row[lp];
@@ -137,6 +138,8 @@ static int put_entry(const cache_view* c, int32_t h, int64_t e,
     for (int32_t i = 0; i < c->d; ++i) {
         store_elem(c->dtype, c->k, ph * PAGE * (size_t)c->d + slot_elem(c->d, slot, i), key[i]);
         store_elem(c->dtype, c->v, ph * PAGE * (size_t)c->d + slot_elem(c->d, slot, i), val[i]);
+        if (c->s2)
+            store_elem(c->dtype, c->s2, ph * PAGE * (size_t)c->d + slot_elem(c->d, slot, i), s2 ? s2[i] : 0.0);
     }
     store_elem(c->dtype, c->ab, (ph * PAGE + (size_t)slot) * 2 + 0, alpha);
     store_elem(c->dtype, c->ab, (ph * PAGE + (size_t)slot) * 2 + 1, beta);
@@ -168,7 +171,7 @@ static int put_entry(const cache_view* c, int32_t h, int64_t e,
  * entries (alpha = -inf, zero key and value) up to that count, and the tail
  * of the last page touched is padded with nulls as well.
  * lengths_out[b] = entry_start[b] + max over heads of the entry count. */
-int oracle_coarsen(int in_dtype, int dtype, int32_t H_kv, int32_t d,
+static int coarsen_impl(int in_dtype, int dtype, int32_t H_kv, int32_t d,
                    const void* k_pre, const void* v,
                    const int32_t* seq_offsets, const int32_t* pos_base,
                    const int32_t* seg_offsets, const int32_t* seq_seg_ptr,
@@ -178,7 +181,7 @@ int oracle_coarsen(int in_dtype, int dtype, int32_t H_kv, int32_t d,
                    int32_t num_pages,
                    const int32_t* page_table, int32_t max_pages_per_seq,
                    const int32_t* entry_start, int32_t* lengths_out,
-                   int32_t b_begin, int32_t b_end) {
+                   int32_t b_begin, int32_t b_end, void* s2_pool) {
     if (dtype < 0 || dtype > 2 || in_dtype < 0 || in_dtype > 2) return 1;
     if (H_kv <= 0 || !head_dim_ok(d) || (d % 2) != 0 || B < 0) return 1;
     if (!k_pre || !v || !seq_offsets || !seg_offsets || !seq_seg_ptr || !protected_mask) return 1;
@@ -190,8 +193,11 @@ int oracle_coarsen(int in_dtype, int dtype, int32_t H_kv, int32_t d,
     double* val = malloc(sizeof(double) * (size_t)d);
     double* zero = calloc((size_t)d, sizeof(double));
     int64_t* total = malloc(sizeof(int64_t) * (size_t)H_kv);
-    if (!key || !rot || !val || !zero || !total) {
-        free(key); free(rot); free(val); free(zero); free(total);
+    double* s2v = malloc(sizeof(double) * (size_t)d);
+    double* kt = malloc(sizeof(double) * (size_t)d);
+    double* rkt = malloc(sizeof(double) * (size_t)d);
+    if (!key || !rot || !val || !zero || !total || !s2v || !kt || !rkt) {
+        free(key); free(rot); free(val); free(zero); free(total); free(s2v); free(kt); free(rkt);
         return 1;
     }
     int rc = 0;
@@ -199,7 +205,7 @@ int oracle_coarsen(int in_dtype, int dtype, int32_t H_kv, int32_t d,
     for (int32_t b = b_begin; b < b_end && rc == 0; ++b) {
         cache_view c = {dtype, H_kv, d, num_pages, max_pages_per_seq,
                         k_pool, v_pool, ab_pool, (oracle_meta*)meta,
-                        page_table + (size_t)b * (size_t)max_pages_per_seq};
+                        page_table + (size_t)b * (size_t)max_pages_per_seq, s2_pool};
         int32_t t0 = seq_offsets[b], t1 = seq_offsets[b + 1];
         int32_t s0 = seq_seg_ptr[b], s1 = seq_seg_ptr[b + 1];
         int64_t e0 = entry_start ? entry_start[b] : 0;
@@ -244,8 +250,27 @@ int oracle_coarsen(int in_dtype, int dtype, int32_t H_kv, int32_t d,
                     double sigma2 = ss / ((double)m * (double)d);
                     double tbar = (double)pos_sum / (double)m;
                     oracle_rope(rot, key, d, tbar, rope_base);
+                    if (s2_pool) {
+                        /* diagonal closure: per-dimension population variance
+                         * of the member keys rotated to the anchor, the frame
+                         * of the stored key (their mean is R(tbar) kbar) */
+                        for (int32_t i = 0; i < d; ++i) s2v[i] = 0.0;
+                        for (int32_t t = a; t < z; ++t) {
+                            if (protected_mask[(size_t)t * (size_t)H_kv + (size_t)h]) continue;
+                            for (int32_t i = 0; i < d; ++i) {
+                                size_t ix = ((size_t)t * (size_t)H_kv + (size_t)h) * (size_t)d + (size_t)i;
+                                kt[i] = load_elem(in_dtype, k_pre, ix);
+                            }
+                            oracle_rope(rkt, kt, d, tbar, rope_base);
+                            for (int32_t i = 0; i < d; ++i) {
+                                double dv = rkt[i] - rot[i];
+                                s2v[i] += dv * dv;
+                            }
+                        }
+                        for (int32_t i = 0; i < d; ++i) s2v[i] /= (double)m;
+                    }
                     rc = put_entry(&c, h, e, rot, val, log((double)m),
-                                   sigma2 / (2.0 * (double)d), 2, m, pos_sum);
+                                   sigma2 / (2.0 * (double)d), 2, m, pos_sum, s2_pool ? s2v : NULL);
                     ++e;
                 }
 
@@ -259,7 +284,7 @@ int oracle_coarsen(int in_dtype, int dtype, int32_t H_kv, int32_t d,
                         val[i] = load_elem(in_dtype, v, ix);
                     }
                     oracle_rope(rot, key, d, (double)p, rope_base);
-                    rc = put_entry(&c, h, e, rot, val, 0.0, 0.0, 1, 1, p);
+                    rc = put_entry(&c, h, e, rot, val, 0.0, 0.0, 1, 1, p, NULL);
                     ++e;
                 }
             }
@@ -273,12 +298,49 @@ int oracle_coarsen(int in_dtype, int dtype, int32_t H_kv, int32_t d,
         int64_t padded = (len + PAGE - 1) / PAGE * PAGE;
         for (int32_t h = 0; h < H_kv && rc == 0; ++h)
             for (int64_t e = e0 + total[h]; e < padded && rc == 0; ++e)
-                rc = put_entry(&c, h, e, zero, zero, -INFINITY, 0.0, 0, 0, 0);
+                rc = put_entry(&c, h, e, zero, zero, -INFINITY, 0.0, 0, 0, 0, NULL);
         if (rc) break;
         lengths_out[b] = (int32_t)len;
     }
-    free(key); free(rot); free(val); free(zero); free(total);
+    free(key); free(rot); free(val); free(zero); free(total); free(s2v); free(kt); free(rkt);
     return rc;
+}
+
+int oracle_coarsen(int in_dtype, int dtype, int32_t H_kv, int32_t d,
+                   const void* k_pre, const void* v,
+                   const int32_t* seq_offsets, const int32_t* pos_base,
+                   const int32_t* seg_offsets, const int32_t* seq_seg_ptr,
+                   const uint8_t* protected_mask,
+                   int32_t B, double rope_base,
+                   void* k_pool, void* v_pool, void* ab_pool, void* meta,
+                   int32_t num_pages,
+                   const int32_t* page_table, int32_t max_pages_per_seq,
+                   const int32_t* entry_start, int32_t* lengths_out,
+                   int32_t b_begin, int32_t b_end) {
+    return coarsen_impl(in_dtype, dtype, H_kv, d, k_pre, v, seq_offsets, pos_base, seg_offsets, seq_seg_ptr,
+                        protected_mask, B, rope_base, k_pool, v_pool, ab_pool, meta, num_pages, page_table,
+                        max_pages_per_seq, entry_start, lengths_out, b_begin, b_end, NULL);
+}
+
+/* The diagonal closure (SPICY-KV demo page, Claim 3: the sub-grid variance
+ * as a "diagonal vector"): oracle_coarsen that also stores, per entry, the
+ * per-dimension population variance of a macro-node's member keys rotated to
+ * its anchor into s2_pool (layout of k_pool); C-points and nulls store 0. */
+int oracle_coarsen_diag(int in_dtype, int dtype, int32_t H_kv, int32_t d,
+                        const void* k_pre, const void* v,
+                        const int32_t* seq_offsets, const int32_t* pos_base,
+                        const int32_t* seg_offsets, const int32_t* seq_seg_ptr,
+                        const uint8_t* protected_mask,
+                        int32_t B, double rope_base,
+                        void* k_pool, void* v_pool, void* ab_pool, void* meta, void* s2_pool,
+                        int32_t num_pages,
+                        const int32_t* page_table, int32_t max_pages_per_seq,
+                        const int32_t* entry_start, int32_t* lengths_out,
+                        int32_t b_begin, int32_t b_end) {
+    if (!s2_pool) return 1;
+    return coarsen_impl(in_dtype, dtype, H_kv, d, k_pre, v, seq_offsets, pos_base, seg_offsets, seq_seg_ptr,
+                        protected_mask, B, rope_base, k_pool, v_pool, ab_pool, meta, num_pages, page_table,
+                        max_pages_per_seq, entry_start, lengths_out, b_begin, b_end, s2_pool);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -293,14 +355,14 @@ int oracle_coarsen(int in_dtype, int dtype, int32_t H_kv, int32_t d,
  *   LSE = ln sum_e exp(s_e),   O = sum_e exp(s_e - LSE) v_e.
  * A null entry (alpha = -inf) has weight zero.  With no entry of non-zero
  * weight: LSE = -inf and O = 0.  o is [B][H_q][d], lse is [B][H_q]. */
-int oracle_decode(int q_dtype, int dtype, int32_t H_q, int32_t H_kv, int32_t d,
+static int decode_impl(int q_dtype, int dtype, int32_t H_q, int32_t H_kv, int32_t d,
                   const void* q,
                   const void* k_pool, const void* v_pool, const void* ab_pool,
                   int32_t num_pages,
                   const int32_t* page_table, int32_t max_pages_per_seq,
                   const int32_t* lengths, int32_t B,
                   double* o, double* lse,
-                  int32_t b_begin, int32_t b_end) {
+                  int32_t b_begin, int32_t b_end, const void* s2_pool) {
     if (dtype < 0 || dtype > 2 || q_dtype < 0 || q_dtype > 2) return 1;
     if (H_q <= 0 || H_kv <= 0 || !head_dim_ok(d) || (H_q % H_kv) != 0) return 1;
     if (!q || !k_pool || !v_pool || !ab_pool || !page_table || !lengths || !o || !lse) return 1;
@@ -346,7 +408,17 @@ int oracle_decode(int q_dtype, int dtype, int32_t H_q, int32_t H_kv, int32_t d,
                 for (int32_t i = 0; i < d; ++i)
                     dot += load_elem(q_dtype, q, qo + (size_t)i) *
                            load_elem(dtype, k_pool, ph * PAGE * (size_t)d + slot_elem(d, slot, i));
-                s[e] = dot / sqrt((double)d) + alpha + qn2 * beta;
+                double closure = qn2 * beta;
+                if (s2_pool) {
+                    /* diagonal closure: sum_i q_i^2 s2_i / (2 d) */
+                    double acc = 0.0;
+                    for (int32_t i = 0; i < d; ++i) {
+                        double qi = load_elem(q_dtype, q, qo + (size_t)i);
+                        acc += qi * qi * load_elem(dtype, s2_pool, ph * PAGE * (size_t)d + slot_elem(d, slot, i));
+                    }
+                    closure = acc / (2.0 * (double)d);
+                }
+                s[e] = dot / sqrt((double)d) + alpha + closure;
                 if (s[e] > smax) smax = s[e];
             }
             double* out = o + qo;
@@ -371,6 +443,35 @@ int oracle_decode(int q_dtype, int dtype, int32_t H_q, int32_t H_kv, int32_t d,
     }
     free(s);
     return 0;
+}
+
+int oracle_decode(int q_dtype, int dtype, int32_t H_q, int32_t H_kv, int32_t d,
+                  const void* q,
+                  const void* k_pool, const void* v_pool, const void* ab_pool,
+                  int32_t num_pages,
+                  const int32_t* page_table, int32_t max_pages_per_seq,
+                  const int32_t* lengths, int32_t B,
+                  double* o, double* lse,
+                  int32_t b_begin, int32_t b_end) {
+    return decode_impl(q_dtype, dtype, H_q, H_kv, d, q, k_pool, v_pool, ab_pool, num_pages, page_table,
+                       max_pages_per_seq, lengths, B, o, lse, b_begin, b_end, NULL);
+}
+
+/* The diagonal closure at decode: the logit's closure term is
+ * sum_i q_i^2 s2_i / (2 d) with the entry's per-dimension variance s2 (the
+ * Gaussian second cumulant of q . k / sqrt(d) for a diagonal covariance)
+ * instead of ||q||^2 beta; everything else as oracle_decode. */
+int oracle_decode_diag(int q_dtype, int dtype, int32_t H_q, int32_t H_kv, int32_t d,
+                       const void* q,
+                       const void* k_pool, const void* v_pool, const void* ab_pool, const void* s2_pool,
+                       int32_t num_pages,
+                       const int32_t* page_table, int32_t max_pages_per_seq,
+                       const int32_t* lengths, int32_t B,
+                       double* o, double* lse,
+                       int32_t b_begin, int32_t b_end) {
+    if (!s2_pool) return 1;
+    return decode_impl(q_dtype, dtype, H_q, H_kv, d, q, k_pool, v_pool, ab_pool, num_pages, page_table,
+                       max_pages_per_seq, lengths, B, o, lse, b_begin, b_end, s2_pool);
 }
 
 /* ------------------------------------------------------------------------

@@ -64,6 +64,30 @@ int oracle_decode(int q_dtype, int dtype, int32_t H_q, int32_t H_kv, int32_t d,
                   double* o, double* lse,
                   int32_t b_begin, int32_t b_end);
 
+/* The diagonal closure: coarsening also stores each entry's per-dimension
+ * variance (of a macro-node's member keys rotated to its anchor; 0 for
+ * C-points and nulls) into s2_pool, laid out like k_pool; decoding uses
+ * sum_i q_i^2 s2_i / (2 d) as the closure term. */
+int oracle_coarsen_diag(int in_dtype, int dtype, int32_t H_kv, int32_t d,
+                        const void* k_pre, const void* v,
+                        const int32_t* seq_offsets, const int32_t* pos_base,
+                        const int32_t* seg_offsets, const int32_t* seq_seg_ptr,
+                        const uint8_t* protected_mask,
+                        int32_t B, double rope_base,
+                        void* k_pool, void* v_pool, void* ab_pool, void* meta, void* s2_pool,
+                        int32_t num_pages,
+                        const int32_t* page_table, int32_t max_pages_per_seq,
+                        const int32_t* entry_start, int32_t* lengths_out,
+                        int32_t b_begin, int32_t b_end);
+int oracle_decode_diag(int q_dtype, int dtype, int32_t H_q, int32_t H_kv, int32_t d,
+                       const void* q,
+                       const void* k_pool, const void* v_pool, const void* ab_pool, const void* s2_pool,
+                       int32_t num_pages,
+                       const int32_t* page_table, int32_t max_pages_per_seq,
+                       const int32_t* lengths, int32_t B,
+                       double* o, double* lse,
+                       int32_t b_begin, int32_t b_end);
+
 uint16_t oracle_bf16_round(double x);
 double oracle_bf16_value(uint16_t bits);
 void oracle_rope(double* y, const double* x, int32_t d, double pos, double base);
