@@ -52,7 +52,7 @@ class _Cache(ctypes.Structure):
     _fields_ = [("dtype", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("num_pages", ctypes.c_int32),
                 ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
-                ("ab", ctypes.c_void_p), ("meta", ctypes.c_void_p)]
+                ("ab", ctypes.c_void_p), ("meta", ctypes.c_void_p), ("s2", ctypes.c_void_p)]
 
 
 def library_path() -> str:
@@ -130,21 +130,24 @@ class PagedCache:
     v    [num_pages, H_kv, d/32, 16, 32] value rows, the same way
     ab   [num_pages, H_kv, 16, 2]       (alpha, beta)
     meta [num_pages, H_kv, 16, 4] int32 {kind, mass, pos_sum lo, pos_sum hi} or None
+    s2   [num_pages, H_kv, d/32, 16, 32] per-dimension variance (diagonal closure) or None
     """
     k: torch.Tensor
     v: torch.Tensor
     ab: torch.Tensor
     meta: torch.Tensor | None
+    s2: torch.Tensor | None = None
 
     @staticmethod
     def empty(num_pages: int, H_kv: int, d: int, dtype: torch.dtype, device, meta: bool = True,
-              fill: float | None = None) -> "PagedCache":
+              fill: float | None = None, diag: bool = False) -> "PagedCache":
         mk = torch.empty if fill is None else (lambda *s, **kw: torch.full(s, fill, **kw))
         k = mk(num_pages, H_kv, d // 32, PAGE_SIZE, 32, dtype=dtype, device=device)
         v = mk(num_pages, H_kv, d // 32, PAGE_SIZE, 32, dtype=dtype, device=device)
         ab = mk(num_pages, H_kv, PAGE_SIZE, 2, dtype=dtype, device=device)
         mt = torch.zeros(num_pages, H_kv, PAGE_SIZE, 4, dtype=torch.int32, device=device) if meta else None
-        return PagedCache(k, v, ab, mt)
+        s2 = mk(num_pages, H_kv, d // 32, PAGE_SIZE, 32, dtype=dtype, device=device) if diag else None
+        return PagedCache(k, v, ab, mt, s2)
 
     @property
     def num_pages(self) -> int:
@@ -168,7 +171,7 @@ class PagedCache:
 
     def struct(self) -> _Cache:
         return _Cache(self.dtype_code, self.num_kv_heads, self.head_dim, self.num_pages,
-                      _ptr(self.k), _ptr(self.v), _ptr(self.ab), _ptr(self.meta))
+                      _ptr(self.k), _ptr(self.v), _ptr(self.ab), _ptr(self.meta), _ptr(self.s2))
 
 
 def spicy_coarsen_workspace_bytes(B: int, n_seg: int, total_tokens: int, num_kv_heads: int, head_dim: int,

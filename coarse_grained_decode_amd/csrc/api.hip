@@ -124,7 +124,7 @@ size_t spicy_coarsen_workspace_bytes(int32_t B, int32_t n_seg, int32_t total_tok
     const size_t nb = static_cast<size_t>(B);
     const size_t d = static_cast<size_t>(head_dim);
     return SPICY_WORKSPACE_HEADER + align_up(16 * ns) + align_up(8 * nh) + align_up(8 * items) + align_up(4 * nb) +
-           align_up(4 * nb * static_cast<size_t>(num_kv_heads)) + 2 * align_up(nh * d * elem) +
+           align_up(4 * nb * static_cast<size_t>(num_kv_heads)) + 3 * align_up(nh * d * elem) +
            align_up(nh * 2 * elem) + align_up(16 * nh);
 }
 
@@ -151,7 +151,8 @@ spicy_status spicy_coarsen(const spicy_cache* cache, const void* k_pre, const vo
         return SPICY_ERR_CAPACITY;
 
     spicy::CoarsenArgs a{};
-    a.cache = spicy::CacheArgs{cache->k, cache->v, cache->ab, cache->meta, cache->num_pages, cache->num_kv_heads};
+    a.cache = spicy::CacheArgs{cache->k, cache->v, cache->ab, cache->meta, cache->num_pages, cache->num_kv_heads,
+                               cache->s2};
     a.k_pre = k_pre;
     a.v = v;
     a.seq_offsets = seq_offsets;
@@ -184,6 +185,8 @@ spicy_status spicy_coarsen(const spicy_cache* cache, const void* k_pre, const vo
     a.stage_ab = ws + off;
     off += align_up(nh * 2 * elem);
     a.stage_meta = reinterpret_cast<int4*>(ws + off);
+    off += align_up(16 * nh);
+    a.stage_s2 = ws + off;
     a.total_tokens = total_tokens;
     a.n_seg = n_seg;
     a.B = B;
@@ -282,7 +285,8 @@ spicy_status spicy_decode_attn_multi(const spicy_cache* cache, const void* q, in
                                         num_q_tokens);
 
     spicy::DecodeArgs a{};
-    a.cache = spicy::CacheArgs{cache->k, cache->v, cache->ab, cache->meta, cache->num_pages, cache->num_kv_heads};
+    a.cache = spicy::CacheArgs{cache->k, cache->v, cache->ab, cache->meta, cache->num_pages, cache->num_kv_heads,
+                               cache->s2};
     a.q = q;
     a.page_table = page_table;
     a.lengths = lengths;

@@ -91,6 +91,15 @@ template <> struct Row8<uint16_t> {
         const uint32_t bits = (i & 1) ? (w & 0xFFFF0000u) : (w << 16);
         return static_cast<double>(__uint_as_float(bits));
     }
+    // the row held by lane (this lane xor P), P < 32 (a swizzle, no LDS access)
+    template <int P>
+    __device__ __forceinline__ Row8 lane_xor() const {
+        constexpr int pat = 0x1F | (P << 10);
+        Row8 r;
+        r.x = make_uint4(__builtin_amdgcn_ds_swizzle(x.x, pat), __builtin_amdgcn_ds_swizzle(x.y, pat),
+                         __builtin_amdgcn_ds_swizzle(x.z, pat), __builtin_amdgcn_ds_swizzle(x.w, pat));
+        return r;
+    }
 };
 template <> struct Row8<float> {
     float4 x, y;
@@ -111,6 +120,15 @@ template <> struct Row8<float> {
         return j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w;
     }
     __device__ __forceinline__ double f64(int i) const { return static_cast<double>(raw(i)); }
+    template <int P>
+    __device__ __forceinline__ Row8 lane_xor() const {
+        constexpr int pat = 0x1F | (P << 10);
+        auto sw = [](float f) { return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(f), pat)); };
+        Row8 r;
+        r.x = make_float4(sw(x.x), sw(x.y), sw(x.z), sw(x.w));
+        r.y = make_float4(sw(y.x), sw(y.y), sw(y.z), sw(y.w));
+        return r;
+    }
 };
 
 template <typename T> struct Pack8;
@@ -433,6 +451,19 @@ struct Lanes {
             theta[r] = a.theta[pair0 + r];
     }
 
+    // cos and sin of pos * theta for the rotary pairs of this lane's
+    // dimensions q and 4 + q (all lanes of the wave must call it together).
+    __device__ __forceinline__ void angle(double pos, int q, double& ca, double& sa, double& cb, double& sb) const {
+        double sq, cq;
+        sincos_f64(pos * theta[q], &sq, &cq);          // index (hi ? 4 : 0) + q
+        const double oc = __shfl_xor(cq, PARTNER);      // index (hi ? 0 : 4) + q
+        const double os = __shfl_xor(sq, PARTNER);
+        ca = hi_half ? oc : cq;
+        sa = hi_half ? os : sq;
+        cb = hi_half ? cq : oc;
+        sb = hi_half ? sq : os;
+    }
+
     // Rotate this lane's 8 key values to position pos (all lanes of the wave
     // must call it together: it exchanges sin/cos and partner values).  One
     // rotary pair index q at a time, to keep few double-precision values live.
@@ -478,7 +509,18 @@ __device__ __forceinline__ int32_t find_sequence(const CoarsenArgs& a, int32_t s
 // macro-node (mean key rotated to the mean position, mean value, alpha,
 // beta) written to the staging area at (segment, head).  Needs nothing from
 // the plan role, which runs at the same time.
-template <typename T, int D>
+//
+// DIAG (diagonal closure, SPICY-KV demo page, Claim 3: the sub-grid variance
+// as a diagonal vector): also the per-dimension variance of the member keys
+// rotated to the anchor tbar.  Rotation mixes only the dimensions of one
+// rotary pair (i, i + d/2), so with c, s the cosine and sine of tbar * theta_i
+// and the pair's pre-rotation variances and covariance,
+//     s2_i       = c^2 Var_i + s^2 Var_(i+d/2) - 2 c s Cov
+//     s2_(i+d/2) = s^2 Var_i + c^2 Var_(i+d/2) + 2 c s Cov;
+// one pass suffices: each lane also sums the product of its values with its
+// rotary partner's (exchanged lane to lane), exact in double precision for
+// bf16 inputs like the other sums.
+template <typename T, int D, bool DIAG>
 __device__ __forceinline__ void stream_segment(const CoarsenArgs& a, const Lanes<T, D>& L, int32_t s) {
     const int H = a.cache.H;
     // the segment bounds are the same for the whole wave: keep them in scalar registers
@@ -494,14 +536,15 @@ __device__ __forceinline__ void stream_segment(const CoarsenArgs& a, const Lanes
     // tokens): the per-token offset is a scalar, and reads past the segment's
     // end return zeros, which add nothing to the sums.  Positions are summed
     // relative to the segment's first token.
-    double sk[8], sq[8], sv[8];
+    constexpr int RING = kRing;
+    double sk[8], sq[8], sv[8], sx[8];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) sk[r] = sq[r] = sv[r] = 0.0;
+    for (int r = 0; r < 8; ++r) sk[r] = sq[r] = sv[r] = sx[r] = 0.0;
     int32_t m = 0;
     int64_t prel = 0;
     struct Block {
-        Row8<T> k[kRing], v[kRing];
-        uint8_t mk[kRing];
+        Row8<T> k[RING], v[RING];
+        uint8_t mk[RING];
     };
     Block A, Bk;
     constexpr uint32_t kRow = static_cast<uint32_t>(D * sizeof(T));      // one head's row
@@ -515,7 +558,7 @@ __device__ __forceinline__ void stream_segment(const CoarsenArgs& a, const Lanes
         const __amdgpu_buffer_rsrc_t rm = make_rsrc(a.mask + row0, static_cast<uint32_t>(wn * H));
         auto fetch = [&](Block& X, int32_t u0) {
 #pragma unroll
-            for (int u = 0; u < kRing; ++u) {
+            for (int u = 0; u < RING; ++u) {
                 const int so = (u0 + u) * static_cast<int>(tok_bytes);
                 Row8<T>::load_buf(X.k[u], rk, lane_off, so);
                 Row8<T>::load_buf(X.v[u], rv, lane_off, so);
@@ -523,11 +566,13 @@ __device__ __forceinline__ void stream_segment(const CoarsenArgs& a, const Lanes
             }
         };
         auto accumulate = [&](const Block& X, int32_t u0) {
-            const int nvalid = min(kRing, wn - u0);
+            const int nvalid = min(RING, wn - u0);
 #pragma unroll
-            for (int u = 0; u < kRing; ++u) {
+            for (int u = 0; u < RING; ++u) {
                 const bool take = (u < nvalid) && !X.mk[u];
                 const double w = take ? 1.0 : 0.0;
+                Row8<T> kp;
+                if constexpr (DIAG) kp = X.k[u].template lane_xor<Lanes<T, D>::PARTNER>();
 #pragma unroll
                 for (int r = 0; r < 8; ++r) {
                     const double x = X.k[u].f64(r);
@@ -535,6 +580,7 @@ __device__ __forceinline__ void stream_segment(const CoarsenArgs& a, const Lanes
                     sk[r] += xw;
                     sq[r] = fma(xw, x, sq[r]);
                     sv[r] = fma(X.v[u].f64(r), w, sv[r]);
+                    if constexpr (DIAG) sx[r] = fma(xw, kp.f64(r), sx[r]);
                 }
                 m += take ? 1 : 0;
                 prel += take ? static_cast<int64_t>(w0 - sa) + u0 + u : 0;
@@ -545,21 +591,21 @@ __device__ __forceinline__ void stream_segment(const CoarsenArgs& a, const Lanes
         // so each wait covers only the token about to be accumulated
         fetch(A, 0);
         __builtin_amdgcn_sched_barrier(0);
-        fetch(Bk, kRing);
+        fetch(Bk, RING);
         __builtin_amdgcn_sched_barrier(0);
         // steady state refills a block only while it starts inside the
         // window; the last two blocks are drained without refills
         int32_t u0 = 0;
-        for (; u0 + 2 * kRing < wn; u0 += 2 * kRing) {
+        for (; u0 + 2 * RING < wn; u0 += 2 * RING) {
             accumulate(A, u0);
-            fetch(A, u0 + 2 * kRing);
+            fetch(A, u0 + 2 * RING);
             __builtin_amdgcn_sched_barrier(0);
-            accumulate(Bk, u0 + kRing);
-            fetch(Bk, u0 + 3 * kRing);
+            accumulate(Bk, u0 + RING);
+            fetch(Bk, u0 + 3 * RING);
             __builtin_amdgcn_sched_barrier(0);
         }
         accumulate(A, u0);
-        if (u0 + kRing < wn) accumulate(Bk, u0 + kRing);
+        if (u0 + RING < wn) accumulate(Bk, u0 + RING);
     }
 
     // the macro-node (all lanes take part in the shuffles)
@@ -576,10 +622,36 @@ __device__ __forceinline__ void stream_segment(const CoarsenArgs& a, const Lanes
     const bool mine = L.active && m > 0;
     if (!__any(mine)) return;
     double y[8];
-    L.rope([&](int r) { return sk[r] / md; }, static_cast<double>(psum) / md, y);
+    const double tbar = static_cast<double>(psum) / md;
+    L.rope([&](int r) { return sk[r] / md; }, tbar, y);
+    double s2[8];
+    if constexpr (DIAG) {
+        constexpr int P = Lanes<T, D>::PARTNER;
+        double var[8], cov[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const double skp = __shfl_xor(sk[r], P);
+            var[r] = (sq[r] - sk[r] * sk[r] / md) / md;
+            cov[r] = (sx[r] - sk[r] * skp / md) / md;     // the same value in both partner lanes
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            double c[2] = {1.0, 1.0}, sn[2] = {0.0, 0.0};
+            if (L.rotate) L.angle(tbar, q, c[0], sn[0], c[1], sn[1]);
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int r = q + 4 * u;
+                const double varp = __shfl_xor(var[r], P);
+                const double c2s = 2.0 * c[u] * sn[u] * cov[r];
+                const double v2 = c[u] * c[u] * var[r] + sn[u] * sn[u] * varp + (L.hi_half ? c2s : -c2s);
+                s2[r] = v2 > 0.0 ? v2 : 0.0;
+            }
+        }
+    }
     if (!mine) return;
     const double sigma2 = (part > 0.0 ? part : 0.0) / (md * D);
     const int64_t idx = static_cast<int64_t>(s) * H + L.h;
+    if constexpr (DIAG) Pack8<T>::store(static_cast<T*>(a.stage_s2) + idx * D + L.d0, s2);
     Pack8<T>::store(static_cast<T*>(a.stage_k) + idx * D + L.d0, y);
     Store8<T>::store(static_cast<T*>(a.stage_v) + idx * D + L.d0,
                      [&](int r) { return Elem<T>::from_f64(sv[r] / md); });
@@ -594,7 +666,7 @@ __device__ __forceinline__ void stream_segment(const CoarsenArgs& a, const Lanes
 // coarsen_main: workgroups x < B plan sequence x (with head group 0); the
 // others are persistent streaming workgroups: wave w takes segments w,
 // w + W, w + 2W, ...  The two roles share nothing, so they run side by side.
-template <typename T, int D>
+template <typename T, int D, bool DIAG>
 __global__ __launch_bounds__(256, 2) void coarsen_main_kernel(CoarsenArgs a) {
     if (static_cast<int>(blockIdx.x) < a.B) {
         if (blockIdx.y == 0) plan_role<T, D>(a);
@@ -605,7 +677,7 @@ __global__ __launch_bounds__(256, 2) void coarsen_main_kernel(CoarsenArgs a) {
     const int32_t nstream = gridDim.x - a.B;
     const int32_t stride = nstream * (blockDim.x / kWave);
     for (int32_t s = (blockIdx.x - a.B) * (blockDim.x / kWave) + wave; s < a.n_seg; s += stride)
-        stream_segment<T, D>(a, L, s);
+        stream_segment<T, D, DIAG>(a, L, s);
 }
 
 // coarsen_cpoint: places every entry of sequence b, spread over workgroups
@@ -631,9 +703,10 @@ __device__ __forceinline__ void place_macro(const CoarsenArgs& a, int b, int32_t
     const int32_t owner = a.seg_desc[sg].x;
     const int2 hd = a.seg_head[idx];
     const int4 mt = a.stage_meta[idx];
-    Row8<T> kx, vx;
+    Row8<T> kx, vx, sx;
     kx.load(static_cast<const T*>(a.stage_k) + idx * D + d0);
     vx.load(static_cast<const T*>(a.stage_v) + idx * D + d0);
+    if (a.cache.s2) sx.load(static_cast<const T*>(a.stage_s2) + idx * D + d0);
     if (owner != b) return;                             // sequence failed its checks
     if (!(hd.y & 1)) return;                            // no F-token in this head
     if (mt.y != b || mt.x <= 0) {
@@ -648,6 +721,9 @@ __device__ __forceinline__ void place_macro(const CoarsenArgs& a, int b, int32_t
                      [&](int r) { return kx.raw(r); });
     Store8<T>::store(static_cast<T*>(a.cache.v) + ph * kPage * D + slot_elem(slot, d0),
                      [&](int r) { return vx.raw(r); });
+    if (a.cache.s2)
+        Store8<T>::store(static_cast<T*>(a.cache.s2) + ph * kPage * D + slot_elem(slot, d0),
+                         [&](int r) { return sx.raw(r); });
     if (j == 0) {
         const T* sab = static_cast<const T*>(a.stage_ab);
         T* abc = static_cast<T*>(a.cache.ab);
@@ -709,6 +785,8 @@ __device__ __forceinline__ void place_cpoint(const CoarsenArgs& a, int b, int2 i
     Pack8<T>::store(static_cast<T*>(a.cache.k) + ph * kPage * D + slot_elem(slot, d0), y);
     Store8<T>::store(static_cast<T*>(a.cache.v) + ph * kPage * D + slot_elem(slot, d0),
                      [&](int r) { return vx.raw(r); });
+    const double zero[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (a.cache.s2) Pack8<T>::store(static_cast<T*>(a.cache.s2) + ph * kPage * D + slot_elem(slot, d0), zero);
     if (j == 0) {
         T* abc = static_cast<T*>(a.cache.ab);
         abc[(ph * kPage + slot) * 2 + 0] = Elem<T>::from_f32(0.f);
@@ -727,6 +805,7 @@ __device__ __forceinline__ void place_null(const CoarsenArgs& a, int b, int h, i
     const double zero[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     Pack8<T>::store(static_cast<T*>(a.cache.k) + ph * kPage * D + slot_elem(slot, d0), zero);
     Pack8<T>::store(static_cast<T*>(a.cache.v) + ph * kPage * D + slot_elem(slot, d0), zero);
+    if (a.cache.s2) Pack8<T>::store(static_cast<T*>(a.cache.s2) + ph * kPage * D + slot_elem(slot, d0), zero);
     if (j == 0) {
         T* abc = static_cast<T*>(a.cache.ab);
         abc[(ph * kPage + slot) * 2 + 0] = Elem<T>::from_f32(-__builtin_huge_valf());
@@ -804,7 +883,10 @@ static spicy_status launch_coarsen_t(const CoarsenArgs& a, hipStream_t stream) {
     const int wpb = 4;
     const int nstream = max(1, min((a.n_seg + wpb - 1) / wpb, kResidentBlocks));
     dim3 grid(a.B + nstream, (a.cache.H + HW - 1) / HW);
-    hipLaunchKernelGGL((coarsen_main_kernel<T, D>), grid, dim3(wpb * kWave), 0, stream, a);
+    if (a.cache.s2)
+        hipLaunchKernelGGL((coarsen_main_kernel<T, D, true>), grid, dim3(wpb * kWave), 0, stream, a);
+    else
+        hipLaunchKernelGGL((coarsen_main_kernel<T, D, false>), grid, dim3(wpb * kWave), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return SPICY_ERR_HIP;
     // entries: about kResidentBlocks workgroups shared by the sequences
     const int cx = max(1, min(kCpointBlocksPerSeq, kResidentBlocks / max(a.B, 1)));

@@ -4,7 +4,9 @@
 // Logit (SPICY-KV demo page, section "2. FlashAttention-2/3 & PagedAttention
 // Online-Softmax Kernel Fusion"; Claim 3):
 //     s = q.k / sqrt(d) + alpha + |q|^2 * beta
-// followed by an ordinary online softmax.  Everything runs in base 2:
+// followed by an ordinary online softmax.  With the diagonal closure (the
+// cache carries a per-dimension variance s2 per entry) the last term is
+// sum_i q_i^2 s2_i / (2d) instead.  Everything runs in base 2:
 // s2 = s * log2(e), so p = exp2(s2 - m2) and LSE = ln2 * (m2 + log2 l).
 //
 // bf16 caches (decode_mfma_kernel).  A query "tile" is up to 16 query rows
@@ -23,6 +25,10 @@
 //       32-dim chunk becomes two V^T operand tiles through two MFMAs with
 //       0/1 selector matrices (exact), whose accumulator layout is the A
 //       operand layout the product needs.
+//   diagonal closure: C^T[16 entries x 16 rows] = S2_page . (Q^2)^T, the
+//       variance pages loaded like K; q^2 (16 significant bits) is split
+//       into two bf16 terms hi + lo that hold it exactly, so the product is
+//       d/16 MFMAs with fp32 accumulation of exact bf16 products.
 // One launch holds two kinds of workgroups:
 //   split-K: one wavefront per (sequence, KV head, split).  Its tile is the
 //       G = H_q / H_kv query heads of that KV head, and it prefetches its pages
@@ -75,18 +81,19 @@ __device__ __forceinline__ int32_t check_length(const DecodeArgs& a, int32_t len
 
 __device__ __forceinline__ int32_t checked_length(const DecodeArgs& a, int b) { return check_length(a, a.lengths[b]); }
 
-template <int D>
+template <int D, bool DIAG>
 struct PageRegs {
     bf16x8 k[D / 32];      // K rows: entry lane%16, dims 32i + 8(lane/16) .. +8
     bf16x8 v[D / 32];      // V rows, the same way
+    bf16x8 s2[DIAG ? D / 32 : 1];   // per-dimension variances, like K (DIAG only)
     bf16x8 ab;             // (alpha, beta) of entries 4(lane/16) .. +4
     bool ok;               // page id was valid (uniform)
 };
 
 // Load KV head h of physical page pid, or of page 0 when pid is invalid
 // (then r.ok is false and the page is skipped when processed).
-template <int D>
-__device__ __forceinline__ void load_page(const DecodeArgs& a, PageRegs<D>& r, int32_t pid, int h) {
+template <int D, bool DIAG>
+__device__ __forceinline__ void load_page(const DecodeArgs& a, PageRegs<D, DIAG>& r, int32_t pid, int h) {
     constexpr int KC = D / 32;
     const int lane = threadIdx.x % kWave;
     const int row = lane % 16, grp = lane / 16;
@@ -100,15 +107,21 @@ __device__ __forceinline__ void load_page(const DecodeArgs& a, PageRegs<D>& r, i
     const uint16_t* vp = static_cast<const uint16_t*>(a.cache.v) + ph * kPage * D + slot_elem(row, 8 * grp);
 #pragma unroll
     for (int i = 0; i < KC; ++i) r.v[i] = *reinterpret_cast<const bf16x8*>(vp + kPage * kChunk * i);
+    if constexpr (DIAG) {
+        const uint16_t* sp = static_cast<const uint16_t*>(a.cache.s2) + ph * kPage * D + slot_elem(row, 8 * grp);
+#pragma unroll
+        for (int i = 0; i < KC; ++i) r.s2[i] = *reinterpret_cast<const bf16x8*>(sp + kPage * kChunk * i);
+    }
     r.ab = *reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(a.cache.ab) + ph * kPage * 2 + 8 * grp);
 }
 
 // Online-softmax state of one query tile; lane l serves query row l%16.
-template <int D>
+template <int D, bool DIAG>
 struct Tile {
     static constexpr int KC = D / 32;
     static constexpr int NT = D / 16;
     bf16x8 q[KC];          // B operand of S^T = K Q^T: 8 dims of each 32-dim chunk
+    bf16x8 q2h[DIAG ? KC : 1], q2l[DIAG ? KC : 1];   // q^2 = hi + lo, the same layout (DIAG only)
     bf16x8 sel[2];         // B operands [I; 0] and [0; I] (32 x 16) that transpose V
     float c_beta;          // |q|^2 log2(e) of this lane's row
     int32_t len;           // entries of this row's sequence (0 for a padding row)
@@ -137,6 +150,12 @@ struct Tile {
             for (int j = 0; j < 8; ++j) {
                 const float x = static_cast<float>(q[i][j]);
                 n2 += x * x;
+                if constexpr (DIAG) {
+                    const float x2 = x * x;                         // exact: 16 significant bits
+                    const __bf16 hi = static_cast<__bf16>(x2);
+                    q2h[i][j] = hi;
+                    q2l[i][j] = static_cast<__bf16>(x2 - static_cast<float>(hi));   // exact remainder
+                }
             }
         }
         n2 += __shfl_xor(n2, 16);
@@ -163,20 +182,34 @@ struct Tile {
 
     // Fold logical page lp into the state.  A row's entries at or past its
     // length get weight zero; a page whose id was invalid is skipped.
-    __device__ __forceinline__ void process(const PageRegs<D>& r, int32_t lp) {
+    __device__ __forceinline__ void process(const PageRegs<D, DIAG>& r, int32_t lp) {
         if (!r.ok) return;
         const int grp = (threadIdx.x % kWave) / 16;
         const float c_dot = kLog2e / sqrtf(static_cast<float>(D));
         f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < KC; ++i) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.k[i], q[i], s, 0, 0, 0);
+        f32x4 cl = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (DIAG) {
+#pragma unroll
+            for (int i = 0; i < KC; ++i) {
+                cl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.s2[i], q2h[i], cl, 0, 0, 0);
+                cl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.s2[i], q2l[i], cl, 0, 0, 0);
+            }
+        }
         const int32_t ebase = lp * kPage + 4 * grp;
         float s2[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const float alpha = static_cast<float>(r.ab[2 * j]);
-            const float beta = static_cast<float>(r.ab[2 * j + 1]);
-            const float x = s[j] * c_dot + (alpha * kLog2e + beta * c_beta);
+            float x;
+            if constexpr (DIAG) {
+                constexpr float c_cl = kLog2e / (2.f * D);
+                x = s[j] * c_dot + (alpha * kLog2e + cl[j] * c_cl);
+            } else {
+                const float beta = static_cast<float>(r.ab[2 * j + 1]);
+                x = s[j] * c_dot + (alpha * kLog2e + beta * c_beta);
+            }
             s2[j] = (ebase + j < len) ? x : -__builtin_huge_valf();
         }
         float pm = fmaxf(fmaxf(s2[0], s2[1]), fmaxf(s2[2], s2[3]));
@@ -263,7 +296,7 @@ struct Tile {
 // (uniform).  Pages past the window's end load its last page again (every
 // load is unconditional, so each wait covers exactly one page); they are
 // never processed.
-template <int D, int NBUF>
+template <int D, int NBUF, bool DIAG>
 __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
     const int lane = threadIdx.x % kWave;
     const int wave = threadIdx.x / kWave;
@@ -283,7 +316,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
     // The query rows and the first window of page ids do not depend on the
     // length: each role issues their loads together with it, so the wavefront
     // waits one memory round trip before its first pages are requested.
-    Tile<D> T;
+    Tile<D, DIAG> T;
     int32_t ids;
     int64_t prow0;         // a valid query row of the wavefront's KV head
     auto issue_loads = [&]() {
@@ -353,12 +386,12 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
     // Pages go in windows of 64: one vector load brings the window's page ids
     // (lane i: page w0 + i) before its pipeline starts, so no wait inside the
     // pipeline depends on it.
-    PageRegs<D> buf[NBUF];
+    PageRegs<D, DIAG> buf[NBUF];
     for (int32_t w0 = p0; w0 < p1; w0 += kWave) {
         const int32_t w1 = min(w0 + kWave, p1);
         if (w0 != p0) ids = (w0 + lane < w1) ? table[w0 + lane] : 0;
-        auto load = [&](PageRegs<D>& r, int32_t lp) {
-            load_page<D>(a, r, __builtin_amdgcn_readlane(ids, min(lp, w1 - 1) - w0), h);
+        auto load = [&](PageRegs<D, DIAG>& r, int32_t lp) {
+            load_page<D, DIAG>(a, r, __builtin_amdgcn_readlane(ids, min(lp, w1 - 1) - w0), h);
         };
 #pragma unroll
         for (int i = 0; i < NBUF; ++i) load(buf[i], w0 + i);
@@ -428,6 +461,7 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
     n2 += __shfl_xor(n2, 2);
     const float c_dot = kLog2e / sqrtf(static_cast<float>(D));
     const float c_beta = n2 * kLog2e;
+    const float* s2pool = static_cast<const float*>(a.cache.s2);   // diagonal closure when set (uniform)
 
     const float* kpool = static_cast<const float*>(a.cache.k);
     const float* vpool = static_cast<const float*>(a.cache.v);
@@ -455,7 +489,17 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
         dot += __shfl_xor(dot, 2);
         const float alpha = abpool[(ph * kPage + ent) * 2 + 0];
         const float beta = abpool[(ph * kPage + ent) * 2 + 1];
-        float s2 = dot * c_dot + (alpha * kLog2e + beta * c_beta);
+        float closure = beta * c_beta;
+        if (s2pool) {
+            const float* srow = s2pool + ph * kPage * D + slot_elem(ent, qtr * QD);
+            float c = 0.f;
+#pragma unroll
+            for (int i = 0; i < QD; ++i) c += qv[i] * qv[i] * srow[i];
+            c += __shfl_xor(c, 1);
+            c += __shfl_xor(c, 2);
+            closure = c * (kLog2e / (2.f * D));
+        }
+        float s2 = dot * c_dot + (alpha * kLog2e + closure);
         if (lp * kPage + ent >= len) s2 = -__builtin_huge_valf();
         float pm = s2;
 #pragma unroll
@@ -547,6 +591,7 @@ __global__ __launch_bounds__(64) void combine_kernel(DecodeArgs a) {
 // ------------------------------------------------------------------ launch
 
 constexpr int kNbuf = 4;
+constexpr int kNbufDiag = 2;              // the variance pages add a third page-sized load
 constexpr int64_t kMaxGridX = 65536;
 
 template <int D>
@@ -565,8 +610,11 @@ static spicy_status launch_decode_t(const DecodeArgs& a0, int dtype, hipStream_t
         const int64_t nblk = a.prefix_blocks + sgb * ntg * a.cache.H * a.B;
         const int64_t gx = nblk < kMaxGridX ? nblk : kMaxGridX;
         const int64_t gy = (nblk + gx - 1) / gx;
-        hipLaunchKernelGGL((decode_mfma_kernel<D, kNbuf>), dim3(static_cast<unsigned>(gx), static_cast<unsigned>(gy)),
-                           dim3(kWavesPerBlock * kWave), 0, stream, a);
+        const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(gy));
+        if (a.cache.s2)
+            hipLaunchKernelGGL((decode_mfma_kernel<D, kNbufDiag, true>), grid, dim3(kWavesPerBlock * kWave), 0, stream, a);
+        else
+            hipLaunchKernelGGL((decode_mfma_kernel<D, kNbuf, false>), grid, dim3(kWavesPerBlock * kWave), 0, stream, a);
     } else {
         const int wpb = a.priv_splits < 4 ? a.priv_splits : 4;
         dim3 grid((a.priv_splits + wpb - 1) / wpb, a.H_q, a.B * a.n_q);

@@ -130,6 +130,7 @@ struct CacheArgs {
     void* meta;
     int32_t num_pages;
     int32_t H;      // KV heads
+    void* s2;       // diagonal closure: per-dimension variance, layout of k (nullptr: scalar closure)
 };
 
 // spicy_policy: per-step segments and protection mask from the chunk itself.
@@ -171,6 +172,7 @@ struct CoarsenArgs {
     void* stage_v;         // [n_seg][H][d]  macro-node values
     void* stage_ab;        // [n_seg][H][2]  alpha, beta
     int4* stage_meta;      // [n_seg][H]     {mass, sequence, pos_sum lo, pos_sum hi}
+    void* stage_s2;        // [n_seg][H][d]  macro-node per-dimension variances (diagonal closure)
     int32_t total_tokens;
     int32_t n_seg;
     int32_t B;

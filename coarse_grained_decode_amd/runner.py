@@ -134,12 +134,13 @@ class DeviceWorkload:
     @staticmethod
     def of(wl: Workload, device="cuda", meta: bool = True, num_splits: int = 0,
            fill: float | None = float("nan"), use_shared_prefix: bool = True,
-           q_tokens: int = 1) -> "DeviceWorkload":
+           q_tokens: int = 1, diag: bool = False) -> "DeviceWorkload":
         """q_tokens > 1: every decode call is spicy_decode_attn_multi with that
-        many query tokens per sequence (workloads.query_tokens)."""
+        many query tokens per sequence (workloads.query_tokens).  diag: the
+        cache carries the diagonal closure's per-dimension variances."""
         device = torch.device(device)
         tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
-        cache = PagedCache.empty(wl.num_pages, wl.H_kv, wl.d, tdt, device, meta=meta, fill=fill)
+        cache = PagedCache.empty(wl.num_pages, wl.H_kv, wl.d, tdt, device, meta=meta, fill=fill, diag=diag)
         setup = [DeviceCall.of(c, device) for c in wl.setup]
         step = DeviceCall.of(wl.step, device) if wl.step is not None else None
         table = _tensor(wl.page_table, None, device)

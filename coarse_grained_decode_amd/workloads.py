@@ -543,6 +543,20 @@ def random_decode_case(seed: int, *, B: int, H_q: int, H_kv: int, d: int, dtype:
                       _store(ab, dtype), table, lengths, _store(q, dtype), prefix_pages)
 
 
+def random_variances(c: DecodeCase, seed: int, scale: float = 2.0) -> np.ndarray:
+    """Per-dimension variances for a DecodeCase's entries (the diagonal
+    closure's sidecar, the cache's k layout, storage format): U(0, scale),
+    NaN wherever the case planted NaN (slots past a sequence's length)."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([5500 + seed, c.d])))
+    P, H = c.ab.shape[:2]
+    s2 = rng.uniform(0.0, scale, size=(P, H, PAGE, c.d)).astype(np.float32)
+    alpha = c.ab[..., 0]
+    if c.dtype == "bf16":
+        alpha = (alpha.astype(np.uint32) << 16).view(np.float32)
+    s2[np.isnan(alpha)] = np.nan
+    return _store(chunked(s2), c.dtype)
+
+
 @dataclasses.dataclass
 class PolicyCase:
     """Inputs of one spicy_policy call (host copies, bf16 bits)."""

@@ -51,11 +51,18 @@
  *   ab   : [num_pages][H_kv][16][2]   per entry (alpha, beta):
  *                                     alpha = ln(mass), beta = sigma^2/(2d);
  *                                     a null entry has alpha = -inf
+ *   s2   : optional (may be NULL), laid out like k: the diagonal closure
+ *          (SPICY-KV demo page, Claim 3, the sub-grid variance as a
+ *          diagonal vector).  Per entry, the per-dimension population
+ *          variance of the member keys rotated to the entry's anchor (the
+ *          frame of the stored key); 0 for C-points and nulls.  When set,
+ *          spicy_coarsen writes it and every decode entry point uses the
+ *          closure sum_i q_i^2 s2_i / (2d) in place of |q|^2 beta.
  *   meta : optional (may be NULL), [num_pages][H_kv][16] x 16 bytes
  *          { int32 kind; int32 mass; int64 pos_sum; }
  *          kind 0 = null, 1 = exact C-point, 2 = macro-node; pos_sum is the sum
  *          of the member positions (anchor = pos_sum / mass).
- *   Element type of k, v, ab: dtype (SPICY_BF16 or SPICY_F32).
+ *   Element type of k, v, ab, s2: dtype (SPICY_BF16 or SPICY_F32).
  *   Logical entry e of sequence b lives in page page_table[b*max_pages + e/16],
  *   slot e%16.
  */
@@ -103,6 +110,8 @@ typedef struct {
     void* v;                /* device                                        */
     void* ab;               /* device                                        */
     void* meta;             /* device or NULL                                */
+    void* s2;               /* device or NULL: the diagonal closure's
+                               per-dimension variance, laid out like k      */
 } spicy_cache;
 
 /* Workspace bytes spicy_coarsen needs for `n_seg` segments and
@@ -110,8 +119,8 @@ typedef struct {
  * `head_dim` dims in cache dtype `dtype` (header, per segment and per
  * (segment, head) plan, a list of C-point items of up to
  * total_tokens x num_kv_heads entries, per (sequence, head) counts, and one
- * macro-node per (segment, head) staged before it is placed).  0 for
- * invalid sizes. */
+ * macro-node per (segment, head), with its variance row, staged before it
+ * is placed).  0 for invalid sizes. */
 size_t spicy_coarsen_workspace_bytes(int32_t B, int32_t n_seg, int32_t total_tokens, int32_t num_kv_heads,
                                      int32_t head_dim, int32_t dtype);
 
@@ -147,6 +156,9 @@ size_t spicy_coarsen_workspace_bytes(int32_t B, int32_t n_seg, int32_t total_tok
  *   entry count.  RoPE uses the half-split pairing (i, i+d/2) with
  *   theta_i = rope_base^(-2i/d); rope_base <= 0 means no rotation.  Values are
  *   accumulated in double precision and rounded once, to nearest-even, on store.
+ *   With cache->s2 set, each macro-node also gets its per-dimension variance
+ *   s2 (see the cache layout), computed from one pass of sums (per dimension,
+ *   and per rotary pair the product sum), C-points and nulls get s2 = 0.
  * Workspace: device, >= spicy_coarsen_workspace_bytes(B, n_seg, total_tokens, H_kv, d, dtype) bytes,
  *   first int32 = sticky device error word (not cleared by the library).
  * Errors: SPICY_ERR_ARG (null required pointer, B < 0, n_seg < 0, bad dtype),
@@ -185,7 +197,8 @@ size_t spicy_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t num_
  * Output (device):
  *   o        float32 [B][num_q_heads][d]: sum_e softmax(s)_e v_e with
  *            s_e = q.k_e / sqrt(d) + alpha_e + |q|^2 beta_e (|q|^2 of the
- *            unscaled query).
+ *            unscaled query); with cache->s2 set the last term is
+ *            sum_i q_i^2 s2_e,i / (2d).
  *   lse      float32 [B][num_q_heads]: natural-log log-sum-exp of s; -inf (and
  *            o = 0) when a sequence has no entry of non-zero weight.
  * The entries of each (sequence, KV head) are split over up to

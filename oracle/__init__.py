@@ -217,11 +217,12 @@ def decode_multi(q: np.ndarray, q_dtype: str, cache: Cache, page_table: np.ndarr
     return o.reshape(B, n_q, H_q, d), lse.reshape(B, n_q, H_q)
 
 
-def run_workload(wl, store: str | None = None, threads: int | None = None):
+def run_workload(wl, store: str | None = None, threads: int | None = None, diag: bool = False):
     """Coarsen every call of a workload (setup calls, then the step call once)
-    into a fresh cache and decode its queries.  Returns (cache, lengths, o, lse)."""
+    into a fresh cache and decode its queries.  Returns (cache, lengths, o, lse).
+    diag: the cache carries the diagonal closure's variance sidecar."""
     store = store or wl.dtype
-    cache = Cache(store, wl.num_pages, wl.H_kv, wl.d)
+    cache = Cache(store, wl.num_pages, wl.H_kv, wl.d, diag=diag)
     lengths = None
     for call in wl.calls:
         lengths = coarsen(call, cache, threads=threads)

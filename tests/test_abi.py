@@ -78,7 +78,8 @@ def test_workspace_and_split_plan(lib):
     # header, 16 B per segment, 8 B per (segment, head), 8 B per C-point
     # item (at most tokens x heads), 4 B per sequence and per (sequence,
     # head), then staged macro-nodes: key and value rows, alpha/beta, 16 B
-    stage = 2 * up(40 * 128 * 2) + up(40 * 2 * 2) + up(40 * 16)
+    # of metadata, and the per-dimension variance row (diagonal closure)
+    stage = 3 * up(40 * 128 * 2) + up(40 * 2 * 2) + up(40 * 16)
     assert cgd.spicy_coarsen_workspace_bytes(2, 10, 100, 4, 128, 1) == 256 + 256 + 512 + 3328 + 256 + 256 + stage
     assert cgd.spicy_coarsen_workspace_bytes(-1, 10, 100, 4, 128, 1) == 0
     assert cgd.spicy_coarsen_workspace_bytes(2, 10, -1, 4, 128, 1) == 0
