@@ -59,6 +59,9 @@ def parse():
     ap.add_argument("--query-tokens", type=int, default=1,
                     help="query tokens per sequence in every decode call (spicy_decode_attn_multi when > 1, "
                          "as for speculative verification against the compressed cache)")
+    ap.add_argument("--diag-closure", action="store_true",
+                    help="the cache carries per-dimension variances (diagonal closure): coarsen writes them, "
+                         "decode reads them in place of the scalar beta")
     ap.add_argument("--no-shared-prefix", action="store_true",
                     help="decode a shared-prefix batch with spicy_decode_attn (every page per sequence)")
     return ap.parse_args()
@@ -75,10 +78,10 @@ def policy_alg_bytes(call, spec) -> int:
     return 2 * T * H * d * elem_bytes(call.dtype) + T * H + 4 * (call.B * spec.n_segments + 1) + 4 * (call.B + 1)
 
 
-def coarsen_alg_bytes(call, lengths: np.ndarray) -> int:
+def coarsen_alg_bytes(call, lengths: np.ndarray, diag: bool = False) -> int:
     """Bytes the coarsening must move: read K and V of every token and the
-    mask; write every entry it produces (key row, value column, alpha, beta),
-    null padding included."""
+    mask; write every entry it produces (key row, value column, alpha, beta,
+    and with `diag` the variance row), null padding included."""
     eb = elem_bytes(call.dtype)
     T, H, d = call.total_tokens, call.H_kv, call.d
     read = T * H * d * 2 * eb + T * H
@@ -86,14 +89,15 @@ def coarsen_alg_bytes(call, lengths: np.ndarray) -> int:
     for b in range(call.B):
         end = -(-int(lengths[b]) // 16) * 16
         written_entries += H * (end - int(call.entry_start[b]))
-    write = written_entries * (2 * d + 2) * eb + call.B * 4
+    write = written_entries * ((3 if diag else 2) * d + 2) * eb + call.B * 4
     return read + write
 
 
-def decode_alg_bytes(wl, lengths: np.ndarray, q_tokens: int = 1) -> int:
-    """Bytes the decode must move: every cache entry it attends to, once per
-    physical slot (the shared prefix is read from HBM once), plus Q, O, LSE of
-    every query token."""
+def decode_alg_bytes(wl, lengths: np.ndarray, q_tokens: int = 1, diag: bool = False) -> int:
+    """Bytes the decode must move: every cache entry it attends to (key,
+    value, alpha, beta, and with `diag` the variance row), once per physical
+    slot (the shared prefix is read from HBM once), plus Q, O, LSE of every
+    query token."""
     eb = elem_bytes(wl.dtype)
     used = {}
     for b in range(wl.B):
@@ -102,7 +106,7 @@ def decode_alg_bytes(wl, lengths: np.ndarray, q_tokens: int = 1) -> int:
             p = int(wl.page_table[b, lp])
             used[p] = max(used.get(p, 0), min(16, L - 16 * lp))
     entries = sum(used.values()) * wl.H_kv
-    per_entry = (2 * wl.d + 2) * eb
+    per_entry = ((3 if diag else 2) * wl.d + 2) * eb
     qol = wl.B * q_tokens * wl.H_q * (wl.d * eb + wl.d * 4 + 4)
     return entries * per_entry + qol
 
@@ -163,7 +167,7 @@ def measured_traffic(workload: str):
     return table
 
 
-def cpu_baseline(wl, reps: int, policy: bool = False, q_tokens: int = 1):
+def cpu_baseline(wl, reps: int, policy: bool = False, q_tokens: int = 1, diag: bool = False):
     """The oracle (plain C, double precision) on the host cores: one whole
     step for every sequence of the batch (with `policy`, the oracle's policy
     on the chunk first; then the per-step coarsen and the decode), setup calls
@@ -171,7 +175,7 @@ def cpu_baseline(wl, reps: int, policy: bool = False, q_tokens: int = 1):
     import dataclasses
     import oracle
     threads = oracle.default_threads()
-    cache = oracle.Cache(wl.dtype, wl.num_pages, wl.H_kv, wl.d, fill=False)
+    cache = oracle.Cache(wl.dtype, wl.num_pages, wl.H_kv, wl.d, fill=False, diag=diag)
     lengths = None
     for call in wl.setup:
         lengths = oracle.coarsen(call, cache, threads=threads)
@@ -203,7 +207,8 @@ def cpu_baseline(wl, reps: int, policy: bool = False, q_tokens: int = 1):
                 sample=f"one whole step of the same workload ({wl.B} sequences: "
                        f"{'policy (single thread) + ' if policy else ''}"
                        f"{'per-step coarsen + ' if wl.step is not None else ''}decode"
-                       f"{f' of {q_tokens} query tokens per sequence' if q_tokens > 1 else ''}), "
+                       f"{f' of {q_tokens} query tokens per sequence' if q_tokens > 1 else ''}"
+                       f"{', diagonal closure' if diag else ''}), "
                        f"median of {reps} after 1 warm-up, {med:.3f} s per step")
 
 
@@ -220,9 +225,11 @@ def decode_only(args, wl, dw):
         dw.lengths = dw.step.lengths
     torch.cuda.synchronize()
     lengths = dw.lengths.cpu().numpy()
-    cache_bytes = sum(t.numel() * t.element_size() for t in (dw.cache.k, dw.cache.v, dw.cache.ab))
+    parts = (dw.cache.k, dw.cache.v, dw.cache.ab) + ((dw.cache.s2,) if dw.cache.s2 is not None else ())
+    cache_bytes = sum(t.numel() * t.element_size() for t in parts)
     L = max(1, int(np.ceil(args.rotate_bytes / cache_bytes)))
-    copies = [PagedCache(dw.cache.k.clone(), dw.cache.v.clone(), dw.cache.ab.clone(), None) for _ in range(L)]
+    copies = [PagedCache(dw.cache.k.clone(), dw.cache.v.clone(), dw.cache.ab.clone(), None,
+                         dw.cache.s2.clone() if dw.cache.s2 is not None else None) for _ in range(L)]
     for i in range(args.warmup * L):
         dw.decode(copies[i % L])
     torch.cuda.synchronize()
@@ -234,7 +241,7 @@ def decode_only(args, wl, dw):
     ev1.record()
     torch.cuda.synchronize()
     us = ev0.elapsed_time(ev1) * 1e3 / n
-    db = decode_alg_bytes(wl, lengths, dw.q_tokens)
+    db = decode_alg_bytes(wl, lengths, dw.q_tokens, dw.cache.s2 is not None)
     gbs = db / (us * 1e-6) / 1e9
     print(json.dumps({"mode": "decode-only", "workload": wl.name, "calls": n, "layers_rotated": L,
                       "cache_bytes": int(cache_bytes), "alg_bytes_per_call": int(db), "mean_call_us": round(us, 2),
@@ -267,7 +274,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     dw = DeviceWorkload.of(wl, dev, meta=False, num_splits=args.splits, fill=None,
-                           use_shared_prefix=not args.no_shared_prefix, q_tokens=args.query_tokens)
+                           use_shared_prefix=not args.no_shared_prefix, q_tokens=args.query_tokens,
+                           diag=args.diag_closure)
     dw.run_setup()
     torch.cuda.synchronize()
     # a step: the per-step coarsen call if the workload has one, else its whole
@@ -331,11 +339,12 @@ def main():
     decode_ms = statistics.mean(e[1].elapsed_time(e[2]) for e in evs)
     policy_ms = statistics.mean(e[3].elapsed_time(e[0]) for e in evs) if policy is not None else None
     lengths = dw.lengths.cpu().numpy()
-    cb = sum(coarsen_alg_bytes(c.call, c.lengths.cpu().numpy()) for c in step_calls)
-    db = decode_alg_bytes(wl, lengths, args.query_tokens)
+    cb = sum(coarsen_alg_bytes(c.call, c.lengths.cpu().numpy(), args.diag_closure) for c in step_calls)
+    db = decode_alg_bytes(wl, lengths, args.query_tokens, args.diag_closure)
 
     traffic = measured_traffic(wl.name + ("_policy" if policy is not None else "") +
-                               (f"_q{args.query_tokens}" if args.query_tokens > 1 else ""))
+                               (f"_q{args.query_tokens}" if args.query_tokens > 1 else "") +
+                               ("_diag" if args.diag_closure else ""))
 
     def roof(nbytes, ms, kernels):
         gbs = nbytes / (ms * 1e-3) / 1e9
@@ -380,7 +389,8 @@ def main():
                    "num_q_heads": wl.H_q, "num_kv_heads": wl.H_kv, "head_dim": wl.d,
                    "decode_splits": dw.splits, "shared_prefix_pages": dw.shared_prefix_pages,
                    "cache_entries_per_seq_mean": float(lengths.mean()),
-                   "device_policy": policy is not None, "query_tokens_per_seq": args.query_tokens},
+                   "device_policy": policy is not None, "query_tokens_per_seq": args.query_tokens,
+                   "diag_closure": args.diag_closure},
         "roofline": dominant,
         "roofline_other": other,
         "decode_query_tokens_per_s": round(wl.B * args.query_tokens / (decode_ms * 1e-3), 1),
@@ -389,7 +399,7 @@ def main():
         out["roofline_policy"] = r_policy
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_reps, policy=policy is not None,
-                                           q_tokens=args.query_tokens)
+                                           q_tokens=args.query_tokens, diag=args.diag_closure)
     print(json.dumps(out), flush=True)
 
 

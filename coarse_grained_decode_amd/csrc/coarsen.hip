@@ -69,6 +69,22 @@ __device__ __forceinline__ int32_t entry_page(const CoarsenArgs& a, int b, int64
     return P;
 }
 
+// The value of lane (this lane xor P) through DPP moves (VALU only, no LDS
+// round trip): P = 8 is a rotation by 8 inside each 16-lane row; P = 4 is a
+// reversal inside each quad (lane xor 3) followed by a mirror inside each
+// half-row of 8 (lane xor 7).
+template <int P>
+__device__ __forceinline__ uint32_t dpp_xor(uint32_t v) {
+    static_assert(P == 4 || P == 8, "lane distance");
+    const int x = static_cast<int>(v);
+    if constexpr (P == 8) {
+        return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false));    // row_ror:8
+    } else {
+        const int r = __builtin_amdgcn_mov_dpp(x, 0x1B, 0xF, 0xF, false);                      // quad_perm [3,2,1,0]
+        return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(r, 0x141, 0xF, 0xF, false));     // row_half_mirror
+    }
+}
+
 // 8 consecutive elements of one row: a 16-byte (bf16) or 32-byte (fp32) load
 template <typename T> struct Row8;
 template <> struct Row8<uint16_t> {
@@ -91,13 +107,11 @@ template <> struct Row8<uint16_t> {
         const uint32_t bits = (i & 1) ? (w & 0xFFFF0000u) : (w << 16);
         return static_cast<double>(__uint_as_float(bits));
     }
-    // the row held by lane (this lane xor P), P < 32 (a swizzle, no LDS access)
+    // the row held by lane (this lane xor P), P = 4 or 8
     template <int P>
     __device__ __forceinline__ Row8 lane_xor() const {
-        constexpr int pat = 0x1F | (P << 10);
         Row8 r;
-        r.x = make_uint4(__builtin_amdgcn_ds_swizzle(x.x, pat), __builtin_amdgcn_ds_swizzle(x.y, pat),
-                         __builtin_amdgcn_ds_swizzle(x.z, pat), __builtin_amdgcn_ds_swizzle(x.w, pat));
+        r.x = make_uint4(dpp_xor<P>(x.x), dpp_xor<P>(x.y), dpp_xor<P>(x.z), dpp_xor<P>(x.w));
         return r;
     }
 };
@@ -122,8 +136,7 @@ template <> struct Row8<float> {
     __device__ __forceinline__ double f64(int i) const { return static_cast<double>(raw(i)); }
     template <int P>
     __device__ __forceinline__ Row8 lane_xor() const {
-        constexpr int pat = 0x1F | (P << 10);
-        auto sw = [](float f) { return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(f), pat)); };
+        auto sw = [](float f) { return __uint_as_float(dpp_xor<P>(__float_as_uint(f))); };
         Row8 r;
         r.x = make_float4(sw(x.x), sw(x.y), sw(x.z), sw(x.w));
         r.y = make_float4(sw(y.x), sw(y.y), sw(y.z), sw(y.w));

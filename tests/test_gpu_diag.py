@@ -45,6 +45,12 @@ def compare_s2(g, r, kind, store):
     return float((ulp == 0).mean()) if ulp.size else 1.0
 
 
+# the parity workloads, plus bf16 at d = 64 (rotary partners 4 lanes apart
+# instead of 8) with and without rotation
+DIAG_CASES = dict(CASES)
+DIAG_CASES["bf16_d64"] = lambda: W.qwen2_1p5b(d=64, B=4, T=4096)
+DIAG_CASES["bf16_d64_no_rope"] = lambda: W.qwen2_1p5b(d=64, B=3, T=3000, rope_base=0.0)
+
 _runs = {}
 
 
@@ -52,7 +58,7 @@ def run_diag(name):
     if name in _runs:
         return _runs[name]
     from coarse_grained_decode_amd.runner import DeviceWorkload
-    wl = CASES[name]()
+    wl = DIAG_CASES[name]()
     print(f"[diag case] {name}: B={wl.B} H_q={wl.H_q} H_kv={wl.H_kv} d={wl.d} pages={wl.num_pages}", flush=True)
     ref = oracle.run_workload(wl, diag=True)
     out = {}
@@ -68,7 +74,7 @@ def run_diag(name):
     return _runs[name]
 
 
-@pytest.mark.parametrize("name", list(CASES))
+@pytest.mark.parametrize("name", list(DIAG_CASES))
 def test_diag_coarsen_matches_oracle(name):
     _need_gpu()
     wl, out, (rcache, rlen, ro, rlse) = run_diag(name)
@@ -83,7 +89,7 @@ def test_diag_coarsen_matches_oracle(name):
     print(f"[{name}] s2 exact {frac:.6f}")
 
 
-@pytest.mark.parametrize("name", list(CASES))
+@pytest.mark.parametrize("name", list(DIAG_CASES))
 def test_diag_decode_end_to_end_matches_oracle(name):
     _need_gpu()
     wl, out, (rcache, rlen, ro, rlse) = run_diag(name)
