@@ -63,6 +63,9 @@ def lib():
             L.oracle_coarsen_diag.restype = ctypes.c_int
             L.oracle_coarsen_diag.argtypes = [ctypes.c_int, ctypes.c_int, i32, i32, P, P, P, P, P, P, P,
                                               i32, ctypes.c_double, P, P, P, P, P, i32, P, i32, P, P, i32, i32]
+            L.oracle_coarsen_weighted.restype = ctypes.c_int
+            L.oracle_coarsen_weighted.argtypes = [ctypes.c_int, ctypes.c_int, i32, i32, P, P, P, P, P, P, P, P,
+                                                  i32, ctypes.c_double, P, P, P, P, P, i32, P, i32, P, P, i32, i32]
             L.oracle_decode_diag.restype = ctypes.c_int
             L.oracle_decode_diag.argtypes = [ctypes.c_int, ctypes.c_int, i32, i32, i32, P, P, P, P, P, i32,
                                              P, i32, P, i32, P, P, i32, i32]
@@ -132,14 +135,19 @@ class Cache:
             self.meta["kind"] = -1
 
 
-def coarsen(call, cache: Cache, in_dtype: str | None = None, threads: int | None = None) -> np.ndarray:
+def coarsen(call, cache: Cache, in_dtype: str | None = None, threads: int | None = None,
+            token_weight: np.ndarray | None = None) -> np.ndarray:
     """Run oracle_coarsen for one CoarsenCall into `cache` (oracle_coarsen_diag
-    when the cache carries the diagonal-variance sidecar); returns lengths_out."""
+    when the cache carries the diagonal-variance sidecar; oracle_coarsen_weighted
+    with per-token weights, int64 [total_tokens]); returns lengths_out."""
     L = lib()
     in_dtype = in_dtype or call.dtype
     k = np.ascontiguousarray(call.k)
     v = np.ascontiguousarray(call.v)
     lengths = np.zeros(call.B, dtype=np.int32)
+    tw = None if token_weight is None else np.ascontiguousarray(token_weight, dtype=np.int64)
+    if tw is not None and tw.shape != (k.shape[0],):
+        raise ValueError("token_weight needs one int64 per token")
     args_fixed = dict()
     rcs = []
 
@@ -150,7 +158,9 @@ def coarsen(call, cache: Cache, in_dtype: str | None = None, threads: int | None
                 _p(call.seq_seg_ptr), _p(call.mask), call.B, call.rope_base,
                 _p(cache.k), _p(cache.v), _p(cache.ab), _p(cache.meta))
         tail = (cache.num_pages, _p(call.page_table), call.max_pages, _p(call.entry_start), _p(lengths), b0, b1)
-        if cache.s2 is None:
+        if tw is not None:
+            rc = L.oracle_coarsen_weighted(*head[:11], _p(tw), *head[11:], _p(cache.s2), *tail)
+        elif cache.s2 is None:
             rc = L.oracle_coarsen(*head, *tail)
         else:
             rc = L.oracle_coarsen_diag(*head, _p(cache.s2), *tail)

@@ -181,7 +181,7 @@ static int coarsen_impl(int in_dtype, int dtype, int32_t H_kv, int32_t d,
                    int32_t num_pages,
                    const int32_t* page_table, int32_t max_pages_per_seq,
                    const int32_t* entry_start, int32_t* lengths_out,
-                   int32_t b_begin, int32_t b_end, void* s2_pool) {
+                   int32_t b_begin, int32_t b_end, void* s2_pool, const int64_t* token_weight) {
     if (dtype < 0 || dtype > 2 || in_dtype < 0 || in_dtype > 2) return 1;
     if (H_kv <= 0 || !head_dim_ok(d) || (d % 2) != 0 || B < 0) return 1;
     if (!k_pre || !v || !seq_offsets || !seg_offsets || !seq_seg_ptr || !protected_mask) return 1;
@@ -196,8 +196,12 @@ static int coarsen_impl(int in_dtype, int dtype, int32_t H_kv, int32_t d,
     double* s2v = malloc(sizeof(double) * (size_t)d);
     double* kt = malloc(sizeof(double) * (size_t)d);
     double* rkt = malloc(sizeof(double) * (size_t)d);
-    if (!key || !rot || !val || !zero || !total || !s2v || !kt || !rkt) {
+    double* wkey = malloc(sizeof(double) * (size_t)d);
+    double* wval = malloc(sizeof(double) * (size_t)d);
+    double* rotm = malloc(sizeof(double) * (size_t)d);
+    if (!key || !rot || !val || !zero || !total || !s2v || !kt || !rkt || !wkey || !wval || !rotm) {
         free(key); free(rot); free(val); free(zero); free(total); free(s2v); free(kt); free(rkt);
+        free(wkey); free(wval); free(rotm);
         return 1;
     }
     int rc = 0;
@@ -224,19 +228,40 @@ static int coarsen_impl(int in_dtype, int dtype, int32_t H_kv, int32_t d,
                 /* F-points: the unprotected tokens of the segment. */
                 int32_t m = 0;
                 int64_t pos_sum = 0;
-                for (int32_t i = 0; i < d; ++i) { key[i] = 0.0; val[i] = 0.0; }
-                for (int32_t t = a; t < z; ++t) {
+                double wsum = 0.0;
+                for (int32_t i = 0; i < d; ++i) { key[i] = 0.0; val[i] = 0.0; wkey[i] = 0.0; wval[i] = 0.0; }
+                for (int32_t t = a; t < z && rc == 0; ++t) {
                     if (protected_mask[(size_t)t * (size_t)H_kv + (size_t)h]) continue;
                     ++m;
                     pos_sum += p0 + (t - t0);
+                    double w = 0.0;
+                    if (token_weight) {
+                        if (token_weight[t] < 0) { rc = 1; break; }
+                        w = (double)token_weight[t];
+                        wsum += w;
+                    }
                     for (int32_t i = 0; i < d; ++i) {
                         size_t ix = ((size_t)t * (size_t)H_kv + (size_t)h) * (size_t)d + (size_t)i;
-                        key[i] += load_elem(in_dtype, k_pre, ix);
-                        val[i] += load_elem(in_dtype, v, ix);
+                        double kx = load_elem(in_dtype, k_pre, ix), vx = load_elem(in_dtype, v, ix);
+                        key[i] += kx;
+                        val[i] += vx;
+                        if (token_weight) { wkey[i] += w * kx; wval[i] += w * vx; }
                     }
                 }
+                if (rc) break;
                 if (m > 0) {
                     for (int32_t i = 0; i < d; ++i) { key[i] /= (double)m; val[i] /= (double)m; }
+                    /* the representative: the plain mean, or with token weights
+                     * (the equal-variation page's implementation notes) the
+                     * weighted means sum w k / sum w and sum w v / sum w; a
+                     * segment whose weights are all zero keeps the plain mean */
+                    const double* rkey = key;
+                    const double* rval = val;
+                    if (token_weight && wsum > 0.0) {
+                        for (int32_t i = 0; i < d; ++i) { wkey[i] /= wsum; wval[i] /= wsum; }
+                        rkey = wkey;
+                        rval = wval;
+                    }
                     /* second pass: population variance around the mean */
                     double ss = 0.0;
                     for (int32_t t = a; t < z; ++t) {
@@ -249,11 +274,12 @@ static int coarsen_impl(int in_dtype, int dtype, int32_t H_kv, int32_t d,
                     }
                     double sigma2 = ss / ((double)m * (double)d);
                     double tbar = (double)pos_sum / (double)m;
-                    oracle_rope(rot, key, d, tbar, rope_base);
+                    oracle_rope(rot, rkey, d, tbar, rope_base);
                     if (s2_pool) {
                         /* diagonal closure: per-dimension population variance
                          * of the member keys rotated to the anchor, the frame
                          * of the stored key (their mean is R(tbar) kbar) */
+                        oracle_rope(rotm, key, d, tbar, rope_base);
                         for (int32_t i = 0; i < d; ++i) s2v[i] = 0.0;
                         for (int32_t t = a; t < z; ++t) {
                             if (protected_mask[(size_t)t * (size_t)H_kv + (size_t)h]) continue;
@@ -263,13 +289,13 @@ static int coarsen_impl(int in_dtype, int dtype, int32_t H_kv, int32_t d,
                             }
                             oracle_rope(rkt, kt, d, tbar, rope_base);
                             for (int32_t i = 0; i < d; ++i) {
-                                double dv = rkt[i] - rot[i];
+                                double dv = rkt[i] - rotm[i];
                                 s2v[i] += dv * dv;
                             }
                         }
                         for (int32_t i = 0; i < d; ++i) s2v[i] /= (double)m;
                     }
-                    rc = put_entry(&c, h, e, rot, val, log((double)m),
+                    rc = put_entry(&c, h, e, rot, rval, log((double)m),
                                    sigma2 / (2.0 * (double)d), 2, m, pos_sum, s2_pool ? s2v : NULL);
                     ++e;
                 }
@@ -303,6 +329,7 @@ static int coarsen_impl(int in_dtype, int dtype, int32_t H_kv, int32_t d,
         lengths_out[b] = (int32_t)len;
     }
     free(key); free(rot); free(val); free(zero); free(total); free(s2v); free(kt); free(rkt);
+    free(wkey); free(wval); free(rotm);
     return rc;
 }
 
@@ -319,7 +346,7 @@ int oracle_coarsen(int in_dtype, int dtype, int32_t H_kv, int32_t d,
                    int32_t b_begin, int32_t b_end) {
     return coarsen_impl(in_dtype, dtype, H_kv, d, k_pre, v, seq_offsets, pos_base, seg_offsets, seq_seg_ptr,
                         protected_mask, B, rope_base, k_pool, v_pool, ab_pool, meta, num_pages, page_table,
-                        max_pages_per_seq, entry_start, lengths_out, b_begin, b_end, NULL);
+                        max_pages_per_seq, entry_start, lengths_out, b_begin, b_end, NULL, NULL);
 }
 
 /* The diagonal closure (SPICY-KV demo page, Claim 3: the sub-grid variance
@@ -340,7 +367,31 @@ int oracle_coarsen_diag(int in_dtype, int dtype, int32_t H_kv, int32_t d,
     if (!s2_pool) return 1;
     return coarsen_impl(in_dtype, dtype, H_kv, d, k_pre, v, seq_offsets, pos_base, seg_offsets, seq_seg_ptr,
                         protected_mask, B, rope_base, k_pool, v_pool, ab_pool, meta, num_pages, page_table,
-                        max_pages_per_seq, entry_start, lengths_out, b_begin, b_end, s2_pool);
+                        max_pages_per_seq, entry_start, lengths_out, b_begin, b_end, s2_pool, NULL);
+}
+
+/* Variation-weighted representatives (Equal-Variation KV Cache page,
+ * implementation notes): oracle_coarsen (or oracle_coarsen_diag when s2_pool
+ * is not NULL) whose macro-node key and value are the token_weight-weighted
+ * means of its F-tokens, sum w k / sum w and sum w v / sum w (the plain means
+ * when every weight is zero).  token_weight: one non-negative integer per
+ * token (the per-token variation d_t), indexed like k_pre's tokens.  Mass,
+ * alpha, the anchor, beta and s2 stay the plain statistics. */
+int oracle_coarsen_weighted(int in_dtype, int dtype, int32_t H_kv, int32_t d,
+                            const void* k_pre, const void* v,
+                            const int32_t* seq_offsets, const int32_t* pos_base,
+                            const int32_t* seg_offsets, const int32_t* seq_seg_ptr,
+                            const uint8_t* protected_mask, const int64_t* token_weight,
+                            int32_t B, double rope_base,
+                            void* k_pool, void* v_pool, void* ab_pool, void* meta, void* s2_pool,
+                            int32_t num_pages,
+                            const int32_t* page_table, int32_t max_pages_per_seq,
+                            const int32_t* entry_start, int32_t* lengths_out,
+                            int32_t b_begin, int32_t b_end) {
+    if (!token_weight) return 1;
+    return coarsen_impl(in_dtype, dtype, H_kv, d, k_pre, v, seq_offsets, pos_base, seg_offsets, seq_seg_ptr,
+                        protected_mask, B, rope_base, k_pool, v_pool, ab_pool, meta, num_pages, page_table,
+                        max_pages_per_seq, entry_start, lengths_out, b_begin, b_end, s2_pool, token_weight);
 }
 
 /* ------------------------------------------------------------------------ */

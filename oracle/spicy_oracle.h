@@ -79,6 +79,20 @@ int oracle_coarsen_diag(int in_dtype, int dtype, int32_t H_kv, int32_t d,
                         const int32_t* page_table, int32_t max_pages_per_seq,
                         const int32_t* entry_start, int32_t* lengths_out,
                         int32_t b_begin, int32_t b_end);
+/* Variation-weighted representatives: the macro-node key and value are the
+ * token_weight-weighted means of its F-tokens (plain means when every weight
+ * is zero); everything else as oracle_coarsen.  s2_pool may be NULL. */
+int oracle_coarsen_weighted(int in_dtype, int dtype, int32_t H_kv, int32_t d,
+                            const void* k_pre, const void* v,
+                            const int32_t* seq_offsets, const int32_t* pos_base,
+                            const int32_t* seg_offsets, const int32_t* seq_seg_ptr,
+                            const uint8_t* protected_mask, const int64_t* token_weight,
+                            int32_t B, double rope_base,
+                            void* k_pool, void* v_pool, void* ab_pool, void* meta, void* s2_pool,
+                            int32_t num_pages,
+                            const int32_t* page_table, int32_t max_pages_per_seq,
+                            const int32_t* entry_start, int32_t* lengths_out,
+                            int32_t b_begin, int32_t b_end);
 int oracle_decode_diag(int q_dtype, int dtype, int32_t H_q, int32_t H_kv, int32_t d,
                        const void* q,
                        const void* k_pool, const void* v_pool, const void* ab_pool, const void* s2_pool,
