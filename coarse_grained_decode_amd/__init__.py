@@ -77,6 +77,9 @@ def load_library():
     L.spicy_coarsen.restype = ctypes.c_int
     L.spicy_coarsen.argtypes = [CP, P, P, i32, P, P, P, P, i32, P, i32, ctypes.c_double, P, i32,
                                 P, P, P, sz, P]
+    L.spicy_coarsen_weighted.restype = ctypes.c_int
+    L.spicy_coarsen_weighted.argtypes = [CP, P, P, i32, P, P, P, P, i32, P, P, i32, ctypes.c_double, P, i32,
+                                         P, P, P, sz, P]
     L.spicy_decode_num_splits.restype = i32
     L.spicy_decode_num_splits.argtypes = [i32, i32, i32, i32]
     L.spicy_decode_workspace_bytes.restype = sz
@@ -208,6 +211,28 @@ def spicy_coarsen(cache: PagedCache, k_pre, v, seq_offsets, pos_base, seg_offset
                          _ptr(lengths_out), _ptr(workspace), ws_bytes, _stream(stream))
     if rc != 0:
         raise SpicyError(rc, "spicy_coarsen")
+
+
+def spicy_coarsen_weighted(cache: PagedCache, k_pre, v, seq_offsets, pos_base, seg_offsets, seq_seg_ptr,
+                           protected_mask, token_weight, rope_base: float, page_table, entry_start, lengths_out,
+                           workspace, stream=None, *, total_tokens: int | None = None, n_seg: int | None = None,
+                           B: int | None = None, max_pages_per_seq: int | None = None) -> None:
+    """spicy_coarsen_weighted through the C ABI (see include/spicy.h);
+    token_weight: int64 device tensor [total_tokens]."""
+    L = load_library()
+    B = int(seq_offsets.shape[0] - 1) if B is None else B
+    n_seg = int(seg_offsets.shape[0] - 1) if n_seg is None else n_seg
+    total_tokens = int(k_pre.shape[0]) if total_tokens is None else total_tokens
+    max_pages = int(page_table.shape[-1]) if max_pages_per_seq is None else max_pages_per_seq
+    st = cache.struct()
+    ws_bytes = workspace.numel() * workspace.element_size() if isinstance(workspace, torch.Tensor) else 0
+    rc = L.spicy_coarsen_weighted(ctypes.byref(st), _ptr(k_pre), _ptr(v), total_tokens, _ptr(seq_offsets),
+                                  _ptr(pos_base), _ptr(seg_offsets), _ptr(seq_seg_ptr), n_seg,
+                                  _ptr(protected_mask), _ptr(token_weight), B, float(rope_base), _ptr(page_table),
+                                  max_pages, _ptr(entry_start), _ptr(lengths_out), _ptr(workspace), ws_bytes,
+                                  _stream(stream))
+    if rc != 0:
+        raise SpicyError(rc, "spicy_coarsen_weighted")
 
 
 def spicy_decode_attn(cache: PagedCache, q, page_table, lengths, o, lse, workspace,

@@ -128,13 +128,13 @@ size_t spicy_coarsen_workspace_bytes(int32_t B, int32_t n_seg, int32_t total_tok
            align_up(nh * 2 * elem) + align_up(16 * nh);
 }
 
-spicy_status spicy_coarsen(const spicy_cache* cache, const void* k_pre, const void* v,
-                           int32_t total_tokens, const int32_t* seq_offsets, const int32_t* pos_base,
-                           const int32_t* seg_offsets, const int32_t* seq_seg_ptr, int32_t n_seg,
-                           const uint8_t* protected_mask, int32_t B, double rope_base,
-                           const int32_t* page_table, int32_t max_pages_per_seq,
-                           const int32_t* entry_start, int32_t* lengths_out, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+static spicy_status coarsen_call(const spicy_cache* cache, const void* k_pre, const void* v,
+                                 int32_t total_tokens, const int32_t* seq_offsets, const int32_t* pos_base,
+                                 const int32_t* seg_offsets, const int32_t* seq_seg_ptr, int32_t n_seg,
+                                 const uint8_t* protected_mask, const int64_t* token_weight, int32_t B,
+                                 double rope_base, const int32_t* page_table, int32_t max_pages_per_seq,
+                                 const int32_t* entry_start, int32_t* lengths_out, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
     spicy_status st = check_cache(cache);
     if (st != SPICY_OK) return st;
     if (B < 0 || n_seg < 0 || total_tokens < 0) return SPICY_ERR_ARG;
@@ -162,6 +162,7 @@ spicy_status spicy_coarsen(const spicy_cache* cache, const void* k_pre, const vo
     a.mask = protected_mask;
     a.page_table = page_table;
     a.entry_start = entry_start;
+    a.token_weight = total_tokens > 0 ? token_weight : nullptr;
     a.lengths_out = lengths_out;
     char* ws = static_cast<char*>(workspace);
     a.err = reinterpret_cast<int32_t*>(ws);
@@ -195,6 +196,31 @@ spicy_status spicy_coarsen(const spicy_cache* cache, const void* k_pre, const vo
     for (int i = 0; i < cache->head_dim / 2; ++i)
         a.theta[i] = rope_base > 0.0 ? std::pow(rope_base, -2.0 * static_cast<double>(i) / cache->head_dim) : 0.0;
     return spicy::launch_coarsen(a, cache->dtype, cache->head_dim, static_cast<hipStream_t>(stream));
+}
+
+spicy_status spicy_coarsen(const spicy_cache* cache, const void* k_pre, const void* v,
+                           int32_t total_tokens, const int32_t* seq_offsets, const int32_t* pos_base,
+                           const int32_t* seg_offsets, const int32_t* seq_seg_ptr, int32_t n_seg,
+                           const uint8_t* protected_mask, int32_t B, double rope_base,
+                           const int32_t* page_table, int32_t max_pages_per_seq,
+                           const int32_t* entry_start, int32_t* lengths_out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    return coarsen_call(cache, k_pre, v, total_tokens, seq_offsets, pos_base, seg_offsets, seq_seg_ptr, n_seg,
+                        protected_mask, nullptr, B, rope_base, page_table, max_pages_per_seq, entry_start,
+                        lengths_out, workspace, workspace_bytes, stream);
+}
+
+spicy_status spicy_coarsen_weighted(const spicy_cache* cache, const void* k_pre, const void* v,
+                                    int32_t total_tokens, const int32_t* seq_offsets, const int32_t* pos_base,
+                                    const int32_t* seg_offsets, const int32_t* seq_seg_ptr, int32_t n_seg,
+                                    const uint8_t* protected_mask, const int64_t* token_weight, int32_t B,
+                                    double rope_base, const int32_t* page_table, int32_t max_pages_per_seq,
+                                    const int32_t* entry_start, int32_t* lengths_out, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+    if (total_tokens > 0 && B > 0 && !token_weight) return SPICY_ERR_ARG;
+    return coarsen_call(cache, k_pre, v, total_tokens, seq_offsets, pos_base, seg_offsets, seq_seg_ptr, n_seg,
+                        protected_mask, token_weight, B, rope_base, page_table, max_pages_per_seq, entry_start,
+                        lengths_out, workspace, workspace_bytes, stream);
 }
 
 int32_t spicy_decode_num_splits(int32_t B, int32_t num_kv_heads, int32_t max_pages_per_seq,

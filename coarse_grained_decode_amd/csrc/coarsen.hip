@@ -533,7 +533,14 @@ __device__ __forceinline__ int32_t find_sequence(const CoarsenArgs& a, int32_t s
 // one pass suffices: each lane also sums the product of its values with its
 // rotary partner's (exchanged lane to lane), exact in double precision for
 // bf16 inputs like the other sums.
-template <typename T, int D, bool DIAG>
+//
+// WEIGHTED (Equal-Variation KV Cache page, implementation notes: variation-
+// weighted representatives): the key and value of the macro-node are
+// sum w k / sum w and sum w v / sum w with one integer weight per token (the
+// plain means when every weight of the segment's F-tokens is zero); mass,
+// anchor, beta and s2 keep the plain sums.  w k is exact in double precision
+// for bf16 k and w < 2^45, and so are the sums while they stay below 2^53.
+template <typename T, int D, bool DIAG, bool WEIGHTED>
 __device__ __forceinline__ void stream_segment(const CoarsenArgs& a, const Lanes<T, D>& L, int32_t s) {
     const int H = a.cache.H;
     // the segment bounds are the same for the whole wave: keep them in scalar registers
@@ -550,14 +557,16 @@ __device__ __forceinline__ void stream_segment(const CoarsenArgs& a, const Lanes
     // end return zeros, which add nothing to the sums.  Positions are summed
     // relative to the segment's first token.
     constexpr int RING = kRing;
-    double sk[8], sq[8], sv[8], sx[8];
+    double sk[8], sq[8], sv[8], sx[8], skw[8], svw[8];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) sk[r] = sq[r] = sv[r] = sx[r] = 0.0;
+    for (int r = 0; r < 8; ++r) sk[r] = sq[r] = sv[r] = sx[r] = skw[r] = svw[r] = 0.0;
+    double sw = 0.0;
     int32_t m = 0;
     int64_t prel = 0;
     struct Block {
         Row8<T> k[RING], v[RING];
         uint8_t mk[RING];
+        int64_t wt[WEIGHTED ? RING : 1];
     };
     Block A, Bk;
     constexpr uint32_t kRow = static_cast<uint32_t>(D * sizeof(T));      // one head's row
@@ -569,6 +578,8 @@ __device__ __forceinline__ void stream_segment(const CoarsenArgs& a, const Lanes
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(kin + row0 * D, static_cast<uint32_t>(wn) * tok_bytes);
         const __amdgpu_buffer_rsrc_t rv = make_rsrc(vin + row0 * D, static_cast<uint32_t>(wn) * tok_bytes);
         const __amdgpu_buffer_rsrc_t rm = make_rsrc(a.mask + row0, static_cast<uint32_t>(wn * H));
+        const __amdgpu_buffer_rsrc_t rw =
+            make_rsrc(WEIGHTED ? a.token_weight + w0 : nullptr, WEIGHTED ? static_cast<uint32_t>(wn) * 8u : 0u);
         auto fetch = [&](Block& X, int32_t u0) {
 #pragma unroll
             for (int u = 0; u < RING; ++u) {
@@ -576,6 +587,12 @@ __device__ __forceinline__ void stream_segment(const CoarsenArgs& a, const Lanes
                 Row8<T>::load_buf(X.k[u], rk, lane_off, so);
                 Row8<T>::load_buf(X.v[u], rv, lane_off, so);
                 X.mk[u] = __builtin_amdgcn_raw_buffer_load_b8(rm, L.hh, (u0 + u) * H, 0);
+                if constexpr (WEIGHTED) {
+                    // the token's weight, the same for every lane (0 past the window)
+                    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+                    const u32x2 wv = __builtin_amdgcn_raw_buffer_load_b64(rw, 0, (u0 + u) * 8, 0);
+                    X.wt[u] = static_cast<int64_t>((static_cast<uint64_t>(wv[1]) << 32) | wv[0]);
+                }
             }
         };
         auto accumulate = [&](const Block& X, int32_t u0) {
@@ -584,16 +601,26 @@ __device__ __forceinline__ void stream_segment(const CoarsenArgs& a, const Lanes
             for (int u = 0; u < RING; ++u) {
                 const bool take = (u < nvalid) && !X.mk[u];
                 const double w = take ? 1.0 : 0.0;
+                double tw = 0.0;
+                if constexpr (WEIGHTED) {
+                    tw = take ? static_cast<double>(X.wt[u]) : 0.0;
+                    sw += tw;
+                }
                 Row8<T> kp;
                 if constexpr (DIAG) kp = X.k[u].template lane_xor<Lanes<T, D>::PARTNER>();
 #pragma unroll
                 for (int r = 0; r < 8; ++r) {
                     const double x = X.k[u].f64(r);
                     const double xw = x * w;
+                    const double vx = X.v[u].f64(r);
                     sk[r] += xw;
                     sq[r] = fma(xw, x, sq[r]);
-                    sv[r] = fma(X.v[u].f64(r), w, sv[r]);
+                    sv[r] = fma(vx, w, sv[r]);
                     if constexpr (DIAG) sx[r] = fma(xw, kp.f64(r), sx[r]);
+                    if constexpr (WEIGHTED) {
+                        skw[r] = fma(x, tw, skw[r]);
+                        svw[r] = fma(vx, tw, svw[r]);
+                    }
                 }
                 m += take ? 1 : 0;
                 prel += take ? static_cast<int64_t>(w0 - sa) + u0 + u : 0;
@@ -636,7 +663,9 @@ __device__ __forceinline__ void stream_segment(const CoarsenArgs& a, const Lanes
     if (!__any(mine)) return;
     double y[8];
     const double tbar = static_cast<double>(psum) / md;
-    L.rope([&](int r) { return sk[r] / md; }, tbar, y);
+    // the representative: weighted means when the segment's weights are not all zero
+    const bool wmean = WEIGHTED && sw > 0.0;
+    L.rope([&](int r) { return wmean ? skw[r] / sw : sk[r] / md; }, tbar, y);
     double s2[8];
     if constexpr (DIAG) {
         constexpr int P = Lanes<T, D>::PARTNER;
@@ -667,7 +696,7 @@ __device__ __forceinline__ void stream_segment(const CoarsenArgs& a, const Lanes
     if constexpr (DIAG) Pack8<T>::store(static_cast<T*>(a.stage_s2) + idx * D + L.d0, s2);
     Pack8<T>::store(static_cast<T*>(a.stage_k) + idx * D + L.d0, y);
     Store8<T>::store(static_cast<T*>(a.stage_v) + idx * D + L.d0,
-                     [&](int r) { return Elem<T>::from_f64(sv[r] / md); });
+                     [&](int r) { return Elem<T>::from_f64(wmean ? svw[r] / sw : sv[r] / md); });
     if (L.j == 0) {
         T* ab = static_cast<T*>(a.stage_ab);
         ab[idx * 2 + 0] = Elem<T>::from_f64(log(md));
@@ -679,7 +708,7 @@ __device__ __forceinline__ void stream_segment(const CoarsenArgs& a, const Lanes
 // coarsen_main: workgroups x < B plan sequence x (with head group 0); the
 // others are persistent streaming workgroups: wave w takes segments w,
 // w + W, w + 2W, ...  The two roles share nothing, so they run side by side.
-template <typename T, int D, bool DIAG>
+template <typename T, int D, bool DIAG, bool WEIGHTED>
 __global__ __launch_bounds__(256, 2) void coarsen_main_kernel(CoarsenArgs a) {
     if (static_cast<int>(blockIdx.x) < a.B) {
         if (blockIdx.y == 0) plan_role<T, D>(a);
@@ -690,7 +719,7 @@ __global__ __launch_bounds__(256, 2) void coarsen_main_kernel(CoarsenArgs a) {
     const int32_t nstream = gridDim.x - a.B;
     const int32_t stride = nstream * (blockDim.x / kWave);
     for (int32_t s = (blockIdx.x - a.B) * (blockDim.x / kWave) + wave; s < a.n_seg; s += stride)
-        stream_segment<T, D, DIAG>(a, L, s);
+        stream_segment<T, D, DIAG, WEIGHTED>(a, L, s);
 }
 
 // coarsen_cpoint: places every entry of sequence b, spread over workgroups
@@ -896,10 +925,15 @@ static spicy_status launch_coarsen_t(const CoarsenArgs& a, hipStream_t stream) {
     const int wpb = 4;
     const int nstream = max(1, min((a.n_seg + wpb - 1) / wpb, kResidentBlocks));
     dim3 grid(a.B + nstream, (a.cache.H + HW - 1) / HW);
-    if (a.cache.s2)
-        hipLaunchKernelGGL((coarsen_main_kernel<T, D, true>), grid, dim3(wpb * kWave), 0, stream, a);
+    const dim3 block(wpb * kWave);
+    if (a.cache.s2 && a.token_weight)
+        hipLaunchKernelGGL((coarsen_main_kernel<T, D, true, true>), grid, block, 0, stream, a);
+    else if (a.cache.s2)
+        hipLaunchKernelGGL((coarsen_main_kernel<T, D, true, false>), grid, block, 0, stream, a);
+    else if (a.token_weight)
+        hipLaunchKernelGGL((coarsen_main_kernel<T, D, false, true>), grid, block, 0, stream, a);
     else
-        hipLaunchKernelGGL((coarsen_main_kernel<T, D, false>), grid, dim3(wpb * kWave), 0, stream, a);
+        hipLaunchKernelGGL((coarsen_main_kernel<T, D, false, false>), grid, block, 0, stream, a);
     if (hipGetLastError() != hipSuccess) return SPICY_ERR_HIP;
     // entries: about kResidentBlocks workgroups shared by the sequences
     const int cx = max(1, min(kCpointBlocksPerSeq, kResidentBlocks / max(a.B, 1)));

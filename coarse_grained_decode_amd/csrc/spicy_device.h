@@ -160,6 +160,7 @@ struct CoarsenArgs {
     const uint8_t* mask;
     const int32_t* page_table;
     const int32_t* entry_start;
+    const int64_t* token_weight;   // [total_tokens] or null: weights of the representatives
     int32_t* lengths_out;
     int32_t* err;          // workspace header word
     int4* seg_desc;        // [n_seg]     {sequence (-1 = skip), first token, end token, position offset}

@@ -14,7 +14,7 @@ from typing import List, Optional
 import numpy as np
 import torch
 
-from . import (PagedCache, spicy_coarsen, spicy_coarsen_workspace_bytes, spicy_decode_attn,
+from . import (PagedCache, spicy_coarsen, spicy_coarsen_weighted, spicy_coarsen_workspace_bytes, spicy_decode_attn,
                spicy_decode_attn_shared, spicy_decode_num_splits, spicy_decode_shared_workspace_bytes,
                spicy_decode_attn_multi, spicy_decode_multi_workspace_bytes, spicy_policy,
                spicy_policy_workspace_bytes, workspace)
@@ -42,6 +42,7 @@ class DeviceCall:
     entry_start: torch.Tensor
     lengths: torch.Tensor
     ws: torch.Tensor
+    token_weight: Optional[torch.Tensor] = None   # int64 [total_tokens]: spicy_coarsen_weighted
 
     @staticmethod
     def of(call: CoarsenCall, device) -> "DeviceCall":
@@ -59,10 +60,15 @@ class DeviceCall:
 
     def run(self, cache: PagedCache, stream=None) -> None:
         c = self.call
-        spicy_coarsen(cache, self.k, self.v, self.seq_offsets, self.pos_base, self.seg_offsets,
-                      self.seq_seg_ptr, self.mask, c.rope_base, self.page_table, self.entry_start,
-                      self.lengths, self.ws, stream, total_tokens=c.total_tokens, n_seg=c.n_seg, B=c.B,
-                      max_pages_per_seq=c.max_pages)
+        kw = dict(total_tokens=c.total_tokens, n_seg=c.n_seg, B=c.B, max_pages_per_seq=c.max_pages)
+        if self.token_weight is None:
+            spicy_coarsen(cache, self.k, self.v, self.seq_offsets, self.pos_base, self.seg_offsets,
+                          self.seq_seg_ptr, self.mask, c.rope_base, self.page_table, self.entry_start,
+                          self.lengths, self.ws, stream, **kw)
+        else:
+            spicy_coarsen_weighted(cache, self.k, self.v, self.seq_offsets, self.pos_base, self.seg_offsets,
+                                   self.seq_seg_ptr, self.mask, self.token_weight, c.rope_base, self.page_table,
+                                   self.entry_start, self.lengths, self.ws, stream, **kw)
 
     @property
     def input_bytes(self) -> int:
@@ -101,8 +107,16 @@ class DevicePolicy:
                      sp.n_landmarks, sp.sink, sp.recent, self.seg_offsets, self.seq_seg_ptr, self.mask, self.ws,
                      stream, B=step.call.B, total_tokens=step.call.total_tokens)
 
-    def feed(self, step: "DeviceCall", device) -> "DeviceCall":
-        """The step call reading this policy's outputs (N slots per sequence)."""
+    @property
+    def variation(self) -> torch.Tensor:
+        """d_t (int64 [total_tokens]) as spicy_policy leaves it in its workspace."""
+        T = self.mask.shape[0]
+        return self.ws.view(torch.uint8)[256:256 + 8 * T].view(torch.int64)
+
+    def feed(self, step: "DeviceCall", device, weighted: bool = False) -> "DeviceCall":
+        """The step call reading this policy's outputs (N slots per sequence);
+        weighted: spicy_coarsen_weighted with the policy's variation d_t as
+        the token weights."""
         c = step.call
         B, N = c.B, self.spec.n_segments
         shaped = dataclasses.replace(c, seg_offsets=np.zeros(B * N + 1, dtype=np.int32),
@@ -111,7 +125,8 @@ class DevicePolicy:
             step, call=shaped, seg_offsets=self.seg_offsets, seq_seg_ptr=self.seq_seg_ptr, mask=self.mask,
             lengths=torch.zeros(B, dtype=torch.int32, device=device),
             ws=workspace(spicy_coarsen_workspace_bytes(B, B * N, c.total_tokens, c.H_kv, c.d,
-                                                       1 if c.dtype == "bf16" else 0), device))
+                                                       1 if c.dtype == "bf16" else 0), device),
+            token_weight=self.variation if weighted else None)
 
 
 @dataclass

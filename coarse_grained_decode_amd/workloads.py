@@ -543,6 +543,19 @@ def random_decode_case(seed: int, *, B: int, H_q: int, H_kv: int, d: int, dtype:
                       _store(ab, dtype), table, lengths, _store(q, dtype), prefix_pages)
 
 
+def token_weights(call: "CoarsenCall", seed: int, hi: int = 1 << 20) -> np.ndarray:
+    """Per-token integer weights for a coarsen call (int64 [total_tokens]):
+    U[0, hi), a fifth of them 0, and every token of every 7th segment 0 (so
+    some macro-nodes fall back to the plain mean)."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([5700 + seed, call.total_tokens])))
+    w = rng.integers(0, hi, size=call.total_tokens, dtype=np.int64)
+    w[rng.random(call.total_tokens) < 0.2] = 0
+    so = np.asarray(call.seg_offsets)
+    for s in range(0, len(so) - 1, 7):
+        w[so[s]:so[s + 1]] = 0
+    return w
+
+
 def random_variances(c: DecodeCase, seed: int, scale: float = 2.0) -> np.ndarray:
     """Per-dimension variances for a DecodeCase's entries (the diagonal
     closure's sidecar, the cache's k layout, storage format): U(0, scale),

@@ -174,6 +174,35 @@ spicy_status spicy_coarsen(const spicy_cache* cache,              /* host struct
                            const int32_t* entry_start, int32_t* lengths_out,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* spicy_coarsen_weighted — spicy_coarsen with variation-weighted
+ * representatives (Equal-Variation KV Cache page, implementation notes: each
+ * segment's representative key and value are the variation-weighted averages
+ * sum_r d_r k_r / sum_r d_r and sum_r d_r v_r / sum_r d_r).
+ *   token_weight  int64 [total_tokens] (device): one non-negative weight per
+ *                 token, indexed like k_pre's tokens; spicy_policy leaves its
+ *                 variation d_t in exactly this form in its workspace.
+ * A macro-node's key (before rotation) and value are the weighted means of
+ * its F-tokens; when every such weight is zero, the plain means.  Mass,
+ * alpha, the anchor tbar, beta and the diagonal variances keep their plain
+ * definitions; C-points and nulls are unchanged.  The weighted sums are exact
+ * in double precision (so the result is rounded once) while weight times
+ * |value| sums stay below 2^53 (bf16 inputs, weights below 2^30, segments
+ * below 2^14 tokens).  A negative weight is the caller's error (the result is
+ * then unspecified, not a fault).  Everything else as spicy_coarsen; the
+ * workspace size is the same.
+ * Errors: those of spicy_coarsen; SPICY_ERR_ARG also for a null token_weight
+ *   when there are tokens. */
+spicy_status spicy_coarsen_weighted(const spicy_cache* cache,
+                                    const void* k_pre, const void* v, int32_t total_tokens,
+                                    const int32_t* seq_offsets, const int32_t* pos_base,
+                                    const int32_t* seg_offsets, const int32_t* seq_seg_ptr,
+                                    int32_t n_seg, const uint8_t* protected_mask,
+                                    const int64_t* token_weight,
+                                    int32_t B, double rope_base,
+                                    const int32_t* page_table, int32_t max_pages_per_seq,
+                                    const int32_t* entry_start, int32_t* lengths_out,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
 /* Split-K plan: how many splits per (sequence, KV head) the decode uses when
  * asked for `num_splits` (0 = automatic) for a batch of B sequences of at most
  * max_pages_per_seq pages.  Pure host function. */
@@ -332,7 +361,9 @@ const char* spicy_status_string(spicy_status s);
  *   [total_tokens][H_kv] (1 = keep exact), ready to be passed to spicy_coarsen
  *   with n_seg = B * n_segments.  B = 0 writes nothing.
  * Workspace: device, >= spicy_policy_workspace_bytes(total_tokens, H_kv),
- *   first int32 = sticky device error word (SPICY_DEVERR_POLICY).
+ *   first int32 = sticky device error word (SPICY_DEVERR_POLICY).  On return
+ *   it holds d_t as int64 [total_tokens] from byte SPICY_WORKSPACE_HEADER:
+ *   the token weights spicy_coarsen_weighted takes.
  * Errors: SPICY_ERR_ARG (null pointer, negative count, n_segments < 1,
  *   proj_rows outside [1, 16], B * n_segments + 1 > INT32_MAX),
  *   SPICY_ERR_UNSUPPORTED (dtype not bf16, head_dim not 64/128, H_kv outside

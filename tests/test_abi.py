@@ -33,7 +33,8 @@ def test_every_declared_symbol_is_exported(lib):
             "spicy_decode_workspace_bytes", "spicy_decode_num_splits", "spicy_status_string",
             "spicy_decode_attn_shared", "spicy_decode_shared_workspace_bytes",
             "spicy_policy", "spicy_policy_workspace_bytes",
-            "spicy_decode_attn_multi", "spicy_decode_multi_workspace_bytes"} <= set(names)
+            "spicy_decode_attn_multi", "spicy_decode_multi_workspace_bytes",
+            "spicy_coarsen_weighted"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -154,6 +155,22 @@ def test_coarsen_rejects_bad_arguments(lib):
     assert call(cache=_cache(pages=0)) == 2
     assert call(wsb=100) == 3
     assert call(B=0) == 0
+
+
+def test_weighted_coarsen_rejects_bad_arguments(lib):
+    P = 0x1000
+    c = _cache()
+
+    def call(w=P, total=100, B=2, k=P, wsb=1 << 30):
+        return lib.spicy_coarsen_weighted(ctypes.byref(c), k, P, total, P, P, P, P, 10, P, w, B, 1e4, P, 8, P, P, P,
+                                          wsb, None)
+
+    assert call(w=0) == 1                   # weights are required when there are tokens
+    assert call(k=0) == 1
+    assert call(B=-1) == 1
+    assert call(wsb=100) == 3
+    assert call(w=0, B=0) == 0
+    assert call(w=0, total=0, B=0) == 0
 
 
 def test_multi_decode_rejects_bad_arguments(lib):
