@@ -59,6 +59,9 @@ def parse():
     ap.add_argument("--query-tokens", type=int, default=1,
                     help="query tokens per sequence in every decode call (spicy_decode_attn_multi when > 1, "
                          "as for speculative verification against the compressed cache)")
+    ap.add_argument("--weighted", action="store_true",
+                    help="with --device-policy: spicy_coarsen_weighted, the macro-nodes' keys and values weighted "
+                         "by the policy's per-token variation")
     ap.add_argument("--diag-closure", action="store_true",
                     help="the cache carries per-dimension variances (diagonal closure): coarsen writes them, "
                          "decode reads them in place of the scalar beta")
@@ -78,13 +81,14 @@ def policy_alg_bytes(call, spec) -> int:
     return 2 * T * H * d * elem_bytes(call.dtype) + T * H + 4 * (call.B * spec.n_segments + 1) + 4 * (call.B + 1)
 
 
-def coarsen_alg_bytes(call, lengths: np.ndarray, diag: bool = False) -> int:
+def coarsen_alg_bytes(call, lengths: np.ndarray, diag: bool = False, weighted: bool = False) -> int:
     """Bytes the coarsening must move: read K and V of every token and the
-    mask; write every entry it produces (key row, value column, alpha, beta,
-    and with `diag` the variance row), null padding included."""
+    mask (and with `weighted` one int64 weight per token); write every entry
+    it produces (key row, value column, alpha, beta, and with `diag` the
+    variance row), null padding included."""
     eb = elem_bytes(call.dtype)
     T, H, d = call.total_tokens, call.H_kv, call.d
-    read = T * H * d * 2 * eb + T * H
+    read = T * H * d * 2 * eb + T * H + (8 * T if weighted else 0)
     written_entries = 0
     for b in range(call.B):
         end = -(-int(lengths[b]) // 16) * 16
@@ -167,7 +171,8 @@ def measured_traffic(workload: str):
     return table
 
 
-def cpu_baseline(wl, reps: int, policy: bool = False, q_tokens: int = 1, diag: bool = False):
+def cpu_baseline(wl, reps: int, policy: bool = False, q_tokens: int = 1, diag: bool = False,
+                 weighted: bool = False):
     """The oracle (plain C, double precision) on the host cores: one whole
     step for every sequence of the batch (with `policy`, the oracle's policy
     on the chunk first; then the per-step coarsen and the decode), setup calls
@@ -193,7 +198,8 @@ def cpu_baseline(wl, reps: int, policy: bool = False, q_tokens: int = 1, diag: b
                                sp.sink, sp.recent)
             step = dataclasses.replace(c, seg_offsets=pr.seg_offsets, seq_seg_ptr=pr.seq_seg_ptr, mask=pr.mask)
         if step is not None:
-            lengths = oracle.coarsen(step, cache, threads=threads)
+            lengths = oracle.coarsen(step, cache, threads=threads,
+                                     token_weight=pr.variation if (policy and weighted) else None)
         if q_tokens > 1:
             oracle.decode_multi(qm, wl.dtype, cache, wl.page_table, lengths, threads=threads)
         else:
@@ -208,7 +214,8 @@ def cpu_baseline(wl, reps: int, policy: bool = False, q_tokens: int = 1, diag: b
                        f"{'policy (single thread) + ' if policy else ''}"
                        f"{'per-step coarsen + ' if wl.step is not None else ''}decode"
                        f"{f' of {q_tokens} query tokens per sequence' if q_tokens > 1 else ''}"
-                       f"{', diagonal closure' if diag else ''}), "
+                       f"{', diagonal closure' if diag else ''}"
+                       f"{', variation-weighted representatives' if weighted else ''}), "
                        f"median of {reps} after 1 warm-up, {med:.3f} s per step")
 
 
@@ -287,7 +294,9 @@ def main():
         if wl.policy is None or dw.step is None:
             sys.exit(f"--device-policy: workload {wl.name} has no per-step chunk with a policy")
         policy = DevicePolicy.of(wl.policy, dw.step.call, dev)
-        step_calls = [policy.feed(dw.step, dev)]
+        step_calls = [policy.feed(dw.step, dev, weighted=args.weighted)]
+    elif args.weighted:
+        sys.exit("--weighted needs --device-policy (the weights are the policy's per-token variation)")
 
     def step():
         if policy is not None:
@@ -339,12 +348,13 @@ def main():
     decode_ms = statistics.mean(e[1].elapsed_time(e[2]) for e in evs)
     policy_ms = statistics.mean(e[3].elapsed_time(e[0]) for e in evs) if policy is not None else None
     lengths = dw.lengths.cpu().numpy()
-    cb = sum(coarsen_alg_bytes(c.call, c.lengths.cpu().numpy(), args.diag_closure) for c in step_calls)
+    cb = sum(coarsen_alg_bytes(c.call, c.lengths.cpu().numpy(), args.diag_closure, args.weighted)
+             for c in step_calls)
     db = decode_alg_bytes(wl, lengths, args.query_tokens, args.diag_closure)
 
     traffic = measured_traffic(wl.name + ("_policy" if policy is not None else "") +
                                (f"_q{args.query_tokens}" if args.query_tokens > 1 else "") +
-                               ("_diag" if args.diag_closure else ""))
+                               ("_weighted" if args.weighted else "") + ("_diag" if args.diag_closure else ""))
 
     def roof(nbytes, ms, kernels):
         gbs = nbytes / (ms * 1e-3) / 1e9
@@ -390,7 +400,7 @@ def main():
                    "decode_splits": dw.splits, "shared_prefix_pages": dw.shared_prefix_pages,
                    "cache_entries_per_seq_mean": float(lengths.mean()),
                    "device_policy": policy is not None, "query_tokens_per_seq": args.query_tokens,
-                   "diag_closure": args.diag_closure},
+                   "diag_closure": args.diag_closure, "weighted_representatives": args.weighted},
         "roofline": dominant,
         "roofline_other": other,
         "decode_query_tokens_per_s": round(wl.B * args.query_tokens / (decode_ms * 1e-3), 1),
@@ -399,7 +409,8 @@ def main():
         out["roofline_policy"] = r_policy
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_reps, policy=policy is not None,
-                                           q_tokens=args.query_tokens, diag=args.diag_closure)
+                                           q_tokens=args.query_tokens, diag=args.diag_closure,
+                                           weighted=args.weighted)
     print(json.dumps(out), flush=True)
 
 

@@ -66,6 +66,9 @@ def lib():
             L.oracle_coarsen_weighted.restype = ctypes.c_int
             L.oracle_coarsen_weighted.argtypes = [ctypes.c_int, ctypes.c_int, i32, i32, P, P, P, P, P, P, P, P,
                                                   i32, ctypes.c_double, P, P, P, P, P, i32, P, i32, P, P, i32, i32]
+            L.oracle_merge_level.restype = ctypes.c_int
+            L.oracle_merge_level.argtypes = [ctypes.c_int, i32, i32, P, P, P, P, P, i32, P, i32, P, P, i32,
+                                             ctypes.c_double, i32, i32]
             L.oracle_decode_diag.restype = ctypes.c_int
             L.oracle_decode_diag.argtypes = [ctypes.c_int, ctypes.c_int, i32, i32, i32, P, P, P, P, P, i32,
                                              P, i32, P, i32, P, P, i32, i32]
@@ -238,6 +241,32 @@ def run_workload(wl, store: str | None = None, threads: int | None = None, diag:
         lengths = coarsen(call, cache, threads=threads)
     o, lse = decode(wl.q, wl.dtype, cache, wl.H_q, wl.page_table, lengths, threads=threads)
     return cache, lengths, o, lse
+
+
+def merge_level(cache: Cache, page_table: np.ndarray, entry_begin: np.ndarray, entry_end: np.ndarray,
+                rope_base: float, threads: int | None = None) -> None:
+    """oracle_merge_level: one level of the dyadic merge, in place, over
+    entries [entry_begin[b], entry_end[b]) of every sequence b."""
+    L = lib()
+    table = np.ascontiguousarray(page_table, dtype=np.int32)
+    eb = np.ascontiguousarray(entry_begin, dtype=np.int32)
+    ee = np.ascontiguousarray(entry_end, dtype=np.int32)
+    B = table.shape[0]
+    rcs = []
+
+    def run(rng):
+        rcs.append(L.oracle_merge_level(DT[cache.store], cache.H_kv, cache.d, _p(cache.k), _p(cache.v),
+                                        _p(cache.ab), _p(cache.meta), _p(cache.s2), cache.num_pages, _p(table),
+                                        table.shape[1], _p(eb), _p(ee), B, float(rope_base), rng[0], rng[1]))
+
+    chunks = _chunks(B, threads or default_threads())
+    if len(chunks) == 1:
+        run(chunks[0])
+    else:
+        with ThreadPoolExecutor(len(chunks)) as ex:
+            list(ex.map(run, chunks))
+    if any(rc != 0 for rc in rcs):
+        raise ValueError(f"oracle_merge_level failed: codes {sorted(set(rcs))}")
 
 
 def bf16_round(x: float) -> int:

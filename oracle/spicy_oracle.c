@@ -395,6 +395,113 @@ int oracle_coarsen_weighted(int in_dtype, int dtype, int32_t H_kv, int32_t d,
 }
 
 /* ------------------------------------------------------------------------ */
+/* One level of the dyadic merge cascade                                     */
+/* ------------------------------------------------------------------------ */
+
+/* Read entry e of a sequence: key and value rows as stored, alpha, beta and
+ * the metadata.  Returns 0, or 2/3 for a page outside the pool / table. */
+static int get_entry(const cache_view* c, int32_t h, int64_t e, double* key, double* val,
+                     double* alpha, double* beta, oracle_meta* meta) {
+    int64_t lp = e / PAGE;
+    if (lp >= c->max_pages) return 3;
+    int32_t P = c->table_row[lp];
+    if (P < 0 || P >= c->num_pages) return 2;
+    int32_t slot = (int32_t)(e % PAGE);
+    size_t ph = (size_t)P * (size_t)c->H + (size_t)h;
+    for (int32_t i = 0; i < c->d; ++i) {
+        key[i] = load_elem(c->dtype, c->k, ph * PAGE * (size_t)c->d + slot_elem(c->d, slot, i));
+        val[i] = load_elem(c->dtype, c->v, ph * PAGE * (size_t)c->d + slot_elem(c->d, slot, i));
+    }
+    *alpha = load_elem(c->dtype, c->ab, (ph * PAGE + (size_t)slot) * 2 + 0);
+    *beta = load_elem(c->dtype, c->ab, (ph * PAGE + (size_t)slot) * 2 + 1);
+    *meta = c->meta[ph * PAGE + (size_t)slot];
+    return 0;
+}
+
+/* One level of the cascaded dyadic merge (SPICY-KV demo page: the cascaded
+ * dyadic ring-buffer pyramid, Claim 12, and the law of total variance across
+ * cascades, Claim 10).  For every sequence b and KV head h, the macro-nodes
+ * (meta kind 2) among entries [entry_begin[b], entry_end[b]) are paired in
+ * entry order, first with second, third with fourth, ...; an odd last one is
+ * left alone.  A pair (1, 2) with masses m1, m2, position sums P1, P2 becomes
+ * one macro-node of the union of their members:
+ *   m = m1 + m2,  P = P1 + P2,  tbar = P / m
+ *   mu_i = R(-tbar_i) k_i               (the stored key rotated back to the
+ *                                        pre-RoPE mean of its members)
+ *   mu = (m1 mu_1 + m2 mu_2) / m,        v = (m1 v_1 + m2 v_2) / m
+ *   sigma^2 = (m1 sigma_1^2 + m2 sigma_2^2) / m + m1 m2 ||mu_1 - mu_2||^2 / (m^2 d)
+ *             with sigma_i^2 = 2 d beta_i  (the law of total variance)
+ * stored at the first entry as key R(tbar) mu, value v, alpha = ln m,
+ * beta = sigma^2 / (2 d), meta {2, m, P}; the second entry becomes a null
+ * (zero key and value, alpha = -inf, beta = 0, meta {0, 0, 0}).  C-points,
+ * nulls and the sequence length are untouched.  The metadata pool is
+ * required (it holds the exact masses and anchors); a cache with the
+ * diagonal-variance sidecar is not supported (rc 1). */
+int oracle_merge_level(int dtype, int32_t H_kv, int32_t d,
+                       void* k_pool, void* v_pool, void* ab_pool, void* meta, void* s2_pool,
+                       int32_t num_pages, const int32_t* page_table, int32_t max_pages_per_seq,
+                       const int32_t* entry_begin, const int32_t* entry_end, int32_t B, double rope_base,
+                       int32_t b_begin, int32_t b_end) {
+    if (dtype < 0 || dtype > 2 || H_kv <= 0 || !head_dim_ok(d) || (d % 2) != 0 || B < 0) return 1;
+    if (!k_pool || !v_pool || !ab_pool || !meta || s2_pool || !page_table || !entry_begin || !entry_end) return 1;
+    if (b_begin < 0 || b_end > B || b_begin > b_end) return 1;
+    double* k1 = malloc(sizeof(double) * (size_t)d);
+    double* k2 = malloc(sizeof(double) * (size_t)d);
+    double* v1 = malloc(sizeof(double) * (size_t)d);
+    double* v2 = malloc(sizeof(double) * (size_t)d);
+    double* mu1 = malloc(sizeof(double) * (size_t)d);
+    double* mu2 = malloc(sizeof(double) * (size_t)d);
+    double* mu = malloc(sizeof(double) * (size_t)d);
+    double* key = malloc(sizeof(double) * (size_t)d);
+    double* zero = calloc((size_t)d, sizeof(double));
+    int rc = (!k1 || !k2 || !v1 || !v2 || !mu1 || !mu2 || !mu || !key || !zero) ? 1 : 0;
+    for (int32_t b = b_begin; b < b_end && rc == 0; ++b) {
+        cache_view c = {dtype, H_kv, d, num_pages, max_pages_per_seq, k_pool, v_pool, ab_pool,
+                        (oracle_meta*)meta, page_table + (size_t)b * (size_t)max_pages_per_seq, NULL};
+        int64_t e0 = entry_begin[b], e1 = entry_end[b];
+        if (e0 < 0 || e0 > e1) { rc = 1; break; }
+        for (int32_t h = 0; h < H_kv && rc == 0; ++h) {
+            int64_t first = -1;                     /* the unpaired macro-node so far */
+            for (int64_t e = e0; e < e1 && rc == 0; ++e) {
+                double a2, b2;
+                oracle_meta m2;
+                rc = get_entry(&c, h, e, k2, v2, &a2, &b2, &m2);
+                if (rc || m2.kind != 2) continue;
+                if (m2.mass <= 0) { rc = 1; break; }
+                if (first < 0) { first = e; continue; }
+                double a1, b1;
+                oracle_meta m1;
+                rc = get_entry(&c, h, first, k1, v1, &a1, &b1, &m1);
+                if (rc) break;
+                const double M1 = (double)m1.mass, M2 = (double)m2.mass;
+                const int64_t mass = (int64_t)m1.mass + (int64_t)m2.mass;
+                if (mass > INT32_MAX) { rc = 1; break; }
+                const double M = (double)mass;
+                const int64_t psum = m1.pos_sum + m2.pos_sum;
+                oracle_rope(mu1, k1, d, -(double)m1.pos_sum / M1, rope_base);
+                oracle_rope(mu2, k2, d, -(double)m2.pos_sum / M2, rope_base);
+                double dist = 0.0;
+                for (int32_t i = 0; i < d; ++i) {
+                    const double dm = mu1[i] - mu2[i];
+                    dist += dm * dm;
+                    mu[i] = (M1 * mu1[i] + M2 * mu2[i]) / M;
+                    v1[i] = (M1 * v1[i] + M2 * v2[i]) / M;
+                }
+                const double sig1 = 2.0 * (double)d * b1, sig2 = 2.0 * (double)d * b2;
+                const double sigma2 = (M1 * sig1 + M2 * sig2) / M + M1 * M2 * dist / (M * M * (double)d);
+                oracle_rope(key, mu, d, (double)psum / M, rope_base);
+                rc = put_entry(&c, h, first, key, v1, log(M), sigma2 / (2.0 * (double)d), 2, (int32_t)mass, psum,
+                               NULL);
+                if (!rc) rc = put_entry(&c, h, e, zero, zero, -INFINITY, 0.0, 0, 0, 0, NULL);
+                first = -1;
+            }
+        }
+    }
+    free(k1); free(k2); free(v1); free(v2); free(mu1); free(mu2); free(mu); free(key); free(zero);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Decode                                                                    */
 /* ------------------------------------------------------------------------ */
 

@@ -93,6 +93,15 @@ int oracle_coarsen_weighted(int in_dtype, int dtype, int32_t H_kv, int32_t d,
                             const int32_t* page_table, int32_t max_pages_per_seq,
                             const int32_t* entry_start, int32_t* lengths_out,
                             int32_t b_begin, int32_t b_end);
+/* One level of the dyadic merge: consecutive macro-node pairs among each
+ * (sequence, head)'s entries [entry_begin[b], entry_end[b]) become one
+ * macro-node (law of total variance) at the first entry and a null at the
+ * second.  Needs the metadata pool; s2_pool must be NULL. */
+int oracle_merge_level(int dtype, int32_t H_kv, int32_t d,
+                       void* k_pool, void* v_pool, void* ab_pool, void* meta, void* s2_pool,
+                       int32_t num_pages, const int32_t* page_table, int32_t max_pages_per_seq,
+                       const int32_t* entry_begin, const int32_t* entry_end, int32_t B, double rope_base,
+                       int32_t b_begin, int32_t b_end);
 int oracle_decode_diag(int q_dtype, int dtype, int32_t H_q, int32_t H_kv, int32_t d,
                        const void* q,
                        const void* k_pool, const void* v_pool, const void* ab_pool, const void* s2_pool,
