@@ -77,6 +77,10 @@ def load_library():
     L.spicy_coarsen.restype = ctypes.c_int
     L.spicy_coarsen.argtypes = [CP, P, P, i32, P, P, P, P, i32, P, i32, ctypes.c_double, P, i32,
                                 P, P, P, sz, P]
+    L.spicy_merge_workspace_bytes.restype = sz
+    L.spicy_merge_workspace_bytes.argtypes = [i32, i32, i32]
+    L.spicy_merge_level.restype = ctypes.c_int
+    L.spicy_merge_level.argtypes = [CP, i32, ctypes.c_double, P, i32, P, P, i32, P, sz, P]
     L.spicy_coarsen_weighted.restype = ctypes.c_int
     L.spicy_coarsen_weighted.argtypes = [CP, P, P, i32, P, P, P, P, i32, P, P, i32, ctypes.c_double, P, i32,
                                          P, P, P, sz, P]
@@ -211,6 +215,26 @@ def spicy_coarsen(cache: PagedCache, k_pre, v, seq_offsets, pos_base, seg_offset
                          _ptr(lengths_out), _ptr(workspace), ws_bytes, _stream(stream))
     if rc != 0:
         raise SpicyError(rc, "spicy_coarsen")
+
+
+def spicy_merge_workspace_bytes(B: int, num_kv_heads: int, max_range: int) -> int:
+    return int(load_library().spicy_merge_workspace_bytes(B, num_kv_heads, max_range))
+
+
+def spicy_merge_level(cache: PagedCache, rope_base: float, page_table, entry_begin, entry_end, max_range: int,
+                      workspace, stream=None, *, B: int | None = None,
+                      max_pages_per_seq: int | None = None) -> None:
+    """spicy_merge_level through the C ABI (see include/spicy.h): one level of
+    the dyadic merge over entries [entry_begin[b], entry_end[b]) in place."""
+    L = load_library()
+    B = int(entry_begin.shape[0]) if B is None else B
+    max_pages = int(page_table.shape[-1]) if max_pages_per_seq is None else max_pages_per_seq
+    st = cache.struct()
+    ws_bytes = workspace.numel() * workspace.element_size() if isinstance(workspace, torch.Tensor) else 0
+    rc = L.spicy_merge_level(ctypes.byref(st), B, float(rope_base), _ptr(page_table), max_pages, _ptr(entry_begin),
+                             _ptr(entry_end), int(max_range), _ptr(workspace), ws_bytes, _stream(stream))
+    if rc != 0:
+        raise SpicyError(rc, "spicy_merge_level")
 
 
 def spicy_coarsen_weighted(cache: PagedCache, k_pre, v, seq_offsets, pos_base, seg_offsets, seq_seg_ptr,

@@ -12,7 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libspicy.so")
-SOURCES = ["api.hip", "coarsen.hip", "decode.hip", "policy.hip"]
+SOURCES = ["api.hip", "coarsen.hip", "decode.hip", "policy.hip", "merge.hip"]
 HEADERS = ["launch.h", "spicy_device.h"]
 ARCH = os.environ.get("SPICY_OFFLOAD_ARCH", "gfx950")
 

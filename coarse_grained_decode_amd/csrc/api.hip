@@ -396,4 +396,45 @@ spicy_status spicy_policy(const void* k_pre, const void* v, int32_t total_tokens
     return spicy::launch_policy(a, static_cast<hipStream_t>(stream));
 }
 
+size_t spicy_merge_workspace_bytes(int32_t B, int32_t num_kv_heads, int32_t max_range) {
+    if (B < 0 || num_kv_heads < 1 || max_range < 0) return 0;
+    const size_t units = static_cast<size_t>(B) * static_cast<size_t>(num_kv_heads);
+    const size_t cap = (static_cast<size_t>(max_range) + 1) / 2;
+    return SPICY_WORKSPACE_HEADER + align_up(4 * units) + align_up(8 * units * cap);
+}
+
+spicy_status spicy_merge_level(const spicy_cache* cache, int32_t B, double rope_base, const int32_t* page_table,
+                               int32_t max_pages_per_seq, const int32_t* entry_begin, const int32_t* entry_end,
+                               int32_t max_range, void* workspace, size_t workspace_bytes, void* stream) {
+    spicy_status st = check_cache(cache);
+    if (st != SPICY_OK) return st;
+    if (B < 0 || max_range < 0) return SPICY_ERR_ARG;
+    if (!cache->meta) return SPICY_ERR_ARG;              // the exact masses and anchors live there
+    if (cache->s2) return SPICY_ERR_UNSUPPORTED;         // per-dimension variances do not merge from the diagonal
+    if (B == 0) return SPICY_OK;
+    if (!page_table || !entry_begin || !entry_end || !workspace) return SPICY_ERR_ARG;
+    if (max_pages_per_seq < 1) return SPICY_ERR_ARG;
+    if (static_cast<int64_t>(B) * cache->num_kv_heads > kMaxGridY) return SPICY_ERR_UNSUPPORTED;
+    if (workspace_bytes < spicy_merge_workspace_bytes(B, cache->num_kv_heads, max_range)) return SPICY_ERR_CAPACITY;
+    spicy::MergeArgs a{};
+    a.cache = spicy::CacheArgs{cache->k, cache->v, cache->ab, cache->meta, cache->num_pages, cache->num_kv_heads,
+                               cache->s2};
+    a.page_table = page_table;
+    a.entry_begin = entry_begin;
+    a.entry_end = entry_end;
+    char* ws = static_cast<char*>(workspace);
+    a.err = reinterpret_cast<int32_t*>(ws);
+    const size_t units = static_cast<size_t>(B) * static_cast<size_t>(cache->num_kv_heads);
+    a.pair_count = reinterpret_cast<int32_t*>(ws + SPICY_WORKSPACE_HEADER);
+    a.pairs = reinterpret_cast<int2*>(ws + SPICY_WORKSPACE_HEADER + align_up(4 * units));
+    a.cap = static_cast<int32_t>((static_cast<int64_t>(max_range) + 1) / 2);
+    a.B = B;
+    a.max_pages = max_pages_per_seq;
+    a.max_range = max_range;
+    a.rope_base = rope_base;
+    for (int i = 0; i < cache->head_dim / 2; ++i)
+        a.theta[i] = rope_base > 0.0 ? std::pow(rope_base, -2.0 * static_cast<double>(i) / cache->head_dim) : 0.0;
+    return spicy::launch_merge(a, cache->dtype, cache->head_dim, static_cast<hipStream_t>(stream));
+}
+
 }  // extern "C"

@@ -11,5 +11,6 @@ namespace spicy {
 spicy_status launch_coarsen(const CoarsenArgs& a, int dtype, int head_dim, hipStream_t stream);
 spicy_status launch_decode(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream);
 spicy_status launch_policy(const PolicyArgs& a, hipStream_t stream);
+spicy_status launch_merge(const MergeArgs& a, int dtype, int head_dim, hipStream_t stream);
 
 }  // namespace spicy

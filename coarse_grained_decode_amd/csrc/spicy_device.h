@@ -182,6 +182,23 @@ struct CoarsenArgs {
     double theta[64];      // rotary frequencies rope_base^(-2i/d), i < d/2 (host libm pow)
 };
 
+// spicy_merge_level: one level of the dyadic merge cascade.
+struct MergeArgs {
+    CacheArgs cache;
+    const int32_t* page_table;    // [B][max_pages]
+    const int32_t* entry_begin;   // [B]
+    const int32_t* entry_end;     // [B]
+    int32_t* err;
+    int32_t* pair_count;          // [B*H]       workspace: pairs of each (sequence, head)
+    int2* pairs;                  // [B*H][cap]  workspace: {first entry, second entry}
+    int32_t cap;                  // pairs per (sequence, head) = (max_range + 1) / 2
+    int32_t B;
+    int32_t max_pages;
+    int32_t max_range;
+    double rope_base;
+    double theta[64];             // rotary frequencies rope_base^(-2i/d), i < d/2 (host libm pow)
+};
+
 struct DecodeArgs {
     CacheArgs cache;
     const void* q;

@@ -203,6 +203,53 @@ spicy_status spicy_coarsen_weighted(const spicy_cache* cache,
                                     const int32_t* entry_start, int32_t* lengths_out,
                                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * spicy_merge_level — one level of the cascaded dyadic merge, in place.
+ *
+ * SPICY-KV demo page: the cascaded dyadic ring-buffer pyramid (Claim 12) and
+ * the recursive law of total variance across cascades (Claim 10).  For every
+ * sequence b and KV head h, the macro-nodes (meta kind 2) among logical
+ * entries [entry_begin[b], entry_end[b]) are paired in entry order (first
+ * with second, third with fourth, ...; an odd last one is left as it is).
+ * A pair with masses m1, m2, position sums P1, P2, stored keys k1, k2,
+ * values v1, v2 and betas b1, b2 becomes one macro-node of the union of their
+ * members, written at the first entry:
+ *   m = m1 + m2, P = P1 + P2, tbar = P / m,
+ *   mu_i = R(-P_i / m_i) k_i (pre-RoPE means), mu = (m1 mu_1 + m2 mu_2) / m,
+ *   key R(tbar) mu, value (m1 v1 + m2 v2) / m, alpha = ln m,
+ *   sigma^2 = (m1 2d b1 + m2 2d b2) / m + m1 m2 |mu_1 - mu_2|^2 / (m^2 d),
+ *   beta = sigma^2 / (2d), meta {2, m, P};
+ * the second entry becomes a null (zero key and value, alpha = -inf,
+ * beta = 0, meta {0, 0, 0}).  C-points, nulls, entries outside the range and
+ * the sequence lengths are untouched; attention over the result equals
+ * attention over the coarsening of the joined segments up to the storage
+ * rounding.  Calling it again merges the next level.  Arithmetic in double
+ * precision, one rounding on store.
+ *
+ * The ranges of different sequences must not share physical pages (merge a
+ * shared prefix through one sequence only): calls race on a shared page.
+ * Requirements: cache->meta (exact masses and anchors) set; cache->s2 NULL
+ * (a diagonal variance does not merge from its own diagonal: the rotated
+ * pair covariances are not stored).  rope_base as for spicy_coarsen.
+ *   page_table    int32 [B][max_pages_per_seq] (device).
+ *   entry_begin, entry_end  int32 [B] (device); end - begin <= max_range.
+ * Workspace: device, >= spicy_merge_workspace_bytes(B, H_kv, max_range)
+ *   bytes; first int32 = sticky device error word: SPICY_DEVERR_SEGMENTS for
+ *   a range outside [0, max_range] or a pair whose metadata is not two
+ *   macro-nodes of positive mass (that pair is skipped), SPICY_DEVERR_PAGE_ID
+ *   and SPICY_DEVERR_CAPACITY for entries the table or pool cannot hold.
+ * Errors: SPICY_ERR_ARG (null pointer, B < 0, max_range < 0, meta NULL),
+ *   SPICY_ERR_UNSUPPORTED (s2 set, head_dim not 64/128, B * H_kv > 65535),
+ *   SPICY_ERR_CAPACITY (workspace too small), SPICY_ERR_HIP.
+ * ------------------------------------------------------------------------ */
+size_t spicy_merge_workspace_bytes(int32_t B, int32_t num_kv_heads, int32_t max_range);
+
+spicy_status spicy_merge_level(const spicy_cache* cache, int32_t B, double rope_base,
+                               const int32_t* page_table, int32_t max_pages_per_seq,
+                               const int32_t* entry_begin, const int32_t* entry_end,
+                               int32_t max_range, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
 /* Split-K plan: how many splits per (sequence, KV head) the decode uses when
  * asked for `num_splits` (0 = automatic) for a batch of B sequences of at most
  * max_pages_per_seq pages.  Pure host function. */

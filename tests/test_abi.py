@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(lib):
             "spicy_decode_attn_shared", "spicy_decode_shared_workspace_bytes",
             "spicy_policy", "spicy_policy_workspace_bytes",
             "spicy_decode_attn_multi", "spicy_decode_multi_workspace_bytes",
-            "spicy_coarsen_weighted"} <= set(names)
+            "spicy_coarsen_weighted", "spicy_merge_level", "spicy_merge_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -171,6 +171,35 @@ def test_weighted_coarsen_rejects_bad_arguments(lib):
     assert call(wsb=100) == 3
     assert call(w=0, B=0) == 0
     assert call(w=0, total=0, B=0) == 0
+
+
+def test_merge_rejects_bad_arguments(lib):
+    P = 0x1000
+    c = _cache()
+    c.meta = P
+
+    def call(cache=c, B=2, tb=P, eb=P, ee=P, rng=100, ws=P, wsb=1 << 30):
+        return lib.spicy_merge_level(ctypes.byref(cache) if cache is not None else None, B, 1e4, tb, 8, eb, ee, rng,
+                                     ws, wsb, None)
+
+    assert call(cache=None) == 1
+    assert call(B=-1) == 1
+    assert call(rng=-1) == 1
+    assert call(tb=0) == 1
+    assert call(ee=0) == 1
+    assert call(ws=0) == 1
+    assert call(wsb=64) == 3
+    assert call(B=20000) == 4               # B * H_kv above the 65535 units of the pair grid
+    assert call(B=0) == 0
+    nometa = _cache()
+    assert call(cache=nometa) == 1          # the metadata (exact masses, anchors) is required
+    diag = _cache()
+    diag.meta, diag.s2 = P, P
+    assert call(cache=diag) == 4
+    # header, int32 count per (sequence, head), int2 per pair, (range + 1) / 2 pairs
+    up = lambda x: (x + 255) // 256 * 256
+    assert lib.spicy_merge_workspace_bytes(3, 4, 101) == 256 + up(4 * 12) + up(8 * 12 * 51)
+    assert lib.spicy_merge_workspace_bytes(3, 0, 101) == 0
 
 
 def test_multi_decode_rejects_bad_arguments(lib):
