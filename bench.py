@@ -62,6 +62,9 @@ def parse():
     ap.add_argument("--weighted", action="store_true",
                     help="with --device-policy: spicy_coarsen_weighted, the macro-nodes' keys and values weighted "
                          "by the policy's per-token variation")
+    ap.add_argument("--merge", action="store_true",
+                    help="every step also merges one dyadic level over the entries its coarsening wrote "
+                         "(spicy_merge_level; the cache keeps its metadata)")
     ap.add_argument("--diag-closure", action="store_true",
                     help="the cache carries per-dimension variances (diagonal closure): coarsen writes them, "
                          "decode reads them in place of the scalar beta")
@@ -81,11 +84,12 @@ def policy_alg_bytes(call, spec) -> int:
     return 2 * T * H * d * elem_bytes(call.dtype) + T * H + 4 * (call.B * spec.n_segments + 1) + 4 * (call.B + 1)
 
 
-def coarsen_alg_bytes(call, lengths: np.ndarray, diag: bool = False, weighted: bool = False) -> int:
+def coarsen_alg_bytes(call, lengths: np.ndarray, diag: bool = False, weighted: bool = False,
+                      meta: bool = False) -> int:
     """Bytes the coarsening must move: read K and V of every token and the
     mask (and with `weighted` one int64 weight per token); write every entry
-    it produces (key row, value column, alpha, beta, and with `diag` the
-    variance row), null padding included."""
+    it produces (key row, value column, alpha, beta, with `diag` the variance
+    row, with `meta` the 16-byte metadata record), null padding included."""
     eb = elem_bytes(call.dtype)
     T, H, d = call.total_tokens, call.H_kv, call.d
     read = T * H * d * 2 * eb + T * H + (8 * T if weighted else 0)
@@ -93,8 +97,19 @@ def coarsen_alg_bytes(call, lengths: np.ndarray, diag: bool = False, weighted: b
     for b in range(call.B):
         end = -(-int(lengths[b]) // 16) * 16
         written_entries += H * (end - int(call.entry_start[b]))
-    write = written_entries * ((3 if diag else 2) * d + 2) * eb + call.B * 4
+    write = written_entries * (((3 if diag else 2) * d + 2) * eb + (16 if meta else 0)) + call.B * 4
     return read + write
+
+
+def merge_alg_bytes(call, lengths: np.ndarray, pairs: int) -> int:
+    """Bytes one merge level must move: the 16-byte metadata record of every
+    entry in the range (its kind), then per merged pair both entries read
+    (key and value rows, alpha and beta, metadata) and both written."""
+    eb = elem_bytes(call.dtype)
+    H, d = call.H_kv, call.d
+    ranged = int(sum(int(lengths[b]) - int(call.entry_start[b]) for b in range(call.B))) * H
+    per_entry = (2 * d + 2) * eb + 16
+    return 16 * ranged + 4 * per_entry * pairs
 
 
 def decode_alg_bytes(wl, lengths: np.ndarray, q_tokens: int = 1, diag: bool = False) -> int:
@@ -135,6 +150,7 @@ KERNEL_SOURCE = {
     "coarsen_main_kernel": "coarsen.hip", "coarsen_cpoint_kernel": "coarsen.hip",
     "decode_mfma_kernel": "decode.hip", "combine_kernel": "decode.hip", "decode_f32_kernel": "decode.hip",
     "policy_token_kernel": "policy.hip", "policy_seq_kernel": "policy.hip",
+    "merge_list_kernel": "merge.hip", "merge_pair_kernel": "merge.hip",
 }
 
 
@@ -172,7 +188,7 @@ def measured_traffic(workload: str):
 
 
 def cpu_baseline(wl, reps: int, policy: bool = False, q_tokens: int = 1, diag: bool = False,
-                 weighted: bool = False):
+                 weighted: bool = False, merge: bool = False):
     """The oracle (plain C, double precision) on the host cores: one whole
     step for every sequence of the batch (with `policy`, the oracle's policy
     on the chunk first; then the per-step coarsen and the decode), setup calls
@@ -200,6 +216,8 @@ def cpu_baseline(wl, reps: int, policy: bool = False, q_tokens: int = 1, diag: b
         if step is not None:
             lengths = oracle.coarsen(step, cache, threads=threads,
                                      token_weight=pr.variation if (policy and weighted) else None)
+            if merge:
+                oracle.merge_level(cache, wl.page_table, step.entry_start, lengths, step.rope_base, threads=threads)
         if q_tokens > 1:
             oracle.decode_multi(qm, wl.dtype, cache, wl.page_table, lengths, threads=threads)
         else:
@@ -215,7 +233,8 @@ def cpu_baseline(wl, reps: int, policy: bool = False, q_tokens: int = 1, diag: b
                        f"{'per-step coarsen + ' if wl.step is not None else ''}decode"
                        f"{f' of {q_tokens} query tokens per sequence' if q_tokens > 1 else ''}"
                        f"{', diagonal closure' if diag else ''}"
-                       f"{', variation-weighted representatives' if weighted else ''}), "
+                       f"{', variation-weighted representatives' if weighted else ''}"
+                       f"{', one merge level over the chunk' if merge else ''}), "
                        f"median of {reps} after 1 warm-up, {med:.3f} s per step")
 
 
@@ -280,7 +299,7 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    dw = DeviceWorkload.of(wl, dev, meta=False, num_splits=args.splits, fill=None,
+    dw = DeviceWorkload.of(wl, dev, meta=args.merge, num_splits=args.splits, fill=None,
                            use_shared_prefix=not args.no_shared_prefix, q_tokens=args.query_tokens,
                            diag=args.diag_closure)
     dw.run_setup()
@@ -297,12 +316,29 @@ def main():
         step_calls = [policy.feed(dw.step, dev, weighted=args.weighted)]
     elif args.weighted:
         sys.exit("--weighted needs --device-policy (the weights are the policy's per-token variation)")
+    run_merge, mws = None, None
+    if args.merge and args.diag_closure:
+        sys.exit("--merge does not combine with --diag-closure (the diagonal variances do not merge)")
+    if args.merge:
+        from coarse_grained_decode_amd import spicy_merge_level, spicy_merge_workspace_bytes, workspace
+        if dw.step is None:
+            sys.exit(f"--merge: workload {wl.name} has no per-step chunk to merge")
+        mc = step_calls[-1]
+        seg_per_seq = wl.policy.n_segments if policy is not None else int(np.diff(mc.call.seq_seg_ptr).max())
+        max_range = int(np.diff(mc.call.seq_offsets).max()) + seg_per_seq + 16
+        mws = workspace(spicy_merge_workspace_bytes(mc.call.B, mc.call.H_kv, max_range), dev)
+
+        def run_merge():
+            spicy_merge_level(dw.cache, mc.call.rope_base, mc.page_table, mc.entry_start, mc.lengths, max_range,
+                              mws, max_pages_per_seq=mc.call.max_pages)
 
     def step():
         if policy is not None:
             policy.run(dw.step)
         for c in step_calls:
             c.run(dw.cache)
+        if run_merge is not None:
+            run_merge()
         dw.lengths = step_calls[-1].lengths
         dw.decode()
 
@@ -331,7 +367,7 @@ def main():
     # throughput loop because an event recorded between two calls leaves the
     # GPU idle for a few microseconds; part of that idle time lands inside the
     # bracketed durations, so these err on the slow side.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for e in evs:
         e[3].record()
@@ -341,20 +377,25 @@ def main():
         for c in step_calls:
             c.run(dw.cache)
         e[1].record()
+        if run_merge is not None:
+            run_merge()
+        e[4].record()
         dw.decode()
         e[2].record()
     torch.cuda.synchronize()
     coarsen_ms = statistics.mean(e[0].elapsed_time(e[1]) for e in evs)
-    decode_ms = statistics.mean(e[1].elapsed_time(e[2]) for e in evs)
+    decode_ms = statistics.mean(e[4].elapsed_time(e[2]) for e in evs)
+    merge_ms = statistics.mean(e[1].elapsed_time(e[4]) for e in evs) if run_merge is not None else None
     policy_ms = statistics.mean(e[3].elapsed_time(e[0]) for e in evs) if policy is not None else None
     lengths = dw.lengths.cpu().numpy()
-    cb = sum(coarsen_alg_bytes(c.call, c.lengths.cpu().numpy(), args.diag_closure, args.weighted)
+    cb = sum(coarsen_alg_bytes(c.call, c.lengths.cpu().numpy(), args.diag_closure, args.weighted, args.merge)
              for c in step_calls)
     db = decode_alg_bytes(wl, lengths, args.query_tokens, args.diag_closure)
 
     traffic = measured_traffic(wl.name + ("_policy" if policy is not None else "") +
                                (f"_q{args.query_tokens}" if args.query_tokens > 1 else "") +
-                               ("_weighted" if args.weighted else "") + ("_diag" if args.diag_closure else ""))
+                               ("_weighted" if args.weighted else "") + ("_diag" if args.diag_closure else "") +
+                               ("_merge" if args.merge else ""))
 
     def roof(nbytes, ms, kernels):
         gbs = nbytes / (ms * 1e-3) / 1e9
@@ -378,6 +419,17 @@ def main():
         r_policy["kernel"] = "spicy_policy (policy_token: fixed point, projection, variation, key norms; " \
                              "then policy_seq: scan, boundaries, landmark radix select)"
         calls.append((policy_ms, r_policy))
+    if run_merge is not None:
+        mc = step_calls[-1]
+        units = mc.call.B * mc.call.H_kv
+        pairs = int(mws.view(torch.uint8)[256:256 + 4 * units].view(torch.int32).sum().item())
+        assert int(mws[0].item()) == 0, "device error word set (merge)"
+        mb = merge_alg_bytes(mc.call, mc.lengths.cpu().numpy(), pairs)
+        r_merge = roof(mb, merge_ms, ["merge_list_kernel", "merge_pair_kernel"])
+        r_merge["kernel"] = "spicy_merge_level (merge_list: pairs per sequence and head; merge_pair: law of " \
+                            "total variance per pair)"
+        r_merge["pairs_per_call"] = pairs
+        calls.append((merge_ms, r_merge))
     calls.sort(key=lambda x: -x[0])
     dominant, other = calls[0][1], calls[1][1]
 
@@ -400,17 +452,20 @@ def main():
                    "decode_splits": dw.splits, "shared_prefix_pages": dw.shared_prefix_pages,
                    "cache_entries_per_seq_mean": float(lengths.mean()),
                    "device_policy": policy is not None, "query_tokens_per_seq": args.query_tokens,
-                   "diag_closure": args.diag_closure, "weighted_representatives": args.weighted},
+                   "diag_closure": args.diag_closure, "weighted_representatives": args.weighted,
+                   "merge_level": args.merge},
         "roofline": dominant,
         "roofline_other": other,
         "decode_query_tokens_per_s": round(wl.B * args.query_tokens / (decode_ms * 1e-3), 1),
     }
     if policy is not None:
         out["roofline_policy"] = r_policy
+    if run_merge is not None:
+        out["roofline_merge"] = r_merge
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_reps, policy=policy is not None,
                                            q_tokens=args.query_tokens, diag=args.diag_closure,
-                                           weighted=args.weighted)
+                                           weighted=args.weighted, merge=args.merge)
     print(json.dumps(out), flush=True)
 
 

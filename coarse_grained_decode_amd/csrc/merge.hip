@@ -9,6 +9,7 @@
 // P_i / m_i), values v1, v2 and betas b1, b2 becomes, at the first entry,
 //     m = m1 + m2, P = P1 + P2, tbar = P / m,
 //     mu_i = R(-P_i / m_i) k_i,  mu = (m1 mu_1 + m2 mu_2) / m,
+//     (computed as R(tbar) mu = (m1 R(tbar - tbar_1) k1 + m2 R(tbar - tbar_2) k2) / m)
 //     v = (m1 v1 + m2 v2) / m,
 //     sigma^2 = (m1 2d b1 + m2 2d b2) / m + m1 m2 |mu_1 - mu_2|^2 / (m^2 d),
 //     key R(tbar) mu, alpha = ln m, beta = sigma^2 / (2d), meta {2, m, P},
@@ -74,33 +75,45 @@ __global__ __launch_bounds__(kListWaves * kWave) void merge_list_kernel(MergeArg
     const MetaRec* meta = static_cast<const MetaRec*>(a.cache.meta);
     int2* out = a.pairs + unit * a.cap;
     int32_t carry = -1;                                  // the unpaired macro-node so far (uniform)
-    for (int32_t base = e0; base < e1; base += kWave) {
-        const int32_t e = base + lane;
-        bool mac = false;
-        if (e < e1) {
-            const int32_t P = page_of(a, b, e);
-            if (P >= 0) {
-                const MetaRec r = meta[(static_cast<int64_t>(P) * H + h) * kPage + e % kPage];
-                mac = r.kind == 2;
-            }
+    // kBatch windows of 64 entries at a time: their page ids, then their
+    // kinds, are requested together before the windows are paired in order
+    constexpr int kBatch = 4;
+    for (int32_t base0 = e0; base0 < e1; base0 += kBatch * kWave) {
+        int32_t pg[kBatch];
+        int32_t kind[kBatch];
+#pragma unroll
+        for (int w = 0; w < kBatch; ++w) {
+            const int32_t e = base0 + w * kWave + lane;
+            pg[w] = e < e1 ? page_of(a, b, e) : -1;
         }
-        const uint64_t M = __ballot(mac);
-        const int c = carry >= 0 ? 1 : 0;
-        const int n = __popcll(M);
-        if (mac) {
-            const int r = __popcll(M & ((1ull << lane) - 1));   // rank among this window's macro-nodes
-            const int p = c + r;                                 // place in the sequence carry, m_0, m_1, ...
-            if (p & 1) {
-                const uint64_t below = M & ((1ull << lane) - 1);
-                const int32_t first = (r == 0) ? carry : base + (63 - __clzll(below));
-                const int32_t j = npairs + (p >> 1);
-                if (j < a.cap) out[j] = make_int2(first, e);
-                else raise_err(a.err, SPICY_DEVERR_CAPACITY);
-            }
+#pragma unroll
+        for (int w = 0; w < kBatch; ++w) {
+            const int32_t e = base0 + w * kWave + lane;
+            kind[w] = pg[w] >= 0 ? meta[(static_cast<int64_t>(pg[w]) * H + h) * kPage + e % kPage].kind : 0;
         }
-        npairs += (c + n) >> 1;
-        if ((c + n) & 1) carry = n > 0 ? base + (63 - __clzll(M)) : carry;
-        else carry = -1;
+#pragma unroll
+        for (int w = 0; w < kBatch; ++w) {
+            const int32_t base = base0 + w * kWave;
+            const int32_t e = base + lane;
+            const bool mac = kind[w] == 2;
+            const uint64_t M = __ballot(mac);
+            const int c = carry >= 0 ? 1 : 0;
+            const int n = __popcll(M);
+            if (mac) {
+                const int r = __popcll(M & ((1ull << lane) - 1));   // rank among this window's macro-nodes
+                const int p = c + r;                                 // place in the sequence carry, m_0, m_1, ...
+                if (p & 1) {
+                    const uint64_t below = M & ((1ull << lane) - 1);
+                    const int32_t first = (r == 0) ? carry : base + (63 - __clzll(below));
+                    const int32_t j = npairs + (p >> 1);
+                    if (j < a.cap) out[j] = make_int2(first, e);
+                    else raise_err(a.err, SPICY_DEVERR_CAPACITY);
+                }
+            }
+            npairs += (c + n) >> 1;
+            if ((c + n) & 1) carry = n > 0 ? base + (63 - __clzll(M)) : carry;
+            else carry = -1;
+        }
     }
     if (lane == 0) a.pair_count[unit] = npairs < a.cap ? npairs : a.cap;
 }
@@ -176,13 +189,11 @@ __global__ __launch_bounds__(256) void merge_pair_kernel(MergeArgs a) {
             sn[4 + q] = hi_half ? sq : os;
         }
     };
-    // y = R(sign * angle) x for this lane's dims (sign +1 forward, -1 inverse)
-    auto rot = [&](const double (&x)[8], const double (&cs)[8], const double (&sn)[8], double sign,
-                   double (&y)[8]) {
+    // y = R(angle) x for this lane's dims
+    auto rot = [&](const double (&x)[8], const double (&cs)[8], const double (&sn)[8], double (&y)[8]) {
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            const double p = __shfl_xor(x[r], PARTNER);
-            const double ps = sign * p * sn[r];
+            const double ps = __shfl_xor(x[r], PARTNER) * sn[r];
             y[r] = hi_half ? x[r] * cs[r] + ps : x[r] * cs[r] - ps;
         }
     };
@@ -237,36 +248,33 @@ __global__ __launch_bounds__(256) void merge_pair_kernel(MergeArgs a) {
         }
         const double m = m1 + m2;
         const int64_t P = q1 + q2;
-        double mu1[8], mu2[8], mu[8], key[8], cs[8], sn[8];
+        // R(tbar) mu = (m1 R(tbar - tbar_1) k1 + m2 R(tbar - tbar_2) k2) / m, and
+        // |mu_1 - mu_2| is the norm of the difference of the two rotated keys
+        // (rotations keep norms): two sets of angles instead of three
+        const double tb = static_cast<double>(P) / m;
+        double y1[8], y2[8], key[8], cs[8], sn[8];
         if (rotate) {
-            angles(static_cast<double>(q1) / m1, cs, sn);
-            rot(k1, cs, sn, -1.0, mu1);
-            angles(static_cast<double>(q2) / m2, cs, sn);
-            rot(k2, cs, sn, -1.0, mu2);
+            angles(tb - static_cast<double>(q1) / m1, cs, sn);
+            rot(k1, cs, sn, y1);
+            angles(tb - static_cast<double>(q2) / m2, cs, sn);
+            rot(k2, cs, sn, y2);
         } else {
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
-                mu1[r] = k1[r];
-                mu2[r] = k2[r];
+                y1[r] = k1[r];
+                y2[r] = k2[r];
             }
         }
         double dist = 0.0;
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            const double dm = mu1[r] - mu2[r];
+            const double dm = y1[r] - y2[r];
             dist += dm * dm;
-            mu[r] = (m1 * mu1[r] + m2 * mu2[r]) / m;
+            key[r] = (m1 * y1[r] + m2 * y2[r]) / m;
             v1[r] = (m1 * v1[r] + m2 * v2[r]) / m;
         }
 #pragma unroll
         for (int o = 1; o < LPH; o <<= 1) dist += __shfl_xor(dist, o);
-        if (rotate) {
-            angles(static_cast<double>(P) / m, cs, sn);
-            rot(mu, cs, sn, 1.0, key);
-        } else {
-#pragma unroll
-            for (int r = 0; r < 8; ++r) key[r] = mu[r];
-        }
         if (!ok || i1 <= 0) continue;
         const double sig = (m1 * (2.0 * D * b1) + m2 * (2.0 * D * b2)) / m + m1 * m2 * dist / (m * m * D);
         T* kp = static_cast<T*>(a.cache.k);

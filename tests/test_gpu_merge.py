@@ -4,11 +4,14 @@ the CPU oracle, through the C ABI.
 Both sides start every level from the same bytes (the oracle's cache so far
 uploaded, metadata included).  Bars: entry kinds, masses, position sums and
 alpha = bf16(ln m) bit-exact; beta within 1 unit in the last place; keys and
-values within 1 unit in the last place, or within 1e-12 of the largest
+values within 1 unit in the last place, or within 1e-10 of the largest
 magnitude in their row: both sides work in double precision and round once,
 but a component that cancels to nearly zero (a rotated or averaged pair)
 keeps only rounding noise of the row's scale, where the storage ulp is far
-finer; nulls exact.  Then the decode of the merged GPU cache against the
+finer.  That noise is set by the rotation angles: position times frequency
+reaches about 1e5 rad here, whose double-precision rounding is about 1e-11
+(the GPU rotates once by tbar - tbar_i, the oracle back by tbar_i and forward
+by tbar).  Nulls exact.  Then the decode of the merged GPU cache against the
 decode of the merged oracle cache at the decode bars.
 """
 import numpy as np
@@ -79,7 +82,7 @@ def compare_merged(gcache, ref, wl, lengths):
         du = ulp_dist(g, r, store)
         gv, rv = store_value(g, store), store_value(r, store)
         scale = np.abs(rv).max(-1, keepdims=True)
-        ok = (du <= 1) | (np.abs(gv - rv) <= 1e-12 * scale)
+        ok = (du <= 1) | (np.abs(gv - rv) <= 1e-10 * scale)
         assert ok.all(), f"{f} differs: {du.max()} ulp, worst abs {np.abs(gv - rv).max()}"
         exact[f] = float((du == 0).mean())
     return exact
