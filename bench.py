@@ -449,7 +449,8 @@ def main():
         "data": "synthetic (seeded clustered-Gaussian keys, Gaussian values/queries)",
         "config": {"workload": wl.name, "description": wl.description, "batch": wl.B,
                    "num_q_heads": wl.H_q, "num_kv_heads": wl.H_kv, "head_dim": wl.d,
-                   "decode_splits": dw.splits, "shared_prefix_pages": dw.shared_prefix_pages,
+                   "decode_splits": dw.splits, "decode_plan": dw.plan,
+                   "shared_prefix_pages": dw.shared_prefix_pages,
                    "cache_entries_per_seq_mean": float(lengths.mean()),
                    "device_policy": policy is not None, "query_tokens_per_seq": args.query_tokens,
                    "diag_closure": args.diag_closure, "weighted_representatives": args.weighted,

@@ -77,6 +77,8 @@ def load_library():
     L.spicy_coarsen.restype = ctypes.c_int
     L.spicy_coarsen.argtypes = [CP, P, P, i32, P, P, P, P, i32, P, i32, ctypes.c_double, P, i32,
                                 P, P, P, sz, P]
+    L.spicy_decode_plan.restype = ctypes.c_int
+    L.spicy_decode_plan.argtypes = [i32, i32, i32, i32, i32, i32, i32, P]
     L.spicy_merge_workspace_bytes.restype = sz
     L.spicy_merge_workspace_bytes.argtypes = [i32, i32, i32]
     L.spicy_merge_level.restype = ctypes.c_int
@@ -215,6 +217,18 @@ def spicy_coarsen(cache: PagedCache, k_pre, v, seq_offsets, pos_base, seg_offset
                          _ptr(lengths_out), _ptr(workspace), ws_bytes, _stream(stream))
     if rc != 0:
         raise SpicyError(rc, "spicy_coarsen")
+
+
+def spicy_decode_plan(B: int, num_q_heads: int, num_kv_heads: int, max_pages_per_seq: int,
+                      shared_prefix_pages: int = 0, num_splits: int = 0, num_q_tokens: int = 1) -> dict:
+    """spicy_decode_plan: the decode's split-K plan for these sizes."""
+    out = (ctypes.c_int32 * 4)()
+    rc = load_library().spicy_decode_plan(B, num_q_heads, num_kv_heads, max_pages_per_seq, shared_prefix_pages,
+                                          num_splits, num_q_tokens, out)
+    if rc != 0:
+        raise SpicyError(rc, "spicy_decode_plan")
+    return dict(prefix_chunks=out[0], prefix_chunk_pages=out[1], private_splits=out[2],
+                private_pages_per_split=out[3])
 
 
 def spicy_merge_workspace_bytes(B: int, num_kv_heads: int, max_range: int) -> int:

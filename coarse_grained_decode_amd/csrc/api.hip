@@ -239,6 +239,22 @@ int32_t spicy_decode_num_splits(int32_t B, int32_t num_kv_heads, int32_t max_pag
     return ceil_div(max_pages_per_seq, pages_per_split(max_pages_per_seq, s));
 }
 
+spicy_status spicy_decode_plan(int32_t B, int32_t num_q_heads, int32_t num_kv_heads, int32_t max_pages_per_seq,
+                               int32_t shared_prefix_pages, int32_t num_splits, int32_t num_q_tokens,
+                               int32_t* plan) {
+    if (!plan || B < 0 || num_q_heads < 1 || num_kv_heads < 1 || max_pages_per_seq < 1 || num_q_tokens < 1 ||
+        shared_prefix_pages < 0 || num_splits < 0)
+        return SPICY_ERR_ARG;
+    if (shared_prefix_pages > max_pages_per_seq) return SPICY_ERR_RANGE;
+    const DecodePlan p = plan_decode(B, num_q_heads, num_kv_heads, max_pages_per_seq, shared_prefix_pages,
+                                     num_splits, num_q_tokens);
+    plan[0] = p.prefix_splits;
+    plan[1] = p.prefix_splits > 0 ? p.prefix_chunk : 0;
+    plan[2] = max_pages_per_seq > shared_prefix_pages ? p.priv_splits : 0;
+    plan[3] = max_pages_per_seq > shared_prefix_pages ? p.pages_per_split : 0;
+    return SPICY_OK;
+}
+
 size_t spicy_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
                                     int32_t head_dim, int32_t max_pages_per_seq, int32_t num_splits) {
     return spicy_decode_shared_workspace_bytes(B, num_q_heads, num_kv_heads, head_dim, max_pages_per_seq, 0,

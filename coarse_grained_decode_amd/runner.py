@@ -15,7 +15,7 @@ import numpy as np
 import torch
 
 from . import (PagedCache, spicy_coarsen, spicy_coarsen_weighted, spicy_coarsen_workspace_bytes, spicy_decode_attn,
-               spicy_decode_attn_shared, spicy_decode_num_splits, spicy_decode_shared_workspace_bytes,
+               spicy_decode_attn_shared, spicy_decode_num_splits, spicy_decode_plan, spicy_decode_shared_workspace_bytes,
                spicy_decode_attn_multi, spicy_decode_multi_workspace_bytes, spicy_policy,
                spicy_policy_workspace_bytes, workspace)
 from .workloads import CoarsenCall, PolicySpec, Workload, query_tokens
@@ -205,4 +205,11 @@ class DeviceWorkload:
 
     @property
     def splits(self) -> int:
-        return spicy_decode_num_splits(self.wl.B, self.wl.H_kv, self.wl.max_pages, self.num_splits)
+        """Private splits per (sequence, KV head) of this workload's decode call."""
+        return self.plan["private_splits"]
+
+    @property
+    def plan(self) -> dict:
+        """The decode call's split-K plan (spicy_decode_plan)."""
+        return spicy_decode_plan(self.wl.B, self.wl.H_q, self.wl.H_kv, self.wl.max_pages,
+                                 self.shared_prefix_pages, self.num_splits, self.q_tokens)

@@ -250,11 +250,27 @@ spicy_status spicy_merge_level(const spicy_cache* cache, int32_t B, double rope_
                                int32_t max_range, void* workspace, size_t workspace_bytes,
                                void* stream);
 
-/* Split-K plan: how many splits per (sequence, KV head) the decode uses when
- * asked for `num_splits` (0 = automatic) for a batch of B sequences of at most
- * max_pages_per_seq pages.  Pure host function. */
+/* Split-K plan: how many splits per (sequence, KV head) spicy_decode_attn
+ * uses when asked for `num_splits` (0 = automatic) for a batch of B sequences
+ * of at most max_pages_per_seq pages.  Pure host function.  The shared-prefix
+ * and multi-token entry points plan over the work of the whole call (prefix
+ * chunks and query tiles included): spicy_decode_plan gives their plan. */
 int32_t spicy_decode_num_splits(int32_t B, int32_t num_kv_heads, int32_t max_pages_per_seq,
                                 int32_t num_splits);
+
+/* The decode's work plan for spicy_decode_attn_multi (and so for
+ * spicy_decode_attn: shared_prefix_pages = 0, num_q_tokens = 1; and for
+ * spicy_decode_attn_shared: num_q_tokens = 1).  Writes plan[4] (host):
+ *   plan[0] shared-prefix chunks (0 without a prefix),
+ *   plan[1] prefix pages per chunk (0 without a prefix),
+ *   plan[2] splits of each (sequence, KV head)'s private pages (0 if none),
+ *   plan[3] private pages per split (0 if none).
+ * Pure host function.  Errors: SPICY_ERR_ARG (null plan, counts < 1 where
+ * required, negative prefix or num_splits), SPICY_ERR_RANGE (prefix longer
+ * than max_pages_per_seq). */
+spicy_status spicy_decode_plan(int32_t B, int32_t num_q_heads, int32_t num_kv_heads, int32_t max_pages_per_seq,
+                               int32_t shared_prefix_pages, int32_t num_splits, int32_t num_q_tokens,
+                               int32_t* plan);
 
 /* Workspace bytes spicy_decode_attn needs (header + fp32 partial (m, l, o[d])
  * per (sequence, query head, split)). */

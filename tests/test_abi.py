@@ -34,7 +34,8 @@ def test_every_declared_symbol_is_exported(lib):
             "spicy_decode_attn_shared", "spicy_decode_shared_workspace_bytes",
             "spicy_policy", "spicy_policy_workspace_bytes",
             "spicy_decode_attn_multi", "spicy_decode_multi_workspace_bytes",
-            "spicy_coarsen_weighted", "spicy_merge_level", "spicy_merge_workspace_bytes"} <= set(names)
+            "spicy_coarsen_weighted", "spicy_merge_level", "spicy_merge_workspace_bytes",
+            "spicy_decode_plan"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -171,6 +172,26 @@ def test_weighted_coarsen_rejects_bad_arguments(lib):
     assert call(wsb=100) == 3
     assert call(w=0, B=0) == 0
     assert call(w=0, total=0, B=0) == 0
+
+
+def test_decode_plan(lib):
+    """spicy_decode_plan: the plain decode's private splits are
+    spicy_decode_num_splits; a prefix gets chunks that cover it; errors."""
+    for B, H_kv, maxp, ns in [(32, 4, 200, 0), (3, 2, 17, 0), (32, 4, 200, 16), (1, 1, 1, 0), (64, 8, 9000, 5)]:
+        pl = cgd.spicy_decode_plan(B, 4 * H_kv, H_kv, maxp, 0, ns)
+        assert pl["prefix_chunks"] == 0 and pl["prefix_chunk_pages"] == 0
+        assert pl["private_splits"] == lib.spicy_decode_num_splits(B, H_kv, maxp, ns)
+        assert pl["private_splits"] * pl["private_pages_per_split"] >= maxp
+        assert (pl["private_splits"] - 1) * pl["private_pages_per_split"] < maxp
+    pl = cgd.spicy_decode_plan(32, 28, 4, 300, 144, 0)
+    assert pl["prefix_chunks"] * pl["prefix_chunk_pages"] >= 144
+    assert (pl["prefix_chunks"] - 1) * pl["prefix_chunk_pages"] < 144
+    assert pl["private_splits"] * pl["private_pages_per_split"] >= 300 - 144
+    assert cgd.spicy_decode_plan(2, 8, 2, 10, 10, 0)["private_splits"] == 0   # prefix only
+    out = (ctypes.c_int32 * 4)()
+    assert lib.spicy_decode_plan(2, 8, 2, 10, 11, 0, 1, out) == 2           # prefix longer than the table
+    assert lib.spicy_decode_plan(2, 8, 2, 10, 0, 0, 0, out) == 1            # no query tokens
+    assert lib.spicy_decode_plan(2, 8, 2, 10, 0, 0, 1, None) == 1
 
 
 def test_merge_rejects_bad_arguments(lib):
