@@ -536,12 +536,15 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
 // ----------------------------------------------------------------- combine
 
 // One wavefront per (sequence, query head): merge its partials (prefix chunks
-// first, then the private splits that hold pages) by log-sum-exp.  Loads of
-// kChunk partials are issued together; lanes own D/64 dimensions.
+// first, then the private splits that hold pages) by log-sum-exp, in one
+// pass with a running maximum: the loads of kChunk partials are issued
+// together and nothing waits for a separate maximum pass.  Every lane reads
+// the same (m, l) of a partial, so the maximum needs no lane exchange; lanes
+// own D/64 dimensions.
 template <int D>
 __global__ __launch_bounds__(64) void combine_kernel(DecodeArgs a) {
     constexpr int DL = D / kWave;
-    constexpr int kChunk = 16;
+    constexpr int kChunk = 32;
     const int lane = threadIdx.x;
     const int hq = blockIdx.x;
     const int bv = blockIdx.y;                 // sequence * n_q + token
@@ -552,11 +555,6 @@ __global__ __launch_bounds__(64) void combine_kernel(DecodeArgs a) {
     const int64_t base = (static_cast<int64_t>(bv) * a.H_q + hq) * a.splits;
 
     float M = -__builtin_huge_valf();
-    for (int s = lane; s < nsplit; s += kWave) M = fmaxf(M, a.part_ml[2 * (base + s)]);
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
-    const float msub = (M == -__builtin_huge_valf()) ? 0.f : M;
-
     float L = 0.f;
     float acc[DL];
 #pragma unroll
@@ -571,6 +569,14 @@ __global__ __launch_bounds__(64) void combine_kernel(DecodeArgs a) {
 #pragma unroll
             for (int j = 0; j < DL; ++j) ov[u][j] = a.part_o[(base + s) * D + lane + kWave * j];
         }
+        float mc = M;
+#pragma unroll
+        for (int u = 0; u < kChunk; ++u) mc = fmaxf(mc, w[u]);     // repeats of the last partial change nothing
+        const float msub = (mc == -__builtin_huge_valf()) ? 0.f : mc;
+        const float scale = fast_exp2(M - msub);                   // 0 while M is -inf
+        L *= scale;
+#pragma unroll
+        for (int j = 0; j < DL; ++j) acc[j] *= scale;
 #pragma unroll
         for (int u = 0; u < kChunk; ++u) {
             const float wu = (s0 + u < nsplit) ? fast_exp2(w[u] - msub) : 0.f;
@@ -578,7 +584,9 @@ __global__ __launch_bounds__(64) void combine_kernel(DecodeArgs a) {
 #pragma unroll
             for (int j = 0; j < DL; ++j) acc[j] += wu * ov[u][j];
         }
+        M = mc;
     }
+    const float msub = (M == -__builtin_huge_valf()) ? 0.f : M;
     float* orow = a.o + (static_cast<int64_t>(bv) * a.H_q + hq) * D;
     const bool live = L > 0.f;
     const float inv = live ? 1.f / L : 0.f;
