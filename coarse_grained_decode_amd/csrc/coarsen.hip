@@ -46,6 +46,10 @@ constexpr int kCpointBlocksPerSeq = 64;
 constexpr int kMaxH = 16;
 constexpr int kRing = 3;
 constexpr int kResidentBlocks = 1024;   // 4 workgroups of 4 waves per CU
+// coarsen_cpoint's register use allows 5 waves per SIMD: 5 workgroups of 4
+// waves per CU, 1280 on the chip.  A grid of exactly that many runs in one
+// round (measured: 1024 or 2048 workgroups are 2-4 us slower).
+constexpr int kCpointResident = 1280;
 constexpr int32_t kWindow = 65536;      // tokens per buffer resource (< 4 GiB)
 
 struct Meta {
@@ -935,8 +939,8 @@ static spicy_status launch_coarsen_t(const CoarsenArgs& a, hipStream_t stream) {
     else
         hipLaunchKernelGGL((coarsen_main_kernel<T, D, false, false>), grid, block, 0, stream, a);
     if (hipGetLastError() != hipSuccess) return SPICY_ERR_HIP;
-    // entries: about kResidentBlocks workgroups shared by the sequences
-    const int cx = max(1, min(kCpointBlocksPerSeq, kResidentBlocks / max(a.B, 1)));
+    // entries: the resident workgroups shared by the sequences
+    const int cx = max(1, min(kCpointBlocksPerSeq, kCpointResident / max(a.B, 1)));
     hipLaunchKernelGGL((coarsen_cpoint_kernel<T, D>), dim3(cx, a.B), dim3(256), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return SPICY_ERR_HIP;
     return SPICY_OK;
