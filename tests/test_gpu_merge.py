@@ -156,3 +156,45 @@ def test_merge_of_gpu_coarsening_runs_in_the_pipeline():
     oracle.merge_level(ref, wl.page_table, wl.step.entry_start, rlen, wl.step.rope_base)
     ro, rlse = oracle.decode(wl.q, wl.dtype, ref, wl.H_q, wl.page_table, rlen)
     compare_decode(dw.o, dw.lse, ro, rlse, wl.dtype)
+
+
+def test_merge_edge_ranges():
+    """Empty ranges, a range holding one macro-node, a range that starts on a
+    C-point, and fp32 storage at d = 128: the same as the oracle; an empty
+    call (every range empty) leaves the cache bit-identical."""
+    _need_gpu()
+    wl = W.qwen2_7b(B=4, T=3000, dtype="f32")
+    ref = oracle.Cache(wl.dtype, wl.num_pages, wl.H_kv, wl.d)
+    lengths = None
+    for c in wl.calls:
+        lengths = oracle.coarsen(c, ref)
+    g0 = upload_with_meta(ref)
+    before = {f: getattr(g0, f).clone() for f in ("k", "v", "ab", "meta")}
+    gpu_merge(g0, wl, lengths, lengths)                          # every range empty
+    for f, t in before.items():
+        assert torch.equal(getattr(g0, f), t), f"an empty merge changed {f}"
+    kinds = ref.meta["kind"]
+    # sequence 0: from its second entry; 1: nothing; 2: only its first macro-node; 3: everything
+    first_mac = [next(e for e in range(int(lengths[b])) if kinds[wl.page_table[b, e // 16], 0, e % 16] == 2)
+                 for b in range(wl.B)]
+    begin = np.array([1, 5, first_mac[2], 0], dtype=np.int32)
+    end = np.array([lengths[0], 5, first_mac[2] + 1, lengths[3]], dtype=np.int32)
+    gcache = upload_with_meta(ref)
+    oracle.merge_level(ref, wl.page_table, begin, end, wl.calls[-1].rope_base)
+    gpu_merge(gcache, wl, begin, end)
+    ex = compare_merged(gcache, ref, wl, lengths)
+    assert ex["k"] > 0.99 and ex["v"] > 0.99
+
+
+def test_merge_rejects_diagonal_caches_and_missing_metadata():
+    _need_gpu()
+    import coarse_grained_decode_amd as cgd
+    wl = W.qwen2_1p5b(d=64, B=4, T=4096)
+    tb = torch.from_numpy(wl.page_table.astype(np.int32)).to(DEV)
+    z = torch.zeros(wl.B, dtype=torch.int32, device=DEV)
+    ws = cgd.workspace(cgd.spicy_merge_workspace_bytes(wl.B, wl.H_kv, 16), DEV)
+    for kw, code in ((dict(meta=True, diag=True), 4), (dict(meta=False), 1)):
+        cache = cgd.PagedCache.empty(wl.num_pages, wl.H_kv, wl.d, torch.bfloat16, DEV, **kw)
+        with pytest.raises(cgd.SpicyError) as e:
+            cgd.spicy_merge_level(cache, 1e6, tb, z, z, 16, ws)
+        assert e.value.status == code

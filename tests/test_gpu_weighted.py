@@ -129,3 +129,21 @@ def test_policy_variation_feeds_weighted_coarsen():
     assert np.array_equal(glen, rlen)
     stats = compare_cache(types.SimpleNamespace(wl=wl, cache=cache), rcache, rlen)
     assert stats["k_exact"] > 0.999 and stats["v_exact"] > 0.999
+
+
+def test_weighted_with_diagonal_closure_matches_oracle():
+    """Both variants at once (the streaming role's DIAG + WEIGHTED
+    instantiation): the cache and the variance sidecar against the oracle."""
+    _need_gpu()
+    from test_gpu_diag import compare_s2
+    for name in ("qwen2_7b_small", "bf16_d64"):
+        wl = WORKLOADS[name]()
+        print(f"[weighted+diag] {name}", flush=True)
+        weights = [W.token_weights(c, 31 + i) for i, c in enumerate(wl.calls)]
+        rcache, rlen = oracle_run(wl, weights, diag=True)
+        gcache, glen = gpu_run(wl, weights, diag=True)
+        assert np.array_equal(glen, rlen)
+        stats = compare_cache(types.SimpleNamespace(wl=wl, cache=gcache), rcache, rlen)
+        assert stats["k_exact"] > 0.999 and stats["v_exact"] > 0.999
+        pages = touched_pages(wl.page_table, rlen)
+        compare_s2(host(gcache.s2)[pages], rcache.s2[pages], rcache.meta["kind"][pages], wl.dtype)
