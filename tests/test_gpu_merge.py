@@ -198,3 +198,27 @@ def test_merge_rejects_diagonal_caches_and_missing_metadata():
         with pytest.raises(cgd.SpicyError) as e:
             cgd.spicy_merge_level(cache, 1e6, tb, z, z, 16, ws)
         assert e.value.status == code
+
+
+def test_merge_range_above_max_range_sets_error_and_merges_nothing():
+    """A range longer than max_range raises SPICY_DEVERR_SEGMENTS and that
+    (sequence, head) is left alone; max_range = 0 with every range empty is
+    a no-op without error."""
+    _need_gpu()
+    import coarse_grained_decode_amd as cgd
+    wl = W.qwen2_1p5b(d=64, B=4, T=4096)
+    ref = oracle.Cache(wl.dtype, wl.num_pages, wl.H_kv, wl.d)
+    for c in wl.calls:
+        lengths = oracle.coarsen(c, ref)
+    g = upload_with_meta(ref)
+    before = {f: getattr(g, f).clone() for f in ("k", "v", "ab", "meta")}
+    tb = torch.from_numpy(wl.page_table.astype(np.int32)).to(DEV)
+    zero = torch.zeros(wl.B, dtype=torch.int32, device=DEV)
+    ln = torch.from_numpy(lengths.astype(np.int32)).to(DEV)
+    for rng, end, err in ((8, ln, 0x4), (0, zero, 0)):
+        ws = cgd.workspace(cgd.spicy_merge_workspace_bytes(wl.B, wl.H_kv, rng), DEV)
+        cgd.spicy_merge_level(g, wl.calls[-1].rope_base, tb, zero, end, rng, ws)
+        torch.cuda.synchronize()
+        assert cgd.device_error(ws) == err
+        for f, t in before.items():
+            assert torch.equal(getattr(g, f), t), f"{f} changed"
