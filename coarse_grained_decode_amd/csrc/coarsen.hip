@@ -7,26 +7,33 @@
 // beta = sigma^2 / (2d) (sigma^2 = per-dimension population variance of the
 // member keys); protected ("C") tokens stay exact (mass 1, own position).
 //
-// Three kernels:
-//   coarsen_plan  one 256-thread workgroup per sequence, one thread per
-//                 segment: counts the protected tokens of each (segment,
-//                 head) with 32 mask rows in flight, block-scans the per-head
-//                 entry counts into entry offsets (and the C-point counts into
-//                 item offsets), writes a compact descriptor per segment, then
-//                 lists the segment's C-points as items {token, entry, head}
-//                 in position order per head; records the sequence's length
-//                 and where each head's null padding starts.
-//   coarsen_main  one wavefront per segment and group of KV heads (4 heads at
-//                 d = 128).  A lane owns 8 consecutive dimensions of one head,
-//                 so one 16-byte load per lane reads a whole token row of the
-//                 wave's heads; tokens stream through a register ring.
-//                 F-tokens are accumulated branch-free in double precision
-//                 (mask as a 0/1 weight) and the macro-node is written at the
-//                 segment end.  Bound by reading K and V from HBM.
-//   coarsen_cpoint the listed C-point items, spread over ~1024 workgroups:
-//                 every 16-lane group stores one item at a time (value bits
-//                 copied, key rotated to the token's position), prefetching
-//                 the next; then the null entries the same way.
+// Two kernels:
+//   coarsen_main   two roles that share nothing, so they run side by side.
+//     plan role:   one 256-thread workgroup per sequence, one thread per
+//                  segment: counts the protected tokens of each (segment,
+//                  head) with 32 mask rows in flight, block-scans the per-head
+//                  entry counts into entry offsets (and the C-point counts
+//                  into item offsets), writes a compact descriptor per
+//                  segment, then lists the segment's C-points as items
+//                  {token, entry, head} in position order per head; records
+//                  the sequence's length and where each head's null padding
+//                  starts.
+//     streaming:   persistent workgroups, one wavefront per segment and group
+//                  of KV heads (4 heads at d = 128).  A lane owns 8
+//                  consecutive dimensions of one head, so one 16-byte load per
+//                  lane reads a whole token row of the wave's heads; tokens
+//                  stream through a register ring.  F-tokens are accumulated
+//                  branch-free in double precision (mask as a 0/1 weight) and
+//                  the macro-node is staged at the segment end.  Bound by
+//                  reading K and V from HBM.
+//   coarsen_cpoint every entry of a sequence in one index space (staged
+//                  macro-nodes, listed C-points with the key rotated to the
+//                  token's position, null padding), spread over its 1280
+//                  resident workgroups, one entry per 16-lane group at a time.
+// Variants of the streaming role: the diagonal closure (per-dimension
+// variances of the rotated member keys, when the cache has that sidecar) and
+// variation-weighted representatives (per-token weights, from
+// spicy_coarsen_weighted); they are described where they are summed.
 //
 // Exactness: inputs are bf16 (8 significant bits).  Sums of bf16 values and
 // of their squares are exact in double precision for any realistic segment,
@@ -45,7 +52,9 @@ constexpr int kPlanWaves = kPlanThreads / kWave;
 constexpr int kCpointBlocksPerSeq = 64;
 constexpr int kMaxH = 16;
 constexpr int kRing = 3;
-constexpr int kResidentBlocks = 1024;   // 4 workgroups of 4 waves per CU
+// streaming workgroups: twice the 512 that coarsen_main's register use fits
+// at once (2 of 4 waves per CU); the later ones start as earlier ones finish
+constexpr int kResidentBlocks = 1024;
 // coarsen_cpoint's register use allows 5 waves per SIMD: 5 workgroups of 4
 // waves per CU, 1280 on the chip.  A grid of exactly that many runs in one
 // round (measured: 1024 or 2048 workgroups are 2-4 us slower).

@@ -30,17 +30,22 @@
 //       into two bf16 terms hi + lo that hold it exactly, so the product is
 //       d/16 MFMAs with fp32 accumulation of exact bf16 products.
 // One launch holds two kinds of workgroups:
-//   split-K: one wavefront per (sequence, KV head, split).  Its tile is the
-//       G = H_q / H_kv query heads of that KV head, and it prefetches its pages
-//       NBUF deep in registers.
+//   split-K: one wavefront per (sequence, KV head, split, query tile).  A
+//       query row is a (query token, query head of that KV head) pair: with
+//       n_q query tokens per sequence a KV head has n_q x G rows in
+//       ceil(n_q G / 16) tiles (one tile of G rows for single-token decode).
+//       The wavefronts of a workgroup are the tiles of one split (1, 2 or 4
+//       of them), so they read its pages together through one L2; each
+//       prefetches its pages NBUF deep in registers.
 //   shared prefix (only when the caller declares one): the first P logical
 //       pages map to the same physical pages in every sequence.  One wavefront
 //       applies a chunk of them to a tile of 16 rows drawn from all sequences
-//       (B x G rows per KV head).  The wavefronts of one (chunk, KV head) run
-//       on one XCD, so HBM delivers each shared page once to its L2.
+//       (B x n_q x G rows per KV head).  The wavefronts of one (chunk, KV
+//       head) run on one XCD, so HBM delivers each shared page once to its L2.
 // Both kinds write partials (running max, sum, unnormalised output) to the
 // workspace.  combine_kernel merges the partials of each (sequence, query
-// head) by log-sum-exp and writes O (fp32) and LSE (natural log).
+// token, query head) by log-sum-exp and writes O (fp32) and LSE (natural
+// log).
 //
 // fp32 caches (decode_f32_kernel): a plain VALU kernel, one wavefront per
 // (sequence, query head, split), lanes = 16 entries x 4 quarter-rows.  It has
