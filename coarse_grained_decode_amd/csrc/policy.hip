@@ -54,11 +54,15 @@ constexpr int kSeqThreads = 512;
 constexpr int kPer = 16;             // tokens (or candidates) a sequence-kernel thread holds
 constexpr int64_t kRangeLimit = int64_t(1) << 62;
 
+// fix(x): x * 2^16 rounded half to even (exact in fp32), then the hardware
+// conversion to int32, which saturates out-of-range values and turns NaN into
+// 0 (written as the instruction itself: a C++ conversion of NaN or of an
+// out-of-range value is undefined), then the clamp to +-2^28.
 __device__ __forceinline__ int32_t fix16(uint32_t bf16_bits) {
-    const float x = __uint_as_float(bf16_bits << 16);
-    if (x != x) return 0;
-    const float y = __builtin_amdgcn_fmed3f(__builtin_rintf(x * 65536.0f), -268435456.0f, 268435456.0f);
-    return static_cast<int32_t>(y);
+    const float y = __builtin_rintf(__uint_as_float(bf16_bits << 16) * 65536.0f);
+    int32_t i;
+    asm("v_cvt_i32_f32 %0, %1" : "=v"(i) : "v"(y));
+    return min(max(i, -268435456), 268435456);
 }
 
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {
