@@ -185,10 +185,11 @@ struct Tile {
         for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    // Fold logical page lp into the state.  A row's entries at or past its
-    // length get weight zero; a page whose id was invalid is skipped.
-    __device__ __forceinline__ void process(const PageRegs<D, DIAG>& r, int32_t lp) {
-        if (!r.ok) return;
+    // The logits of logical page lp for this tile's rows and the online-softmax
+    // update: returns the factor the running output must be scaled by and the
+    // probabilities as the B operand of the P.V product.  A row's entries at
+    // or past its length get weight zero.
+    __device__ __forceinline__ float softmax(const PageRegs<D, DIAG>& r, int32_t lp, s16x4& pk) {
         const int grp = (threadIdx.x % kWave) / 16;
         const float c_dot = kLog2e / sqrtf(static_cast<float>(D));
         f32x4 s = {0.f, 0.f, 0.f, 0.f};
@@ -230,35 +231,8 @@ struct Tile {
         m_run = m_new;
         const bf16x4 pb = {static_cast<__bf16>(p[0]), static_cast<__bf16>(p[1]),
                            static_cast<__bf16>(p[2]), static_cast<__bf16>(p[3])};
-        const s16x4 pk = __builtin_bit_cast(s16x4, pb);
-        // V^T tiles for the product: V_chunk (16 entries x 32 dims, loaded as
-        // an A operand like K) times a selector gives V^T of 16 of its dims in
-        // the accumulator layout (lane: entries 4g .. 4g+3 of dim lane%16),
-        // exactly the A operand layout of O^T += V^T P^T.  The products are
-        // exact: one bf16 term per output, the rest zeros.
-        const bool partial = lp * kPage + kPage > vlen;
-#pragma unroll
-        for (int i = 0; i < KC; ++i) {
-#pragma unroll
-            for (int hsel = 0; hsel < 2; ++hsel) {
-                const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                const f32x4 vtf = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.v[i], sel[hsel], z, 0, 0, 0);
-                uint32_t u[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    u[j] = __float_as_uint(vtf[j]);
-                    // slots no row uses may hold anything: zero their values so
-                    // that 0 * NaN cannot poison the product
-                    if (partial && ebase + j >= vlen) u[j] = 0;
-                }
-                const uint32_t w0 = __builtin_amdgcn_perm(u[1], u[0], 0x07060302u);
-                const uint32_t w1 = __builtin_amdgcn_perm(u[3], u[2], 0x07060302u);
-                const s16x4 vt = __builtin_bit_cast(s16x4, make_uint2(w0, w1));
-                const int t = 2 * i + hsel;
-                acc[t] *= scale;
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pk, acc[t], 0, 0, 0);
-            }
-        }
+        pk = __builtin_bit_cast(s16x4, pb);
+        return scale;
     }
 
     // Finish the row sums (held per lane group) and store this lane's row as
@@ -279,6 +253,55 @@ struct Tile {
         for (int t = 0; t < NT; ++t) *reinterpret_cast<f32x4*>(po + 16 * t) = acc[t];
     }
 };
+
+// Fold logical page lp into the first `ntile` (uniform, >= 1) of a
+// wavefront's TPW tiles; a page whose id was invalid is skipped.  The V^T
+// operand tiles are formed once and serve every tile: V_chunk (16 entries x
+// 32 dims, loaded as an A operand like K) times a selector gives V^T of 16 of
+// its dims in the accumulator layout (lane: entries 4g .. 4g+3 of dim
+// lane%16), exactly the A operand layout of O^T += V^T P^T.  The products
+// are exact: one bf16 term per output, the rest zeros.  vlen: the largest
+// length of the tiles' rows; slots at or past it may hold anything, so their
+// values are zeroed (0 * NaN must not poison the product).
+template <int D, bool DIAG, int TPW>
+__device__ __forceinline__ void fold_page(Tile<D, DIAG> (&T)[TPW], int ntile, const PageRegs<D, DIAG>& r,
+                                          int32_t lp, int32_t vlen) {
+    constexpr int KC = D / 32;
+    if (!r.ok) return;
+    s16x4 pk[TPW];
+    float scale[TPW];
+#pragma unroll
+    for (int k = 0; k < TPW; ++k)
+        if (k < ntile) scale[k] = T[k].softmax(r, lp, pk[k]);
+    const int grp = (threadIdx.x % kWave) / 16;
+    const int32_t ebase = lp * kPage + 4 * grp;
+    const bool partial = lp * kPage + kPage > vlen;
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+#pragma unroll
+        for (int hsel = 0; hsel < 2; ++hsel) {
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            const f32x4 vtf = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.v[i], T[0].sel[hsel], z, 0, 0, 0);
+            uint32_t u[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                u[j] = __float_as_uint(vtf[j]);
+                if (partial && ebase + j >= vlen) u[j] = 0;
+            }
+            const uint32_t w0 = __builtin_amdgcn_perm(u[1], u[0], 0x07060302u);
+            const uint32_t w1 = __builtin_amdgcn_perm(u[3], u[2], 0x07060302u);
+            const s16x4 vt = __builtin_bit_cast(s16x4, make_uint2(w0, w1));
+            const int t = 2 * i + hsel;
+#pragma unroll
+            for (int k = 0; k < TPW; ++k) {
+                if (k < ntile) {
+                    T[k].acc[t] *= scale[k];
+                    T[k].acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pk[k], T[k].acc[t], 0, 0, 0);
+                }
+            }
+        }
+    }
+}
 
 }  // namespace
 
@@ -301,7 +324,7 @@ struct Tile {
 // (uniform).  Pages past the window's end load its last page again (every
 // load is unconditional, so each wait covers exactly one page); they are
 // never processed.
-template <int D, int NBUF, bool DIAG>
+template <int D, int NBUF, bool DIAG, int TPW>
 __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
     const int lane = threadIdx.x % kWave;
     const int wave = threadIdx.x / kWave;
@@ -310,22 +333,26 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
     const int G = a.H_q / H;
     int64_t blk = static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x;
 
-    int h, slot, t = 0;
+    // The wavefront's TPW query tiles are tiles TPW * wt + k, k < ntile
+    // (ntile: the ones that hold rows); per tile, this lane's row.
+    int h, slot, wt = 0, ntile = 1;
     int32_t p0, p1;
     int32_t id_end;        // page-id entries this wavefront's table row holds
     const int32_t* table;
-    int64_t prow;          // this lane's partial row (sequence * H_q + query head)
-    int32_t raw_len;       // this lane's sequence length as read, checked below
-    bool row_valid;
+    int64_t prow[TPW];     // this lane's partial row (sequence * H_q + query head) in tile k
+    int32_t raw_len[TPW];  // that row's sequence length as read, checked below
+    bool row_valid[TPW];
     const bool prefix_role = blk < a.prefix_blocks;
     // The query rows and the first window of page ids do not depend on the
     // length: each role issues their loads together with it, so the wavefront
     // waits one memory round trip before its first pages are requested.
-    Tile<D, DIAG> T;
+    Tile<D, DIAG> T[TPW];
     int32_t ids;
     int64_t prow0;         // a valid query row of the wavefront's KV head
     auto issue_loads = [&]() {
-        T.load_q(static_cast<const uint16_t*>(a.q) + (row_valid ? prow : prow0) * D);
+#pragma unroll
+        for (int k = 0; k < TPW; ++k)
+            T[k].load_q(static_cast<const uint16_t*>(a.q) + (row_valid[k] ? prow[k] : prow0) * D);
         ids = (p0 + lane < min(p0 + kWave, id_end)) ? table[p0 + lane] : 0;
         // keep the compiler from sinking those loads below the exit test
         asm volatile("" ::: "memory");
@@ -334,59 +361,77 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
         const int per_xcd = a.prefix_blocks / kXcds;      // prefix_blocks is a multiple of 8
         int w = static_cast<int>(blk % kXcds) * per_xcd + static_cast<int>(blk / kXcds);
         const int tgb = a.prefix_tile_blocks;
-        t = (w % tgb) * kWavesPerBlock + wave;
+        wt = (w % tgb) * kWavesPerBlock + wave;
         w /= tgb;
         h = w % H;
         const int c = w / H;
         const int rows = a.B * a.n_q * G;                  // rows (sequence, token, query head)
-        if (c >= a.prefix_splits || t * 16 >= rows) return;
+        if (c >= a.prefix_splits || TPW * wt * 16 >= rows) return;
+        ntile = min(TPW, (rows - TPW * wt * 16 + 15) / 16);
         slot = c;
         p0 = c * a.prefix_chunk;
         p1 = min(p0 + a.prefix_chunk, a.prefix_pages);
         id_end = a.prefix_pages;
         table = a.page_table;
-        const int r = t * 16 + row;
-        row_valid = r < rows;
-        const int rq = row_valid ? r : 0;
-        const int bq = rq / (a.n_q * G);                    // sequence
-        const int vq = rq / G;                              // sequence * n_q + token
-        prow = static_cast<int64_t>(vq) * a.H_q + static_cast<int64_t>(h) * G + rq % G;
-        raw_len = row_valid ? a.lengths[bq] : 0;
         prow0 = static_cast<int64_t>(h) * G;
+#pragma unroll
+        for (int k = 0; k < TPW; ++k) {
+            const int r = (TPW * wt + k) * 16 + row;
+            row_valid[k] = r < rows;
+            const int rq = row_valid[k] ? r : 0;
+            const int bq = rq / (a.n_q * G);                // sequence
+            const int vq = rq / G;                          // sequence * n_q + token
+            prow[k] = static_cast<int64_t>(vq) * a.H_q + static_cast<int64_t>(h) * G + rq % G;
+            raw_len[k] = row_valid[k] ? a.lengths[bq] : 0;
+        }
         issue_loads();
     } else {
         blk -= a.prefix_blocks;
-        // a workgroup's wavefronts: kWavesPerBlock / wpt splits x wpt tiles of
-        // each, so the tiles of one split read its pages together (one L2)
+        // a workgroup's wavefronts: kWavesPerBlock / wpt splits x wpt
+        // wavefronts of each, so the tiles of one split read its pages
+        // together (one L2)
+        const int wtiles = (a.priv_tiles + TPW - 1) / TPW;   // wavefronts per split
         const int wpt = a.priv_wpt;
         const int spb = kWavesPerBlock / wpt;
         const int sgb = (a.priv_splits + spb - 1) / spb;
-        const int ntg = (a.priv_tiles + wpt - 1) / wpt;
+        const int ntg = (wtiles + wpt - 1) / wpt;
         const int split = static_cast<int>(blk % sgb) * spb + wave / wpt;
         blk /= sgb;
-        const int tile = static_cast<int>(blk % ntg) * wpt + wave % wpt;
+        wt = static_cast<int>(blk % ntg) * wpt + wave % wpt;
         blk /= ntg;
         h = static_cast<int>(blk % H);
         const int64_t b = blk / H;
-        if (split >= a.priv_splits || tile >= a.priv_tiles || b >= a.B) return;
+        if (split >= a.priv_splits || wt >= wtiles || b >= a.B) return;
+        ntile = min(TPW, a.priv_tiles - TPW * wt);
         slot = a.prefix_splits + split;
-        raw_len = a.lengths[b];
         p0 = a.page_begin + split * a.pages_per_split;
         p1 = p0 + a.pages_per_split;                      // clamped to the length below
         id_end = a.max_pages;
         table = a.page_table + b * a.max_pages;
-        // the tile's rows: (token, query head) pairs r = token * G + g of this KV head
-        const int r = tile * 16 + row;
-        row_valid = r < a.n_q * G;
-        const int rq = row_valid ? r : 0;
-        prow = (b * a.n_q + rq / G) * a.H_q + static_cast<int64_t>(h) * G + rq % G;
         prow0 = b * a.n_q * a.H_q + static_cast<int64_t>(h) * G;
+        // the tiles' rows: (token, query head) pairs r = token * G + g of this KV head
+        const int32_t lb = a.lengths[b];
+#pragma unroll
+        for (int k = 0; k < TPW; ++k) {
+            const int r = (TPW * wt + k) * 16 + row;
+            row_valid[k] = r < a.n_q * G;
+            const int rq = row_valid[k] ? r : 0;
+            prow[k] = (b * a.n_q + rq / G) * a.H_q + static_cast<int64_t>(h) * G + rq % G;
+            raw_len[k] = lb;
+        }
         issue_loads();
     }
-    const int32_t len = (prefix_role && !row_valid) ? 0 : check_length(a, raw_len);
-    if (!prefix_role) p1 = min(p1, (len + kPage - 1) / kPage);
+    int32_t len[TPW];
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) len[k] = (prefix_role && !row_valid[k]) ? 0 : check_length(a, raw_len[k]);
+    if (!prefix_role) p1 = min(p1, (len[0] + kPage - 1) / kPage);
     if (p0 >= p1) return;
-    T.init(row_valid, row_valid ? len : 0);
+    int32_t vlen = 0;
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+        T[k].init(row_valid[k], row_valid[k] ? len[k] : 0);
+        if (k < ntile) vlen = max(vlen, T[k].vlen);
+    }
 
     // Pages go in windows of 64: one vector load brings the window's page ids
     // (lane i: page w0 + i) before its pipeline starts, so no wait inside the
@@ -403,20 +448,22 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
         for (int32_t lp = w0; lp < w1; lp += NBUF) {
 #pragma unroll
             for (int i = 0; i < NBUF; ++i) {
-                if (lp + i < w1) T.process(buf[i], lp + i);
+                if (lp + i < w1) fold_page<D, DIAG, TPW>(T, ntile, buf[i], lp + i, vlen);
                 load(buf[i], lp + i + NBUF);
             }
         }
     }
-    T.store(a, row_valid, prow, slot);
+#pragma unroll
+    for (int k = 0; k < TPW; ++k)
+        if (k < ntile) T[k].store(a, row_valid[k], prow[k], slot);
 
     // The KV head 0 wavefronts of the shared prefix check that the sequences
-    // of their tile map the chunk's pages like sequence 0 (independent loads,
+    // of their tiles map the chunk's pages like sequence 0 (independent loads,
     // one flag).  It is done last, off the path to the first pages.
     if (prefix_role && h == 0) {
         const int rows = a.B * a.n_q * G;
-        const int b_first = (t * 16) / (a.n_q * G);
-        const int b_last = min(rows - 1, t * 16 + 15) / (a.n_q * G);
+        const int b_first = (TPW * wt * 16) / (a.n_q * G);
+        const int b_last = min(rows - 1, (TPW * wt + ntile) * 16 - 1) / (a.n_q * G);
         const int npg = p1 - p0;
         const int n = (b_last - b_first + 1) * npg;
         bool bad = false;
@@ -603,31 +650,49 @@ __global__ __launch_bounds__(64) void combine_kernel(DecodeArgs a) {
 
 // ------------------------------------------------------------------ launch
 
-constexpr int kNbuf = 4;
+constexpr int kNbuf = 4;                  // one tile per wavefront
+constexpr int kNbufPair = 2;              // two tiles per wavefront: their state takes a page's registers
 constexpr int kNbufDiag = 2;              // the variance pages add a third page-sized load
 constexpr int64_t kMaxGridX = 65536;
+
+// Grid of the bf16 kernel with TPW tiles per wavefront: the shared-prefix
+// workgroups (a multiple of 8, see the XCD remap), then the split-K ones.
+template <int TPW>
+static dim3 mfma_grid(DecodeArgs& a) {
+    const int G = a.H_q / a.cache.H;
+    const int tiles = (a.B * a.n_q * G + 15) / 16;
+    const int wtiles = (tiles + TPW - 1) / TPW;
+    a.prefix_tile_blocks = (wtiles + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int64_t pb = static_cast<int64_t>(a.prefix_splits) * a.cache.H * a.prefix_tile_blocks;
+    a.prefix_blocks = static_cast<int32_t>((pb + kXcds - 1) / kXcds * kXcds);
+    const int pw = (a.priv_tiles + TPW - 1) / TPW;   // wavefronts per split
+    a.priv_wpt = pw >= 3 ? 4 : pw;
+    const int64_t spb = kWavesPerBlock / a.priv_wpt;
+    const int64_t sgb = (a.priv_splits + spb - 1) / spb;
+    const int64_t ntg = (pw + a.priv_wpt - 1) / a.priv_wpt;
+    const int64_t nblk = a.prefix_blocks + sgb * ntg * a.cache.H * a.B;
+    const int64_t gx = nblk < kMaxGridX ? nblk : kMaxGridX;
+    const int64_t gy = (nblk + gx - 1) / gx;
+    return dim3(static_cast<unsigned>(gx), static_cast<unsigned>(gy));
+}
 
 template <int D>
 static spicy_status launch_decode_t(const DecodeArgs& a0, int dtype, hipStream_t stream) {
     DecodeArgs a = a0;
     if (dtype == SPICY_BF16) {
-        const int G = a.H_q / a.cache.H;
-        const int tiles = (a.B * a.n_q * G + 15) / 16;
-        a.prefix_tile_blocks = (tiles + kWavesPerBlock - 1) / kWavesPerBlock;
-        const int64_t pb = static_cast<int64_t>(a.prefix_splits) * a.cache.H * a.prefix_tile_blocks;
-        a.prefix_blocks = static_cast<int32_t>((pb + kXcds - 1) / kXcds * kXcds);
-        a.priv_wpt = a.priv_tiles >= 3 ? 4 : a.priv_tiles;
-        const int64_t spb = kWavesPerBlock / a.priv_wpt;
-        const int64_t sgb = (a.priv_splits + spb - 1) / spb;
-        const int64_t ntg = (a.priv_tiles + a.priv_wpt - 1) / a.priv_wpt;
-        const int64_t nblk = a.prefix_blocks + sgb * ntg * a.cache.H * a.B;
-        const int64_t gx = nblk < kMaxGridX ? nblk : kMaxGridX;
-        const int64_t gy = (nblk + gx - 1) / gx;
-        const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(gy));
-        if (a.cache.s2)
-            hipLaunchKernelGGL((decode_mfma_kernel<D, kNbufDiag, true>), grid, dim3(kWavesPerBlock * kWave), 0, stream, a);
-        else
-            hipLaunchKernelGGL((decode_mfma_kernel<D, kNbuf, false>), grid, dim3(kWavesPerBlock * kWave), 0, stream, a);
+        const dim3 block(kWavesPerBlock * kWave);
+        if (a.cache.s2) {
+            const dim3 grid = mfma_grid<1>(a);
+            hipLaunchKernelGGL((decode_mfma_kernel<D, kNbufDiag, true, 1>), grid, block, 0, stream, a);
+        } else if (a.priv_tiles >= 2) {
+            // several query tiles per (sequence, KV head): a wavefront takes two,
+            // so each page it loads serves both and its V^T is formed once
+            const dim3 grid = mfma_grid<2>(a);
+            hipLaunchKernelGGL((decode_mfma_kernel<D, kNbufPair, false, 2>), grid, block, 0, stream, a);
+        } else {
+            const dim3 grid = mfma_grid<1>(a);
+            hipLaunchKernelGGL((decode_mfma_kernel<D, kNbuf, false, 1>), grid, block, 0, stream, a);
+        }
     } else {
         const int wpb = a.priv_splits < 4 ? a.priv_splits : 4;
         dim3 grid((a.priv_splits + wpb - 1) / wpb, a.H_q, a.B * a.n_q);
