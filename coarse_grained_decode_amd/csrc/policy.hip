@@ -352,6 +352,7 @@ __global__ __launch_bounds__(kSeqThreads) void policy_seq_kernel(PolicyArgs a) {
     __shared__ uint32_t hist[256];
     __shared__ uint32_t s_digit;
     __shared__ int64_t s_above;
+    __shared__ unsigned long long s_or;
     constexpr int64_t kRound = static_cast<int64_t>(kSeqThreads) * kPer;   // tokens per round
     const int tid = threadIdx.x;
     const int b = blockIdx.x;
@@ -454,7 +455,25 @@ __global__ __launch_bounds__(kSeqThreads) void policy_seq_kernel(PolicyArgs a) {
             const int64_t u = c_lo + tid + static_cast<int64_t>(kSeqThreads) * m;
             vals[m] = (in_regs && u < c_hi) ? a.norm2[(t0 + u) * H + h] : 0;
         }
-        for (int shift = 56; shift >= 0; shift -= 8) {
+        // digits above the largest candidate's top byte are 0 for every
+        // candidate: those passes would select digit 0 and change nothing, so
+        // the select starts at that byte
+        unsigned long long vor = 0;
+        if (in_regs) {
+#pragma unroll
+            for (int m = 0; m < kPer; ++m) vor |= vals[m];
+        } else {
+            for (int64_t u = c_lo + tid; u < c_hi; u += kSeqThreads) vor |= a.norm2[(t0 + u) * H + h];
+        }
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) vor |= shfl_xor_u64(vor, o);
+        if (tid == 0) s_or = 0;
+        __syncthreads();
+        if ((threadIdx.x % kWave) == 0) atomicOr(&s_or, vor);
+        __syncthreads();
+        const uint64_t top = s_or;
+        const int shift0 = top ? (63 - __clzll(top)) / 8 * 8 : 0;
+        for (int shift = shift0; shift >= 0; shift -= 8) {
             if (tid < 256) hist[tid] = 0;
             __syncthreads();
             if (in_regs) {
