@@ -47,7 +47,7 @@ namespace spicy {
 namespace {
 
 constexpr int kRun = 32;             // tokens per wavefront
-constexpr int kRing = 4;             // token rows in flight per wavefront
+constexpr int kRing = 3;             // token rows in flight per wavefront (3: 128 VGPRs, 4 waves per SIMD)
 constexpr int kMaxEnt = 16;          // projection entries a lane keeps in registers
 constexpr int kTokWaves = 4;         // wavefronts per token workgroup
 constexpr int kSeqThreads = 512;
