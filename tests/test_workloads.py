@@ -147,3 +147,28 @@ def test_shared_prefix_structure():
     assert np.all(chunk.pos_base == 4096 + S)
     assert np.all(chunk.entry_start == pp * 16 + (-(-S // 16)) * 16)
     assert chunk.mask.sum(axis=0).tolist() == [4 * W.landmark_count(1024, 0.01)] * 4
+
+
+def test_variant_inputs_are_seeded_and_shaped():
+    """The next-row input generators: per-token weights (a fifth zero, every
+    7th segment all zero), random variance sidecars (NaN exactly where the
+    decode case planted NaN), query tokens; all deterministic."""
+    wl = W.qwen2_7b(B=2, T=6000)
+    call = wl.calls[-1]
+    w1, w2 = W.token_weights(call, 3), W.token_weights(call, 3)
+    assert w1.dtype == np.int64 and w1.shape == (call.total_tokens,)
+    assert np.array_equal(w1, w2) and not np.array_equal(w1, W.token_weights(call, 4))
+    assert (w1 >= 0).all() and 0.1 < (w1 == 0).mean() < 0.5
+    so = np.asarray(call.seg_offsets)
+    for s in range(0, len(so) - 1, 7):
+        assert not w1[so[s]:so[s + 1]].any()
+    c = W.random_decode_case(5, B=3, H_q=8, H_kv=2, d=64, prefix_pages=2, private_pages=(1, 3))
+    s2 = W.random_variances(c, 5)
+    assert s2.shape == c.k.shape and np.array_equal(s2, W.random_variances(c, 5))
+    vals = (s2.astype(np.uint32) << 16).view(np.float32)
+    alpha = (c.ab[..., 0].astype(np.uint32) << 16).view(np.float32)
+    planted = np.isnan(oracle.rows(vals)).all(-1)
+    assert np.array_equal(planted, np.isnan(alpha))
+    assert (oracle.rows(vals)[~planted] >= 0).all()
+    q4 = W.query_tokens(wl, 4)
+    assert q4.shape == (wl.B, 4, wl.H_q, wl.d) and np.array_equal(q4, W.query_tokens(wl, 4))
