@@ -282,8 +282,8 @@ def main():
     if args.copy_calibration:
         return copy_calibration()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path has no "
-              "multi-GPU leg in this build", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the library has no "
+              "multi-GPU path", file=sys.stderr)
         sys.exit(2)
 
     import torch
