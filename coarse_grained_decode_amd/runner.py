@@ -17,7 +17,7 @@ import torch
 from . import (PagedCache, spicy_coarsen, spicy_coarsen_weighted, spicy_coarsen_workspace_bytes, spicy_decode_attn,
                spicy_decode_attn_shared, spicy_decode_num_splits, spicy_decode_plan, spicy_decode_shared_workspace_bytes,
                spicy_decode_attn_multi, spicy_decode_multi_workspace_bytes, spicy_policy,
-               spicy_policy_workspace_bytes, workspace)
+               spicy_policy_workspace_bytes, spicy_merge_level, spicy_merge_workspace_bytes, workspace)
 from .workloads import CoarsenCall, PolicySpec, Workload, query_tokens
 
 
@@ -127,6 +127,48 @@ class DevicePolicy:
             ws=workspace(spicy_coarsen_workspace_bytes(B, B * N, c.total_tokens, c.H_kv, c.d,
                                                        1 if c.dtype == "bf16" else 0), device),
             token_weight=self.variation if weighted else None)
+
+
+class DyadicPyramid:
+    """Host-side schedule of the cascaded dyadic merge for a batch whose
+    sequences append chunks in lockstep (SPICY-KV demo page, Claim 12: the
+    cascaded dyadic ring-buffer pyramid; Claim 10: the law of total variance
+    across cascades).  The blocks of entries form a binary counter: an
+    appended chunk is a level-0 block; while the two newest blocks have the
+    same level they merge into one block a level up, with one
+    spicy_merge_level call over their union (each macro-node pairs with its
+    neighbour, so the nodes of a level-l block cover 2^l of the chunk's
+    segments).  The schedule is the host's: the pages give no rule for it.
+    """
+
+    def __init__(self, B: int):
+        self.B = B
+        self.blocks: List[tuple] = []          # (begin int32[B], end int32[B], level)
+
+    def append(self, begin, end) -> List[tuple]:
+        """Record a chunk coarsened into entries [begin[b], end[b]) and return
+        the merges it triggers, in order, as (begin, end) int32 arrays."""
+        self.blocks.append((np.asarray(begin, np.int32).copy(), np.asarray(end, np.int32).copy(), 0))
+        merges = []
+        while len(self.blocks) >= 2 and self.blocks[-1][2] == self.blocks[-2][2]:
+            b2 = self.blocks.pop()
+            b1 = self.blocks.pop()
+            merges.append((b1[0], b2[1]))
+            self.blocks.append((b1[0], b2[1], b1[2] + 1))
+        return merges
+
+    @property
+    def levels(self) -> List[int]:
+        return [blk[2] for blk in self.blocks]
+
+    @staticmethod
+    def run(cache: PagedCache, merges, rope_base: float, page_table: torch.Tensor, device, stream=None) -> None:
+        """Issue spicy_merge_level for each (begin, end) merge on the GPU."""
+        for begin, end in merges:
+            rng = int((end - begin).max()) if len(begin) else 0
+            ws = workspace(spicy_merge_workspace_bytes(len(begin), cache.k.shape[1], rng), device)
+            spicy_merge_level(cache, rope_base, page_table, _tensor(begin, None, device), _tensor(end, None, device),
+                              rng, ws, stream)
 
 
 @dataclass
