@@ -1,7 +1,7 @@
 /*
  * spicy.h — C ABI of the MI355X (gfx950) SPICY-KV coarse-grained decode library.
  *
- * Two operations, following the pages' statement of the problem:
+ * Two core operations, following the pages' statement of the problem:
  *
  *   spicy_coarsen      pre-RoPE keys + values + segment partition + protected
  *                      mask  ->  paged compressed cache
@@ -19,6 +19,15 @@
  *                      |q|^2 * half_inv_dk_sigma_sq inside a standard online
  *                      softmax; Claim 3 and abstract item (4): first-order
  *                      log-mass offset and second-order variance closure)
+ *
+ * and the entry points around them: spicy_decode_attn_shared (a prefix of
+ * pages shared by every sequence, read once per KV head), spicy_decode_attn_multi
+ * (several query tokens per sequence), spicy_policy (the per-step segments and
+ * protection mask computed from the chunk itself), spicy_coarsen_weighted
+ * (variation-weighted representatives), spicy_merge_level (one level of the
+ * dyadic merge cascade), the optional per-dimension variance sidecar of the
+ * cache (diagonal closure), and host helpers for workspace sizes and the
+ * split-K plan.
  *
  * Conventions for every entry point
  *   - All buffers are owned and allocated by the caller.  Pointers are DEVICE
