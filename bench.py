@@ -238,43 +238,148 @@ def cpu_baseline(wl, reps: int, policy: bool = False, q_tokens: int = 1, diag: b
                        f"median of {reps} after 1 warm-up, {med:.3f} s per step")
 
 
-def decode_only(args, wl, dw):
-    """Diagnostic mode: the decode call alone.  The compressed cache is
-    copied into L distinct buffers (L x cache bytes >= --rotate-bytes, well
-    above the 256 MB Infinity Cache) and the calls rotate through them, so
-    every call streams its cache from HBM."""
-    import torch
+def _rotating_copies(dw, rotate_bytes: float):
+    """L distinct copies of the compressed cache (L x cache bytes >= rotate_bytes,
+    well above the 256 MB Infinity Cache), so that calls rotating through them
+    stream their cache from HBM."""
     from coarse_grained_decode_amd import PagedCache
-    if dw.step is not None:
-        for c in [dw.step]:
-            c.run(dw.cache)
-        dw.lengths = dw.step.lengths
-    torch.cuda.synchronize()
-    lengths = dw.lengths.cpu().numpy()
     parts = (dw.cache.k, dw.cache.v, dw.cache.ab) + ((dw.cache.s2,) if dw.cache.s2 is not None else ())
     cache_bytes = sum(t.numel() * t.element_size() for t in parts)
-    L = max(1, int(np.ceil(args.rotate_bytes / cache_bytes)))
+    L = max(1, int(np.ceil(rotate_bytes / cache_bytes)))
     copies = [PagedCache(dw.cache.k.clone(), dw.cache.v.clone(), dw.cache.ab.clone(), None,
                          dw.cache.s2.clone() if dw.cache.s2 is not None else None) for _ in range(L)]
-    for i in range(args.warmup * L):
-        dw.decode(copies[i % L])
+    return copies, cache_bytes
+
+
+_SLEEP = {}
+
+
+def _sleep_cycles_for(us: float) -> int:
+    """Cycles for torch.cuda._sleep to keep the GPU busy about `us` microseconds
+    (calibrated once per process)."""
+    import torch
+    if "per_cycle_us" not in _SLEEP:
+        n = 1 << 22
+        torch.cuda._sleep(n)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.cuda._sleep(n)
+        e1.record()
+        e1.synchronize()
+        _SLEEP["per_cycle_us"] = e0.elapsed_time(e1) * 1e3 / n
+    return max(1, int(us / _SLEEP["per_cycle_us"]))
+
+
+def _queued_per_call_us(issue, n_calls: int, reps: int, warmup: int = 2):
+    """Per-call microseconds of `issue()` (n_calls calls on the current
+    stream), measured with the calls back to back on the GPU: a sleep kernel
+    holds the stream while the host enqueues them, and the events bracket only
+    the calls.  The sleep is sized from the host's enqueue time, so no call
+    waits for the host."""
+    import torch
+    t0 = time.perf_counter()
+    issue()
     torch.cuda.synchronize()
-    n = args.steps * L
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    for i in range(n):
-        dw.decode(copies[i % L])
-    ev1.record()
+    host_us = (time.perf_counter() - t0) * 1e6
+    cycles = _sleep_cycles_for(3 * host_us + 2000)
+    out = []
+    for r in range(warmup + reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(cycles)
+        e0.record()
+        t0 = time.perf_counter()
+        issue()
+        host = (time.perf_counter() - t0) * 1e6
+        e1.record()
+        e1.synchronize()
+        gpu = e0.elapsed_time(e1) * 1e3
+        if host > 0.9 * _SLEEP["per_cycle_us"] * cycles:
+            print(f"[bench] warning: enqueueing took {host:.0f} us, longer than the sleep", file=sys.stderr)
+        if r >= warmup:
+            out.append(gpu / n_calls)
+    return out
+
+
+def _stats(xs):
+    xs = sorted(xs)
+    q = lambda f: xs[min(len(xs) - 1, max(0, int(round(f * (len(xs) - 1)))))]
+    return {"median": round(statistics.median(xs), 3), "p10": round(q(0.1), 3), "p90": round(q(0.9), 3)}
+
+
+def read_ceiling_us(nbytes: int, rotate_bytes: float, replays: int = 20):
+    """Plain streaming-read ceiling at `nbytes`: the fastest of a few torch
+    read-only reductions over a tensor of that size, rotating through distinct
+    tensors (L x nbytes >= rotate_bytes), back to back on the GPU.  Returns
+    (microseconds per read, the op that gave it)."""
+    import torch
+    # rows of 4096 floats reduced along the row: each output depends on one
+    # row only, so the reduction needs no cross-workgroup staging; the
+    # output is 1/4096 of the bytes read
+    cols = 4096
+    rows = max(1, nbytes // (4 * cols))
+    L = max(1, int(np.ceil(rotate_bytes / (4 * rows * cols))))
+    bufs = [torch.ones(rows, cols, dtype=torch.float32, device="cuda") for _ in range(L)]
+    outs = [torch.empty(rows, dtype=torch.float32, device="cuda") for _ in range(L)]
+    ops = {"sum": lambda x, o: torch.sum(x, dim=1, out=o), "amax": lambda x, o: torch.amax(x, dim=1, out=o)}
+    best = None
+    for name, op in ops.items():
+        def issue(op=op):
+            for x, o in zip(bufs, outs):
+                op(x, o)
+        us = statistics.median(_queued_per_call_us(issue, L, replays))
+        if best is None or us < best[0]:
+            best = (us, name)
+    del bufs
+    return best
+
+
+def decode_only(args, wl, dw):
+    """Diagnostic mode: the decode call alone, back to back over rotated
+    copies of the cache, next to the streaming-read ceiling of the same byte
+    count."""
+    import torch
+    if dw.step is not None:
+        dw.step.run(dw.cache)
+        dw.lengths = dw.step.lengths
     torch.cuda.synchronize()
-    us = ev0.elapsed_time(ev1) * 1e3 / n
+    line = decode_config_line(wl, dw, args.rotate_bytes, max(args.steps, 10))
+    line["mode"] = "decode-only"
+    print(json.dumps(line), flush=True)
+
+
+def decode_config_line(wl, dw, rotate_bytes: float, replays: int, ceiling: bool = True):
+    """Per-call decode time (median, p10, p90 over repetitions of L rotated
+    calls run back to back), algorithmic bytes and rate, and the read ceiling
+    at that size."""
+    import torch
+    lengths = dw.lengths.cpu().numpy()
+    copies, cache_bytes = _rotating_copies(dw, rotate_bytes)
+    L = len(copies)
+
+    def issue():
+        for c in copies:
+            dw.decode(c)
+    per_call = _queued_per_call_us(issue, L, replays)
+    assert int(dw.dws[0].item()) == 0, "device error word set (decode)"
     db = decode_alg_bytes(wl, lengths, dw.q_tokens, dw.cache.s2 is not None)
+    st = _stats(per_call)
+    us = st["median"]
     gbs = db / (us * 1e-6) / 1e9
-    print(json.dumps({"mode": "decode-only", "workload": wl.name, "calls": n, "layers_rotated": L,
-                      "cache_bytes": int(cache_bytes), "alg_bytes_per_call": int(db), "mean_call_us": round(us, 2),
-                      "achieved_GBps": round(gbs, 1), "frac_of_8TBps": round(gbs / HBM_PEAK_GBS, 4),
-                      "query_tokens_per_s": round(wl.B * dw.q_tokens / (us * 1e-6), 1),
-                      "query_tokens_per_seq": dw.q_tokens, "decode_splits": dw.splits,
-                      "shared_prefix_pages": dw.shared_prefix_pages}), flush=True)
+    out = {"workload": wl.name, "calls_per_replay": L, "replays": replays, "cache_bytes": int(cache_bytes),
+           "alg_bytes_per_call": int(db), "call_us": st, "achieved_GBps": round(gbs, 1),
+           "frac": round(gbs / HBM_PEAK_GBS, 4),
+           "query_tokens_per_s": round(wl.B * dw.q_tokens / (us * 1e-6), 1),
+           "query_tokens_per_seq": dw.q_tokens, "plan": dw.plan, "shared_prefix_pages": dw.shared_prefix_pages}
+    del copies
+    if ceiling:
+        cus, op = read_ceiling_us(db, rotate_bytes)
+        cg = db / (cus * 1e-6) / 1e9
+        out["ceiling"] = {"us": round(cus, 3), "GBps": round(cg, 1), "frac": round(cg / HBM_PEAK_GBS, 4),
+                          "op": f"torch.{op}(dim=1) over fp32 rows of 4096, same byte count, rotated, "
+                                "back to back"}
+        out["frac_of_ceiling"] = round(gbs / cg, 4)
+    return out
 
 
 def main():

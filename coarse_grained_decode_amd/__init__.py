@@ -135,11 +135,11 @@ def _stream(stream) -> int | None:
 class PagedCache:
     """Caller-owned paged compressed cache (device tensors in the library's layout).
 
-    k    [num_pages, H_kv, d/32, 16, 32] rotated key rows, cut in 32-dim chunks
-    v    [num_pages, H_kv, d/32, 16, 32] value rows, the same way
+    k    [num_pages, H_kv, d/8, 16, 8] rotated key rows, cut in 8-dim groups
+    v    [num_pages, H_kv, d/8, 16, 8] value rows, the same way
     ab   [num_pages, H_kv, 16, 2]       (alpha, beta)
     meta [num_pages, H_kv, 16, 4] int32 {kind, mass, pos_sum lo, pos_sum hi} or None
-    s2   [num_pages, H_kv, d/32, 16, 32] per-dimension variance (diagonal closure) or None
+    s2   [num_pages, H_kv, d/8, 16, 8] per-dimension variance (diagonal closure) or None
     """
     k: torch.Tensor
     v: torch.Tensor
@@ -151,11 +151,11 @@ class PagedCache:
     def empty(num_pages: int, H_kv: int, d: int, dtype: torch.dtype, device, meta: bool = True,
               fill: float | None = None, diag: bool = False) -> "PagedCache":
         mk = torch.empty if fill is None else (lambda *s, **kw: torch.full(s, fill, **kw))
-        k = mk(num_pages, H_kv, d // 32, PAGE_SIZE, 32, dtype=dtype, device=device)
-        v = mk(num_pages, H_kv, d // 32, PAGE_SIZE, 32, dtype=dtype, device=device)
+        k = mk(num_pages, H_kv, d // 8, PAGE_SIZE, 8, dtype=dtype, device=device)
+        v = mk(num_pages, H_kv, d // 8, PAGE_SIZE, 8, dtype=dtype, device=device)
         ab = mk(num_pages, H_kv, PAGE_SIZE, 2, dtype=dtype, device=device)
         mt = torch.zeros(num_pages, H_kv, PAGE_SIZE, 4, dtype=torch.int32, device=device) if meta else None
-        s2 = mk(num_pages, H_kv, d // 32, PAGE_SIZE, 32, dtype=dtype, device=device) if diag else None
+        s2 = mk(num_pages, H_kv, d // 8, PAGE_SIZE, 8, dtype=dtype, device=device) if diag else None
         return PagedCache(k, v, ab, mt, s2)
 
     @property

@@ -16,11 +16,18 @@ namespace {
 constexpr size_t kAlign = 256;
 constexpr int32_t kMaxKvHeads = 16;
 constexpr int32_t kMaxGroup = 16;       // query heads per KV head (MFMA columns)
-// The decode wavefronts all fit the chip at once: 256 CUs x 4 SIMDs x 2
-// wavefronts (its register use allows two per SIMD).  Spreading the pages
-// evenly over that many wavefronts, in one round, is what bounds its time.
-constexpr int32_t kResidentWaves = 2048;
-constexpr int32_t kPagesInFlight = 4;     // decode pipeline depth: fewer pages per wave gain nothing
+// Page groups: one workgroup of kWpg wavefronts each; the MFMA kernel's
+// register use allows two wavefronts per SIMD, so two such workgroups per CU
+// run at a time (kRound on the chip).  Every unit (a tile-set of query rows
+// and the pages it reads) is cut into about kTarget / units groups (at least
+// one page per wavefront), and the prefix units take what is left of one
+// round: a workgroup that starts only when another ends pays the whole
+// latency chain of the call again (measured: 5 groups of the 7B layer's
+// units, 320 workgroups of 8 wavefronts, 23 us against 16).
+constexpr int32_t kWpg = 4;
+constexpr int32_t kRound = 512;           // 256 CUs x 2 workgroups
+constexpr int32_t kTarget = 192;          // groups per role: about 3/4 of the CUs
+constexpr int32_t kF32Chunk = 16;         // fp32 kernel: pages per group (4 wavefronts x 4 pages)
 constexpr int32_t kMaxSplits = 256;
 constexpr int32_t kMaxGridY = 65535;      // grid y/z extent limit (sequences, heads)
 constexpr int32_t kMaxPagesPerSeq = 1 << 23;  // entry ids fit the 27 bits a C-point item keeps
@@ -40,61 +47,69 @@ spicy_status check_cache(const spicy_cache* c) {
 
 int32_t ceil_div(int64_t a, int64_t b) { return static_cast<int32_t>((a + b - 1) / b); }
 
-int32_t pages_per_split(int32_t max_pages, int32_t splits) {
-    return std::max<int32_t>(1, ceil_div(max_pages, splits));
-}
-
-// Partial-slot plan of one decode call: prefix_splits chunks of the shared
-// prefix, then priv_splits splits of the private pages [P, max_pages).
+// Page groups of one decode call: prefix_groups groups of the shared prefix
+// (slots 0 .. prefix_groups-1), then priv_groups groups of each (sequence,
+// KV head)'s private pages [P, max_pages).
 struct DecodePlan {
-    int32_t prefix_chunk = 1;
-    int32_t prefix_splits = 0;
-    int32_t priv_splits = 1;
-    int32_t pages_per_split = 1;
-    int32_t slots() const { return prefix_splits + priv_splits; }
+    int32_t prefix_chunk = 0;
+    int32_t prefix_groups = 0;
+    int32_t priv_chunk = 0;
+    int32_t priv_groups = 0;
+    int32_t wpg = kWpg;
+    int32_t slots() const { return prefix_groups + priv_groups; }
 };
-
-constexpr int32_t kMaxPrefixChunk = 64;     // one page id per lane
-
-// Pages per wavefront that spread `visits` page visits (one wavefront visit
-// = one page of one KV head for one tile of query rows) over the resident
-// wavefronts, at least the pipeline depth.
-int32_t pages_per_wave(int64_t visits) {
-    return std::max<int32_t>(kPagesInFlight, ceil_div(visits, kResidentWaves));
-}
 
 // 16-row query tiles of one (sequence, KV head): its n_q * G (token, head) rows
 int32_t priv_tiles(int32_t n_q, int32_t H_q, int32_t H_kv) {
     return ceil_div(static_cast<int64_t>(n_q) * (H_q / std::max(1, H_kv)), 16);
 }
 
+// n groups over `pages` pages: the chunk, and the group count that leaves no
+// group empty
+void cut(int32_t pages, int32_t n, int32_t& chunk, int32_t& groups) {
+    n = std::max(1, std::min(n, pages));
+    chunk = ceil_div(pages, n);
+    groups = ceil_div(pages, chunk);
+}
+
 DecodePlan plan_decode(int32_t B, int32_t H_q, int32_t H_kv, int32_t max_pages, int32_t P, int32_t num_splits,
-                       int32_t n_q = 1) {
+                       int32_t n_q, bool bf16) {
     DecodePlan p;
-    const int64_t units = static_cast<int64_t>(B) * std::max(1, H_kv) * priv_tiles(n_q, H_q, H_kv);
+    if (!bf16) {                                  // the fp32 kernel reads every page per sequence
+        const int32_t n = num_splits > 0 ? std::min(num_splits, kMaxSplits) : ceil_div(max_pages, kF32Chunk);
+        cut(max_pages, n, p.priv_chunk, p.priv_groups);
+        return p;
+    }
     const int32_t priv = max_pages - P;
     const int64_t rows = static_cast<int64_t>(B) * n_q * (H_q / std::max(1, H_kv));
     const int64_t tiles = (rows + 15) / 16;
-    // the work of the whole call: private pages per (sequence, KV head, query
-    // tile) and shared pages per (KV head, query tile)
-    const int64_t visits = units * std::max(priv, 0) + static_cast<int64_t>(P) * std::max(1, H_kv) * tiles;
-    const int32_t ppw = pages_per_wave(visits);
-    if (P > 0) {
-        const int32_t c = std::min(std::min(ppw, kMaxPrefixChunk), P);
-        p.prefix_splits = ceil_div(P, c);
-        p.prefix_chunk = ceil_div(P, p.prefix_splits);
-    }
+    const int32_t tpw = priv_tiles(n_q, H_q, H_kv) >= 2 ? 2 : 1;       // tiles per wavefront (launcher's rule)
+    const int64_t units_v = static_cast<int64_t>(B) * H_kv * ceil_div(priv_tiles(n_q, H_q, H_kv), tpw);
+    const int64_t units_p = static_cast<int64_t>(H_kv) * ceil_div(tiles, tpw);
+    auto groups_for = [](int64_t units, int32_t pages) {
+        const int64_t want = std::max<int64_t>(1, (kTarget + units - 1) / std::max<int64_t>(units, 1));
+        return static_cast<int32_t>(std::min<int64_t>(want, std::max(1, pages / kWpg)));
+    };
+    int32_t gv = 0;
     if (priv > 0) {
-        p.priv_splits = num_splits > 0 ? spicy_decode_num_splits(B, H_kv, priv, num_splits)
-                                       : ceil_div(priv, pages_per_split(priv, ceil_div(priv, ppw)));
-        p.pages_per_split = pages_per_split(priv, p.priv_splits);
+        gv = num_splits > 0 ? std::min(num_splits, kMaxSplits) : groups_for(units_v, priv);
+        cut(priv, gv, p.priv_chunk, p.priv_groups);
     }
+    if (P > 0) {
+        int32_t gp = groups_for(units_p, P);
+        const int64_t left = kRound - units_v * p.priv_groups;
+        gp = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(gp, left / std::max<int64_t>(units_p, 1))));
+        cut(P, gp, p.prefix_chunk, p.prefix_groups);
+    }
+    (void)gv;
     return p;
 }
 
-size_t decode_workspace(int32_t B, int32_t H_q, int32_t d, int32_t slots) {
-    const size_t rows = static_cast<size_t>(B) * static_cast<size_t>(H_q) * static_cast<size_t>(slots);
-    return SPICY_WORKSPACE_HEADER + align_up(rows * 2 * sizeof(float)) + align_up(rows * static_cast<size_t>(d) * sizeof(float));
+size_t decode_workspace(int64_t rows, int32_t d, int32_t slots) {
+    const size_t r = static_cast<size_t>(rows);
+    const size_t rs = r * static_cast<size_t>(slots);
+    return SPICY_WORKSPACE_HEADER + align_up(4 * r) + align_up(rs * 2 * sizeof(float)) +
+           align_up(rs * static_cast<size_t>(d) * sizeof(float));
 }
 
 }  // namespace
@@ -226,17 +241,8 @@ spicy_status spicy_coarsen_weighted(const spicy_cache* cache, const void* k_pre,
 int32_t spicy_decode_num_splits(int32_t B, int32_t num_kv_heads, int32_t max_pages_per_seq,
                                 int32_t num_splits) {
     if (max_pages_per_seq < 1) return 1;
-    int32_t s;
-    if (num_splits > 0) {
-        s = std::min(num_splits, max_pages_per_seq);
-    } else {
-        // the pages of every (sequence, KV head) spread evenly over the
-        // resident wavefronts, at least kPagesInFlight pages each
-        const int64_t units = std::max<int64_t>(1, static_cast<int64_t>(B) * std::max(1, num_kv_heads));
-        s = ceil_div(max_pages_per_seq, pages_per_wave(units * max_pages_per_seq));
-    }
-    s = std::max(1, std::min(s, kMaxSplits));
-    return ceil_div(max_pages_per_seq, pages_per_split(max_pages_per_seq, s));
+    const int32_t H = std::max(1, num_kv_heads);
+    return plan_decode(std::max(B, 0), H, H, max_pages_per_seq, 0, std::max(num_splits, 0), 1, true).priv_groups;
 }
 
 spicy_status spicy_decode_plan(int32_t B, int32_t num_q_heads, int32_t num_kv_heads, int32_t max_pages_per_seq,
@@ -247,11 +253,11 @@ spicy_status spicy_decode_plan(int32_t B, int32_t num_q_heads, int32_t num_kv_he
         return SPICY_ERR_ARG;
     if (shared_prefix_pages > max_pages_per_seq) return SPICY_ERR_RANGE;
     const DecodePlan p = plan_decode(B, num_q_heads, num_kv_heads, max_pages_per_seq, shared_prefix_pages,
-                                     num_splits, num_q_tokens);
-    plan[0] = p.prefix_splits;
-    plan[1] = p.prefix_splits > 0 ? p.prefix_chunk : 0;
-    plan[2] = max_pages_per_seq > shared_prefix_pages ? p.priv_splits : 0;
-    plan[3] = max_pages_per_seq > shared_prefix_pages ? p.pages_per_split : 0;
+                                     num_splits, num_q_tokens, true);
+    plan[0] = p.prefix_groups;
+    plan[1] = p.prefix_chunk;
+    plan[2] = p.priv_groups;
+    plan[3] = p.priv_chunk;
     return SPICY_OK;
 }
 
@@ -272,13 +278,18 @@ size_t spicy_decode_multi_workspace_bytes(int32_t B, int32_t num_q_tokens, int32
                                           int32_t num_kv_heads, int32_t head_dim, int32_t max_pages_per_seq,
                                           int32_t shared_prefix_pages, int32_t num_splits) {
     if (B < 0 || num_q_tokens < 1 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 ||
-        shared_prefix_pages < 0)
+        shared_prefix_pages < 0 || num_splits < 0)
         return 0;
-    // the fp32 path ignores the prefix; reserve for whichever plan is larger
-    const DecodePlan p0 = plan_decode(B, num_q_heads, num_kv_heads, max_pages_per_seq, 0, num_splits, num_q_tokens);
+    if (max_pages_per_seq < 1) max_pages_per_seq = 1;
+    shared_prefix_pages = std::min(shared_prefix_pages, max_pages_per_seq);
+    // reserve for the larger of the bf16 and fp32 plans (the fp32 kernel has
+    // no prefix role)
+    const DecodePlan p0 = plan_decode(B, num_q_heads, num_kv_heads, max_pages_per_seq, 0, num_splits,
+                                      num_q_tokens, false);
     const DecodePlan p1 = plan_decode(B, num_q_heads, num_kv_heads, max_pages_per_seq, shared_prefix_pages,
-                                      num_splits, num_q_tokens);
-    return decode_workspace(B * num_q_tokens, num_q_heads, head_dim, std::max(p0.slots(), p1.slots()));
+                                      num_splits, num_q_tokens, true);
+    return decode_workspace(static_cast<int64_t>(B) * num_q_tokens * num_q_heads, head_dim,
+                            std::max(p0.slots(), p1.slots()));
 }
 
 spicy_status spicy_decode_attn(const spicy_cache* cache, const void* q, int32_t num_q_heads,
@@ -322,9 +333,10 @@ spicy_status spicy_decode_attn_multi(const spicy_cache* cache, const void* q, in
                                                              shared_prefix_pages, num_splits))
         return SPICY_ERR_CAPACITY;
     // the fp32 kernel has no shared-prefix role: every page is private there
-    const int32_t P = cache->dtype == SPICY_BF16 ? shared_prefix_pages : 0;
+    const bool bf16 = cache->dtype == SPICY_BF16;
+    const int32_t P = bf16 ? shared_prefix_pages : 0;
     const DecodePlan plan = plan_decode(B, num_q_heads, cache->num_kv_heads, max_pages_per_seq, P, num_splits,
-                                        num_q_tokens);
+                                        num_q_tokens, bf16);
 
     spicy::DecodeArgs a{};
     a.cache = spicy::CacheArgs{cache->k, cache->v, cache->ab, cache->meta, cache->num_pages, cache->num_kv_heads,
@@ -336,24 +348,26 @@ spicy_status spicy_decode_attn_multi(const spicy_cache* cache, const void* q, in
     a.lse = lse;
     char* ws = static_cast<char*>(workspace);
     const size_t rows = static_cast<size_t>(B) * static_cast<size_t>(num_q_tokens) *
-                        static_cast<size_t>(num_q_heads) * static_cast<size_t>(plan.slots());
+                        static_cast<size_t>(num_q_heads);
     a.err = reinterpret_cast<int32_t*>(ws);
     size_t off = SPICY_WORKSPACE_HEADER;
+    a.ticket = reinterpret_cast<int32_t*>(ws + off);
+    off += align_up(4 * rows);
     a.part_ml = reinterpret_cast<float*>(ws + off);
-    off += align_up(rows * 2 * sizeof(float));
+    off += align_up(rows * static_cast<size_t>(plan.slots()) * 2 * sizeof(float));
     a.part_o = reinterpret_cast<float*>(ws + off);
     a.B = B;
     a.H_q = num_q_heads;
     a.max_pages = max_pages_per_seq;
-    a.splits = plan.slots();
-    a.pages_per_split = plan.pages_per_split;
-    a.page_begin = P;
-    a.priv_splits = plan.priv_splits;
-    a.prefix_pages = P;
-    a.prefix_chunk = plan.prefix_chunk;
-    a.prefix_splits = plan.prefix_splits;
     a.n_q = num_q_tokens;
+    a.slots = plan.slots();
+    a.prefix_pages = P;
+    a.prefix_groups = plan.prefix_groups;
+    a.prefix_chunk = plan.prefix_chunk;
+    a.priv_groups = plan.priv_groups;
+    a.priv_chunk = plan.priv_chunk;
     a.priv_tiles = priv_tiles(num_q_tokens, num_q_heads, cache->num_kv_heads);
+    a.wpg = plan.wpg;
     return spicy::launch_decode(a, cache->dtype, cache->head_dim, static_cast<hipStream_t>(stream));
 }
 

@@ -932,7 +932,7 @@ __global__ __launch_bounds__(256) void coarsen_cpoint_kernel(CoarsenArgs a) {
 // ------------------------------------------------------------------ launch
 
 template <typename T, int D>
-static spicy_status launch_coarsen_t(const CoarsenArgs& a, hipStream_t stream) {
+spicy_status launch_coarsen_t(const CoarsenArgs& a, hipStream_t stream) {
     constexpr int HW = kWave / (D / 8);
     // plan workgroups (one per sequence) + persistent streaming workgroups
     const int wpb = 4;
@@ -955,6 +955,18 @@ static spicy_status launch_coarsen_t(const CoarsenArgs& a, hipStream_t stream) {
     return SPICY_OK;
 }
 
+// The library compiles this file once per (element type, head dim), with
+// SPICY_COARSEN_PART = 0 .. 3; each object instantiates its own launcher
+// (and kernels), and part 0 also holds the dispatcher.
+#ifndef SPICY_COARSEN_PART
+#define SPICY_COARSEN_PART 0
+#endif
+#if SPICY_COARSEN_PART == 0
+template spicy_status launch_coarsen_t<uint16_t, 128>(const CoarsenArgs&, hipStream_t);
+extern template spicy_status launch_coarsen_t<uint16_t, 64>(const CoarsenArgs&, hipStream_t);
+extern template spicy_status launch_coarsen_t<float, 128>(const CoarsenArgs&, hipStream_t);
+extern template spicy_status launch_coarsen_t<float, 64>(const CoarsenArgs&, hipStream_t);
+
 spicy_status launch_coarsen(const CoarsenArgs& a, int dtype, int D, hipStream_t stream) {
     if (a.B == 0) return SPICY_OK;
     if (dtype == SPICY_BF16) {
@@ -962,5 +974,13 @@ spicy_status launch_coarsen(const CoarsenArgs& a, int dtype, int D, hipStream_t 
     }
     return D == 128 ? launch_coarsen_t<float, 128>(a, stream) : launch_coarsen_t<float, 64>(a, stream);
 }
+
+#elif SPICY_COARSEN_PART == 1
+template spicy_status launch_coarsen_t<uint16_t, 64>(const CoarsenArgs&, hipStream_t);
+#elif SPICY_COARSEN_PART == 2
+template spicy_status launch_coarsen_t<float, 128>(const CoarsenArgs&, hipStream_t);
+#elif SPICY_COARSEN_PART == 3
+template spicy_status launch_coarsen_t<float, 64>(const CoarsenArgs&, hipStream_t);
+#endif
 
 }  // namespace spicy

@@ -1,5 +1,5 @@
-// SPICY-KV decode attention on gfx950: split-K over 16-entry pages + a
-// log-sum-exp combine.
+// SPICY-KV decode attention on gfx950: one launch, split-K over 16-entry pages
+// with the log-sum-exp combine fused in.
 //
 // Logit (SPICY-KV demo page, section "2. FlashAttention-2/3 & PagedAttention
 // Online-Softmax Kernel Fusion"; Claim 3):
@@ -20,36 +20,47 @@
 //   exp2 to bf16 to MFMA without any lane exchange:
 //   O^T[d x 16 rows] += V^T_page[d x 16 entries] . P^T[16 entries x 16 rows]
 //       d/16 x v_mfma_f32_16x16x16_bf16.  Values are stored like keys (rows
-//       cut in 32-dim chunks, so the coarsening writes 64-byte pieces and a
-//       chunk of all 16 slots is one contiguous 1 KB load); each
-//       32-dim chunk becomes two V^T operand tiles through two MFMAs with
+//       cut in 8-dim groups, so the coarsening writes 16-byte pieces and the
+//       operand of a 32-dim chunk of all 16 slots is one sequential 1 KB
+//       load); each 32-dim chunk becomes two V^T operand tiles through two MFMAs with
 //       0/1 selector matrices (exact), whose accumulator layout is the A
 //       operand layout the product needs.
 //   diagonal closure: C^T[16 entries x 16 rows] = S2_page . (Q^2)^T, the
 //       variance pages loaded like K; q^2 (16 significant bits) is split
 //       into two bf16 terms hi + lo that hold it exactly, so the product is
 //       d/16 MFMAs with fp32 accumulation of exact bf16 products.
-// One launch holds two kinds of workgroups:
-//   split-K: one wavefront per (sequence, KV head, split, query tile).  A
-//       query row is a (query token, query head of that KV head) pair: with
-//       n_q query tokens per sequence a KV head has n_q x G rows in
-//       ceil(n_q G / 16) tiles (one tile of G rows for single-token decode).
-//       The wavefronts of a workgroup are the tiles of one split (1, 2 or 4
-//       of them), so they read its pages together through one L2; each
-//       prefetches its pages NBUF deep in registers.
-//   shared prefix (only when the caller declares one): the first P logical
-//       pages map to the same physical pages in every sequence.  One wavefront
-//       applies a chunk of them to a tile of 16 rows drawn from all sequences
-//       (B x n_q x G rows per KV head).  The wavefronts of one (chunk, KV
-//       head) run on one XCD, so HBM delivers each shared page once to its L2.
-// Both kinds write partials (running max, sum, unnormalised output) to the
-// workspace.  combine_kernel merges the partials of each (sequence, query
-// token, query head) by log-sum-exp and writes O (fp32) and LSE (natural
-// log).
 //
-// fp32 caches (decode_f32_kernel): a plain VALU kernel, one wavefront per
-// (sequence, query head, split), lanes = 16 entries x 4 quarter-rows.  It has
-// no shared-prefix role: the host gives it every page as private.
+// Work decomposition.  A "unit" is a set of query rows and the pages they
+// read:
+//   shared prefix (only when the caller declares one): a tile-set of the
+//       B x n_q x G (sequence, token, query head) rows of one KV head and the
+//       first P logical pages, which every sequence maps to the same physical
+//       pages;
+//   private: a tile-set of the n_q x G rows of one (sequence, KV head) and
+//       its pages [P, ceil(length / 16)).
+// A unit's pages are cut into page groups; one workgroup of WPG wavefronts
+// takes one (unit, group) and its wavefronts take the group's pages in turn
+// (wavefront w: pages w, w + WPG, ...), each prefetching its pages NBUF deep
+// in registers.  The wavefronts' online-softmax states then merge through LDS
+// in a fixed pairwise tree, so a workgroup yields one partial per row.  The
+// prefix groups of one (group, KV head) are placed on one XCD, so HBM
+// delivers each shared page once to that XCD's L2.
+//
+// Finishing a row (no second launch).  A row whose unit set has a single
+// group in total (prefix groups + its sequence's private groups) is written
+// directly as O and LSE.  Otherwise each group writes its partial (running
+// max, sum, unnormalised output) to its slot with device-coherent stores
+// (sc1: they write through this XCD's L2), waits for them to complete, and
+// takes a ticket from the row's counter with a device-scope atomic; the group
+// that takes the last ticket reads the row's partials with device-coherent
+// loads, merges them by log-sum-exp in slot order (so the result does not
+// depend on arrival order), writes O and LSE, and puts the counter back to
+// zero for the next call.  Nothing waits on another workgroup.
+//
+// fp32 caches (decode_f32_kernel): a plain VALU kernel, one workgroup of four
+// wavefronts per (sequence, token, query head, page group), lanes = 16
+// entries x 4 quarter-rows, the same merge and finishing.  It has no
+// shared-prefix role: the host gives it every page as private.
 #include "launch.h"
 #include "spicy_device.h"
 
@@ -64,8 +75,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kWavesPerBlock = 4;
 constexpr int kXcds = 8;                  // MI355X: workgroups go round-robin over 8 XCDs
+constexpr int kF32Waves = 4;              // wavefronts per workgroup of the fp32 kernel
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -84,7 +95,42 @@ __device__ __forceinline__ int32_t check_length(const DecodeArgs& a, int32_t len
     return len;
 }
 
-__device__ __forceinline__ int32_t checked_length(const DecodeArgs& a, int b) { return check_length(a, a.lengths[b]); }
+// Partials a row of sequence b receives: one per prefix group, and one per
+// private group that holds pages of b (at least one, so that a sequence
+// without pages still gets its row written).  len: b's checked length.
+__device__ __forceinline__ int32_t row_count(const DecodeArgs& a, int32_t len) {
+    if (a.priv_groups == 0) return a.prefix_groups;
+    const int32_t priv = max(0, (len + kPage - 1) / kPage - a.prefix_pages);
+    const int32_t g = (priv + a.priv_chunk - 1) / a.priv_chunk;
+    return a.prefix_groups + min(max(g, 1), a.priv_groups);
+}
+
+// Device-coherent 8-byte accesses: relaxed atomics at device scope are
+// issued with sc1, which writes through and reads past this XCD's L2.
+__device__ __forceinline__ void store2_dev(float* p, float x, float y) {
+    const uint64_t v = static_cast<uint64_t>(__float_as_uint(x)) | (static_cast<uint64_t>(__float_as_uint(y)) << 32);
+    __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float2 load2_dev(const float* p) {
+    const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    return make_float2(__uint_as_float(static_cast<uint32_t>(v)), __uint_as_float(static_cast<uint32_t>(v >> 32)));
+}
+
+// Wait until every store of this wavefront has completed (for sc1 stores:
+// reached the device's point of coherence), and keep the compiler from
+// moving memory operations across.
+__device__ __forceinline__ void stores_complete() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// One ticket of row prow's counter; returns the counter's previous value.
+__device__ __forceinline__ int32_t take_ticket(const DecodeArgs& a, int64_t prow) {
+    return __hip_atomic_fetch_add(a.ticket + prow, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void reset_ticket(const DecodeArgs& a, int64_t prow) {
+    __hip_atomic_store(a.ticket + prow, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 template <int D, bool DIAG>
 struct PageRegs {
@@ -131,8 +177,8 @@ struct Tile {
     float c_beta;          // |q|^2 log2(e) of this lane's row
     int32_t len;           // entries of this row's sequence (0 for a padding row)
     int32_t vlen;          // uniform: largest len of the tile
-    float m_run, l_run;
-    f32x4 acc[NT];
+    float m_run, l_run;    // running max (uniform over a row's lanes); this lane's part of the sum
+    f32x4 acc[NT];         // O^T: dims 16t + 4(lane/16) + j of row lane%16
 
     // rowq: this lane's query row (a padding row passes any valid row).  Only
     // issues the loads, unconditionally, so that nothing waits on them here;
@@ -235,22 +281,17 @@ struct Tile {
         return scale;
     }
 
-    // Finish the row sums (held per lane group) and store this lane's row as
-    // partial `slot` of partial row `prow` (= sequence * H_q + query head).
-    __device__ __forceinline__ void store(const DecodeArgs& a, bool row_valid, int64_t prow, int slot) {
-        const int grp = (threadIdx.x % kWave) / 16;
-        float l = l_run;
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
-        if (!row_valid) return;
-        const int64_t idx = prow * a.splits + slot;
-        if (grp == 0) {
-            a.part_ml[2 * idx + 0] = m_run;
-            a.part_ml[2 * idx + 1] = l;
-        }
-        float* po = a.part_o + idx * D + 4 * grp;
+    // Merge another state of the same rows (lane by lane: the other state's
+    // lane holds the same row and the same part of the sum and the output).
+    __device__ __forceinline__ void merge(float m_b, float l_b, const f32x4 (&acc_b)[NT]) {
+        const float m_new = fmaxf(m_run, m_b);
+        const float msub = (m_new == -__builtin_huge_valf()) ? 0.f : m_new;
+        const float sa = fast_exp2(m_run - msub);
+        const float sb = fast_exp2(m_b - msub);
+        l_run = l_run * sa + l_b * sb;
 #pragma unroll
-        for (int t = 0; t < NT; ++t) *reinterpret_cast<f32x4*>(po + 16 * t) = acc[t];
+        for (int t = 0; t < NT; ++t) acc[t] = acc[t] * sa + acc_b[t] * sb;
+        m_run = m_new;
     }
 };
 
@@ -303,29 +344,172 @@ __device__ __forceinline__ void fold_page(Tile<D, DIAG> (&T)[TPW], int ntile, co
     }
 }
 
+// The end of a workgroup, for one tile of query rows (every wavefront takes
+// part; lane l of a wavefront: row l%16).  Each wavefront's online-softmax
+// state of the tile goes to LDS; wavefront w then merges column block w
+// (dims 16w .. 16w+15, lane: dims 16w + 4(l/16) .. +4) over the WPG states in
+// a fixed order, so the result does not depend on timing, and writes that
+// block: as the row's O when the row has a single group (cnt == 1), else as
+// this group's partial (slot `slot`, device-coherent stores).  After a
+// barrier wavefront 0 takes one ticket per shared row; the rows whose last
+// ticket this group took are merged from all their partials (in slot order,
+// each wavefront its block), written, and their counters reset.
+// valid: the lane's row is a query row; prow: its row index (sequence-token
+// * H_q + query head); cnt: the partials the row receives.
+template <int D, int WPG>
+struct Finish {
+    static constexpr int NT = D / 16;
+    static constexpr int BPW = (NT + WPG - 1) / WPG;   // column blocks per wavefront: t = wave + WPG i
+    f32x4 acc[WPG][NT][kWave];
+    float2 ml[WPG][kWave];
+    int32_t fin[kWave];              // per row (lanes 0..15): slots to merge, 0 = not finished here
+
+    template <bool DIAG>
+    __device__ __forceinline__ void run(const DecodeArgs& a, const Tile<D, DIAG>& T, bool valid, int64_t prow,
+                                        int32_t cnt, int slot) {
+        constexpr int SB = 8;                // slots whose loads are in flight together
+        const int lane = threadIdx.x % kWave;
+        const int wave = threadIdx.x / kWave;
+        const int row = lane % 16, grp = lane / 16;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[wave][t][lane] = T.acc[t];
+        ml[wave][lane] = make_float2(T.m_run, T.l_run);
+        __syncthreads();
+        // every wavefront: the merged max and the row's sum (the sum over
+        // lane groups of the merged per-lane parts)
+        float M = -__builtin_huge_valf();
+#pragma unroll
+        for (int w = 0; w < WPG; ++w) M = fmaxf(M, ml[w][lane].x);
+        const float msub = (M == -__builtin_huge_valf()) ? 0.f : M;
+        float sc[WPG];
+        float L = 0.f;
+#pragma unroll
+        for (int w = 0; w < WPG; ++w) {
+            sc[w] = fast_exp2(ml[w][lane].x - msub);
+            L += sc[w] * ml[w][lane].y;
+        }
+        L += __shfl_xor(L, 16);
+        L += __shfl_xor(L, 32);
+        const bool shared = valid && cnt > 1;
+        const int64_t base = prow * a.slots;
+#pragma unroll
+        for (int i = 0; i < BPW; ++i) {
+            const int t = wave + WPG * i;
+            if (t < NT) {
+                f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int w = 0; w < WPG; ++w) o += sc[w] * acc[w][t][lane];
+                if (valid && cnt == 1) {
+                    const bool live = L > 0.f;
+                    *reinterpret_cast<f32x4*>(a.o + prow * D + 16 * t + 4 * grp) = live ? o * (1.f / L) : f32x4{};
+                }
+                if (shared) {
+                    float* po = a.part_o + (base + slot) * D + 16 * t + 4 * grp;
+                    store2_dev(po, o[0], o[1]);
+                    store2_dev(po + 2, o[2], o[3]);
+                }
+            }
+        }
+        if (wave == 0 && grp == 0) {
+            if (valid && cnt == 1) a.lse[prow] = L > 0.f ? (msub + __log2f(L)) * kLn2 : -__builtin_huge_valf();
+            if (shared) store2_dev(a.part_ml + 2 * (base + slot), M, L);
+        }
+        stores_complete();
+        __syncthreads();
+        if (wave == 0) {
+            int32_t old = 0;
+            if (shared && grp == 0) old = take_ticket(a, prow);
+            if (shared && grp == 0 && old >= cnt) raise_err(a.err, SPICY_DEVERR_TICKET);
+            if (lane < 16) fin[lane] = (shared && old == cnt - 1) ? cnt : 0;
+        }
+        __syncthreads();
+        const int32_t n_row = fin[row];
+        int32_t n = n_row;
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) n = max(n, __shfl_xor(n, o));
+        if (n == 0 || wave >= NT) return;        // uniform over the workgroup / this wavefront
+        // merge the finished rows' partials: this wavefront's blocks of each
+        float M2 = -__builtin_huge_valf(), L2 = 0.f;
+        f32x4 o2[BPW];
+#pragma unroll
+        for (int i = 0; i < BPW; ++i) o2[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int s0 = 0; s0 < n; s0 += SB) {
+            float2 pm[SB];
+            f32x4 po[SB][BPW];
+#pragma unroll
+            for (int u = 0; u < SB; ++u) {
+                const bool ok = s0 + u < n_row;
+                const int64_t ps = base + (ok ? s0 + u : 0);
+                pm[u] = ok ? load2_dev(a.part_ml + 2 * ps) : make_float2(-__builtin_huge_valf(), 0.f);
+#pragma unroll
+                for (int i = 0; i < BPW; ++i) {
+                    const int t = wave + WPG * i;
+                    const float* src = a.part_o + ps * D + 16 * t + 4 * grp;
+                    const bool okt = ok && t < NT;
+                    const float2 x = okt ? load2_dev(src) : make_float2(0.f, 0.f);
+                    const float2 y = okt ? load2_dev(src + 2) : make_float2(0.f, 0.f);
+                    po[u][i] = f32x4{x.x, x.y, y.x, y.y};
+                }
+            }
+            float mc = M2;
+#pragma unroll
+            for (int u = 0; u < SB; ++u) mc = fmaxf(mc, pm[u].x);
+            const float ms = (mc == -__builtin_huge_valf()) ? 0.f : mc;
+            const float scale = fast_exp2(M2 - ms);
+            L2 *= scale;
+#pragma unroll
+            for (int i = 0; i < BPW; ++i) o2[i] *= scale;
+#pragma unroll
+            for (int u = 0; u < SB; ++u) {
+                const float w = fast_exp2(pm[u].x - ms);     // 0 for a slot past the row's count
+                L2 += w * pm[u].y;
+#pragma unroll
+                for (int i = 0; i < BPW; ++i) o2[i] += w * po[u][i];
+            }
+            M2 = mc;
+        }
+        if (n_row > 0) {
+            const bool live = L2 > 0.f;
+#pragma unroll
+            for (int i = 0; i < BPW; ++i) {
+                const int t = wave + WPG * i;
+                if (t < NT)
+                    *reinterpret_cast<f32x4*>(a.o + prow * D + 16 * t + 4 * grp) = live ? o2[i] * (1.f / L2) : f32x4{};
+            }
+            if (wave == 0 && grp == 0) {
+                const float ms = (M2 == -__builtin_huge_valf()) ? 0.f : M2;
+                a.lse[prow] = live ? (ms + __log2f(L2)) * kLn2 : -__builtin_huge_valf();
+                reset_ticket(a, prow);
+            }
+        }
+    }
+};
+
 }  // namespace
 
 // ---------------------------------------------------------------- bf16 MFMA
 
-// Workgroup w (linear over a 2-D grid) of 4 wavefronts.  Both roles run the
-// same page pipeline; they differ in the rows of their tile, the page range
-// and where its page ids come from.
-//   w < prefix_blocks: shared-prefix role, work item (chunk c, KV head h, tile
-//       t).  Tile t holds rows r = 16t .. 16t+15 of the B x G (sequence,
-//       query head of h) rows; its pages are [c * prefix_chunk, ...) of the
-//       shared prefix, with ids from sequence 0's table row.  w is first
-//       remapped so that the prefix_blocks / 8 consecutive work items of each
-//       XCD are contiguous: the tiles of one (chunk, KV head) share an L2.
-//   otherwise: split-K role, work item (split, KV head h, sequence b).  The
-//       tile is the G query heads of h; the pages are private pages
-//       [page_begin + split * pages_per_split, ...) of sequence b.
-// Pages are prefetched NBUF deep in registers.  Page ids are read 64 at a
-// time with one vector load, then each page's id is read out of its lane
-// (uniform).  Pages past the window's end load its last page again (every
-// load is unconditional, so each wait covers exactly one page); they are
-// never processed.
-template <int D, int NBUF, bool DIAG, int TPW>
-__global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
+// Workgroup w (linear over a 2-D grid) of WPG wavefronts takes one (unit,
+// page group):
+//   w < prefix_blocks: shared-prefix role.  w is first remapped so that the
+//       prefix_blocks / 8 consecutive work items of each XCD are contiguous;
+//       then (group c, KV head h, tile-set ts): the rows of tiles
+//       TPW ts .. TPW ts + TPW-1 of the B x n_q x G rows of h, the pages
+//       [c prefix_chunk, ...) of the prefix, with ids from sequence 0's table
+//       row.  The tile-sets of one (c, h) are consecutive, so they share an
+//       XCD's L2.
+//   otherwise: private role, (group s, tile-set ts, KV head h, sequence b):
+//       the rows of tiles TPW ts .. of (b, h), pages
+//       [P + s priv_chunk, ...) of sequence b.  A group past b's pages does
+//       nothing (group 0 always takes part, so that every row is written).
+// Wavefront w of the workgroup takes the group's pages w, w + WPG, ...  Page
+// ids come 64 of the wavefront's pages at a time with one vector load, then
+// each page's id is read out of its lane (uniform).  Pages past the
+// wavefront's last load its last page again (every load is unconditional, so
+// each wait covers exactly one page); they are never processed.
+template <int D, int NBUF, bool DIAG, int TPW, int WPG>
+__global__ __launch_bounds__(WPG * kWave, 8 / WPG) void decode_mfma_kernel(DecodeArgs a) {
+    constexpr int NT = D / 16;
     const int lane = threadIdx.x % kWave;
     const int wave = threadIdx.x / kWave;
     const int row = lane % 16;
@@ -333,41 +517,39 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
     const int G = a.H_q / H;
     int64_t blk = static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x;
 
-    // The wavefront's TPW query tiles are tiles TPW * wt + k, k < ntile
-    // (ntile: the ones that hold rows); per tile, this lane's row.
-    int h, slot, wt = 0, ntile = 1;
+    int h, ts, slot, ntile;
     int32_t p0, p1;
-    int32_t id_end;        // page-id entries this wavefront's table row holds
+    int32_t id_end;        // page-id entries the table row holds
     const int32_t* table;
-    int64_t prow[TPW];     // this lane's partial row (sequence * H_q + query head) in tile k
-    int32_t raw_len[TPW];  // that row's sequence length as read, checked below
+    int64_t prow[TPW];     // this lane's row (sequence-token * H_q + query head) in tile k
+    int32_t raw_len[TPW];  // the length of that row's sequence as read, checked below
     bool row_valid[TPW];
     const bool prefix_role = blk < a.prefix_blocks;
     // The query rows and the first window of page ids do not depend on the
-    // length: each role issues their loads together with it, so the wavefront
+    // length: each role issues their loads together with it, so a wavefront
     // waits one memory round trip before its first pages are requested.
     Tile<D, DIAG> T[TPW];
     int32_t ids;
-    int64_t prow0;         // a valid query row of the wavefront's KV head
+    int64_t prow0;         // a valid query row of the workgroup's KV head
     auto issue_loads = [&]() {
 #pragma unroll
         for (int k = 0; k < TPW; ++k)
             T[k].load_q(static_cast<const uint16_t*>(a.q) + (row_valid[k] ? prow[k] : prow0) * D);
-        ids = (p0 + lane < min(p0 + kWave, id_end)) ? table[p0 + lane] : 0;
-        // keep the compiler from sinking those loads below the exit test
+        const int32_t pg = p0 + wave + WPG * lane;
+        ids = pg < min(p1, id_end) ? table[pg] : 0;
+        // keep the compiler from sinking those loads below the length checks
         asm volatile("" ::: "memory");
     };
     if (prefix_role) {
         const int per_xcd = a.prefix_blocks / kXcds;      // prefix_blocks is a multiple of 8
         int w = static_cast<int>(blk % kXcds) * per_xcd + static_cast<int>(blk / kXcds);
-        const int tgb = a.prefix_tile_blocks;
-        wt = (w % tgb) * kWavesPerBlock + wave;
-        w /= tgb;
+        ts = w % a.prefix_sets;
+        w /= a.prefix_sets;
         h = w % H;
         const int c = w / H;
-        const int rows = a.B * a.n_q * G;                  // rows (sequence, token, query head)
-        if (c >= a.prefix_splits || TPW * wt * 16 >= rows) return;
-        ntile = min(TPW, (rows - TPW * wt * 16 + 15) / 16);
+        if (c >= a.prefix_groups) return;                 // padding workgroup
+        const int rows = a.B * a.n_q * G;                 // rows (sequence, token, query head)
+        ntile = min(TPW, (rows - TPW * ts * 16 + 15) / 16);
         slot = c;
         p0 = c * a.prefix_chunk;
         p1 = min(p0 + a.prefix_chunk, a.prefix_pages);
@@ -376,7 +558,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
         prow0 = static_cast<int64_t>(h) * G;
 #pragma unroll
         for (int k = 0; k < TPW; ++k) {
-            const int r = (TPW * wt + k) * 16 + row;
+            const int r = (TPW * ts + k) * 16 + row;
             row_valid[k] = r < rows;
             const int rq = row_valid[k] ? r : 0;
             const int bq = rq / (a.n_q * G);                // sequence
@@ -387,25 +569,17 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
         issue_loads();
     } else {
         blk -= a.prefix_blocks;
-        // a workgroup's wavefronts: kWavesPerBlock / wpt splits x wpt
-        // wavefronts of each, so the tiles of one split read its pages
-        // together (one L2)
-        const int wtiles = (a.priv_tiles + TPW - 1) / TPW;   // wavefronts per split
-        const int wpt = a.priv_wpt;
-        const int spb = kWavesPerBlock / wpt;
-        const int sgb = (a.priv_splits + spb - 1) / spb;
-        const int ntg = (wtiles + wpt - 1) / wpt;
-        const int split = static_cast<int>(blk % sgb) * spb + wave / wpt;
-        blk /= sgb;
-        wt = static_cast<int>(blk % ntg) * wpt + wave % wpt;
-        blk /= ntg;
+        const int s = static_cast<int>(blk % a.priv_groups);
+        blk /= a.priv_groups;
+        ts = static_cast<int>(blk % a.priv_sets);
+        blk /= a.priv_sets;
         h = static_cast<int>(blk % H);
         const int64_t b = blk / H;
-        if (split >= a.priv_splits || wt >= wtiles || b >= a.B) return;
-        ntile = min(TPW, a.priv_tiles - TPW * wt);
-        slot = a.prefix_splits + split;
-        p0 = a.page_begin + split * a.pages_per_split;
-        p1 = p0 + a.pages_per_split;                      // clamped to the length below
+        if (b >= a.B) return;
+        ntile = min(TPW, a.priv_tiles - TPW * ts);
+        slot = a.prefix_groups + s;
+        p0 = a.prefix_pages + s * a.priv_chunk;
+        p1 = p0 + a.priv_chunk;                           // clamped to the length below
         id_end = a.max_pages;
         table = a.page_table + b * a.max_pages;
         prow0 = b * a.n_q * a.H_q + static_cast<int64_t>(h) * G;
@@ -413,7 +587,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
         const int32_t lb = a.lengths[b];
 #pragma unroll
         for (int k = 0; k < TPW; ++k) {
-            const int r = (TPW * wt + k) * 16 + row;
+            const int r = (TPW * ts + k) * 16 + row;
             row_valid[k] = r < a.n_q * G;
             const int rq = row_valid[k] ? r : 0;
             prow[k] = (b * a.n_q + rq / G) * a.H_q + static_cast<int64_t>(h) * G + rq % G;
@@ -421,11 +595,16 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
         }
         issue_loads();
     }
+    // the length of each row's sequence; in the private role every lane of
+    // the workgroup holds the one sequence's length (padding rows included),
+    // so the page range below is uniform
     int32_t len[TPW];
 #pragma unroll
     for (int k = 0; k < TPW; ++k) len[k] = (prefix_role && !row_valid[k]) ? 0 : check_length(a, raw_len[k]);
-    if (!prefix_role) p1 = min(p1, (len[0] + kPage - 1) / kPage);
-    if (p0 >= p1) return;
+    if (!prefix_role) {
+        p1 = min(p1, (len[0] + kPage - 1) / kPage);
+        if (p0 >= p1 && slot != a.prefix_groups) return;  // a group past the sequence's pages
+    }
     int32_t vlen = 0;
 #pragma unroll
     for (int k = 0; k < TPW; ++k) {
@@ -433,73 +612,82 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
         if (k < ntile) vlen = max(vlen, T[k].vlen);
     }
 
-    // Pages go in windows of 64: one vector load brings the window's page ids
-    // (lane i: page w0 + i) before its pipeline starts, so no wait inside the
-    // pipeline depends on it.
+    // This wavefront's pages: p0 + wave + WPG i, i < nmine, in windows of 64
+    // (lane i of a window holds the id of its i-th page).
+    const int32_t nmine = p1 > p0 + wave ? (p1 - p0 - wave + WPG - 1) / WPG : 0;
     PageRegs<D, DIAG> buf[NBUF];
-    for (int32_t w0 = p0; w0 < p1; w0 += kWave) {
-        const int32_t w1 = min(w0 + kWave, p1);
-        if (w0 != p0) ids = (w0 + lane < w1) ? table[w0 + lane] : 0;
-        auto load = [&](PageRegs<D, DIAG>& r, int32_t lp) {
-            load_page<D, DIAG>(a, r, __builtin_amdgcn_readlane(ids, min(lp, w1 - 1) - w0), h);
+    for (int32_t i0 = 0; i0 < nmine; i0 += kWave) {
+        const int32_t i1 = min(i0 + kWave, nmine);
+        if (i0 != 0) ids = (i0 + lane < i1) ? table[p0 + wave + WPG * (i0 + lane)] : 0;
+        auto load = [&](PageRegs<D, DIAG>& r, int32_t i) {
+            load_page<D, DIAG>(a, r, __builtin_amdgcn_readlane(ids, min(i, i1 - 1) - i0), h);
         };
 #pragma unroll
-        for (int i = 0; i < NBUF; ++i) load(buf[i], w0 + i);
-        for (int32_t lp = w0; lp < w1; lp += NBUF) {
+        for (int i = 0; i < NBUF; ++i) load(buf[i], i0 + i);
+        for (int32_t i = i0; i < i1; i += NBUF) {
 #pragma unroll
-            for (int i = 0; i < NBUF; ++i) {
-                if (lp + i < w1) fold_page<D, DIAG, TPW>(T, ntile, buf[i], lp + i, vlen);
-                load(buf[i], lp + i + NBUF);
+            for (int u = 0; u < NBUF; ++u) {
+                if (i + u < i1) fold_page<D, DIAG, TPW>(T, ntile, buf[u], p0 + wave + WPG * (i + u), vlen);
+                load(buf[u], i + u + NBUF);
             }
         }
     }
-#pragma unroll
-    for (int k = 0; k < TPW; ++k)
-        if (k < ntile) T[k].store(a, row_valid[k], prow[k], slot);
 
-    // The KV head 0 wavefronts of the shared prefix check that the sequences
-    // of their tiles map the chunk's pages like sequence 0 (independent loads,
-    // one flag).  It is done last, off the path to the first pages.
+    // The KV head 0 prefix groups check that the sequences of their tiles map
+    // the group's pages like sequence 0 (each wavefront its own pages).
     if (prefix_role && h == 0) {
         const int rows = a.B * a.n_q * G;
-        const int b_first = (TPW * wt * 16) / (a.n_q * G);
-        const int b_last = min(rows - 1, (TPW * wt + ntile) * 16 - 1) / (a.n_q * G);
-        const int npg = p1 - p0;
-        const int n = (b_last - b_first + 1) * npg;
+        const int b_first = (TPW * ts * 16) / (a.n_q * G);
+        const int b_last = min(rows - 1, (TPW * ts + ntile) * 16 - 1) / (a.n_q * G);
+        const int n = (b_last - b_first + 1) * nmine;
         bool bad = false;
         for (int i = lane; i < n; i += kWave) {
-            const int32_t pg = p0 + i % npg;
-            const int64_t bb = b_first + i / npg;
+            const int32_t pg = p0 + wave + WPG * (i % nmine);
+            const int64_t bb = b_first + i / nmine;
             bad |= a.page_table[bb * a.max_pages + pg] != a.page_table[pg];
         }
         if (bad) raise_err(a.err, SPICY_DEVERR_SHARED);
+    }
+
+    // The workgroup's rows, one tile at a time through the same LDS.
+    __shared__ Finish<D, WPG> fs;
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+        if (k < ntile) {
+            if (k > 0) __syncthreads();          // the previous tile's LDS reads are done
+            const int32_t cnt = row_valid[k] ? row_count(a, len[k]) : 0;
+            fs.run(a, T[k], row_valid[k], prow[k], cnt, slot);
+        }
     }
 }
 
 // -------------------------------------------------------------- fp32 VALU
 
+// Workgroup (group s, query head hq, sequence-token bv) of four wavefronts:
+// the group's private pages [s priv_chunk, ...) of sequence bv / n_q, taken
+// in turn by the wavefronts, merged through LDS, then finished like the MFMA
+// kernel's rows.
 template <int D>
-__global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kF32Waves * kWave) void decode_f32_kernel(DecodeArgs a) {
     constexpr int QD = D / 4;          // dims per quarter-row
     constexpr int DL = D / kWave;      // output dims per lane
     const int lane = threadIdx.x % kWave;
     const int wave = threadIdx.x / kWave;
     const int ent = lane / 4;
     const int qtr = lane % 4;
-    const int split = blockIdx.x * (blockDim.x / kWave) + wave;
+    const int s = blockIdx.x;
     const int hq = blockIdx.y;
     const int bv = blockIdx.z;                 // sequence * n_q + token
     const int b = bv / a.n_q;
     const int H = a.cache.H;
     const int G = a.H_q / H;
     const int h = hq / G;
-    if (split >= a.priv_splits) return;
 
-    const int32_t len = checked_length(a, b);
+    const int32_t len = check_length(a, a.lengths[b]);
     const int32_t npages = (len + kPage - 1) / kPage;
-    const int32_t p0 = a.page_begin + split * a.pages_per_split;
-    const int32_t p1 = min(p0 + a.pages_per_split, npages);
-    if (p0 >= p1) return;
+    const int32_t p0 = s * a.priv_chunk;
+    const int32_t p1 = min(p0 + a.priv_chunk, npages);
+    if (p0 >= p1 && s != 0) return;            // a group past the sequence's pages (uniform)
 
     const float* qrow = static_cast<const float*>(a.q) + (static_cast<int64_t>(bv) * a.H_q + hq) * D;
     float qv[QD];
@@ -526,27 +714,27 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < DL; ++j) acc[j] = 0.f;
 
-    for (int32_t lp = p0; lp < p1; ++lp) {
+    for (int32_t lp = p0 + wave; lp < p1; lp += kF32Waves) {
         const int32_t pid = table[lp];
         if (pid < 0 || pid >= a.cache.num_pages) {
             raise_err(a.err, SPICY_DEVERR_PAGE_ID);
             continue;
         }
         const int64_t ph = static_cast<int64_t>(pid) * H + h;
-        const float* krow = kpool + ph * kPage * D + slot_elem(ent, qtr * QD);   // QD <= 32: one chunk
+        const float* kpage = kpool + ph * kPage * D;
         float dot = 0.f;
 #pragma unroll
-        for (int i = 0; i < QD; ++i) dot += qv[i] * krow[i];
+        for (int i = 0; i < QD; ++i) dot += qv[i] * kpage[slot_elem(ent, qtr * QD + i)];
         dot += __shfl_xor(dot, 1);
         dot += __shfl_xor(dot, 2);
         const float alpha = abpool[(ph * kPage + ent) * 2 + 0];
         const float beta = abpool[(ph * kPage + ent) * 2 + 1];
         float closure = beta * c_beta;
         if (s2pool) {
-            const float* srow = s2pool + ph * kPage * D + slot_elem(ent, qtr * QD);
+            const float* spage = s2pool + ph * kPage * D;
             float c = 0.f;
 #pragma unroll
-            for (int i = 0; i < QD; ++i) c += qv[i] * qv[i] * srow[i];
+            for (int i = 0; i < QD; ++i) c += qv[i] * qv[i] * spage[slot_elem(ent, qtr * QD + i)];
             c += __shfl_xor(c, 1);
             c += __shfl_xor(c, 2);
             closure = c * (kLog2e / (2.f * D));
@@ -576,130 +764,135 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
     }
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) l_run += __shfl_xor(l_run, o);
-    const int64_t idx = (static_cast<int64_t>(bv) * a.H_q + hq) * a.splits + a.prefix_splits + split;
-    if (lane == 0) {
-        a.part_ml[2 * idx + 0] = m_run;
-        a.part_ml[2 * idx + 1] = l_run;
-    }
+
+    // merge the four wavefronts (fixed pairs) through LDS
+    __shared__ float red[kF32Waves / 2][DL + 2][kWave];
 #pragma unroll
-    for (int j = 0; j < DL; ++j) a.part_o[idx * D + lane + kWave * j] = acc[j];
-}
+    for (int half = kF32Waves / 2; half >= 1; half /= 2) {
+        if (wave >= half && wave < 2 * half) {
+#pragma unroll
+            for (int j = 0; j < DL; ++j) red[wave - half][j][lane] = acc[j];
+            red[wave - half][DL][lane] = m_run;
+            red[wave - half][DL + 1][lane] = l_run;
+        }
+        __syncthreads();
+        if (wave < half) {
+            const float m_b = red[wave][DL][lane], l_b = red[wave][DL + 1][lane];
+            const float m_new = fmaxf(m_run, m_b);
+            const float msub = (m_new == -__builtin_huge_valf()) ? 0.f : m_new;
+            const float sa = fast_exp2(m_run - msub), sb = fast_exp2(m_b - msub);
+            l_run = l_run * sa + l_b * sb;
+#pragma unroll
+            for (int j = 0; j < DL; ++j) acc[j] = acc[j] * sa + red[wave][j][lane] * sb;
+            m_run = m_new;
+        }
+        if (half > 1) __syncthreads();
+    }
+    if (wave != 0) return;
 
-// ----------------------------------------------------------------- combine
-
-// One wavefront per (sequence, query head): merge its partials (prefix chunks
-// first, then the private splits that hold pages) by log-sum-exp, in one
-// pass with a running maximum: the loads of kChunk partials are issued
-// together and nothing waits for a separate maximum pass.  Every lane reads
-// the same (m, l) of a partial, so the maximum needs no lane exchange; lanes
-// own D/64 dimensions.
-template <int D>
-__global__ __launch_bounds__(64) void combine_kernel(DecodeArgs a) {
-    constexpr int DL = D / kWave;
-    constexpr int kChunk = 32;
-    const int lane = threadIdx.x;
-    const int hq = blockIdx.x;
-    const int bv = blockIdx.y;                 // sequence * n_q + token
-    const int32_t len = checked_length(a, bv / a.n_q);
-    const int32_t npages = (len + kPage - 1) / kPage;
-    const int32_t priv = max(0, npages - a.page_begin);
-    const int nsplit = a.prefix_splits + min(a.priv_splits, (priv + a.pages_per_split - 1) / a.pages_per_split);
-    const int64_t base = (static_cast<int64_t>(bv) * a.H_q + hq) * a.splits;
-
-    float M = -__builtin_huge_valf();
-    float L = 0.f;
-    float acc[DL];
+    const int64_t prow = static_cast<int64_t>(bv) * a.H_q + hq;
+    const int32_t cnt = row_count(a, len);
+    float* orow = a.o + prow * D;
+    if (cnt == 1) {
+        const bool live = l_run > 0.f;
+        const float inv = live ? 1.f / l_run : 0.f;
+#pragma unroll
+        for (int j = 0; j < DL; ++j) orow[lane + kWave * j] = live ? acc[j] * inv : 0.f;
+        if (lane == 0) {
+            const float msub = (m_run == -__builtin_huge_valf()) ? 0.f : m_run;
+            a.lse[prow] = live ? (msub + __log2f(l_run)) * kLn2 : -__builtin_huge_valf();
+        }
+        return;
+    }
+    const int64_t base = prow * a.slots;
+    float* po = a.part_o + (base + a.prefix_groups + s) * D;
+#pragma unroll
+    for (int j = 0; j < DL; ++j)
+        __hip_atomic_store(po + lane + kWave * j, acc[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0) store2_dev(a.part_ml + 2 * (base + a.prefix_groups + s), m_run, l_run);
+    stores_complete();
+    int32_t old = lane == 0 ? take_ticket(a, prow) : 0;
+    old = __shfl(old, 0);
+    if (old >= cnt) raise_err(a.err, SPICY_DEVERR_TICKET);
+    if (old != cnt - 1) return;
+    float M = -__builtin_huge_valf(), L = 0.f;
 #pragma unroll
     for (int j = 0; j < DL; ++j) acc[j] = 0.f;
-    for (int s0 = 0; s0 < nsplit; s0 += kChunk) {
-        float w[kChunk], l[kChunk], ov[kChunk][DL];
+    for (int sl = 0; sl < cnt; ++sl) {
+        const float2 ml = load2_dev(a.part_ml + 2 * (base + sl));
+        float ov[DL];
 #pragma unroll
-        for (int u = 0; u < kChunk; ++u) {
-            const int s = min(s0 + u, nsplit - 1);
-            w[u] = a.part_ml[2 * (base + s)];
-            l[u] = a.part_ml[2 * (base + s) + 1];
-#pragma unroll
-            for (int j = 0; j < DL; ++j) ov[u][j] = a.part_o[(base + s) * D + lane + kWave * j];
-        }
-        float mc = M;
-#pragma unroll
-        for (int u = 0; u < kChunk; ++u) mc = fmaxf(mc, w[u]);     // repeats of the last partial change nothing
+        for (int j = 0; j < DL; ++j)
+            ov[j] = __hip_atomic_load(a.part_o + (base + sl) * D + lane + kWave * j, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+        const float mc = fmaxf(M, ml.x);
         const float msub = (mc == -__builtin_huge_valf()) ? 0.f : mc;
-        const float scale = fast_exp2(M - msub);                   // 0 while M is -inf
-        L *= scale;
+        const float sa = fast_exp2(M - msub), sb = fast_exp2(ml.x - msub);
+        L = L * sa + ml.y * sb;
 #pragma unroll
-        for (int j = 0; j < DL; ++j) acc[j] *= scale;
-#pragma unroll
-        for (int u = 0; u < kChunk; ++u) {
-            const float wu = (s0 + u < nsplit) ? fast_exp2(w[u] - msub) : 0.f;
-            L += wu * l[u];
-#pragma unroll
-            for (int j = 0; j < DL; ++j) acc[j] += wu * ov[u][j];
-        }
+        for (int j = 0; j < DL; ++j) acc[j] = acc[j] * sa + ov[j] * sb;
         M = mc;
     }
-    const float msub = (M == -__builtin_huge_valf()) ? 0.f : M;
-    float* orow = a.o + (static_cast<int64_t>(bv) * a.H_q + hq) * D;
     const bool live = L > 0.f;
     const float inv = live ? 1.f / L : 0.f;
 #pragma unroll
     for (int j = 0; j < DL; ++j) orow[lane + kWave * j] = live ? acc[j] * inv : 0.f;
-    if (lane == 0)
-        a.lse[static_cast<int64_t>(bv) * a.H_q + hq] = live ? (msub + __log2f(L)) * kLn2 : -__builtin_huge_valf();
+    if (lane == 0) {
+        const float msub = (M == -__builtin_huge_valf()) ? 0.f : M;
+        a.lse[prow] = live ? (msub + __log2f(L)) * kLn2 : -__builtin_huge_valf();
+        reset_ticket(a, prow);
+    }
 }
 
 // ------------------------------------------------------------------ launch
 
-constexpr int kNbuf = 4;                  // one tile per wavefront
+constexpr int kNbuf = 3;                  // one tile per wavefront
 constexpr int kNbufPair = 2;              // two tiles per wavefront: their state takes a page's registers
 constexpr int kNbufDiag = 2;              // the variance pages add a third page-sized load
 constexpr int64_t kMaxGridX = 65536;
 
 // Grid of the bf16 kernel with TPW tiles per wavefront: the shared-prefix
-// workgroups (a multiple of 8, see the XCD remap), then the split-K ones.
+// workgroups (a multiple of 8, see the XCD remap), then the private ones.
 template <int TPW>
 static dim3 mfma_grid(DecodeArgs& a) {
     const int G = a.H_q / a.cache.H;
     const int tiles = (a.B * a.n_q * G + 15) / 16;
-    const int wtiles = (tiles + TPW - 1) / TPW;
-    a.prefix_tile_blocks = (wtiles + kWavesPerBlock - 1) / kWavesPerBlock;
-    const int64_t pb = static_cast<int64_t>(a.prefix_splits) * a.cache.H * a.prefix_tile_blocks;
+    a.prefix_sets = (tiles + TPW - 1) / TPW;
+    const int64_t pb = static_cast<int64_t>(a.prefix_groups) * a.cache.H * a.prefix_sets;
     a.prefix_blocks = static_cast<int32_t>((pb + kXcds - 1) / kXcds * kXcds);
-    const int pw = (a.priv_tiles + TPW - 1) / TPW;   // wavefronts per split
-    a.priv_wpt = pw >= 3 ? 4 : pw;
-    const int64_t spb = kWavesPerBlock / a.priv_wpt;
-    const int64_t sgb = (a.priv_splits + spb - 1) / spb;
-    const int64_t ntg = (pw + a.priv_wpt - 1) / a.priv_wpt;
-    const int64_t nblk = a.prefix_blocks + sgb * ntg * a.cache.H * a.B;
+    a.priv_sets = (a.priv_tiles + TPW - 1) / TPW;
+    const int64_t nblk = a.prefix_blocks + static_cast<int64_t>(a.priv_groups) * a.priv_sets * a.cache.H * a.B;
     const int64_t gx = nblk < kMaxGridX ? nblk : kMaxGridX;
     const int64_t gy = (nblk + gx - 1) / gx;
     return dim3(static_cast<unsigned>(gx), static_cast<unsigned>(gy));
+}
+
+template <int D, int NBUF, bool DIAG, int TPW>
+static void launch_mfma(DecodeArgs& a, hipStream_t stream) {
+    const dim3 grid = mfma_grid<TPW>(a);
+    if (a.wpg == 4)
+        hipLaunchKernelGGL((decode_mfma_kernel<D, NBUF, DIAG, TPW, 4>), grid, dim3(4 * kWave), 0, stream, a);
+    else
+        hipLaunchKernelGGL((decode_mfma_kernel<D, NBUF, DIAG, TPW, 8>), grid, dim3(8 * kWave), 0, stream, a);
 }
 
 template <int D>
 static spicy_status launch_decode_t(const DecodeArgs& a0, int dtype, hipStream_t stream) {
     DecodeArgs a = a0;
     if (dtype == SPICY_BF16) {
-        const dim3 block(kWavesPerBlock * kWave);
         if (a.cache.s2) {
-            const dim3 grid = mfma_grid<1>(a);
-            hipLaunchKernelGGL((decode_mfma_kernel<D, kNbufDiag, true, 1>), grid, block, 0, stream, a);
+            launch_mfma<D, kNbufDiag, true, 1>(a, stream);
         } else if (a.priv_tiles >= 2) {
             // several query tiles per (sequence, KV head): a wavefront takes two,
             // so each page it loads serves both and its V^T is formed once
-            const dim3 grid = mfma_grid<2>(a);
-            hipLaunchKernelGGL((decode_mfma_kernel<D, kNbufPair, false, 2>), grid, block, 0, stream, a);
+            launch_mfma<D, kNbufPair, false, 2>(a, stream);
         } else {
-            const dim3 grid = mfma_grid<1>(a);
-            hipLaunchKernelGGL((decode_mfma_kernel<D, kNbuf, false, 1>), grid, block, 0, stream, a);
+            launch_mfma<D, kNbuf, false, 1>(a, stream);
         }
     } else {
-        const int wpb = a.priv_splits < 4 ? a.priv_splits : 4;
-        dim3 grid((a.priv_splits + wpb - 1) / wpb, a.H_q, a.B * a.n_q);
-        hipLaunchKernelGGL((decode_f32_kernel<D>), grid, dim3(wpb * kWave), 0, stream, a);
+        dim3 grid(a.priv_groups, a.H_q, a.B * a.n_q);
+        hipLaunchKernelGGL((decode_f32_kernel<D>), grid, dim3(kF32Waves * kWave), 0, stream, a);
     }
-    if (hipGetLastError() != hipSuccess) return SPICY_ERR_HIP;
-    hipLaunchKernelGGL((combine_kernel<D>), dim3(a.H_q, a.B * a.n_q), dim3(kWave), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return SPICY_ERR_HIP;
     return SPICY_OK;
 }

@@ -11,13 +11,16 @@ namespace spicy {
 
 constexpr int kPage = 16;      // entries per page
 constexpr int kWave = 64;      // gfx950 wavefront
-constexpr int kChunk = 32;     // dims per chunk of a key/value page row
+constexpr int kGroup = 8;      // dims per group of a key/value page row
+constexpr int kChunk = 32;     // dims of one MFMA operand chunk (4 groups)
 
 // Offset of element (slot s, dim i) inside a page-head's 16 x d key or value
-// block: 32-dim chunks outermost, then the 16 slots, then the chunk's dims.
-// One chunk of all 16 slots is 1 KB of bf16, read by one wavefront-wide load.
+// block: 8-dim groups outermost, then the 16 slots, then the group's dims.
+// The MFMA operand of a 32-dim chunk (lane 16g + r: slot r, dims
+// 32c + 8g .. +8) is then the 1 KB at 512c elements with lane l reading the
+// l-th 16 bytes: every wavefront-wide load is one sequential 1 KB run.
 __device__ __forceinline__ int slot_elem(int s, int i) {
-    return ((i / kChunk) * kPage + s) * kChunk + i % kChunk;
+    return ((i / kGroup) * kPage + s) * kGroup + i % kGroup;
 }
 
 // ---------------------------------------------------------------- numerics
@@ -207,23 +210,24 @@ struct DecodeArgs {
     float* o;
     float* lse;
     int32_t* err;
-    float* part_ml;        // [B][n_q][H_q][S][2]  running max (log2 units) and sum
-    float* part_o;         // [B][n_q][H_q][S][d]  unnormalised output
+    int32_t* ticket;       // [B][n_q][H_q]        arrivals per query row (zero between calls)
+    float* part_ml;        // [B][n_q][H_q][S][2]  running max (log2 units) and sum of a page group
+    float* part_o;         // [B][n_q][H_q][S][d]  its unnormalised output
     int32_t B;
     int32_t H_q;
     int32_t max_pages;
-    int32_t splits;        // S = prefix_splits + priv_splits partial slots per row
-    int32_t pages_per_split;   // private pages per split
-    int32_t page_begin;        // first private logical page (= prefix_pages on the MFMA path)
-    int32_t priv_splits;       // split-K wavefronts per (sequence, KV head)
-    int32_t prefix_pages;      // P shared logical pages (0 = none)
-    int32_t prefix_chunk;      // pages per shared-prefix wavefront (<= 64)
-    int32_t prefix_splits;     // ceil(P / prefix_chunk) chunks (slots 0 .. prefix_splits-1)
-    int32_t prefix_blocks;     // set by the launcher: workgroups of the prefix role
-    int32_t prefix_tile_blocks;  // set by the launcher: workgroups per (chunk, KV head)
     int32_t n_q;               // query tokens per sequence (rows: (b * n_q + token) * H_q + head)
+    int32_t slots;             // S = prefix_groups + priv_groups partial slots per row
+    int32_t prefix_pages;      // P shared logical pages (0 = none)
+    int32_t prefix_groups;     // page groups of the shared prefix (slots 0 .. prefix_groups-1)
+    int32_t prefix_chunk;      // prefix pages per group
+    int32_t priv_groups;       // page groups of each (sequence, KV head)'s private pages [P, ...)
+    int32_t priv_chunk;        // private pages per group
     int32_t priv_tiles;        // 16-row tiles of one (sequence, KV head): ceil(n_q * G / 16)
-    int32_t priv_wpt;          // set by the launcher: wavefronts of a workgroup on one split's tiles (1, 2, 4)
+    int32_t wpg;               // wavefronts per workgroup of the MFMA kernel (4 or 8)
+    int32_t prefix_sets;       // set by the launcher: tile-sets of one KV head's prefix rows
+    int32_t priv_sets;         // set by the launcher: tile-sets of one (sequence, KV head)
+    int32_t prefix_blocks;     // set by the launcher: workgroups of the prefix role (a multiple of 8)
 };
 
 }  // namespace spicy

@@ -477,9 +477,9 @@ def make_shared_prefix(config_id: int = 4, *, B: int = 32, H_q: int = 28, H_kv: 
 
 def chunked(x: np.ndarray) -> np.ndarray:
     """[P, H, 16, d] entry rows in the cache's page layout [P, H, d/W, 16, W],
-    W = min(32, d)."""
+    W = min(8, d)."""
     P, H, S, d = x.shape
-    W = d if d < 32 else 32
+    W = d if d < 8 else 8
     return np.ascontiguousarray(x.reshape(P, H, S, d // W, W).transpose(0, 1, 3, 2, 4))
 
 

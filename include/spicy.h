@@ -52,11 +52,13 @@
  * Paged compressed cache (caller-allocated pool of `num_pages` pages; one page
  * holds PAGE_SIZE = 16 consecutive logical entries of one sequence for all KV
  * heads):
- *   k    : [num_pages][H_kv][d/32][16][32]  key rows, already rotated (RoPE)
- *                                     to the entry's position, cut in 32-dim
- *                                     chunks: element (slot s, dim i) of a
- *                                     page-head is at ((i/32)*16 + s)*32 + i%32
- *   v    : [num_pages][H_kv][d/32][16][32]  value rows, the same way
+ *   k    : [num_pages][H_kv][d/8][16][8]  key rows, already rotated (RoPE)
+ *                                     to the entry's position, cut in 8-dim
+ *                                     groups: element (slot s, dim i) of a
+ *                                     page-head is at ((i/8)*16 + s)*8 + i%8
+ *                                     (so the 16 slots' dims 8g .. 8g+7 are
+ *                                     256 contiguous bytes in bf16)
+ *   v    : [num_pages][H_kv][d/8][16][8]  value rows, the same way
  *   ab   : [num_pages][H_kv][16][2]   per entry (alpha, beta):
  *                                     alpha = ln(mass), beta = sigma^2/(2d);
  *                                     a null entry has alpha = -inf
@@ -106,6 +108,10 @@ typedef enum { SPICY_F32 = 0, SPICY_BF16 = 1 } spicy_dtype;
                                           [k_t; v_t], bad row pointers, a sequence
                                           longer than 2^20 tokens or one whose
                                           total variation times N reaches 2^62   */
+#define SPICY_DEVERR_TICKET      0x40 /* decode: a row's arrival counter was not
+                                          zero when the call started (workspace
+                                          not zero-filled, or reused for more
+                                          query rows than it was zeroed for)    */
 
 #define SPICY_PAGE_SIZE 16
 #define SPICY_WORKSPACE_HEADER 256   /* bytes before any per-call scratch     */

@@ -104,8 +104,8 @@ def default_threads() -> int:
 
 
 def chunk_width(d: int) -> int:
-    """Dims per chunk of the key/value page layout: min(32, d)."""
-    return d if d < 32 else 32
+    """Dims per group of the key/value page layout: min(8, d)."""
+    return d if d < 8 else 8
 
 
 def rows(x: np.ndarray) -> np.ndarray:
@@ -116,7 +116,7 @@ def rows(x: np.ndarray) -> np.ndarray:
 
 class Cache:
     """Host copy of a paged compressed cache in the library's layout:
-    k, v [P, H, d/W, 16, W] (entry rows cut in chunks of W = min(32, d) dims),
+    k, v [P, H, d/W, 16, W] (entry rows cut in groups of W = min(8, d) dims),
     ab [P, H, 16, 2], meta [P, H, 16]."""
 
     def __init__(self, store: str, num_pages: int, H_kv: int, d: int, fill: bool = True, diag: bool = False):

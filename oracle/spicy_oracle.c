@@ -112,16 +112,16 @@ typedef struct {
 } cache_view;
 
 /* Offset of element (slot, i) inside a page-head block of 16 x d values:
- * chunks of W = min(32, d) dimensions outermost, then the 16 slots, then the
- * W dims of the chunk (the cache layout the header documents; for d < 32 it
+ * groups of W = min(8, d) dimensions outermost, then the 16 slots, then the
+ * W dims of the group (the cache layout the header documents; for d < 8 it
  * is plain entry-major rows). */
 static size_t slot_elem(int32_t d, int32_t slot, int32_t i) {
-    const int32_t W = d < 32 ? d : 32;
+    const int32_t W = d < 8 ? d : 8;
     return ((size_t)(i / W) * PAGE + (size_t)slot) * (size_t)W + (size_t)(i % W);
 }
 
-/* Head sizes the chunked layout can hold: below 32, or a multiple of 32. */
-static int head_dim_ok(int32_t d) { return d > 0 && (d < 32 || d % 32 == 0); }
+/* Head sizes the grouped layout can hold: below 8, or a multiple of 8. */
+static int head_dim_ok(int32_t d) { return d > 0 && (d < 8 || d % 8 == 0); }
 
 /* Store one entry at logical index e of a sequence.  key and val are
  * d-vectors already in their final (rotated) form. */

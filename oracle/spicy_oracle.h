@@ -22,8 +22,8 @@
  *
  * Cache layout (the same contract the GPU library documents, implemented
  * here independently):
- *   k_pool : [num_pages][H_kv][d/W][16][W]  key rows by chunks of W = min(32, d)
- *            dims (d < 32 or d a multiple of 32)
+ *   k_pool : [num_pages][H_kv][d/W][16][W]  key rows by groups of W = min(8, d)
+ *            dims (d < 8 or d a multiple of 8)
  *   v_pool : [num_pages][H_kv][d/W][16][W]  value rows, the same way
  *   ab_pool: [num_pages][H_kv][16][2]      (alpha, beta) per entry
  *   meta   : [num_pages][H_kv][16] x {int32 kind, int32 mass, int64 pos_sum}

@@ -57,18 +57,34 @@ def test_workspace_and_split_plan(lib):
         s = cgd.spicy_decode_num_splits(B, H, P, 0)
         pps = -(-P // s)
         assert 1 <= s <= P and -(-P // pps) == s
-        # every wavefront gets at least 4 pages; together they cover about
-        # the resident 2048 wavefronts when there is that much work
-        assert pps >= min(4, P) and s * B * H >= min(2048, B * H * -(-P // 4)) // 2
-    n = cgd.spicy_decode_workspace_bytes(16, 28, 4, 128, 72, 8)
+        # a page group is one workgroup of 4 wavefronts: about 192 groups over
+        # the call's (sequence, KV head) units, at least one page per
+        # wavefront, cut so that no group is empty
+        want = max(1, min(-(-192 // (B * H)), max(1, P // 4)))
+        n = max(1, min(want, P))
+        assert s == -(-P // -(-P // n))
+        assert pps >= min(4, P) or s == 1
     up = lambda x: (x + 255) // 256 * 256
-    assert n == 256 + up(16 * 28 * 8 * 2 * 4) + up(16 * 28 * 8 * 128 * 4)
-    # shared prefix: slots = prefix chunks + private splits.  32 sequences x 7
-    # query heads per KV head = 14 tiles; page visits 32*4*97 + 144*4*14 =
-    # 20480 over 2048 wavefronts = 10 pages each -> 15 prefix chunks; 97
-    # private pages in 8 explicit splits
-    assert cgd.spicy_decode_shared_workspace_bytes(32, 28, 4, 128, 241, 144, 8) == \
-        256 + up(32 * 28 * 23 * 2 * 4) + up(32 * 28 * 23 * 128 * 4)
+
+    def ws(B, n_q, H_q, d, slots):
+        # header, one int32 ticket per query row, then per (row, slot) the
+        # (max, sum) pair and the d-float unnormalised output
+        rows = B * n_q * H_q
+        return 256 + up(4 * rows) + up(8 * rows * slots) + up(4 * rows * slots * d)
+
+    def f32_groups(maxp, ns):
+        n = min(ns, 256) if ns > 0 else -(-maxp // 16)
+        n = max(1, min(n, maxp))
+        return -(-maxp // -(-maxp // n))
+
+    # 8 explicit splits: 8 private groups on both kernels
+    assert cgd.spicy_decode_workspace_bytes(16, 28, 4, 128, 72, 8) == ws(16, 1, 28, 128, 8)
+    # shared prefix: slots = prefix groups + private groups (bf16), or the fp32
+    # kernel's groups over every page, whichever is larger
+    pl = cgd.spicy_decode_plan(32, 28, 4, 241, 144, 8)
+    assert pl["private_splits"] == 8
+    slots = max(pl["prefix_chunks"] + pl["private_splits"], f32_groups(241, 8))
+    assert cgd.spicy_decode_shared_workspace_bytes(32, 28, 4, 128, 241, 144, 8) == ws(32, 1, 28, 128, slots)
     # fp32 caches ignore the prefix, so the size covers the plain plan too
     assert cgd.spicy_decode_shared_workspace_bytes(2, 4, 2, 64, 40, 39, 5) >= \
         cgd.spicy_decode_workspace_bytes(2, 4, 2, 64, 40, 5)

@@ -31,7 +31,7 @@ def store_value(bits, store):
 
 
 def compare_s2(g, r, kind, store):
-    """g, r: [P, H, d/32, 16, 32] storage; kind [P, H, 16] from the oracle."""
+    """g, r: [P, H, d/8, 16, 8] storage; kind [P, H, 16] from the oracle."""
     gr, rr = oracle.rows(g), oracle.rows(r)                    # [P, H, 16, d]
     exact0 = (kind == 0) | (kind == 1)
     assert not store_value(gr[exact0], store).any(), "C-point or null entry with non-zero variance"
