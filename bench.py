@@ -2,8 +2,9 @@
 
 One step = one pass of the whole hot path over one batch: spicy_coarsen of the
 batch's fresh chunk into the paged cache (plan + segmented moments + RoPE +
-pack), then spicy_decode_attn of one query token per sequence over the whole
-compressed cache (split-K decode + log-sum-exp combine).
+pack), then the decode of one query token per sequence over the whole
+compressed cache (split-K decode with the log-sum-exp combine in the same
+launch).
 
 Default workload: the shared-prefix batch (32 sequences sharing one
 65536-token prefix compressed 28.6x, a private exact suffix of U[512, 2048]
@@ -13,17 +14,28 @@ d = 128), bf16.  Other workloads: --workload qwen2_7b_layer | long_ragged |
 qwen2_1.5b_layer | tiny_fp32 (those have no per-step coarsen; a step is their
 whole coarsen + decode).
 
-Prints ONE JSON line.  `value` = query tokens per second of whole steps.
-`roofline` describes the step's dominant launch (largest share of the step
-time), `roofline_decode` the decode call; `achieved` = algorithmic bytes per
-call / mean call duration from HIP events recorded on the stream the
-kernels run on.  Inputs are resident in HBM before the timed region.
+Prints ONE JSON line.  `value` = query tokens per second of K whole steps.
+Per-call durations come from HIP events on the launch stream, with the calls
+queued behind a sleep kernel so that no call waits for the host: `roofline`
+describes the step's dominant call (largest median duration), and
+`roofline_decode` the decode call, beside the streaming-read ceiling at its
+byte count.  `decode_configs` adds the decode alone on the 7B layer and the
+long ragged batch, over rotated cache copies.  `achieved` = algorithmic bytes
+per call / mean call duration.  Inputs are resident in HBM before the timed
+region.
+
+Other modes: --decode-only (the decode call alone), --copy-calibration (the
+known-size copy that scales rocprofv3's byte counters), --summarize-profile DIR
+(writes profiles/<name>.txt from rocprofv3 CSV output).
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -34,10 +46,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
-ENTRY_EXTRA_META = 16          # bytes of optional metadata per entry-head (not used here)
+DECODE_TARGET_FRAC = 0.70      # the target on compressed-cache decode: 70% of peak HBM bandwidth
+DECODE_CONFIGS = ("qwen2_7b_layer", "long_ragged")
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
@@ -46,13 +59,23 @@ def parse():
     ap.add_argument("--splits", type=int, default=0, help="decode split count (0 = automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--no-decode-configs", action="store_true",
+                    help="skip the decode-alone lines of the 7B layer and the long ragged batch")
     ap.add_argument("--decode-only", action="store_true",
-                    help="diagnostic: time spicy_decode_attn alone over rotated copies of the cache")
+                    help="diagnostic: time the decode call alone over rotated copies of the cache")
     ap.add_argument("--rotate-bytes", type=float, default=1.5e9,
-                    help="decode-only: total bytes of distinct cache copies rotated through")
+                    help="decode-alone timing: total bytes of distinct cache copies rotated through")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 512 MiB device copy (torch.neg, fp32) 5 times: the known-size "
                          "reference that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes")
+    ap.add_argument("--summarize-profile", metavar="DIR",
+                    help="summarize rocprofv3 CSV output under DIR (trace/, FETCH_SIZE/, WRITE_SIZE/, "
+                         "copy_FETCH_SIZE/, copy_WRITE_SIZE/, pmc_<counters>/) into profiles/<--profile-name>.txt")
+    ap.add_argument("--profile-name", default=None, help="name of the summary file under profiles/")
+    ap.add_argument("--profile-commands", default="",
+                    help="the commands that produced DIR, recorded in the summary (one per ';')")
+    ap.add_argument("--profile-last", type=int, default=0,
+                    help="summary: also give the statistics of each kernel's last N dispatches (0 = 2 x steps)")
     ap.add_argument("--device-policy", action="store_true",
                     help="every step also runs spicy_policy on the chunk (equal-variation segments and "
                          "key-norm landmarks on the GPU) and coarsens with its output")
@@ -70,7 +93,7 @@ def parse():
                          "decode reads them in place of the scalar beta")
     ap.add_argument("--no-shared-prefix", action="store_true",
                     help="decode a shared-prefix batch with spicy_decode_attn (every page per sequence)")
-    return ap.parse_args()
+    return ap.parse_args(argv)
 
 
 def elem_bytes(dtype: str) -> int:
@@ -144,13 +167,21 @@ def copy_calibration():
                       "kernel": "torch.neg fp32", "launches": 5}), flush=True)
 
 
+
 # the source file that defines each kernel; its digest also covers the
 # headers every kernel includes
 KERNEL_SOURCE = {
     "coarsen_main_kernel": "coarsen.hip", "coarsen_cpoint_kernel": "coarsen.hip",
-    "decode_mfma_kernel": "decode.hip", "combine_kernel": "decode.hip", "decode_f32_kernel": "decode.hip",
+    "decode_mfma_kernel": "decode.hip", "decode_f32_kernel": "decode.hip",
     "policy_token_kernel": "policy.hip", "policy_seq_kernel": "policy.hip",
     "merge_list_kernel": "merge.hip", "merge_pair_kernel": "merge.hip",
+}
+# the kernels of each call, for its traffic
+CALL_KERNELS = {
+    "coarsen": ["coarsen_main_kernel", "coarsen_cpoint_kernel"],
+    "decode": ["decode_mfma_kernel"],
+    "policy": ["policy_token_kernel", "policy_seq_kernel"],
+    "merge": ["merge_list_kernel", "merge_pair_kernel"],
 }
 
 
@@ -187,15 +218,40 @@ def measured_traffic(workload: str):
     return table
 
 
+# ------------------------------------------------------------------ host cores
+
+def host_description() -> dict:
+    """The host the oracle runs on: its CPU model, the logical CPUs of the
+    machine and of this process's affinity set, and the thread count the
+    oracle uses (the affinity set, capped by OMP_NUM_THREADS when the
+    environment sets it, as the GPU machines do for each process's share)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.lower().startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    aff = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    cap = os.environ.get("OMP_NUM_THREADS")
+    threads = min(aff, int(cap)) if cap and cap.isdigit() and int(cap) > 0 else aff
+    return {"cpu_model": model, "nproc": os.cpu_count(), "affinity": aff, "threads": threads}
+
+
 def cpu_baseline(wl, reps: int, policy: bool = False, q_tokens: int = 1, diag: bool = False,
                  weighted: bool = False, merge: bool = False):
     """The oracle (plain C, double precision) on the host cores: one whole
     step for every sequence of the batch (with `policy`, the oracle's policy
     on the chunk first; then the per-step coarsen and the decode), setup calls
-    untimed.  Returns query tokens/s and details."""
+    untimed.  Coarsening runs one sequence per work item, decoding one
+    (sequence, KV head) per work item, over all the threads host_description
+    gives.  Returns query tokens/s and details."""
     import dataclasses
     import oracle
-    threads = oracle.default_threads()
+    host = host_description()
+    threads = host["threads"]
     cache = oracle.Cache(wl.dtype, wl.num_pages, wl.H_kv, wl.d, fill=False, diag=diag)
     lengths = None
     for call in wl.setup:
@@ -227,29 +283,20 @@ def cpu_baseline(wl, reps: int, policy: bool = False, q_tokens: int = 1, diag: b
             times.append(dt)
         print(f"[bench] cpu oracle step {r}: {dt:.3f} s", file=sys.stderr, flush=True)
     med = statistics.median(times)
-    return dict(value=wl.B * q_tokens / med, unit="query-tokens/s", cores=threads, kind="oracle",
-                sample=f"one whole step of the same workload ({wl.B} sequences: "
-                       f"{'policy (single thread) + ' if policy else ''}"
-                       f"{'per-step coarsen + ' if wl.step is not None else ''}decode"
-                       f"{f' of {q_tokens} query tokens per sequence' if q_tokens > 1 else ''}"
-                       f"{', diagonal closure' if diag else ''}"
-                       f"{', variation-weighted representatives' if weighted else ''}"
-                       f"{', one merge level over the chunk' if merge else ''}), "
-                       f"median of {reps} after 1 warm-up, {med:.3f} s per step")
+    out = dict(value=wl.B * q_tokens / med, unit="query-tokens/s", cores=threads, kind="oracle",
+               sample=f"one whole step of the same workload ({wl.B} sequences: "
+                      f"{'policy (single thread) + ' if policy else ''}"
+                      f"{'per-step coarsen + ' if wl.step is not None else ''}decode"
+                      f"{f' of {q_tokens} query tokens per sequence' if q_tokens > 1 else ''}"
+                      f"{', diagonal closure' if diag else ''}"
+                      f"{', variation-weighted representatives' if weighted else ''}"
+                      f"{', one merge level over the chunk' if merge else ''}), "
+                      f"median of {reps} after 1 warm-up, {med:.3f} s per step")
+    out.update(host)
+    return out
 
 
-def _rotating_copies(dw, rotate_bytes: float):
-    """L distinct copies of the compressed cache (L x cache bytes >= rotate_bytes,
-    well above the 256 MB Infinity Cache), so that calls rotating through them
-    stream their cache from HBM."""
-    from coarse_grained_decode_amd import PagedCache
-    parts = (dw.cache.k, dw.cache.v, dw.cache.ab) + ((dw.cache.s2,) if dw.cache.s2 is not None else ())
-    cache_bytes = sum(t.numel() * t.element_size() for t in parts)
-    L = max(1, int(np.ceil(rotate_bytes / cache_bytes)))
-    copies = [PagedCache(dw.cache.k.clone(), dw.cache.v.clone(), dw.cache.ab.clone(), None,
-                         dw.cache.s2.clone() if dw.cache.s2 is not None else None) for _ in range(L)]
-    return copies, cache_bytes
-
+# --------------------------------------------------------------- GPU timing
 
 _SLEEP = {}
 
@@ -271,67 +318,149 @@ def _sleep_cycles_for(us: float) -> int:
     return max(1, int(us / _SLEEP["per_cycle_us"]))
 
 
+def _hold_stream(host_us: float) -> None:
+    """Queue a sleep kernel long enough (3x the host time of what follows, +2
+    ms) that the host enqueues everything behind it before the GPU gets there."""
+    import torch
+    torch.cuda._sleep(_sleep_cycles_for(3 * host_us + 2000))
+
+
 def _queued_per_call_us(issue, n_calls: int, reps: int, warmup: int = 2):
     """Per-call microseconds of `issue()` (n_calls calls on the current
     stream), measured with the calls back to back on the GPU: a sleep kernel
     holds the stream while the host enqueues them, and the events bracket only
-    the calls.  The sleep is sized from the host's enqueue time, so no call
-    waits for the host."""
+    the calls."""
     import torch
     t0 = time.perf_counter()
     issue()
     torch.cuda.synchronize()
     host_us = (time.perf_counter() - t0) * 1e6
-    cycles = _sleep_cycles_for(3 * host_us + 2000)
     out = []
     for r in range(warmup + reps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda._sleep(cycles)
+        _hold_stream(host_us)
         e0.record()
-        t0 = time.perf_counter()
         issue()
-        host = (time.perf_counter() - t0) * 1e6
         e1.record()
         e1.synchronize()
-        gpu = e0.elapsed_time(e1) * 1e3
-        if host > 0.9 * _SLEEP["per_cycle_us"] * cycles:
-            print(f"[bench] warning: enqueueing took {host:.0f} us, longer than the sleep", file=sys.stderr)
         if r >= warmup:
-            out.append(gpu / n_calls)
+            out.append(e0.elapsed_time(e1) * 1e3 / n_calls)
     return out
 
 
 def _stats(xs):
     xs = sorted(xs)
     q = lambda f: xs[min(len(xs) - 1, max(0, int(round(f * (len(xs) - 1)))))]
-    return {"median": round(statistics.median(xs), 3), "p10": round(q(0.1), 3), "p90": round(q(0.9), 3)}
+    return {"median": round(statistics.median(xs), 3), "p10": round(q(0.1), 3), "p90": round(q(0.9), 3),
+            "mean": round(statistics.mean(xs), 3), "n": len(xs)}
 
 
-def read_ceiling_us(nbytes: int, rotate_bytes: float, replays: int = 20):
-    """Plain streaming-read ceiling at `nbytes`: the fastest of a few torch
-    read-only reductions over a tensor of that size, rotating through distinct
-    tensors (L x nbytes >= rotate_bytes), back to back on the GPU.  Returns
-    (microseconds per read, the op that gave it)."""
+def _rotating_copies(dw, rotate_bytes: float):
+    """L distinct copies of the compressed cache (L x cache bytes >= rotate_bytes,
+    well above the 256 MB Infinity Cache), so that calls rotating through them
+    stream their cache from HBM."""
+    from coarse_grained_decode_amd import PagedCache
+    parts = (dw.cache.k, dw.cache.v, dw.cache.ab) + ((dw.cache.s2,) if dw.cache.s2 is not None else ())
+    cache_bytes = sum(t.numel() * t.element_size() for t in parts)
+    L = max(1, int(np.ceil(rotate_bytes / cache_bytes)))
+    copies = [PagedCache(dw.cache.k.clone(), dw.cache.v.clone(), dw.cache.ab.clone(), None,
+                         dw.cache.s2.clone() if dw.cache.s2 is not None else None) for _ in range(L)]
+    return copies, cache_bytes
+
+
+# ------------------------------------------------------------ read ceilings
+
+_PROBE = {}
+
+
+def _probe_lib():
+    """libspicy_probe.so: the plain streaming-read kernel (not part of the
+    SPICY-KV library; built beside it)."""
+    import ctypes
+    if "lib" not in _PROBE:
+        from coarse_grained_decode_amd import build as B
+        if not os.path.exists(B.PROBE_LIB):
+            raise RuntimeError(f"{B.PROBE_LIB} is missing: build with python -m coarse_grained_decode_amd.build")
+        L = ctypes.CDLL(B.PROBE_LIB)
+        L.spicy_probe_stream_read.restype = ctypes.c_int
+        L.spicy_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32,
+                                              ctypes.c_void_p, ctypes.c_void_p]
+        _PROBE["lib"] = L
+    return _PROBE["lib"]
+
+
+def read_ceiling(nbytes: int, rotate_bytes: float, reps: int = 10) -> dict:
+    """Plain streaming-read ceiling at `nbytes`, over distinct buffers rotated
+    through (L x nbytes >= rotate_bytes), calls back to back on the GPU:
+      probe: the fastest of a few launch shapes of a grid-stride read of
+             16-byte loads (libspicy_probe.so);
+      torch: the fastest torch read-only reduction of the same bytes (rows
+             of 4096 fp32 reduced along the row)."""
     import torch
-    # rows of 4096 floats reduced along the row: each output depends on one
-    # row only, so the reduction needs no cross-workgroup staging; the
-    # output is 1/4096 of the bytes read
-    cols = 4096
-    rows = max(1, nbytes // (4 * cols))
-    L = max(1, int(np.ceil(rotate_bytes / (4 * rows * cols))))
-    bufs = [torch.ones(rows, cols, dtype=torch.float32, device="cuda") for _ in range(L)]
-    outs = [torch.empty(rows, dtype=torch.float32, device="cuda") for _ in range(L)]
-    ops = {"sum": lambda x, o: torch.sum(x, dim=1, out=o), "amax": lambda x, o: torch.amax(x, dim=1, out=o)}
+    lib = _probe_lib()
+    nb = max(16, nbytes // 16 * 16)
+    L = max(1, int(np.ceil(rotate_bytes / nb)))
+    bufs = [torch.ones(nb // 4, dtype=torch.float32, device="cuda") for _ in range(L)]
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
     best = None
-    for name, op in ops.items():
-        def issue(op=op):
-            for x, o in zip(bufs, outs):
-                op(x, o)
-        us = statistics.median(_queued_per_call_us(issue, L, replays))
+    for blocks_per_cu, unroll in ((8, 1), (16, 1), (8, 8), (4, 2)):
+        def issue(bpc=blocks_per_cu, u=unroll):
+            for x in bufs:
+                rc = lib.spicy_probe_stream_read(x.data_ptr(), nb, 256 * bpc, u, sink.data_ptr(), stream)
+                assert rc == 0, rc
+        us = statistics.median(_queued_per_call_us(issue, L, reps))
         if best is None or us < best[0]:
-            best = (us, name)
-    del bufs
-    return best
+            best = (us, f"grid-stride 16-byte loads, {256 * blocks_per_cu} workgroups x 256, {unroll} in flight")
+    cols = 4096
+    rows = max(1, nb // (4 * cols))
+    views = [x[:rows * cols].view(rows, cols) for x in bufs]
+    outs = [torch.empty(rows, dtype=torch.float32, device="cuda") for _ in range(L)]
+    tbest = None
+    for name, op in (("sum", torch.sum), ("amax", torch.amax)):
+        def issue(op=op):
+            for x, o in zip(views, outs):
+                op(x, dim=1, out=o)
+        us = statistics.median(_queued_per_call_us(issue, L, reps))
+        if tbest is None or us < tbest[0]:
+            tbest = (us, f"torch.{name}(dim=1) over fp32 rows of 4096")
+    del bufs, views, outs
+    gbs = lambda us: nb / (us * 1e-6) / 1e9
+    return {"us": round(best[0], 3), "GBps": round(gbs(best[0]), 1), "frac": round(gbs(best[0]) / HBM_PEAK_GBS, 4),
+            "op": best[1], "bytes": int(nb),
+            "torch": {"us": round(tbest[0], 3), "GBps": round(gbs(tbest[0]), 1), "op": tbest[1]}}
+
+
+# ------------------------------------------------------------ decode alone
+
+def decode_config_line(wl, dw, rotate_bytes: float, reps: int, ceiling: bool = True) -> dict:
+    """The decode call alone, back to back over rotated cache copies:
+    per-call time (median, p10, p90), algorithmic bytes and rate, and the
+    streaming-read ceiling at that byte count."""
+    lengths = dw.lengths.cpu().numpy()
+    copies, cache_bytes = _rotating_copies(dw, rotate_bytes)
+    L = len(copies)
+
+    def issue():
+        for c in copies:
+            dw.decode(c)
+    per_call = _queued_per_call_us(issue, L, reps)
+    assert int(dw.dws[0].item()) == 0, "device error word set (decode)"
+    db = decode_alg_bytes(wl, lengths, dw.q_tokens, dw.cache.s2 is not None)
+    st = _stats(per_call)
+    gbs = db / (st["mean"] * 1e-6) / 1e9
+    out = {"workload": wl.name, "description": wl.description, "calls_per_rep": L, "cache_bytes": int(cache_bytes),
+           "bound": "hbm", "alg_bytes_per_call": int(db), "call_us": st, "achieved": round(gbs, 1),
+           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+           "target_frac": DECODE_TARGET_FRAC,
+           "query_tokens_per_s": round(wl.B * dw.q_tokens / (st["mean"] * 1e-6), 1),
+           "query_tokens_per_seq": dw.q_tokens, "plan": dw.plan, "shared_prefix_pages": dw.shared_prefix_pages}
+    del copies
+    if ceiling:
+        c = read_ceiling(db, rotate_bytes)
+        out["ceiling"] = c
+        out["frac_of_ceiling"] = round(c["us"] / st["mean"], 4)
+    return out
 
 
 def decode_only(args, wl, dw):
@@ -348,47 +477,175 @@ def decode_only(args, wl, dw):
     print(json.dumps(line), flush=True)
 
 
-def decode_config_line(wl, dw, rotate_bytes: float, replays: int, ceiling: bool = True):
-    """Per-call decode time (median, p10, p90 over repetitions of L rotated
-    calls run back to back), algorithmic bytes and rate, and the read ceiling
-    at that size."""
+def decode_configs(args, dev) -> list:
+    """The decode alone on the 7B layer and the long ragged batch (their
+    coarsening once, untimed), one line each."""
     import torch
-    lengths = dw.lengths.cpu().numpy()
-    copies, cache_bytes = _rotating_copies(dw, rotate_bytes)
-    L = len(copies)
-
-    def issue():
-        for c in copies:
-            dw.decode(c)
-    per_call = _queued_per_call_us(issue, L, replays)
-    assert int(dw.dws[0].item()) == 0, "device error word set (decode)"
-    db = decode_alg_bytes(wl, lengths, dw.q_tokens, dw.cache.s2 is not None)
-    st = _stats(per_call)
-    us = st["median"]
-    gbs = db / (us * 1e-6) / 1e9
-    out = {"workload": wl.name, "calls_per_replay": L, "replays": replays, "cache_bytes": int(cache_bytes),
-           "alg_bytes_per_call": int(db), "call_us": st, "achieved_GBps": round(gbs, 1),
-           "frac": round(gbs / HBM_PEAK_GBS, 4),
-           "query_tokens_per_s": round(wl.B * dw.q_tokens / (us * 1e-6), 1),
-           "query_tokens_per_seq": dw.q_tokens, "plan": dw.plan, "shared_prefix_pages": dw.shared_prefix_pages}
-    del copies
-    if ceiling:
-        cus, op = read_ceiling_us(db, rotate_bytes)
-        cg = db / (cus * 1e-6) / 1e9
-        out["ceiling"] = {"us": round(cus, 3), "GBps": round(cg, 1), "frac": round(cg / HBM_PEAK_GBS, 4),
-                          "op": f"torch.{op}(dim=1) over fp32 rows of 4096, same byte count, rotated, "
-                                "back to back"}
-        out["frac_of_ceiling"] = round(gbs / cg, 4)
+    from coarse_grained_decode_amd import workloads as W
+    from coarse_grained_decode_amd.runner import DeviceWorkload
+    out = []
+    for name in DECODE_CONFIGS:
+        t0 = time.perf_counter()
+        wl = W.WORKLOADS[name]()
+        dw = DeviceWorkload.of(wl, dev, meta=False, fill=None)
+        dw.run_setup()
+        torch.cuda.synchronize()
+        print(f"[bench] decode config {name}: generated and coarsened in {time.perf_counter() - t0:.1f} s",
+              file=sys.stderr, flush=True)
+        out.append(decode_config_line(wl, dw, args.rotate_bytes, max(10, args.steps // 2)))
+        del dw, wl
+        torch.cuda.empty_cache()
     return out
 
 
+# --------------------------------------------------------- profile summary
+
+def _base_kernel_name(name: str) -> str:
+    """'void spicy::decode_mfma_kernel<128, 3, ...>(spicy::DecodeArgs)' ->
+    'decode_mfma_kernel' (and torch's kernels to their template name)."""
+    n = name.split("(")[0]
+    n = re.sub(r"<.*", "", n)
+    return n.split("::")[-1].replace("void ", "").strip()
+
+
+def _read_csvs(pattern):
+    rows = []
+    for path in sorted(glob.glob(pattern, recursive=True)):
+        with open(path, newline="") as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def _dispatches(d):
+    """Kernel dispatches of a rocprofv3 --kernel-trace CSV dir, in start order:
+    (base name, duration us)."""
+    rows = _read_csvs(os.path.join(d, "**", "*kernel_trace.csv"))
+    out = [(_base_kernel_name(r["Kernel_Name"]), int(r["Start_Timestamp"]),
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3) for r in rows]
+    out.sort(key=lambda x: x[1])
+    return [(n, du) for n, _, du in out]
+
+
+def _counters(d):
+    """Per dispatch counter values of a rocprofv3 --pmc CSV dir, in dispatch
+    order: {base kernel name: [{counter: value}, ...]}."""
+    rows = _read_csvs(os.path.join(d, "**", "*counter_collection.csv"))
+    per = {}
+    for r in rows:
+        key = (int(r.get("Dispatch_Id", 0)), _base_kernel_name(r["Kernel_Name"]))
+        per.setdefault(key, {})
+        name = r["Counter_Name"]
+        per[key][name] = per[key].get(name, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (did, k), v in sorted(per.items()):
+        out.setdefault(k, []).append(v)
+    return out
+
+
+def summarize_profile(args) -> None:
+    """Write profiles/<name>.txt from the rocprofv3 CSV output under DIR:
+    per-kernel durations (all dispatches and the last N), HBM traffic per
+    launch (FETCH_SIZE and WRITE_SIZE scaled by the copy calibration), any
+    other counter passes, and the machine-read traffic lines with the
+    kernels' source digests."""
+    d = args.summarize_profile
+    name = args.profile_name or "profile"
+    last = args.profile_last or 2 * args.steps
+    lines = [f"# rocprofv3 summary: SPICY-KV kernels, {name}", ""]
+    if args.profile_commands:
+        lines.append("Commands (run from /tmp with TMPDIR=/tmp; R = repository root, OUT = output dir):")
+        lines += [f"  {c.strip()}" for c in args.profile_commands.split(";") if c.strip()]
+        lines.append("")
+    disp = _dispatches(os.path.join(d, "trace"))
+    if disp:
+        lines.append(f"## Kernel durations (kernel trace; 'last' = each kernel's last {last} dispatches)")
+        lines.append("")
+        lines.append(f"{'kernel':34s} {'calls':>6s} {'mean us':>9s} {'median':>8s} {'min':>8s} {'max':>8s}   "
+                     f"{'last mean':>9s} {'last med':>9s} {'last p10':>9s} {'last p90':>9s}")
+        by = {}
+        for n, du in disp:
+            by.setdefault(n, []).append(du)
+        for n, xs in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+            tl = sorted(xs[-last:])
+            q = lambda f: tl[min(len(tl) - 1, int(round(f * (len(tl) - 1))))]
+            lines.append(f"{n[:34]:34s} {len(xs):6d} {statistics.mean(xs):9.2f} {statistics.median(xs):8.2f} "
+                         f"{min(xs):8.2f} {max(xs):8.2f}   {statistics.mean(tl):9.2f} {statistics.median(tl):9.2f} "
+                         f"{q(0.1):9.2f} {q(0.9):9.2f}")
+        lines.append("")
+    fetch = _counters(os.path.join(d, "FETCH_SIZE"))
+    write = _counters(os.path.join(d, "WRITE_SIZE"))
+    cf = _counters(os.path.join(d, "copy_FETCH_SIZE"))
+    cw = _counters(os.path.join(d, "copy_WRITE_SIZE"))
+    digest_lines = []
+    if fetch and write and cf and cw:
+        def copy_kib(c, ctr):
+            vals = [v[ctr] for k, vs in c.items() if "neg" in k or "elementwise" in k for v in vs if ctr in v]
+            return statistics.median(vals)
+        fk = copy_kib(cf, "FETCH_SIZE")
+        wk = copy_kib(cw, "WRITE_SIZE")
+        ff = COPY_BYTES / (fk * 1024.0)
+        wf = COPY_BYTES / (wk * 1024.0)
+        lines.append("## HBM traffic per launch (FETCH_SIZE / WRITE_SIZE, KiB per dispatch, median of each "
+                     "kernel's last 3 dispatches)")
+        lines.append("")
+        lines.append(f"Calibration: a plain fp32 copy of {COPY_BYTES} bytes (torch.neg) reads FETCH_SIZE {fk:.0f} KiB "
+                     f"and WRITE_SIZE {wk:.0f} KiB per dispatch: bytes = KiB x 1024 x {ff:.4f} (fetch), "
+                     f"x {wf:.4f} (write).")
+        lines.append("")
+        lines.append(f"{'kernel':34s} {'FETCH KiB':>12s} {'WRITE KiB':>12s} {'bytes/launch':>14s}")
+        for k in sorted(set(fetch) & set(write)):
+            fv = statistics.median([v["FETCH_SIZE"] for v in fetch[k][-3:] if "FETCH_SIZE" in v])
+            wv = statistics.median([v["WRITE_SIZE"] for v in write[k][-3:] if "WRITE_SIZE" in v])
+            b = fv * 1024 * ff + wv * 1024 * wf
+            lines.append(f"{k[:34]:34s} {fv:12.0f} {wv:12.0f} {b:14.0f}")
+            if k in KERNEL_SOURCE:
+                digest_lines.append(f"traffic_bytes {k} {b:.0f} {kernel_digest(k)}")
+        lines.append("")
+    for pdir in sorted(glob.glob(os.path.join(d, "pmc_*"))):
+        ctr = _counters(pdir)
+        if not ctr:
+            continue
+        names = sorted({c for vs in ctr.values() for v in vs for c in v})
+        lines.append(f"## Counters {', '.join(names)} (per dispatch, median of each kernel's last 3 dispatches)")
+        lines.append("")
+        lines.append(f"{'kernel':34s} " + " ".join(f"{n:>24s}" for n in names))
+        for k, vs in sorted(ctr.items()):
+            row = []
+            for n in names:
+                xs = [v[n] for v in vs[-3:] if n in v]
+                row.append(f"{statistics.median(xs):24.6g}" if xs else f"{'-':>24s}")
+            lines.append(f"{k[:34]:34s} " + " ".join(row))
+        lines.append("")
+    if digest_lines:
+        lines.append("Machine-read lines (bench.py reports a kernel's `traffic` only while its sources hash to the "
+                     "value given):")
+        lines.append("(each line: kernel, bytes per launch, sha256 of the kernel's source file and the shared headers)")
+        lines += digest_lines
+        lines.append("")
+    bench_line = os.path.join(d, "bench_line.json")
+    if os.path.exists(bench_line):
+        lines.append("## bench.py line of the same tree")
+        lines.append("")
+        with open(bench_line) as fh:
+            lines.append(fh.read().strip().splitlines()[-1])
+        lines.append("")
+    out = os.path.join(ROOT, "profiles", f"{name}.txt")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines))
+    print(f"wrote {out}", flush=True)
+
+
+# ---------------------------------------------------------------------- main
+
 def main():
     args = parse()
+    if args.summarize_profile:
+        return summarize_profile(args)
     if args.copy_calibration:
         return copy_calibration()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the library has no "
-              "multi-GPU path", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the library has no "
+              "multi-GPU path, and every number it reports is one GPU's", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -437,15 +694,27 @@ def main():
             spicy_merge_level(dw.cache, mc.call.rope_base, mc.page_table, mc.entry_start, mc.lengths, max_range,
                               mws, max_pages_per_seq=mc.call.max_pages)
 
-    def step():
+    def step(ev=None):
+        """One step; with ev (5 events) each call is bracketed:
+        ev[3] policy ev[0] coarsen ev[1] merge ev[4] decode ev[2]."""
+        if ev is not None:
+            ev[3].record()
         if policy is not None:
             policy.run(dw.step)
+        if ev is not None:
+            ev[0].record()
         for c in step_calls:
             c.run(dw.cache)
+        if ev is not None:
+            ev[1].record()
         if run_merge is not None:
             run_merge()
+        if ev is not None:
+            ev[4].record()
         dw.lengths = step_calls[-1].lengths
         dw.decode()
+        if ev is not None:
+            ev[2].record()
 
     if args.decode_only:
         return decode_only(args, wl, dw)
@@ -467,76 +736,72 @@ def main():
     elapsed = time.perf_counter() - t0
     assert int(dw.dws[0].item()) == 0, "device error word set (decode)"
 
-    # per-call durations for the rooflines: K more whole steps, each call
-    # bracketed by HIP events on the launch stream.  They run after the
-    # throughput loop because an event recorded between two calls leaves the
-    # GPU idle for a few microseconds; part of that idle time lands inside the
-    # bracketed durations, so these err on the slow side.
+    # per-call durations: K more whole steps queued behind a sleep kernel (so
+    # that no call waits for the host), each call bracketed by HIP events on
+    # the launch stream
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
+    _hold_stream(elapsed * 1e6 * 1.5)
     for e in evs:
-        e[3].record()
-        if policy is not None:
-            policy.run(dw.step)
-        e[0].record()
-        for c in step_calls:
-            c.run(dw.cache)
-        e[1].record()
-        if run_merge is not None:
-            run_merge()
-        e[4].record()
-        dw.decode()
-        e[2].record()
+        step(e)
     torch.cuda.synchronize()
-    coarsen_ms = statistics.mean(e[0].elapsed_time(e[1]) for e in evs)
-    decode_ms = statistics.mean(e[4].elapsed_time(e[2]) for e in evs)
-    merge_ms = statistics.mean(e[1].elapsed_time(e[4]) for e in evs) if run_merge is not None else None
-    policy_ms = statistics.mean(e[3].elapsed_time(e[0]) for e in evs) if policy is not None else None
+    per = {
+        "coarsen": [e[0].elapsed_time(e[1]) * 1e3 for e in evs],
+        "decode": [e[4].elapsed_time(e[2]) * 1e3 for e in evs],
+    }
+    if run_merge is not None:
+        per["merge"] = [e[1].elapsed_time(e[4]) * 1e3 for e in evs]
+    if policy is not None:
+        per["policy"] = [e[3].elapsed_time(e[0]) * 1e3 for e in evs]
+    step_us = [e[3].elapsed_time(e[2]) * 1e3 for e in evs]
+
     lengths = dw.lengths.cpu().numpy()
-    cb = sum(coarsen_alg_bytes(c.call, c.lengths.cpu().numpy(), args.diag_closure, args.weighted, args.merge)
-             for c in step_calls)
-    db = decode_alg_bytes(wl, lengths, args.query_tokens, args.diag_closure)
+    alg = {
+        "coarsen": sum(coarsen_alg_bytes(c.call, c.lengths.cpu().numpy(), args.diag_closure, args.weighted, args.merge)
+                       for c in step_calls),
+        "decode": decode_alg_bytes(wl, lengths, args.query_tokens, args.diag_closure),
+    }
+    names = {
+        "coarsen": "spicy_coarsen (coarsen_main: plan + streaming, then coarsen_cpoint: entries)",
+        "decode": ("spicy_decode_attn_multi" if args.query_tokens > 1 else
+                   "spicy_decode_attn_shared" if dw.shared_prefix_pages else "spicy_decode_attn") +
+                  " (decode_mfma: split-K pages, log-sum-exp combine in the same launch)",
+        "policy": "spicy_policy (policy_token: fixed point, projection, variation, key norms; "
+                  "then policy_seq: scan, boundaries, landmark radix select)",
+        "merge": "spicy_merge_level (merge_list: pairs per sequence and head; merge_pair: law of total "
+                 "variance per pair)",
+    }
+    pairs = None
+    if policy is not None:
+        alg["policy"] = policy_alg_bytes(dw.step.call, wl.policy)
+    if run_merge is not None:
+        mc = step_calls[-1]
+        units = mc.call.B * mc.call.H_kv
+        pairs = int(mws.view(torch.uint8)[256:256 + 4 * units].view(torch.int32).sum().item())
+        assert int(mws[0].item()) == 0, "device error word set (merge)"
+        alg["merge"] = merge_alg_bytes(mc.call, mc.lengths.cpu().numpy(), pairs)
 
     traffic = measured_traffic(wl.name + ("_policy" if policy is not None else "") +
                                (f"_q{args.query_tokens}" if args.query_tokens > 1 else "") +
                                ("_weighted" if args.weighted else "") + ("_diag" if args.diag_closure else "") +
                                ("_merge" if args.merge else ""))
 
-    def roof(nbytes, ms, kernels):
-        gbs = nbytes / (ms * 1e-3) / 1e9
+    def roof(call):
+        st = _stats(per[call])
+        gbs = alg[call] / (st["mean"] * 1e-6) / 1e9
+        ks = CALL_KERNELS[call]
         t = None
-        if traffic is not None and all(k in traffic for k in kernels):
-            t = int(sum(traffic[k] for k in kernels))
+        if traffic is not None and all(k in traffic for k in ks):
+            t = int(sum(traffic[k] for k in ks))
         return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": t,
-                "alg_bytes_per_call": int(nbytes), "mean_call_us": round(ms * 1e3, 2)}
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": t, "alg_bytes_per_call": int(alg[call]),
+                "mean_call_us": st["mean"], "call_us": st, "kernel": names[call]}
 
-    r_coarsen = roof(cb, coarsen_ms, ["coarsen_main_kernel", "coarsen_cpoint_kernel"])
-    r_decode = roof(db, decode_ms, ["decode_mfma_kernel", "combine_kernel"])
-    r_coarsen["kernel"] = "spicy_coarsen (coarsen_main: plan + streaming, then coarsen_cpoint: entries)"
-    r_decode["kernel"] = ("spicy_decode_attn_shared" if dw.shared_prefix_pages else "spicy_decode_attn") + \
-        " (decode_mfma + combine)"
-    calls = [(coarsen_ms, r_coarsen), (decode_ms, r_decode)]
-    if policy is not None:
-        c = dw.step.call
-        pb = policy_alg_bytes(c, wl.policy)
-        r_policy = roof(pb, policy_ms, ["policy_token_kernel", "policy_seq_kernel"])
-        r_policy["kernel"] = "spicy_policy (policy_token: fixed point, projection, variation, key norms; " \
-                             "then policy_seq: scan, boundaries, landmark radix select)"
-        calls.append((policy_ms, r_policy))
-    if run_merge is not None:
-        mc = step_calls[-1]
-        units = mc.call.B * mc.call.H_kv
-        pairs = int(mws.view(torch.uint8)[256:256 + 4 * units].view(torch.int32).sum().item())
-        assert int(mws[0].item()) == 0, "device error word set (merge)"
-        mb = merge_alg_bytes(mc.call, mc.lengths.cpu().numpy(), pairs)
-        r_merge = roof(mb, merge_ms, ["merge_list_kernel", "merge_pair_kernel"])
-        r_merge["kernel"] = "spicy_merge_level (merge_list: pairs per sequence and head; merge_pair: law of " \
-                            "total variance per pair)"
-        r_merge["pairs_per_call"] = pairs
-        calls.append((merge_ms, r_merge))
-    calls.sort(key=lambda x: -x[0])
-    dominant, other = calls[0][1], calls[1][1]
+    rooflines = {c: roof(c) for c in per}
+    dominant = max(rooflines, key=lambda c: rooflines[c]["call_us"]["median"])
+    r_decode = dict(rooflines["decode"])
+    r_decode["target_frac"] = DECODE_TARGET_FRAC
+    r_decode["ceiling"] = read_ceiling(alg["decode"], args.rotate_bytes)
+    r_decode["frac_of_ceiling"] = round(r_decode["ceiling"]["us"] / r_decode["call_us"]["mean"], 4)
 
     ms_per_step = elapsed * 1e3 / args.steps
     out = {
@@ -554,20 +819,25 @@ def main():
         "data": "synthetic (seeded clustered-Gaussian keys, Gaussian values/queries)",
         "config": {"workload": wl.name, "description": wl.description, "batch": wl.B,
                    "num_q_heads": wl.H_q, "num_kv_heads": wl.H_kv, "head_dim": wl.d,
-                   "decode_splits": dw.splits, "decode_plan": dw.plan,
-                   "shared_prefix_pages": dw.shared_prefix_pages,
+                   "decode_plan": dw.plan, "shared_prefix_pages": dw.shared_prefix_pages,
                    "cache_entries_per_seq_mean": float(lengths.mean()),
                    "device_policy": policy is not None, "query_tokens_per_seq": args.query_tokens,
                    "diag_closure": args.diag_closure, "weighted_representatives": args.weighted,
                    "merge_level": args.merge},
-        "roofline": dominant,
-        "roofline_other": other,
-        "decode_query_tokens_per_s": round(wl.B * args.query_tokens / (decode_ms * 1e-3), 1),
+        "step_us": _stats(step_us),
+        "roofline": rooflines[dominant],
+        "roofline_decode": r_decode,
+        "decode_query_tokens_per_s": round(wl.B * args.query_tokens / (r_decode["call_us"]["mean"] * 1e-6), 1),
     }
-    if policy is not None:
-        out["roofline_policy"] = r_policy
-    if run_merge is not None:
-        out["roofline_merge"] = r_merge
+    for c in ("coarsen", "policy", "merge"):
+        if c in rooflines and c != dominant:
+            out[f"roofline_{c}"] = rooflines[c]
+    if pairs is not None:
+        out["roofline_merge" if dominant != "merge" else "roofline"]["pairs_per_call"] = pairs
+    if not args.no_decode_configs:
+        del dw
+        torch.cuda.empty_cache()
+        out["decode_configs"] = decode_configs(args, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_reps, policy=policy is not None,
                                            q_tokens=args.query_tokens, diag=args.diag_closure,

@@ -21,9 +21,11 @@ __all__ = [
     "spicy_decode_attn_shared", "spicy_decode_shared_workspace_bytes",
     "spicy_policy", "spicy_policy_workspace_bytes",
     "spicy_decode_attn_multi", "spicy_decode_multi_workspace_bytes",
-    "spicy_status_string", "library_path", "load_library",
+    "spicy_coarsen_weighted", "spicy_merge_level", "spicy_merge_workspace_bytes", "spicy_decode_plan",
+    "spicy_status_string", "library_path", "load_library", "workspace", "device_error",
     "SPICY_F32", "SPICY_BF16", "PAGE_SIZE", "WORKSPACE_HEADER",
-    "DEVERR_PAGE_ID", "DEVERR_CAPACITY", "DEVERR_SEGMENTS", "DEVERR_LENGTH", "DEVERR_POLICY",
+    "DEVERR_PAGE_ID", "DEVERR_CAPACITY", "DEVERR_SEGMENTS", "DEVERR_LENGTH", "DEVERR_SHARED", "DEVERR_POLICY",
+    "DEVERR_TICKET",
 ]
 
 SPICY_F32 = 0
@@ -36,6 +38,7 @@ DEVERR_SEGMENTS = 0x4
 DEVERR_LENGTH = 0x8
 DEVERR_SHARED = 0x10
 DEVERR_POLICY = 0x20
+DEVERR_TICKET = 0x40
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libspicy.so")
@@ -131,6 +134,38 @@ def _stream(stream) -> int | None:
     return int(stream) or None
 
 
+_TORCH_DTYPE = {SPICY_BF16: torch.bfloat16, SPICY_F32: torch.float32}
+
+
+def _check(t, name: str, dtype=None, shape=None, ndim=None, device=None, optional: bool = False):
+    """Raise ValueError unless t is a contiguous tensor of the given dtype,
+    shape (None entries match anything) or dimension count, on `device`.
+    Runs before anything reaches the C ABI: a wrong dtype, layout or size
+    would otherwise be read or written past the tensor's bytes."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name}: required")
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name}: {t.dim()} dimensions, expected {ndim}")
+    if shape is not None:
+        if t.dim() != len(shape) or any(w is not None and int(n) != int(w) for n, w in zip(t.shape, shape)):
+            raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple('*' if w is None else w for w in shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name}: on {t.device}, the cache is on {device}")
+
+
+def _check_count(value: int, limit: int, name: str):
+    if value < 0 or value > limit:
+        raise ValueError(f"{name}: {value} outside [0, {limit}]")
+
+
 @dataclass
 class PagedCache:
     """Caller-owned paged compressed cache (device tensors in the library's layout).
@@ -178,6 +213,18 @@ class PagedCache:
             return SPICY_F32
         raise ValueError(f"unsupported cache dtype {self.k.dtype}")
 
+    def check(self):
+        """The pool tensors' dtypes, shapes and devices agree."""
+        dt = _TORCH_DTYPE[self.dtype_code]
+        P, H, d = self.num_pages, self.num_kv_heads, self.head_dim
+        dev = self.k.device
+        _check(self.k, "cache.k", dt, (P, H, d // 8, PAGE_SIZE, 8))
+        _check(self.v, "cache.v", dt, (P, H, d // 8, PAGE_SIZE, 8), device=dev)
+        _check(self.ab, "cache.ab", dt, (P, H, PAGE_SIZE, 2), device=dev)
+        _check(self.meta, "cache.meta", torch.int32, (P, H, PAGE_SIZE, 4), device=dev, optional=True)
+        _check(self.s2, "cache.s2", dt, (P, H, d // 8, PAGE_SIZE, 8), device=dev, optional=True)
+        return dev
+
     def struct(self) -> _Cache:
         return _Cache(self.dtype_code, self.num_kv_heads, self.head_dim, self.num_pages,
                       _ptr(self.k), _ptr(self.v), _ptr(self.ab), _ptr(self.meta), _ptr(self.s2))
@@ -205,10 +252,10 @@ def spicy_coarsen(cache: PagedCache, k_pre, v, seq_offsets, pos_base, seg_offset
                   B: int | None = None, max_pages_per_seq: int | None = None) -> None:
     """spicy_coarsen through the C ABI (see include/spicy.h)."""
     L = load_library()
-    B = int(seq_offsets.shape[0] - 1) if B is None else B
-    n_seg = int(seg_offsets.shape[0] - 1) if n_seg is None else n_seg
-    total_tokens = int(k_pre.shape[0]) if total_tokens is None else total_tokens
-    max_pages = int(page_table.shape[-1]) if max_pages_per_seq is None else max_pages_per_seq
+    B, n_seg, total_tokens, max_pages = _check_coarsen(cache, k_pre, v, seq_offsets, pos_base, seg_offsets,
+                                                       seq_seg_ptr, protected_mask, page_table, entry_start,
+                                                       lengths_out, workspace, total_tokens, n_seg, B,
+                                                       max_pages_per_seq)
     st = cache.struct()
     ws_bytes = workspace.numel() * workspace.element_size() if isinstance(workspace, torch.Tensor) else 0
     rc = L.spicy_coarsen(ctypes.byref(st), _ptr(k_pre), _ptr(v), total_tokens, _ptr(seq_offsets),
@@ -217,6 +264,64 @@ def spicy_coarsen(cache: PagedCache, k_pre, v, seq_offsets, pos_base, seg_offset
                          _ptr(lengths_out), _ptr(workspace), ws_bytes, _stream(stream))
     if rc != 0:
         raise SpicyError(rc, "spicy_coarsen")
+
+
+def _check_coarsen(cache, k_pre, v, seq_offsets, pos_base, seg_offsets, seq_seg_ptr, protected_mask, page_table,
+                   entry_start, lengths_out, workspace, total_tokens, n_seg, B, max_pages_per_seq):
+    """Validate spicy_coarsen's tensors; returns (B, n_seg, total_tokens, max_pages)."""
+    dev = cache.check()
+    dt = _TORCH_DTYPE[cache.dtype_code]
+    H, d = cache.num_kv_heads, cache.head_dim
+    _check(k_pre, "k_pre", dt, (None, H, d), device=dev)
+    _check(v, "v", dt, tuple(k_pre.shape), device=dev)
+    _check(protected_mask, "protected_mask", torch.uint8, (k_pre.shape[0], H), device=dev)
+    _check(seq_offsets, "seq_offsets", torch.int32, ndim=1, device=dev)
+    _check(seg_offsets, "seg_offsets", torch.int32, ndim=1, device=dev)
+    _check(seq_seg_ptr, "seq_seg_ptr", torch.int32, tuple(seq_offsets.shape), device=dev)
+    _check(page_table, "page_table", torch.int32, ndim=2, device=dev)
+    _check(workspace, "workspace", ndim=1, device=dev)
+    nb = int(seq_offsets.shape[0]) - 1
+    B = nb if B is None else B
+    _check_count(B, max(nb, 0), "B")
+    _check(pos_base, "pos_base", torch.int32, (None,), device=dev, optional=True)
+    _check(entry_start, "entry_start", torch.int32, (None,), device=dev, optional=True)
+    _check(lengths_out, "lengths_out", torch.int32, (None,), device=dev)
+    for t, nm in ((pos_base, "pos_base"), (entry_start, "entry_start"), (lengths_out, "lengths_out")):
+        if t is not None and t.shape[0] < B:
+            raise ValueError(f"{nm}: {t.shape[0]} entries for {B} sequences")
+    if page_table.shape[0] < B:
+        raise ValueError(f"page_table: {page_table.shape[0]} rows for {B} sequences")
+    n_seg = int(seg_offsets.shape[0]) - 1 if n_seg is None else n_seg
+    _check_count(n_seg, int(seg_offsets.shape[0]) - 1, "n_seg")
+    total_tokens = int(k_pre.shape[0]) if total_tokens is None else total_tokens
+    _check_count(total_tokens, int(k_pre.shape[0]), "total_tokens")
+    max_pages = int(page_table.shape[1]) if max_pages_per_seq is None else max_pages_per_seq
+    _check_count(max_pages, int(page_table.shape[1]), "max_pages_per_seq")
+    return B, n_seg, total_tokens, max_pages
+
+
+def _check_decode(cache, q, page_table, lengths, o, lse, workspace, n_q, B, max_pages_per_seq):
+    """Validate a decode call's tensors: q [B, (n_q,) H_q, d] in the cache's
+    dtype, o float32 of q's shape, lse float32 [B, (n_q,) H_q]; returns
+    (B, H_q, max_pages)."""
+    dev = cache.check()
+    dt = _TORCH_DTYPE[cache.dtype_code]
+    d = cache.head_dim
+    lead = (None, n_q) if n_q is not None else (None,)
+    _check(q, "q", dt, lead + (None, d), device=dev)
+    _check(o, "o", torch.float32, tuple(q.shape), device=dev)
+    _check(lse, "lse", torch.float32, tuple(q.shape[:-1]), device=dev)
+    _check(page_table, "page_table", torch.int32, ndim=2, device=dev)
+    _check(lengths, "lengths", torch.int32, (None,), device=dev)
+    _check(workspace, "workspace", ndim=1, device=dev)
+    nb = int(q.shape[0])
+    B = nb if B is None else B
+    _check_count(B, nb, "B")
+    if page_table.shape[0] < B or lengths.shape[0] < B:
+        raise ValueError(f"page_table / lengths: fewer rows than the {B} sequences")
+    max_pages = int(page_table.shape[1]) if max_pages_per_seq is None else max_pages_per_seq
+    _check_count(max_pages, int(page_table.shape[1]), "max_pages_per_seq")
+    return B, int(q.shape[-2]), max_pages
 
 
 def spicy_decode_plan(B: int, num_q_heads: int, num_kv_heads: int, max_pages_per_seq: int,
@@ -241,8 +346,17 @@ def spicy_merge_level(cache: PagedCache, rope_base: float, page_table, entry_beg
     """spicy_merge_level through the C ABI (see include/spicy.h): one level of
     the dyadic merge over entries [entry_begin[b], entry_end[b]) in place."""
     L = load_library()
+    dev = cache.check()
+    _check(page_table, "page_table", torch.int32, ndim=2, device=dev)
+    _check(entry_begin, "entry_begin", torch.int32, (None,), device=dev)
+    _check(entry_end, "entry_end", torch.int32, tuple(entry_begin.shape), device=dev)
+    _check(workspace, "workspace", ndim=1, device=dev)
     B = int(entry_begin.shape[0]) if B is None else B
-    max_pages = int(page_table.shape[-1]) if max_pages_per_seq is None else max_pages_per_seq
+    _check_count(B, int(entry_begin.shape[0]), "B")
+    if page_table.shape[0] < B:
+        raise ValueError(f"page_table: {page_table.shape[0]} rows for {B} sequences")
+    max_pages = int(page_table.shape[1]) if max_pages_per_seq is None else max_pages_per_seq
+    _check_count(max_pages, int(page_table.shape[1]), "max_pages_per_seq")
     st = cache.struct()
     ws_bytes = workspace.numel() * workspace.element_size() if isinstance(workspace, torch.Tensor) else 0
     rc = L.spicy_merge_level(ctypes.byref(st), B, float(rope_base), _ptr(page_table), max_pages, _ptr(entry_begin),
@@ -258,10 +372,13 @@ def spicy_coarsen_weighted(cache: PagedCache, k_pre, v, seq_offsets, pos_base, s
     """spicy_coarsen_weighted through the C ABI (see include/spicy.h);
     token_weight: int64 device tensor [total_tokens]."""
     L = load_library()
-    B = int(seq_offsets.shape[0] - 1) if B is None else B
-    n_seg = int(seg_offsets.shape[0] - 1) if n_seg is None else n_seg
-    total_tokens = int(k_pre.shape[0]) if total_tokens is None else total_tokens
-    max_pages = int(page_table.shape[-1]) if max_pages_per_seq is None else max_pages_per_seq
+    B, n_seg, total_tokens, max_pages = _check_coarsen(cache, k_pre, v, seq_offsets, pos_base, seg_offsets,
+                                                       seq_seg_ptr, protected_mask, page_table, entry_start,
+                                                       lengths_out, workspace, total_tokens, n_seg, B,
+                                                       max_pages_per_seq)
+    _check(token_weight, "token_weight", torch.int64, (None,), device=k_pre.device)
+    if token_weight.shape[0] < total_tokens:
+        raise ValueError(f"token_weight: {token_weight.shape[0]} weights for {total_tokens} tokens")
     st = cache.struct()
     ws_bytes = workspace.numel() * workspace.element_size() if isinstance(workspace, torch.Tensor) else 0
     rc = L.spicy_coarsen_weighted(ctypes.byref(st), _ptr(k_pre), _ptr(v), total_tokens, _ptr(seq_offsets),
@@ -278,9 +395,9 @@ def spicy_decode_attn(cache: PagedCache, q, page_table, lengths, o, lse, workspa
                       num_q_heads: int | None = None, max_pages_per_seq: int | None = None) -> None:
     """spicy_decode_attn through the C ABI (see include/spicy.h)."""
     L = load_library()
-    B = int(q.shape[0]) if B is None else B
-    H_q = int(q.shape[1]) if num_q_heads is None else num_q_heads
-    max_pages = int(page_table.shape[-1]) if max_pages_per_seq is None else max_pages_per_seq
+    B, H_q, max_pages = _check_decode(cache, q, page_table, lengths, o, lse, workspace, None, B, max_pages_per_seq)
+    if num_q_heads is not None and num_q_heads != H_q:
+        raise ValueError(f"num_q_heads {num_q_heads} differs from q's {H_q}")
     st = cache.struct()
     ws_bytes = workspace.numel() * workspace.element_size() if isinstance(workspace, torch.Tensor) else 0
     rc = L.spicy_decode_attn(ctypes.byref(st), _ptr(q), H_q, _ptr(page_table), max_pages, _ptr(lengths), B,
@@ -302,9 +419,9 @@ def spicy_decode_attn_shared(cache: PagedCache, q, page_table, lengths, shared_p
                              num_q_heads: int | None = None, max_pages_per_seq: int | None = None) -> None:
     """spicy_decode_attn_shared through the C ABI (see include/spicy.h)."""
     L = load_library()
-    B = int(q.shape[0]) if B is None else B
-    H_q = int(q.shape[1]) if num_q_heads is None else num_q_heads
-    max_pages = int(page_table.shape[-1]) if max_pages_per_seq is None else max_pages_per_seq
+    B, H_q, max_pages = _check_decode(cache, q, page_table, lengths, o, lse, workspace, None, B, max_pages_per_seq)
+    if num_q_heads is not None and num_q_heads != H_q:
+        raise ValueError(f"num_q_heads {num_q_heads} differs from q's {H_q}")
     st = cache.struct()
     ws_bytes = workspace.numel() * workspace.element_size() if isinstance(workspace, torch.Tensor) else 0
     rc = L.spicy_decode_attn_shared(ctypes.byref(st), _ptr(q), H_q, _ptr(page_table), max_pages,
@@ -328,9 +445,10 @@ def spicy_decode_attn_multi(cache: PagedCache, q, page_table, lengths, shared_pr
     """spicy_decode_attn_multi through the C ABI (see include/spicy.h):
     q [B, n_q, H_q, d] -> o [B, n_q, H_q, d], lse [B, n_q, H_q]."""
     L = load_library()
-    B = int(q.shape[0]) if B is None else B
-    n_q, H_q = int(q.shape[1]), int(q.shape[2])
-    max_pages = int(page_table.shape[-1]) if max_pages_per_seq is None else max_pages_per_seq
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError("q: expected a [B, n_q, H_q, d] tensor")
+    n_q = int(q.shape[1])
+    B, H_q, max_pages = _check_decode(cache, q, page_table, lengths, o, lse, workspace, n_q, B, max_pages_per_seq)
     st = cache.struct()
     ws_bytes = workspace.numel() * workspace.element_size() if isinstance(workspace, torch.Tensor) else 0
     rc = L.spicy_decode_attn_multi(ctypes.byref(st), _ptr(q), n_q, H_q, _ptr(page_table), max_pages,
@@ -350,10 +468,23 @@ def spicy_policy(k_pre, v, seq_offsets, proj_ptr, proj_idx, n_segments: int, n_l
     """spicy_policy through the C ABI (see include/spicy.h): segment slots and
     protection mask of a chunk (k_pre, v: [total_tokens, H, d] bf16)."""
     L = load_library()
-    B = int(seq_offsets.shape[0] - 1) if B is None else B
-    total_tokens = int(k_pre.shape[0]) if total_tokens is None else total_tokens
+    _check(k_pre, "k_pre", torch.bfloat16, ndim=3)
+    dev = k_pre.device
+    _check(v, "v", torch.bfloat16, tuple(k_pre.shape), device=dev)
     H, d = int(k_pre.shape[1]), int(k_pre.shape[2])
-    dtype = SPICY_BF16 if k_pre.dtype == torch.bfloat16 else SPICY_F32
+    _check(seq_offsets, "seq_offsets", torch.int32, ndim=1, device=dev)
+    _check(proj_ptr, "proj_ptr", torch.int32, ndim=1, device=dev)
+    _check(proj_idx, "proj_idx", torch.int32, ndim=1, device=dev)
+    _check(workspace, "workspace", ndim=1, device=dev)
+    nb = int(seq_offsets.shape[0]) - 1
+    B = nb if B is None else B
+    _check_count(B, max(nb, 0), "B")
+    _check(seg_offsets, "seg_offsets", torch.int32, (B * int(n_segments) + 1,), device=dev)
+    _check(seq_seg_ptr, "seq_seg_ptr", torch.int32, (B + 1,), device=dev)
+    _check(protected_mask, "protected_mask", torch.uint8, (k_pre.shape[0], H), device=dev)
+    total_tokens = int(k_pre.shape[0]) if total_tokens is None else total_tokens
+    _check_count(total_tokens, int(k_pre.shape[0]), "total_tokens")
+    dtype = SPICY_BF16
     ws_bytes = workspace.numel() * workspace.element_size() if isinstance(workspace, torch.Tensor) else 0
     rc = L.spicy_policy(_ptr(k_pre), _ptr(v), total_tokens, H, d, dtype, _ptr(seq_offsets), B,
                         _ptr(proj_ptr), _ptr(proj_idx), int(proj_ptr.shape[0] - 1), int(proj_idx.numel()),

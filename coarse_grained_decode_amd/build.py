@@ -16,6 +16,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libspicy.so")
+# the benchmark's streaming-read reference, a library of its own
+PROBE_LIB = os.path.join(PKG, "libspicy_probe.so")
+PROBE_SOURCE = "readprobe.hip"
 OBJDIR = os.path.join(PKG, "_build")
 SOURCES = ["api.hip", "coarsen.hip", "decode.hip", "policy.hip", "merge.hip"]
 # (source, object, extra flags): coarsen.hip builds once per (element type,
@@ -59,6 +62,8 @@ def build(verbose: bool = True, jobs: int | None = None) -> str:
     def run(c):
         return subprocess.run(c, capture_output=True, text=True)
 
+    probe_obj = os.path.join(OBJDIR, "readprobe.o")
+    cmds.append(compile_command(PROBE_SOURCE, probe_obj))
     jobs = jobs or min(len(cmds), max(1, os.cpu_count() or 1))
     with ThreadPoolExecutor(jobs) as ex:
         results = list(ex.map(run, cmds))
@@ -68,12 +73,13 @@ def build(verbose: bool = True, jobs: int | None = None) -> str:
             print(err, file=sys.stderr, flush=True)
         if r.returncode != 0:
             raise subprocess.CalledProcessError(r.returncode, c)
-    tmp = LIB + ".tmp"
-    lcmd = link_command(objs, tmp)
-    if verbose:
-        print(" ".join(lcmd), flush=True)
-    subprocess.run(lcmd, check=True)
-    os.replace(tmp, LIB)
+    for out, ob in ((LIB, objs), (PROBE_LIB, [probe_obj])):
+        tmp = out + ".tmp"
+        lcmd = link_command(ob, tmp)
+        if verbose:
+            print(" ".join(lcmd), flush=True)
+        subprocess.run(lcmd, check=True)
+        os.replace(tmp, out)
     return LIB
 
 
@@ -82,6 +88,8 @@ def stale() -> bool:
         return True
     t = os.path.getmtime(LIB)
     deps = [os.path.join(CSRC, f) for f in SOURCES + HEADERS] + [os.path.join(ROOT, "include", "spicy.h")]
+    if not os.path.exists(PROBE_LIB) or os.path.getmtime(os.path.join(CSRC, PROBE_SOURCE)) > os.path.getmtime(PROBE_LIB):
+        return True
     return any(os.path.getmtime(p) > t for p in deps)
 
 

@@ -566,8 +566,11 @@ __device__ __forceinline__ void stream_segment(const CoarsenArgs& a, const Lanes
     // masked sums of the F-tokens, double-buffered: block B (kRing tokens)
     // is in flight while block A is accumulated and vice versa.  Rows are read
     // through buffer resources spanning the segment (rebased every kWindow
-    // tokens): the per-token offset is a scalar, and reads past the segment's
-    // end return zeros, which add nothing to the sums.  Positions are summed
+    // tokens), the whole offset in the vector offset, which the hardware
+    // range-checks: reads past the segment's end return zeros and touch no
+    // memory.  A token that is not taken (protected, or past the end)
+    // contributes through selects, not products with a zero weight, so
+    // whatever its bytes hold (NaN, inf) adds nothing.  Positions are summed
     // relative to the segment's first token.
     constexpr int RING = kRing;
     double sk[8], sq[8], sv[8], sx[8], skw[8], svw[8];
@@ -596,14 +599,14 @@ __device__ __forceinline__ void stream_segment(const CoarsenArgs& a, const Lanes
         auto fetch = [&](Block& X, int32_t u0) {
 #pragma unroll
             for (int u = 0; u < RING; ++u) {
-                const int so = (u0 + u) * static_cast<int>(tok_bytes);
-                Row8<T>::load_buf(X.k[u], rk, lane_off, so);
-                Row8<T>::load_buf(X.v[u], rv, lane_off, so);
-                X.mk[u] = __builtin_amdgcn_raw_buffer_load_b8(rm, L.hh, (u0 + u) * H, 0);
+                const uint32_t to = static_cast<uint32_t>(u0 + u) * tok_bytes;
+                Row8<T>::load_buf(X.k[u], rk, lane_off + to, 0);
+                Row8<T>::load_buf(X.v[u], rv, lane_off + to, 0);
+                X.mk[u] = __builtin_amdgcn_raw_buffer_load_b8(rm, L.hh + (u0 + u) * H, 0, 0);
                 if constexpr (WEIGHTED) {
                     // the token's weight, the same for every lane (0 past the window)
                     typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-                    const u32x2 wv = __builtin_amdgcn_raw_buffer_load_b64(rw, 0, (u0 + u) * 8, 0);
+                    const u32x2 wv = __builtin_amdgcn_raw_buffer_load_b64(rw, (u0 + u) * 8, 0, 0);
                     X.wt[u] = static_cast<int64_t>((static_cast<uint64_t>(wv[1]) << 32) | wv[0]);
                 }
             }
@@ -613,7 +616,6 @@ __device__ __forceinline__ void stream_segment(const CoarsenArgs& a, const Lanes
 #pragma unroll
             for (int u = 0; u < RING; ++u) {
                 const bool take = (u < nvalid) && !X.mk[u];
-                const double w = take ? 1.0 : 0.0;
                 double tw = 0.0;
                 if constexpr (WEIGHTED) {
                     tw = take ? static_cast<double>(X.wt[u]) : 0.0;
@@ -623,16 +625,15 @@ __device__ __forceinline__ void stream_segment(const CoarsenArgs& a, const Lanes
                 if constexpr (DIAG) kp = X.k[u].template lane_xor<Lanes<T, D>::PARTNER>();
 #pragma unroll
                 for (int r = 0; r < 8; ++r) {
-                    const double x = X.k[u].f64(r);
-                    const double xw = x * w;
-                    const double vx = X.v[u].f64(r);
+                    const double xw = take ? X.k[u].f64(r) : 0.0;
+                    const double vw = take ? X.v[u].f64(r) : 0.0;
                     sk[r] += xw;
-                    sq[r] = fma(xw, x, sq[r]);
-                    sv[r] = fma(vx, w, sv[r]);
-                    if constexpr (DIAG) sx[r] = fma(xw, kp.f64(r), sx[r]);
+                    sq[r] = fma(xw, xw, sq[r]);
+                    sv[r] += vw;
+                    if constexpr (DIAG) sx[r] = fma(xw, take ? kp.f64(r) : 0.0, sx[r]);
                     if constexpr (WEIGHTED) {
-                        skw[r] = fma(x, tw, skw[r]);
-                        svw[r] = fma(vx, tw, svw[r]);
+                        skw[r] = fma(xw, tw, skw[r]);
+                        svw[r] = fma(vw, tw, svw[r]);
                     }
                 }
                 m += take ? 1 : 0;
@@ -739,7 +740,7 @@ __global__ __launch_bounds__(256, 2) void coarsen_main_kernel(CoarsenArgs a) {
 // (x, b) and their 16-lane groups (8 at d = 64).  The sequence's entries form
 // one index space walked with a grid stride, so each group pays one chain of
 // dependent reads per entry whatever its kind:
-//   [0, n_mac)              the staged macro-nodes, unit (segment, head), at
+//   [0, n_mac)              the staged macro-nodes, unit (head, segment), at
 //                           the entry the plan gave them;
 //   [n_mac, n_mac + n_cp)   the C-point items {token, entry, head} the plan
 //                           listed, stored exact (value bits copied, key
@@ -748,11 +749,16 @@ __global__ __launch_bounds__(256, 2) void coarsen_main_kernel(CoarsenArgs a) {
 //   [.., + n_null)          the null entries: each head from its own end up
 //                           to the end of the sequence's last page
 //                           (k = v = 0, alpha = -inf, beta = 0).
+// u runs head-major (the segments of head 0, then head 1, ...): the groups of
+// a wavefront take consecutive segments of one head, whose entries are mostly
+// consecutive slots, so their 16-byte pieces of each 8-dim group of the page
+// land side by side.
 template <typename T, int D>
-__device__ __forceinline__ void place_macro(const CoarsenArgs& a, int b, int32_t s0, int64_t u, int d0, int j) {
+__device__ __forceinline__ void place_macro(const CoarsenArgs& a, int b, int32_t s0, int32_t nseg, int64_t u, int d0,
+                                            int j) {
     const int H = a.cache.H;
-    const int32_t sg = s0 + static_cast<int32_t>(u / H);
-    const int h = static_cast<int>(u % H);
+    const int32_t sg = s0 + static_cast<int32_t>(u % nseg);
+    const int h = static_cast<int>(u / nseg);
     const int64_t idx = static_cast<int64_t>(sg) * H + h;
     // every read of the unit is independent: issue them together
     const int32_t owner = a.seg_desc[sg].x;
@@ -908,7 +914,7 @@ __global__ __launch_bounds__(256) void coarsen_cpoint_kernel(CoarsenArgs a) {
     const int64_t stride = static_cast<int64_t>(gridDim.x) * ngrp;
     for (int64_t u = static_cast<int64_t>(blockIdx.x) * ngrp + grp; u < n_all; u += stride) {
         if (u < n_mac) {
-            place_macro<T, D>(a, b, s0, u, d0, j);
+            place_macro<T, D>(a, b, s0, s1 - s0, u, d0, j);
         } else if (u < n_mac + n_cp) {
             place_cpoint<T, D>(a, b, items[u - n_mac], t0, t1, pos_off, theta, d0, j);
         } else {

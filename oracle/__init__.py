@@ -69,6 +69,9 @@ def lib():
             L.oracle_merge_level.restype = ctypes.c_int
             L.oracle_merge_level.argtypes = [ctypes.c_int, i32, i32, P, P, P, P, P, i32, P, i32, P, P, i32,
                                              ctypes.c_double, i32, i32]
+            L.oracle_decode_heads.restype = ctypes.c_int
+            L.oracle_decode_heads.argtypes = [ctypes.c_int, ctypes.c_int, i32, i32, i32, P, P, P, P, P, i32,
+                                              P, i32, P, i32, P, P, i32, i32, i32, i32]
             L.oracle_decode_diag.restype = ctypes.c_int
             L.oracle_decode_diag.argtypes = [ctypes.c_int, ctypes.c_int, i32, i32, i32, P, P, P, P, P, i32,
                                              P, i32, P, i32, P, P, i32, i32]
@@ -100,7 +103,13 @@ def _chunks(B, threads):
 
 
 def default_threads() -> int:
-    return max(1, min(16, os.cpu_count() or 1))
+    """Host threads: the process's affinity set, capped by OMP_NUM_THREADS
+    when the environment sets it (each GPU process's share of the host)."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
 
 
 def chunk_width(d: int) -> int:
@@ -183,8 +192,9 @@ def coarsen(call, cache: Cache, in_dtype: str | None = None, threads: int | None
 
 def decode(q: np.ndarray, q_dtype: str, cache: Cache, H_q: int, page_table: np.ndarray,
            lengths: np.ndarray, threads: int | None = None):
-    """Run oracle_decode (oracle_decode_diag on a cache with the diagonal
-    sidecar); returns (o [B, H_q, d] float64, lse [B, H_q] float64)."""
+    """Run the oracle decode (with the diagonal closure on a cache with the
+    diagonal sidecar), one (sequence, KV head) per work item over `threads`
+    host threads; returns (o [B, H_q, d] float64, lse [B, H_q] float64)."""
     L = lib()
     q = np.ascontiguousarray(q)
     B = int(q.shape[0])
@@ -194,22 +204,24 @@ def decode(q: np.ndarray, q_dtype: str, cache: Cache, H_q: int, page_table: np.n
     table = np.ascontiguousarray(page_table, dtype=np.int32)
     lens = np.ascontiguousarray(lengths, dtype=np.int32)
     rcs = []
+    G = H_q // cache.H_kv if cache.H_kv > 0 and H_q % cache.H_kv == 0 else H_q
 
-    def run(rng):
-        b0, b1 = rng
-        head = (DT[q_dtype], DT[cache.store], H_q, cache.H_kv, d, _p(q), _p(cache.k), _p(cache.v), _p(cache.ab))
-        tail = (cache.num_pages, _p(table), int(table.shape[1]), _p(lens), B, _p(o), _p(lse), b0, b1)
-        if cache.s2 is None:
-            rcs.append(L.oracle_decode(*head, *tail))
-        else:
-            rcs.append(L.oracle_decode_diag(*head, _p(cache.s2), *tail))
+    def run(unit):
+        # one work item: the query heads of one KV head of one sequence
+        b, h = unit
+        rcs.append(L.oracle_decode_heads(DT[q_dtype], DT[cache.store], H_q, cache.H_kv, d, _p(q), _p(cache.k),
+                                         _p(cache.v), _p(cache.ab), _p(cache.s2), cache.num_pages, _p(table),
+                                         int(table.shape[1]), _p(lens), B, _p(o), _p(lse), b, b + 1,
+                                         h * G, (h + 1) * G))
 
-    chunks = _chunks(B, threads or default_threads())
-    if len(chunks) == 1:
-        run(chunks[0])
+    units = [(b, h) for b in range(B) for h in range(H_q // G)]
+    n = max(1, min(threads or default_threads(), len(units)))
+    if n == 1:
+        for u in units:
+            run(u)
     else:
-        with ThreadPoolExecutor(len(chunks)) as ex:
-            list(ex.map(run, chunks))
+        with ThreadPoolExecutor(n) as ex:
+            list(ex.map(run, units))
     if any(rc != 0 for rc in rcs):
         raise ValueError(f"oracle_decode failed: codes {sorted(set(rcs))}")
     return o, lse

@@ -520,11 +520,12 @@ static int decode_impl(int q_dtype, int dtype, int32_t H_q, int32_t H_kv, int32_
                   const int32_t* page_table, int32_t max_pages_per_seq,
                   const int32_t* lengths, int32_t B,
                   double* o, double* lse,
-                  int32_t b_begin, int32_t b_end, const void* s2_pool) {
+                  int32_t b_begin, int32_t b_end, int32_t g_begin, int32_t g_end, const void* s2_pool) {
     if (dtype < 0 || dtype > 2 || q_dtype < 0 || q_dtype > 2) return 1;
     if (H_q <= 0 || H_kv <= 0 || !head_dim_ok(d) || (H_q % H_kv) != 0) return 1;
     if (!q || !k_pool || !v_pool || !ab_pool || !page_table || !lengths || !o || !lse) return 1;
     if (b_begin < 0 || b_end > B || b_begin > b_end) return 1;
+    if (g_begin < 0 || g_end > H_q || g_begin > g_end) return 1;
     int32_t G = H_q / H_kv;
     for (int32_t b = b_begin; b < b_end; ++b) {
         int32_t L = lengths[b];
@@ -547,7 +548,7 @@ static int decode_impl(int q_dtype, int dtype, int32_t H_q, int32_t H_kv, int32_
         }
         if (!s) return 1;
         const int32_t* row = page_table + (size_t)b * (size_t)max_pages_per_seq;
-        for (int32_t g = 0; g < H_q; ++g) {
+        for (int32_t g = g_begin; g < g_end; ++g) {
             int32_t h = g / G;
             size_t qo = ((size_t)b * (size_t)H_q + (size_t)g) * (size_t)d;
             double qn2 = 0.0;
@@ -612,7 +613,22 @@ int oracle_decode(int q_dtype, int dtype, int32_t H_q, int32_t H_kv, int32_t d,
                   double* o, double* lse,
                   int32_t b_begin, int32_t b_end) {
     return decode_impl(q_dtype, dtype, H_q, H_kv, d, q, k_pool, v_pool, ab_pool, num_pages, page_table,
-                       max_pages_per_seq, lengths, B, o, lse, b_begin, b_end, NULL);
+                       max_pages_per_seq, lengths, B, o, lse, b_begin, b_end, 0, H_q, NULL);
+}
+
+/* oracle_decode (s2_pool NULL) or oracle_decode_diag for the query heads
+ * [g_begin, g_end) of sequences [b_begin, b_end) only: a smaller work item of
+ * the same computation (the other rows of o and lse are untouched). */
+int oracle_decode_heads(int q_dtype, int dtype, int32_t H_q, int32_t H_kv, int32_t d,
+                        const void* q,
+                        const void* k_pool, const void* v_pool, const void* ab_pool, const void* s2_pool,
+                        int32_t num_pages,
+                        const int32_t* page_table, int32_t max_pages_per_seq,
+                        const int32_t* lengths, int32_t B,
+                        double* o, double* lse,
+                        int32_t b_begin, int32_t b_end, int32_t g_begin, int32_t g_end) {
+    return decode_impl(q_dtype, dtype, H_q, H_kv, d, q, k_pool, v_pool, ab_pool, num_pages, page_table,
+                       max_pages_per_seq, lengths, B, o, lse, b_begin, b_end, g_begin, g_end, s2_pool);
 }
 
 /* The diagonal closure at decode: the logit's closure term is
@@ -629,7 +645,7 @@ int oracle_decode_diag(int q_dtype, int dtype, int32_t H_q, int32_t H_kv, int32_
                        int32_t b_begin, int32_t b_end) {
     if (!s2_pool) return 1;
     return decode_impl(q_dtype, dtype, H_q, H_kv, d, q, k_pool, v_pool, ab_pool, num_pages, page_table,
-                       max_pages_per_seq, lengths, B, o, lse, b_begin, b_end, s2_pool);
+                       max_pages_per_seq, lengths, B, o, lse, b_begin, b_end, 0, H_q, s2_pool);
 }
 
 /* ------------------------------------------------------------------------

@@ -102,6 +102,14 @@ int oracle_merge_level(int dtype, int32_t H_kv, int32_t d,
                        int32_t num_pages, const int32_t* page_table, int32_t max_pages_per_seq,
                        const int32_t* entry_begin, const int32_t* entry_end, int32_t B, double rope_base,
                        int32_t b_begin, int32_t b_end);
+int oracle_decode_heads(int q_dtype, int dtype, int32_t H_q, int32_t H_kv, int32_t d,
+                        const void* q,
+                        const void* k_pool, const void* v_pool, const void* ab_pool, const void* s2_pool,
+                        int32_t num_pages,
+                        const int32_t* page_table, int32_t max_pages_per_seq,
+                        const int32_t* lengths, int32_t B,
+                        double* o, double* lse,
+                        int32_t b_begin, int32_t b_end, int32_t g_begin, int32_t g_end);
 int oracle_decode_diag(int q_dtype, int dtype, int32_t H_q, int32_t H_kv, int32_t d,
                        const void* q,
                        const void* k_pool, const void* v_pool, const void* ab_pool, const void* s2_pool,

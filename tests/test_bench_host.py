@@ -54,9 +54,62 @@ def test_traffic_table_follows_the_sources(tmp_path, monkeypatch):
     dig = bench.kernel_digest("decode_mfma_kernel")
     (prof / "traffic_w.txt").write_text(
         f"traffic_bytes decode_mfma_kernel 123 {dig}\n"
-        f"traffic_bytes combine_kernel 456 {'0' * 64}\n")
+        f"traffic_bytes merge_pair_kernel 456 {'0' * 64}\n")
     digests = {k: bench.kernel_digest(k) for k in bench.KERNEL_SOURCE}   # of the real sources
     monkeypatch.setattr(bench, "kernel_digest", lambda k: digests[k])
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     t = bench.measured_traffic("w")
     assert t == {"decode_mfma_kernel": 123.0}
+
+
+def test_host_description_reports_threads_within_affinity(monkeypatch):
+    monkeypatch.setenv("OMP_NUM_THREADS", "3")
+    h = bench.host_description()
+    assert h["nproc"] >= h["affinity"] >= 1
+    assert h["threads"] == min(3, h["affinity"])
+    monkeypatch.delenv("OMP_NUM_THREADS")
+    assert bench.host_description()["threads"] == h["affinity"]
+
+
+def _write_csv(path, header, rows):
+    import csv
+    path.parent.mkdir(parents=True, exist_ok=True)
+    with open(path, "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(header)
+        w.writerows(rows)
+
+
+def test_profile_summary_from_rocprof_csv(tmp_path, monkeypatch):
+    """The summary's durations, calibrated traffic and digest lines, from
+    hand-made rocprofv3 CSV files (kernel trace and counter collection)."""
+    out = tmp_path / "out"
+    th = ["Kind", "Kernel_Name", "Start_Timestamp", "End_Timestamp"]
+    name = "void spicy::decode_mfma_kernel<128, 3, false, 1, 4>(spicy::DecodeArgs)"
+    _write_csv(out / "trace" / "run_kernel_trace.csv", th,
+               [["KERNEL_DISPATCH", name, 1000 * i, 1000 * i + 10000 + 1000 * (i % 2)] for i in range(4)])
+    ch = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    _write_csv(out / "FETCH_SIZE" / "run_counter_collection.csv", ch,
+               [[i, name, "FETCH_SIZE", 100.0] for i in range(3)])
+    _write_csv(out / "WRITE_SIZE" / "run_counter_collection.csv", ch,
+               [[i, name, "WRITE_SIZE", 10.0] for i in range(3)])
+    neg = "void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda>(int)"
+    _write_csv(out / "copy_FETCH_SIZE" / "run_counter_collection.csv", ch, [[0, neg, "FETCH_SIZE", 262144.0]])
+    _write_csv(out / "copy_WRITE_SIZE" / "run_counter_collection.csv", ch, [[0, neg, "WRITE_SIZE", 524288.0]])
+    _write_csv(out / "pmc_occupancy" / "run_counter_collection.csv", ch,
+               [[i, name, "SQ_WAVES", 2048.0] for i in range(3)])
+    (tmp_path / "profiles").mkdir()
+    digests = {k: bench.kernel_digest(k) for k in bench.KERNEL_SOURCE}   # of the real sources
+    monkeypatch.setattr(bench, "kernel_digest", lambda k: digests[k])
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    args = bench.parse(["--summarize-profile", str(out), "--profile-name", "t", "--profile-commands", "a; b",
+                        "--profile-last", "2"])
+    bench.summarize_profile(args)
+    text = (tmp_path / "profiles" / "t.txt").read_text()
+    assert "  a" in text and "  b" in text
+    row = [l for l in text.splitlines() if l.startswith("decode_mfma_kernel")][0].split()
+    assert row[1] == "4" and abs(float(row[2]) - 10.5) < 1e-9       # 4 dispatches of 10 or 11 us
+    # 512 MiB copy: FETCH 256 MiB -> factor 2, WRITE 512 MiB -> factor 1
+    b = 100 * 1024 * 2 + 10 * 1024 * 1
+    assert f"traffic_bytes decode_mfma_kernel {b} {digests['decode_mfma_kernel']}" in text
+    assert "SQ_WAVES" in text and "2048" in text

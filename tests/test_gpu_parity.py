@@ -175,6 +175,37 @@ def test_coarsen_layout_matches_oracle(name):
     assert stats["k_exact"] > 0.999 and stats["v_exact"] > 0.999
 
 
+@pytest.mark.parametrize("name", ["tiny_fp32", "qwen2_7b_small", "shared_prefix_small"])
+def test_coarsen_reads_nothing_past_its_inputs(name):
+    """k_pre, v and the mask sit at the front of allocations whose tail holds
+    NaN (keys, values) and 0 (mask: unprotected), so the batch's last segment
+    ends right before bytes that would poison any macro-node reading them (a
+    read past a segment's end); the cache must still match the oracle's."""
+    _need_gpu()
+    from coarse_grained_decode_amd.runner import DeviceWorkload
+    wl = CASES[name]()
+    ref_cache, ref_len, _, _ = oracle.run_workload(wl)
+    dw = DeviceWorkload.of(wl, DEV)
+    pad = 64
+    for c in dw.setup + ([dw.step] if dw.step else []):
+        T = c.k.shape[0]
+        for attr in ("k", "v"):
+            t = getattr(c, attr)
+            big = torch.full((T + pad,) + tuple(t.shape[1:]), float("nan"), dtype=t.dtype, device=DEV)
+            big[:T] = t
+            setattr(c, attr, big[:T])
+        big = torch.zeros((T + pad,) + tuple(c.mask.shape[1:]), dtype=c.mask.dtype, device=DEV)
+        big[:T] = c.mask
+        c.mask = big[:T]
+    dw.run_setup()
+    dw.run_step_coarsen()
+    torch.cuda.synchronize()
+    for c in dw.setup + ([dw.step] if dw.step else []):
+        assert int(c.ws[0].item()) == 0, "device error word set"
+    assert np.array_equal(dw.lengths.cpu().numpy(), ref_len)
+    compare_cache(dw, ref_cache, ref_len)
+
+
 @pytest.mark.parametrize("name", list(CASES))
 def test_decode_end_to_end_matches_oracle(name):
     _need_gpu()

@@ -443,3 +443,15 @@ def test_decode_multi_is_per_token_decode():
     for t in range(3):
         o1, l1 = oracle.decode(np.ascontiguousarray(c.q[:, t]), c.dtype, cache, 8, c.page_table, c.lengths)
         assert np.array_equal(o[:, t], o1) and np.array_equal(lse[:, t], l1)
+
+
+def test_decode_work_items_are_the_whole_decode():
+    """The decode split into (sequence, KV head) work items over threads gives
+    exactly the one-thread result (each row's arithmetic is the same)."""
+    c = W.random_decode_case(41, B=3, H_q=8, H_kv=2, d=64, q_tokens=1, dtype="bf16")
+    cache = oracle.Cache(c.dtype, c.k.shape[0], c.H_kv, c.d, fill=False)
+    cache.k[:] = c.k; cache.v[:] = c.v; cache.ab[:] = c.ab
+    q = np.ascontiguousarray(c.q[:, 0])
+    o1, l1 = oracle.decode(q, c.dtype, cache, 8, c.page_table, c.lengths, threads=1)
+    o4, l4 = oracle.decode(q, c.dtype, cache, 8, c.page_table, c.lengths, threads=4)
+    assert np.array_equal(o1, o4) and np.array_equal(l1, l4)
