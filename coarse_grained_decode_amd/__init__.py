@@ -21,6 +21,7 @@ __all__ = [
     "spicy_decode_attn_shared", "spicy_decode_shared_workspace_bytes",
     "spicy_policy", "spicy_policy_workspace_bytes",
     "spicy_decode_attn_multi", "spicy_decode_multi_workspace_bytes",
+    "spicy_decode_attn_multi_noalloc", "spicy_decode_noalloc_max_bytes",
     "spicy_coarsen_weighted", "spicy_merge_level", "spicy_merge_workspace_bytes", "spicy_decode_plan",
     "spicy_status_string", "library_path", "load_library", "workspace", "device_error",
     "SPICY_F32", "SPICY_BF16", "PAGE_SIZE", "WORKSPACE_HEADER",
@@ -103,6 +104,10 @@ def load_library():
     L.spicy_decode_multi_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32]
     L.spicy_decode_attn_multi.restype = ctypes.c_int
     L.spicy_decode_attn_multi.argtypes = [CP, P, i32, i32, P, i32, P, i32, i32, P, P, P, sz, i32, P]
+    L.spicy_decode_noalloc_max_bytes.restype = sz
+    L.spicy_decode_noalloc_max_bytes.argtypes = []
+    L.spicy_decode_attn_multi_noalloc.restype = ctypes.c_int
+    L.spicy_decode_attn_multi_noalloc.argtypes = [CP, P, i32, i32, P, i32, P, i32, i32, P, P, P, i32, P]
     L.spicy_policy_workspace_bytes.restype = sz
     L.spicy_policy_workspace_bytes.argtypes = [i32, i32]
     L.spicy_policy.restype = ctypes.c_int
@@ -456,6 +461,31 @@ def spicy_decode_attn_multi(cache: PagedCache, q, page_table, lengths, shared_pr
                                    _ptr(workspace), ws_bytes, int(num_splits), _stream(stream))
     if rc != 0:
         raise SpicyError(rc, "spicy_decode_attn_multi")
+
+
+def spicy_decode_noalloc_max_bytes() -> int:
+    return int(load_library().spicy_decode_noalloc_max_bytes())
+
+
+def spicy_decode_attn_multi_noalloc(cache: PagedCache, q, page_table, lengths, shared_prefix_pages: int, o, lse,
+                                    device_error=None, num_splits: int = 0, stream=None, *, B: int | None = None,
+                                    max_pages_per_seq: int | None = None) -> None:
+    """spicy_decode_attn_multi_noalloc through the C ABI (see include/spicy.h):
+    spicy_decode_attn_multi without a workspace; device_error: an int32
+    device tensor of one element (the sticky error word) or None."""
+    L = load_library()
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError("q: expected a [B, n_q, H_q, d] tensor")
+    n_q = int(q.shape[1])
+    ws_stub = torch.empty(1, dtype=torch.int32, device=q.device)
+    B, H_q, max_pages = _check_decode(cache, q, page_table, lengths, o, lse, ws_stub, n_q, B, max_pages_per_seq)
+    _check(device_error, "device_error", torch.int32, (None,), device=q.device, optional=True)
+    st = cache.struct()
+    rc = L.spicy_decode_attn_multi_noalloc(ctypes.byref(st), _ptr(q), n_q, H_q, _ptr(page_table), max_pages,
+                                           _ptr(lengths), B, int(shared_prefix_pages), _ptr(o), _ptr(lse),
+                                           _ptr(device_error), int(num_splits), _stream(stream))
+    if rc != 0:
+        raise SpicyError(rc, "spicy_decode_attn_multi_noalloc")
 
 
 def spicy_policy_workspace_bytes(total_tokens: int, num_kv_heads: int) -> int:

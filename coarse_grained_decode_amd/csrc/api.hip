@@ -1,11 +1,13 @@
 // C ABI of the gfx950 SPICY-KV library: host-side validation, workspace
-// carving and launches on the caller's stream.  No allocation, no
-// synchronisation, no global state.
+// carving and launches on the caller's stream.  No allocation and no
+// synchronisation; the only state is the per-device address of the
+// no-allocation decode's scratch array, looked up once per device.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "launch.h"
 #include "spicy.h"
@@ -310,11 +312,23 @@ spicy_status spicy_decode_attn_shared(const spicy_cache* cache, const void* q, i
                                    shared_prefix_pages, o, lse, workspace, workspace_bytes, num_splits, stream);
 }
 
-spicy_status spicy_decode_attn_multi(const spicy_cache* cache, const void* q, int32_t num_q_tokens,
-                                     int32_t num_q_heads, const int32_t* page_table, int32_t max_pages_per_seq,
-                                     const int32_t* lengths, int32_t B, int32_t shared_prefix_pages, float* o,
-                                     float* lse, void* workspace, size_t workspace_bytes, int32_t num_splits,
-                                     void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Where a decode call keeps its per-row state: the sticky error word (may be
+// null), the per-row tickets, and the partial (max, sum) pairs and outputs.
+struct DecodeScratch {
+    int32_t* err;
+    int32_t* ticket;
+    float* part_ml;
+    float* part_o;
+};
+
+// Host checks shared by the decode entry points (nothing launched on error).
+spicy_status check_decode(const spicy_cache* cache, const void* q, int32_t num_q_tokens, int32_t num_q_heads,
+                          const int32_t* page_table, int32_t max_pages_per_seq, const int32_t* lengths, int32_t B,
+                          int32_t shared_prefix_pages, const float* o, const float* lse, int32_t num_splits) {
     spicy_status st = check_cache(cache);
     if (st != SPICY_OK) return st;
     if (B < 0 || num_q_heads < 1 || num_q_tokens < 1 || num_splits < 0 || shared_prefix_pages < 0)
@@ -325,19 +339,16 @@ spicy_status spicy_decode_attn_multi(const spicy_cache* cache, const void* q, in
     if (static_cast<int64_t>(B) * num_q_tokens * num_q_heads >= (int64_t(1) << 31) / kMaxGroup)
         return SPICY_ERR_UNSUPPORTED;
     if (B == 0) return SPICY_OK;
-    if (!q || !page_table || !lengths || !o || !lse || !workspace) return SPICY_ERR_ARG;
+    if (!q || !page_table || !lengths || !o || !lse) return SPICY_ERR_ARG;
     if (max_pages_per_seq < 1) return SPICY_ERR_ARG;
     if (shared_prefix_pages > max_pages_per_seq) return SPICY_ERR_RANGE;
-    if (workspace_bytes < spicy_decode_multi_workspace_bytes(B, num_q_tokens, num_q_heads, cache->num_kv_heads,
-                                                             cache->head_dim, max_pages_per_seq,
-                                                             shared_prefix_pages, num_splits))
-        return SPICY_ERR_CAPACITY;
-    // the fp32 kernel has no shared-prefix role: every page is private there
-    const bool bf16 = cache->dtype == SPICY_BF16;
-    const int32_t P = bf16 ? shared_prefix_pages : 0;
-    const DecodePlan plan = plan_decode(B, num_q_heads, cache->num_kv_heads, max_pages_per_seq, P, num_splits,
-                                        num_q_tokens, bf16);
+    return SPICY_OK;
+}
 
+spicy_status decode_launch(const spicy_cache* cache, const void* q, int32_t num_q_tokens, int32_t num_q_heads,
+                           const int32_t* page_table, int32_t max_pages_per_seq, const int32_t* lengths, int32_t B,
+                           int32_t shared_prefix_pages, float* o, float* lse, const DecodeScratch& sc,
+                           const DecodePlan& plan, int32_t P, void* stream) {
     spicy::DecodeArgs a{};
     a.cache = spicy::CacheArgs{cache->k, cache->v, cache->ab, cache->meta, cache->num_pages, cache->num_kv_heads,
                                cache->s2};
@@ -346,16 +357,10 @@ spicy_status spicy_decode_attn_multi(const spicy_cache* cache, const void* q, in
     a.lengths = lengths;
     a.o = o;
     a.lse = lse;
-    char* ws = static_cast<char*>(workspace);
-    const size_t rows = static_cast<size_t>(B) * static_cast<size_t>(num_q_tokens) *
-                        static_cast<size_t>(num_q_heads);
-    a.err = reinterpret_cast<int32_t*>(ws);
-    size_t off = SPICY_WORKSPACE_HEADER;
-    a.ticket = reinterpret_cast<int32_t*>(ws + off);
-    off += align_up(4 * rows);
-    a.part_ml = reinterpret_cast<float*>(ws + off);
-    off += align_up(rows * static_cast<size_t>(plan.slots()) * 2 * sizeof(float));
-    a.part_o = reinterpret_cast<float*>(ws + off);
+    a.err = sc.err;
+    a.ticket = sc.ticket;
+    a.part_ml = sc.part_ml;
+    a.part_o = sc.part_o;
     a.B = B;
     a.H_q = num_q_heads;
     a.max_pages = max_pages_per_seq;
@@ -369,6 +374,113 @@ spicy_status spicy_decode_attn_multi(const spicy_cache* cache, const void* q, in
     a.priv_tiles = priv_tiles(num_q_tokens, num_q_heads, cache->num_kv_heads);
     a.wpg = plan.wpg;
     return spicy::launch_decode(a, cache->dtype, cache->head_dim, static_cast<hipStream_t>(stream));
+}
+
+// ------------------------------------------------ the no-allocation decode
+
+// The decode scratch of spicy_decode_attn_multi_noalloc: one array per GPU,
+// in the library's code object (zero when the library loads; every call
+// leaves its tickets at zero).  Layout: [0, 256) unused header; the tickets
+// of up to kNoAllocMaxRows query rows at a fixed place, so that calls of any
+// shape find theirs at zero; then the partials of the call.
+constexpr size_t kNoAllocBytes = size_t(32) << 20;
+constexpr int64_t kNoAllocMaxRows = 65536;
+constexpr size_t kNoAllocTickets = SPICY_WORKSPACE_HEADER;
+constexpr size_t kNoAllocPartials = SPICY_WORKSPACE_HEADER + 4 * kNoAllocMaxRows;
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch[kMaxDevices];        // per device: scratch's device address (from hipGetSymbolAddress)
+
+// The scratch address on the current device, looked up once per device with
+// that device current; nullptr if the lookup fails.
+void* scratch_on_current_device(int* dev_out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    *dev_out = dev;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        g_scratch[dev] = p;
+    }
+    return g_scratch[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+spicy_status spicy_decode_attn_multi(const spicy_cache* cache, const void* q, int32_t num_q_tokens,
+                                     int32_t num_q_heads, const int32_t* page_table, int32_t max_pages_per_seq,
+                                     const int32_t* lengths, int32_t B, int32_t shared_prefix_pages, float* o,
+                                     float* lse, void* workspace, size_t workspace_bytes, int32_t num_splits,
+                                     void* stream) {
+    spicy_status st = check_decode(cache, q, num_q_tokens, num_q_heads, page_table, max_pages_per_seq, lengths, B,
+                                   shared_prefix_pages, o, lse, num_splits);
+    if (st != SPICY_OK || B == 0) return st;
+    if (!workspace) return SPICY_ERR_ARG;
+    if (workspace_bytes < spicy_decode_multi_workspace_bytes(B, num_q_tokens, num_q_heads, cache->num_kv_heads,
+                                                             cache->head_dim, max_pages_per_seq,
+                                                             shared_prefix_pages, num_splits))
+        return SPICY_ERR_CAPACITY;
+    // the fp32 kernel has no shared-prefix role: every page is private there
+    const bool bf16 = cache->dtype == SPICY_BF16;
+    const int32_t P = bf16 ? shared_prefix_pages : 0;
+    const DecodePlan plan = plan_decode(B, num_q_heads, cache->num_kv_heads, max_pages_per_seq, P, num_splits,
+                                        num_q_tokens, bf16);
+    char* ws = static_cast<char*>(workspace);
+    const size_t rows = static_cast<size_t>(B) * static_cast<size_t>(num_q_tokens) *
+                        static_cast<size_t>(num_q_heads);
+    DecodeScratch sc;
+    sc.err = reinterpret_cast<int32_t*>(ws);
+    size_t off = SPICY_WORKSPACE_HEADER;
+    sc.ticket = reinterpret_cast<int32_t*>(ws + off);
+    off += align_up(4 * rows);
+    sc.part_ml = reinterpret_cast<float*>(ws + off);
+    off += align_up(rows * static_cast<size_t>(plan.slots()) * 2 * sizeof(float));
+    sc.part_o = reinterpret_cast<float*>(ws + off);
+    return decode_launch(cache, q, num_q_tokens, num_q_heads, page_table, max_pages_per_seq, lengths, B,
+                         shared_prefix_pages, o, lse, sc, plan, P, stream);
+}
+
+size_t spicy_decode_noalloc_max_bytes(void) { return kNoAllocBytes; }
+
+spicy_status spicy_decode_attn_multi_noalloc(const spicy_cache* cache, const void* q, int32_t num_q_tokens,
+                                             int32_t num_q_heads, const int32_t* page_table,
+                                             int32_t max_pages_per_seq, const int32_t* lengths, int32_t B,
+                                             int32_t shared_prefix_pages, float* o, float* lse,
+                                             int32_t* device_error, int32_t num_splits, void* stream) {
+    spicy_status st = check_decode(cache, q, num_q_tokens, num_q_heads, page_table, max_pages_per_seq, lengths, B,
+                                   shared_prefix_pages, o, lse, num_splits);
+    if (st != SPICY_OK || B == 0) return st;
+    const bool bf16 = cache->dtype == SPICY_BF16;
+    const int32_t P = bf16 ? shared_prefix_pages : 0;
+    const DecodePlan plan = plan_decode(B, num_q_heads, cache->num_kv_heads, max_pages_per_seq, P, num_splits,
+                                        num_q_tokens, bf16);
+    const int64_t rows = static_cast<int64_t>(B) * num_q_tokens * num_q_heads;
+    const size_t rs = static_cast<size_t>(rows) * static_cast<size_t>(plan.slots());
+    const size_t ml_bytes = align_up(rs * 2 * sizeof(float));
+    if (rows > kNoAllocMaxRows ||
+        kNoAllocPartials + ml_bytes + rs * static_cast<size_t>(cache->head_dim) * sizeof(float) > kNoAllocBytes)
+        return SPICY_ERR_CAPACITY;
+    // the stream must run on the current device, whose scratch the call uses
+    int dev = -1;
+    char* base = static_cast<char*>(scratch_on_current_device(&dev));
+    if (!base) return SPICY_ERR_HIP;
+    if (stream) {
+        hipDevice_t sdev = -1;
+        if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev) != hipSuccess) return SPICY_ERR_HIP;
+        if (sdev != dev) return SPICY_ERR_ARG;
+    }
+    DecodeScratch sc;
+    sc.err = device_error;
+    sc.ticket = reinterpret_cast<int32_t*>(base + kNoAllocTickets);
+    sc.part_ml = reinterpret_cast<float*>(base + kNoAllocPartials);
+    sc.part_o = reinterpret_cast<float*>(base + kNoAllocPartials + ml_bytes);
+    return decode_launch(cache, q, num_q_tokens, num_q_heads, page_table, max_pages_per_seq, lengths, B,
+                         shared_prefix_pages, o, lse, sc, plan, P, stream);
 }
 
 size_t spicy_policy_workspace_bytes(int32_t total_tokens, int32_t num_kv_heads) {

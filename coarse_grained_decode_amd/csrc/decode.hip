@@ -509,7 +509,6 @@ struct Finish {
 // each wait covers exactly one page); they are never processed.
 template <int D, int NBUF, bool DIAG, int TPW, int WPG>
 __global__ __launch_bounds__(WPG * kWave, 8 / WPG) void decode_mfma_kernel(DecodeArgs a) {
-    constexpr int NT = D / 16;
     const int lane = threadIdx.x % kWave;
     const int wave = threadIdx.x / kWave;
     const int row = lane % 16;

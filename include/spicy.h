@@ -287,8 +287,13 @@ spicy_status spicy_decode_plan(int32_t B, int32_t num_q_heads, int32_t num_kv_he
                                int32_t shared_prefix_pages, int32_t num_splits, int32_t num_q_tokens,
                                int32_t* plan);
 
-/* Workspace bytes spicy_decode_attn needs (header + fp32 partial (m, l, o[d])
- * per (sequence, query head, split)). */
+/* Workspace bytes spicy_decode_attn needs: the header; one int32 arrival
+ * counter ("ticket") per query row; per (query row, page group) an fp32
+ * partial (max, sum, o[d]).  The tickets must be zero when a call starts:
+ * allocate the workspace zero-filled, and zero it again before reusing it
+ * for a call with more query rows (B x n_q x H_q) than any earlier call on it
+ * (a call finds its tickets right after the header and leaves every ticket
+ * it used at zero).  A non-zero ticket sets SPICY_DEVERR_TICKET. */
 size_t spicy_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
                                     int32_t head_dim, int32_t max_pages_per_seq,
                                     int32_t num_splits);
@@ -308,9 +313,12 @@ size_t spicy_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t num_
  *            sum_i q_i^2 s2_e,i / (2d).
  *   lse      float32 [B][num_q_heads]: natural-log log-sum-exp of s; -inf (and
  *            o = 0) when a sequence has no entry of non-zero weight.
- * The entries of each (sequence, KV head) are split over up to
- * spicy_decode_num_splits(...) wavefronts of equal page count (split-K); a
- * second kernel merges the partials by log-sum-exp.
+ * One launch: the pages of each (sequence, KV head) are cut into page groups
+ * (spicy_decode_num_splits(...) of them, each one workgroup, split-K); a row
+ * whose pages form a single group is written directly, otherwise every group
+ * writes its partial and the last group to arrive at the row (counted with a
+ * device-scope atomic ticket) merges the row's partials by log-sum-exp in
+ * group order, so the result does not depend on arrival order.
  * Workspace: device, >= spicy_decode_workspace_bytes(...) with the same
  *   num_splits; first int32 = sticky device error word.
  * Errors: SPICY_ERR_ARG, SPICY_ERR_UNSUPPORTED (head_dim not 64/128,
@@ -394,6 +402,36 @@ spicy_status spicy_decode_attn_multi(const spicy_cache* cache,   /* host struct 
                                      const int32_t* lengths, int32_t B, int32_t shared_prefix_pages,
                                      float* o, float* lse, void* workspace, size_t workspace_bytes,
                                      int32_t num_splits, void* stream);
+
+/* ------------------------------------------------------------------------
+ * spicy_decode_attn_multi_noalloc — spicy_decode_attn_multi for callers that
+ * cannot allocate: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  It takes no workspace and calls no
+ * allocating routine: the per-row tickets and the partials live in one
+ * file-scope device array of the library, spicy_decode_noalloc_max_bytes()
+ * bytes on each GPU the library runs on (held until the process ends; its
+ * tickets start at zero and every completed call leaves them at zero).
+ * Same arguments, results, plan and kernels as spicy_decode_attn_multi,
+ * without workspace and workspace_bytes, plus:
+ *   device_error  int32 (device) or NULL: the sticky device error word (the
+ *                 SPICY_DEVERR_* bits are OR-ed into it; the caller clears
+ *                 it); NULL drops device errors.
+ * The stream must belong to the current device.  Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (other
+ * streams, other threads) race and give wrong results; order them.
+ * Errors: those of spicy_decode_attn_multi without the workspace ones;
+ *   SPICY_ERR_CAPACITY if B x num_q_tokens x num_q_heads > 65536 or the
+ *   call's partials do not fit the array; SPICY_ERR_ARG if the stream is on
+ *   another device; SPICY_ERR_HIP if the array's address cannot be found.
+ * ------------------------------------------------------------------------ */
+size_t spicy_decode_noalloc_max_bytes(void);
+
+spicy_status spicy_decode_attn_multi_noalloc(const spicy_cache* cache,   /* host struct */
+                                             const void* q, int32_t num_q_tokens, int32_t num_q_heads,
+                                             const int32_t* page_table, int32_t max_pages_per_seq,
+                                             const int32_t* lengths, int32_t B, int32_t shared_prefix_pages,
+                                             float* o, float* lse, int32_t* device_error,
+                                             int32_t num_splits, void* stream);
 
 /* Human-readable name of a status code (static string). */
 const char* spicy_status_string(spicy_status s);
