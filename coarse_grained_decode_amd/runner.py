@@ -145,16 +145,36 @@ class DyadicPyramid:
         self.B = B
         self.blocks: List[tuple] = []          # (begin int32[B], end int32[B], level)
 
+    def push(self, begin, end) -> None:
+        """Record a chunk coarsened into entries [begin[b], end[b]) as a
+        level-0 block."""
+        self.blocks.append((np.asarray(begin, np.int32).copy(), np.asarray(end, np.int32).copy(), 0))
+
+    def next_merge(self) -> Optional[tuple]:
+        """(begin, end) int32 arrays of the merge the two newest blocks are
+        due for (they have the same level), or None."""
+        if len(self.blocks) >= 2 and self.blocks[-1][2] == self.blocks[-2][2]:
+            return self.blocks[-2][0], self.blocks[-1][1]
+        return None
+
+    def merged(self, end=None) -> None:
+        """Replace the two newest blocks by their union one level up.  end:
+        the union's end after spicy_compact_range gave back its freed
+        entries (default: the newer block's end, nothing compacted)."""
+        b2 = self.blocks.pop()
+        b1 = self.blocks.pop()
+        e = b2[1] if end is None else np.asarray(end, np.int32).copy()
+        self.blocks.append((b1[0], e, b1[2] + 1))
+
     def append(self, begin, end) -> List[tuple]:
         """Record a chunk coarsened into entries [begin[b], end[b]) and return
-        the merges it triggers, in order, as (begin, end) int32 arrays."""
-        self.blocks.append((np.asarray(begin, np.int32).copy(), np.asarray(end, np.int32).copy(), 0))
+        the merges it triggers, in order, as (begin, end) int32 arrays (no
+        compaction between them)."""
+        self.push(begin, end)
         merges = []
-        while len(self.blocks) >= 2 and self.blocks[-1][2] == self.blocks[-2][2]:
-            b2 = self.blocks.pop()
-            b1 = self.blocks.pop()
-            merges.append((b1[0], b2[1]))
-            self.blocks.append((b1[0], b2[1], b1[2] + 1))
+        while (m := self.next_merge()) is not None:
+            merges.append(m)
+            self.merged()
         return merges
 
     @property

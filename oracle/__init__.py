@@ -69,6 +69,9 @@ def lib():
             L.oracle_merge_level.restype = ctypes.c_int
             L.oracle_merge_level.argtypes = [ctypes.c_int, i32, i32, P, P, P, P, P, i32, P, i32, P, P, i32,
                                              ctypes.c_double, i32, i32]
+            L.oracle_compact_range.restype = ctypes.c_int
+            L.oracle_compact_range.argtypes = [ctypes.c_int, i32, i32, P, P, P, P, P, i32, P, i32, P, P, i32, P,
+                                               i32, i32]
             L.oracle_decode_heads.restype = ctypes.c_int
             L.oracle_decode_heads.argtypes = [ctypes.c_int, ctypes.c_int, i32, i32, i32, P, P, P, P, P, i32,
                                               P, i32, P, i32, P, P, i32, i32, i32, i32]
@@ -279,6 +282,35 @@ def merge_level(cache: Cache, page_table: np.ndarray, entry_begin: np.ndarray, e
             list(ex.map(run, chunks))
     if any(rc != 0 for rc in rcs):
         raise ValueError(f"oracle_merge_level failed: codes {sorted(set(rcs))}")
+
+
+def compact_range(cache: Cache, page_table: np.ndarray, entry_begin: np.ndarray, lengths: np.ndarray,
+                  threads: int | None = None) -> np.ndarray:
+    """oracle_compact_range: per sequence and head, the non-null entries of
+    [entry_begin[b], lengths[b]) move in order to the front of the range, in
+    place; returns the new lengths (int32 [B])."""
+    L = lib()
+    table = np.ascontiguousarray(page_table, dtype=np.int32)
+    eb = np.ascontiguousarray(entry_begin, dtype=np.int32)
+    ln = np.ascontiguousarray(lengths, dtype=np.int32)
+    B = table.shape[0]
+    out = ln.copy()
+    rcs = []
+
+    def run(rng):
+        rcs.append(L.oracle_compact_range(DT[cache.store], cache.H_kv, cache.d, _p(cache.k), _p(cache.v),
+                                          _p(cache.ab), _p(cache.meta), _p(cache.s2), cache.num_pages, _p(table),
+                                          table.shape[1], _p(eb), _p(ln), B, _p(out), rng[0], rng[1]))
+
+    chunks = _chunks(B, threads or default_threads())
+    if len(chunks) == 1:
+        run(chunks[0])
+    else:
+        with ThreadPoolExecutor(len(chunks)) as ex:
+            list(ex.map(run, chunks))
+    if any(rc != 0 for rc in rcs):
+        raise ValueError(f"oracle_compact_range failed: codes {sorted(set(rcs))}")
+    return out
 
 
 def bf16_round(x: float) -> int:

@@ -502,6 +502,118 @@ int oracle_merge_level(int dtype, int32_t H_kv, int32_t d,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Compaction of a merged range                                              */
+/* ------------------------------------------------------------------------ */
+
+static size_t dtype_bytes(int dtype) {
+    return dtype == ORACLE_F32 ? 4 : dtype == ORACLE_BF16 ? 2 : 8;
+}
+
+/* Copy every stored byte of entry (P_src, slot_src) of head h to
+ * (P_dst, slot_dst): key, value and variance rows, (alpha, beta), metadata. */
+static void copy_entry_raw(const cache_view* c, int32_t h, int32_t P_src, int32_t s_src,
+                           int32_t P_dst, int32_t s_dst) {
+    const size_t es = dtype_bytes(c->dtype);
+    const size_t src = (size_t)P_src * (size_t)c->H + (size_t)h;
+    const size_t dst = (size_t)P_dst * (size_t)c->H + (size_t)h;
+    void* rows[3] = {c->k, c->v, c->s2};
+    for (int r = 0; r < 3; ++r) {
+        if (!rows[r]) continue;
+        char* base = (char*)rows[r];
+        for (int32_t i = 0; i < c->d; ++i)
+            memmove(base + (dst * PAGE * (size_t)c->d + slot_elem(c->d, s_dst, i)) * es,
+                    base + (src * PAGE * (size_t)c->d + slot_elem(c->d, s_src, i)) * es, es);
+    }
+    char* ab = (char*)c->ab;
+    memmove(ab + (dst * PAGE + (size_t)s_dst) * 2 * es, ab + (src * PAGE + (size_t)s_src) * 2 * es, 2 * es);
+    if (c->meta) c->meta[dst * PAGE + (size_t)s_dst] = c->meta[src * PAGE + (size_t)s_src];
+}
+
+/* Give a merged range its freed slots back (SPICY-KV demo page: the cascaded
+ * dyadic ring-buffer pyramid, Claim 12, where a level that has merged
+ * occupies half its slots; Equal-Variation KV Cache page, implementation
+ * notes: the reservoir is split and merged as it streams).  For every
+ * sequence b, over logical entries [entry_begin[b], lengths[b]):
+ *   - an entry is null when its alpha is -inf (zero softmax weight);
+ *   - per KV head h, the c_h entries that are not null keep their order and
+ *     move to entries entry_begin[b], entry_begin[b] + 1, ...;
+ *   - lengths_out[b] = entry_begin[b] + max over heads of c_h;
+ *   - per head, entries from entry_begin[b] + c_h to the end of the page that
+ *     holds entry lengths_out[b] - 1 become nulls (zero key, value and
+ *     variance, alpha = -inf, beta = 0, meta {0, 0, 0});
+ *   - entries before entry_begin[b] and pages after that one are untouched.
+ * A moved entry keeps every stored byte.  Attention over the result equals
+ * attention over the input: only zero-weight entries are dropped and the
+ * others keep their order.  Return codes: 1 for entry_begin outside
+ * [0, lengths], 3 for an entry beyond max_pages_per_seq pages, 2 for a page id
+ * outside the pool (nothing of that sequence is changed in these cases). */
+int oracle_compact_range(int dtype, int32_t H_kv, int32_t d,
+                         void* k_pool, void* v_pool, void* ab_pool, void* meta, void* s2_pool,
+                         int32_t num_pages, const int32_t* page_table, int32_t max_pages_per_seq,
+                         const int32_t* entry_begin, const int32_t* lengths, int32_t B,
+                         int32_t* lengths_out, int32_t b_begin, int32_t b_end) {
+    if (dtype < 0 || dtype > 2 || H_kv <= 0 || !head_dim_ok(d) || B < 0) return 1;
+    if (!k_pool || !v_pool || !ab_pool || !page_table || !entry_begin || !lengths || !lengths_out) return 1;
+    if (b_begin < 0 || b_end > B || b_begin > b_end) return 1;
+    int rc = 0;
+    int64_t* kept = NULL;                 /* source entries of the head being moved */
+    int64_t cap = 0;
+    int32_t* count = malloc(sizeof(int32_t) * (size_t)H_kv);
+    double* zero = calloc((size_t)d, sizeof(double));
+    if (!count || !zero) { free(count); free(zero); return 1; }
+    for (int32_t b = b_begin; b < b_end && rc == 0; ++b) {
+        const int32_t* row = page_table + (size_t)b * (size_t)max_pages_per_seq;
+        cache_view c = {dtype, H_kv, d, num_pages, max_pages_per_seq, k_pool, v_pool, ab_pool,
+                        (oracle_meta*)meta, row, s2_pool};
+        const int64_t e0 = entry_begin[b], L = lengths[b];
+        if (e0 < 0 || e0 > L) { rc = 1; break; }
+        if ((L + PAGE - 1) / PAGE > max_pages_per_seq) { rc = 3; break; }
+        for (int64_t lp = e0 / PAGE; lp < (L + PAGE - 1) / PAGE; ++lp)
+            if (row[lp] < 0 || row[lp] >= num_pages) rc = 2;
+        if (rc) break;
+        if (L - e0 > cap) {
+            free(kept);
+            cap = L - e0;
+            kept = malloc(sizeof(int64_t) * (size_t)cap);
+            if (!kept) { rc = 1; break; }
+        }
+        int32_t longest = 0;
+        for (int32_t h = 0; h < H_kv; ++h) {
+            count[h] = 0;
+            for (int64_t e = e0; e < L; ++e) {
+                const size_t ph = (size_t)row[e / PAGE] * (size_t)H_kv + (size_t)h;
+                if (load_elem(dtype, ab_pool, (ph * PAGE + (size_t)(e % PAGE)) * 2) != -INFINITY) ++count[h];
+            }
+            if (count[h] > longest) longest = count[h];
+        }
+        const int64_t new_len = e0 + longest;
+        const int64_t pad_end = (new_len + PAGE - 1) / PAGE * PAGE;
+        for (int32_t h = 0; h < H_kv; ++h) {
+            int64_t n = 0;
+            for (int64_t e = e0; e < L; ++e) {
+                const size_t ph = (size_t)row[e / PAGE] * (size_t)H_kv + (size_t)h;
+                if (load_elem(dtype, ab_pool, (ph * PAGE + (size_t)(e % PAGE)) * 2) != -INFINITY) kept[n++] = e;
+            }
+            /* kept[i] >= e0 + i: moving in increasing i never overwrites an
+             * entry still to be moved */
+            for (int64_t i = 0; i < n; ++i) {
+                const int64_t src = kept[i], dst = e0 + i;
+                if (src != dst)
+                    copy_entry_raw(&c, h, row[src / PAGE], (int32_t)(src % PAGE), row[dst / PAGE],
+                                   (int32_t)(dst % PAGE));
+            }
+            for (int64_t e = e0 + n; e < pad_end && rc == 0; ++e)
+                rc = put_entry(&c, h, e, zero, zero, -INFINITY, 0.0, 0, 0, 0, NULL);
+        }
+        lengths_out[b] = (int32_t)new_len;
+    }
+    free(kept);
+    free(count);
+    free(zero);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Decode                                                                    */
 /* ------------------------------------------------------------------------ */
 

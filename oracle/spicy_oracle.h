@@ -102,6 +102,15 @@ int oracle_merge_level(int dtype, int32_t H_kv, int32_t d,
                        int32_t num_pages, const int32_t* page_table, int32_t max_pages_per_seq,
                        const int32_t* entry_begin, const int32_t* entry_end, int32_t B, double rope_base,
                        int32_t b_begin, int32_t b_end);
+/* Compaction after a merge: per (sequence, head) the non-null entries
+ * (alpha != -inf) of [entry_begin[b], lengths[b]) move, in order, to the
+ * front of the range; lengths_out[b] = entry_begin[b] + the longest head's
+ * count; shorter heads and the rest of that last page become nulls. */
+int oracle_compact_range(int dtype, int32_t H_kv, int32_t d,
+                         void* k_pool, void* v_pool, void* ab_pool, void* meta, void* s2_pool,
+                         int32_t num_pages, const int32_t* page_table, int32_t max_pages_per_seq,
+                         const int32_t* entry_begin, const int32_t* lengths, int32_t B,
+                         int32_t* lengths_out, int32_t b_begin, int32_t b_end);
 int oracle_decode_heads(int q_dtype, int dtype, int32_t H_q, int32_t H_kv, int32_t d,
                         const void* q,
                         const void* k_pool, const void* v_pool, const void* ab_pool, const void* s2_pool,
