@@ -22,7 +22,8 @@ __all__ = [
     "spicy_policy", "spicy_policy_workspace_bytes",
     "spicy_decode_attn_multi", "spicy_decode_multi_workspace_bytes",
     "spicy_decode_attn_multi_noalloc", "spicy_decode_noalloc_max_bytes",
-    "spicy_coarsen_weighted", "spicy_merge_level", "spicy_merge_workspace_bytes", "spicy_decode_plan",
+    "spicy_coarsen_weighted", "spicy_merge_level", "spicy_merge_workspace_bytes", "spicy_compact_range",
+    "spicy_decode_plan",
     "spicy_status_string", "library_path", "load_library", "workspace", "device_error",
     "SPICY_F32", "SPICY_BF16", "PAGE_SIZE", "WORKSPACE_HEADER",
     "DEVERR_PAGE_ID", "DEVERR_CAPACITY", "DEVERR_SEGMENTS", "DEVERR_LENGTH", "DEVERR_SHARED", "DEVERR_POLICY",
@@ -87,6 +88,8 @@ def load_library():
     L.spicy_merge_workspace_bytes.argtypes = [i32, i32, i32]
     L.spicy_merge_level.restype = ctypes.c_int
     L.spicy_merge_level.argtypes = [CP, i32, ctypes.c_double, P, i32, P, P, i32, P, sz, P]
+    L.spicy_compact_range.restype = ctypes.c_int
+    L.spicy_compact_range.argtypes = [CP, i32, P, i32, P, P, P, P, P]
     L.spicy_coarsen_weighted.restype = ctypes.c_int
     L.spicy_coarsen_weighted.argtypes = [CP, P, P, i32, P, P, P, P, i32, P, P, i32, ctypes.c_double, P, i32,
                                          P, P, P, sz, P]
@@ -368,6 +371,37 @@ def spicy_merge_level(cache: PagedCache, rope_base: float, page_table, entry_beg
                              _ptr(entry_end), int(max_range), _ptr(workspace), ws_bytes, _stream(stream))
     if rc != 0:
         raise SpicyError(rc, "spicy_merge_level")
+
+
+def spicy_compact_range(cache: PagedCache, page_table, entry_begin, lengths, lengths_out, device_error,
+                        stream=None, *, B: int | None = None, max_pages_per_seq: int | None = None) -> None:
+    """spicy_compact_range through the C ABI (see include/spicy.h): per
+    sequence and KV head the non-null entries of [entry_begin[b], lengths[b])
+    move, in order, to the front of the range; lengths_out[b] gets the new
+    length.  device_error: int32 device tensor whose first element receives
+    SPICY_DEVERR_* bits."""
+    L = load_library()
+    dev = cache.check()
+    _check(page_table, "page_table", torch.int32, ndim=2, device=dev)
+    _check(entry_begin, "entry_begin", torch.int32, (None,), device=dev)
+    _check(lengths, "lengths", torch.int32, tuple(entry_begin.shape), device=dev)
+    _check(lengths_out, "lengths_out", torch.int32, tuple(entry_begin.shape), device=dev)
+    _check(device_error, "device_error", torch.int32, ndim=1, device=dev)
+    if device_error.numel() < 1:
+        raise ValueError("device_error: needs one int32")
+    if lengths_out.data_ptr() in (lengths.data_ptr(), entry_begin.data_ptr()):
+        raise ValueError("lengths_out: must be a tensor of its own (not lengths or entry_begin)")
+    B = int(entry_begin.shape[0]) if B is None else B
+    _check_count(B, int(entry_begin.shape[0]), "B")
+    if page_table.shape[0] < B:
+        raise ValueError(f"page_table: {page_table.shape[0]} rows for {B} sequences")
+    max_pages = int(page_table.shape[1]) if max_pages_per_seq is None else max_pages_per_seq
+    _check_count(max_pages, int(page_table.shape[1]), "max_pages_per_seq")
+    st = cache.struct()
+    rc = L.spicy_compact_range(ctypes.byref(st), B, _ptr(page_table), max_pages, _ptr(entry_begin), _ptr(lengths),
+                               _ptr(lengths_out), _ptr(device_error), _stream(stream))
+    if rc != 0:
+        raise SpicyError(rc, "spicy_compact_range")
 
 
 def spicy_coarsen_weighted(cache: PagedCache, k_pre, v, seq_offsets, pos_base, seg_offsets, seq_seg_ptr,

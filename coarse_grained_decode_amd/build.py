@@ -24,7 +24,7 @@ SOURCES = ["api.hip", "coarsen.hip", "decode.hip", "policy.hip", "merge.hip"]
 # (source, object, extra flags): coarsen.hip builds once per (element type,
 # head dim) so that its kernels compile in parallel
 UNITS = [("api.hip", "api", []), ("decode.hip", "decode", []), ("policy.hip", "policy", []),
-         ("merge.hip", "merge", [])] + [("coarsen.hip", f"coarsen{i}", [f"-DSPICY_COARSEN_PART={i}"])
+         ("merge.hip", "merge", []), ("compact.hip", "compact", [])] + [("coarsen.hip", f"coarsen{i}", [f"-DSPICY_COARSEN_PART={i}"])
                                          for i in range(4)]
 HEADERS = ["launch.h", "spicy_device.h"]
 ARCH = os.environ.get("SPICY_OFFLOAD_ARCH", "gfx950")

@@ -579,4 +579,31 @@ spicy_status spicy_merge_level(const spicy_cache* cache, int32_t B, double rope_
     return spicy::launch_merge(a, cache->dtype, cache->head_dim, static_cast<hipStream_t>(stream));
 }
 
+spicy_status spicy_compact_range(const spicy_cache* cache, int32_t B, const int32_t* page_table,
+                                 int32_t max_pages_per_seq, const int32_t* entry_begin, const int32_t* lengths,
+                                 int32_t* lengths_out, int32_t* device_error, void* stream) {
+    spicy_status st = check_cache(cache);
+    if (st != SPICY_OK) return st;
+    if (B < 0) return SPICY_ERR_ARG;
+    if (B == 0) return SPICY_OK;
+    if (!page_table || !entry_begin || !lengths || !lengths_out || !device_error) return SPICY_ERR_ARG;
+    if (max_pages_per_seq < 1) return SPICY_ERR_ARG;
+    // the move launch reads entry_begin and lengths after the count launch
+    // has written lengths_out
+    if (lengths_out == lengths || lengths_out == entry_begin) return SPICY_ERR_ARG;
+    if (B > kMaxGridY) return SPICY_ERR_UNSUPPORTED;
+    spicy::CompactArgs a{};
+    a.cache = spicy::CacheArgs{cache->k, cache->v, cache->ab, cache->meta, cache->num_pages, cache->num_kv_heads,
+                               cache->s2};
+    a.page_table = page_table;
+    a.entry_begin = entry_begin;
+    a.lengths = lengths;
+    a.lengths_out = lengths_out;
+    a.err = device_error;
+    a.B = B;
+    a.max_pages = max_pages_per_seq;
+    a.D = cache->head_dim;
+    return spicy::launch_compact(a, cache->dtype, static_cast<hipStream_t>(stream));
+}
+
 }  // extern "C"

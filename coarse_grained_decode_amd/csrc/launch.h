@@ -12,5 +12,6 @@ spicy_status launch_coarsen(const CoarsenArgs& a, int dtype, int head_dim, hipSt
 spicy_status launch_decode(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream);
 spicy_status launch_policy(const PolicyArgs& a, hipStream_t stream);
 spicy_status launch_merge(const MergeArgs& a, int dtype, int head_dim, hipStream_t stream);
+spicy_status launch_compact(const CompactArgs& a, int dtype, hipStream_t stream);
 
 }  // namespace spicy

@@ -202,6 +202,20 @@ struct MergeArgs {
     double theta[64];             // rotary frequencies rope_base^(-2i/d), i < d/2 (host libm pow)
 };
 
+// spicy_compact_range: non-null entries of [entry_begin, lengths) moved to
+// the front of the range, per head.
+struct CompactArgs {
+    CacheArgs cache;
+    const int32_t* page_table;    // [B][max_pages]
+    const int32_t* entry_begin;   // [B]
+    const int32_t* lengths;       // [B]
+    int32_t* lengths_out;         // [B]
+    int32_t* err;
+    int32_t B;
+    int32_t max_pages;
+    int32_t D;
+};
+
 struct DecodeArgs {
     CacheArgs cache;
     const void* q;

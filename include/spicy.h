@@ -265,6 +265,50 @@ spicy_status spicy_merge_level(const spicy_cache* cache, int32_t B, double rope_
                                int32_t max_range, void* workspace, size_t workspace_bytes,
                                void* stream);
 
+/* ------------------------------------------------------------------------
+ * spicy_compact_range — give a merged range its freed entries back, in place.
+ *
+ * SPICY-KV demo page, Claim 12: in the cascaded dyadic ring-buffer pyramid a
+ * level that has merged holds half as many nodes, so it needs half the
+ * storage; spicy_merge_level leaves the second entry of every pair as a null,
+ * and this call removes the nulls.  For every sequence b, over logical
+ * entries [entry_begin[b], lengths[b]):
+ *   - an entry is null when its alpha is -inf (zero weight in the decode);
+ *   - per KV head h, the c_h non-null entries keep their order and move to
+ *     entries entry_begin[b], entry_begin[b] + 1, ...; a moved entry keeps
+ *     every stored byte (key, value, variance row, alpha, beta, metadata);
+ *   - lengths_out[b] = entry_begin[b] + max over heads of c_h;
+ *   - per head, entries from entry_begin[b] + c_h to the end of the page
+ *     holding entry lengths_out[b] - 1 become nulls (zero key, value and
+ *     variance, alpha = -inf, beta = 0, meta {0, 0, 0});
+ *   - entries before entry_begin[b] and the pages after that last page are
+ *     not written: those pages are free for the next appended chunk
+ *     (coarsen it at entry_start = lengths_out[b]).
+ * The decode over lengths_out equals the decode over lengths up to the
+ * order of floating-point additions (only zero-weight entries are dropped);
+ * a range with no nulls inside it is left as it is.
+ *   page_table    int32 [B][max_pages_per_seq] (device).
+ *   entry_begin, lengths  int32 [B] (device); lengths_out int32 [B]
+ *                 (device) must not be either of them (it is written before
+ *                 the entries move, and they are read again then).
+ *   device_error  int32 (device): SPICY_DEVERR_* bits are OR-ed into it:
+ *                 SPICY_DEVERR_SEGMENTS for entry_begin[b] outside
+ *                 [0, lengths[b]], SPICY_DEVERR_CAPACITY for lengths[b]
+ *                 beyond max_pages_per_seq pages, SPICY_DEVERR_PAGE_ID for a
+ *                 page id of the range outside the pool; such a sequence is
+ *                 left untouched with lengths_out[b] = lengths[b].
+ * Ranges of different sequences must not share physical pages.  Needs no
+ * workspace: two launches (a count per sequence, then the moves per
+ * (sequence, KV head)) on `stream`.
+ * Errors: SPICY_ERR_ARG (null pointer, B < 0, max_pages_per_seq < 1,
+ *   lengths_out equal to lengths or entry_begin, bad cache),
+ *   SPICY_ERR_UNSUPPORTED (B > 65535, head_dim not 64/128), SPICY_ERR_HIP.
+ * ------------------------------------------------------------------------ */
+spicy_status spicy_compact_range(const spicy_cache* cache, int32_t B,
+                                 const int32_t* page_table, int32_t max_pages_per_seq,
+                                 const int32_t* entry_begin, const int32_t* lengths,
+                                 int32_t* lengths_out, int32_t* device_error, void* stream);
+
 /* Split-K plan: how many splits per (sequence, KV head) spicy_decode_attn
  * uses when asked for `num_splits` (0 = automatic) for a batch of B sequences
  * of at most max_pages_per_seq pages.  Pure host function.  The shared-prefix

@@ -124,3 +124,17 @@ def test_merge_and_policy_reject(lib):
     with pytest.raises(ValueError, match="k_pre: dtype"):
         cgd.spicy_policy(k.float(), k, i32(B + 1), i32(3), i32(4), 5, 1, 0, 0, i32(B * 5 + 1), i32(B + 1),
                          torch.zeros(10, H, dtype=torch.uint8), i32(64))
+
+
+def test_compact_rejects(lib):
+    c = cache()
+    i32 = lambda *s: torch.zeros(*s, dtype=torch.int32)
+    ln = i32(B)
+    with pytest.raises(ValueError, match="lengths_out: must be a tensor of its own"):
+        cgd.spicy_compact_range(c, i32(B, 4), i32(B), ln, ln, i32(1))
+    with pytest.raises(ValueError, match="lengths: shape"):
+        cgd.spicy_compact_range(c, i32(B, 4), i32(B), i32(B + 1), i32(B), i32(1))
+    with pytest.raises(ValueError, match="device_error: dtype"):
+        cgd.spicy_compact_range(c, i32(B, 4), i32(B), i32(B), i32(B), torch.zeros(1, dtype=torch.int64))
+    with pytest.raises(ValueError, match="page_table"):
+        cgd.spicy_compact_range(c, i32(B - 1, 4), i32(B), i32(B), i32(B), i32(1))
