@@ -87,7 +87,10 @@ def parse(argv=None):
                          "by the policy's per-token variation")
     ap.add_argument("--merge", action="store_true",
                     help="every step also merges one dyadic level over the entries its coarsening wrote "
-                         "(spicy_merge_level; the cache keeps its metadata)")
+                         "(spicy_merge_level; the cache keeps its metadata), then gives the freed entries "
+                         "back (spicy_compact_range): the decode reads the compacted cache")
+    ap.add_argument("--no-compact", action="store_true",
+                    help="with --merge: leave the merged range's nulls in place (the decode reads them)")
     ap.add_argument("--diag-closure", action="store_true",
                     help="the cache carries per-dimension variances (diagonal closure): coarsen writes them, "
                          "decode reads them in place of the scalar beta")
@@ -135,6 +138,33 @@ def merge_alg_bytes(call, lengths: np.ndarray, pairs: int) -> int:
     return 16 * ranged + 4 * per_entry * pairs
 
 
+def compact_alg_bytes(call, page_table: np.ndarray, alpha_null: np.ndarray, lengths: np.ndarray,
+                      new_lengths: np.ndarray, meta: bool = True) -> int:
+    """Bytes one spicy_compact_range must move.  alpha_null: bool
+    [pages, H, 16], the cache's nulls before the call.  Per sequence: the
+    alpha of every entry of the range and head once (the null test), the
+    range's page ids; per head, every entry that moves (a non-null one after
+    the range's first null) read and written whole (key and value rows,
+    alpha and beta, metadata), and the nulls written from its last entry to
+    the end of the new last page; entry_begin, lengths and lengths_out."""
+    eb = elem_bytes(call.dtype)
+    H, d = call.H_kv, call.d
+    entry = (2 * d + 2) * eb + (16 if meta else 0)
+    total = 12 * call.B
+    for b in range(call.B):
+        e0, L = int(call.entry_start[b]), int(lengths[b])
+        es = np.arange(e0, L)
+        total += H * (L - e0) * eb + 4 * (-(-L // 16) - e0 // 16)
+        pad_end = -(-int(new_lengths[b]) // 16) * 16
+        for h in range(H):
+            nul = alpha_null[page_table[b, es // 16], h, es % 16]
+            first = int(np.argmax(nul)) if nul.any() else len(nul)
+            moved = int((~nul[first:]).sum())
+            live = int((~nul).sum())
+            total += 2 * entry * moved + entry * (pad_end - (e0 + live))
+    return total
+
+
 def decode_alg_bytes(wl, lengths: np.ndarray, q_tokens: int = 1, diag: bool = False) -> int:
     """Bytes the decode must move: every cache entry it attends to (key,
     value, alpha, beta, and with `diag` the variance row), once per physical
@@ -175,6 +205,7 @@ KERNEL_SOURCE = {
     "decode_mfma_kernel": "decode.hip", "decode_f32_kernel": "decode.hip",
     "policy_token_kernel": "policy.hip", "policy_seq_kernel": "policy.hip",
     "merge_list_kernel": "merge.hip", "merge_pair_kernel": "merge.hip",
+    "compact_count_kernel": "compact.hip", "compact_move_kernel": "compact.hip",
 }
 # the kernels of each call, for its traffic
 CALL_KERNELS = {
@@ -182,6 +213,7 @@ CALL_KERNELS = {
     "decode": ["decode_mfma_kernel"],
     "policy": ["policy_token_kernel", "policy_seq_kernel"],
     "merge": ["merge_list_kernel", "merge_pair_kernel"],
+    "compact": ["compact_count_kernel", "compact_move_kernel"],
 }
 
 
@@ -241,7 +273,7 @@ def host_description() -> dict:
 
 
 def cpu_baseline(wl, reps: int, policy: bool = False, q_tokens: int = 1, diag: bool = False,
-                 weighted: bool = False, merge: bool = False):
+                 weighted: bool = False, merge: bool = False, compact: bool = False):
     """The oracle (plain C, double precision) on the host cores: one whole
     step for every sequence of the batch (with `policy`, the oracle's policy
     on the chunk first; then the per-step coarsen and the decode), setup calls
@@ -274,6 +306,8 @@ def cpu_baseline(wl, reps: int, policy: bool = False, q_tokens: int = 1, diag: b
                                      token_weight=pr.variation if (policy and weighted) else None)
             if merge:
                 oracle.merge_level(cache, wl.page_table, step.entry_start, lengths, step.rope_base, threads=threads)
+            if merge and compact:
+                lengths = oracle.compact_range(cache, wl.page_table, step.entry_start, lengths, threads=threads)
         if q_tokens > 1:
             oracle.decode_multi(qm, wl.dtype, cache, wl.page_table, lengths, threads=threads)
         else:
@@ -290,10 +324,18 @@ def cpu_baseline(wl, reps: int, policy: bool = False, q_tokens: int = 1, diag: b
                       f"{f' of {q_tokens} query tokens per sequence' if q_tokens > 1 else ''}"
                       f"{', diagonal closure' if diag else ''}"
                       f"{', variation-weighted representatives' if weighted else ''}"
-                      f"{', one merge level over the chunk' if merge else ''}), "
+                      f"{', one merge level over the chunk' if merge else ''}"
+                      f"{' and its compaction' if merge and compact else ''}), "
                       f"median of {reps} after 1 warm-up, {med:.3f} s per step")
     out.update(host)
     return out
+
+
+def _loadavg():
+    try:
+        return float(open("/proc/loadavg").read().split()[0])
+    except (OSError, ValueError, IndexError):
+        return None
 
 
 # --------------------------------------------------------------- GPU timing
@@ -693,10 +735,22 @@ def main():
         def run_merge():
             spicy_merge_level(dw.cache, mc.call.rope_base, mc.page_table, mc.entry_start, mc.lengths, max_range,
                               mws, max_pages_per_seq=mc.call.max_pages)
+    elif args.no_compact:
+        sys.exit("--no-compact needs --merge")
+    run_compact, clen, cerr = None, None, None
+    if args.merge and not args.no_compact:
+        from coarse_grained_decode_amd import spicy_compact_range
+        clen = torch.empty_like(mc.lengths)
+        cerr = torch.zeros(1, dtype=torch.int32, device=dev)
 
-    def step(ev=None):
-        """One step; with ev (5 events) each call is bracketed:
-        ev[3] policy ev[0] coarsen ev[1] merge ev[4] decode ev[2]."""
+        def run_compact():
+            spicy_compact_range(dw.cache, mc.page_table, mc.entry_start, mc.lengths, clen, cerr,
+                                max_pages_per_seq=mc.call.max_pages)
+
+    def step(ev=None, until=None):
+        """One step; with ev (6 events) each call is bracketed:
+        ev[3] policy ev[0] coarsen ev[1] merge ev[5] compact ev[4] decode ev[2].
+        until="merge": stop after the merge."""
         if ev is not None:
             ev[3].record()
         if policy is not None:
@@ -709,9 +763,15 @@ def main():
             ev[1].record()
         if run_merge is not None:
             run_merge()
+        if until == "merge":
+            return
+        if ev is not None:
+            ev[5].record()
+        if run_compact is not None:
+            run_compact()
         if ev is not None:
             ev[4].record()
-        dw.lengths = step_calls[-1].lengths
+        dw.lengths = clen if run_compact is not None else step_calls[-1].lengths
         dw.decode()
         if ev is not None:
             ev[2].record()
@@ -732,6 +792,7 @@ def main():
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
+    t_issue = time.perf_counter() - t0
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     assert int(dw.dws[0].item()) == 0, "device error word set (decode)"
@@ -739,7 +800,7 @@ def main():
     # per-call durations: K more whole steps queued behind a sleep kernel (so
     # that no call waits for the host), each call bracketed by HIP events on
     # the launch stream
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     _hold_stream(elapsed * 1e6 * 1.5)
     for e in evs:
         step(e)
@@ -749,7 +810,9 @@ def main():
         "decode": [e[4].elapsed_time(e[2]) * 1e3 for e in evs],
     }
     if run_merge is not None:
-        per["merge"] = [e[1].elapsed_time(e[4]) * 1e3 for e in evs]
+        per["merge"] = [e[1].elapsed_time(e[5]) * 1e3 for e in evs]
+    if run_compact is not None:
+        per["compact"] = [e[5].elapsed_time(e[4]) * 1e3 for e in evs]
     if policy is not None:
         per["policy"] = [e[3].elapsed_time(e[0]) * 1e3 for e in evs]
     step_us = [e[3].elapsed_time(e[2]) * 1e3 for e in evs]
@@ -769,6 +832,8 @@ def main():
                   "then policy_seq: scan, boundaries, landmark radix select)",
         "merge": "spicy_merge_level (merge_list: pairs per sequence and head; merge_pair: law of total "
                  "variance per pair)",
+        "compact": "spicy_compact_range (compact_count: new lengths; compact_move: live entries moved to the "
+                   "front of the merged range, nulls to the end of the new last page)",
     }
     pairs = None
     if policy is not None:
@@ -779,11 +844,29 @@ def main():
         pairs = int(mws.view(torch.uint8)[256:256 + 4 * units].view(torch.int32).sum().item())
         assert int(mws[0].item()) == 0, "device error word set (merge)"
         alg["merge"] = merge_alg_bytes(mc.call, mc.lengths.cpu().numpy(), pairs)
+    compaction = None
+    if run_compact is not None:
+        assert int(cerr.item()) == 0, "device error word set (compact)"
+        # the nulls the compaction sees: one more step up to the merge
+        step(until="merge")
+        torch.cuda.synchronize()
+        ab = dw.cache.ab[..., 0]
+        bits = ab.view(torch.int16) if ab.dtype == torch.bfloat16 else ab.view(torch.int32)
+        neg_inf = -128 if ab.dtype == torch.bfloat16 else -8388608          # 0xFF80, 0xFF800000
+        alpha_null = (bits == neg_inf).cpu().numpy()
+        full = mc.lengths.cpu().numpy()
+        run_compact()
+        torch.cuda.synchronize()
+        new = clen.cpu().numpy()
+        alg["compact"] = compact_alg_bytes(mc.call, mc.call.page_table, alpha_null, full, new)
+        compaction = {"entries_before": int((full - mc.call.entry_start).sum()),
+                      "entries_after": int((new - mc.call.entry_start).sum()),
+                      "lengths_max_before": int(full.max()), "lengths_max_after": int(new.max())}
 
     traffic = measured_traffic(wl.name + ("_policy" if policy is not None else "") +
                                (f"_q{args.query_tokens}" if args.query_tokens > 1 else "") +
                                ("_weighted" if args.weighted else "") + ("_diag" if args.diag_closure else "") +
-                               ("_merge" if args.merge else ""))
+                               ("_merge" if args.merge else "") + ("_nocompact" if args.no_compact else ""))
 
     def roof(call):
         st = _stats(per[call])
@@ -823,17 +906,22 @@ def main():
                    "cache_entries_per_seq_mean": float(lengths.mean()),
                    "device_policy": policy is not None, "query_tokens_per_seq": args.query_tokens,
                    "diag_closure": args.diag_closure, "weighted_representatives": args.weighted,
-                   "merge_level": args.merge},
+                   "merge_level": args.merge, "compacted": args.merge and not args.no_compact},
         "step_us": _stats(step_us),
+        # host time to enqueue the K steps (the loop is host-bound when it nears ms_per_step)
+        "host_issue_us_per_step": round(t_issue / args.steps * 1e6, 1),
+        "host_loadavg": _loadavg(),
         "roofline": rooflines[dominant],
         "roofline_decode": r_decode,
         "decode_query_tokens_per_s": round(wl.B * args.query_tokens / (r_decode["call_us"]["mean"] * 1e-6), 1),
     }
-    for c in ("coarsen", "policy", "merge"):
+    for c in ("coarsen", "policy", "merge", "compact"):
         if c in rooflines and c != dominant:
             out[f"roofline_{c}"] = rooflines[c]
     if pairs is not None:
         out["roofline_merge" if dominant != "merge" else "roofline"]["pairs_per_call"] = pairs
+    if compaction is not None:
+        out["roofline_compact" if dominant != "compact" else "roofline"]["entries"] = compaction
     if not args.no_decode_configs:
         del dw
         torch.cuda.empty_cache()
@@ -841,7 +929,8 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_reps, policy=policy is not None,
                                            q_tokens=args.query_tokens, diag=args.diag_closure,
-                                           weighted=args.weighted, merge=args.merge)
+                                           weighted=args.weighted, merge=args.merge,
+                                           compact=args.merge and not args.no_compact)
     print(json.dumps(out), flush=True)
 
 

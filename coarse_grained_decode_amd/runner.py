@@ -17,7 +17,8 @@ import torch
 from . import (PagedCache, spicy_coarsen, spicy_coarsen_weighted, spicy_coarsen_workspace_bytes, spicy_decode_attn,
                spicy_decode_attn_shared, spicy_decode_num_splits, spicy_decode_plan, spicy_decode_shared_workspace_bytes,
                spicy_decode_attn_multi, spicy_decode_multi_workspace_bytes, spicy_policy,
-               spicy_policy_workspace_bytes, spicy_merge_level, spicy_merge_workspace_bytes, workspace)
+               spicy_policy_workspace_bytes, spicy_merge_level, spicy_merge_workspace_bytes, workspace,
+               spicy_compact_range)
 from .workloads import CoarsenCall, PolicySpec, Workload, query_tokens
 
 
@@ -138,7 +139,10 @@ class DyadicPyramid:
     same level they merge into one block a level up, with one
     spicy_merge_level call over their union (each macro-node pairs with its
     neighbour, so the nodes of a level-l block cover 2^l of the chunk's
-    segments).  The schedule is the host's: the pages give no rule for it.
+    segments).  With compaction (cascade), each merge is followed by
+    spicy_compact_range, so a level-l block holds one entry per 2^l base
+    segments plus its C-points and the freed pages take the next chunk.  The
+    schedule is the host's: the pages give no rule for it.
     """
 
     def __init__(self, B: int):
@@ -189,6 +193,31 @@ class DyadicPyramid:
             ws = workspace(spicy_merge_workspace_bytes(len(begin), cache.k.shape[1], rng), device)
             spicy_merge_level(cache, rope_base, page_table, _tensor(begin, None, device), _tensor(end, None, device),
                               rng, ws, stream)
+
+    def cascade(self, cache: PagedCache, lengths: np.ndarray, rope_base: float, page_table: torch.Tensor, device,
+                stream=None) -> np.ndarray:
+        """Run, on the GPU, every merge the newest block is due for, each
+        followed by spicy_compact_range over the merged union, so the pyramid
+        keeps only live entries; lengths: the sequences' lengths now (the end
+        of the newest block).  Returns the lengths after the last compaction
+        (read back after each one: the next merge's range ends there)."""
+        lengths = np.asarray(lengths, np.int32).copy()
+        err = torch.zeros(1, dtype=torch.int32, device=device)
+        while (m := self.next_merge()) is not None:
+            begin, _ = m
+            rng = int((lengths - begin).max()) if len(begin) else 0
+            ws = workspace(spicy_merge_workspace_bytes(len(begin), cache.k.shape[1], rng), device)
+            tb, tl = _tensor(begin, None, device), _tensor(lengths, None, device)
+            spicy_merge_level(cache, rope_base, page_table, tb, tl, rng, ws, stream)
+            out = torch.empty_like(tl)
+            spicy_compact_range(cache, page_table, tb, tl, out, err, stream)
+            if stream is not None:                      # the readback below orders after torch's stream only
+                torch.cuda.synchronize(device)
+            lengths = out.cpu().numpy()
+            if int(ws[0].item()) or int(err.item()):
+                raise RuntimeError(f"pyramid cascade: device error {int(ws[0].item()) | int(err.item()):#x}")
+            self.merged(lengths)
+        return lengths
 
 
 @dataclass

@@ -113,3 +113,28 @@ def test_profile_summary_from_rocprof_csv(tmp_path, monkeypatch):
     b = 100 * 1024 * 2 + 10 * 1024 * 1
     assert f"traffic_bytes decode_mfma_kernel {b} {digests['decode_mfma_kernel']}" in text
     assert "SQ_WAVES" in text and "2048" in text
+
+
+def test_compact_bytes():
+    """Two sequences, H = 2, d = 64 bf16 with metadata: every alpha of the
+    range read once, moved entries read and written whole, nulls written to
+    the end of the new last page, the range's page ids and three int32 per
+    sequence."""
+    c = types.SimpleNamespace(dtype="bf16", H_kv=2, d=64, B=2, entry_start=np.array([3, 16], np.int32))
+    table = np.array([[0, 1], [2, 3]], np.int32)
+    null = np.zeros((4, 2, 16), bool)
+    # sequence 0, range [3, 20): head 0 nulls at 5 and 17, head 1 none
+    null[0, 0, 5] = True
+    null[1, 0, 1] = True
+    # sequence 1, range [16, 24): head 0 all null, head 1 null at 16 only
+    null[3, 0, :8] = True
+    null[3, 1, 0] = True
+    lengths = np.array([20, 24], np.int32)
+    new = np.array([20, 23], np.int32)           # head 1 keeps all 17 / head 1 keeps 7
+    entry = (2 * 64 + 2) * 2 + 16
+    # seq 0: head 0 moves 6..16 (11 entries) and 18, 19 (2): 13 moves; live 15, pad 3+15..32 -> 14 nulls
+    #        head 1: nothing moves, pad 20..32 -> 12 nulls
+    s0 = 2 * 17 * 2 + 4 * 2 + 2 * entry * 13 + entry * (32 - 18) + entry * (32 - 20)
+    # seq 1: head 0: no live entries, pad 16..32 -> 16 nulls; head 1: 7 moves, pad 23..32 -> 9 nulls
+    s1 = 2 * 8 * 2 + 4 * 1 + entry * 16 + 2 * entry * 7 + entry * 9
+    assert bench.compact_alg_bytes(c, table, null, lengths, new) == s0 + s1 + 12 * 2
