@@ -26,10 +26,11 @@
 //                  branch-free in double precision (mask as a 0/1 weight) and
 //                  the macro-node is staged at the segment end.  Bound by
 //                  reading K and V from HBM.
-//   coarsen_cpoint every entry of a sequence in one index space (staged
-//                  macro-nodes, listed C-points with the key rotated to the
-//                  token's position, null padding), spread over its 1280
-//                  resident workgroups, one entry per 16-lane group at a time.
+//     The plan workgroups then place the C-points they listed (key rotated
+//     to the token's position) and each head's null padding while the
+//     streaming role is still running.
+//   coarsen_cpoint the staged macro-nodes of every sequence, one per 16-lane
+//                  group, copied to the entries the plan gave them.
 // Variants of the streaming role: the diagonal closure (per-dimension
 // variances of the rotated member keys, when the cache has that sidecar) and
 // variation-weighted representatives (per-token weights, from
@@ -40,6 +41,8 @@
 // so the mean is one correctly rounded division, as in a sequential sum, and
 // the variance sum (k^2) - (sum k)^2 / m is zero for a segment of identical
 // keys.  Every stored value is rounded once, to nearest-even.
+#include <algorithm>
+
 #include "launch.h"
 #include "spicy_device.h"
 
@@ -55,10 +58,9 @@ constexpr int kRing = 3;
 // streaming workgroups: twice the 512 that coarsen_main's register use fits
 // at once (2 of 4 waves per CU); the later ones start as earlier ones finish
 constexpr int kResidentBlocks = 1024;
-// coarsen_cpoint's register use allows 5 waves per SIMD: 5 workgroups of 4
-// waves per CU, 1280 on the chip.  A grid of exactly that many runs in one
-// round (measured: 1024 or 2048 workgroups are 2-4 us slower).
-constexpr int kCpointResident = 1280;
+// coarsen_cpoint's register use allows 8 waves per SIMD: 8 workgroups of 4
+// waves per CU, 2048 on the chip; its grid stays within one such round.
+constexpr int kCpointResident = 2048;
 constexpr int32_t kWindow = 65536;      // tokens per buffer resource (< 4 GiB)
 
 struct Meta {
@@ -263,11 +265,25 @@ __device__ __forceinline__ void load_round(const CoarsenArgs& a, int32_t tb, int
     for (int u = 0; u < kRound; ++u) w[u] = row_bits<NQ>(a, max(min(tb + u, last), 0));
 }
 
+template <typename T, int D>
+__device__ __forceinline__ void place_listed(const CoarsenArgs& a, int b, int32_t t0, int32_t t1, int64_t pos_off,
+                                             const int2* items, int32_t n_cp, int64_t padded);
+
 // One workgroup plans sequence b: per segment (one thread each) the
 // protected tokens of every head, block scans into entry and item offsets,
 // descriptors, and the C-point items in position order per head.
+// What placing the listed entries needs from the plan (ok false: the
+// sequence failed its checks and gets nothing).
+struct PlanOut {
+    bool ok;
+    int32_t t0, t1;
+    int32_t n_cp;
+    int64_t padded;
+};
+
 template <typename T, int D, int NQ>
-__device__ __forceinline__ void plan_sequence(const CoarsenArgs& a, int32_t (*s_wave)[kPlanWaves], int32_t& s_ok) {
+__device__ __forceinline__ void plan_sequence(const CoarsenArgs& a, int32_t (*s_wave)[kPlanWaves], int32_t& s_ok,
+                                              PlanOut& out) {
     constexpr int NH = NQ > 0 ? 4 * NQ : kMaxH;      // heads a mask row can hold
     constexpr int kRound = NQ > 0 ? 64 / NQ : 8;     // mask rows in flight per thread
     const int b = blockIdx.x;
@@ -382,7 +398,13 @@ __device__ __forceinline__ void plan_sequence(const CoarsenArgs& a, int32_t (*s_
         if (s < s1) {
 #pragma unroll
             for (int h = 0; h < NH; ++h)
-                if (h < H) a.seg_head[static_cast<int64_t>(s) * H + h] = make_int2(first[h], has_f[h]);
+                if (h < H) {
+                    // the macro-node's physical page, resolved here so that
+                    // placing it needs no table lookup (-1: none, or an
+                    // entry the table cannot hold, reported here)
+                    const int32_t Pg = has_f[h] ? entry_page(a, b, first[h]) : -1;
+                    a.seg_head[static_cast<int64_t>(s) * H + h] = make_int2(first[h], Pg);
+                }
             // the segment's C-point items, in position order within each head
             int nxt[NH];
 #pragma unroll
@@ -430,20 +452,35 @@ __device__ __forceinline__ void plan_sequence(const CoarsenArgs& a, int32_t (*s_
 #pragma unroll
     for (int h = 0; h < NH; ++h)
         if (h < H && tid == h) a.null_from[static_cast<int64_t>(b) * H + h] = e0 + carry[h];
+    out.ok = true;
+    out.t0 = t0;
+    out.t1 = t1;
+    out.n_cp = carry[kMaxH];
+    out.padded = padded;
 }
 
 template <typename T, int D>
 __device__ __forceinline__ void plan_role(const CoarsenArgs& a) {
     __shared__ int32_t s_wave[kMaxH + 1][kPlanWaves];
     __shared__ int32_t s_ok;
+    PlanOut out{false, 0, 0, 0, 0};
     // mask rows read as H / 4 dwords when H is a multiple of 4, else as bytes
     switch (a.cache.H % 4 == 0 ? a.cache.H / 4 : 0) {
-    case 1: plan_sequence<T, D, 1>(a, s_wave, s_ok); break;
-    case 2: plan_sequence<T, D, 2>(a, s_wave, s_ok); break;
-    case 3: plan_sequence<T, D, 3>(a, s_wave, s_ok); break;
-    case 4: plan_sequence<T, D, 4>(a, s_wave, s_ok); break;
-    default: plan_sequence<T, D, 0>(a, s_wave, s_ok); break;
+    case 1: plan_sequence<T, D, 1>(a, s_wave, s_ok, out); break;
+    case 2: plan_sequence<T, D, 2>(a, s_wave, s_ok, out); break;
+    case 3: plan_sequence<T, D, 3>(a, s_wave, s_ok, out); break;
+    case 4: plan_sequence<T, D, 4>(a, s_wave, s_ok, out); break;
+    default: plan_sequence<T, D, 0>(a, s_wave, s_ok, out); break;
     }
+    if (!out.ok) return;                               // the same for the whole workgroup
+    // the listed C-points and the null padding are placed now, while the
+    // streaming role runs (they need nothing from it); every thread's items
+    // and null starts are visible to the workgroup after the barrier
+    __syncthreads();
+    const int b = blockIdx.x;
+    const int64_t pos_off = static_cast<int64_t>(a.pos_base ? a.pos_base[b] : 0) - out.t0;
+    place_listed<T, D>(a, b, out.t0, out.t1, pos_off, a.cp_items + static_cast<int64_t>(out.t0) * a.cache.H,
+                       out.n_cp, out.padded);
 }
 
 // ---------------------------------------------------------- main + C-points
@@ -736,23 +773,13 @@ __global__ __launch_bounds__(256, 2) void coarsen_main_kernel(CoarsenArgs a) {
         stream_segment<T, D, DIAG, WEIGHTED>(a, L, s);
 }
 
-// coarsen_cpoint: places every entry of sequence b, spread over workgroups
-// (x, b) and their 16-lane groups (8 at d = 64).  The sequence's entries form
-// one index space walked with a grid stride, so each group pays one chain of
-// dependent reads per entry whatever its kind:
-//   [0, n_mac)              the staged macro-nodes, unit (head, segment), at
-//                           the entry the plan gave them;
-//   [n_mac, n_mac + n_cp)   the C-point items {token, entry, head} the plan
-//                           listed, stored exact (value bits copied, key
-//                           rotated to the token's own position,
-//                           alpha = beta = 0);
-//   [.., + n_null)          the null entries: each head from its own end up
-//                           to the end of the sequence's last page
-//                           (k = v = 0, alpha = -inf, beta = 0).
-// u runs head-major (the segments of head 0, then head 1, ...): the groups of
-// a wavefront take consecutive segments of one head, whose entries are mostly
-// consecutive slots, so their 16-byte pieces of each 8-dim group of the page
-// land side by side.
+// Placing entries.  The plan role places the C-points it listed and each
+// head's null padding (place_listed, below) while the streaming role runs;
+// coarsen_cpoint then places the staged macro-nodes, spread over workgroups
+// (x, b) and their 16-lane groups (8 at d = 64), unit u = (head, segment)
+// head-major: the groups of a wavefront take consecutive segments of one
+// head, whose entries are mostly consecutive slots, so their 16-byte pieces
+// of each 8-dim group of the page land side by side.
 template <typename T, int D>
 __device__ __forceinline__ void place_macro(const CoarsenArgs& a, int b, int32_t s0, int32_t nseg, int64_t u, int d0,
                                             int j) {
@@ -769,13 +796,12 @@ __device__ __forceinline__ void place_macro(const CoarsenArgs& a, int b, int32_t
     vx.load(static_cast<const T*>(a.stage_v) + idx * D + d0);
     if (a.cache.s2) sx.load(static_cast<const T*>(a.stage_s2) + idx * D + d0);
     if (owner != b) return;                             // sequence failed its checks
-    if (!(hd.y & 1)) return;                            // no F-token in this head
+    const int32_t Pg = hd.y;                            // -1: no F-token in this head, or no page
+    if (Pg < 0) return;
     if (mt.y != b || mt.x <= 0) {
         raise_err(a.err, SPICY_DEVERR_SEGMENTS);
         return;
     }
-    const int32_t Pg = entry_page(a, b, hd.x);
-    if (Pg < 0) return;
     const int slot = hd.x % kPage;
     const int64_t ph = static_cast<int64_t>(Pg) * H + h;
     Store8<T>::store(static_cast<T*>(a.cache.k) + ph * kPage * D + slot_elem(slot, d0),
@@ -798,26 +824,44 @@ __device__ __forceinline__ void place_macro(const CoarsenArgs& a, int b, int32_t
     }
 }
 
+// A listed C-point {token, entry << 4 | head}: its rows and page are loaded
+// by cp_fetch (indexes clamped, so a bad item never reads out of bounds) and
+// stored exact by cp_store (value bits copied, key rotated to the token's own
+// position, alpha = beta = 0).
+template <typename T>
+struct CpFetch {
+    Row8<T> kx, vx;
+    int32_t Pg;            // -1: nothing to store
+    int32_t t;
+    int h;
+    int64_t e;
+};
+
 template <typename T, int D>
-__device__ __forceinline__ void place_cpoint(const CoarsenArgs& a, int b, int2 it, int32_t t0, int32_t t1,
-                                             int64_t pos_off, const double (&theta)[4], int d0, int j) {
+__device__ __forceinline__ CpFetch<T> cp_fetch(const CoarsenArgs& a, int b, int2 it, int32_t t0, int32_t t1, int d0) {
+    const int H = a.cache.H;
+    CpFetch<T> f;
+    f.t = it.x;
+    f.h = it.y & 15;
+    f.e = static_cast<uint32_t>(it.y) >> 4;
+    const bool sane = f.t >= t0 && f.t < t1 && f.h < H;
+    const int64_t base = (static_cast<int64_t>(min(max(f.t, t0), t1 - 1)) * H + min(f.h, H - 1)) * D + d0;
+    f.kx.load(static_cast<const T*>(a.k_pre) + base);
+    f.vx.load(static_cast<const T*>(a.v) + base);
+    if (!sane) raise_err(a.err, SPICY_DEVERR_SEGMENTS);
+    f.Pg = sane ? entry_page(a, b, f.e) : -1;
+    return f;
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void cp_store(const CoarsenArgs& a, const CpFetch<T>& f, int64_t pos_off,
+                                         const double (&theta)[4], int d0, int j) {
     constexpr int PARTNER = D / 16;
     const int H = a.cache.H;
     const bool hi_half = j >= PARTNER;
-    // indexes are clamped so a bad list never reads out of bounds
-    const int32_t t = it.x;
-    const int h = it.y & 15;
-    const int64_t e = static_cast<uint32_t>(it.y) >> 4;
-    const bool sane = t >= t0 && t < t1 && h < H;
-    const int64_t base = (static_cast<int64_t>(min(max(t, t0), t1 - 1)) * H + min(h, H - 1)) * D + d0;
-    Row8<T> kx, vx;
-    kx.load(static_cast<const T*>(a.k_pre) + base);
-    vx.load(static_cast<const T*>(a.v) + base);
-    if (!sane) raise_err(a.err, SPICY_DEVERR_SEGMENTS);
-    const int32_t Pg = sane ? entry_page(a, b, e) : -1;
     double y[8];
     if (a.rope_base > 0.0) {
-        const double pos = static_cast<double>(t + pos_off);
+        const double pos = static_cast<double>(f.t + pos_off);
         double c4[4], s4[4], cs[8], sn[8];
 #pragma unroll
         for (int r = 0; r < 4; ++r) sincos_f64(pos * theta[r], &s4[r], &c4[r]);
@@ -832,27 +876,27 @@ __device__ __forceinline__ void place_cpoint(const CoarsenArgs& a, int b, int2 i
         }
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            const double x = kx.f64(r);
+            const double x = f.kx.f64(r);
             const double other = __shfl_xor(x, PARTNER);
             y[r] = hi_half ? x * cs[r] + other * sn[r] : x * cs[r] - other * sn[r];
         }
     } else {
 #pragma unroll
-        for (int r = 0; r < 8; ++r) y[r] = kx.f64(r);
+        for (int r = 0; r < 8; ++r) y[r] = f.kx.f64(r);
     }
-    if (Pg < 0) return;
-    const int slot = static_cast<int>(e % kPage);
-    const int64_t ph = static_cast<int64_t>(Pg) * H + h;
+    if (f.Pg < 0) return;
+    const int slot = static_cast<int>(f.e % kPage);
+    const int64_t ph = static_cast<int64_t>(f.Pg) * H + f.h;
     Pack8<T>::store(static_cast<T*>(a.cache.k) + ph * kPage * D + slot_elem(slot, d0), y);
     Store8<T>::store(static_cast<T*>(a.cache.v) + ph * kPage * D + slot_elem(slot, d0),
-                     [&](int r) { return vx.raw(r); });
+                     [&](int r) { return f.vx.raw(r); });
     const double zero[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (a.cache.s2) Pack8<T>::store(static_cast<T*>(a.cache.s2) + ph * kPage * D + slot_elem(slot, d0), zero);
     if (j == 0) {
         T* abc = static_cast<T*>(a.cache.ab);
         abc[(ph * kPage + slot) * 2 + 0] = Elem<T>::from_f32(0.f);
         abc[(ph * kPage + slot) * 2 + 1] = Elem<T>::from_f32(0.f);
-        if (a.cache.meta) static_cast<Meta*>(a.cache.meta)[ph * kPage + slot] = Meta{1, 1, t + pos_off};
+        if (a.cache.meta) static_cast<Meta*>(a.cache.meta)[ph * kPage + slot] = Meta{1, 1, f.t + pos_off};
     }
 }
 
@@ -875,32 +919,22 @@ __device__ __forceinline__ void place_null(const CoarsenArgs& a, int b, int h, i
     }
 }
 
+// The plan workgroup of sequence b places its n_cp listed C-points, a batch
+// of kCpBatch per 16-lane group (8 at d = 64) with every load of the batch
+// issued before any store, then each head's nulls from its own end up to
+// `padded` (the end of the sequence's last page).
+constexpr int kCpBatch = 4;
+
 template <typename T, int D>
-__global__ __launch_bounds__(256) void coarsen_cpoint_kernel(CoarsenArgs a) {
+__device__ __forceinline__ void place_listed(const CoarsenArgs& a, int b, int32_t t0, int32_t t1, int64_t pos_off,
+                                             const int2* items, int32_t n_cp, int64_t padded) {
     constexpr int LPH = D / 8;                // lanes per item
     constexpr int IPW = kWave / LPH;          // items per wavefront step
+    constexpr int NG = kPlanWaves * IPW;      // groups of the workgroup
     constexpr int PARTNER = LPH / 2;
-    const int b = blockIdx.y;
     const int H = a.cache.H;
-    // the sequence's bounds: independent reads, issued together
-    const int32_t t0 = a.seq_offsets[b], t1 = a.seq_offsets[b + 1];
-    const int32_t s0 = a.seq_seg_ptr[b], s1 = a.seq_seg_ptr[b + 1];
-    int32_t n_cp = a.cp_count[b];
-    const int64_t len = a.lengths_out[b];
-    const int64_t pos_off = static_cast<int64_t>(a.pos_base ? a.pos_base[b] : 0) - t0;
-    const int64_t padded = (len + kPage - 1) / kPage * kPage;
-    int64_t n_null = 0;
-    for (int h = 0; h < H; ++h) {
-        const int64_t c = padded - a.null_from[static_cast<int64_t>(b) * H + h];
-        n_null += c > 0 ? c : 0;
-    }
-    if (n_cp < 0 || t0 < 0 || t0 > t1 || t1 > a.total_tokens || n_cp > static_cast<int64_t>(t1 - t0) * H) n_cp = 0;
-    const int64_t n_mac = (0 <= s0 && s0 <= s1 && s1 <= a.n_seg) ? static_cast<int64_t>(s1 - s0) * H : 0;
-    const int64_t n_all = n_mac + n_cp + n_null;
-
     const int lane = threadIdx.x % kWave;
     const int grp = (threadIdx.x / kWave) * IPW + lane / LPH;
-    const int ngrp = (blockDim.x / kWave) * IPW;
     const int j = lane % LPH;
     const int d0 = 8 * j;
     double theta[4];
@@ -910,29 +944,62 @@ __global__ __launch_bounds__(256) void coarsen_cpoint_kernel(CoarsenArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) theta[r] = a.theta[pair0 + r];
     }
-    const int2* items = a.cp_items + static_cast<int64_t>(t0) * H;
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * ngrp;
-    for (int64_t u = static_cast<int64_t>(blockIdx.x) * ngrp + grp; u < n_all; u += stride) {
-        if (u < n_mac) {
-            place_macro<T, D>(a, b, s0, s1 - s0, u, d0, j);
-        } else if (u < n_mac + n_cp) {
-            place_cpoint<T, D>(a, b, items[u - n_mac], t0, t1, pos_off, theta, d0, j);
-        } else {
-            int64_t rem = u - n_mac - n_cp, e = 0;
-            int h = 0;
-            for (int q = 0; q < H; ++q) {
-                const int64_t nf = a.null_from[static_cast<int64_t>(b) * H + q];
-                const int64_t cnt = padded - nf > 0 ? padded - nf : 0;
-                if (rem < cnt) {
-                    h = q;
-                    e = nf + rem;
-                    break;
-                }
-                rem -= cnt;
-            }
-            place_null<T, D>(a, b, h, e, d0, j);
+    for (int32_t k0 = 0; k0 < n_cp; k0 += kCpBatch * NG) {
+        int2 it[kCpBatch];
+#pragma unroll
+        for (int i = 0; i < kCpBatch; ++i) {
+            const int32_t k = k0 + i * NG + grp;
+            it[i] = k < n_cp ? items[k] : make_int2(t0, 0);
+        }
+        CpFetch<T> f[kCpBatch];
+#pragma unroll
+        for (int i = 0; i < kCpBatch; ++i) f[i] = cp_fetch<T, D>(a, b, it[i], t0, t1, d0);
+#pragma unroll
+        for (int i = 0; i < kCpBatch; ++i) {
+            if (k0 + i * NG + grp >= n_cp) f[i].Pg = -1;       // past the list: nothing to store
+            cp_store<T, D>(a, f[i], pos_off, theta, d0, j);
         }
     }
+    int64_t n_null = 0;
+    for (int h = 0; h < H; ++h) {
+        const int64_t c = padded - a.null_from[static_cast<int64_t>(b) * H + h];
+        n_null += c > 0 ? c : 0;
+    }
+    for (int64_t u = grp; u < n_null; u += NG) {
+        int64_t rem = u, e = 0;
+        int h = 0;
+        for (int q = 0; q < H; ++q) {
+            const int64_t nf = a.null_from[static_cast<int64_t>(b) * H + q];
+            const int64_t cnt = padded - nf > 0 ? padded - nf : 0;
+            if (rem < cnt) {
+                h = q;
+                e = nf + rem;
+                break;
+            }
+            rem -= cnt;
+        }
+        place_null<T, D>(a, b, h, e, d0, j);
+    }
+}
+
+// coarsen_cpoint: the staged macro-nodes of sequence b, unit u = (head,
+// segment) with a grid stride over the workgroups (x, b).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void coarsen_cpoint_kernel(CoarsenArgs a) {
+    constexpr int LPH = D / 8;                // lanes per item
+    constexpr int IPW = kWave / LPH;          // items per wavefront step
+    const int b = blockIdx.y;
+    const int H = a.cache.H;
+    const int32_t s0 = a.seq_seg_ptr[b], s1 = a.seq_seg_ptr[b + 1];
+    const int64_t n_mac = (0 <= s0 && s0 <= s1 && s1 <= a.n_seg) ? static_cast<int64_t>(s1 - s0) * H : 0;
+    const int lane = threadIdx.x % kWave;
+    const int grp = (threadIdx.x / kWave) * IPW + lane / LPH;
+    const int ngrp = (blockDim.x / kWave) * IPW;
+    const int j = lane % LPH;
+    const int d0 = 8 * j;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * ngrp;
+    for (int64_t u = static_cast<int64_t>(blockIdx.x) * ngrp + grp; u < n_mac; u += stride)
+        place_macro<T, D>(a, b, s0, s1 - s0, u, d0, j);
 }
 
 // ------------------------------------------------------------------ launch
@@ -955,7 +1022,12 @@ spicy_status launch_coarsen_t(const CoarsenArgs& a, hipStream_t stream) {
         hipLaunchKernelGGL((coarsen_main_kernel<T, D, false, false>), grid, block, 0, stream, a);
     if (hipGetLastError() != hipSuccess) return SPICY_ERR_HIP;
     // entries: the resident workgroups shared by the sequences
-    const int cx = max(1, min(kCpointBlocksPerSeq, kCpointResident / max(a.B, 1)));
+    // macro-nodes: about n_seg * H / B per sequence, one per 16-lane group
+    // (16 groups per workgroup at d = 128, 32 at d = 64)
+    const int per_wg = 4 * (kWave / (D / 8));
+    const int64_t want = (static_cast<int64_t>(a.n_seg) * a.cache.H / std::max(a.B, 1) + per_wg - 1) / per_wg;
+    const int64_t cap = std::min(kCpointBlocksPerSeq, kCpointResident / std::max(a.B, 1));
+    const int cx = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(want, cap)));
     hipLaunchKernelGGL((coarsen_cpoint_kernel<T, D>), dim3(cx, a.B), dim3(256), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return SPICY_ERR_HIP;
     return SPICY_OK;

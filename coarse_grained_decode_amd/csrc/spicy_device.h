@@ -167,7 +167,7 @@ struct CoarsenArgs {
     int32_t* lengths_out;
     int32_t* err;          // workspace header word
     int4* seg_desc;        // [n_seg]     {sequence (-1 = skip), first token, end token, position offset}
-    int2* seg_head;        // [n_seg][H]  {first entry of the segment, has a macro-node}
+    int2* seg_head;        // [n_seg][H]  {first entry of the segment, physical page of its macro-node (-1: none)}
     int2* cp_items;        // C-points of sequence b at [seq_offsets[b] * H, + cp_count[b]):
                            //   {token, entry << 4 | head}
     int32_t* cp_count;     // [B]
