@@ -9,15 +9,15 @@ in the GPU kernels and in the oracle.
 What the generator decides is the cache *policy*, which the pages leave to the
 caller of the coarsening step:
 
-* sink and recent tokens stay exact (SPICY-KV demo page, section 1:
-  ``protect_sink_tokens=8, protect_recent_tokens=48``);
+* sink and recent tokens stay exact (SPICY-KV demo page, section 1: its
+  configuration protects 8 sink and 48 recent tokens);
 * "landmark" tokens stay exact (SPICY-KV demo page, Claim 2: C-points); we pick
   the top fraction of tokens by key norm per (sequence, KV head);
 * segments: a fixed grid, a two-level dyadic grid sized to hit the target
-  compression ratio (SPICY-KV title: "dYadic"; Claim 1 (c): "one or more
-  resolution scales"), or equal-variation boundaries (Equal-Variation KV Cache
-  page, "Implementation notes": thresholds q_j = j c_T / N, boundary at the first
-  token whose cumulative variation crosses the next threshold).
+  compression ratio (SPICY-KV title: dyadic renormalization; Claim 1 (c): the
+  coarsening at one or several resolution scales), or equal-variation boundaries (Equal-Variation KV Cache
+  page, implementation notes: the total variation is cut into N equal shares,
+  and each segment ends where the running variation reaches its share).
 
 Seeds: workload ``c`` draws from ``numpy.random.Generator(PCG64(SeedSequence(1000 + c)))``
 children, one child stream per role.  Data are drawn in float32 and, for bf16
