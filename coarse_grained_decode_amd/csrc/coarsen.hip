@@ -84,22 +84,6 @@ __device__ __forceinline__ int32_t entry_page(const CoarsenArgs& a, int b, int64
     return P;
 }
 
-// The value of lane (this lane xor P) through DPP moves (VALU only, no LDS
-// round trip): P = 8 is a rotation by 8 inside each 16-lane row; P = 4 is a
-// reversal inside each quad (lane xor 3) followed by a mirror inside each
-// half-row of 8 (lane xor 7).
-template <int P>
-__device__ __forceinline__ uint32_t dpp_xor(uint32_t v) {
-    static_assert(P == 4 || P == 8, "lane distance");
-    const int x = static_cast<int>(v);
-    if constexpr (P == 8) {
-        return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false));    // row_ror:8
-    } else {
-        const int r = __builtin_amdgcn_mov_dpp(x, 0x1B, 0xF, 0xF, false);                      // quad_perm [3,2,1,0]
-        return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(r, 0x141, 0xF, 0xF, false));     // row_half_mirror
-    }
-}
-
 // 8 consecutive elements of one row: a 16-byte (bf16) or 32-byte (fp32) load
 template <typename T> struct Row8;
 template <> struct Row8<uint16_t> {

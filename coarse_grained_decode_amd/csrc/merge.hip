@@ -16,14 +16,20 @@
 // and the second entry becomes a null.  Everything in double precision,
 // rounded once on store.  The sequence lengths do not change.
 //
-// Two kernels:
-//   merge_list  one wavefront per (sequence, head): reads the entry kinds 64
-//               at a time (one ballot), pairs the macro-nodes in order with
-//               a carried odd one, and lists the pairs in the workspace.
+// Two kernels, 4 wavefronts per workgroup:
+//   merge_list  one workgroup per (sequence, head) walks its range in windows
+//               of 1024 entries: page ids and entry kinds are read (one entry
+//               per thread per round, every load of the window in flight
+//               together), a workgroup scan ranks the macro-nodes, and pair i
+//               (macro-nodes 2i and 2i + 1 of the range, the odd one of a
+//               window carried into the next) is written to the workspace
+//               with both entries and both pages.  The whole range is listed
+//               before any pair merges: merging turns entries into nulls.
 //   merge_pair  workgroups (x, sequence * H + head); every 16-lane group (8
-//               at d = 64) merges one listed pair per round, a lane owning 8
-//               dims as in the coarsening; the rounds of a wavefront are
-//               uniform so that the rotary-partner shuffles see every lane.
+//               at d = 64) takes its pairs two at a time, both pairs' rows
+//               loaded before either is computed (the pages come with the
+//               pair, so the rows are the only dependent reads), a lane
+//               owning 8 dims as in the coarsening.
 #include "launch.h"
 #include "spicy_device.h"
 
@@ -31,8 +37,10 @@ namespace spicy {
 
 namespace {
 
-constexpr int kListWaves = 4;
-constexpr int kResident = 1024;
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kWin = 1024;                  // entries listed per window
+constexpr int kResident = 512;              // merge_pair workgroups resident at once (2 per CU)
 
 struct MetaRec {
     int32_t kind;
@@ -54,68 +62,6 @@ __device__ __forceinline__ int32_t page_of(const MergeArgs& a, int b, int64_t e)
         return -1;
     }
     return P;
-}
-
-__global__ __launch_bounds__(kListWaves * kWave) void merge_list_kernel(MergeArgs a) {
-    const int lane = threadIdx.x % kWave;
-    const int H = a.cache.H;
-    const int64_t unit = static_cast<int64_t>(blockIdx.x) * kListWaves + threadIdx.x / kWave;
-    if (unit >= static_cast<int64_t>(a.B) * H) return;
-    const int b = static_cast<int>(unit / H);
-    const int h = static_cast<int>(unit % H);
-    const int32_t e0 = a.entry_begin[b], e1 = a.entry_end[b];
-    int32_t npairs = 0;
-    if (e0 < 0 || e0 > e1 || e1 - e0 > a.max_range) {
-        if (lane == 0) {
-            raise_err(a.err, SPICY_DEVERR_SEGMENTS);
-            a.pair_count[unit] = 0;
-        }
-        return;
-    }
-    const MetaRec* meta = static_cast<const MetaRec*>(a.cache.meta);
-    int2* out = a.pairs + unit * a.cap;
-    int32_t carry = -1;                                  // the unpaired macro-node so far (uniform)
-    // kBatch windows of 64 entries at a time: their page ids, then their
-    // kinds, are requested together before the windows are paired in order
-    constexpr int kBatch = 4;
-    for (int32_t base0 = e0; base0 < e1; base0 += kBatch * kWave) {
-        int32_t pg[kBatch];
-        int32_t kind[kBatch];
-#pragma unroll
-        for (int w = 0; w < kBatch; ++w) {
-            const int32_t e = base0 + w * kWave + lane;
-            pg[w] = e < e1 ? page_of(a, b, e) : -1;
-        }
-#pragma unroll
-        for (int w = 0; w < kBatch; ++w) {
-            const int32_t e = base0 + w * kWave + lane;
-            kind[w] = pg[w] >= 0 ? meta[(static_cast<int64_t>(pg[w]) * H + h) * kPage + e % kPage].kind : 0;
-        }
-#pragma unroll
-        for (int w = 0; w < kBatch; ++w) {
-            const int32_t base = base0 + w * kWave;
-            const int32_t e = base + lane;
-            const bool mac = kind[w] == 2;
-            const uint64_t M = __ballot(mac);
-            const int c = carry >= 0 ? 1 : 0;
-            const int n = __popcll(M);
-            if (mac) {
-                const int r = __popcll(M & ((1ull << lane) - 1));   // rank among this window's macro-nodes
-                const int p = c + r;                                 // place in the sequence carry, m_0, m_1, ...
-                if (p & 1) {
-                    const uint64_t below = M & ((1ull << lane) - 1);
-                    const int32_t first = (r == 0) ? carry : base + (63 - __clzll(below));
-                    const int32_t j = npairs + (p >> 1);
-                    if (j < a.cap) out[j] = make_int2(first, e);
-                    else raise_err(a.err, SPICY_DEVERR_CAPACITY);
-                }
-            }
-            npairs += (c + n) >> 1;
-            if ((c + n) & 1) carry = n > 0 ? base + (63 - __clzll(M)) : carry;
-            else carry = -1;
-        }
-    }
-    if (lane == 0) a.pair_count[unit] = npairs < a.cap ? npairs : a.cap;
 }
 
 // 8 consecutive elements of a row as doubles, and back (one rounding).
@@ -154,35 +100,101 @@ template <> struct Vec8<float> {
     }
 };
 
-template <typename T, int D>
-__global__ __launch_bounds__(256) void merge_pair_kernel(MergeArgs a) {
-    constexpr int LPH = D / 8;                // lanes per pair
-    constexpr int PPW = kWave / LPH;          // pairs per wavefront round
-    constexpr int PARTNER = LPH / 2;          // lane distance to the rotary partner
-    const int H = a.cache.H;
-    const int64_t unit = blockIdx.y;          // sequence * H + head
-    const int b = static_cast<int>(unit / H);
-    const int h = static_cast<int>(unit % H);
-    const int lane = threadIdx.x % kWave;
-    const int j = lane % LPH;
-    const int d0 = 8 * j;
-    const bool hi_half = j >= PARTNER;
-    const int wave_grp = (threadIdx.x / kWave) * PPW;
-    const int ngrp = (blockDim.x / kWave) * PPW;
-    const bool rotate = a.rope_base > 0.0;
-    double theta[4];
-    {
-        const int pair0 = 8 * (hi_half ? j - PARTNER : j) + (hi_half ? 4 : 0);
+// 8 consecutive elements of a row as stored (converted to double when used).
+template <typename T> struct Raw8;
+template <> struct Raw8<uint16_t> {
+    uint4 x;
+    __device__ __forceinline__ void load(const uint16_t* p) { x = *reinterpret_cast<const uint4*>(p); }
+    __device__ __forceinline__ void zero() { x = make_uint4(0u, 0u, 0u, 0u); }
+    __device__ __forceinline__ void f64(double (&y)[8]) const {
+        const uint32_t u[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) theta[r] = a.theta[pair0 + r];
+        for (int i = 0; i < 4; ++i) {
+            y[2 * i] = static_cast<double>(__uint_as_float(u[i] << 16));
+            y[2 * i + 1] = static_cast<double>(__uint_as_float(u[i] & 0xFFFF0000u));
+        }
     }
+};
+template <> struct Raw8<float> {
+    float4 lo, hi;
+    __device__ __forceinline__ void load(const float* p) {
+        lo = *reinterpret_cast<const float4*>(p);
+        hi = *reinterpret_cast<const float4*>(p + 4);
+    }
+    __device__ __forceinline__ void zero() { lo = hi = make_float4(0.f, 0.f, 0.f, 0.f); }
+    __device__ __forceinline__ void f64(double (&y)[8]) const {
+        y[0] = lo.x; y[1] = lo.y; y[2] = lo.z; y[3] = lo.w;
+        y[4] = hi.x; y[5] = hi.y; y[6] = hi.z; y[7] = hi.w;
+    }
+};
+
+// One listed pair's inputs, loaded by pair_load and merged by pair_store.
+template <typename T>
+struct PairIn {
+    Raw8<T> k1, k2, v1, v2;
+    T b1, b2;
+    MetaRec r1, r2;
+    int64_t ph1, ph2;
+    int s1, s2;
+    bool ok;
+};
+
+template <typename T, int D>
+__device__ __forceinline__ void pair_load(const MergeArgs& a, int h, bool live, int32_t e1, int32_t P1, int32_t e2,
+                                          int32_t P2, int d0, PairIn<T>& in) {
+    const int H = a.cache.H;
+    in.ok = live && P1 >= 0 && P2 >= 0;
+    in.ph1 = static_cast<int64_t>(in.ok ? P1 : 0) * H + h;
+    in.ph2 = static_cast<int64_t>(in.ok ? P2 : 0) * H + h;
+    in.s1 = e1 % kPage;
+    in.s2 = e2 % kPage;
+    in.b1 = in.b2 = T(0);
+    in.r1 = in.r2 = MetaRec{0, 0, 0};
+    if (in.ok) {
+        const T* kp = static_cast<const T*>(a.cache.k);
+        const T* vp = static_cast<const T*>(a.cache.v);
+        const T* ab = static_cast<const T*>(a.cache.ab);
+        const MetaRec* meta = static_cast<const MetaRec*>(a.cache.meta);
+        in.k1.load(kp + in.ph1 * kPage * D + slot_elem(in.s1, d0));
+        in.k2.load(kp + in.ph2 * kPage * D + slot_elem(in.s2, d0));
+        in.v1.load(vp + in.ph1 * kPage * D + slot_elem(in.s1, d0));
+        in.v2.load(vp + in.ph2 * kPage * D + slot_elem(in.s2, d0));
+        in.b1 = ab[(in.ph1 * kPage + in.s1) * 2 + 1];
+        in.b2 = ab[(in.ph2 * kPage + in.s2) * 2 + 1];
+        in.r1 = meta[in.ph1 * kPage + in.s1];
+        in.r2 = meta[in.ph2 * kPage + in.s2];
+    } else {
+        in.k1.zero();
+        in.k2.zero();
+        in.v1.zero();
+        in.v2.zero();
+    }
+}
+
+// The merge of one pair (every lane of the wavefront takes part in the
+// shuffles, live or not).
+template <typename T, int D>
+__device__ __forceinline__ void pair_store(const MergeArgs& a, const PairIn<T>& in, int j, bool hi_half,
+                                           bool rotate, const double (&theta)[4]) {
+    constexpr int LPH = D / 8;                // lanes per pair
+    constexpr int PARTNER = LPH / 2;          // lane distance to the rotary partner
+    int32_t i1 = in.r1.mass, i2 = in.r2.mass;
+    if (in.ok && (in.r1.kind != 2 || in.r2.kind != 2 || in.r1.mass <= 0 || in.r2.mass <= 0 ||
+                  static_cast<int64_t>(in.r1.mass) + in.r2.mass > 0x7FFFFFFF)) {
+        raise_err(a.err, SPICY_DEVERR_SEGMENTS);
+        i1 = i2 = 0;                                          // not stored
+    }
+    const double m1 = in.ok && i1 > 0 ? static_cast<double>(i1) : 1.0;
+    const double m2 = in.ok && i2 > 0 ? static_cast<double>(i2) : 1.0;
+    const int64_t q1 = in.ok ? in.r1.pos_sum : 0, q2 = in.ok ? in.r2.pos_sum : 0;
     // cos and sin at pos for the rotary pair of each of this lane's 8 dims
+    // (the partner's values through DPP lane moves)
     auto angles = [&](double pos, double (&cs)[8], double (&sn)[8]) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             double sq, cq;
             sincos_f64(pos * theta[q], &sq, &cq);
-            const double oc = __shfl_xor(cq, PARTNER), os = __shfl_xor(sq, PARTNER);
+            const double oc = dpp_xor_f64<PARTNER>(cq), os = dpp_xor_f64<PARTNER>(sq);
             cs[q] = hi_half ? oc : cq;
             sn[q] = hi_half ? os : sq;
             cs[4 + q] = hi_half ? cq : oc;
@@ -193,123 +205,205 @@ __global__ __launch_bounds__(256) void merge_pair_kernel(MergeArgs a) {
     auto rot = [&](const double (&x)[8], const double (&cs)[8], const double (&sn)[8], double (&y)[8]) {
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            const double ps = __shfl_xor(x[r], PARTNER) * sn[r];
+            const double ps = dpp_xor_f64<PARTNER>(x[r]) * sn[r];
             y[r] = hi_half ? x[r] * cs[r] + ps : x[r] * cs[r] - ps;
         }
     };
-
-    const int32_t count = a.pair_count[unit];
-    const int64_t start = static_cast<int64_t>(blockIdx.x) * ngrp;
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * ngrp;
-    const MetaRec* meta = static_cast<const MetaRec*>(a.cache.meta);
-    for (int64_t r0 = start; r0 < count; r0 += stride) {              // uniform over the workgroup
-        const int64_t pj = r0 + wave_grp + lane / LPH;
-        const bool live = pj < count;
-        int32_t P1 = -1, P2 = -1, e1 = 0, e2 = 0;
-        if (live) {
-            const int2 pr = a.pairs[unit * a.cap + pj];
-            e1 = pr.x;
-            e2 = pr.y;
-            P1 = page_of(a, b, e1);
-            P2 = page_of(a, b, e2);
-        }
-        const bool ok = live && P1 >= 0 && P2 >= 0;
-        const int64_t ph1 = static_cast<int64_t>(ok ? P1 : 0) * H + h, ph2 = static_cast<int64_t>(ok ? P2 : 0) * H + h;
-        const int s1 = e1 % kPage, s2 = e2 % kPage;
-        double k1[8], k2[8], v1[8], v2[8];
-        double m1 = 1.0, m2 = 1.0, b1 = 0.0, b2 = 0.0;
-        int64_t q1 = 0, q2 = 0;
-        int32_t i1 = 1, i2 = 1;
-        if (ok) {
-            const T* kp = static_cast<const T*>(a.cache.k);
-            const T* vp = static_cast<const T*>(a.cache.v);
-            const T* ab = static_cast<const T*>(a.cache.ab);
-            Vec8<T>::load(kp + ph1 * kPage * D + slot_elem(s1, d0), k1);
-            Vec8<T>::load(kp + ph2 * kPage * D + slot_elem(s2, d0), k2);
-            Vec8<T>::load(vp + ph1 * kPage * D + slot_elem(s1, d0), v1);
-            Vec8<T>::load(vp + ph2 * kPage * D + slot_elem(s2, d0), v2);
-            b1 = Elem<T>::to_f64(ab[(ph1 * kPage + s1) * 2 + 1]);
-            b2 = Elem<T>::to_f64(ab[(ph2 * kPage + s2) * 2 + 1]);
-            const MetaRec r1 = meta[ph1 * kPage + s1], r2 = meta[ph2 * kPage + s2];
-            i1 = r1.mass;
-            i2 = r2.mass;
-            q1 = r1.pos_sum;
-            q2 = r2.pos_sum;
-            if (r1.kind != 2 || r2.kind != 2 || r1.mass <= 0 || r2.mass <= 0 ||
-                static_cast<int64_t>(r1.mass) + r2.mass > 0x7FFFFFFF) {
-                raise_err(a.err, SPICY_DEVERR_SEGMENTS);
-                i1 = i2 = 0;                                  // not stored
-            }
-            m1 = i1 > 0 ? static_cast<double>(i1) : 1.0;
-            m2 = i2 > 0 ? static_cast<double>(i2) : 1.0;
-        } else {
-#pragma unroll
-            for (int r = 0; r < 8; ++r) k1[r] = k2[r] = v1[r] = v2[r] = 0.0;
-        }
-        const double m = m1 + m2;
-        const int64_t P = q1 + q2;
-        // R(tbar) mu = (m1 R(tbar - tbar_1) k1 + m2 R(tbar - tbar_2) k2) / m, and
-        // |mu_1 - mu_2| is the norm of the difference of the two rotated keys
-        // (rotations keep norms): two sets of angles instead of three
-        const double tb = static_cast<double>(P) / m;
-        double y1[8], y2[8], key[8], cs[8], sn[8];
-        if (rotate) {
-            angles(tb - static_cast<double>(q1) / m1, cs, sn);
-            rot(k1, cs, sn, y1);
-            angles(tb - static_cast<double>(q2) / m2, cs, sn);
-            rot(k2, cs, sn, y2);
-        } else {
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                y1[r] = k1[r];
-                y2[r] = k2[r];
-            }
-        }
-        double dist = 0.0;
+    const double m = m1 + m2;
+    const int64_t P = q1 + q2;
+    double k1[8], k2[8];
+    in.k1.f64(k1);
+    in.k2.f64(k2);
+    const double b1 = Elem<T>::to_f64(in.b1), b2 = Elem<T>::to_f64(in.b2);
+    // R(tbar) mu = (m1 R(tbar - tbar_1) k1 + m2 R(tbar - tbar_2) k2) / m, and
+    // |mu_1 - mu_2| is the norm of the difference of the two rotated keys
+    // (rotations keep norms): two sets of angles instead of three
+    const double tb = static_cast<double>(P) / m;
+    double y1[8], y2[8], key[8], val[8], cs[8], sn[8];
+    if (rotate) {
+        angles(tb - static_cast<double>(q1) / m1, cs, sn);
+        rot(k1, cs, sn, y1);
+        angles(tb - static_cast<double>(q2) / m2, cs, sn);
+        rot(k2, cs, sn, y2);
+    } else {
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            const double dm = y1[r] - y2[r];
-            dist += dm * dm;
-            key[r] = (m1 * y1[r] + m2 * y2[r]) / m;
-            v1[r] = (m1 * v1[r] + m2 * v2[r]) / m;
+            y1[r] = k1[r];
+            y2[r] = k2[r];
+        }
+    }
+    // the weighted means with one reciprocal of m (the double-precision
+    // value moves by at most an ulp of double before the storage rounding)
+    const double inv_m = 1.0 / m;
+    double dist = 0.0;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const double dm = y1[r] - y2[r];
+        dist += dm * dm;
+        key[r] = (m1 * y1[r] + m2 * y2[r]) * inv_m;
+    }
+    {
+        double v1[8], v2[8];
+        in.v1.f64(v1);
+        in.v2.f64(v2);
+#pragma unroll
+        for (int r = 0; r < 8; ++r) val[r] = (m1 * v1[r] + m2 * v2[r]) * inv_m;
+    }
+    // sum over the pair's lanes (LPH = 16 or 8)
+    dist += dpp_xor_f64<1>(dist);
+    dist += dpp_xor_f64<2>(dist);
+    dist += dpp_xor_f64<4>(dist);
+    if constexpr (LPH == 16) dist += dpp_xor_f64<8>(dist);
+    if (!in.ok || i1 <= 0) return;
+    const double sig = (m1 * (2.0 * D * b1) + m2 * (2.0 * D * b2)) / m + m1 * m2 * dist / (m * m * D);
+    T* kp = static_cast<T*>(a.cache.k);
+    T* vp = static_cast<T*>(a.cache.v);
+    const int d0 = 8 * j;
+    Vec8<T>::store(kp + in.ph1 * kPage * D + slot_elem(in.s1, d0), key);
+    Vec8<T>::store(vp + in.ph1 * kPage * D + slot_elem(in.s1, d0), val);
+    const double zero[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    Vec8<T>::store(kp + in.ph2 * kPage * D + slot_elem(in.s2, d0), zero);
+    Vec8<T>::store(vp + in.ph2 * kPage * D + slot_elem(in.s2, d0), zero);
+    if (j == 0) {
+        T* ab = static_cast<T*>(a.cache.ab);
+        ab[(in.ph1 * kPage + in.s1) * 2 + 0] = Elem<T>::from_f64(log(m));
+        ab[(in.ph1 * kPage + in.s1) * 2 + 1] = Elem<T>::from_f64(sig / (2.0 * D));
+        ab[(in.ph2 * kPage + in.s2) * 2 + 0] = Elem<T>::from_f32(-__builtin_huge_valf());
+        ab[(in.ph2 * kPage + in.s2) * 2 + 1] = Elem<T>::from_f32(0.f);
+        MetaRec* mt = static_cast<MetaRec*>(a.cache.meta);
+        mt[in.ph1 * kPage + in.s1] = MetaRec{2, i1 + i2, P};
+        mt[in.ph2 * kPage + in.s2] = MetaRec{0, 0, 0};
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void merge_list_kernel(MergeArgs a) {
+    __shared__ int32_t l_e[kWin + 1];         // the window's macro-nodes in order (slot 0: the carried one)
+    __shared__ int32_t l_p[kWin + 1];         // their pages
+    __shared__ int32_t w_cnt[kWaves];
+    const int H = a.cache.H;
+    const int64_t unit = blockIdx.x;          // sequence * H + head
+    const int b = static_cast<int>(unit / H);
+    const int h = static_cast<int>(unit % H);
+    const int t = threadIdx.x;
+    const int lane = t % kWave, wave = t / kWave;
+    const int32_t e0 = a.entry_begin[b], e1 = a.entry_end[b];
+    if (e0 < 0 || e0 > e1 || e1 - e0 > a.max_range) {
+        if (t == 0) {
+            raise_err(a.err, SPICY_DEVERR_SEGMENTS);
+            a.pair_count[unit] = 0;
+        }
+        return;
+    }
+    const MetaRec* meta = static_cast<const MetaRec*>(a.cache.meta);
+    int4* out = a.pairs + unit * a.cap;
+    int32_t carried = 0;                      // 1: slot 0 holds an unpaired macro-node
+    int32_t done = 0;                         // pairs of the range before this window
+    for (int32_t w0 = e0; w0 < e1; w0 += kWin) {
+        constexpr int kRounds = kWin / kThreads;
+        int32_t pg[kRounds];
+        bool mac[kRounds];
+#pragma unroll
+        for (int r = 0; r < kRounds; ++r) {
+            const int32_t e = w0 + r * kThreads + t;
+            pg[r] = e < e1 ? page_of(a, b, e) : -1;
         }
 #pragma unroll
-        for (int o = 1; o < LPH; o <<= 1) dist += __shfl_xor(dist, o);
-        if (!ok || i1 <= 0) continue;
-        const double sig = (m1 * (2.0 * D * b1) + m2 * (2.0 * D * b2)) / m + m1 * m2 * dist / (m * m * D);
-        T* kp = static_cast<T*>(a.cache.k);
-        T* vp = static_cast<T*>(a.cache.v);
-        Vec8<T>::store(kp + ph1 * kPage * D + slot_elem(s1, d0), key);
-        Vec8<T>::store(vp + ph1 * kPage * D + slot_elem(s1, d0), v1);
-        const double zero[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        Vec8<T>::store(kp + ph2 * kPage * D + slot_elem(s2, d0), zero);
-        Vec8<T>::store(vp + ph2 * kPage * D + slot_elem(s2, d0), zero);
-        if (j == 0) {
-            T* ab = static_cast<T*>(a.cache.ab);
-            ab[(ph1 * kPage + s1) * 2 + 0] = Elem<T>::from_f64(log(m));
-            ab[(ph1 * kPage + s1) * 2 + 1] = Elem<T>::from_f64(sig / (2.0 * D));
-            ab[(ph2 * kPage + s2) * 2 + 0] = Elem<T>::from_f32(-__builtin_huge_valf());
-            ab[(ph2 * kPage + s2) * 2 + 1] = Elem<T>::from_f32(0.f);
-            MetaRec* mt = static_cast<MetaRec*>(a.cache.meta);
-            mt[ph1 * kPage + s1] = MetaRec{2, i1 + i2, P};
-            mt[ph2 * kPage + s2] = MetaRec{0, 0, 0};
+        for (int r = 0; r < kRounds; ++r) {
+            const int32_t e = w0 + r * kThreads + t;
+            mac[r] = pg[r] >= 0 && meta[(static_cast<int64_t>(pg[r]) * H + h) * kPage + e % kPage].kind == 2;
         }
+        int32_t base = carried;               // list slot of this round's first macro-node
+#pragma unroll
+        for (int r = 0; r < kRounds; ++r) {
+            const uint64_t M = __ballot(mac[r]);
+            if (lane == 0) w_cnt[wave] = __popcll(M);
+            __syncthreads();
+            int32_t before = 0, total = 0;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                before += w < wave ? w_cnt[w] : 0;
+                total += w_cnt[w];
+            }
+            if (mac[r]) {
+                const int32_t slot = base + before + __popcll(M & ((1ull << lane) - 1ull));
+                l_e[slot] = w0 + r * kThreads + t;
+                l_p[slot] = pg[r];
+            }
+            base += total;
+            __syncthreads();                  // w_cnt is rewritten by the next round
+        }
+        const int32_t n = base;
+        const int32_t np = n / 2;
+        for (int32_t i = t; i < np; i += kThreads) {
+            const int32_t q = done + i;
+            if (q < a.cap) out[q] = make_int4(l_e[2 * i], l_e[2 * i + 1], l_p[2 * i], l_p[2 * i + 1]);
+            else raise_err(a.err, SPICY_DEVERR_CAPACITY);
+        }
+        done += np;
+        const int32_t odd = n & 1;
+        const int32_t last_e = odd ? l_e[n - 1] : 0, last_p = odd ? l_p[n - 1] : 0;
+        __syncthreads();                      // every read of the list is done
+        if (odd && t == 0) {
+            l_e[0] = last_e;
+            l_p[0] = last_p;
+        }
+        carried = odd;
+        __syncthreads();
+    }
+    if (t == 0) a.pair_count[unit] = done < a.cap ? done : a.cap;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void merge_pair_kernel(MergeArgs a) {
+    constexpr int LPH = D / 8;                // lanes per pair
+    constexpr int PPW = kWave / LPH;          // pairs per wavefront round
+    constexpr int NG = kWaves * PPW;          // groups of the workgroup
+    constexpr int PARTNER = LPH / 2;
+    const int64_t unit = blockIdx.y;          // sequence * H + head
+    const int h = static_cast<int>(unit % a.cache.H);
+    const int lane = threadIdx.x % kWave;
+    const int j = lane % LPH;
+    const int d0 = 8 * j;
+    const bool hi_half = j >= PARTNER;
+    const int grp = (threadIdx.x / kWave) * PPW + lane / LPH;
+    const bool rotate = a.rope_base > 0.0;
+    double theta[4];
+    {
+        const int pair0 = 8 * (hi_half ? j - PARTNER : j) + (hi_half ? 4 : 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) theta[r] = a.theta[pair0 + r];
+    }
+    const int32_t count = a.pair_count[unit];
+    const int64_t start = static_cast<int64_t>(blockIdx.x) * NG;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * NG;
+    for (int64_t r0 = start; r0 < count; r0 += 2 * stride) {          // uniform over the workgroup
+        PairIn<T> in[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int64_t pj = r0 + u * stride + grp;
+            const bool live = pj < count;
+            const int4 pr = live ? a.pairs[unit * a.cap + pj] : make_int4(0, 0, -1, -1);
+            pair_load<T, D>(a, h, live, pr.x, pr.z, pr.y, pr.w, d0, in[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) pair_store<T, D>(a, in[u], j, hi_half, rotate, theta);
     }
 }
 
 template <typename T, int D>
 spicy_status launch_merge_t(const MergeArgs& a, hipStream_t stream) {
     const int64_t units = static_cast<int64_t>(a.B) * a.cache.H;
-    const int64_t lb = (units + kListWaves - 1) / kListWaves;
-    hipLaunchKernelGGL(merge_list_kernel, dim3(static_cast<unsigned>(lb)), dim3(kListWaves * kWave), 0, stream, a);
+    hipLaunchKernelGGL(merge_list_kernel, dim3(static_cast<unsigned>(units)), dim3(kThreads), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return SPICY_ERR_HIP;
-    // about kResident workgroups over all (sequence, head) units; each takes
-    // 16 (d = 128) or 32 (d = 64) pairs per round
-    constexpr int ngrp = 4 * (kWave / (D / 8));
-    const int64_t want = (static_cast<int64_t>(a.cap) + ngrp - 1) / ngrp;
-    const int64_t cx = want < 1 ? 1 : (want < kResident / units + 1 ? want : kResident / units + 1);
+    // at most kResident workgroups over all (sequence, head) units, so that
+    // they all run at once (a second round of workgroups doubles the time);
+    // each takes 2 x 16 (d = 128) or 2 x 32 (d = 64) pairs per pass
+    constexpr int ngrp = kWaves * (kWave / (D / 8));
+    const int64_t want = (static_cast<int64_t>(a.cap) + 2 * ngrp - 1) / (2 * ngrp);
+    const int64_t fill = kResident / units > 1 ? kResident / units : 1;
+    const int64_t cx = want < 1 ? 1 : (want < fill ? want : fill);
     hipLaunchKernelGGL((merge_pair_kernel<T, D>), dim3(static_cast<unsigned>(cx), static_cast<unsigned>(units)),
-                       dim3(256), 0, stream, a);
+                       dim3(kThreads), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return SPICY_ERR_HIP;
     return SPICY_OK;
 }

@@ -109,6 +109,35 @@ template <> struct Elem<float> {
     static __device__ __forceinline__ float from_f32(float x) { return x; }
 };
 
+// ------------------------------------------------------------- lane moves
+
+// The value of lane (this lane xor P), P = 1, 2, 4 or 8, through DPP moves
+// (VALU only, no LDS round trip): P = 1 and 2 are quad permutations; P = 8 is
+// a rotation by 8 inside each 16-lane row; P = 4 is a reversal inside each
+// quad (lane xor 3) followed by a mirror inside each half-row of 8 (lane xor 7).
+template <int P>
+__device__ __forceinline__ uint32_t dpp_xor(uint32_t v) {
+    static_assert(P == 1 || P == 2 || P == 4 || P == 8, "lane distance");
+    const int x = static_cast<int>(v);
+    if constexpr (P == 1) {
+        return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false));     // quad_perm [1,0,3,2]
+    } else if constexpr (P == 2) {
+        return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false));     // quad_perm [2,3,0,1]
+    } else if constexpr (P == 8) {
+        return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false));    // row_ror:8
+    } else {
+        const int r = __builtin_amdgcn_mov_dpp(x, 0x1B, 0xF, 0xF, false);                      // quad_perm [3,2,1,0]
+        return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(r, 0x141, 0xF, 0xF, false));     // row_half_mirror
+    }
+}
+
+template <int P>
+__device__ __forceinline__ double dpp_xor_f64(double v) {
+    const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
+    const uint32_t lo = dpp_xor<P>(static_cast<uint32_t>(u)), hi = dpp_xor<P>(static_cast<uint32_t>(u >> 32));
+    return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+
 // ------------------------------------------------------------ buffer loads
 
 // Raw buffer resource over `bytes` bytes at p: loads at offsets >= bytes
@@ -193,7 +222,7 @@ struct MergeArgs {
     const int32_t* entry_end;     // [B]
     int32_t* err;
     int32_t* pair_count;          // [B*H]       workspace: pairs of each (sequence, head)
-    int2* pairs;                  // [B*H][cap]  workspace: {first entry, second entry}
+    int4* pairs;                  // [B*H][cap]  workspace: {first entry, second entry, their pages}
     int32_t cap;                  // pairs per (sequence, head) = (max_range + 1) / 2
     int32_t B;
     int32_t max_pages;

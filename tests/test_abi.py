@@ -233,9 +233,9 @@ def test_merge_rejects_bad_arguments(lib):
     diag = _cache()
     diag.meta, diag.s2 = P, P
     assert call(cache=diag) == 4
-    # header, int32 count per (sequence, head), int2 per pair, (range + 1) / 2 pairs
+    # header, int32 count per (sequence, head), int4 per pair, (range + 1) / 2 pairs
     up = lambda x: (x + 255) // 256 * 256
-    assert lib.spicy_merge_workspace_bytes(3, 4, 101) == 256 + up(4 * 12) + up(8 * 12 * 51)
+    assert lib.spicy_merge_workspace_bytes(3, 4, 101) == 256 + up(4 * 12) + up(16 * 12 * 51)
     assert lib.spicy_merge_workspace_bytes(3, 0, 101) == 0
 
 
