@@ -492,7 +492,7 @@ def decode_config_line(wl, dw, rotate_bytes: float, reps: int, ceiling: bool = T
     st = _stats(per_call)
     gbs = db / (st["mean"] * 1e-6) / 1e9
     out = {"workload": wl.name, "description": wl.description, "calls_per_rep": L, "cache_bytes": int(cache_bytes),
-           "bound": "hbm", "alg_bytes_per_call": int(db), "call_us": st, "achieved": round(gbs, 1),
+           "bound": "hbm", "call": "decode", "alg_bytes_per_call": int(db), "call_us": st, "achieved": round(gbs, 1),
            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
            "target_frac": DECODE_TARGET_FRAC,
            "query_tokens_per_s": round(wl.B * dw.q_tokens / (st["mean"] * 1e-6), 1),
@@ -619,6 +619,7 @@ def summarize_profile(args) -> None:
     cf = _counters(os.path.join(d, "copy_FETCH_SIZE"))
     cw = _counters(os.path.join(d, "copy_WRITE_SIZE"))
     digest_lines = []
+    measured = {}
     if fetch and write and cf and cw:
         def copy_kib(c, ctr):
             vals = [v[ctr] for k, vs in c.items() if "neg" in k or "elementwise" in k for v in vs if ctr in v]
@@ -640,6 +641,7 @@ def summarize_profile(args) -> None:
             wv = statistics.median([v["WRITE_SIZE"] for v in write[k][-3:] if "WRITE_SIZE" in v])
             b = fv * 1024 * ff + wv * 1024 * wf
             lines.append(f"{k[:34]:34s} {fv:12.0f} {wv:12.0f} {b:14.0f}")
+            measured[k] = b
             if k in KERNEL_SOURCE:
                 digest_lines.append(f"traffic_bytes {k} {b:.0f} {kernel_digest(k)}")
         lines.append("")
@@ -666,10 +668,30 @@ def summarize_profile(args) -> None:
         lines.append("")
     bench_line = os.path.join(d, "bench_line.json")
     if os.path.exists(bench_line):
+        with open(bench_line) as fh:
+            raw = fh.read().strip().splitlines()[-1]
+        if measured:
+            # measured HBM bytes of each call's kernels over the call's algorithmic bytes
+            rec = json.loads(raw)
+            if rec.get("mode") == "decode-only":        # the line is the decode call itself
+                rec = {"roofline": dict(rec, call="decode")}
+            rows = []
+            for key, r in sorted(rec.items()):
+                if not (key.startswith("roofline") and isinstance(r, dict) and r.get("call") in CALL_KERNELS):
+                    continue
+                ks = CALL_KERNELS[r["call"]]
+                if all(k in measured for k in ks) and r.get("alg_bytes_per_call"):
+                    tb = sum(measured[k] for k in ks)
+                    rows.append(f"{r['call']:10s} {r['alg_bytes_per_call']:14d} {tb:14.0f} {tb / r['alg_bytes_per_call']:8.3f}")
+            if rows:
+                lines.append("## Measured traffic over algorithmic bytes, per call")
+                lines.append("")
+                lines.append(f"{'call':10s} {'algorithmic':>14s} {'measured':>14s} {'ratio':>8s}")
+                lines += rows
+                lines.append("")
         lines.append("## bench.py line of the same tree")
         lines.append("")
-        with open(bench_line) as fh:
-            lines.append(fh.read().strip().splitlines()[-1])
+        lines.append(raw)
         lines.append("")
     out = os.path.join(ROOT, "profiles", f"{name}.txt")
     with open(out, "w") as fh:
@@ -877,7 +899,7 @@ def main():
             t = int(sum(traffic[k] for k in ks))
         return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": t, "alg_bytes_per_call": int(alg[call]),
-                "mean_call_us": st["mean"], "call_us": st, "kernel": names[call]}
+                "mean_call_us": st["mean"], "call_us": st, "call": call, "kernel": names[call]}
 
     rooflines = {c: roof(c) for c in per}
     dominant = max(rooflines, key=lambda c: rooflines[c]["call_us"]["median"])
