@@ -545,7 +545,8 @@ def decode_configs(args, dev) -> list:
 def _base_kernel_name(name: str) -> str:
     """'void spicy::decode_mfma_kernel<128, 3, ...>(spicy::DecodeArgs)' ->
     'decode_mfma_kernel' (and torch's kernels to their template name)."""
-    n = name.split("(")[0]
+    n = name.replace("(anonymous namespace)::", "")
+    n = n.split("(")[0]
     n = re.sub(r"<.*", "", n)
     return n.split("::")[-1].replace("void ", "").strip()
 
@@ -822,11 +823,14 @@ def main():
     # per-call durations: K more whole steps queued behind a sleep kernel (so
     # that no call waits for the host), each call bracketed by HIP events on
     # the launch stream
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    # (two more steps go first, untimed: the first queued steps behind the
+    # sleep have shown host-side stalls of up to milliseconds)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps + 2)]
     _hold_stream(elapsed * 1e6 * 1.5)
     for e in evs:
         step(e)
     torch.cuda.synchronize()
+    evs = evs[2:]
     per = {
         "coarsen": [e[0].elapsed_time(e[1]) * 1e3 for e in evs],
         "decode": [e[4].elapsed_time(e[2]) * 1e3 for e in evs],

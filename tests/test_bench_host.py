@@ -138,3 +138,15 @@ def test_compact_bytes():
     # seq 1: head 0: no live entries, pad 16..32 -> 16 nulls; head 1: 7 moves, pad 23..32 -> 9 nulls
     s1 = 2 * 8 * 2 + 4 * 1 + entry * 16 + 2 * entry * 7 + entry * 9
     assert bench.compact_alg_bytes(c, table, null, lengths, new) == s0 + s1 + 12 * 2
+
+
+def test_kernel_names_from_rocprof():
+    """Template arguments, namespaces and anonymous namespaces removed."""
+    assert bench._base_kernel_name("void spicy::decode_mfma_kernel<128, 3, false, 1, 4>(spicy::DecodeArgs)") == \
+        "decode_mfma_kernel"
+    assert bench._base_kernel_name("spicy::(anonymous namespace)::merge_list_kernel(spicy::MergeArgs)") == \
+        "merge_list_kernel"
+    assert bench._base_kernel_name("void spicy::(anonymous namespace)::compact_move_kernel<2>(spicy::CompactArgs)") \
+        == "compact_move_kernel"
+    assert bench._base_kernel_name("void (anonymous namespace)::stream_read_kernel<1>(HIP_vector_type<unsigned "
+                                   "int, 4u> const*, unsigned long, unsigned int*)") == "stream_read_kernel"
