@@ -202,6 +202,10 @@ def decode(q: np.ndarray, q_dtype: str, cache: Cache, H_q: int, page_table: np.n
     q = np.ascontiguousarray(q)
     B = int(q.shape[0])
     d = cache.d
+    if q.ndim != 3 or q.shape[1:] != (H_q, d) or q.dtype != NP[q_dtype]:
+        raise ValueError(f"q must be [B, {H_q}, {d}] of {q_dtype} storage, got {q.shape} {q.dtype}")
+    if np.shape(lengths) != (B,) or np.shape(page_table)[0] != B:
+        raise ValueError("page_table and lengths need one row per sequence")
     o = np.zeros((B, H_q, d), dtype=np.float64)
     lse = np.zeros((B, H_q), dtype=np.float64)
     table = np.ascontiguousarray(page_table, dtype=np.int32)

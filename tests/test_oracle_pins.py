@@ -451,7 +451,21 @@ def test_decode_work_items_are_the_whole_decode():
     c = W.random_decode_case(41, B=3, H_q=8, H_kv=2, d=64, q_tokens=1, dtype="bf16")
     cache = oracle.Cache(c.dtype, c.k.shape[0], c.H_kv, c.d, fill=False)
     cache.k[:] = c.k; cache.v[:] = c.v; cache.ab[:] = c.ab
-    q = np.ascontiguousarray(c.q[:, 0])
+    q = np.ascontiguousarray(c.q)                      # [B, H_q, d] with one query token
     o1, l1 = oracle.decode(q, c.dtype, cache, 8, c.page_table, c.lengths, threads=1)
     o4, l4 = oracle.decode(q, c.dtype, cache, 8, c.page_table, c.lengths, threads=4)
     assert np.array_equal(o1, o4) and np.array_equal(l1, l4)
+
+
+def test_decode_rejects_misshaped_queries():
+    """A query array that is not [B, H_q, d] of the stated storage is refused
+    before the C code reads it (it would read past the array's end)."""
+    c = W.random_decode_case(41, B=3, H_q=8, H_kv=2, d=64, dtype="bf16")
+    cache = oracle.Cache(c.dtype, c.k.shape[0], c.H_kv, c.d, fill=False)
+    cache.k[:] = c.k; cache.v[:] = c.v; cache.ab[:] = c.ab
+    with pytest.raises(ValueError):
+        oracle.decode(np.ascontiguousarray(c.q[:, 0]), c.dtype, cache, 8, c.page_table, c.lengths)
+    with pytest.raises(ValueError):
+        oracle.decode(c.q.astype(np.float32), c.dtype, cache, 8, c.page_table, c.lengths)
+    with pytest.raises(ValueError):
+        oracle.decode(c.q, c.dtype, cache, 8, c.page_table, c.lengths[:2])
