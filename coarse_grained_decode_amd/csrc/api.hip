@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <mutex>
@@ -187,6 +188,12 @@ static spicy_status coarsen_call(const spicy_cache* cache, const void* k_pre, co
     a.seg_desc = reinterpret_cast<int4*>(ws + SPICY_WORKSPACE_HEADER);
     size_t off = SPICY_WORKSPACE_HEADER + align_up(16 * ns);
     a.seg_head = reinterpret_cast<int2*>(ws + off);
+    // a tag per call for its destination hints (1 .. 2^32 - 1), so that a
+    // hint another call published is never taken for this call's
+    static std::atomic<uint32_t> calls{0};
+    const bool hints = static_cast<int64_t>(n_seg) * cache->num_kv_heads <= spicy::kDestHintWords &&
+                       cache->num_pages < (int32_t{1} << 28);
+    a.gen = hints ? calls.fetch_add(1, std::memory_order_relaxed) % 0xFFFFFFFFu + 1 : 0u;
     off += align_up(8 * ns * static_cast<size_t>(cache->num_kv_heads));
     a.cp_items = reinterpret_cast<int2*>(ws + off);
     off += align_up(8 * static_cast<size_t>(total_tokens) * static_cast<size_t>(cache->num_kv_heads));

@@ -84,6 +84,39 @@ __device__ __forceinline__ int32_t entry_page(const CoarsenArgs& a, int b, int64
     return P;
 }
 
+// Destination hints.  The plan role knows where each (segment, head)
+// macro-node goes; the streaming role computes the macro-node.  When the plan
+// has already published the destination by the time the streaming role
+// finishes the segment, the streaming role writes the macro-node straight
+// into the cache; otherwise it stages it and coarsen_cpoint copies it there
+// from the plan's record in the workspace (seg_head), which alone is
+// authoritative.  A hint is one 64-bit word, gen << 32 | page << 4 | slot,
+// published and read with single device-scope atomic accesses; gen is the
+// call's nonzero tag, so a word left by another call (on this or another
+// stream) never matches and only sends its macro-node down the staged path.
+// The array starts zero, only the library writes it, and coarsen_cpoint
+// clears every word of its call.
+__device__ uint64_t g_dest_hint[kDestHintWords];
+
+__device__ __forceinline__ uint64_t dest_word(int32_t page, int64_t entry, uint32_t gen) {
+    return (static_cast<uint64_t>(gen) << 32) | (static_cast<uint64_t>(static_cast<uint32_t>(page)) << 4) |
+           static_cast<uint64_t>(entry % kPage);
+}
+
+struct Dest {
+    int32_t page;
+    int slot;
+    bool ok;
+};
+
+__device__ __forceinline__ Dest read_dest(uint64_t w, uint32_t gen) {
+    Dest d;
+    d.page = static_cast<int32_t>((w >> 4) & 0x0FFFFFFFu);
+    d.slot = static_cast<int>(w & 15u);
+    d.ok = gen != 0 && static_cast<uint32_t>(w >> 32) == gen;
+    return d;
+}
+
 // 8 consecutive elements of one row: a 16-byte (bf16) or 32-byte (fp32) load
 template <typename T> struct Row8;
 template <> struct Row8<uint16_t> {
@@ -385,9 +418,14 @@ __device__ __forceinline__ void plan_sequence(const CoarsenArgs& a, int32_t (*s_
                 if (h < H) {
                     // the macro-node's physical page, resolved here so that
                     // placing it needs no table lookup (-1: none, or an
-                    // entry the table cannot hold, reported here)
+                    // entry the table cannot hold, reported here), and
+                    // published as a hint for the streaming role
                     const int32_t Pg = has_f[h] ? entry_page(a, b, first[h]) : -1;
-                    a.seg_head[static_cast<int64_t>(s) * H + h] = make_int2(first[h], Pg);
+                    const int64_t idx = static_cast<int64_t>(s) * H + h;
+                    a.seg_head[idx] = make_int2(first[h], Pg);
+                    if (a.gen != 0 && Pg >= 0)
+                        __hip_atomic_store(&g_dest_hint[idx], dest_word(Pg, first[h], a.gen), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
                 }
             // the segment's C-point items, in position order within each head
             int nxt[NH];
@@ -725,18 +763,31 @@ __device__ __forceinline__ void stream_segment(const CoarsenArgs& a, const Lanes
             }
         }
     }
+    const int64_t idx = static_cast<int64_t>(s) * H + L.hh;
+    // if the plan role has already published where this macro-node goes, it
+    // is written there; otherwise it is staged for coarsen_cpoint.  The word
+    // of the head's first lane decides for all 16 lanes of the head.
+    const uint64_t w0 =
+        a.gen != 0 ? __hip_atomic_load(&g_dest_hint[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+    const uint64_t w = static_cast<uint64_t>(__shfl(static_cast<long long>(w0), L.lane - L.j));
     if (!mine) return;
+    const Dest dst = read_dest(w, a.gen);
     const double sigma2 = (part > 0.0 ? part : 0.0) / (md * D);
-    const int64_t idx = static_cast<int64_t>(s) * H + L.h;
-    if constexpr (DIAG) Pack8<T>::store(static_cast<T*>(a.stage_s2) + idx * D + L.d0, s2);
-    Pack8<T>::store(static_cast<T*>(a.stage_k) + idx * D + L.d0, y);
-    Store8<T>::store(static_cast<T*>(a.stage_v) + idx * D + L.d0,
+    const int64_t ph = static_cast<int64_t>(dst.ok ? dst.page : 0) * H + L.h;
+    const int64_t row = dst.ok ? ph * kPage * D + slot_elem(dst.slot, L.d0) : idx * D + L.d0;
+    if constexpr (DIAG) Pack8<T>::store(static_cast<T*>(dst.ok ? a.cache.s2 : a.stage_s2) + row, s2);
+    Pack8<T>::store(static_cast<T*>(dst.ok ? a.cache.k : a.stage_k) + row, y);
+    Store8<T>::store(static_cast<T*>(dst.ok ? a.cache.v : a.stage_v) + row,
                      [&](int r) { return Elem<T>::from_f64(wmean ? svw[r] / sw : sv[r] / md); });
     if (L.j == 0) {
-        T* ab = static_cast<T*>(a.stage_ab);
-        ab[idx * 2 + 0] = Elem<T>::from_f64(log(md));
-        ab[idx * 2 + 1] = Elem<T>::from_f64(sigma2 / (2.0 * D));
-        a.stage_meta[idx] = make_int4(m, b, static_cast<int32_t>(psum & 0xFFFFFFFF), static_cast<int32_t>(psum >> 32));
+        const int64_t ab_at = dst.ok ? ph * kPage + dst.slot : idx;
+        T* ab = static_cast<T*>(dst.ok ? a.cache.ab : a.stage_ab);
+        ab[ab_at * 2 + 0] = Elem<T>::from_f64(log(md));
+        ab[ab_at * 2 + 1] = Elem<T>::from_f64(sigma2 / (2.0 * D));
+        if (dst.ok && a.cache.meta) static_cast<Meta*>(a.cache.meta)[ab_at] = Meta{2, m, psum};
+        // mass 0 tells coarsen_cpoint the macro-node is already in place
+        a.stage_meta[idx] = make_int4(dst.ok ? 0 : m, b, static_cast<int32_t>(psum & 0xFFFFFFFF),
+                                      static_cast<int32_t>(psum >> 32));
     }
 }
 
@@ -771,21 +822,24 @@ __device__ __forceinline__ void place_macro(const CoarsenArgs& a, int b, int32_t
     const int32_t sg = s0 + static_cast<int32_t>(u % nseg);
     const int h = static_cast<int>(u / nseg);
     const int64_t idx = static_cast<int64_t>(sg) * H + h;
-    // every read of the unit is independent: issue them together
+    // every read of the unit is independent: issue them together; the hint
+    // is cleared once read (the array starts every call zero)
     const int32_t owner = a.seg_desc[sg].x;
     const int2 hd = a.seg_head[idx];
     const int4 mt = a.stage_meta[idx];
+    if (a.gen != 0 && j == 0) __hip_atomic_store(&g_dest_hint[idx], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (owner != b) return;                             // sequence failed its checks
+    const int32_t Pg = hd.y;                            // -1: no F-token in this head, or no page
+    if (Pg < 0) return;
+    if (mt.y != b || mt.x < 0) {
+        raise_err(a.err, SPICY_DEVERR_SEGMENTS);
+        return;
+    }
+    if (mt.x == 0) return;                              // written in place by the streaming role
     Row8<T> kx, vx, sx;
     kx.load(static_cast<const T*>(a.stage_k) + idx * D + d0);
     vx.load(static_cast<const T*>(a.stage_v) + idx * D + d0);
     if (a.cache.s2) sx.load(static_cast<const T*>(a.stage_s2) + idx * D + d0);
-    if (owner != b) return;                             // sequence failed its checks
-    const int32_t Pg = hd.y;                            // -1: no F-token in this head, or no page
-    if (Pg < 0) return;
-    if (mt.y != b || mt.x <= 0) {
-        raise_err(a.err, SPICY_DEVERR_SEGMENTS);
-        return;
-    }
     const int slot = hd.x % kPage;
     const int64_t ph = static_cast<int64_t>(Pg) * H + h;
     Store8<T>::store(static_cast<T*>(a.cache.k) + ph * kPage * D + slot_elem(slot, d0),

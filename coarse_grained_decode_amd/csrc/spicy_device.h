@@ -181,6 +181,12 @@ struct PolicyArgs {
     int32_t total_tokens, B, H, d, R, nnz, N, L, sink, recent;
 };
 
+// Destination hints of the coarsening: one 64-bit word per (segment, head)
+// of a call, in a device array of this many words that the library owns.
+// Calls with more (segment, head) pairs, or pools of 2^28 pages or more, run
+// without hints.
+constexpr int64_t kDestHintWords = int64_t{1} << 17;
+
 struct CoarsenArgs {
     CacheArgs cache;
     const void* k_pre;
@@ -210,6 +216,7 @@ struct CoarsenArgs {
     int32_t n_seg;
     int32_t B;
     int32_t max_pages;
+    uint32_t gen;          // this call's tag in the destination hints (0: no hints this call)
     double rope_base;
     double theta[64];      // rotary frequencies rope_base^(-2i/d), i < d/2 (host libm pow)
 };

@@ -176,6 +176,12 @@ size_t spicy_coarsen_workspace_bytes(int32_t B, int32_t n_seg, int32_t total_tok
  *   and per rotary pair the product sum), C-points and nulls get s2 = 0.
  * Workspace: device, >= spicy_coarsen_workspace_bytes(B, n_seg, total_tokens, H_kv, d, dtype) bytes,
  *   first int32 = sticky device error word (not cleared by the library).
+ *   Besides the workspace, the library keeps 1 MiB of device memory per
+ *   element type and head dim on each GPU (allocated when the library loads)
+ *   for hints that let most macro-nodes go straight into the cache; a hint
+ *   carries its call's tag, so calls in flight together (on one stream or
+ *   several) never take each other's, and a call with more than 2^17
+ *   (segment, head) pairs, or a pool of 2^28 pages or more, runs without them.
  * Errors: SPICY_ERR_ARG (null required pointer, B < 0, n_seg < 0, bad dtype),
  *   SPICY_ERR_UNSUPPORTED (head_dim not 64/128, H_kv > 16, max_pages_per_seq > 2^23),
  *   SPICY_ERR_CAPACITY (workspace too small), SPICY_ERR_HIP. */

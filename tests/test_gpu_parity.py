@@ -437,3 +437,26 @@ def test_shared_and_plain_decode_agree_on_full_workload():
     compare_decode(o1, l1, ro, rlse, wl.dtype)
     e = float((o1 - dw.o).abs().max())
     assert e <= 1e-2, e
+
+
+def test_many_segments_run_without_hints():
+    """More (segment, head) pairs than the library's destination-hint array
+    holds (2^17): every macro-node takes the staged path.  Layout and decode
+    as the oracle's, at the same bars as the other cases."""
+    _need_gpu()
+    from coarse_grained_decode_amd.runner import DeviceWorkload
+    wl = W.make_single(8, dtype="bf16", B=2, H_q=16, H_kv=16, d=64, rope_base=1e4, T=[8300, 8300], run=None,
+                       mean_run=9.0, frac=0.1, ratio=None, grid=2, permute=True, name="many_segments")
+    call = wl.calls[-1]
+    assert (len(call.seg_offsets) - 1) * call.H_kv > 1 << 17
+    print(f"[case] many_segments: {len(call.seg_offsets) - 1} segments x {call.H_kv} heads", flush=True)
+    ref_cache, ref_len, ro, rlse = oracle.run_workload(wl)
+    dw = DeviceWorkload.of(wl, DEV)
+    dw.run_setup()
+    dw.decode()
+    torch.cuda.synchronize()
+    for c in dw.setup:
+        assert int(c.ws[0].item()) == 0, "device error word set"
+    assert np.array_equal(dw.lengths.cpu().numpy(), ref_len)
+    compare_cache(dw, ref_cache, ref_len)
+    compare_decode(dw.o, dw.lse, ro, rlse, "bf16")
