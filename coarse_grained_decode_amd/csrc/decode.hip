@@ -498,8 +498,8 @@ struct Finish {
 //       [c prefix_chunk, ...) of the prefix, with ids from sequence 0's table
 //       row.  The tile-sets of one (c, h) are consecutive, so they share an
 //       XCD's L2.
-//   otherwise: private role, (group s, tile-set ts, KV head h, sequence b):
-//       the rows of tiles TPW ts .. of (b, h), pages
+//   otherwise: private role, (group s, sequence b, tile-set ts, KV head h),
+//       h fastest and s slowest: the rows of tiles TPW ts .. of (b, h), pages
 //       [P + s priv_chunk, ...) of sequence b.  A group past b's pages does
 //       nothing (group 0 always takes part, so that every row is written).
 // Wavefront w of the workgroup takes the group's pages w, w + WPG, ...  Page
@@ -567,14 +567,19 @@ __global__ __launch_bounds__(WPG * kWave, 8 / WPG) void decode_mfma_kernel(Decod
         }
         issue_loads();
     } else {
+        // the split slowest and the KV head fastest: workgroups go round-robin
+        // over the XCDs, and this way each XCD gets the same splits of
+        // sequences spread over the batch (a split-fastest order would give
+        // one XCD every sequence's first, fullest split)
         blk -= a.prefix_blocks;
-        const int s = static_cast<int>(blk % a.priv_groups);
-        blk /= a.priv_groups;
-        ts = static_cast<int>(blk % a.priv_sets);
-        blk /= a.priv_sets;
+        const int64_t units = static_cast<int64_t>(a.B) * H * a.priv_sets;
+        const int s = static_cast<int>(blk / units);
+        if (s >= a.priv_groups) return;
+        blk %= units;
         h = static_cast<int>(blk % H);
-        const int64_t b = blk / H;
-        if (b >= a.B) return;
+        blk /= H;
+        ts = static_cast<int>(blk % a.priv_sets);
+        const int64_t b = blk / a.priv_sets;
         ntile = min(TPW, a.priv_tiles - TPW * ts);
         slot = a.prefix_groups + s;
         p0 = a.prefix_pages + s * a.priv_chunk;
