@@ -24,6 +24,12 @@ long ragged batch, over rotated cache copies.  `achieved` = algorithmic bytes
 per call / mean call duration.  Inputs are resident in HBM before the timed
 region.
 
+The K timed steps replay one captured HIP graph of the step (`launch` in the
+line; --eager issues every call from the host instead): the same kernels on
+the same buffers, with one launch per step, so that a slow or loaded host does
+not starve the GPU.  `step_us` and the per-call figures come from eagerly
+issued steps.
+
 Other modes: --decode-only (the decode call alone), --copy-calibration (the
 known-size copy that scales rocprofv3's byte counters), --summarize-profile DIR
 (writes profiles/<name>.txt from rocprofv3 CSV output).
@@ -53,8 +59,8 @@ DECODE_CONFIGS = ("qwen2_7b_layer", "long_ragged")
 def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="shared_prefix")
     ap.add_argument("--splits", type=int, default=0, help="decode split count (0 = automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -94,6 +100,9 @@ def parse(argv=None):
     ap.add_argument("--diag-closure", action="store_true",
                     help="the cache carries per-dimension variances (diagonal closure): coarsen writes them, "
                          "decode reads them in place of the scalar beta")
+    ap.add_argument("--eager", action="store_true",
+                    help="issue every call of each timed step from the host (default: one step captured "
+                         "once as a HIP graph and replayed per step)")
     ap.add_argument("--no-shared-prefix", action="store_true",
                     help="decode a shared-prefix batch with spicy_decode_attn (every page per sequence)")
     return ap.parse_args(argv)
@@ -810,11 +819,34 @@ def main():
     if policy is not None:
         assert int(policy.ws[0].item()) == 0, "device error word set (policy)"
 
+    # the step as one HIP graph (the same kernels on the same buffers; the
+    # library neither allocates nor synchronises inside a call), so that each
+    # timed step is one launch from the host instead of a few marshalled
+    # calls; eager issue on request or if the capture fails
+    launch = "eager"
+    run_step = step
+    if not args.eager:
+        try:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                step()
+            for _ in range(3):
+                graph.replay()
+            torch.cuda.synchronize()
+            for c in dw.setup + step_calls:
+                assert int(c.ws[0].item()) == 0, "device error word set (graph replay)"
+            run_step = graph.replay
+            launch = "hip graph (one step captured, one replay per timed step)"
+        except Exception as e:               # noqa: BLE001 - report and time the eager path instead
+            launch = f"eager (graph capture failed: {type(e).__name__}: {e})"
+            print(f"[bench] {launch}", file=sys.stderr, flush=True)
+            torch.cuda.synchronize()
+
     # throughput: exactly K whole steps with nothing else on the stream
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step()
+        run_step()
     t_issue = time.perf_counter() - t0
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
@@ -934,6 +966,7 @@ def main():
                    "diag_closure": args.diag_closure, "weighted_representatives": args.weighted,
                    "merge_level": args.merge, "compacted": args.merge and not args.no_compact},
         "step_us": _stats(step_us),
+        "launch": launch,
         # host time to enqueue the K steps (the loop is host-bound when it nears ms_per_step)
         "host_issue_us_per_step": round(t_issue / args.steps * 1e6, 1),
         "host_loadavg": _loadavg(),

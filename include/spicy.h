@@ -182,6 +182,9 @@ size_t spicy_coarsen_workspace_bytes(int32_t B, int32_t n_seg, int32_t total_tok
  *   carries its call's tag, so calls in flight together (on one stream or
  *   several) never take each other's, and a call with more than 2^17
  *   (segment, head) pairs, or a pool of 2^28 pages or more, runs without them.
+ *   A call captured into a HIP graph keeps the tag it was captured with, so
+ *   replays of one captured call must not be in flight together on one GPU
+ *   (which sharing its workspace already rules out).
  * Errors: SPICY_ERR_ARG (null required pointer, B < 0, n_seg < 0, bad dtype),
  *   SPICY_ERR_UNSUPPORTED (head_dim not 64/128, H_kv > 16, max_pages_per_seq > 2^23),
  *   SPICY_ERR_CAPACITY (workspace too small), SPICY_ERR_HIP. */

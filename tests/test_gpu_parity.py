@@ -283,6 +283,10 @@ RANDOM_SHAPES = [
     ("bf16", 64, 5, 8, 1500, 0.01),
     ("f32", 128, 2, 3, 500, 0.02),
     ("f32", 64, 1, 4, 65, 0.1),
+    # the most KV heads the library takes (16): several workgroups per
+    # segment row in the coarsening, 16 heads in every mask row
+    ("bf16", 128, 16, 2, 400, 0.03),
+    ("f32", 64, 16, 1, 200, 0.05),
 ]
 
 
