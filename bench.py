@@ -31,7 +31,8 @@ not starve the GPU.  `step_us` and the per-call figures come from eagerly
 issued steps.
 
 Other modes: --decode-only (the decode call alone), --copy-calibration (the
-known-size copy that scales rocprofv3's byte counters), --summarize-profile DIR
+known-size copy that scales rocprofv3's byte counters), --cu-probe (how fast
+a few workgroups can read, against the whole chip), --summarize-profile DIR
 (writes profiles/<name>.txt from rocprofv3 CSV output).
 """
 from __future__ import annotations
@@ -74,6 +75,9 @@ def parse(argv=None):
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 512 MiB device copy (torch.neg, fp32) 5 times: the known-size "
                          "reference that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes")
+    ap.add_argument("--cu-probe", action="store_true",
+                    help="streaming-read rate of N workgroups (one per CU up to 256), each reading about "
+                         "600 KB, for N from 8 to 512: what one CU can pull against the whole chip")
     ap.add_argument("--summarize-profile", metavar="DIR",
                     help="summarize rocprofv3 CSV output under DIR (trace/, FETCH_SIZE/, WRITE_SIZE/, "
                          "copy_FETCH_SIZE/, copy_WRITE_SIZE/, pmc_<counters>/) into profiles/<--profile-name>.txt")
@@ -205,6 +209,40 @@ def copy_calibration():
     print(json.dumps({"mode": "copy-calibration", "bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES,
                       "kernel": "torch.neg fp32", "launches": 5}), flush=True)
 
+
+
+CU_PROBE_BYTES_PER_WG = 600 * 1024       # about one private page group of the benchmark's decode (72 pages)
+
+
+def cu_probe(rotate_bytes: float = 1.5e9, reps: int = 10) -> list:
+    """The plain streaming read (libspicy_probe.so) with N workgroups of 256
+    threads, N x 600 KB per call over rotated buffers: per-workgroup and total
+    GB/s.  Up to 256 workgroups the dispatcher gives each its own CU, so the
+    per-workgroup rate at small N is what one CU can pull; at 256 and 512 the
+    whole chip reads."""
+    import torch
+    lib = _probe_lib()
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    out = []
+    for n in (8, 32, 64, 128, 256, 512):
+        nb = n * CU_PROBE_BYTES_PER_WG
+        L = max(2, int(np.ceil(rotate_bytes / nb)))
+        bufs = [torch.ones(nb // 4, dtype=torch.float32, device="cuda") for _ in range(L)]
+        for unroll in (1, 8):
+            def issue(u=unroll):
+                for x in bufs:
+                    rc = lib.spicy_probe_stream_read(x.data_ptr(), nb, n, u, sink.data_ptr(), stream)
+                    assert rc == 0, rc
+            us = statistics.median(_queued_per_call_us(issue, L, reps))
+            line = {"mode": "cu-probe", "workgroups": n, "threads_per_workgroup": 256, "loads_in_flight": unroll,
+                    "bytes_per_workgroup": CU_PROBE_BYTES_PER_WG, "us": round(us, 3),
+                    "GBps_per_workgroup": round(CU_PROBE_BYTES_PER_WG / (us * 1e-6) / 1e9, 1),
+                    "GBps_total": round(nb / (us * 1e-6) / 1e9, 1)}
+            print(json.dumps(line), flush=True)
+            out.append(line)
+        del bufs
+    return out
 
 
 # the source file that defines each kernel; its digest also covers the
@@ -717,6 +755,9 @@ def main():
         return summarize_profile(args)
     if args.copy_calibration:
         return copy_calibration()
+    if args.cu_probe:
+        cu_probe(args.rotate_bytes)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the library has no "
               "multi-GPU path, and every number it reports is one GPU's", file=sys.stderr)
