@@ -378,15 +378,21 @@ __global__ __launch_bounds__(kThreads) void merge_pair_kernel(MergeArgs a) {
     const int64_t stride = static_cast<int64_t>(gridDim.x) * NG;
     for (int64_t r0 = start; r0 < count; r0 += 2 * stride) {          // uniform over the workgroup
         PairIn<T> in[2];
+        bool any[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int64_t pj = r0 + u * stride + grp;
             const bool live = pj < count;
+            any[u] = __any(live);                  // uniform over the wavefront
             const int4 pr = live ? a.pairs[unit * a.cap + pj] : make_int4(0, 0, -1, -1);
             pair_load<T, D>(a, h, live, pr.x, pr.z, pr.y, pr.w, d0, in[u]);
         }
+        // a wavefront whose pairs of this pass are all past the count skips
+        // their arithmetic (its lanes only ever exchange values among
+        // themselves), which leaves the SIMD's fp64 unit to the others
 #pragma unroll
-        for (int u = 0; u < 2; ++u) pair_store<T, D>(a, in[u], j, hi_half, rotate, theta);
+        for (int u = 0; u < 2; ++u)
+            if (any[u]) pair_store<T, D>(a, in[u], j, hi_half, rotate, theta);
     }
 }
 
