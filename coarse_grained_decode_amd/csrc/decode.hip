@@ -850,7 +850,7 @@ __global__ __launch_bounds__(kF32Waves * kWave) void decode_f32_kernel(DecodeArg
 
 // ------------------------------------------------------------------ launch
 
-constexpr int kNbuf = 3;                  // one tile per wavefront
+constexpr int kNbuf = 2;                  // one tile per wavefront (three pages in flight were slower)
 constexpr int kNbufPair = 2;              // two tiles per wavefront: their state takes a page's registers
 constexpr int kNbufDiag = 2;              // the variance pages add a third page-sized load
 constexpr int64_t kMaxGridX = 65536;
