@@ -20,12 +20,12 @@ LIB = os.path.join(PKG, "libspicy.so")
 PROBE_LIB = os.path.join(PKG, "libspicy_probe.so")
 PROBE_SOURCE = "readprobe.hip"
 OBJDIR = os.path.join(PKG, "_build")
-SOURCES = ["api.hip", "coarsen.hip", "decode.hip", "policy.hip", "merge.hip"]
 # (source, object, extra flags): coarsen.hip builds once per (element type,
 # head dim) so that its kernels compile in parallel
 UNITS = [("api.hip", "api", []), ("decode.hip", "decode", []), ("policy.hip", "policy", []),
          ("merge.hip", "merge", []), ("compact.hip", "compact", [])] + [("coarsen.hip", f"coarsen{i}", [f"-DSPICY_COARSEN_PART={i}"])
                                          for i in range(4)]
+SOURCES = sorted({src for src, _, _ in UNITS})   # the library's sources
 HEADERS = ["launch.h", "spicy_device.h"]
 ARCH = os.environ.get("SPICY_OFFLOAD_ARCH", "gfx950")
 
