@@ -140,6 +140,18 @@ def coarsen_alg_bytes(call, lengths: np.ndarray, diag: bool = False, weighted: b
     return read + write
 
 
+def merge_pair_count(meta: np.ndarray, table: np.ndarray, entry_start, lengths) -> int:
+    """Pairs one merge level forms: per sequence and KV head, half the
+    macro-nodes (metadata kind 2) among entries [entry_start[b], lengths[b]),
+    rounded down.  meta [pages, H, 16, 4] int32 records, table [B, max_pages]."""
+    total = 0
+    for b in range(table.shape[0]):
+        e = np.arange(int(entry_start[b]), int(lengths[b]))
+        kinds = meta[table[b, e // 16], :, e % 16, 0]            # [entries, H]
+        total += int((np.count_nonzero(kinds == 2, axis=0) // 2).sum())
+    return total
+
+
 def merge_alg_bytes(call, lengths: np.ndarray, pairs: int) -> int:
     """Bytes one merge level must move: the 16-byte metadata record of every
     entry in the range (its kind), then per merged pair both entries read
@@ -251,7 +263,7 @@ KERNEL_SOURCE = {
     "coarsen_main_kernel": "coarsen.hip", "coarsen_cpoint_kernel": "coarsen.hip",
     "decode_mfma_kernel": "decode.hip", "decode_f32_kernel": "decode.hip",
     "policy_token_kernel": "policy.hip", "policy_seq_kernel": "policy.hip",
-    "merge_list_kernel": "merge.hip", "merge_pair_kernel": "merge.hip",
+    "merge_level_kernel": "merge.hip",
     "compact_count_kernel": "compact.hip", "compact_move_kernel": "compact.hip",
 }
 # the kernels of each call, for its traffic
@@ -259,7 +271,7 @@ CALL_KERNELS = {
     "coarsen": ["coarsen_main_kernel", "coarsen_cpoint_kernel"],
     "decode": ["decode_mfma_kernel"],
     "policy": ["policy_token_kernel", "policy_seq_kernel"],
-    "merge": ["merge_list_kernel", "merge_pair_kernel"],
+    "merge": ["merge_level_kernel"],
     "compact": ["compact_count_kernel", "compact_move_kernel"],
 }
 
@@ -929,8 +941,8 @@ def main():
                   " (decode_mfma: split-K pages, log-sum-exp combine in the same launch)",
         "policy": "spicy_policy (policy_token: fixed point, projection, variation, key norms; "
                   "then policy_seq: scan, boundaries, landmark radix select)",
-        "merge": "spicy_merge_level (merge_list: pairs per sequence and head; merge_pair: law of total "
-                 "variance per pair)",
+        "merge": "spicy_merge_level (merge_level: each workgroup lists its sequence and head's pairs, merges "
+                 "its share by the law of total variance; the last one writes the records)",
         "compact": "spicy_compact_range (compact_count: new lengths; compact_move: live entries moved to the "
                    "front of the merged range, nulls to the end of the new last page)",
     }
@@ -939,9 +951,12 @@ def main():
         alg["policy"] = policy_alg_bytes(dw.step.call, wl.policy)
     if run_merge is not None:
         mc = step_calls[-1]
-        units = mc.call.B * mc.call.H_kv
-        pairs = int(mws.view(torch.uint8)[256:256 + 4 * units].view(torch.int32).sum().item())
         assert int(mws[0].item()) == 0, "device error word set (merge)"
+        for c in step_calls:                      # the chunk as the merge finds it
+            c.run(dw.cache)
+        torch.cuda.synchronize()
+        pairs = merge_pair_count(dw.cache.meta.cpu().numpy(), mc.page_table.cpu().numpy(),
+                                 mc.entry_start.cpu().numpy(), mc.lengths.cpu().numpy())
         alg["merge"] = merge_alg_bytes(mc.call, mc.lengths.cpu().numpy(), pairs)
     compaction = None
     if run_compact is not None:

@@ -548,8 +548,7 @@ spicy_status spicy_policy(const void* k_pre, const void* v, int32_t total_tokens
 size_t spicy_merge_workspace_bytes(int32_t B, int32_t num_kv_heads, int32_t max_range) {
     if (B < 0 || num_kv_heads < 1 || max_range < 0) return 0;
     const size_t units = static_cast<size_t>(B) * static_cast<size_t>(num_kv_heads);
-    const size_t cap = (static_cast<size_t>(max_range) + 1) / 2;
-    return SPICY_WORKSPACE_HEADER + align_up(4 * units) + align_up(16 * units * cap);
+    return SPICY_WORKSPACE_HEADER + align_up(4 * units);
 }
 
 spicy_status spicy_merge_level(const spicy_cache* cache, int32_t B, double rope_base, const int32_t* page_table,
@@ -573,9 +572,7 @@ spicy_status spicy_merge_level(const spicy_cache* cache, int32_t B, double rope_
     a.entry_end = entry_end;
     char* ws = static_cast<char*>(workspace);
     a.err = reinterpret_cast<int32_t*>(ws);
-    const size_t units = static_cast<size_t>(B) * static_cast<size_t>(cache->num_kv_heads);
-    a.pair_count = reinterpret_cast<int32_t*>(ws + SPICY_WORKSPACE_HEADER);
-    a.pairs = reinterpret_cast<int4*>(ws + SPICY_WORKSPACE_HEADER + align_up(4 * units));
+    a.ticket = reinterpret_cast<int32_t*>(ws + SPICY_WORKSPACE_HEADER);
     a.cap = static_cast<int32_t>((static_cast<int64_t>(max_range) + 1) / 2);
     a.B = B;
     a.max_pages = max_pages_per_seq;

@@ -16,20 +16,26 @@
 // and the second entry becomes a null.  Everything in double precision,
 // rounded once on store.  The sequence lengths do not change.
 //
-// Two kernels, 4 wavefronts per workgroup:
-//   merge_list  one workgroup per (sequence, head) walks its range in windows
-//               of 1024 entries: page ids and entry kinds are read (one entry
-//               per thread per round, every load of the window in flight
-//               together), a workgroup scan ranks the macro-nodes, and pair i
-//               (macro-nodes 2i and 2i + 1 of the range, the odd one of a
-//               window carried into the next) is written to the workspace
-//               with both entries and both pages.  The whole range is listed
-//               before any pair merges: merging turns entries into nulls.
-//   merge_pair  workgroups (x, sequence * H + head); every 16-lane group (8
-//               at d = 64) takes its pairs two at a time, both pairs' rows
-//               loaded before either is computed (the pages come with the
-//               pair, so the rows are the only dependent reads), a lane
-//               owning 8 dims as in the coarsening.
+// One kernel, workgroups (x, sequence * H + head) of 4 wavefronts, cx of them
+// per (sequence, head) unit:
+//   every workgroup lists its unit's range itself, in windows of 1024
+//   entries: page ids and entry kinds are read (one entry per thread per
+//   round, every load of the window in flight together), a workgroup scan
+//   ranks the macro-nodes, and pair i (macro-nodes 2i and 2i + 1 of the
+//   range, the odd one of a window carried into the next) goes to LDS with
+//   both entries and both pages.  Pairs come in blocks of one per 16-lane
+//   group (8 at d = 64); block k belongs to workgroup k mod cx, and a group
+//   takes its pairs two at a time, both pairs' rows loaded before either is
+//   computed, a lane owning 8 dims as in the coarsening.  A workgroup writes
+//   the merged key, value, alpha and beta and the null's key, value and
+//   alpha, but no entry metadata: the kinds stay as they were while any
+//   workgroup of the unit may still be listing.  Each workgroup then takes a
+//   ticket from its unit's counter (device-scope atomic, after every load and
+//   store of the workgroup has completed); the one that takes the last ticket
+//   writes the metadata of every pair of the unit from the original records
+//   ({2, m, P} at the first entry, a null record at the second, the same
+//   checks as the merge itself), then resets the counter.  Nothing waits for
+//   another workgroup.
 #include "launch.h"
 #include "spicy_device.h"
 
@@ -40,7 +46,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kWin = 1024;                  // entries listed per window
-constexpr int kResident = 512;              // merge_pair workgroups resident at once (2 per CU)
+constexpr int kResident = 512;              // merge_level workgroups resident at once (2 per CU)
 
 struct MetaRec {
     int32_t kind;
@@ -139,9 +145,16 @@ struct PairIn {
     bool ok;
 };
 
+// A pair's records are merged when both are macro-nodes of positive mass
+// whose mass sum fits int32 (else the pair is skipped and flagged).
+__device__ __forceinline__ bool pair_ok(const MetaRec& r1, const MetaRec& r2) {
+    return r1.kind == 2 && r2.kind == 2 && r1.mass > 0 && r2.mass > 0 &&
+           static_cast<int64_t>(r1.mass) + r2.mass <= 0x7FFFFFFF;
+}
+
 template <typename T, int D>
 __device__ __forceinline__ void pair_load(const MergeArgs& a, int h, bool live, int32_t e1, int32_t P1, int32_t e2,
-                                          int32_t P2, int d0, PairIn<T>& in) {
+                                          int32_t P2, const MetaRec& r1, const MetaRec& r2, int d0, PairIn<T>& in) {
     const int H = a.cache.H;
     in.ok = live && P1 >= 0 && P2 >= 0;
     in.ph1 = static_cast<int64_t>(in.ok ? P1 : 0) * H + h;
@@ -154,15 +167,14 @@ __device__ __forceinline__ void pair_load(const MergeArgs& a, int h, bool live, 
         const T* kp = static_cast<const T*>(a.cache.k);
         const T* vp = static_cast<const T*>(a.cache.v);
         const T* ab = static_cast<const T*>(a.cache.ab);
-        const MetaRec* meta = static_cast<const MetaRec*>(a.cache.meta);
         in.k1.load(kp + in.ph1 * kPage * D + slot_elem(in.s1, d0));
         in.k2.load(kp + in.ph2 * kPage * D + slot_elem(in.s2, d0));
         in.v1.load(vp + in.ph1 * kPage * D + slot_elem(in.s1, d0));
         in.v2.load(vp + in.ph2 * kPage * D + slot_elem(in.s2, d0));
         in.b1 = ab[(in.ph1 * kPage + in.s1) * 2 + 1];
         in.b2 = ab[(in.ph2 * kPage + in.s2) * 2 + 1];
-        in.r1 = meta[in.ph1 * kPage + in.s1];
-        in.r2 = meta[in.ph2 * kPage + in.s2];
+        in.r1 = r1;
+        in.r2 = r2;
     } else {
         in.k1.zero();
         in.k2.zero();
@@ -179,8 +191,7 @@ __device__ __forceinline__ void pair_store(const MergeArgs& a, const PairIn<T>& 
     constexpr int LPH = D / 8;                // lanes per pair
     constexpr int PARTNER = LPH / 2;          // lane distance to the rotary partner
     int32_t i1 = in.r1.mass, i2 = in.r2.mass;
-    if (in.ok && (in.r1.kind != 2 || in.r2.kind != 2 || in.r1.mass <= 0 || in.r2.mass <= 0 ||
-                  static_cast<int64_t>(in.r1.mass) + in.r2.mass > 0x7FFFFFFF)) {
+    if (in.ok && !pair_ok(in.r1, in.r2)) {
         raise_err(a.err, SPICY_DEVERR_SEGMENTS);
         i1 = i2 = 0;                                          // not stored
     }
@@ -270,137 +281,187 @@ __device__ __forceinline__ void pair_store(const MergeArgs& a, const PairIn<T>& 
         ab[(in.ph1 * kPage + in.s1) * 2 + 1] = Elem<T>::from_f64(sig / (2.0 * D));
         ab[(in.ph2 * kPage + in.s2) * 2 + 0] = Elem<T>::from_f32(-__builtin_huge_valf());
         ab[(in.ph2 * kPage + in.s2) * 2 + 1] = Elem<T>::from_f32(0.f);
-        MetaRec* mt = static_cast<MetaRec*>(a.cache.meta);
-        mt[in.ph1 * kPage + in.s1] = MetaRec{2, i1 + i2, P};
-        mt[in.ph2 * kPage + in.s2] = MetaRec{0, 0, 0};
     }
 }
 
-__global__ __launch_bounds__(kThreads) void merge_list_kernel(MergeArgs a) {
-    __shared__ int32_t l_e[kWin + 1];         // the window's macro-nodes in order (slot 0: the carried one)
-    __shared__ int32_t l_p[kWin + 1];         // their pages
-    __shared__ int32_t w_cnt[kWaves];
+// Lists the macro-nodes of the window [w0, min(w0 + kWin, e1)) of sequence b,
+// head h, after the carried one (slot 0 when `carried`): entries in l_e,
+// pages in l_p, metadata records in l_r, in entry order.  Returns their
+// number, the carried one included.  Every thread of the workgroup calls it.
+__device__ __forceinline__ int32_t list_window(const MergeArgs& a, int b, int h, int32_t w0, int32_t e1,
+                                               int32_t carried, int32_t* l_e, int32_t* l_p, MetaRec* l_r,
+                                               int32_t* w_cnt) {
+    constexpr int kRounds = kWin / kThreads;
     const int H = a.cache.H;
-    const int64_t unit = blockIdx.x;          // sequence * H + head
-    const int b = static_cast<int>(unit / H);
-    const int h = static_cast<int>(unit % H);
-    const int t = threadIdx.x;
-    const int lane = t % kWave, wave = t / kWave;
-    const int32_t e0 = a.entry_begin[b], e1 = a.entry_end[b];
-    if (e0 < 0 || e0 > e1 || e1 - e0 > a.max_range) {
-        if (t == 0) {
-            raise_err(a.err, SPICY_DEVERR_SEGMENTS);
-            a.pair_count[unit] = 0;
-        }
-        return;
-    }
+    const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
     const MetaRec* meta = static_cast<const MetaRec*>(a.cache.meta);
-    int4* out = a.pairs + unit * a.cap;
-    int32_t carried = 0;                      // 1: slot 0 holds an unpaired macro-node
-    int32_t done = 0;                         // pairs of the range before this window
-    for (int32_t w0 = e0; w0 < e1; w0 += kWin) {
-        constexpr int kRounds = kWin / kThreads;
-        int32_t pg[kRounds];
-        bool mac[kRounds];
+    int32_t pg[kRounds];
+    MetaRec rec[kRounds];
+    bool mac[kRounds];
 #pragma unroll
-        for (int r = 0; r < kRounds; ++r) {
-            const int32_t e = w0 + r * kThreads + t;
-            pg[r] = e < e1 ? page_of(a, b, e) : -1;
-        }
-#pragma unroll
-        for (int r = 0; r < kRounds; ++r) {
-            const int32_t e = w0 + r * kThreads + t;
-            mac[r] = pg[r] >= 0 && meta[(static_cast<int64_t>(pg[r]) * H + h) * kPage + e % kPage].kind == 2;
-        }
-        int32_t base = carried;               // list slot of this round's first macro-node
-#pragma unroll
-        for (int r = 0; r < kRounds; ++r) {
-            const uint64_t M = __ballot(mac[r]);
-            if (lane == 0) w_cnt[wave] = __popcll(M);
-            __syncthreads();
-            int32_t before = 0, total = 0;
-#pragma unroll
-            for (int w = 0; w < kWaves; ++w) {
-                before += w < wave ? w_cnt[w] : 0;
-                total += w_cnt[w];
-            }
-            if (mac[r]) {
-                const int32_t slot = base + before + __popcll(M & ((1ull << lane) - 1ull));
-                l_e[slot] = w0 + r * kThreads + t;
-                l_p[slot] = pg[r];
-            }
-            base += total;
-            __syncthreads();                  // w_cnt is rewritten by the next round
-        }
-        const int32_t n = base;
-        const int32_t np = n / 2;
-        for (int32_t i = t; i < np; i += kThreads) {
-            const int32_t q = done + i;
-            if (q < a.cap) out[q] = make_int4(l_e[2 * i], l_e[2 * i + 1], l_p[2 * i], l_p[2 * i + 1]);
-            else raise_err(a.err, SPICY_DEVERR_CAPACITY);
-        }
-        done += np;
-        const int32_t odd = n & 1;
-        const int32_t last_e = odd ? l_e[n - 1] : 0, last_p = odd ? l_p[n - 1] : 0;
-        __syncthreads();                      // every read of the list is done
-        if (odd && t == 0) {
-            l_e[0] = last_e;
-            l_p[0] = last_p;
-        }
-        carried = odd;
-        __syncthreads();
+    for (int r = 0; r < kRounds; ++r) {
+        const int32_t e = w0 + r * kThreads + t;
+        pg[r] = e < e1 ? page_of(a, b, e) : -1;
     }
-    if (t == 0) a.pair_count[unit] = done < a.cap ? done : a.cap;
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) {
+        const int32_t e = w0 + r * kThreads + t;
+        rec[r] = pg[r] >= 0 ? meta[(static_cast<int64_t>(pg[r]) * H + h) * kPage + e % kPage] : MetaRec{0, 0, 0};
+        mac[r] = rec[r].kind == 2;
+    }
+    int32_t base = carried;                   // list slot of this round's first macro-node
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) {
+        const uint64_t M = __ballot(mac[r]);
+        if (lane == 0) w_cnt[wave] = __popcll(M);
+        __syncthreads();
+        int32_t before = 0, total = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            before += w < wave ? w_cnt[w] : 0;
+            total += w_cnt[w];
+        }
+        if (mac[r]) {
+            const int32_t slot = base + before + __popcll(M & ((1ull << lane) - 1ull));
+            l_e[slot] = w0 + r * kThreads + t;
+            l_p[slot] = pg[r];
+            l_r[slot] = rec[r];
+        }
+        base += total;
+        __syncthreads();                      // w_cnt is rewritten by the next round; the list is complete
+    }
+    return base;
+}
+
+// The odd last macro-node of a window becomes slot 0 of the next one.
+__device__ __forceinline__ void carry_last(int32_t n, int32_t* l_e, int32_t* l_p, MetaRec* l_r) {
+    const int32_t odd = n & 1;
+    const int32_t last_e = odd ? l_e[n - 1] : 0, last_p = odd ? l_p[n - 1] : 0;
+    const MetaRec last_r = odd ? l_r[n - 1] : MetaRec{0, 0, 0};
+    __syncthreads();                          // every read of the list is done
+    if (odd && threadIdx.x == 0) {
+        l_e[0] = last_e;
+        l_p[0] = last_p;
+        l_r[0] = last_r;
+    }
+    __syncthreads();
+}
+
+// The metadata of the listed pairs 0 .. np-1 (one pair per thread), from
+// their records as listed: the merged record at the first entry, a null
+// record at the second.
+__device__ __forceinline__ void write_meta(const MergeArgs& a, int h, const int32_t* l_e, const int32_t* l_p,
+                                           const MetaRec* l_r, int32_t np) {
+    const int H = a.cache.H;
+    MetaRec* meta = static_cast<MetaRec*>(a.cache.meta);
+    for (int32_t i = threadIdx.x; i < np; i += kThreads) {
+        const int32_t P1 = l_p[2 * i], P2 = l_p[2 * i + 1];
+        if (P1 < 0 || P2 < 0) continue;
+        const int64_t x1 = (static_cast<int64_t>(P1) * H + h) * kPage + l_e[2 * i] % kPage;
+        const int64_t x2 = (static_cast<int64_t>(P2) * H + h) * kPage + l_e[2 * i + 1] % kPage;
+        const MetaRec r1 = l_r[2 * i], r2 = l_r[2 * i + 1];
+        if (!pair_ok(r1, r2)) continue;
+        meta[x1] = MetaRec{2, r1.mass + r2.mass, r1.pos_sum + r2.pos_sum};
+        meta[x2] = MetaRec{0, 0, 0};
+    }
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void merge_pair_kernel(MergeArgs a) {
+__global__ __launch_bounds__(kThreads) void merge_level_kernel(MergeArgs a) {
     constexpr int LPH = D / 8;                // lanes per pair
     constexpr int PPW = kWave / LPH;          // pairs per wavefront round
-    constexpr int NG = kWaves * PPW;          // groups of the workgroup
+    constexpr int NG = kWaves * PPW;          // groups of the workgroup: pairs per block
     constexpr int PARTNER = LPH / 2;
+    __shared__ int32_t l_e[kWin + 1];         // the window's macro-nodes in order (slot 0: the carried one)
+    __shared__ int32_t l_p[kWin + 1];         // their pages
+    __shared__ MetaRec l_r[kWin + 1];         // their metadata records
+    __shared__ int32_t w_cnt[kWaves];
+    __shared__ int32_t s_last;
+    const int H = a.cache.H;
     const int64_t unit = blockIdx.y;          // sequence * H + head
-    const int h = static_cast<int>(unit % a.cache.H);
+    const int b = static_cast<int>(unit / H);
+    const int h = static_cast<int>(unit % H);
     const int lane = threadIdx.x % kWave;
     const int j = lane % LPH;
     const int d0 = 8 * j;
     const bool hi_half = j >= PARTNER;
     const int grp = (threadIdx.x / kWave) * PPW + lane / LPH;
     const bool rotate = a.rope_base > 0.0;
+    const int32_t cx = static_cast<int32_t>(gridDim.x), x = static_cast<int32_t>(blockIdx.x);
     double theta[4];
     {
         const int pair0 = 8 * (hi_half ? j - PARTNER : j) + (hi_half ? 4 : 0);
 #pragma unroll
         for (int r = 0; r < 4; ++r) theta[r] = a.theta[pair0 + r];
     }
-    const int32_t count = a.pair_count[unit];
-    const int64_t start = static_cast<int64_t>(blockIdx.x) * NG;
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * NG;
-    for (int64_t r0 = start; r0 < count; r0 += 2 * stride) {          // uniform over the workgroup
-        PairIn<T> in[2];
-        bool any[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int64_t pj = r0 + u * stride + grp;
-            const bool live = pj < count;
-            any[u] = __any(live);                  // uniform over the wavefront
-            const int4 pr = live ? a.pairs[unit * a.cap + pj] : make_int4(0, 0, -1, -1);
-            pair_load<T, D>(a, h, live, pr.x, pr.z, pr.y, pr.w, d0, in[u]);
-        }
-        // a wavefront whose pairs of this pass are all past the count skips
-        // their arithmetic (its lanes only ever exchange values among
-        // themselves), which leaves the SIMD's fp64 unit to the others
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-            if (any[u]) pair_store<T, D>(a, in[u], j, hi_half, rotate, theta);
+    const int32_t e0 = a.entry_begin[b], e1 = a.entry_end[b];
+    if (e0 < 0 || e0 > e1 || e1 - e0 > a.max_range) {
+        if (threadIdx.x == 0 && x == 0) raise_err(a.err, SPICY_DEVERR_SEGMENTS);
+        return;                               // uniform over the unit's workgroups: no ticket taken
     }
+    int32_t carried = 0;
+    int32_t done = 0;                         // pairs of the range before this window
+    int32_t n = 0;
+    for (int32_t w0 = e0; w0 < e1; w0 += kWin) {
+        n = list_window(a, b, h, w0, e1, carried, l_e, l_p, l_r, w_cnt);
+        const int32_t q_lo = done, q_hi = done + n / 2;
+        // this workgroup's blocks k = x, x + cx, ... of the window's pairs,
+        // two blocks per pass (uniform over the workgroup)
+        int32_t k = q_lo / NG;
+        k += ((x - k % cx) % cx + cx) % cx;
+        for (; static_cast<int64_t>(k) * NG < q_hi; k += 2 * cx) {
+            PairIn<T> in[2];
+            bool any[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int64_t q = (static_cast<int64_t>(k) + u * cx) * NG + grp;
+                const bool live = q >= q_lo && q < q_hi;
+                any[u] = __any(live);             // uniform over the wavefront
+                const int32_t i = live ? static_cast<int32_t>(q - q_lo) : 0;
+                pair_load<T, D>(a, h, live, l_e[2 * i], l_p[2 * i], l_e[2 * i + 1], l_p[2 * i + 1], l_r[2 * i],
+                                l_r[2 * i + 1], d0, in[u]);
+            }
+            // a wavefront whose pairs of this pass are all past the count
+            // skips their arithmetic (its lanes only ever exchange values
+            // among themselves), which leaves the SIMD's fp64 unit to the others
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+                if (any[u]) pair_store<T, D>(a, in[u], j, hi_half, rotate, theta);
+        }
+        done = q_hi;
+        carried = n & 1;
+        if (w0 + kWin < e1) carry_last(n, l_e, l_p, l_r);
+    }
+    // arrival: every load and store of this workgroup has completed
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int32_t old = __hip_atomic_fetch_add(a.ticket + unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (old >= cx) raise_err(a.err, SPICY_DEVERR_TICKET);
+        s_last = old == cx - 1;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    // the last workgroup of the unit: every listing is done, so the records
+    // can change now (a range of one window is still listed in LDS; a
+    // longer one is listed again, from the unchanged records)
+    if (e1 - e0 <= kWin) {
+        write_meta(a, h, l_e, l_p, l_r, n / 2);
+    } else {
+        carried = 0;
+        for (int32_t w0 = e0; w0 < e1; w0 += kWin) {
+            n = list_window(a, b, h, w0, e1, carried, l_e, l_p, l_r, w_cnt);
+            write_meta(a, h, l_e, l_p, l_r, n / 2);
+            carried = n & 1;
+            if (w0 + kWin < e1) carry_last(n, l_e, l_p, l_r);
+        }
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(a.ticket + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <typename T, int D>
 spicy_status launch_merge_t(const MergeArgs& a, hipStream_t stream) {
     const int64_t units = static_cast<int64_t>(a.B) * a.cache.H;
-    hipLaunchKernelGGL(merge_list_kernel, dim3(static_cast<unsigned>(units)), dim3(kThreads), 0, stream, a);
-    if (hipGetLastError() != hipSuccess) return SPICY_ERR_HIP;
     // at most kResident workgroups over all (sequence, head) units, so that
     // they all run at once (a second round of workgroups doubles the time);
     // each takes 2 x 16 (d = 128) or 2 x 32 (d = 64) pairs per pass
@@ -408,7 +469,7 @@ spicy_status launch_merge_t(const MergeArgs& a, hipStream_t stream) {
     const int64_t want = (static_cast<int64_t>(a.cap) + 2 * ngrp - 1) / (2 * ngrp);
     const int64_t fill = kResident / units > 1 ? kResident / units : 1;
     const int64_t cx = want < 1 ? 1 : (want < fill ? want : fill);
-    hipLaunchKernelGGL((merge_pair_kernel<T, D>), dim3(static_cast<unsigned>(cx), static_cast<unsigned>(units)),
+    hipLaunchKernelGGL((merge_level_kernel<T, D>), dim3(static_cast<unsigned>(cx), static_cast<unsigned>(units)),
                        dim3(kThreads), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return SPICY_ERR_HIP;
     return SPICY_OK;

@@ -228,9 +228,8 @@ struct MergeArgs {
     const int32_t* entry_begin;   // [B]
     const int32_t* entry_end;     // [B]
     int32_t* err;
-    int32_t* pair_count;          // [B*H]       workspace: pairs of each (sequence, head)
-    int4* pairs;                  // [B*H][cap]  workspace: {first entry, second entry, their pages}
-    int32_t cap;                  // pairs per (sequence, head) = (max_range + 1) / 2
+    int32_t* ticket;              // [B*H]  workspace: arrivals per (sequence, head), zero between calls
+    int32_t cap;                  // pairs per (sequence, head) at most = (max_range + 1) / 2
     int32_t B;
     int32_t max_pages;
     int32_t max_range;

@@ -108,10 +108,11 @@ typedef enum { SPICY_F32 = 0, SPICY_BF16 = 1 } spicy_dtype;
                                           [k_t; v_t], bad row pointers, a sequence
                                           longer than 2^20 tokens or one whose
                                           total variation times N reaches 2^62   */
-#define SPICY_DEVERR_TICKET      0x40 /* decode: a row's arrival counter was not
-                                          zero when the call started (workspace
-                                          not zero-filled, or reused for more
-                                          query rows than it was zeroed for)    */
+#define SPICY_DEVERR_TICKET      0x40 /* decode or merge: an arrival counter was
+                                          not zero when the call started
+                                          (workspace not zero-filled, or reused
+                                          for more rows or units than it was
+                                          zeroed for)                           */
 
 #define SPICY_PAGE_SIZE 16
 #define SPICY_WORKSPACE_HEADER 256   /* bytes before any per-call scratch     */
@@ -261,7 +262,12 @@ spicy_status spicy_coarsen_weighted(const spicy_cache* cache,
  *   bytes; first int32 = sticky device error word: SPICY_DEVERR_SEGMENTS for
  *   a range outside [0, max_range] or a pair whose metadata is not two
  *   macro-nodes of positive mass (that pair is skipped), SPICY_DEVERR_PAGE_ID
- *   and SPICY_DEVERR_CAPACITY for entries the table or pool cannot hold.
+ *   and SPICY_DEVERR_CAPACITY for entries the table or pool cannot hold;
+ *   then one int32 arrival counter per (sequence, KV head), which must be
+ *   zero when a call starts: allocate the workspace zero-filled (every
+ *   completed call leaves the counters at zero); a counter found above its
+ *   unit's workgroup count sets SPICY_DEVERR_TICKET.  Calls that overlap on
+ *   one workspace race.
  * Errors: SPICY_ERR_ARG (null pointer, B < 0, max_range < 0, meta NULL),
  *   SPICY_ERR_UNSUPPORTED (s2 set, head_dim not 64/128, B * H_kv > 65535),
  *   SPICY_ERR_CAPACITY (workspace too small), SPICY_ERR_HIP.

@@ -235,7 +235,7 @@ def test_merge_rejects_bad_arguments(lib):
     assert call(cache=diag) == 4
     # header, int32 count per (sequence, head), int4 per pair, (range + 1) / 2 pairs
     up = lambda x: (x + 255) // 256 * 256
-    assert lib.spicy_merge_workspace_bytes(3, 4, 101) == 256 + up(4 * 12) + up(16 * 12 * 51)
+    assert lib.spicy_merge_workspace_bytes(3, 4, 101) == 256 + up(4 * 12)
     assert lib.spicy_merge_workspace_bytes(3, 0, 101) == 0
 
 

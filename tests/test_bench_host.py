@@ -45,6 +45,22 @@ def test_merge_and_policy_bytes():
     assert bench.policy_alg_bytes(c, spec) == 2 * 8 * 2 * 64 * 2 + 8 * 2 + 4 * (2 * 4 + 1) + 4 * 3
 
 
+def test_merge_pair_count_halves_the_macro_nodes_of_each_range():
+    """Per (sequence, head): macro-nodes in [entry_start, length), halved and
+    rounded down; C-points (kind 1), nulls and entries outside the range do
+    not count."""
+    meta = np.zeros((4, 2, 16, 4), np.int32)
+    table = np.array([[2, 0], [1, 3]], np.int32)
+    meta[2, 0, 3:8, 0] = 2                     # sequence 0, head 0: 5 macro-nodes in range
+    meta[2, 0, 5, 0] = 1                       # one of them a C-point: 4 left -> 2 pairs
+    meta[0, 1, 0:3, 0] = 2                     # sequence 0, head 1: entries 16..18 -> 1 pair
+    meta[2, 1, 0:2, 0] = 2                     # before entry_start: not counted
+    meta[1, 0, 14:16, 0] = 2                   # sequence 1, head 0: entries 14, 15
+    meta[3, 0, 0, 0] = 2                       # entry 16 -> 3 nodes -> 1 pair
+    meta[3, 1, 5, 0] = 2                       # entry 21: past length 20, not counted
+    assert bench.merge_pair_count(meta, table, [3, 10], [19, 20]) == 2 + 1 + 1
+
+
 def test_traffic_table_follows_the_sources(tmp_path, monkeypatch):
     """A traffic line counts only while its digest matches the kernel's
     sources; a missing file gives None."""
@@ -54,7 +70,7 @@ def test_traffic_table_follows_the_sources(tmp_path, monkeypatch):
     dig = bench.kernel_digest("decode_mfma_kernel")
     (prof / "traffic_w.txt").write_text(
         f"traffic_bytes decode_mfma_kernel 123 {dig}\n"
-        f"traffic_bytes merge_pair_kernel 456 {'0' * 64}\n")
+        f"traffic_bytes merge_level_kernel 456 {'0' * 64}\n")
     digests = {k: bench.kernel_digest(k) for k in bench.KERNEL_SOURCE}   # of the real sources
     monkeypatch.setattr(bench, "kernel_digest", lambda k: digests[k])
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
@@ -144,8 +160,8 @@ def test_kernel_names_from_rocprof():
     """Template arguments, namespaces and anonymous namespaces removed."""
     assert bench._base_kernel_name("void spicy::decode_mfma_kernel<128, 3, false, 1, 4>(spicy::DecodeArgs)") == \
         "decode_mfma_kernel"
-    assert bench._base_kernel_name("spicy::(anonymous namespace)::merge_list_kernel(spicy::MergeArgs)") == \
-        "merge_list_kernel"
+    assert bench._base_kernel_name("void spicy::(anonymous namespace)::merge_level_kernel<unsigned short, 128>"
+                                   "(spicy::MergeArgs)") == "merge_level_kernel"
     assert bench._base_kernel_name("void spicy::(anonymous namespace)::compact_move_kernel<2>(spicy::CompactArgs)") \
         == "compact_move_kernel"
     assert bench._base_kernel_name("void (anonymous namespace)::stream_read_kernel<1>(HIP_vector_type<unsigned "
