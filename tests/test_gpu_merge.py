@@ -31,6 +31,10 @@ WORKLOADS = {
     "long_ragged_small": lambda: W.long_ragged(T_range=(9000, 20000), B=3),
     "shared_prefix_small": lambda: W.shared_prefix(B=5, prefix_T=6000, chunk_T=2000, suffix_range=(37, 300)),
     "bf16_d64": lambda: W.qwen2_1p5b(d=64, B=4, T=4096),
+    # ranges longer than one listing window of 1024 entries: about 1150
+    # entries per sequence (two windows) and about 2060 (three windows)
+    "qwen2_7b_two_windows": lambda: W.qwen2_7b(B=2),
+    "long_ragged_three_windows": lambda: W.long_ragged(T_range=(100000, 110000), B=1),
 }
 
 
@@ -56,6 +60,9 @@ def gpu_merge(cache, wl, begin, end, levels=1):
         cgd.spicy_merge_level(cache, wl.calls[-1].rope_base, tb, eb, ee, rng, ws)
     torch.cuda.synchronize()
     assert cgd.device_error(ws) == 0
+    # after the 256-byte header, one arrival counter per (sequence, KV head):
+    # every completed call leaves them at zero
+    assert int(ws[64:64 + wl.B * wl.H_kv].abs().sum().item()) == 0
 
 
 def store_value(bits, store):
