@@ -556,6 +556,9 @@ def decode_config_line(wl, dw, rotate_bytes: float, reps: int, ceiling: bool = T
            "target_frac": DECODE_TARGET_FRAC,
            "query_tokens_per_s": round(wl.B * dw.q_tokens / (st["mean"] * 1e-6), 1),
            "query_tokens_per_seq": dw.q_tokens, "plan": dw.plan, "shared_prefix_pages": dw.shared_prefix_pages}
+    # HBM bytes per launch from the workload's rocprofv3 counters, while the sources match
+    t = measured_traffic(wl.name)
+    out["traffic"] = int(t["decode_mfma_kernel"]) if t and "decode_mfma_kernel" in t else None
     del copies
     if ceiling:
         c = read_ceiling(db, rotate_bytes)
